@@ -1,0 +1,298 @@
+#!/usr/bin/env python3
+"""Benchmark of the blockwise-scaled FP8 GEMM hot path on one MI355X.
+
+Workloads (synthetic, seeded; inputs resident in HBM before timing starts):
+  decode   (default) o_proj decode, M=1, N=K=4096.  One step = 1x128
+           activation quantisation + W8A8 GEMM + W8A16 GEMM (bf16 activations).
+           Weights rotate over --copies distinct copies so no call finds its
+           weights in a cache.  Headline: step HBM GB/s (algorithmic bytes).
+  prefill  o_proj prefill, M=N=K=4096, 1% outlier channels.  One step =
+           activation quantisation + W8A8 GEMM.  Headline: TFLOP/s.
+  blk32    block-32 UE8M0 weight-only GEMM, N=4096, K=7168, M=--m (default 1).
+           Headline: HBM GB/s.
+
+Per-kernel durations come from HIP events recorded around every launch in
+the timed steps, on the stream the kernels run on.  The roofline object
+reports the dominant kernel's algorithmic bytes (or FLOPs) per launch over
+its average duration.  The cpu_baseline object times the CPU oracle on a
+bounded sample of the same workload.
+
+Prints exactly one JSON line on stdout.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "µs, TFLOP/s, HBM GB/s and % of roofline; blockwise FP8 GEMM N=K=4096, M=1..4096"
+HBM_PEAK_GBS = 8000.0
+FP8_PEAK_TFLOPS = 5000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", choices=["decode", "prefill", "blk32"], default="decode")
+    p.add_argument("--m", type=int, default=None, help="token count for blk32 / decode")
+    p.add_argument("--copies", type=int, default=32, help="distinct weight copies rotated per call")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+# ------------------------------------------------------------ byte counts ----
+def bytes_quant(M, K):
+    G = (K + 127) // 128
+    return 2 * M * K + M * K + 4 * M * G
+
+
+def bytes_w8a8(M, N, K):
+    return N * K + 4 * ((N + 127) // 128) * (K // 128) + M * K + 4 * M * ((K + 127) // 128) + 2 * M * N
+
+
+def bytes_w8a16(M, N, K):
+    return N * K + 4 * ((N + 127) // 128) * (K // 128) + 2 * M * K + 2 * M * N
+
+
+def bytes_blk32(M, N, K):
+    return N * K + (N // 32) * (K // 32) + 2 * M * K + 2 * M * N
+
+
+# ------------------------------------------------------------- GPU timing ----
+class Timer:
+    """Events around every launch of the timed steps, on the current stream."""
+
+    def __init__(self, torch, names, steps):
+        self.torch = torch
+        self.names = names
+        self.ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(steps)]
+
+    def mark(self, step, i):
+        self.ev[step][i].record()
+
+    def per_kernel_us(self):
+        out = {}
+        for i, n in enumerate(self.names):
+            d = [self.ev[s][i].elapsed_time(self.ev[s][i + 1]) for s in range(len(self.ev))]
+            d.sort()
+            out[n] = {"avg_us": 1e3 * sum(d) / len(d), "median_us": 1e3 * d[len(d) // 2],
+                      "p10_us": 1e3 * d[len(d) // 10], "p90_us": 1e3 * d[(9 * len(d)) // 10]}
+        return out
+
+
+def run_steps(torch, step_fn, names, steps, warmup):
+    for i in range(warmup):
+        step_fn(i, None)
+    torch.cuda.synchronize()
+    timer = Timer(torch, names, steps)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for s in range(steps):
+        step_fn(warmup + s, (timer, s))
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return start.elapsed_time(end) / steps, wall, timer.per_kernel_us()
+
+
+# ------------------------------------------------------------ CPU baseline ----
+def cpu_baseline(fn, seconds, unit_per_call, unit, sample):
+    import numpy as np  # noqa: F401
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    calls = 0
+    t0 = time.perf_counter()
+    while True:
+        fn()
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": unit_per_call * calls / el, "unit": unit, "cores": threads, "kind": "oracle",
+            "sample": f"{sample}; {calls} calls in {el:.1f} s; numpy float64, BLAS threads={threads}"}
+
+
+# --------------------------------------------------------------- workloads ----
+def bench_decode(torch, bfp8, inputs, args):
+    M = args.m or 1
+    N = K = 4096
+    data = inputs.workload(1, M=M)
+    x = data["x"].cuda()
+    w = data["w"].cuda()
+    wq0, ws0 = bfp8.quantize_weight(w)
+    copies = [(wq0.clone(), ws0.clone()) for _ in range(args.copies)]
+    del w
+    xq = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+    xs = torch.empty((M, K // 128), dtype=torch.float32, device="cuda")
+    y8 = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    y16 = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    ws8 = bfp8.make_workspace(bfp8.OP_GEMM_W8A8_BLK128, M, N, K)
+    ws16 = bfp8.make_workspace(bfp8.OP_GEMM_W8A16_BLK128, M, N, K)
+    C = len(copies)
+
+    def step(i, t):
+        a, b = copies[(2 * i) % C], copies[(2 * i + 1) % C]
+        if t: t[0].mark(t[1], 0)
+        bfp8.bfp8_quantize_act_1x128(x, xq, xs)
+        if t: t[0].mark(t[1], 1)
+        bfp8.bfp8_gemm_w8a8_blk128(xq, xs, a[0], a[1], y8, ws8)
+        if t: t[0].mark(t[1], 2)
+        bfp8.bfp8_gemm_w8a16_blk128(x, b[0], b[1], y16, ws16)
+        if t: t[0].mark(t[1], 3)
+
+    names = ["quant_act_1x128", "gemm_w8a8_blk128", "gemm_w8a16_blk128"]
+    ms, wall, kern = run_steps(torch, step, names, args.steps, args.warmup)
+    nbytes = {"quant_act_1x128": bytes_quant(M, K), "gemm_w8a8_blk128": bytes_w8a8(M, N, K),
+              "gemm_w8a16_blk128": bytes_w8a16(M, N, K)}
+    for n in names:
+        kern[n]["alg_bytes"] = nbytes[n]
+        kern[n]["GBps"] = nbytes[n] / (kern[n]["avg_us"] * 1e3)
+        kern[n]["hbm_frac"] = kern[n]["GBps"] / HBM_PEAK_GBS
+    step_bytes = sum(nbytes.values())
+    dom = max(["gemm_w8a8_blk128", "gemm_w8a16_blk128"], key=lambda n: kern[n]["avg_us"])
+    roof = {"kernel": dom, "bound": "hbm", "achieved": kern[dom]["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": kern[dom]["GBps"] / HBM_PEAK_GBS, "traffic": None}
+    result = {"value": step_bytes / (ms * 1e6), "unit": "GB/s", "ms_per_step": ms, "dtype": "e4m3,bf16",
+              "config": {"workload": "o_proj decode: 1x128 act quant + W8A8 blk128 + W8A16 blk128 (bf16 x)",
+                         "M": M, "N": N, "K": K, "weight_copies": C, "out_dtype": "bf16",
+                         "step_alg_bytes": step_bytes},
+              "roofline": roof, "kernels": kern, "wall_s": wall}
+
+    if not args.no_cpu_baseline:
+        import oracle
+        xh = data["x"].float().numpy()
+        wq_h, ws_h = wq0.cpu().numpy(), ws0.cpu().numpy()
+
+        def one():
+            q, s = oracle.quantize_act_1x128(xh)
+            oracle.gemm_w8a8_blk128(q, s, wq_h, ws_h)
+            oracle.gemm_w8a16_blk128(xh, wq_h, ws_h)
+
+        result["cpu_baseline"] = cpu_baseline(one, args.cpu_seconds, step_bytes / 1e9, "GB/s",
+                                              f"full decode step (M={M}, N=K=4096) repeated")
+    return result
+
+
+def bench_prefill(torch, bfp8, inputs, args):
+    M = args.m or 4096
+    N = K = 4096
+    data = inputs.workload(2, M=M)
+    x = data["x"].cuda()
+    wq, ws = bfp8.quantize_weight(data["w"].cuda())
+    copies = [(wq.clone(), ws.clone()) for _ in range(4)]
+    xq = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+    xs = torch.empty((M, K // 128), dtype=torch.float32, device="cuda")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+
+    def step(i, t):
+        a = copies[i % len(copies)]
+        if t: t[0].mark(t[1], 0)
+        bfp8.bfp8_quantize_act_1x128(x, xq, xs)
+        if t: t[0].mark(t[1], 1)
+        bfp8.bfp8_gemm_w8a8_blk128(xq, xs, a[0], a[1], y)
+        if t: t[0].mark(t[1], 2)
+
+    names = ["quant_act_1x128", "gemm_w8a8_blk128"]
+    ms, wall, kern = run_steps(torch, step, names, args.steps, args.warmup)
+    flops = 2.0 * M * N * K
+    kern["quant_act_1x128"]["alg_bytes"] = bytes_quant(M, K)
+    kern["quant_act_1x128"]["GBps"] = bytes_quant(M, K) / (kern["quant_act_1x128"]["avg_us"] * 1e3)
+    g = kern["gemm_w8a8_blk128"]
+    g["alg_bytes"] = bytes_w8a8(M, N, K)
+    g["TFLOPs"] = flops / (g["avg_us"] * 1e6)
+    roof = {"kernel": "gemm_w8a8_blk128", "bound": "mfma", "achieved": g["TFLOPs"], "peak": FP8_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": g["TFLOPs"] / FP8_PEAK_TFLOPS, "traffic": None}
+    result = {"value": flops / (ms * 1e9), "unit": "TFLOP/s", "ms_per_step": ms, "dtype": "e4m3",
+              "config": {"workload": "o_proj prefill: 1x128 act quant + W8A8 blk128, 1% outlier channels",
+                         "M": M, "N": N, "K": K, "out_dtype": "bf16"},
+              "roofline": roof, "kernels": kern, "wall_s": wall}
+    if not args.no_cpu_baseline:
+        import oracle
+        rows = 8
+        xh = data["x"][:rows].float().numpy()
+        wq_h, ws_h = wq.cpu().numpy(), ws.cpu().numpy()
+
+        def one():
+            q, s = oracle.quantize_act_1x128(xh)
+            oracle.gemm_w8a8_blk128(q, s, wq_h, ws_h)
+
+        result["cpu_baseline"] = cpu_baseline(one, args.cpu_seconds, 2.0 * rows * N * K / 1e12, "TFLOP/s",
+                                              f"{rows} of {M} token rows of the prefill step")
+    return result
+
+
+def bench_blk32(torch, bfp8, inputs, args):
+    M = args.m or 1
+    N, K = 4096, 7168
+    x = inputs.activations(M, K, workload=3, dtype=torch.float16).cuda()
+    wq_h = inputs.block32_codes(N, K, workload=3)
+    s_h = inputs.block32_scales(N, K, workload=3)
+    st, e8_h, bad = bfp8.bfp8_prepare_blk32_ue8m0(wq_h, s_h)
+    assert st == 0, (st, bad)
+    copies = [(wq_h.cuda(), e8_h.cuda()) for _ in range(args.copies)]
+    y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    wsb = bfp8.make_workspace(bfp8.OP_GEMM_W8A16_BLK32_UE8M0, M, N, K)
+
+    def step(i, t):
+        a = copies[i % len(copies)]
+        if t: t[0].mark(t[1], 0)
+        bfp8.bfp8_gemm_w8a16_blk32_ue8m0(x, a[0], a[1], y, wsb)
+        if t: t[0].mark(t[1], 1)
+
+    names = ["gemm_w8a16_blk32_ue8m0"]
+    ms, wall, kern = run_steps(torch, step, names, args.steps, args.warmup)
+    nb = bytes_blk32(M, N, K)
+    k = kern[names[0]]
+    k["alg_bytes"] = nb
+    k["GBps"] = nb / (k["avg_us"] * 1e3)
+    roof = {"kernel": names[0], "bound": "hbm", "achieved": k["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": k["GBps"] / HBM_PEAK_GBS, "traffic": None}
+    result = {"value": nb / (ms * 1e6), "unit": "GB/s", "ms_per_step": ms, "dtype": "f16",
+              "config": {"workload": "block-32 UE8M0 W8A16 GEMM, fp16 x and out", "M": M, "N": N, "K": K,
+                         "weight_copies": len(copies)},
+              "roofline": roof, "kernels": kern, "wall_s": wall}
+    if not args.no_cpu_baseline:
+        import oracle
+        xh = x.float().cpu().numpy()
+        wqn, e8n = wq_h.numpy(), e8_h.numpy()
+        result["cpu_baseline"] = cpu_baseline(lambda: oracle.gemm_w8a16_blk32_ue8m0(xh, wqn, e8n), args.cpu_seconds,
+                                              nb / 1e9, "GB/s", f"full block-32 GEMM (M={M}) repeated")
+    return result
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path has no multi-GPU form in this build)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import blockwise_scaled_fp8_amd as bfp8
+    from blockwise_scaled_fp8_amd import inputs
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    bfp8.load()
+    fn = {"decode": bench_decode, "prefill": bench_prefill, "blk32": bench_blk32}[args.workload]
+    r = fn(torch, bfp8, inputs, args)
+    line = {"metric": METRIC, "value": r["value"], "unit": r["unit"], "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": r["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": r["dtype"], "data": "synthetic", "config": r["config"],
+            "roofline": r["roofline"], "cpu_baseline": r.get("cpu_baseline"), "kernels": r["kernels"],
+            "device": torch.cuda.get_device_name(0)}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,193 @@
+// C entry points of libbfp8: argument validation (before any HIP call),
+// kernel choice by M, launches, and the host-only block-32 scale packer.
+
+#include <math.h>
+#include <string.h>
+
+#include "bfp8.h"
+#include "bfp8_launch.hpp"
+
+using namespace bfp8;
+
+namespace {
+
+constexpr int64_t kAlign = 16;
+constexpr int64_t kMaxDim = (int64_t)1 << 31;   // every size must fit the kernels' 32-bit grid math
+
+bool aligned(const void* p) { return ((uintptr_t)p % kAlign) == 0; }
+bool dim_ok(int64_t v, int64_t lo) { return v >= lo && v < kMaxDim; }
+bool is16(int dtype) { return dtype == BFP8_BF16 || dtype == BFP8_F16; }
+bool is_out(int dtype) { return dtype == BFP8_BF16 || dtype == BFP8_F16 || dtype == BFP8_F32; }
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+bfp8_status launched(hipError_t e) { return e == hipSuccess ? BFP8_OK : BFP8_E_LAUNCH; }
+
+// Checks shared by the three GEMMs; `k_mult` / `n_mult` are the op's shape rules.
+bfp8_status check_gemm(const void* a, const void* b, const void* c, const void* y, int y_dtype,
+                       int64_t M, int64_t N, int64_t K, int64_t n_mult, size_t need,
+                       const void* workspace, size_t workspace_bytes) {
+    if (!a || !b || !c || !y) return BFP8_E_NULL;
+    if (!dim_ok(M, 1) || !dim_ok(N, n_mult) || !dim_ok(K, 128)) return BFP8_E_SHAPE;
+    if (N % n_mult != 0 || K % 128 != 0) return BFP8_E_SHAPE;
+    if (M * K >= ((int64_t)1 << 40) || N * K >= ((int64_t)1 << 40)) return BFP8_E_SHAPE;
+    if (!is_out(y_dtype)) return BFP8_E_DTYPE;
+    if (!aligned(a) || !aligned(b) || !aligned(c) || !aligned(y)) return BFP8_E_ALIGN;
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need) return BFP8_E_WORKSPACE;
+        if (!aligned(workspace)) return BFP8_E_ALIGN;
+    }
+    return BFP8_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+bfp8_status bfp8_quantize_act_1x128(const void* x, int x_dtype, int64_t M, int64_t K,
+                                    uint8_t* xq, float* xs, void* stream) {
+    if (!x || !xq || !xs) return BFP8_E_NULL;
+    if (!dim_ok(M, 1) || !dim_ok(K, 8) || K % 8 != 0 || M * K >= ((int64_t)1 << 40)) return BFP8_E_SHAPE;
+    if (!is16(x_dtype)) return BFP8_E_DTYPE;
+    if (!aligned(x) || !aligned(xq) || !aligned(xs)) return BFP8_E_ALIGN;
+    return launched(launch_quant_act_1x128(x, x_dtype == BFP8_BF16, M, K, xq, xs, as_stream(stream)));
+}
+
+bfp8_status bfp8_quantize_weight_128x128(const void* w, int w_dtype, int64_t N, int64_t K,
+                                         uint8_t* wq, float* ws, void* stream) {
+    if (!w || !wq || !ws) return BFP8_E_NULL;
+    if (!dim_ok(N, 1) || !dim_ok(K, 8) || K % 8 != 0 || N * K >= ((int64_t)1 << 40)) return BFP8_E_SHAPE;
+    if ((N + 127) / 128 > 65535) return BFP8_E_SHAPE;      // grid.y limit
+    if (!is16(w_dtype)) return BFP8_E_DTYPE;
+    if (!aligned(w) || !aligned(wq) || !aligned(ws)) return BFP8_E_ALIGN;
+    return launched(launch_quant_weight_128x128(w, w_dtype == BFP8_BF16, N, K, wq, ws, as_stream(stream)));
+}
+
+size_t bfp8_workspace_bytes(int op, int64_t M, int64_t N, int64_t K) {
+    if (M < 1 || N < 16 || K < 128) return 0;
+    switch (op) {
+        case BFP8_OP_GEMM_W8A8_BLK128:
+            if (M > kStreamMaxM) return 0;                  // the tiled kernel needs none
+            return stream_workspace_bytes(plan_stream(M, N, K));
+        case BFP8_OP_GEMM_W8A16_BLK128:
+        case BFP8_OP_GEMM_W8A16_BLK32_UE8M0:
+            return stream_workspace_bytes(plan_stream(M, N, K));
+        default:
+            return 0;
+    }
+}
+
+bfp8_status bfp8_gemm_w8a8_blk128(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
+                                  void* y, int y_dtype, int64_t M, int64_t N, int64_t K,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+    if (!xq || !xs || !wq || !ws || !y) return BFP8_E_NULL;
+    const size_t need = (dim_ok(M, 1) && dim_ok(N, 16) && dim_ok(K, 128))
+                            ? bfp8_workspace_bytes(BFP8_OP_GEMM_W8A8_BLK128, M, N, K) : 0;
+    bfp8_status st = check_gemm(xq, wq, ws, y, y_dtype, M, N, K, 16, need, workspace, workspace_bytes);
+    if (st != BFP8_OK) return st;
+    if (!aligned(xs)) return BFP8_E_ALIGN;
+    if (M <= kStreamMaxM)
+        return launched(launch_w8a8_stream(xq, xs, wq, ws, y, y_dtype, M, N, K, workspace, as_stream(stream)));
+    return launched(launch_w8a8_tile(xq, xs, wq, ws, y, y_dtype, M, N, K, as_stream(stream)));
+}
+
+bfp8_status bfp8_gemm_w8a16_blk128(const void* x, int x_dtype, const uint8_t* wq, const float* ws,
+                                   void* y, int y_dtype, int64_t M, int64_t N, int64_t K,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+    if (!x || !wq || !ws || !y) return BFP8_E_NULL;
+    const size_t need = (dim_ok(M, 1) && dim_ok(N, 16) && dim_ok(K, 128))
+                            ? bfp8_workspace_bytes(BFP8_OP_GEMM_W8A16_BLK128, M, N, K) : 0;
+    bfp8_status st = check_gemm(x, wq, ws, y, y_dtype, M, N, K, 16, need, workspace, workspace_bytes);
+    if (st != BFP8_OK) return st;
+    if (!is16(x_dtype)) return BFP8_E_DTYPE;
+    if ((M + 15) / 16 > 65535) return BFP8_E_SHAPE;         // grid.z limit
+    return launched(launch_w8a16_blk128_stream(x, x_dtype == BFP8_BF16, wq, ws, y, y_dtype, M, N, K,
+                                               workspace, as_stream(stream)));
+}
+
+bfp8_status bfp8_gemm_w8a16_blk32_ue8m0(const void* x, int x_dtype, const uint8_t* wq, const uint8_t* e8m0,
+                                        void* y, int y_dtype, int64_t M, int64_t N, int64_t K,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
+    if (!x || !wq || !e8m0 || !y) return BFP8_E_NULL;
+    const size_t need = (dim_ok(M, 1) && dim_ok(N, 32) && dim_ok(K, 128))
+                            ? bfp8_workspace_bytes(BFP8_OP_GEMM_W8A16_BLK32_UE8M0, M, N, K) : 0;
+    bfp8_status st = check_gemm(x, wq, e8m0, y, y_dtype, M, N, K, 32, need, workspace, workspace_bytes);
+    if (st != BFP8_OK) return st;
+    if (x_dtype != BFP8_F16) return BFP8_E_DTYPE;
+    if ((M + 15) / 16 > 65535) return BFP8_E_SHAPE;
+    return launched(launch_w8a16_blk32_stream(x, wq, e8m0, y, y_dtype, M, N, K, workspace, as_stream(stream)));
+}
+
+bfp8_status bfp8_prepare_blk32_ue8m0(const uint8_t* wq_host, const float* scale_host, int64_t N, int64_t K,
+                                     uint8_t* e8m0_host, int64_t* bad_index) {
+    if (bad_index) *bad_index = -1;
+    if (!wq_host || !scale_host || !e8m0_host || !bad_index) return BFP8_E_NULL;
+    if (N < 32 || K < 32 || N % 32 != 0 || K % 32 != 0 || N >= kMaxDim || K >= kMaxDim) return BFP8_E_SHAPE;
+    const int64_t count = N * K;
+    for (int64_t i = 0; i < count; ++i) {
+        if ((wq_host[i] & 0x7F) == 0x7F) {
+            *bad_index = i;
+            return BFP8_E_NAN_CODE;
+        }
+    }
+    const int64_t scales = (N / 32) * (K / 32);
+    for (int64_t i = 0; i < scales; ++i) {
+        const float s = scale_host[i];
+        if (!isfinite(s) || !(s > 0.0f)) {
+            *bad_index = i;
+            return BFP8_E_SCALE_NOT_POW2;
+        }
+        int e2 = 0;
+        const float frac = frexpf(s, &e2);         // s = frac * 2^e2, frac in [0.5, 1), exact
+        if (frac != 0.5f) {
+            *bad_index = i;
+            return BFP8_E_SCALE_NOT_POW2;
+        }
+        const int e = e2 - 1;
+        if (e < -14 || e > 7) {
+            *bad_index = i;
+            return BFP8_E_SCALE_WINDOW;
+        }
+    }
+    for (int64_t i = 0; i < scales; ++i) {
+        int e2 = 0;
+        frexpf(scale_host[i], &e2);
+        e8m0_host[i] = (uint8_t)(e2 - 1 + 127);
+    }
+    return BFP8_OK;
+}
+
+bfp8_status bfp8_get_limits(int op, int64_t* k_multiple, int64_t* n_multiple, int64_t* align_bytes,
+                            int64_t* m_stream_max) {
+    int64_t k = 0, n = 0, ms = 0;
+    switch (op) {
+        case BFP8_OP_QUANT_ACT_1X128: k = 8; n = 1; ms = 0; break;
+        case BFP8_OP_QUANT_WEIGHT_128X128: k = 8; n = 1; ms = 0; break;
+        case BFP8_OP_GEMM_W8A8_BLK128: k = 128; n = 16; ms = kStreamMaxM; break;
+        case BFP8_OP_GEMM_W8A16_BLK128: k = 128; n = 16; ms = INT32_MAX; break;
+        case BFP8_OP_GEMM_W8A16_BLK32_UE8M0: k = 128; n = 32; ms = INT32_MAX; break;
+        default: return BFP8_E_OP;
+    }
+    if (k_multiple) *k_multiple = k;
+    if (n_multiple) *n_multiple = n;
+    if (align_bytes) *align_bytes = kAlign;
+    if (m_stream_max) *m_stream_max = ms;
+    return BFP8_OK;
+}
+
+const char* bfp8_status_string(bfp8_status s) {
+    switch (s) {
+        case BFP8_OK: return "ok";
+        case BFP8_E_NULL: return "a required pointer is NULL";
+        case BFP8_E_SHAPE: return "a size is out of range or not a required multiple";
+        case BFP8_E_DTYPE: return "unsupported dtype code";
+        case BFP8_E_ALIGN: return "a device pointer is not 16-byte aligned";
+        case BFP8_E_WORKSPACE: return "workspace missing or too small";
+        case BFP8_E_NAN_CODE: return "E4M3 NaN code (0x7F/0xFF) in the weights";
+        case BFP8_E_SCALE_NOT_POW2: return "block scale is not a positive finite power of two";
+        case BFP8_E_SCALE_WINDOW: return "power-of-two scale outside [2^-14, 2^7]";
+        case BFP8_E_LAUNCH: return "HIP kernel launch failed";
+        case BFP8_E_OP: return "unknown op code";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

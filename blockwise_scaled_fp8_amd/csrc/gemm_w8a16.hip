@@ -1,0 +1,210 @@
+// W8A16 GEMMs for gfx950: 16-bit activations, E4M3 weights expanded to
+// 16 bits in registers.
+//
+// There is no MFMA that multiplies a 16-bit operand by an FP8 operand, so
+// with 16-bit activations the weights are widened to the activations' type
+// and the bf16/fp16 MFMA runs ([3090] §2: mixed operand types do not exist
+// in one matrix instruction).  The widening is exact and costs a few integer
+// operations per weight ([3090] §4.1; [SM70] "How it works"); at decode
+// sizes the kernels are bound by streaming the weights from HBM, and the
+// integer work hides under the loads ([3090] §4.3).
+//
+// blk128: weights with one fp32 scale per 128x128 tile.  The weights are
+// decoded to bf16 (value * 2^-120) or fp16 (value * 2^-8); the bias
+// difference is folded into the block scale, so the per-block promotion is
+// one FMA per output: acc += P * (ws * 2^120) or (ws * 2^8) ([3090] §4.1;
+// [ARC] "What this adds").
+//
+// blk32 (UE8M0): weights with one power-of-two scale 2^e per 32x32 tile.
+// Each decoded fp16 weight (value * 2^-8) is multiplied by 2^(e+8) with a
+// packed fp16 multiply; the product value * 2^e is an exact fp16 number for
+// e in [-14, 7] ([SM70] "Exactness"), so the MFMA sees exactly the weights
+// of a load-time fp16 dequantisation and accumulates in fp32 across all K.
+//
+// Both kernels stream the weights like the W8A8 decode kernel: one
+// workgroup per 16 weight rows (and per split of K), 16 tokens on the MFMA
+// column axis; M > 16 is served by more token tiles, each streaming the
+// weights again.
+//
+// Operand mapping: within a 128-K block, lane l (row/column l % 16, slot
+// g = l / 16) holds the 32 K values [32 g, 32 g + 32) of its weight row.
+// MFMA j (j = 0..3) of the block takes bytes [8 j, 8 j + 8) of those, i.e.
+// K indices 32 g + 8 j + (0..7); the activation operand of MFMA j is loaded
+// with the same mapping, so the contraction covers each K index once.
+
+#include "bfp8_device.hpp"
+#include "bfp8_launch.hpp"
+#include "stream_common.hpp"
+
+namespace bfp8 {
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kW8A16Chunk = 4;   // 128-K blocks per wave with loads in flight together
+
+template <bool kXBf16>
+__global__ __launch_bounds__(kStreamThreads) void w8a16_blk128_stream_kernel(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq, const float* __restrict__ ws,
+    void* __restrict__ y, int y_dtype, int64_t M, int64_t N, int64_t K,
+    int64_t n_tiles, int64_t splits, int64_t kb_per_split,
+    float* __restrict__ partials, uint32_t* __restrict__ counters) {
+    __shared__ float red[kStreamWaves * 256];
+    const int64_t nt = blockIdx.x, split = blockIdx.y, mt = blockIdx.z;
+    const int64_t KB = K / 128;
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int r = lane & 15, g = lane >> 4;
+    const int64_t n = nt * 16 + r;
+    const int64_t m = mt * 16 + r;
+    const bool m_ok = m < M;
+    const int64_t kb_begin = split * kb_per_split;
+    const int64_t kb_end = kb_begin + kb_per_split < KB ? kb_begin + kb_per_split : KB;
+
+    const uint8_t* wrow = wq + n * K + g * 32;
+    const uint16_t* xrow = x + (m_ok ? m : 0) * K + g * 32;
+    const float* ws_row = ws + (nt * 16 / 128) * KB;
+    // Exponent-bias difference between E4M3 and the 16-bit type, folded into the scale.
+    const float bias_fold = kXBf16 ? 0x1p120f : 0x1p8f;
+
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int64_t kb0 = kb_begin + wave; kb0 < kb_end; kb0 += kStreamWaves * kW8A16Chunk) {
+        u32x4 wa[kW8A16Chunk][2], xb[kW8A16Chunk][4];
+#pragma unroll
+        for (int c = 0; c < kW8A16Chunk; ++c) {
+            const int64_t kb = kb0 + c * kStreamWaves;
+            if (kb < kb_end) {
+                wa[c][0] = load_nt_16B(wrow + kb * 128);
+                wa[c][1] = load_nt_16B(wrow + kb * 128 + 16);
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < kW8A16Chunk; ++c) {
+            const int64_t kb = kb0 + c * kStreamWaves;
+            if (kb < kb_end) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    xb[c][j] = m_ok ? load_16B(xrow + kb * 128 + 8 * j) : u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < kW8A16Chunk; ++c) {
+            const int64_t kb = kb0 + c * kStreamWaves;
+            if (kb < kb_end) {
+                const uint32_t q[8] = {wa[c][0][0], wa[c][0][1], wa[c][0][2], wa[c][0][3],
+                                       wa[c][1][0], wa[c][1][1], wa[c][1][2], wa[c][1][3]};
+                f32x4 blk = zero;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const u32x4 a = decode8<kXBf16>(q[2 * j], q[2 * j + 1]);
+                    blk = kXBf16 ? mfma_bf16_16x16x32(a, xb[c][j], blk) : mfma_f16_16x16x32(a, xb[c][j], blk);
+                }
+                const float sc = ws_row[kb] * bias_fold;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(blk[i], sc, acc[i]);
+            }
+        }
+    }
+    stream_finish(acc, red, y, y_dtype, M, N, nt, mt, splits, split, n_tiles, partials, counters);
+}
+
+__global__ __launch_bounds__(kStreamThreads) void w8a16_blk32_stream_kernel(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq, const uint8_t* __restrict__ e8m0,
+    void* __restrict__ y, int y_dtype, int64_t M, int64_t N, int64_t K,
+    int64_t n_tiles, int64_t splits, int64_t kb_per_split,
+    float* __restrict__ partials, uint32_t* __restrict__ counters) {
+    __shared__ float red[kStreamWaves * 256];
+    const int64_t nt = blockIdx.x, split = blockIdx.y, mt = blockIdx.z;
+    const int64_t KB = K / 128, K32 = K / 32;
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int r = lane & 15, g = lane >> 4;
+    const int64_t n = nt * 16 + r;
+    const int64_t m = mt * 16 + r;
+    const bool m_ok = m < M;
+    const int64_t kb_begin = split * kb_per_split;
+    const int64_t kb_end = kb_begin + kb_per_split < KB ? kb_begin + kb_per_split : KB;
+
+    const uint8_t* wrow = wq + n * K + g * 32;
+    const uint16_t* xrow = x + (m_ok ? m : 0) * K + g * 32;
+    // This lane's 32 weights of block kb lie in 32x32 tile (n / 32, 4 kb + g).
+    const uint8_t* erow = e8m0 + (n / 32) * K32 + g;
+
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int64_t kb0 = kb_begin + wave; kb0 < kb_end; kb0 += kStreamWaves * kW8A16Chunk) {
+        u32x4 wa[kW8A16Chunk][2], xb[kW8A16Chunk][4];
+        uint32_t ebyte[kW8A16Chunk];
+#pragma unroll
+        for (int c = 0; c < kW8A16Chunk; ++c) {
+            const int64_t kb = kb0 + c * kStreamWaves;
+            if (kb < kb_end) {
+                wa[c][0] = load_nt_16B(wrow + kb * 128);
+                wa[c][1] = load_nt_16B(wrow + kb * 128 + 16);
+                ebyte[c] = erow[kb * 4];
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < kW8A16Chunk; ++c) {
+            const int64_t kb = kb0 + c * kStreamWaves;
+            if (kb < kb_end) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    xb[c][j] = m_ok ? load_16B(xrow + kb * 128 + 8 * j) : u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < kW8A16Chunk; ++c) {
+            const int64_t kb = kb0 + c * kStreamWaves;
+            if (kb < kb_end) {
+                // 2^(E - 127 + 8) as fp16: exponent field (E - 119) + 15 = E - 104, in [9, 30]
+                // for E in [113, 134]; both halves of the packed factor.
+                const uint32_t f = (ebyte[c] - 104u) << 10;
+                const f16x2 factor = __builtin_bit_cast(f16x2, f | (f << 16));
+                const uint32_t q[8] = {wa[c][0][0], wa[c][0][1], wa[c][0][2], wa[c][0][3],
+                                       wa[c][1][0], wa[c][1][1], wa[c][1][2], wa[c][1][3]};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    u32x4 a = decode8<false>(q[2 * j], q[2 * j + 1]);
+#pragma unroll
+                    for (int d = 0; d < 4; ++d)
+                        a[d] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, a[d]) * factor);
+                    acc = mfma_f16_16x16x32(a, xb[c][j], acc);
+                }
+            }
+        }
+    }
+    stream_finish(acc, red, y, y_dtype, M, N, nt, mt, splits, split, n_tiles, partials, counters);
+}
+
+hipError_t launch_w8a16_blk128_stream(const void* x, bool x_bf16, const uint8_t* wq, const float* ws,
+                                      void* y, int y_dtype, int64_t M, int64_t N, int64_t K,
+                                      void* workspace, hipStream_t stream) {
+    const StreamPlan p = plan_stream(M, N, K);
+    uint32_t* counters;
+    float* partials;
+    stream_workspace_parts(p, workspace, counters, partials);
+    const dim3 grid((unsigned)p.n_tiles, (unsigned)p.splits, (unsigned)p.m_tiles);
+    if (x_bf16) {
+        hipLaunchKernelGGL(w8a16_blk128_stream_kernel<true>, grid, dim3(kStreamThreads), 0, stream,
+                           static_cast<const uint16_t*>(x), wq, ws, y, y_dtype, M, N, K,
+                           p.n_tiles, p.splits, p.kb_per_split, partials, counters);
+    } else {
+        hipLaunchKernelGGL(w8a16_blk128_stream_kernel<false>, grid, dim3(kStreamThreads), 0, stream,
+                           static_cast<const uint16_t*>(x), wq, ws, y, y_dtype, M, N, K,
+                           p.n_tiles, p.splits, p.kb_per_split, partials, counters);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_w8a16_blk32_stream(const void* x, const uint8_t* wq, const uint8_t* e8m0,
+                                     void* y, int y_dtype, int64_t M, int64_t N, int64_t K,
+                                     void* workspace, hipStream_t stream) {
+    const StreamPlan p = plan_stream(M, N, K);
+    uint32_t* counters;
+    float* partials;
+    stream_workspace_parts(p, workspace, counters, partials);
+    hipLaunchKernelGGL(w8a16_blk32_stream_kernel, dim3((unsigned)p.n_tiles, (unsigned)p.splits, (unsigned)p.m_tiles),
+                       dim3(kStreamThreads), 0, stream, static_cast<const uint16_t*>(x), wq, e8m0, y, y_dtype,
+                       M, N, K, p.n_tiles, p.splits, p.kb_per_split, partials, counters);
+    return hipGetLastError();
+}
+
+}  // namespace bfp8

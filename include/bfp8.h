@@ -1,0 +1,203 @@
+/*
+ * bfp8.h — C ABI of libbfp8, the blockwise-scaled FP8 GEMM library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Pages cited (by title and section):
+ *   [ADA]  "Blockwise FP8 on Ada GPUs, part 2: my kernel was correct and 4x
+ *          too slow"
+ *   [ARC]  "perf(ArcKernels): blockwise-FP8 GEMM on tensor cores, scale
+ *          promoted per 128-K" (including its "Route-2 handover" comment)
+ *   [SM70] "SM70 FP8 block-32 kernels (PLI Labs)"
+ *   [3090] "FP8 / NVFP4 の weight-only 推論で RTX 3090 が失っているものは無い"
+ *
+ * Conventions shared by every entry point
+ *   - Matrices are row-major.  Weights are W[N, K] with K contiguous and every
+ *     product is Y[M, N] = X[M, K] . W^T ("TN", [ARC] "Route-2 handover"
+ *     item 4; [SM70] "Build and use", weights [N, K] and scales [N/32, K/32]).
+ *   - E4M3 means the OCP "fn" 8-bit format: bias 7, subnormals, no infinity,
+ *     0x7F / 0xFF are NaN, largest magnitude 448 ([ARC] "What this adds";
+ *     [SM70] "Exactness").
+ *   - Device pointers are caller-owned device memory; the library allocates
+ *     nothing and keeps no state between calls.  Every device pointer must
+ *     be 16-byte aligned.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Work is enqueued asynchronously on it; the library never synchronises.
+ *   - Every argument is validated before any HIP call.  A failed check
+ *     returns a nonzero bfp8_status and enqueues nothing.  No entry point
+ *     aborts, throws or prints.  A HIP launch failure returns
+ *     BFP8_E_LAUNCH.
+ *   - Preconditions not checked on the hot path: inputs and scales finite,
+ *     scales >= 0, no E4M3 NaN codes in device operands (the host-side
+ *     bfp8_prepare_blk32_ue8m0 checks its operands), no overlap between
+ *     outputs and inputs.
+ *   - Determinism: every reduction is done in a fixed order (no
+ *     floating-point atomics); two calls on the same inputs give the same bits.
+ */
+#ifndef BFP8_H
+#define BFP8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int bfp8_status;
+
+enum {
+    BFP8_OK = 0,
+    BFP8_E_NULL = 1,            /* a required pointer is NULL */
+    BFP8_E_SHAPE = 2,           /* a size is out of range or not a required multiple */
+    BFP8_E_DTYPE = 3,           /* unknown or unsupported dtype code */
+    BFP8_E_ALIGN = 4,           /* a device pointer is not 16-byte aligned */
+    BFP8_E_WORKSPACE = 5,       /* workspace missing or smaller than bfp8_workspace_bytes() */
+    BFP8_E_NAN_CODE = 6,        /* E4M3 NaN code (0x7F / 0xFF) in a weight */
+    BFP8_E_SCALE_NOT_POW2 = 7,  /* block scale not a positive finite power of two */
+    BFP8_E_SCALE_WINDOW = 8,    /* power-of-two scale 2^e with e outside [-14, 7] */
+    BFP8_E_LAUNCH = 9,          /* the HIP runtime refused a launch */
+    BFP8_E_OP = 10              /* unknown op code */
+};
+
+/* dtype codes of 16-bit/32-bit operands */
+enum { BFP8_BF16 = 0, BFP8_F16 = 1, BFP8_F32 = 2 };
+
+/* op codes for bfp8_workspace_bytes / bfp8_get_limits */
+enum {
+    BFP8_OP_QUANT_ACT_1X128 = 0,
+    BFP8_OP_QUANT_WEIGHT_128X128 = 1,
+    BFP8_OP_GEMM_W8A8_BLK128 = 2,
+    BFP8_OP_GEMM_W8A16_BLK128 = 3,
+    BFP8_OP_GEMM_W8A16_BLK32_UE8M0 = 4
+};
+
+/*
+ * 1x128 activation quantisation ([ADA] "The starting point": one scale per
+ * token per 128 values along K; [ARC] "Route-2 handover" item 2: scales of
+ * shape [M, ceil(K/128)]; item 3: one wave per group with a register
+ * reduction and vector loads instead of 1024-thread blocks and serialised
+ * atomics).
+ *   x   [M, K] bf16 or fp16 (x_dtype BFP8_BF16 / BFP8_F16), device.
+ *   xq  [M, K] E4M3 codes, device, written.
+ *   xs  [M, ceil(K/128)] fp32, row-major, device, written.
+ * Per row m and group g (columns [128g, min(K, 128g+128))):
+ *   amax = max |x|;  s = fl32(amax / 448);  q = RNE-saturating E4M3 of
+ *   fl32(x / s) (IEEE fp32 divisions); amax == 0 gives s = 0 and codes 0x00.
+ * The codes and scales are bit-exact functions of x.
+ * Requires M >= 1, K >= 8, K % 8 == 0 (the last group may be ragged).
+ */
+bfp8_status bfp8_quantize_act_1x128(const void* x, int x_dtype, int64_t M, int64_t K,
+                                    uint8_t* xq, float* xs, void* stream);
+
+/*
+ * 128x128 weight quantisation, the load-time preparation of W8A8/W8A16
+ * blk128 weights ([ADA] "The starting point": 128x128 weight blocks;
+ * [ARC] "What this adds": the [N/128, K/128] block scale).
+ *   w   [N, K] bf16 or fp16, device.
+ *   wq  [N, K] E4M3 codes, device, written.
+ *   ws  [ceil(N/128), ceil(K/128)] fp32, row-major, device, written.
+ * Per tile: the same amax / scale / code rule as the activation quantiser.
+ * Requires N >= 1, K >= 8, K % 8 == 0 (edge tiles may be ragged).
+ */
+bfp8_status bfp8_quantize_weight_128x128(const void* w, int w_dtype, int64_t N, int64_t K,
+                                         uint8_t* wq, float* ws, void* stream);
+
+/*
+ * W8A8 blockwise GEMM ([ADA] "The starting point" and "The fix"; [ARC]
+ * "What this adds"):
+ *   for each 128-wide K block kb:
+ *     P[m, n]  = sum over k in kb of E4M3(xq[m, k]) * E4M3(wq[n, k])   (FP8 MFMA, fp32)
+ *     Y[m, n] += P[m, n] * xs[m, kb] * ws[n / 128, kb]                 (once per block)
+ *   xq  [M, K] E4M3, xs [M, K/128] fp32 (from bfp8_quantize_act_1x128).
+ *   wq  [N, K] E4M3, ws [ceil(N/128), K/128] fp32.
+ *   y   [M, N], y_dtype BFP8_BF16 / BFP8_F16 / BFP8_F32 (round to nearest even
+ *       from the fp32 accumulator).
+ *   workspace: device memory of at least bfp8_workspace_bytes(
+ *       BFP8_OP_GEMM_W8A8_BLK128, M, N, K) bytes (may be NULL when that is 0).
+ *       It must be zero-filled before its first use; every call leaves it
+ *       ready for the next.  Calls that overlap in time must not share one.
+ * Requires M >= 1, N >= 16, N % 16 == 0, K >= 128, K % 128 == 0.
+ */
+bfp8_status bfp8_gemm_w8a8_blk128(const uint8_t* xq, const float* xs,
+                                  const uint8_t* wq, const float* ws,
+                                  void* y, int y_dtype, int64_t M, int64_t N, int64_t K,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * W8A16 blockwise GEMM: 16-bit activations, E4M3 weights expanded to 16 bits
+ * in registers by integer bit operations, the exponent-bias difference
+ * (2^8 for fp16, 2^120 for bf16) folded into the block scale ([3090] §4.1;
+ * [ARC] "What this adds": the conversion is exact and the scale is applied
+ * once per 128 K values).
+ *   Y[m, n] = sum_kb ws[n / 128, kb] * sum over k in kb of x[m, k] * E4M3(wq[n, k])
+ *   x   [M, K] bf16 or fp16, wq [N, K] E4M3, ws [ceil(N/128), K/128] fp32.
+ *   y   [M, N] in y_dtype (BF16 / F16 / F32); workspace as for W8A8.
+ * Requires M >= 1, N % 16 == 0, K % 128 == 0.
+ */
+bfp8_status bfp8_gemm_w8a16_blk128(const void* x, int x_dtype,
+                                   const uint8_t* wq, const float* ws,
+                                   void* y, int y_dtype, int64_t M, int64_t N, int64_t K,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * W8A16 GEMM with 32x32 weight tiles and power-of-two (UE8M0) scales
+ * ([SM70] "How it works", "Exactness"): each weight is expanded to fp16 by
+ * integer bit operations and multiplied exactly by its tile's 2^e (exact in
+ * fp16 for e in [-14, 7]), then contracted with fp32 accumulation.
+ *   Y[m, n] = sum_k x[m, k] * (E4M3(wq[n, k]) * 2^(e8m0[n/32, k/32] - 127))
+ *   x     [M, K] fp16 (x_dtype BFP8_F16).
+ *   wq    [N, K] E4M3.
+ *   e8m0  [N/32, K/32] bytes E, produced by bfp8_prepare_blk32_ue8m0
+ *         (trusted: E must lie in [113, 134]).
+ *   y     [M, N] in y_dtype (F16 / BF16 / F32); workspace as for W8A8.
+ * Requires M >= 1, N % 32 == 0, K % 128 == 0.
+ */
+bfp8_status bfp8_gemm_w8a16_blk32_ue8m0(const void* x, int x_dtype,
+                                        const uint8_t* wq, const uint8_t* e8m0,
+                                        void* y, int y_dtype, int64_t M, int64_t N, int64_t K,
+                                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Load-time validation and packing of 32x32 power-of-two scales ([SM70]
+ * "Exactness": the packer refuses, loudly, scales outside [2^-14, 2^7],
+ * scales that are not powers of two, and E4M3 NaN codes).  HOST memory,
+ * synchronous, touches no GPU.
+ *   wq_host     [N, K] E4M3 codes.
+ *   scale_host  [N/32, K/32] fp32 scales.
+ *   e8m0_host   [N/32, K/32] bytes, written only on success: E = e + 127.
+ *   bad_index   written always: -1 on success, else the flat row-major index
+ *               of the first offending element (weights are checked first,
+ *               then scales).
+ * Returns BFP8_E_NAN_CODE, BFP8_E_SCALE_NOT_POW2 (zero, negative, infinite,
+ * NaN or non-power-of-two scale) or BFP8_E_SCALE_WINDOW (2^e, e outside
+ * [-14, 7]) on refusal.  Requires N, K >= 32 and multiples of 32.
+ */
+bfp8_status bfp8_prepare_blk32_ue8m0(const uint8_t* wq_host, const float* scale_host,
+                                     int64_t N, int64_t K, uint8_t* e8m0_host,
+                                     int64_t* bad_index);
+
+/* Bytes of workspace the op needs for this shape (0 when none). */
+size_t bfp8_workspace_bytes(int op, int64_t M, int64_t N, int64_t K);
+
+/*
+ * Shape rules compiled into the kernels, read from the library rather than
+ * duplicated by callers ([ARC] "Correctness guards": eligibility read from
+ * the kernel so host checks cannot drift from the compiled tiling).
+ *   k_multiple    K must be a multiple of this.
+ *   n_multiple    N must be a multiple of this.
+ *   align_bytes   required alignment of every device pointer.
+ *   m_stream_max  largest M served by the weight-streaming decode kernel
+ *                 (larger M goes to the tiled MFMA kernel where one exists).
+ * Any output pointer may be NULL.
+ */
+bfp8_status bfp8_get_limits(int op, int64_t* k_multiple, int64_t* n_multiple,
+                            int64_t* align_bytes, int64_t* m_stream_max);
+
+/* Static, human-readable text for a status code. */
+const char* bfp8_status_string(bfp8_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BFP8_H */

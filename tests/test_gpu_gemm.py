@@ -1,0 +1,236 @@
+"""GPU parity of the three block-scaled GEMMs against the float64 oracle on the
+same seeded inputs.
+
+The binding bar is on the fp32-output mode (max |err| <= 1e-2 * rms(Y0) and
+relative Frobenius error <= 4e-3).  16-bit outputs must meet the per-element
+bar widened by half an output ulp and equal round-to-nearest-even of the
+kernel's own fp32 result bit for bit.  One-hot cases are exact."""
+
+import numpy as np
+import pytest
+import torch
+
+import blockwise_scaled_fp8_amd as bfp8
+from blockwise_scaled_fp8_amd import inputs
+import oracle
+from tests.gpu_helpers import (FINITE_CODES, say, dev, f32, workspace, run_w8a8, run_w8a16, run_blk32,
+                               assert_fp32_bar, assert_16bit_bar)
+
+pytestmark = pytest.mark.gpu
+
+
+def _w8a8_inputs(M, N, K, wid, outliers=False):
+    x = inputs.activations(M, K, workload=wid, stream=0, outliers=outliers)
+    w = inputs.weights_bf16(N, K, workload=wid, stream=1)
+    xq, xs = oracle.quantize_act_1x128(f32(x))
+    wq, ws = oracle.quantize_weight_128x128(f32(w))
+    return xq, xs, wq, ws
+
+
+def _w8a8_check(M, N, K, wid, outliers=False, what=""):
+    say("w8a8", what, f"M={M} N={N} K={K}")
+    xq, xs, wq, ws = _w8a8_inputs(M, N, K, wid, outliers)
+    y0 = oracle.gemm_w8a8_blk128(xq, xs, wq, ws)
+    d = [dev(a) for a in (xq, xs, wq, ws)]
+    y32 = run_w8a8(*d, torch.float32)
+    assert_fp32_bar(y32, y0, f"w8a8 {what} M={M} N={N} K={K}")
+    y16 = run_w8a8(*d, torch.bfloat16)
+    assert_16bit_bar(y16, y32, y0, "bf16", f"w8a8 {what}")
+    yh = run_w8a8(*d, torch.float16)
+    assert_16bit_bar(yh, y32, y0, "f16", f"w8a8 {what}")
+    return y32
+
+
+def test_w8a8_workload0(gpu_lib):
+    _w8a8_check(4, 512, 512, 0, what="workload 0")
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 5, 8, 15, 16, 17, 31, 64, 129, 200])
+def test_w8a8_across_the_stream_tile_threshold(gpu_lib, M):
+    _w8a8_check(M, 384, 640, 300 + M, what="threshold")
+
+
+@pytest.mark.parametrize("N", [16, 48, 144, 272])
+@pytest.mark.parametrize("M", [4, 40])
+def test_w8a8_weight_scale_rows_straddle(gpu_lib, M, N):
+    """N not a multiple of 128: tiles straddle or subdivide a 128-row weight-scale block."""
+    _w8a8_check(M, N, 256, 400 + N + M, what="straddle")
+
+
+@pytest.mark.parametrize("M", [1, 4, 16])
+def test_w8a8_split_k_narrow_projection(gpu_lib, M):
+    """k/v-shaped N=1024, K=4096 takes the split-K plan; run twice (counters re-arm)."""
+    assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, M, 1024, 4096) > 0
+    xq, xs, wq, ws = _w8a8_inputs(M, 1024, 4096, 500 + M)
+    y0 = oracle.gemm_w8a8_blk128(xq, xs, wq, ws)
+    d = [dev(a) for a in (xq, xs, wq, ws)]
+    wsb = workspace(bfp8.OP_GEMM_W8A8_BLK128, M, 1024, 4096)
+    say("w8a8 split-K", M)
+    y1 = run_w8a8(*d, torch.float32, wsb)
+    y2 = run_w8a8(*d, torch.float32, wsb)
+    assert_fp32_bar(y1, y0, "split-K")
+    assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
+
+
+def test_w8a8_decode_oproj_full(gpu_lib):
+    """Decode o_proj M=1, N=K=4096: full oracle."""
+    _w8a8_check(1, 4096, 4096, 1, what="o_proj decode")
+
+
+def test_w8a8_prefill_oproj_sampled(gpu_lib):
+    """Prefill o_proj M=N=K=4096 with 1% outlier channels: full GPU run, 64 rows checked."""
+    say("w8a8 prefill full size")
+    x = inputs.workload(2)["x"]
+    w = inputs.workload(2)["w"]
+    xq_d, xs_d = bfp8.quantize_act(x.cuda())
+    wq_d, ws_d = bfp8.quantize_weight(w.cuda())
+    y32 = run_w8a8(xq_d, xs_d, wq_d, ws_d, torch.float32)
+    y16 = run_w8a8(xq_d, xs_d, wq_d, ws_d, torch.bfloat16)
+    rows = np.random.default_rng(3).choice(4096, 64, replace=False)
+    xq, xs = oracle.quantize_act_1x128(f32(x[rows]))
+    wq, ws = oracle.quantize_weight_128x128(f32(w))
+    # the GPU quantisers are bit-exact (checked elsewhere); confirm on the sampled rows
+    np.testing.assert_array_equal(xq_d.cpu().numpy()[rows], xq)
+    np.testing.assert_array_equal(wq_d.cpu().numpy(), wq)
+    y0 = oracle.gemm_w8a8_blk128(xq, xs, wq, ws)
+    assert_fp32_bar(y32[rows], y0, "prefill sampled rows")
+    assert_16bit_bar(y16[rows], y32[rows], y0, "bf16", "prefill sampled rows")
+
+
+@pytest.mark.parametrize("M", [3, 48])
+def test_w8a8_one_hot_all_codes_exact(gpu_lib, M):
+    """xq one-hot 1.0 at column k, unit scales: Y[:, n] = E4M3(wq[n, k]) exactly,
+    for every finite code (stream and tile kernels)."""
+    N, K = 256, 256
+    wq = np.zeros((N, K), np.uint8)
+    wq[:254, :] = FINITE_CODES[:, None]
+    for k in (0, 77, 128, 255):
+        say("w8a8 one-hot", M, k)
+        xq = np.zeros((M, K), np.uint8)
+        xq[:, k] = 0x38
+        y = run_w8a8(dev(xq), dev(np.ones((M, 2), np.float32)), dev(wq), dev(np.ones((2, 2), np.float32)),
+                     torch.float32)
+        expect = np.broadcast_to(oracle.e4m3_decode(wq[:, k]), (M, N))
+        np.testing.assert_array_equal(y.cpu().numpy(), expect)
+
+
+def test_w8a8_deterministic(gpu_lib):
+    xq, xs, wq, ws = _w8a8_inputs(64, 512, 1024, 11)
+    d = [dev(a) for a in (xq, xs, wq, ws)]
+    a = run_w8a8(*d, torch.float32)
+    b = run_w8a8(*d, torch.float32)
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+# ------------------------------------------------------------ W8A16 blk128 ----
+
+@pytest.mark.parametrize("xdtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("M", [1, 2, 4, 8, 16, 33])
+def test_w8a16_blk128(gpu_lib, M, xdtype):
+    N, K = 512, 1024
+    say("w8a16 blk128", M, xdtype)
+    x = inputs.activations(M, K, workload=600 + M, dtype=xdtype)
+    wq, ws = oracle.quantize_weight_128x128(f32(inputs.weights_bf16(N, K, workload=600 + M)))
+    y0 = oracle.gemm_w8a16_blk128(f32(x), wq, ws)
+    xd, wqd, wsd = x.cuda(), dev(wq), dev(ws)
+    y32 = run_w8a16(xd, wqd, wsd, torch.float32)
+    assert_fp32_bar(y32, y0, f"w8a16 M={M}")
+    y16 = run_w8a16(xd, wqd, wsd, xdtype)
+    assert_16bit_bar(y16, y32, y0, "bf16" if xdtype == torch.bfloat16 else "f16", f"w8a16 M={M}")
+
+
+@pytest.mark.parametrize("xdtype", [torch.bfloat16, torch.float16])
+def test_w8a16_blk128_one_hot_all_codes_exact(gpu_lib, xdtype):
+    """x one-hot 1.0: Y[:, n] = E4M3(wq[n, k]) * ws exactly, subnormal codes included."""
+    N, K, M = 256, 256, 4
+    wq = np.zeros((N, K), np.uint8)
+    wq[:254, :] = FINITE_CODES[:, None]
+    ws = np.array([[0.5, 2.0], [0.25, 4.0]], np.float32)
+    for k in (0, 100, 129, 255):
+        say("w8a16 one-hot", xdtype, k)
+        x = torch.zeros((M, K), dtype=xdtype)
+        x[:, k] = 1.0
+        y = run_w8a16(x.cuda(), dev(wq), dev(ws), torch.float32)
+        expect = oracle.e4m3_decode(wq[:, k]) * ws[np.arange(N) // 128, k // 128]
+        np.testing.assert_array_equal(y.cpu().numpy(), np.broadcast_to(expect, (M, N)))
+
+
+def test_w8a16_blk128_decode_oproj_full(gpu_lib):
+    say("w8a16 o_proj decode")
+    x = inputs.workload(1)["x"]
+    wq, ws = oracle.quantize_weight_128x128(f32(inputs.workload(1)["w"]))
+    y0 = oracle.gemm_w8a16_blk128(f32(x), wq, ws)
+    y32 = run_w8a16(x.cuda(), dev(wq), dev(ws), torch.float32)
+    assert_fp32_bar(y32, y0, "w8a16 o_proj")
+    y16 = run_w8a16(x.cuda(), dev(wq), dev(ws), torch.bfloat16)
+    assert_16bit_bar(y16, y32, y0, "bf16", "w8a16 o_proj")
+
+
+# ------------------------------------------------------------ blk32 UE8M0 ----
+
+def _blk32_inputs(M, N, K, wid, lo=-14, hi=7):
+    x = inputs.activations(M, K, workload=wid, stream=0, dtype=torch.float16)
+    wq = inputs.block32_codes(N, K, workload=wid).numpy()
+    s = inputs.block32_scales(N, K, workload=wid, lo=lo, hi=hi).numpy()
+    st, e8, bad = bfp8.bfp8_prepare_blk32_ue8m0(torch.from_numpy(wq), torch.from_numpy(s))
+    assert st == 0, (st, bad)
+    ref_st, ref_e8, _ = oracle.prepare_blk32_ue8m0(wq, s)
+    np.testing.assert_array_equal(e8.numpy(), ref_e8)
+    return x, wq, e8.numpy()
+
+
+@pytest.mark.parametrize("M", [1, 2, 4, 8, 16])
+def test_blk32_block32_workload_shape(gpu_lib, M):
+    """N=4096, K=7168 block-32 weights, e uniform on [-14, 7]."""
+    say("blk32", M)
+    x, wq, e8 = _blk32_inputs(M, 4096, 7168, 3)
+    y0 = oracle.gemm_w8a16_blk32_ue8m0(f32(x), wq, e8)
+    xd, wqd, e8d = x.cuda(), dev(wq), dev(e8)
+    y32 = run_blk32(xd, wqd, e8d, torch.float32)
+    assert_fp32_bar(y32, y0, f"blk32 M={M}")
+    yh = run_blk32(xd, wqd, e8d, torch.float16)
+    assert_16bit_bar(yh, y32, y0, "f16", f"blk32 M={M}")
+    ok, e = oracle.check_gemm_fp32(f32(yh), y0)     # fp16 half-ulp is far below the bar here
+    assert ok, e
+
+
+@pytest.mark.parametrize("lo,hi", [(-14, -14), (7, 7)])
+def test_blk32_window_ends(gpu_lib, lo, hi):
+    say("blk32 window end", lo)
+    x, wq, e8 = _blk32_inputs(8, 512, 1024, 30 + lo, lo=lo, hi=hi)
+    y0 = oracle.gemm_w8a16_blk32_ue8m0(f32(x), wq, e8)
+    y32 = run_blk32(x.cuda(), dev(wq), dev(e8), torch.float32)
+    assert_fp32_bar(y32, y0, f"blk32 e={lo}")
+
+
+@pytest.mark.parametrize("out", [torch.float32, torch.float16])
+def test_blk32_one_hot_all_codes_all_exponents_exact(gpu_lib, out):
+    """Every finite code times every window exponent is produced exactly
+    (fp16 subnormals at e = -14 included)."""
+    exps = np.arange(-14, 8)
+    N, K, M = 32 * exps.size, 256, 16
+    wq = np.zeros((N, K), np.uint8)
+    wq[:, :254] = FINITE_CODES[None, :]
+    e8 = np.repeat((exps + 127).astype(np.uint8)[:, None], K // 32, axis=1)
+    d = oracle.e4m3_decode(FINITE_CODES)
+    for base in range(0, 256, M):
+        say("blk32 one-hot", out, base)
+        x = torch.zeros((M, K), dtype=torch.float16)
+        ks = np.arange(base, base + M)
+        x[np.arange(M), ks] = 1.0
+        y = run_blk32(x.cuda(), dev(wq), dev(e8), out).float().cpu().numpy()
+        for row, k in enumerate(ks):
+            expect = (d[k] if k < 254 else 0.0) * np.exp2(exps.astype(np.float64))
+            np.testing.assert_array_equal(y[row].reshape(exps.size, 32), np.repeat(expect[:, None], 32, axis=1))
+
+
+def test_blk32_split_k_and_determinism(gpu_lib):
+    M, N, K = 4, 1024, 7168
+    x, wq, e8 = _blk32_inputs(M, N, K, 31)
+    y0 = oracle.gemm_w8a16_blk32_ue8m0(f32(x), wq, e8)
+    wsb = workspace(bfp8.OP_GEMM_W8A16_BLK32_UE8M0, M, N, K)
+    say("blk32 split-K")
+    a = run_blk32(x.cuda(), dev(wq), dev(e8), torch.float32, wsb)
+    b = run_blk32(x.cuda(), dev(wq), dev(e8), torch.float32, wsb)
+    assert_fp32_bar(a, y0, "blk32 split-K")
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))

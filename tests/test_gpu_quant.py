@@ -1,0 +1,117 @@
+"""GPU parity of the block quantisers: codes and scales bit-exact against the
+oracle on the same seeded inputs."""
+
+import numpy as np
+import pytest
+import torch
+
+import blockwise_scaled_fp8_amd as bfp8
+from blockwise_scaled_fp8_amd import inputs
+import oracle
+from tests.gpu_helpers import say, f32
+
+pytestmark = pytest.mark.gpu
+
+
+def _act_case(x, what):
+    say("quant_act", what, tuple(x.shape), x.dtype)
+    xq, xs = bfp8.quantize_act(x.cuda())
+    torch.cuda.synchronize()
+    ref_q, ref_s = oracle.quantize_act_1x128(f32(x))
+    np.testing.assert_array_equal(xs.cpu().numpy().view(np.uint32), ref_s.view(np.uint32), err_msg=what)
+    np.testing.assert_array_equal(xq.cpu().numpy(), ref_q, err_msg=what)
+
+
+def test_quant_act_workload0(gpu_lib):
+    _act_case(inputs.workload(0)["x"], "workload 0")
+
+
+@pytest.mark.parametrize("M,K", [(1, 4096), (3, 200), (5, 1000), (7, 8), (17, 136), (64, 384)])
+def test_quant_act_shapes_and_ragged_groups(gpu_lib, M, K):
+    _act_case(inputs.activations(M, K, workload=100 + M, stream=K), f"ragged M={M} K={K}")
+
+
+def test_quant_act_fp16_input(gpu_lib):
+    _act_case(inputs.activations(6, 640, workload=7, stream=0, dtype=torch.float16), "fp16")
+
+
+def test_quant_act_special_groups(gpu_lib):
+    x = inputs.activations(4, 512, workload=8, stream=0).float()
+    x[0, :128] = 0.0                       # zero group
+    x[0, 128:256] = -0.0                   # negative-zero group
+    x[1, :128] *= 1e-30                    # tiny values (subnormal-range quotients stay exact)
+    x[2, 5] = 0.0
+    x[2, 6] = -0.0                         # signed zeros inside a live group
+    x[3, :] = torch.where(torch.arange(512) % 2 == 0, x[3, :], -x[3, :])
+    _act_case(x.to(torch.bfloat16), "special groups")
+
+
+def test_quant_act_encoder_exhaustive_over_bf16(gpu_lib):
+    """Every bf16 value in [-448, 448]: each group holds 448 (so s = 1 exactly
+    and x / s = x) plus 127 values to encode."""
+    b = torch.arange(0, 0x8000, dtype=torch.int32).to(torch.int16).view(torch.bfloat16)
+    v = b.float()
+    v = v[(v <= 448.0) & torch.isfinite(v)]
+    vals = torch.cat([v, -v])
+    per = 127
+    rows = (vals.numel() + per - 1) // per
+    pad = rows * per - vals.numel()
+    vals = torch.cat([vals, torch.zeros(pad)]).reshape(rows, per)
+    grid = torch.cat([torch.full((rows, 1), 448.0), vals], dim=1)     # [rows, 128]
+    _act_case(grid.to(torch.bfloat16), f"exhaustive bf16 ({rows} groups)")
+
+
+def test_quant_act_prefill_outliers_sampled(gpu_lib):
+    """Full 4096x4096 run with 1% outlier channels; 64 sampled rows checked."""
+    x = inputs.workload(2)["x"]
+    say("quant_act", "workload 2 full, sampled rows")
+    xq, xs = bfp8.quantize_act(x.cuda())
+    torch.cuda.synchronize()
+    rows = np.random.default_rng(2).choice(4096, 64, replace=False)
+    ref_q, ref_s = oracle.quantize_act_1x128(f32(x[rows]))
+    np.testing.assert_array_equal(xs.cpu().numpy()[rows].view(np.uint32), ref_s.view(np.uint32))
+    np.testing.assert_array_equal(xq.cpu().numpy()[rows], ref_q)
+
+
+def _weight_case(w, what):
+    say("quant_weight", what, tuple(w.shape), w.dtype)
+    wq, ws = bfp8.quantize_weight(w.cuda())
+    torch.cuda.synchronize()
+    ref_q, ref_s = oracle.quantize_weight_128x128(f32(w))
+    np.testing.assert_array_equal(ws.cpu().numpy().view(np.uint32), ref_s.view(np.uint32), err_msg=what)
+    np.testing.assert_array_equal(wq.cpu().numpy(), ref_q, err_msg=what)
+
+
+def test_quant_weight_workload0(gpu_lib):
+    _weight_case(inputs.workload(0)["w"], "workload 0")
+
+
+@pytest.mark.parametrize("N,K", [(200, 264), (16, 128), (384, 1000), (130, 8)])
+def test_quant_weight_ragged(gpu_lib, N, K):
+    _weight_case(inputs.weights_bf16(N, K, workload=200 + N, stream=K), f"ragged N={N} K={K}")
+
+
+def test_quant_weight_fp16_and_zero_tile(gpu_lib):
+    w = inputs.weights_bf16(256, 256, workload=9).float()
+    w[:128, 128:] = 0.0
+    _weight_case(w.to(torch.float16), "fp16 with a zero tile")
+
+
+def test_quant_weight_full_oproj_sampled(gpu_lib):
+    w = inputs.workload(1)["w"]
+    say("quant_weight", "4096x4096, sampled tiles")
+    wq, ws = bfp8.quantize_weight(w.cuda())
+    torch.cuda.synchronize()
+    for nb, kb in [(0, 0), (7, 31), (31, 0), (13, 17)]:
+        blk = w[128 * nb:128 * nb + 128, 128 * kb:128 * kb + 128]
+        ref_q, ref_s = oracle.quantize_weight_128x128(f32(blk))
+        assert ws.cpu().numpy()[nb, kb].view(np.uint32) == ref_s[0, 0].view(np.uint32)
+        np.testing.assert_array_equal(wq.cpu().numpy()[128 * nb:128 * nb + 128, 128 * kb:128 * kb + 128], ref_q)
+
+
+def test_quant_deterministic(gpu_lib):
+    x = inputs.activations(33, 4096, workload=10).cuda()
+    a = bfp8.quantize_act(x)
+    b = bfp8.quantize_act(x)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1].view(torch.int32), b[1].view(torch.int32))
