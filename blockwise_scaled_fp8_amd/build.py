@@ -22,14 +22,17 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libbfp8.so")
 
-SOURCES = ["api.hip", "quant.hip", "gemm_w8a8.hip", "gemm_w8a16.hip"]
+SOURCES = ["api.hip", "quant.hip", "gemm_w8a8.hip", "gemm_w8a8_tile.hip", "gemm_w8a16.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed-fp32 VALU forms are kept out of the generated code on purpose.
+# MFMA results go to ArchVGPRs (not AGPRs) so the fp32 FMAs that apply the
+# per-block scales read them directly, without v_accvgpr_read copies.
 COMMON_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-I" + INCLUDE, "-I" + CSRC,
     "-Wall", "-Wno-unused-parameter", "-Wno-unused-command-line-argument",
 ]

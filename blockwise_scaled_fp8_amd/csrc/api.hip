@@ -86,6 +86,8 @@ bfp8_status bfp8_gemm_w8a8_blk128(const uint8_t* xq, const float* xs, const uint
     if (!aligned(xs)) return BFP8_E_ALIGN;
     if (M <= kStreamMaxM)
         return launched(launch_w8a8_stream(xq, xs, wq, ws, y, y_dtype, M, N, K, workspace, as_stream(stream)));
+    // The tiled kernel addresses a 256-row slab of W through a 32-bit buffer range.
+    if (K > kTileMaxK) return BFP8_E_SHAPE;
     return launched(launch_w8a8_tile(xq, xs, wq, ws, y, y_dtype, M, N, K, as_stream(stream)));
 }
 

@@ -12,6 +12,9 @@ namespace bfp8 {
 constexpr int64_t kStreamMaxM = 16;
 // Rows of W covered by one streaming workgroup (one MFMA row tile).
 constexpr int64_t kStreamRows = 16;
+// Largest K of the tiled W8A8 kernel (256 rows x K bytes must fit a 32-bit
+// buffer range, with room for the scalar offsets).
+constexpr int64_t kTileMaxK = (int64_t)1 << 23;
 
 // Split-K plan of a streaming kernel: `splits` workgroups share one
 // (16-row, 16-token) output tile, each covering `kb_per_split` 128-K blocks.

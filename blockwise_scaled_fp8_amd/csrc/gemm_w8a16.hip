@@ -40,6 +40,12 @@ namespace bfp8 {
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
+// Two fp16 values (one dword) times a packed fp16 factor: one v_pk_mul_f16.
+__device__ __forceinline__ uint32_t scale_f16x2(uint32_t v, f16x2 factor) {
+    const f16x2 p = __builtin_bit_cast(f16x2, v) * factor;
+    return __builtin_bit_cast(uint32_t, p);
+}
+
 constexpr int kW8A16Chunk = 4;   // 128-K blocks per wave with loads in flight together
 
 template <bool kXBf16>
@@ -162,10 +168,11 @@ __global__ __launch_bounds__(kStreamThreads) void w8a16_blk32_stream_kernel(
                                        wa[c][1][0], wa[c][1][1], wa[c][1][2], wa[c][1][3]};
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    u32x4 a = decode8<false>(q[2 * j], q[2 * j + 1]);
-#pragma unroll
-                    for (int d = 0; d < 4; ++d)
-                        a[d] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, a[d]) * factor);
+                    uint32_t d0, d1, d2, d3;
+                    e4m3x4_to_f16x4(q[2 * j], d0, d1);
+                    e4m3x4_to_f16x4(q[2 * j + 1], d2, d3);
+                    const u32x4 a = {scale_f16x2(d0, factor), scale_f16x2(d1, factor),
+                                     scale_f16x2(d2, factor), scale_f16x2(d3, factor)};
                     acc = mfma_f16_16x16x32(a, xb[c][j], acc);
                 }
             }

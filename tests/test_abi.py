@@ -109,6 +109,7 @@ def _w8a8(M=4, N=512, K=512, y_dtype=0, xq=A, ws_ptr=C, y=Y, workspace=None, wby
     (dict(y_dtype=7), 3),
     (dict(y=MISALIGNED), 4),
     (dict(M=1, N=1024, K=4096), 5),                   # split-K plan needs a workspace
+    (dict(M=64, N=256, K=(1 << 23) + 128), 2),        # tiled kernel's K limit
 ])
 def test_w8a8_validation(lib, kw, expect):
     assert lib.bfp8_gemm_w8a8_blk128(*_w8a8(**kw)) == expect
