@@ -1,12 +1,13 @@
 // W8A8 blockwise GEMM, tiled kernel for M > 16 (prefill) on gfx950.
 //
-// Workgroup tile: 256 weight rows (n) x 128 tokens (m), K staged one
+// Workgroup tile: 256 weight rows (n) x 256 tokens (m), K staged one
 // 128-wide scale block at a time ([ARC] "What this adds": the K tile is the
-// scale block, so each stage has one scale per row block and token).  Four
-// waves, one per SIMD, each owning 128 n x 64 m = 8 x 4 MFMA tiles of 16x16.
-// With one wave per SIMD each wave has the full 512-register file, which
-// holds the 128 fp32 accumulators, the operand fragments and the MFMA
-// block temporaries without spilling ([ADA] "Where the registers went").
+// scale block, so each stage has one scale per row block and token).  Eight
+// waves, two per SIMD, each owning 128 n x 64 m = 8 x 4 MFMA tiles of 16x16;
+// two waves per SIMD let one wave's promotion FMAs run in the shadow of the
+// other wave's MFMAs.  Each wave's fp32 accumulators, operand fragments
+// and block temporaries fit its 256 registers without spilling ([ADA] "Where
+// the registers went").
 //
 // Per 128-K block and 16x16 tile: one FP8 MFMA 16x16x128 with a zero
 // accumulator gives the block partial P, and one fp32 FMA per output applies
@@ -17,13 +18,13 @@
 //
 // Data movement: global -> LDS with direct-to-LDS 16-byte buffer loads
 // (buffer_load_dwordx4 ... lds; the lane at LDS granule p fetches whichever
-// global 16 bytes belong there), two LDS stages of 48 KB, so block kb+1 is
-// in flight while block kb is multiplied.  LDS rows are 128 bytes (eight
-// 16-byte chunks); chunk c of row r is stored at chunk position c ^ (r & 7),
-// which makes the MFMA fragment reads (16 rows, same chunk) conflict-free.
-// Fragment K order: MFMA K slot g (lanes 16g..16g+15) takes chunks g and
-// g + 4 of the row, the same for both operands, so the contraction is over
-// the same 128 K values.
+// global 16 bytes belong there), two LDS stages of 65 KB, so block kb+1 is in
+// flight while block kb is multiplied; one barrier per block.  LDS rows are
+// 128 bytes (eight 16-byte chunks); chunk c of row r is stored at chunk
+// position c ^ (r & 7), which makes the MFMA fragment reads (16 rows, same
+// chunk) conflict-free.  Fragment K order: MFMA K slot g (lanes 16g..16g+15)
+// takes chunks g and g + 4 of the row, the same for both operands, so the
+// contraction is over the same 128 K values.
 
 #include "bfp8_device.hpp"
 #include "bfp8_launch.hpp"
@@ -33,37 +34,48 @@ namespace bfp8 {
 namespace {
 
 constexpr int kBN = 256;                  // weight rows per workgroup
-constexpr int kBM = 128;                  // tokens per workgroup
-constexpr int kThreads = 256;             // 4 waves: 2 (n) x 2 (m)
-constexpr int kWaveN = 128, kWaveM = 64;  // per-wave tile
+constexpr int kBM = 256;                  // tokens per workgroup
+constexpr int kWavesN = 2, kWavesM = 4;   // eight waves, two per SIMD
+constexpr int kWaves = kWavesN * kWavesM;
+constexpr int kThreads = kWaves * kWave;
+constexpr int kWaveN = kBN / kWavesN, kWaveM = kBM / kWavesM;   // per-wave tile
 constexpr int kTi = kWaveN / 16, kTj = kWaveM / 16;
 constexpr int kRowBytes = 128;            // one 128-K block of one row
-constexpr int kStageA = kBN * kRowBytes;  // 32 KB
-constexpr int kStageB = kBM * kRowBytes;  // 16 KB
-constexpr int kLoadsPerWave = (kBN + kBM) * kRowBytes / (kThreads * 16);   // 12
+constexpr int kStageA = kBN * kRowBytes;
+constexpr int kStageB = kBM * kRowBytes;
+constexpr int kRowsPerLoad = kWave * 16 / kRowBytes;                        // 8 rows per load instruction
+constexpr int kLoadsPerWave = (kBN + kBM) / (kRowsPerLoad * kWaves);        // tile loads per wave per stage
+constexpr int kLoadsA = kBN / (kRowsPerLoad * kWaves);                      // of which weight rows
+constexpr int kXsLanes = kBM / kWaves;    // token scales loaded per wave
 constexpr int kStageXs = kBM * 4;         // token scales of the block, fp32
-constexpr int kStageWs = 16;              // one weight scale per wave, fp32
+constexpr int kStageWs = kWaves * 4;      // one weight scale per wave, fp32
 constexpr int kOffXs = kStageA + kStageB;
 constexpr int kOffWs = kOffXs + kStageXs;
 constexpr int kStageBytes = kOffWs + kStageWs;
-// Outstanding vector-memory operations one stage adds per wave (12 tile
-// loads, 1 token-scale load, 1 weight-scale load); waiting for vmcnt <= this
-// leaves exactly the next stage in flight.
+constexpr int kStageStride = (kStageBytes + 1023) / 1024 * 1024;
+// Two LDS stages: while block kb is multiplied out of one, block kb+1 lands
+// in the other.
+constexpr int kStages = 2;
+// Vector-memory operations one stage adds per wave: tile loads, the token
+// scales and the weight scale.
 constexpr int kVmemPerStage = kLoadsPerWave + 2;
+static_assert(kStages * kStageStride <= 160 * 1024, "LDS budget");
+static_assert((kBN + kBM) % (kRowsPerLoad * kWaves) == 0 && kBN % (kRowsPerLoad * kWaves) == 0, "load split");
+static_assert(kXsLanes <= kWave && kWaveN % 128 == 0 || 128 % kWaveN == 0, "one weight-scale row per wave");
 
 typedef __attribute__((address_space(3))) void lds_void;
 
 // Byte offset in a stage of (row, 16-byte chunk c) after the XOR swizzle.
 __device__ __forceinline__ int swz(int row, int c) { return row * kRowBytes + ((c ^ (row & 7)) << 4); }
 
-// Issue this wave's 12 direct-to-LDS loads of K block kb into a stage.
-// Instruction q of wave w fills LDS rows 8*(4q + w) .. +7 of the 384-row stage
-// (rows 0..255 weights: q < 8; rows 256..383 tokens: q >= 8); lane l fills
-// granule l of those 1 KB, i.e. row 8*(4q+w) + l/8 at chunk position l%8, so
-// it fetches logical chunk (l%8) ^ (l/8) of that row.  The lane's byte offset
-// inside the tile is the same for every q up to q * 32 rows, which goes into
-// the scalar offset together with the K block.  Rows past the end of the
-// matrix lie outside the buffer descriptor's range and load as zeros.
+// Issue this wave's direct-to-LDS loads of K block kb into a stage.
+// Instruction q of wave w fills LDS rows 8*(W q + w) .. +7 of the stage (W =
+// waves; weight rows first, then token rows); lane l fills granule l of those
+// 1 KB, i.e. row 8*(W q + w) + l/8 at chunk position l%8, so it fetches
+// logical chunk (l%8) ^ (l/8) of that row.  The lane's byte offset inside the
+// tile is the same for every q up to q * 8W rows, which goes into the scalar
+// offset together with the K block.  Rows past the end of the matrix lie
+// outside the buffer descriptor's range and load as zeros.
 // A raw buffer descriptor (gfx9: dword 3 = 0x00020000, untyped 32-bit
 // data; offsets at or past num_records read as zero), kept in SGPRs.
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -101,17 +113,19 @@ __device__ __forceinline__ void issue_stage(uint8_t* stage, i32x4 rsrc_a, i32x4 
     const uint32_t base = lds_address(stage);
 #pragma unroll
     for (int q = 0; q < kLoadsPerWave; ++q) {
-        const uint32_t lds = __builtin_amdgcn_readfirstlane(base + 8 * (4 * q + wave) * kRowBytes);
-        if (q < kBN / 32) {
-            dma16(lds, rsrc_a, lane_off, __builtin_amdgcn_readfirstlane(k_off + (int)(32 * q * K)));
+        const uint32_t lds = __builtin_amdgcn_readfirstlane(base + kRowsPerLoad * (kWaves * q + wave) * kRowBytes);
+        if (q < kLoadsA) {
+            dma16(lds, rsrc_a, lane_off,
+                  __builtin_amdgcn_readfirstlane(k_off + (int)(kRowsPerLoad * kWaves * q * K)));
         } else {
-            dma16(lds, rsrc_b, lane_off, __builtin_amdgcn_readfirstlane(k_off + (int)(32 * (q - kBN / 32) * K)));
+            dma16(lds, rsrc_b, lane_off,
+                  __builtin_amdgcn_readfirstlane(k_off + (int)(kRowsPerLoad * kWaves * (q - kLoadsA) * K)));
         }
     }
-    // Token scales xs[m0 + 32 w + l, kb], lanes l < 32 only (the dword form
-    // writes M0 + 4 * lane for every active lane).
-    if (lane < 32)
-        dma4(__builtin_amdgcn_readfirstlane(base + kOffXs + 128 * wave), rsrc_xs, xs_off,
+    // Token scales xs[m0 + kXsLanes * w + l, kb], lanes l < kXsLanes only (the
+    // dword form writes M0 + 4 * lane for every active lane).
+    if (lane < kXsLanes)
+        dma4(__builtin_amdgcn_readfirstlane(base + kOffXs + 4 * kXsLanes * wave), rsrc_xs, xs_off,
              __builtin_amdgcn_readfirstlane((int)(kb * 4)));
     // This wave's weight scale ws[nb, kb], lane 0 only.
     if (lane == 0)
@@ -163,15 +177,14 @@ __global__ __launch_bounds__(kThreads, 1) void w8a8_tile_kernel(
     const uint8_t* __restrict__ wq, const float* __restrict__ ws,
     void* __restrict__ y, int y_dtype, int64_t M, int64_t N, int64_t K,
     int64_t tiles_n, int64_t tiles_m) {
-    __shared__ __attribute__((aligned(1024))) uint8_t stage0[kStageBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t stage1[kStageBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t stages[kStages * kStageStride];
 
     int64_t tn, tm;
     tile_of_block(blockIdx.x, tiles_n, tiles_m, tn, tm);
     const int64_t n0 = tn * kBN, m0 = tm * kBM;
     const int64_t KB = K / 128, NB = (N + 127) / 128;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
-    const int wn = wave & 1, wm = wave >> 1;
+    const int wn = wave % kWavesN, wm = wave / kWavesN;
     const int r = lane & 15, g = lane >> 4;
 
     // Buffer descriptors over this workgroup's weight rows, token rows and
@@ -182,7 +195,7 @@ __global__ __launch_bounds__(kThreads, 1) void w8a8_tile_kernel(
     const i32x4 rsrc_b = buffer_rsrc(xq + m0 * K, (uint32_t)(rows_b * K));
     const i32x4 rsrc_xs = buffer_rsrc(xs + m0 * KB, (uint32_t)(rows_b * KB * 4));
     const int lane_off = (int)((8 * wave + (lane >> 3)) * K) + ((((lane & 7) ^ ((lane >> 3) & 7))) << 4);
-    const int xs_off = (int)((32 * wave + lane) * KB * 4);
+    const int xs_off = (int)((kXsLanes * wave + lane) * KB * 4);
 
     // Weight scales: one row of ws per wave (its 128 weight rows share it).
     int64_t nb = (n0 + kWaveN * wn) / 128;
@@ -199,11 +212,12 @@ __global__ __launch_bounds__(kThreads, 1) void w8a8_tile_kernel(
     const int a_row0 = kWaveN * wn + r;           // + 16 i
     const int b_row0 = kBN + kWaveM * wm + r;     // + 16 j
 
-    // One 128-K block: for each of the 8 weight sub-tiles i, 4 MFMAs (one per
-    // token sub-tile j) into block temporaries; the FMAs that promote row i's
-    // temporaries are issued after row i+1's MFMAs, so the matrix core and
-    // the VALU work on different rows and no FMA waits on the MFMA before it.
-    auto compute = [&](const uint8_t* stage, int64_t kb) {
+    // Per block, per wave: kTi rows of kTj MFMAs (one per 16x16 tile) into
+    // block temporaries; the FMAs that promote row i are issued after row
+    // i+1's MFMAs, so the matrix core and the VALU work on different rows.
+    // The token fragments and the scales of the block are read first; the
+    // weight fragments are streamed one row ahead.
+    auto compute = [&](const uint8_t* stage) {
         const float wsc = reinterpret_cast<const float*>(stage + kOffWs)[wave];
         const float* xs_lds = reinterpret_cast<const float*>(stage + kOffXs);
         float sc[kTj];
@@ -216,16 +230,16 @@ __global__ __launch_bounds__(kThreads, 1) void w8a8_tile_kernel(
         i32x8 af = read_frag(stage, a_row0, g);
 #pragma unroll
         for (int i = 0; i < kTi; ++i) {
-            const int cur = i & 1;
+            const int c = i & 1;
 #pragma unroll
-            for (int j = 0; j < kTj; ++j) tmp[cur][j] = mfma_e4m3_16x16x128(af, bf[j], zero);
+            for (int j = 0; j < kTj; ++j) tmp[c][j] = mfma_e4m3_16x16x128(af, bf[j], zero);
             if (i + 1 < kTi) af = read_frag(stage, a_row0 + 16 * (i + 1), g);
             if (i > 0) {
 #pragma unroll
                 for (int j = 0; j < kTj; ++j)
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        acc[i - 1][j][e] = __builtin_fmaf(tmp[cur ^ 1][j][e], sc[j], acc[i - 1][j][e]);
+                        acc[i - 1][j][e] = __builtin_fmaf(tmp[c ^ 1][j][e], sc[j], acc[i - 1][j][e]);
             }
         }
 #pragma unroll
@@ -235,34 +249,17 @@ __global__ __launch_bounds__(kThreads, 1) void w8a8_tile_kernel(
                 acc[kTi - 1][j][e] = __builtin_fmaf(tmp[(kTi - 1) & 1][j][e], sc[j], acc[kTi - 1][j][e]);
     };
 
-    constexpr int kWaitNext = (kVmemPerStage & 0xF) | ((kVmemPerStage >> 4) << 14) | (0x7 << 4) | (0xF << 8);
-    constexpr int kWaitAll = (0x7 << 4) | (0xF << 8);
-    constexpr int kWaitLds = (0x3F) | (0x3 << 14) | (0x7 << 4);         // lgkmcnt(0)
-    issue_stage(stage0, rsrc_a, rsrc_b, rsrc_xs, rsrc_ws, lane_off, xs_off, K, 0, wave, lane);
-    for (int64_t kb = 0; kb < KB; kb += 2) {
-        // ---- block kb in stage0; prefetch kb+1 into stage1
-        if (kb + 1 < KB) {
-            issue_stage(stage1, rsrc_a, rsrc_b, rsrc_xs, rsrc_ws, lane_off, xs_off, K, kb + 1, wave, lane);
-            __builtin_amdgcn_s_waitcnt(kWaitNext);
-        } else {
-            __builtin_amdgcn_s_waitcnt(kWaitAll);
-        }
+    auto stage = [&](int64_t kb) { return stages + (int)(kb % kStages) * kStageStride; };
+    issue_stage(stage(0), rsrc_a, rsrc_b, rsrc_xs, rsrc_ws, lane_off, xs_off, K, 0, wave, lane);
+    for (int64_t kb = 0; kb < KB; ++kb) {
+        // This wave's loads of block kb and its LDS reads of block kb-1 are
+        // done; after the barrier every wave's block kb is in LDS and nobody
+        // reads block kb-1's stage, which then receives block kb+1.
+        __builtin_amdgcn_s_waitcnt(0x7 << 4);                  // vmcnt(0), lgkmcnt(0)
         stage_barrier();
-        compute(stage0, kb);
-        __builtin_amdgcn_s_waitcnt(kWaitLds);
-        stage_barrier();
-        if (kb + 1 >= KB) break;
-        // ---- block kb+1 in stage1; prefetch kb+2 into stage0
-        if (kb + 2 < KB) {
-            issue_stage(stage0, rsrc_a, rsrc_b, rsrc_xs, rsrc_ws, lane_off, xs_off, K, kb + 2, wave, lane);
-            __builtin_amdgcn_s_waitcnt(kWaitNext);
-        } else {
-            __builtin_amdgcn_s_waitcnt(kWaitAll);
-        }
-        stage_barrier();
-        compute(stage1, kb + 1);
-        __builtin_amdgcn_s_waitcnt(kWaitLds);
-        stage_barrier();
+        if (kb + 1 < KB)
+            issue_stage(stage(kb + 1), rsrc_a, rsrc_b, rsrc_xs, rsrc_ws, lane_off, xs_off, K, kb + 1, wave, lane);
+        compute(stage(kb));
     }
 
     // Epilogue: lane holds n = n0 + 128 wn + 16 i + 4 g + e (e = 0..3) of token m.
