@@ -46,6 +46,7 @@ bfp8_status bfp8_quantize_act_1x128(const void* x, int x_dtype, int64_t M, int64
                                     uint8_t* xq, float* xs, void* stream) {
     if (!x || !xq || !xs) return BFP8_E_NULL;
     if (!dim_ok(M, 1) || !dim_ok(K, 8) || K % 8 != 0 || M * K >= ((int64_t)1 << 40)) return BFP8_E_SHAPE;
+    if (M * ((K + 2047) / 2048) >= kMaxDim) return BFP8_E_SHAPE;   // one workgroup per row and 2048 columns
     if (!is16(x_dtype)) return BFP8_E_DTYPE;
     if (!aligned(x) || !aligned(xq) || !aligned(xs)) return BFP8_E_ALIGN;
     return launched(launch_quant_act_1x128(x, x_dtype == BFP8_BF16, M, K, xq, xs, as_stream(stream)));

@@ -8,9 +8,11 @@
 // 4-step butterfly over the 16 lanes, and each lane writes its 8 codes with
 // one 8-byte store.  A wave covers 4 groups.
 //
-// The scale and the per-element quotient are IEEE fp32 divisions (the
-// default, correctly rounded, fp32 division of the HIP compiler), so the
-// codes and scales are bit-exact functions of the input.
+// The scale is an IEEE fp32 division (the compiler's default, correctly
+// rounded, fp32 division) and each element's quotient x / s is the correctly
+// rounded fp32 quotient (QuotientBy: one IEEE division per group, three
+// instructions per element), so the codes and scales are bit-exact functions
+// of the input.
 
 #include "bfp8_device.hpp"
 #include "bfp8_launch.hpp"
@@ -18,10 +20,23 @@
 namespace bfp8 {
 
 // Quantise 8 values against scale s; returns the 8 codes packed in K order.
+// A zero group (s == 0) gives code 0x00 everywhere.
 __device__ __forceinline__ void quantize8(const float v[8], float s, uint32_t& lo, uint32_t& hi) {
+    const QuotientBy div(s);
+    float q[8];
+    // The IEEE fallback (scales outside [2^-90, 2^100]) is taken by the whole
+    // wave when any lane needs it, so the common path has no divergence.
+    if (__any(div.ieee)) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[i] = fabsf(v[i]) / s;
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[i] = div.abs_quotient(v[i]);
+    }
     uint32_t c[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) c[i] = (s == 0.0f) ? 0u : e4m3_encode(v[i] / s);
+    for (int i = 0; i < 8; ++i)
+        c[i] = (s == 0.0f) ? 0u : (e4m3_encode(q[i]) | ((__float_as_uint(v[i]) >> 24) & 0x80u));
     lo = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
     hi = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
 }
@@ -37,18 +52,16 @@ __device__ __forceinline__ void unpack8(u32x4 raw, bool bf16, float v[8]) {
 
 constexpr int kQuantActThreads = 256;
 
-// Grid: one thread per 8 input values of a group; 16 threads per group.
+// Grid: one workgroup per (row, run of 16 groups); 16 threads per group,
+// one thread per 8 input values.
 __global__ __launch_bounds__(kQuantActThreads) void quant_act_1x128_kernel(
-    const uint16_t* __restrict__ x, int bf16, int64_t M, int64_t K, int64_t G,
+    const uint16_t* __restrict__ x, int bf16, int64_t M, int64_t K, int64_t G, int64_t blocks_per_row,
     uint8_t* __restrict__ xq, float* __restrict__ xs) {
-    const int64_t tid = (int64_t)blockIdx.x * kQuantActThreads + threadIdx.x;
-    const int64_t group = tid >> 4;                 // flat (row, group) index
-    const int lane16 = (int)(tid & 15);
-    const bool group_valid = group < M * G;
-    const int64_t m = group_valid ? group / G : 0;
-    const int64_t g = group_valid ? group - m * G : 0;
+    const int64_t m = blockIdx.x / blocks_per_row;               // uniform per workgroup
+    const int64_t g = (blockIdx.x - m * blocks_per_row) * (kQuantActThreads / 16) + (threadIdx.x >> 4);
+    const int lane16 = threadIdx.x & 15;
     const int64_t col = g * 128 + lane16 * 8;
-    const bool valid = group_valid && col < K;      // K % 8 == 0: a chunk is all in or all out
+    const bool valid = g < G && col < K;            // K % 8 == 0: a chunk is all in or all out
 
     float v[8];
     if (valid) {
@@ -117,10 +130,9 @@ __global__ __launch_bounds__(kQuantWThreads) void quant_weight_128x128_kernel(
 hipError_t launch_quant_act_1x128(const void* x, bool bf16, int64_t M, int64_t K,
                                   uint8_t* xq, float* xs, hipStream_t stream) {
     const int64_t G = (K + 127) / 128;
-    const int64_t threads = M * G * 16;
-    const int64_t blocks = (threads + kQuantActThreads - 1) / kQuantActThreads;
-    hipLaunchKernelGGL(quant_act_1x128_kernel, dim3((unsigned)blocks), dim3(kQuantActThreads), 0, stream,
-                       static_cast<const uint16_t*>(x), (int)bf16, M, K, G, xq, xs);
+    const int64_t blocks_per_row = (G + kQuantActThreads / 16 - 1) / (kQuantActThreads / 16);
+    hipLaunchKernelGGL(quant_act_1x128_kernel, dim3((unsigned)(M * blocks_per_row)), dim3(kQuantActThreads), 0,
+                       stream, static_cast<const uint16_t*>(x), (int)bf16, M, K, G, blocks_per_row, xq, xs);
     return hipGetLastError();
 }
 

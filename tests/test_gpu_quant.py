@@ -61,6 +61,23 @@ def test_quant_act_encoder_exhaustive_over_bf16(gpu_lib):
     _act_case(grid.to(torch.bfloat16), f"exhaustive bf16 ({rows} groups)")
 
 
+def test_quant_act_wide_scale_range_many_groups(gpu_lib):
+    """65536 groups whose scales span about 2^-91 .. 2^102, including groups next
+    to the limits of the one-division-per-group path and groups that mix
+    bf16 subnormals with a normal maximum: every code and scale bit-exact."""
+    M, K = 2048, 4096
+    g = np.random.default_rng(77)
+    z = g.standard_normal((M, K)).astype(np.float32)
+    row_exp = g.integers(-60, 61, size=M).astype(np.float32)
+    row_exp[:16] = np.linspace(-85, -78, 16)          # s = amax/448 on both sides of 2^-90
+    row_exp[16:32] = np.linspace(104, 111, 16)       # s on both sides of 2^100
+    x = z * np.exp2(row_exp)[:, None]
+    x[32:48] = z[32:48] * np.float32(2.0 ** -133)    # bf16 subnormals ...
+    x[32:48, ::128] = np.float32(2.0 ** -100)       # ... next to a normal group maximum
+    x[48:64, :] = np.float32(0.0)                    # zero rows
+    _act_case(torch.from_numpy(x).to(torch.bfloat16), "wide scale range")
+
+
 def test_quant_act_prefill_outliers_sampled(gpu_lib):
     """Full 4096x4096 run with 1% outlier channels; 64 sampled rows checked."""
     x = inputs.workload(2)["x"]
