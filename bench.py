@@ -10,6 +10,12 @@ Workloads (synthetic, seeded; inputs resident in HBM before timing starts):
            activation quantisation + W8A8 GEMM.  Headline: TFLOP/s.
   blk32    block-32 UE8M0 weight-only GEMM, N=4096, K=7168, M=--m (default 1).
            Headline: HBM GB/s.
+  sweep    W8A8 over the projections (N x K) 4096x4096, 1024x4096, 12288x4096,
+           4096x12288 and M in {1, 2, 4, 8, 16, 32, 64, 128, 512, 4096}; weights
+           rotate over copies totalling >= 512 MiB per shape.  Per point: GEMM
+           and quantiser microseconds and the GEMM's fraction of its roofline
+           time max(bytes / 8 TB/s, FLOPs / 5 PFLOP/s).  Headline: geometric
+           mean of those fractions.
 
 The timed region runs the K steps kernel by kernel (K back-to-back launches
 of each), with one HIP event pair per kernel on the stream the kernels run
@@ -41,7 +47,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", choices=["decode", "prefill", "blk32"], default="decode")
+    p.add_argument("--workload", choices=["decode", "prefill", "blk32", "sweep"], default="decode")
     p.add_argument("--m", type=int, default=None, help="token count for blk32 / decode")
     p.add_argument("--copies", type=int, default=32, help="distinct weight copies rotated per call")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -284,6 +290,53 @@ def bench_blk32(torch, bfp8, inputs, args):
     return result
 
 
+def bench_sweep(torch, bfp8, inputs, args):
+    import math
+    points = []
+    steps = max(10, min(args.steps, 50))
+    for (N, K) in inputs.SWEEP_SHAPES:
+        w = inputs.weights_bf16(N, K, workload=4, stream=N + K).cuda()
+        wq0, ws0 = bfp8.quantize_weight(w)
+        del w
+        ncopy = max(2, min(64, -(-(512 << 20) // (N * K))))
+        copies = [(wq0.clone(), ws0.clone()) for _ in range(ncopy)]
+        for M in inputs.SWEEP_M:
+            x = inputs.activations(M, K, workload=4, stream=M).cuda()
+            xq = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+            xs = torch.empty((M, K // 128), dtype=torch.float32, device="cuda")
+            y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+            wsb = bfp8.make_workspace(bfp8.OP_GEMM_W8A8_BLK128, M, N, K)
+
+            def gemm(i, copies=copies, xq=xq, xs=xs, y=y, wsb=wsb):
+                a = copies[i % len(copies)]
+                bfp8.bfp8_gemm_w8a8_blk128(xq, xs, a[0], a[1], y, wsb)
+
+            phases = [("quant_act_1x128", lambda i, x=x, xq=xq, xs=xs: bfp8.bfp8_quantize_act_1x128(x, xq, xs)),
+                      ("gemm_w8a8_blk128", gemm)]
+            ms, wall, kern, timing = run_steps(torch, phases, steps, 3)
+            g_us = kern["gemm_w8a8_blk128"]["avg_us"]
+            nbytes, flops = bytes_w8a8(M, N, K), 2.0 * M * N * K
+            roof_us = max(nbytes / (HBM_PEAK_GBS * 1e3), flops / (FP8_PEAK_TFLOPS * 1e6))
+            points.append({"N": N, "K": K, "M": M, "gemm_us": g_us, "quant_us": kern["quant_act_1x128"]["avg_us"],
+                           "TFLOPs": flops / (g_us * 1e6), "GBps": nbytes / (g_us * 1e3),
+                           "bound": "hbm" if nbytes / (HBM_PEAK_GBS * 1e3) >= flops / (FP8_PEAK_TFLOPS * 1e6) else "mfma",
+                           "roofline_frac": roof_us / g_us, "copies": len(copies)})
+            print(json.dumps(points[-1]), file=sys.stderr, flush=True)
+            del x, xq, xs, y, wsb
+        del copies
+        torch.cuda.empty_cache()
+    geo = math.exp(sum(math.log(p["roofline_frac"]) for p in points) / len(points))
+    worst = min(points, key=lambda p: p["roofline_frac"])
+    return {"value": geo, "unit": "fraction of roofline (geometric mean)", "ms_per_step": sum(p["gemm_us"] for p in points) / 1e3,
+            "dtype": "e4m3",
+            "config": {"workload": "W8A8 projection sweep (N x K) x M", "shapes": [list(s) for s in inputs.SWEEP_SHAPES],
+                       "M": list(inputs.SWEEP_M), "steps_per_point": steps},
+            "roofline": {"kernel": "gemm_w8a8_blk128", "bound": worst["bound"], "achieved": worst["roofline_frac"],
+                         "peak": 1.0, "unit": "fraction", "frac": worst["roofline_frac"], "traffic": None,
+                         "note": "worst point of the sweep"},
+            "kernels": {"points": points}, "timing": {"method": "per-kernel phases of back-to-back launches, HIP events"}}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -295,7 +348,7 @@ def main():
     from blockwise_scaled_fp8_amd import inputs
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     bfp8.load()
-    fn = {"decode": bench_decode, "prefill": bench_prefill, "blk32": bench_blk32}[args.workload]
+    fn = {"decode": bench_decode, "prefill": bench_prefill, "blk32": bench_blk32, "sweep": bench_sweep}[args.workload]
     r = fn(torch, bfp8, inputs, args)
     line = {"metric": METRIC, "value": r["value"], "unit": r["unit"], "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": r["ms_per_step"], "higher_is_better": True, "scaling": "weak",

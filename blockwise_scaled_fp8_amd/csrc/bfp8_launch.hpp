@@ -8,8 +8,11 @@
 
 namespace bfp8 {
 
-// Largest M served by the weight-streaming (decode) kernels.
-constexpr int64_t kStreamMaxM = 16;
+// Largest M served by the weight-streaming (decode) kernel of W8A8.
+#ifndef BFP8_STREAM_MAX_M
+#define BFP8_STREAM_MAX_M 16
+#endif
+constexpr int64_t kStreamMaxM = BFP8_STREAM_MAX_M;
 // Rows of W covered by one streaming workgroup (one MFMA row tile).
 constexpr int64_t kStreamRows = 16;
 // Largest K of the tiled W8A8 kernel (256 rows x K bytes must fit a 32-bit

@@ -27,10 +27,13 @@
 // weights again.
 //
 // Operand mapping: within a 128-K block, lane l (row/column l % 16, slot
-// g = l / 16) holds the 32 K values [32 g, 32 g + 32) of its weight row.
-// MFMA j (j = 0..3) of the block takes bytes [8 j, 8 j + 8) of those, i.e.
-// K indices 32 g + 8 j + (0..7); the activation operand of MFMA j is loaded
-// with the same mapping, so the contraction covers each K index once.
+// g = l / 16) holds the 16-byte weight chunks g and g + 4 of its row (K
+// offsets 16 g and 64 + 16 g), so each load instruction reads whole 64-byte
+// halves of 16 rows.  MFMA j (j = 0..3) takes 8 of those 32 values: K
+// offsets 16 g + 8 j for j < 2 and 64 + 16 g + 8 (j - 2) for j >= 2; the
+// activation operand of MFMA j is loaded with the same mapping, so the
+// contraction covers each K index once.  The eight waves take interleaved
+// 128-K blocks, so at any time a workgroup reads adjacent blocks of its rows.
 
 #include "bfp8_device.hpp"
 #include "bfp8_launch.hpp"
@@ -65,8 +68,8 @@ __global__ __launch_bounds__(kStreamThreads) void w8a16_blk128_stream_kernel(
     const int64_t kb_begin = split * kb_per_split;
     const int64_t kb_end = kb_begin + kb_per_split < KB ? kb_begin + kb_per_split : KB;
 
-    const uint8_t* wrow = wq + n * K + g * 32;
-    const uint16_t* xrow = x + (m_ok ? m : 0) * K + g * 32;
+    const uint8_t* wrow = wq + n * K + g * 16;
+    const uint16_t* xrow = x + (m_ok ? m : 0) * K + g * 16;
     const float* ws_row = ws + (nt * 16 / 128) * KB;
     // Exponent-bias difference between E4M3 and the 16-bit type, folded into the scale.
     const float bias_fold = kXBf16 ? 0x1p120f : 0x1p8f;
@@ -75,21 +78,23 @@ __global__ __launch_bounds__(kStreamThreads) void w8a16_blk128_stream_kernel(
     const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
     for (int64_t kb0 = kb_begin + wave; kb0 < kb_end; kb0 += kStreamWaves * kW8A16Chunk) {
         u32x4 wa[kW8A16Chunk][2], xb[kW8A16Chunk][4];
-#pragma unroll
-        for (int c = 0; c < kW8A16Chunk; ++c) {
-            const int64_t kb = kb0 + c * kStreamWaves;
-            if (kb < kb_end) {
-                wa[c][0] = load_nt_16B(wrow + kb * 128);
-                wa[c][1] = load_nt_16B(wrow + kb * 128 + 16);
-            }
-        }
+        // Activations first (from L2), then the weight stream.
 #pragma unroll
         for (int c = 0; c < kW8A16Chunk; ++c) {
             const int64_t kb = kb0 + c * kStreamWaves;
             if (kb < kb_end) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    xb[c][j] = m_ok ? load_16B(xrow + kb * 128 + 8 * j) : u32x4{0u, 0u, 0u, 0u};
+                    xb[c][j] = m_ok ? load_16B(xrow + kb * 128 + (j < 2 ? 8 * j : 64 + 8 * (j - 2)))
+                                    : u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < kW8A16Chunk; ++c) {
+            const int64_t kb = kb0 + c * kStreamWaves;
+            if (kb < kb_end) {
+                wa[c][0] = load_16B(wrow + kb * 128);
+                wa[c][1] = load_16B(wrow + kb * 128 + 64);
             }
         }
 #pragma unroll
@@ -129,31 +134,35 @@ __global__ __launch_bounds__(kStreamThreads) void w8a16_blk32_stream_kernel(
     const int64_t kb_begin = split * kb_per_split;
     const int64_t kb_end = kb_begin + kb_per_split < KB ? kb_begin + kb_per_split : KB;
 
-    const uint8_t* wrow = wq + n * K + g * 32;
-    const uint16_t* xrow = x + (m_ok ? m : 0) * K + g * 32;
-    // This lane's 32 weights of block kb lie in 32x32 tile (n / 32, 4 kb + g).
-    const uint8_t* erow = e8m0 + (n / 32) * K32 + g;
+    const uint8_t* wrow = wq + n * K + g * 16;
+    const uint16_t* xrow = x + (m_ok ? m : 0) * K + g * 16;
+    // This lane's chunk g of block kb lies in 32x32 tile (n / 32, 4 kb + g / 2)
+    // and its chunk g + 4 in tile (n / 32, 4 kb + 2 + g / 2).
+    const uint8_t* erow = e8m0 + (n / 32) * K32 + (g >> 1);
 
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
     for (int64_t kb0 = kb_begin + wave; kb0 < kb_end; kb0 += kStreamWaves * kW8A16Chunk) {
         u32x4 wa[kW8A16Chunk][2], xb[kW8A16Chunk][4];
-        uint32_t ebyte[kW8A16Chunk];
-#pragma unroll
-        for (int c = 0; c < kW8A16Chunk; ++c) {
-            const int64_t kb = kb0 + c * kStreamWaves;
-            if (kb < kb_end) {
-                wa[c][0] = load_nt_16B(wrow + kb * 128);
-                wa[c][1] = load_nt_16B(wrow + kb * 128 + 16);
-                ebyte[c] = erow[kb * 4];
-            }
-        }
+        uint32_t ebyte[kW8A16Chunk][2];
+        // Activations and scale bytes first (from L2), then the weight stream.
 #pragma unroll
         for (int c = 0; c < kW8A16Chunk; ++c) {
             const int64_t kb = kb0 + c * kStreamWaves;
             if (kb < kb_end) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    xb[c][j] = m_ok ? load_16B(xrow + kb * 128 + 8 * j) : u32x4{0u, 0u, 0u, 0u};
+                    xb[c][j] = m_ok ? load_16B(xrow + kb * 128 + (j < 2 ? 8 * j : 64 + 8 * (j - 2)))
+                                    : u32x4{0u, 0u, 0u, 0u};
+                ebyte[c][0] = erow[kb * 4];
+                ebyte[c][1] = erow[kb * 4 + 2];
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < kW8A16Chunk; ++c) {
+            const int64_t kb = kb0 + c * kStreamWaves;
+            if (kb < kb_end) {
+                wa[c][0] = load_16B(wrow + kb * 128);
+                wa[c][1] = load_16B(wrow + kb * 128 + 64);
             }
         }
 #pragma unroll
@@ -162,8 +171,9 @@ __global__ __launch_bounds__(kStreamThreads) void w8a16_blk32_stream_kernel(
             if (kb < kb_end) {
                 // 2^(E - 127 + 8) as fp16: exponent field (E - 119) + 15 = E - 104, in [9, 30]
                 // for E in [113, 134]; both halves of the packed factor.
-                const uint32_t f = (ebyte[c] - 104u) << 10;
-                const f16x2 factor = __builtin_bit_cast(f16x2, f | (f << 16));
+                const uint32_t f0 = (ebyte[c][0] - 104u) << 10, f1 = (ebyte[c][1] - 104u) << 10;
+                const f16x2 factor0 = __builtin_bit_cast(f16x2, f0 | (f0 << 16));
+                const f16x2 factor1 = __builtin_bit_cast(f16x2, f1 | (f1 << 16));
                 const uint32_t q[8] = {wa[c][0][0], wa[c][0][1], wa[c][0][2], wa[c][0][3],
                                        wa[c][1][0], wa[c][1][1], wa[c][1][2], wa[c][1][3]};
 #pragma unroll
@@ -171,6 +181,7 @@ __global__ __launch_bounds__(kStreamThreads) void w8a16_blk32_stream_kernel(
                     uint32_t d0, d1, d2, d3;
                     e4m3x4_to_f16x4(q[2 * j], d0, d1);
                     e4m3x4_to_f16x4(q[2 * j + 1], d2, d3);
+                    const f16x2 factor = j < 2 ? factor0 : factor1;
                     const u32x4 a = {scale_f16x2(d0, factor), scale_f16x2(d1, factor),
                                      scale_f16x2(d2, factor), scale_f16x2(d3, factor)};
                     acc = mfma_f16_16x16x32(a, xb[c][j], acc);

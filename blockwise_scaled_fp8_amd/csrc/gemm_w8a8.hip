@@ -23,7 +23,7 @@
 //
 // Two kernels, chosen by M ([ADA] "One tile doesn't fit all M"):
 //   * stream (M <= 16): weight streaming.  One workgroup per 16 weight rows
-//     (and per split of K), eight waves each holding several 128-K blocks of
+//     (and per split of K), sixteen waves each holding its 128-K blocks of
 //     weight loads in flight, tokens padded to 16 on the MFMA column axis.
 //   * tile (M > 16): in gemm_w8a8_tile.hip.
 
@@ -39,11 +39,11 @@ StreamPlan plan_stream(int64_t M, int64_t N, int64_t K) {
     p.n_tiles = N / kStreamRows;
     p.m_tiles = (M + 15) / 16;
     const int64_t KB = K / 128;
-    // Enough workgroups to give each of the 256 CUs one, but keep at least
-    // one 128-K block per wave of a workgroup.
+    // Enough workgroups to give each of the 256 CUs one, while at least half
+    // of a workgroup's waves still get a 128-K block.
     const int64_t tiles = p.n_tiles * p.m_tiles;
     int64_t splits = 1;
-    while (tiles * splits < 256 && KB / (splits * 2) >= kStreamWaves) splits *= 2;
+    while (tiles * splits < 256 && 2 * (KB / (splits * 2)) >= kStreamWaves) splits *= 2;
     p.splits = splits;
     p.kb_per_split = (KB + splits - 1) / splits;
     return p;
@@ -58,6 +58,11 @@ size_t stream_workspace_bytes(const StreamPlan& p) {
 // =================================================================== stream
 constexpr int kW8A8Chunk = 4;   // 128-K blocks per wave with loads in flight together
 
+// Lane (r, g) supplies weight row n0 + r and token m0 + r; of each 128-K
+// block it holds the 16-byte chunks g and g + 4 (K offsets 16g and 64 + 16g),
+// the same for both MFMA operands.  Each load instruction then reads whole
+// 64-byte halves of 16 weight rows.  The eight waves take interleaved 128-K
+// blocks, so at any time a workgroup reads adjacent blocks of its rows.
 __global__ __launch_bounds__(kStreamThreads) void w8a8_stream_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ xs,
     const uint8_t* __restrict__ wq, const float* __restrict__ ws,
@@ -76,8 +81,8 @@ __global__ __launch_bounds__(kStreamThreads) void w8a8_stream_kernel(
     const int64_t kb_begin = split * kb_per_split;
     const int64_t kb_end = kb_begin + kb_per_split < KB ? kb_begin + kb_per_split : KB;
 
-    const uint8_t* wrow = wq + n * K + g * 32;
-    const uint8_t* xrow = xq + (m_ok ? m : 0) * K + g * 32;
+    const uint8_t* wrow = wq + n * K + g * 16;
+    const uint8_t* xrow = xq + (m_ok ? m : 0) * K + g * 16;
     const float* ws_row = ws + (nt * 16 / 128) * KB;
     const float* xs_row = xs + (m_ok ? m : 0) * KB;
 
@@ -86,26 +91,28 @@ __global__ __launch_bounds__(kStreamThreads) void w8a8_stream_kernel(
     for (int64_t kb0 = kb_begin + wave; kb0 < kb_end; kb0 += kStreamWaves * kW8A8Chunk) {
         u32x4 wa[kW8A8Chunk][2], xb[kW8A8Chunk][2];
         float sc[kW8A8Chunk];
-#pragma unroll
-        for (int c = 0; c < kW8A8Chunk; ++c) {
-            const int64_t kb = kb0 + c * kStreamWaves;
-            if (kb < kb_end) {
-                wa[c][0] = load_nt_16B(wrow + kb * 128);
-                wa[c][1] = load_nt_16B(wrow + kb * 128 + 16);
-            }
-        }
+        // Token codes and scales first: they come from L2 and their latency
+        // then hides under the weight stream instead of trailing it.
 #pragma unroll
         for (int c = 0; c < kW8A8Chunk; ++c) {
             const int64_t kb = kb0 + c * kStreamWaves;
             if (kb < kb_end) {
                 if (m_ok) {
                     xb[c][0] = load_16B(xrow + kb * 128);
-                    xb[c][1] = load_16B(xrow + kb * 128 + 16);
+                    xb[c][1] = load_16B(xrow + kb * 128 + 64);
                     sc[c] = xs_row[kb] * ws_row[kb];
                 } else {
                     xb[c][0] = xb[c][1] = u32x4{0u, 0u, 0u, 0u};
                     sc[c] = 0.0f;
                 }
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < kW8A8Chunk; ++c) {
+            const int64_t kb = kb0 + c * kStreamWaves;
+            if (kb < kb_end) {
+                wa[c][0] = load_16B(wrow + kb * 128);
+                wa[c][1] = load_16B(wrow + kb * 128 + 64);
             }
         }
 #pragma unroll

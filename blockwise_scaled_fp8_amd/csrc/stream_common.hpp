@@ -10,6 +10,15 @@
 // the workspace, and the last one to arrive (device-scope counter) sums all
 // of them in split order, stores Y and re-arms the counter.  No
 // floating-point atomics: results are run-to-run identical.
+//
+// The hand-off uses agent-scope relaxed atomic accesses (write-through
+// stores and loads that bypass the per-XCD L2, and a memory-side atomic
+// counter) plus explicit completion waits, not __threadfence(): on this part
+// a device-scope fence writes back and invalidates the XCD's whole L2, which
+// made a split-K call cost tens of microseconds.  Ordering: every thread's
+// partial store has completed (vmcnt 0) before the workgroup barrier that
+// precedes the counter increment, so a workgroup that sees the final count
+// reads complete partial tiles.
 #pragma once
 
 #include "bfp8_device.hpp"
@@ -17,7 +26,7 @@
 
 namespace bfp8 {
 
-constexpr int kStreamWaves = 8;
+constexpr int kStreamWaves = 16;
 constexpr int kStreamThreads = kStreamWaves * kWave;
 
 // Workspace layout of a split-K plan: one uint32 counter per output tile
@@ -73,21 +82,21 @@ __device__ __forceinline__ void stream_finish(f32x4 acc, float* red, void* y, in
 
     const int64_t tile = mt * n_tiles + nt;
     float* my_tiles = partials + tile * splits * 256;
-    if (t < 256) my_tiles[split * 256 + t] = v;
-    __threadfence();                      // release the partial tile at device scope
+    if (t < 256) __hip_atomic_store(&my_tiles[split * 256 + t], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0);            // this thread's partial store has completed
     __syncthreads();
     __shared__ uint32_t arrived;
-    if (t == 0) arrived = atomicAdd(&counters[tile], 1u);
+    if (t == 0) arrived = __hip_atomic_fetch_add(&counters[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     if (arrived != (uint32_t)(splits - 1)) return;   // not the last workgroup of this tile
 
-    __threadfence();                      // acquire the other workgroups' tiles
     if (t < 256) {
         float s = 0.0f;
-        for (int64_t k = 0; k < splits; ++k) s += my_tiles[k * 256 + t];
+        for (int64_t k = 0; k < splits; ++k)
+            s += __hip_atomic_load(&my_tiles[k * 256 + t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (m < M) store_out(y, y_dtype, m * N + n, s);
     }
-    if (t == 0) counters[tile] = 0u;      // re-arm for the next call
+    if (t == 0) __hip_atomic_store(&counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // re-arm
 }
 
 }  // namespace bfp8
