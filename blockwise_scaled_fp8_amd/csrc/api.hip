@@ -66,7 +66,7 @@ size_t bfp8_workspace_bytes(int op, int64_t M, int64_t N, int64_t K) {
     if (M < 1 || N < 16 || K < 128) return 0;
     switch (op) {
         case BFP8_OP_GEMM_W8A8_BLK128:
-            if (M > kStreamMaxM) return 0;                  // the tiled kernel needs none
+            if (M > kStreamMaxM) return K <= kTileMaxK ? tile_workspace_bytes(M, N, K) : 0;
             return stream_workspace_bytes(plan_stream(M, N, K));
         case BFP8_OP_GEMM_W8A16_BLK128:
         case BFP8_OP_GEMM_W8A16_BLK32_UE8M0:
@@ -87,9 +87,9 @@ bfp8_status bfp8_gemm_w8a8_blk128(const uint8_t* xq, const float* xs, const uint
     if (!aligned(xs)) return BFP8_E_ALIGN;
     if (M <= kStreamMaxM)
         return launched(launch_w8a8_stream(xq, xs, wq, ws, y, y_dtype, M, N, K, workspace, as_stream(stream)));
-    // The tiled kernel addresses a 256-row slab of W through a 32-bit buffer range.
+    // The tiled kernels address a 256-row slab of W through 32-bit offsets.
     if (K > kTileMaxK) return BFP8_E_SHAPE;
-    return launched(launch_w8a8_tile(xq, xs, wq, ws, y, y_dtype, M, N, K, as_stream(stream)));
+    return launched(launch_w8a8_tile(xq, xs, wq, ws, y, y_dtype, M, N, K, workspace, as_stream(stream)));
 }
 
 bfp8_status bfp8_gemm_w8a16_blk128(const void* x, int x_dtype, const uint8_t* wq, const float* ws,

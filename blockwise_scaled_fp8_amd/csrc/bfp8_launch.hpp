@@ -15,9 +15,12 @@ namespace bfp8 {
 constexpr int64_t kStreamMaxM = BFP8_STREAM_MAX_M;
 // Rows of W covered by one streaming workgroup (one MFMA row tile).
 constexpr int64_t kStreamRows = 16;
-// Largest K of the tiled W8A8 kernel (256 rows x K bytes must fit a 32-bit
-// buffer range, with room for the scalar offsets).
+// Largest K of the tiled W8A8 kernels (256 rows x K bytes must fit the
+// 32-bit per-lane offsets of their buffer loads).
 constexpr int64_t kTileMaxK = (int64_t)1 << 23;
+// Workspace bytes of the tiled W8A8 kernels (split-K partial tiles and tile
+// counters; 0 when the shape is not split).
+size_t tile_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 // Split-K plan of a streaming kernel: `splits` workgroups share one
 // (16-row, 16-token) output tile, each covering `kb_per_split` 128-K blocks.
@@ -34,7 +37,8 @@ hipError_t launch_quant_weight_128x128(const void* w, bool bf16, int64_t N, int6
                                        uint8_t* wq, float* ws, hipStream_t stream);
 
 hipError_t launch_w8a8_tile(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
-                            void* y, int y_dtype, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+                            void* y, int y_dtype, int64_t M, int64_t N, int64_t K, void* workspace,
+                            hipStream_t stream);
 hipError_t launch_w8a8_stream(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
                               void* y, int y_dtype, int64_t M, int64_t N, int64_t K,
                               void* workspace, hipStream_t stream);

@@ -1,13 +1,13 @@
-// W8A8 blockwise GEMM, tiled kernel for M > 16 (prefill) on gfx950.
+// W8A8 blockwise GEMM, tiled kernels for M > 16 on gfx950.
 //
-// Workgroup tile: 256 weight rows (n) x 256 tokens (m), K staged one
-// 128-wide scale block at a time ([ARC] "What this adds": the K tile is the
-// scale block, so each stage has one scale per row block and token).  Eight
-// waves, two per SIMD, each owning 128 n x 64 m = 8 x 4 MFMA tiles of 16x16;
+// A workgroup computes a BN (weight rows n) x BM (tokens m) tile of Y over a
+// range of 128-wide K blocks, one scale block per LDS stage ([ARC] "What
+// this adds": the K tile is the scale block, so each stage has one scale per
+// row block and token).  Eight waves, two per SIMD, tile the workgroup tile;
 // two waves per SIMD let one wave's promotion FMAs run in the shadow of the
-// other wave's MFMAs.  Each wave's fp32 accumulators, operand fragments
-// and block temporaries fit its 256 registers without spilling ([ADA] "Where
-// the registers went").
+// other wave's MFMAs, and each wave's fp32 accumulators, operand fragments
+// and block temporaries fit its 256 registers without spilling ([ADA]
+// "Where the registers went").
 //
 // Per 128-K block and 16x16 tile: one FP8 MFMA 16x16x128 with a zero
 // accumulator gives the block partial P, and one fp32 FMA per output applies
@@ -18,13 +18,20 @@
 //
 // Data movement: global -> LDS with direct-to-LDS 16-byte buffer loads
 // (buffer_load_dwordx4 ... lds; the lane at LDS granule p fetches whichever
-// global 16 bytes belong there), two LDS stages of 65 KB, so block kb+1 is in
-// flight while block kb is multiplied; one barrier per block.  LDS rows are
-// 128 bytes (eight 16-byte chunks); chunk c of row r is stored at chunk
-// position c ^ (r & 7), which makes the MFMA fragment reads (16 rows, same
-// chunk) conflict-free.  Fragment K order: MFMA K slot g (lanes 16g..16g+15)
-// takes chunks g and g + 4 of the row, the same for both operands, so the
-// contraction is over the same 128 K values.
+// global 16 bytes belong there), two or three LDS stages, one barrier per
+// block.  LDS rows are 128 bytes (eight 16-byte chunks); chunk c of row r is
+// stored at chunk position c ^ (r & 7), which makes the MFMA fragment reads
+// (16 rows, same chunk) conflict-free.  Fragment K order: MFMA K slot g
+// (lanes 16g..16g+15) takes chunks g and g + 4 of the row, the same for both
+// operands, so the contraction is over the same 128 K values.
+//
+// Tile shapes ([ADA] "One tile doesn't fit all M"): the largest of 256x256
+// and 128x128 that still gives at least one workgroup per CU; below that,
+// 64x128 (or 128x64 for M <= 64) with K split over several workgroups so
+// that about one workgroup per CU exists.  Split partial tiles go to the
+// workspace in fp32 and the last workgroup of a tile sums them in split
+// order (no float atomics, identical from run to run), with the same
+// fence-free hand-off as the streaming kernels.
 
 #include "bfp8_device.hpp"
 #include "bfp8_launch.hpp"
@@ -33,52 +40,75 @@ namespace bfp8 {
 
 namespace {
 
-constexpr int kBN = 256;                  // weight rows per workgroup
-constexpr int kBM = 256;                  // tokens per workgroup
-constexpr int kWavesN = 2, kWavesM = 4;   // eight waves, two per SIMD
-constexpr int kWaves = kWavesN * kWavesM;
-constexpr int kThreads = kWaves * kWave;
-constexpr int kWaveN = kBN / kWavesN, kWaveM = kBM / kWavesM;   // per-wave tile
-constexpr int kTi = kWaveN / 16, kTj = kWaveM / 16;
-constexpr int kRowBytes = 128;            // one 128-K block of one row
-constexpr int kStageA = kBN * kRowBytes;
-constexpr int kStageB = kBM * kRowBytes;
-constexpr int kRowsPerLoad = kWave * 16 / kRowBytes;                        // 8 rows per load instruction
-constexpr int kLoadsPerWave = (kBN + kBM) / (kRowsPerLoad * kWaves);        // tile loads per wave per stage
-constexpr int kLoadsA = kBN / (kRowsPerLoad * kWaves);                      // of which weight rows
-constexpr int kXsLanes = kBM / kWaves;    // token scales loaded per wave
-constexpr int kStageXs = kBM * 4;         // token scales of the block, fp32
-constexpr int kStageWs = kWaves * 4;      // one weight scale per wave, fp32
-constexpr int kOffXs = kStageA + kStageB;
-constexpr int kOffWs = kOffXs + kStageXs;
-constexpr int kStageBytes = kOffWs + kStageWs;
-constexpr int kStageStride = (kStageBytes + 1023) / 1024 * 1024;
-// Two LDS stages: while block kb is multiplied out of one, block kb+1 lands
-// in the other.
-constexpr int kStages = 2;
-// Vector-memory operations one stage adds per wave: tile loads, the token
-// scales and the weight scale.
-constexpr int kVmemPerStage = kLoadsPerWave + 2;
-static_assert(kStages * kStageStride <= 160 * 1024, "LDS budget");
-static_assert((kBN + kBM) % (kRowsPerLoad * kWaves) == 0 && kBN % (kRowsPerLoad * kWaves) == 0, "load split");
-static_assert(kXsLanes <= kWave && kWaveN % 128 == 0 || 128 % kWaveN == 0, "one weight-scale row per wave");
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-typedef __attribute__((address_space(3))) void lds_void;
+constexpr int kRowBytes = 128;                          // one 128-K block of one row
+constexpr int kRowsPerLoad = kWave * 16 / kRowBytes;    // 8 rows per 16-byte load instruction
+constexpr int kCUs = 256;
+
+template <int BN_, int BM_, int WAVES_N, int WAVES_M, bool SPLIT>
+struct TileCfg {
+    static constexpr int BN = BN_, BM = BM_;
+    static constexpr bool kSplit = SPLIT;           // plans for this shape may split K
+    static constexpr int kWavesN = WAVES_N, kWavesM = WAVES_M;
+    static constexpr int kWaves = kWavesN * kWavesM;
+    static constexpr int kThreads = kWaves * kWave;
+    static constexpr int kWaveN = BN / kWavesN, kWaveM = BM / kWavesM;   // per-wave tile
+    static constexpr int kTi = kWaveN / 16, kTj = kWaveM / 16;
+    static constexpr int kStageA = BN * kRowBytes;
+    static constexpr int kStageB = BM * kRowBytes;
+    static constexpr int kLoadsPerWave = (BN + BM) / (kRowsPerLoad * kWaves);   // tile loads per wave per stage
+    static constexpr int kLoadsA = BN / (kRowsPerLoad * kWaves);               // of which weight rows
+    static constexpr int kXsLanes = BM / kWaves;                               // token scales per wave
+    static constexpr int kOffXs = kStageA + kStageB;
+    static constexpr int kOffWs = kOffXs + BM * 4;
+    static constexpr int kStageBytes = kOffWs + kWaves * 4;
+    static constexpr int kStageStride = (kStageBytes + 1023) / 1024 * 1024;
+    // As many LDS stages as fit, up to six: blocks kb+1 .. kb+S-1 are in
+    // flight while block kb is multiplied.  The small tiles are bound by
+    // memory latency rather than by the matrix core, so they need the deep
+    // prefetch to keep enough bytes in flight per CU.
+    static constexpr int kStages = (160 * 1024 - 256) / kStageStride < 6 ? (160 * 1024 - 256) / kStageStride : 6;
+    // Vector-memory instructions one stage adds per wave: tile loads, the
+    // token scales and the weight scale.
+    static constexpr int kVmemPerStage = kLoadsPerWave + 2;
+    static_assert(kStages * kStageStride <= 160 * 1024, "LDS budget");
+    static_assert(BN % (kRowsPerLoad * kWaves) == 0 && BM % (kRowsPerLoad * kWaves) == 0, "load split");
+    static_assert(kXsLanes >= 1 && kXsLanes <= kWave, "token-scale loads");
+    static_assert(128 % kWaveN == 0 || kWaveN % 128 == 0, "one weight-scale row per wave");
+    static_assert(kTi >= 1 && kTj >= 1 && kStages >= 2 && (kStages - 2) * kVmemPerStage < 64, "wave tile");
+};
+
+using Cfg256 = TileCfg<256, 256, 2, 4, false>;    // wave tile 128 n x 64 m, 2 stages
+using Cfg128 = TileCfg<128, 128, 2, 4, false>;    // 64 x 32, 4 stages
+using Cfg64x128 = TileCfg<64, 128, 2, 4, true>;   // 32 x 32, 6 stages
+using Cfg128x64 = TileCfg<128, 64, 4, 2, true>;   // 32 x 32, 6 stages
+
+// s_waitcnt vmcnt(N) lgkmcnt(0) (expcnt not waited for).
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
+}
+
+// Wait until at most `younger` stages of this wave's loads are outstanding
+// (each stage is C::kVmemPerStage instructions and loads retire in issue
+// order), and for all of its LDS reads.
+template <class C, int Y = C::kStages - 2>
+__device__ __forceinline__ void wait_stage(int younger) {
+    if constexpr (Y == 0) {
+        wait_vm_lgkm0<0>();
+    } else {
+        if (younger >= Y) wait_vm_lgkm0<Y * C::kVmemPerStage>();
+        else wait_stage<C, Y - 1>(younger);
+    }
+}
 
 // Byte offset in a stage of (row, 16-byte chunk c) after the XOR swizzle.
 __device__ __forceinline__ int swz(int row, int c) { return row * kRowBytes + ((c ^ (row & 7)) << 4); }
 
-// Issue this wave's direct-to-LDS loads of K block kb into a stage.
-// Instruction q of wave w fills LDS rows 8*(W q + w) .. +7 of the stage (W =
-// waves; weight rows first, then token rows); lane l fills granule l of those
-// 1 KB, i.e. row 8*(W q + w) + l/8 at chunk position l%8, so it fetches
-// logical chunk (l%8) ^ (l/8) of that row.  The lane's byte offset inside the
-// tile is the same for every q up to q * 8W rows, which goes into the scalar
-// offset together with the K block.  Rows past the end of the matrix lie
-// outside the buffer descriptor's range and load as zeros.
-// A raw buffer descriptor (gfx9: dword 3 = 0x00020000, untyped 32-bit
-// data; offsets at or past num_records read as zero), kept in SGPRs.
-typedef int i32x4 __attribute__((ext_vector_type(4)));
+// A raw buffer descriptor (gfx9: dword 3 = 0x00020000, untyped 32-bit data;
+// a lane whose offset lies at or past num_records reads zero), in SGPRs.
 __device__ __forceinline__ i32x4 buffer_rsrc(const void* base, uint32_t num_records) {
     const uint64_t a = reinterpret_cast<uint64_t>(base);
     i32x4 r = {(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xFFFFu), (int)num_records, 0x00020000};
@@ -95,7 +125,7 @@ __device__ __forceinline__ uint32_t lds_address(const void* p) {
 // Direct-to-LDS buffer loads, issued as inline assembly: the data goes to LDS
 // at M0 + 16 * lane (4 * lane for the dword form) and is waited for with
 // explicit vmcnt waits.  Written as asm so that the compiler's own wait
-// insertion, which cannot tell the two LDS stages apart, does not drain the
+// insertion, which cannot tell the LDS stages apart, does not drain the
 // prefetch before every LDS read.
 __device__ __forceinline__ void dma16(uint32_t lds, i32x4 rsrc, int voff, int soff) {
     asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds"
@@ -106,36 +136,44 @@ __device__ __forceinline__ void dma4(uint32_t lds, i32x4 rsrc, int voff, int sof
                  :: "v"(voff), "s"(rsrc), "s"(lds), "s"(soff) : "memory");
 }
 
+// Issue this wave's direct-to-LDS loads of K block kb into a stage.
+// Instruction q of wave w fills LDS rows 8*(W q + w) .. +7 of the stage (W =
+// waves; weight rows first, then token rows); lane l fills granule l of those
+// 1 KB, i.e. row 8*(W q + w) + l/8 at chunk position l%8, so it fetches
+// logical chunk (l%8) ^ (l/8) of that row.  The row offset goes into the
+// per-lane offset, which the descriptor's range check sees, so rows past the
+// end of the matrix load as zeros; the K block's byte offset (< K, so it
+// never carries a valid row's access past its own row) goes into the scalar
+// offset.
+template <class C>
 __device__ __forceinline__ void issue_stage(uint8_t* stage, i32x4 rsrc_a, i32x4 rsrc_b, i32x4 rsrc_xs,
-                                            i32x4 rsrc_ws, int lane_off, int xs_off, int64_t K, int64_t kb,
+                                            i32x4 rsrc_ws, int lane_off, int q_stride, int xs_off, int64_t kb,
                                             int wave, int lane) {
-    const int k_off = (int)(kb * kRowBytes);
+    const int k_off = __builtin_amdgcn_readfirstlane((int)(kb * kRowBytes));
     const uint32_t base = lds_address(stage);
 #pragma unroll
-    for (int q = 0; q < kLoadsPerWave; ++q) {
-        const uint32_t lds = __builtin_amdgcn_readfirstlane(base + kRowsPerLoad * (kWaves * q + wave) * kRowBytes);
-        if (q < kLoadsA) {
-            dma16(lds, rsrc_a, lane_off,
-                  __builtin_amdgcn_readfirstlane(k_off + (int)(kRowsPerLoad * kWaves * q * K)));
+    for (int q = 0; q < C::kLoadsPerWave; ++q) {
+        const uint32_t lds = __builtin_amdgcn_readfirstlane(base + kRowsPerLoad * (C::kWaves * q + wave) * kRowBytes);
+        if (q < C::kLoadsA) {
+            dma16(lds, rsrc_a, lane_off + q * q_stride, k_off);
         } else {
-            dma16(lds, rsrc_b, lane_off,
-                  __builtin_amdgcn_readfirstlane(k_off + (int)(kRowsPerLoad * kWaves * (q - kLoadsA) * K)));
+            dma16(lds, rsrc_b, lane_off + (q - C::kLoadsA) * q_stride, k_off);
         }
     }
     // Token scales xs[m0 + kXsLanes * w + l, kb], lanes l < kXsLanes only (the
     // dword form writes M0 + 4 * lane for every active lane).
-    if (lane < kXsLanes)
-        dma4(__builtin_amdgcn_readfirstlane(base + kOffXs + 4 * kXsLanes * wave), rsrc_xs, xs_off,
+    if (lane < C::kXsLanes)
+        dma4(__builtin_amdgcn_readfirstlane(base + C::kOffXs + 4 * C::kXsLanes * wave), rsrc_xs, xs_off,
              __builtin_amdgcn_readfirstlane((int)(kb * 4)));
     // This wave's weight scale ws[nb, kb], lane 0 only.
     if (lane == 0)
-        dma4(__builtin_amdgcn_readfirstlane(base + kOffWs + 4 * wave), rsrc_ws, 0,
+        dma4(__builtin_amdgcn_readfirstlane(base + C::kOffWs + 4 * wave), rsrc_ws, 0,
              __builtin_amdgcn_readfirstlane((int)(kb * 4)));
 }
 
 // Workgroup barrier without the memory fence of __syncthreads(): that fence
 // would wait for every outstanding direct-to-LDS load, including the
-// prefetch of the next stage.  Visibility is handled by explicit counter
+// prefetch of the next stages.  Visibility is handled by explicit counter
 // waits instead (own stage loads complete before the barrier; own LDS reads
 // complete before the barrier that frees a stage for reuse); the empty asm
 // statements keep the compiler from moving memory accesses across it.
@@ -151,15 +189,17 @@ __device__ __forceinline__ i32x8 read_frag(const uint8_t* stage, int row, int g)
     return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-__device__ __forceinline__ void tile_of_block(int64_t bid, int64_t tiles_n, int64_t tiles_m,
-                                              int64_t& tn, int64_t& tm) {
-    // Workgroups are dealt round-robin to the 8 XCDs.  Give each XCD a
-    // contiguous run of tile indices, and walk tiles in groups of 8 token
-    // tiles per weight tile, so the workgroups resident on one XCD share
-    // weight and token rows in that XCD's L2.
-    const int64_t total = tiles_n * tiles_m;
-    int64_t t = bid;
-    if (total % 8 == 0) t = (bid % 8) * (total / 8) + bid / 8;
+// Workgroup -> (tile, split).  Workgroups are dealt round-robin to the 8
+// XCDs; each XCD gets a contiguous run of indices, in which the splits of a
+// tile are adjacent and tiles come in groups of up to 8 token tiles per
+// weight tile, so the workgroups resident on one XCD share weight and token
+// rows in that XCD's L2.
+__device__ __forceinline__ void tile_of_block(int64_t b, int64_t tiles_n, int64_t tiles_m, int64_t splits,
+                                              int64_t& t, int64_t& split, int64_t& tn, int64_t& tm) {
+    const int64_t total = tiles_n * tiles_m * splits;
+    if (total % 8 == 0) b = (b % 8) * (total / 8) + b / 8;
+    split = b % splits;
+    t = b / splits;
     constexpr int64_t kGroup = 8;
     const int64_t per_group = kGroup * tiles_n;
     const int64_t group = t / per_group;
@@ -170,47 +210,69 @@ __device__ __forceinline__ void tile_of_block(int64_t bid, int64_t tiles_n, int6
     tn = in_group / group_m;
 }
 
+__device__ __forceinline__ void store4(void* y, int y_dtype, int64_t idx, f32x4 v) {
+    if (y_dtype == 2) {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(y) + idx) = v;
+    } else {
+        uint32_t h[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) h[e] = y_dtype == 0 ? float_to_bf16_bits(v[e]) : float_to_f16_bits(v[e]);
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + idx) =
+            make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+    }
+}
+
 }  // namespace
 
-__global__ __launch_bounds__(kThreads, 1) void w8a8_tile_kernel(
+// Grid: tiles_n * tiles_m * splits workgroups.  Split s of a tile covers K
+// blocks [s * kb_per_split, min(KB, (s + 1) * kb_per_split)).  With splits
+// > 1, `partials` holds splits fp32 BN x BM tiles per output tile and
+// `counters` one uint32 per output tile (zero on entry, re-armed on exit).
+template <class C>
+__global__ __launch_bounds__(C::kThreads, 1) void w8a8_tile_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ xs,
     const uint8_t* __restrict__ wq, const float* __restrict__ ws,
     void* __restrict__ y, int y_dtype, int64_t M, int64_t N, int64_t K,
-    int64_t tiles_n, int64_t tiles_m) {
-    __shared__ __attribute__((aligned(1024))) uint8_t stages[kStages * kStageStride];
+    int64_t tiles_n, int64_t tiles_m, int64_t splits, int64_t kb_per_split,
+    float* __restrict__ partials, uint32_t* __restrict__ counters) {
+    __shared__ __attribute__((aligned(1024))) uint8_t stages[C::kStages * C::kStageStride];
+    __shared__ uint32_t arrived;
 
-    int64_t tn, tm;
-    tile_of_block(blockIdx.x, tiles_n, tiles_m, tn, tm);
-    const int64_t n0 = tn * kBN, m0 = tm * kBM;
+    int64_t t, split, tn, tm;
+    tile_of_block(blockIdx.x, tiles_n, tiles_m, splits, t, split, tn, tm);
+    const int64_t n0 = tn * C::BN, m0 = tm * C::BM;
     const int64_t KB = K / 128, NB = (N + 127) / 128;
+    const int64_t kb0 = split * kb_per_split;
+    const int64_t nkb = KB - kb0 < kb_per_split ? KB - kb0 : kb_per_split;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
-    const int wn = wave % kWavesN, wm = wave / kWavesN;
+    const int wn = wave % C::kWavesN, wm = wave / C::kWavesN;
     const int r = lane & 15, g = lane >> 4;
 
     // Buffer descriptors over this workgroup's weight rows, token rows and
     // token-scale rows; rows past N or M lie outside them and load as zeros.
-    const int64_t rows_a = N - n0 < kBN ? N - n0 : kBN;
-    const int64_t rows_b = M - m0 < kBM ? M - m0 : kBM;
+    const int64_t rows_a = N - n0 < C::BN ? N - n0 : C::BN;
+    const int64_t rows_b = M - m0 < C::BM ? M - m0 : C::BM;
     const i32x4 rsrc_a = buffer_rsrc(wq + n0 * K, (uint32_t)(rows_a * K));
     const i32x4 rsrc_b = buffer_rsrc(xq + m0 * K, (uint32_t)(rows_b * K));
     const i32x4 rsrc_xs = buffer_rsrc(xs + m0 * KB, (uint32_t)(rows_b * KB * 4));
     const int lane_off = (int)((8 * wave + (lane >> 3)) * K) + ((((lane & 7) ^ ((lane >> 3) & 7))) << 4);
-    const int xs_off = (int)((kXsLanes * wave + lane) * KB * 4);
+    const int q_stride = (int)(kRowsPerLoad * C::kWaves * K);
+    const int xs_off = (int)((C::kXsLanes * wave + lane) * KB * 4);
 
-    // Weight scales: one row of ws per wave (its 128 weight rows share it).
-    int64_t nb = (n0 + kWaveN * wn) / 128;
+    // Weight scales: one row of ws per wave (its weight rows share it).
+    int64_t nb = (n0 + C::kWaveN * wn) / 128;
     nb = nb < NB ? nb : NB - 1;
     const i32x4 rsrc_ws = buffer_rsrc(ws + nb * KB, (uint32_t)(KB * 4));
 
-    f32x4 acc[kTi][kTj];
+    f32x4 acc[C::kTi][C::kTj];
 #pragma unroll
-    for (int i = 0; i < kTi; ++i)
+    for (int i = 0; i < C::kTi; ++i)
 #pragma unroll
-        for (int j = 0; j < kTj; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int j = 0; j < C::kTj; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
 
-    const int a_row0 = kWaveN * wn + r;           // + 16 i
-    const int b_row0 = kBN + kWaveM * wm + r;     // + 16 j
+    const int a_row0 = C::kWaveN * wn + r;           // + 16 i
+    const int b_row0 = C::BN + C::kWaveM * wm + r;   // + 16 j
 
     // Per block, per wave: kTi rows of kTj MFMAs (one per 16x16 tile) into
     // block temporaries; the FMAs that promote row i are issued after row
@@ -218,78 +280,220 @@ __global__ __launch_bounds__(kThreads, 1) void w8a8_tile_kernel(
     // The token fragments and the scales of the block are read first; the
     // weight fragments are streamed one row ahead.
     auto compute = [&](const uint8_t* stage) {
-        const float wsc = reinterpret_cast<const float*>(stage + kOffWs)[wave];
-        const float* xs_lds = reinterpret_cast<const float*>(stage + kOffXs);
-        float sc[kTj];
+        const float wsc = reinterpret_cast<const float*>(stage + C::kOffWs)[wave];
+        const float* xs_lds = reinterpret_cast<const float*>(stage + C::kOffXs);
+        float sc[C::kTj];
 #pragma unroll
-        for (int j = 0; j < kTj; ++j) sc[j] = xs_lds[kWaveM * wm + 16 * j + r] * wsc;
-        i32x8 bf[kTj];
+        for (int j = 0; j < C::kTj; ++j) sc[j] = xs_lds[C::kWaveM * wm + 16 * j + r] * wsc;
+        i32x8 bf[C::kTj];
 #pragma unroll
-        for (int j = 0; j < kTj; ++j) bf[j] = read_frag(stage, b_row0 + 16 * j, g);
-        f32x4 tmp[2][kTj];
+        for (int j = 0; j < C::kTj; ++j) bf[j] = read_frag(stage, b_row0 + 16 * j, g);
+        f32x4 tmp[2][C::kTj];
         i32x8 af = read_frag(stage, a_row0, g);
 #pragma unroll
-        for (int i = 0; i < kTi; ++i) {
+        for (int i = 0; i < C::kTi; ++i) {
             const int c = i & 1;
 #pragma unroll
-            for (int j = 0; j < kTj; ++j) tmp[c][j] = mfma_e4m3_16x16x128(af, bf[j], zero);
-            if (i + 1 < kTi) af = read_frag(stage, a_row0 + 16 * (i + 1), g);
+            for (int j = 0; j < C::kTj; ++j) tmp[c][j] = mfma_e4m3_16x16x128(af, bf[j], zero);
+            if (i + 1 < C::kTi) af = read_frag(stage, a_row0 + 16 * (i + 1), g);
             if (i > 0) {
 #pragma unroll
-                for (int j = 0; j < kTj; ++j)
+                for (int j = 0; j < C::kTj; ++j)
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
                         acc[i - 1][j][e] = __builtin_fmaf(tmp[c ^ 1][j][e], sc[j], acc[i - 1][j][e]);
             }
         }
 #pragma unroll
-        for (int j = 0; j < kTj; ++j)
+        for (int j = 0; j < C::kTj; ++j)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                acc[kTi - 1][j][e] = __builtin_fmaf(tmp[(kTi - 1) & 1][j][e], sc[j], acc[kTi - 1][j][e]);
+                acc[C::kTi - 1][j][e] = __builtin_fmaf(tmp[(C::kTi - 1) & 1][j][e], sc[j], acc[C::kTi - 1][j][e]);
     };
 
-    auto stage = [&](int64_t kb) { return stages + (int)(kb % kStages) * kStageStride; };
-    issue_stage(stage(0), rsrc_a, rsrc_b, rsrc_xs, rsrc_ws, lane_off, xs_off, K, 0, wave, lane);
-    for (int64_t kb = 0; kb < KB; ++kb) {
-        // This wave's loads of block kb and its LDS reads of block kb-1 are
-        // done; after the barrier every wave's block kb is in LDS and nobody
-        // reads block kb-1's stage, which then receives block kb+1.
-        __builtin_amdgcn_s_waitcnt(0x7 << 4);                  // vmcnt(0), lgkmcnt(0)
+    auto stage = [&](int64_t b) { return stages + (int)(b % C::kStages) * C::kStageStride; };
+    // Prologue: the first S-1 blocks in flight.
+#pragma unroll
+    for (int p = 0; p + 1 < C::kStages; ++p)
+        if (p < nkb)
+            issue_stage<C>(stage(p), rsrc_a, rsrc_b, rsrc_xs, rsrc_ws, lane_off, q_stride, xs_off, kb0 + p, wave,
+                           lane);
+    for (int64_t b = 0; b < nkb; ++b) {
+        // This wave's loads of block b are done (those of the younger blocks
+        // b+1 .. b+S-2 that exist may stay in flight), and so are its LDS
+        // reads of block b-1.  After the barrier every wave's block b is in
+        // LDS and no wave reads the stage of block b-1, which receives block
+        // b+S-1.
+        const int64_t left = nkb - 1 - b;
+        wait_stage<C>(left < C::kStages - 2 ? (int)left : C::kStages - 2);
         stage_barrier();
-        if (kb + 1 < KB)
-            issue_stage(stage(kb + 1), rsrc_a, rsrc_b, rsrc_xs, rsrc_ws, lane_off, xs_off, K, kb + 1, wave, lane);
-        compute(stage(kb));
+        if (b + C::kStages - 1 < nkb)
+            issue_stage<C>(stage(b + C::kStages - 1), rsrc_a, rsrc_b, rsrc_xs, rsrc_ws, lane_off, q_stride, xs_off,
+                           kb0 + b + C::kStages - 1, wave, lane);
+        compute(stage(b));
     }
 
-    // Epilogue: lane holds n = n0 + 128 wn + 16 i + 4 g + e (e = 0..3) of token m.
+    // The lane holds n = n0 + kWaveN wn + 16 i + 4 g + e (e = 0..3) of token
+    // m = m0 + kWaveM wm + 16 j + r.
+    const int nl0 = C::kWaveN * wn + 4 * g, ml0 = C::kWaveM * wm + r;
+    if (splits == 1) {
 #pragma unroll
-    for (int j = 0; j < kTj; ++j) {
-        const int64_t m = m0 + kWaveM * wm + 16 * j + r;
-        if (m >= M) continue;
+        for (int j = 0; j < C::kTj; ++j) {
+            const int64_t m = m0 + ml0 + 16 * j;
+            if (m >= M) continue;
 #pragma unroll
-        for (int i = 0; i < kTi; ++i) {
-            const int64_t n = n0 + kWaveN * wn + 16 * i + 4 * g;
-            if (n >= N) continue;
-            const f32x4 v = acc[i][j];
-            if (y_dtype == 2) {
-                *reinterpret_cast<f32x4*>(static_cast<float*>(y) + m * N + n) = v;
-            } else {
-                uint32_t h[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) h[e] = y_dtype == 0 ? float_to_bf16_bits(v[e]) : float_to_f16_bits(v[e]);
-                *reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + m * N + n) =
-                    make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+            for (int i = 0; i < C::kTi; ++i) {
+                const int64_t n = n0 + nl0 + 16 * i;
+                if (n < N) store4(y, y_dtype, m * N + n, acc[i][j]);
             }
         }
+        return;
+    }
+
+    if constexpr (C::kSplit) {
+        // Split K.  Every workgroup of a tile has the same thread -> output
+        // mapping, so a split's partial tile is kept in thread order: slot
+        // (i, j) of thread x at ((split * kSlots + i * kTj + j) * kThreads +
+        // x) * 16 bytes, one contiguous KB per wave and slot.  The slots are
+        // written with 16-byte agent-coherent (sc1) stores, which write
+        // through to memory every XCD sees; after they complete (vmcnt 0) and
+        // the workgroup barrier, one thread counts the arrival on a
+        // device-scope atomic.  The last workgroup reads every split with
+        // 16-byte agent-coherent loads, four splits per round trip, and sums
+        // them in split order.
+        constexpr int kSlots = C::kTi * C::kTj;
+        constexpr int kChunk = 4;
+        constexpr int kSc1 = 16;                      // cache-policy bit: device-coherent access
+        float* tile_parts = partials + t * splits * (C::BN * C::BM);
+        const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
+            tile_parts, 0, (int)(splits * C::BN * C::BM * 4), 0x00020000);
+        auto slot_off = [&](int64_t s, int slot) {
+            return (int)(((s * kSlots + slot) * C::kThreads + threadIdx.x) * 16);
+        };
+#pragma unroll
+        for (int i = 0; i < C::kTi; ++i)
+#pragma unroll
+            for (int j = 0; j < C::kTj; ++j)
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, acc[i][j]), prs,
+                                                       slot_off(split, i * C::kTj + j), 0, kSc1);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (threadIdx.x == 0)
+            arrived = __hip_atomic_fetch_add(&counters[t], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        if (arrived != (uint32_t)(splits - 1)) return;
+
+#pragma unroll
+        for (int i = 0; i < C::kTi; ++i)
+#pragma unroll
+            for (int j = 0; j < C::kTj; ++j) acc[i][j] = zero;
+        for (int64_t s0 = 0; s0 < splits; s0 += kChunk) {
+            i32x4 v[kChunk][kSlots];
+#pragma unroll
+            for (int u = 0; u < kChunk; ++u) {
+                if (s0 + u >= splits) continue;
+#pragma unroll
+                for (int slot = 0; slot < kSlots; ++slot)
+                    v[u][slot] = __builtin_amdgcn_raw_buffer_load_b128(prs, slot_off(s0 + u, slot), 0, kSc1);
+            }
+#pragma unroll
+            for (int u = 0; u < kChunk; ++u) {
+                if (s0 + u >= splits) continue;
+#pragma unroll
+                for (int i = 0; i < C::kTi; ++i)
+#pragma unroll
+                    for (int j = 0; j < C::kTj; ++j) acc[i][j] += __builtin_bit_cast(f32x4, v[u][i * C::kTj + j]);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < C::kTj; ++j) {
+            const int64_t m = m0 + ml0 + 16 * j;
+#pragma unroll
+            for (int i = 0; i < C::kTi; ++i) {
+                const int64_t n = n0 + nl0 + 16 * i;
+                if (m < M && n < N) store4(y, y_dtype, m * N + n, acc[i][j]);
+            }
+        }
+        if (threadIdx.x == 0) __hip_atomic_store(&counters[t], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
+namespace {
+
+enum class TileShape { k256, k128, k64x128, k128x64 };
+
+struct TilePlan {
+    TileShape shape;
+    int64_t bn, bm, tiles_n, tiles_m, splits, kb_per_split;
+};
+
+TilePlan make_plan(TileShape s, int64_t bn, int64_t bm, int64_t M, int64_t N, int64_t K) {
+    TilePlan p{s, bn, bm, (N + bn - 1) / bn, (M + bm - 1) / bm, 1, 0};
+    const int64_t KB = K / 128;
+    int64_t splits = 1;
+    if (s == TileShape::k64x128 || s == TileShape::k128x64) {
+        // About one workgroup per CU, each with at least 4 K blocks.
+        while (p.tiles_n * p.tiles_m * splits < kCUs && KB / (splits * 2) >= 4) splits *= 2;
+    }
+    p.kb_per_split = (KB + splits - 1) / splits;
+    p.splits = (KB + p.kb_per_split - 1) / p.kb_per_split;
+    return p;
+}
+
+TilePlan plan_tile(int64_t M, int64_t N, int64_t K) {
+    const TilePlan big = make_plan(TileShape::k256, 256, 256, M, N, K);
+    if (big.tiles_n * big.tiles_m >= kCUs) return big;
+    const TilePlan mid = make_plan(TileShape::k128, 128, 128, M, N, K);
+    if (mid.tiles_n * mid.tiles_m >= kCUs) return mid;
+    if (M <= 64) return make_plan(TileShape::k128x64, 128, 64, M, N, K);
+    return make_plan(TileShape::k64x128, 64, 128, M, N, K);
+}
+
+size_t counter_bytes(const TilePlan& p) {
+    return ((size_t)(p.tiles_n * p.tiles_m) * sizeof(uint32_t) + 255) / 256 * 256;
+}
+
+template <class C>
+void launch(const TilePlan& p, const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws, void* y,
+            int y_dtype, int64_t M, int64_t N, int64_t K, float* partials, uint32_t* counters,
+            hipStream_t stream) {
+    const dim3 grid((unsigned)(p.tiles_n * p.tiles_m * p.splits));
+    hipLaunchKernelGGL(w8a8_tile_kernel<C>, grid, dim3(C::kThreads), 0, stream, xq, xs, wq, ws, y, y_dtype, M, N,
+                       K, p.tiles_n, p.tiles_m, p.splits, p.kb_per_split, partials, counters);
+}
+
+}  // namespace
+
+size_t tile_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    const TilePlan p = plan_tile(M, N, K);
+    if (p.splits == 1) return 0;
+    return counter_bytes(p) + (size_t)(p.tiles_n * p.tiles_m * p.splits * p.bn * p.bm) * sizeof(float);
+}
+
 hipError_t launch_w8a8_tile(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
-                            void* y, int y_dtype, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
-    const int64_t tiles_n = (N + kBN - 1) / kBN, tiles_m = (M + kBM - 1) / kBM;
-    hipLaunchKernelGGL(w8a8_tile_kernel, dim3((unsigned)(tiles_n * tiles_m)), dim3(kThreads), 0, stream,
-                       xq, xs, wq, ws, y, y_dtype, M, N, K, tiles_n, tiles_m);
+                            void* y, int y_dtype, int64_t M, int64_t N, int64_t K, void* workspace,
+                            hipStream_t stream) {
+    const TilePlan p = plan_tile(M, N, K);
+    uint32_t* counters = nullptr;
+    float* partials = nullptr;
+    if (p.splits > 1) {
+        counters = static_cast<uint32_t*>(workspace);
+        partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + counter_bytes(p));
+    }
+    switch (p.shape) {
+        case TileShape::k256:
+            launch<Cfg256>(p, xq, xs, wq, ws, y, y_dtype, M, N, K, partials, counters, stream);
+            break;
+        case TileShape::k128:
+            launch<Cfg128>(p, xq, xs, wq, ws, y, y_dtype, M, N, K, partials, counters, stream);
+            break;
+        case TileShape::k64x128:
+            launch<Cfg64x128>(p, xq, xs, wq, ws, y, y_dtype, M, N, K, partials, counters, stream);
+            break;
+        case TileShape::k128x64:
+            launch<Cfg128x64>(p, xq, xs, wq, ws, y, y_dtype, M, N, K, partials, counters, stream);
+            break;
+    }
     return hipGetLastError();
 }
 

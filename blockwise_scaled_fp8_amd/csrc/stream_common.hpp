@@ -91,9 +91,20 @@ __device__ __forceinline__ void stream_finish(f32x4 acc, float* red, void* y, in
     if (arrived != (uint32_t)(splits - 1)) return;   // not the last workgroup of this tile
 
     if (t < 256) {
+        // Sum in split order; the loads of eight splits are issued together
+        // before any is added (one memory round trip per eight splits).
+        constexpr int kChunk = 8;
         float s = 0.0f;
-        for (int64_t k = 0; k < splits; ++k)
-            s += __hip_atomic_load(&my_tiles[k * 256 + t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int64_t k0 = 0; k0 < splits; k0 += kChunk) {
+            float p[kChunk];
+#pragma unroll
+            for (int u = 0; u < kChunk; ++u)
+                if (k0 + u < splits)
+                    p[u] = __hip_atomic_load(&my_tiles[(k0 + u) * 256 + t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+            for (int u = 0; u < kChunk; ++u)
+                if (k0 + u < splits) s += p[u];
+        }
         if (m < M) store_out(y, y_dtype, m * N + n, s);
     }
     if (t == 0) __hip_atomic_store(&counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // re-arm

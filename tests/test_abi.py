@@ -67,7 +67,11 @@ def test_workspace_sizes(lib):
     # o_proj decode needs no split-K; a narrow projection does
     assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 1, 4096, 4096) == 0
     assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 1, 1024, 4096) > 0
-    assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 4096, 1024, 4096) == 0   # tiled kernel
+    assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 4096, 1024, 4096) == 0   # 128x128 tiles
+    assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 4096, 4096, 4096) == 0   # 256x256 tiles
+    # mid M: 64-token tiles, K split 8 ways -> counters + 8 fp32 partial tiles per output tile
+    assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 64, 4096, 4096) == 256 + 32 * 8 * 128 * 64 * 4
+    assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 64, 384, 640) == 0      # K too short to split
     assert bfp8.bfp8_workspace_bytes(bfp8.OP_QUANT_ACT_1X128, 1, 4096, 4096) == 0
 
 
@@ -110,6 +114,7 @@ def _w8a8(M=4, N=512, K=512, y_dtype=0, xq=A, ws_ptr=C, y=Y, workspace=None, wby
     (dict(y=MISALIGNED), 4),
     (dict(M=1, N=1024, K=4096), 5),                   # split-K plan needs a workspace
     (dict(M=64, N=256, K=(1 << 23) + 128), 2),        # tiled kernel's K limit
+    (dict(M=100, N=1024, K=4096), 5),                 # mid-M split-K plan needs a workspace
 ])
 def test_w8a8_validation(lib, kw, expect):
     assert lib.bfp8_gemm_w8a8_blk128(*_w8a8(**kw)) == expect

@@ -72,6 +72,43 @@ def test_w8a8_split_k_narrow_projection(gpu_lib, M):
     assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
 
 
+@pytest.mark.parametrize("M,N,K,shape", [
+    (40, 1024, 4096, "128x64, 8 splits"),
+    (100, 1024, 4096, "64x128, 8 splits"),
+    (200, 2048, 2176, "64x128, 4 splits, last split shorter"),
+    (300, 1040, 1024, "64x128, 2 splits, ragged N"),
+    (1000, 4096, 1024, "128x128"),
+])
+def test_w8a8_tile_shapes_and_split_k(gpu_lib, M, N, K, shape):
+    """Every tiled configuration, with ragged M and N tiles and split K; the
+    split plans run twice on one workspace (counters re-arm) and must repeat
+    bit for bit."""
+    say("w8a8 tile", shape, f"M={M} N={N} K={K}")
+    xq, xs, wq, ws = _w8a8_inputs(M, N, K, 700 + M)
+    y0 = oracle.gemm_w8a8_blk128(xq, xs, wq, ws)
+    d = [dev(a) for a in (xq, xs, wq, ws)]
+    wsb = workspace(bfp8.OP_GEMM_W8A8_BLK128, M, N, K)
+    assert (wsb is not None) == ("split" in shape)
+    y1 = run_w8a8(*d, torch.float32, wsb)
+    assert_fp32_bar(y1, y0, f"tile {shape}")
+    y16 = run_w8a8(*d, torch.bfloat16, wsb)
+    assert_16bit_bar(y16, y1, y0, "bf16", f"tile {shape}")
+    y2 = run_w8a8(*d, torch.float32, wsb)
+    assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
+
+
+def test_w8a8_large_tile_ragged_sampled(gpu_lib):
+    """256x256 tiles with ragged M and N (N straddles weight-scale rows):
+    full GPU run, oracle on sampled rows including the last tile's."""
+    M, N, K = 4000, 4304, 384
+    say("w8a8 256x256 ragged", M, N, K)
+    xq, xs, wq, ws = _w8a8_inputs(M, N, K, 800)
+    y32 = run_w8a8(*(dev(a) for a in (xq, xs, wq, ws)), torch.float32)
+    rows = np.concatenate([np.random.default_rng(4).choice(3840, 24, replace=False), np.arange(3840, 4000, 5)])
+    y0 = oracle.gemm_w8a8_blk128(xq[rows], xs[rows], wq, ws)
+    assert_fp32_bar(y32[rows], y0, "256x256 ragged sampled rows")
+
+
 def test_w8a8_decode_oproj_full(gpu_lib):
     """Decode o_proj M=1, N=K=4096: full oracle."""
     _w8a8_check(1, 4096, 4096, 1, what="o_proj decode")
