@@ -104,8 +104,24 @@ __device__ __forceinline__ void wait_stage(int younger) {
     }
 }
 
-// Byte offset in a stage of (row, 16-byte chunk c) after the XOR swizzle.
-__device__ __forceinline__ int swz(int row, int c) { return row * kRowBytes + ((c ^ (row & 7)) << 4); }
+// LDS swizzles: chunk c of stage row R sits at chunk position c ^ s(R).
+// Token rows are read 16 consecutive rows at a time, so s_B(R) = R & 7.
+// Weight rows are read in the permuted order of a_row() below (groups of
+// four consecutive rows, 8 rows apart), so s_A mixes bits 1, 3 and 4 of the
+// row.  Either way the 16 lanes of one ds_read_b128 phase hit 16 distinct
+// 16-byte bank groups.
+__device__ __forceinline__ int swz_a_bits(int row) { return ((row >> 1) & 1) | (((row >> 3) & 3) << 1); }
+__device__ __forceinline__ int swz_a(int row, int c) { return row * kRowBytes + ((c ^ swz_a_bits(row)) << 4); }
+__device__ __forceinline__ int swz_b(int row, int c) { return row * kRowBytes + ((c ^ (row & 7)) << 4); }
+
+// Weight row (local to the wave's kWaveN rows) behind MFMA row rho of the
+// wave's weight tile i.  Chosen so that the MFMA output lane group g (rows
+// 4g..4g+3 of every tile) holds, over tile pairs (2p, 2p+1), the eight
+// consecutive rows 32p + 8g .. 32p + 8g + 7: each lane then stores 16
+// contiguous bytes per pair, and the four lane groups 64 contiguous bytes.
+__device__ __forceinline__ int a_row(int i, int rho) {
+    return 32 * (i >> 1) + 4 * (i & 1) + 8 * (rho >> 2) + (rho & 3);
+}
 
 // A raw buffer descriptor (gfx9: dword 3 = 0x00020000, untyped 32-bit data;
 // a lane whose offset lies at or past num_records reads zero), in SGPRs.
@@ -139,25 +155,27 @@ __device__ __forceinline__ void dma4(uint32_t lds, i32x4 rsrc, int voff, int sof
 // Issue this wave's direct-to-LDS loads of K block kb into a stage.
 // Instruction q of wave w fills LDS rows 8*(W q + w) .. +7 of the stage (W =
 // waves; weight rows first, then token rows); lane l fills granule l of those
-// 1 KB, i.e. row 8*(W q + w) + l/8 at chunk position l%8, so it fetches
-// logical chunk (l%8) ^ (l/8) of that row.  The row offset goes into the
+// 1 KB, i.e. row R = 8*(W q + w) + l/8 at chunk position l%8, so it
+// fetches logical chunk (l%8) ^ s(R) of that row (s_A or s_B; with W a
+// multiple of 4 both are the same for every q, so one lane offset per
+// operand serves all q).  The row offset goes into the
 // per-lane offset, which the descriptor's range check sees, so rows past the
 // end of the matrix load as zeros; the K block's byte offset (< K, so it
 // never carries a valid row's access past its own row) goes into the scalar
 // offset.
 template <class C>
 __device__ __forceinline__ void issue_stage(uint8_t* stage, i32x4 rsrc_a, i32x4 rsrc_b, i32x4 rsrc_xs,
-                                            i32x4 rsrc_ws, int lane_off, int q_stride, int xs_off, int64_t kb,
-                                            int wave, int lane) {
+                                            i32x4 rsrc_ws, int lane_off_a, int lane_off_b, int q_stride,
+                                            int xs_off, int64_t kb, int wave, int lane) {
     const int k_off = __builtin_amdgcn_readfirstlane((int)(kb * kRowBytes));
     const uint32_t base = lds_address(stage);
 #pragma unroll
     for (int q = 0; q < C::kLoadsPerWave; ++q) {
         const uint32_t lds = __builtin_amdgcn_readfirstlane(base + kRowsPerLoad * (C::kWaves * q + wave) * kRowBytes);
         if (q < C::kLoadsA) {
-            dma16(lds, rsrc_a, lane_off + q * q_stride, k_off);
+            dma16(lds, rsrc_a, lane_off_a + q * q_stride, k_off);
         } else {
-            dma16(lds, rsrc_b, lane_off + (q - C::kLoadsA) * q_stride, k_off);
+            dma16(lds, rsrc_b, lane_off_b + (q - C::kLoadsA) * q_stride, k_off);
         }
     }
     // Token scales xs[m0 + kXsLanes * w + l, kb], lanes l < kXsLanes only (the
@@ -183,9 +201,12 @@ __device__ __forceinline__ void stage_barrier() {
     asm volatile("" ::: "memory");
 }
 
+template <bool kWeightRows>
 __device__ __forceinline__ i32x8 read_frag(const uint8_t* stage, int row, int g) {
-    const u32x4 lo = *reinterpret_cast<const u32x4*>(stage + swz(row, g));
-    const u32x4 hi = *reinterpret_cast<const u32x4*>(stage + swz(row, g + 4));
+    const int lo_off = kWeightRows ? swz_a(row, g) : swz_b(row, g);
+    const int hi_off = kWeightRows ? swz_a(row, g + 4) : swz_b(row, g + 4);
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(stage + lo_off);
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(stage + hi_off);
     return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
@@ -210,15 +231,22 @@ __device__ __forceinline__ void tile_of_block(int64_t b, int64_t tiles_n, int64_
     tn = in_group / group_m;
 }
 
-__device__ __forceinline__ void store4(void* y, int y_dtype, int64_t idx, f32x4 v) {
+// Store eight consecutive outputs y[idx .. idx+7] (lo = the first four):
+// one 16-byte store for 16-bit outputs, two for fp32.  idx is a multiple of
+// 8 and, with N % 16 == 0, the eight lie in one row.
+__device__ __forceinline__ void store8(void* y, int y_dtype, int64_t idx, f32x4 lo, f32x4 hi) {
     if (y_dtype == 2) {
-        *reinterpret_cast<f32x4*>(static_cast<float*>(y) + idx) = v;
+        *reinterpret_cast<f32x4*>(static_cast<float*>(y) + idx) = lo;
+        *reinterpret_cast<f32x4*>(static_cast<float*>(y) + idx + 4) = hi;
     } else {
-        uint32_t h[4];
+        uint32_t h[8];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) h[e] = y_dtype == 0 ? float_to_bf16_bits(v[e]) : float_to_f16_bits(v[e]);
-        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + idx) =
-            make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+        for (int e = 0; e < 4; ++e) {
+            h[e] = y_dtype == 0 ? float_to_bf16_bits(lo[e]) : float_to_f16_bits(lo[e]);
+            h[e + 4] = y_dtype == 0 ? float_to_bf16_bits(hi[e]) : float_to_f16_bits(hi[e]);
+        }
+        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(y) + idx) =
+            u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
     }
 }
 
@@ -255,7 +283,9 @@ __global__ __launch_bounds__(C::kThreads, 1) void w8a8_tile_kernel(
     const i32x4 rsrc_a = buffer_rsrc(wq + n0 * K, (uint32_t)(rows_a * K));
     const i32x4 rsrc_b = buffer_rsrc(xq + m0 * K, (uint32_t)(rows_b * K));
     const i32x4 rsrc_xs = buffer_rsrc(xs + m0 * KB, (uint32_t)(rows_b * KB * 4));
-    const int lane_off = (int)((8 * wave + (lane >> 3)) * K) + ((((lane & 7) ^ ((lane >> 3) & 7))) << 4);
+    const int dma_row = 8 * wave + (lane >> 3);     // stage row of this lane's first load, minus 8 W q
+    const int lane_off_a = (int)(dma_row * K) + (((lane & 7) ^ swz_a_bits(dma_row)) << 4);
+    const int lane_off_b = (int)(dma_row * K) + (((lane & 7) ^ (dma_row & 7)) << 4);
     const int q_stride = (int)(kRowsPerLoad * C::kWaves * K);
     const int xs_off = (int)((C::kXsLanes * wave + lane) * KB * 4);
 
@@ -271,7 +301,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void w8a8_tile_kernel(
         for (int j = 0; j < C::kTj; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
 
-    const int a_row0 = C::kWaveN * wn + r;           // + 16 i
+    const int a_base = C::kWaveN * wn;               // + a_row(i, r)
     const int b_row0 = C::BN + C::kWaveM * wm + r;   // + 16 j
 
     // Per block, per wave: kTi rows of kTj MFMAs (one per 16x16 tile) into
@@ -287,15 +317,15 @@ __global__ __launch_bounds__(C::kThreads, 1) void w8a8_tile_kernel(
         for (int j = 0; j < C::kTj; ++j) sc[j] = xs_lds[C::kWaveM * wm + 16 * j + r] * wsc;
         i32x8 bf[C::kTj];
 #pragma unroll
-        for (int j = 0; j < C::kTj; ++j) bf[j] = read_frag(stage, b_row0 + 16 * j, g);
+        for (int j = 0; j < C::kTj; ++j) bf[j] = read_frag<false>(stage, b_row0 + 16 * j, g);
         f32x4 tmp[2][C::kTj];
-        i32x8 af = read_frag(stage, a_row0, g);
+        i32x8 af = read_frag<true>(stage, a_base + a_row(0, r), g);
 #pragma unroll
         for (int i = 0; i < C::kTi; ++i) {
             const int c = i & 1;
 #pragma unroll
             for (int j = 0; j < C::kTj; ++j) tmp[c][j] = mfma_e4m3_16x16x128(af, bf[j], zero);
-            if (i + 1 < C::kTi) af = read_frag(stage, a_row0 + 16 * (i + 1), g);
+            if (i + 1 < C::kTi) af = read_frag<true>(stage, a_base + a_row(i + 1, r), g);
             if (i > 0) {
 #pragma unroll
                 for (int j = 0; j < C::kTj; ++j)
@@ -316,7 +346,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void w8a8_tile_kernel(
 #pragma unroll
     for (int p = 0; p + 1 < C::kStages; ++p)
         if (p < nkb)
-            issue_stage<C>(stage(p), rsrc_a, rsrc_b, rsrc_xs, rsrc_ws, lane_off, q_stride, xs_off, kb0 + p, wave,
+            issue_stage<C>(stage(p), rsrc_a, rsrc_b, rsrc_xs, rsrc_ws, lane_off_a, lane_off_b, q_stride, xs_off, kb0 + p, wave,
                            lane);
     for (int64_t b = 0; b < nkb; ++b) {
         // This wave's loads of block b are done (those of the younger blocks
@@ -328,25 +358,30 @@ __global__ __launch_bounds__(C::kThreads, 1) void w8a8_tile_kernel(
         wait_stage<C>(left < C::kStages - 2 ? (int)left : C::kStages - 2);
         stage_barrier();
         if (b + C::kStages - 1 < nkb)
-            issue_stage<C>(stage(b + C::kStages - 1), rsrc_a, rsrc_b, rsrc_xs, rsrc_ws, lane_off, q_stride, xs_off,
+            issue_stage<C>(stage(b + C::kStages - 1), rsrc_a, rsrc_b, rsrc_xs, rsrc_ws, lane_off_a, lane_off_b, q_stride, xs_off,
                            kb0 + b + C::kStages - 1, wave, lane);
         compute(stage(b));
     }
 
-    // The lane holds n = n0 + kWaveN wn + 16 i + 4 g + e (e = 0..3) of token
-    // m = m0 + kWaveM wm + 16 j + r.
-    const int nl0 = C::kWaveN * wn + 4 * g, ml0 = C::kWaveM * wm + r;
-    if (splits == 1) {
+    // By a_row(), the lane holds, for token m = m0 + kWaveM wm + 16 j + r,
+    // outputs n = n0 + kWaveN wn + 32 p + 8 g + t (t = 0..7) in acc[2p][j]
+    // (t < 4) and acc[2p+1][j] (t >= 4).
+    const int nl0 = C::kWaveN * wn + 8 * g, ml0 = C::kWaveM * wm + r;
+    static_assert(C::kTi % 2 == 0, "tile pairs");
+    auto store_tile = [&]() {
 #pragma unroll
         for (int j = 0; j < C::kTj; ++j) {
             const int64_t m = m0 + ml0 + 16 * j;
             if (m >= M) continue;
 #pragma unroll
-            for (int i = 0; i < C::kTi; ++i) {
-                const int64_t n = n0 + nl0 + 16 * i;
-                if (n < N) store4(y, y_dtype, m * N + n, acc[i][j]);
+            for (int p = 0; p < C::kTi / 2; ++p) {
+                const int64_t n = n0 + nl0 + 32 * p;
+                if (n < N) store8(y, y_dtype, m * N + n, acc[2 * p][j], acc[2 * p + 1][j]);
             }
         }
+    };
+    if (splits == 1) {
+        store_tile();
         return;
     }
 
@@ -405,15 +440,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void w8a8_tile_kernel(
                     for (int j = 0; j < C::kTj; ++j) acc[i][j] += __builtin_bit_cast(f32x4, v[u][i * C::kTj + j]);
             }
         }
-#pragma unroll
-        for (int j = 0; j < C::kTj; ++j) {
-            const int64_t m = m0 + ml0 + 16 * j;
-#pragma unroll
-            for (int i = 0; i < C::kTi; ++i) {
-                const int64_t n = n0 + nl0 + 16 * i;
-                if (m < M && n < N) store4(y, y_dtype, m * N + n, acc[i][j]);
-            }
-        }
+        store_tile();
         if (threadIdx.x == 0) __hip_atomic_store(&counters[t], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
