@@ -33,6 +33,8 @@
 // order (no float atomics, identical from run to run), with the same
 // fence-free hand-off as the streaming kernels.
 
+#include <type_traits>
+
 #include "bfp8_device.hpp"
 #include "bfp8_launch.hpp"
 
@@ -143,13 +145,17 @@ __device__ __forceinline__ uint32_t lds_address(const void* p) {
 // explicit vmcnt waits.  Written as asm so that the compiler's own wait
 // insertion, which cannot tell the LDS stages apart, does not drain the
 // prefetch before every LDS read.
-__device__ __forceinline__ void dma16(uint32_t lds, i32x4 rsrc, int voff, int soff) {
-    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds"
-                 :: "v"(voff), "s"(rsrc), "s"(lds), "s"(soff) : "memory");
+// The 16-byte form adds a wave-uniform row offset to the lane offset inside
+// the asm, so the compiler keeps one lane offset per operand live instead of
+// one per load.
+__device__ __forceinline__ void dma16(uint32_t lds, i32x4 rsrc, int voff, int row_off, int soff) {
+    int tmp;
+    asm volatile("v_add_u32 %0, %1, %2\n\ts_mov_b32 m0, %4\n\tbuffer_load_dwordx4 %0, %3, %5 offen lds"
+                 : "=&v"(tmp) : "v"(voff), "s"(row_off), "s"(rsrc), "s"(lds), "s"(soff) : "memory", "m0");
 }
 __device__ __forceinline__ void dma4(uint32_t lds, i32x4 rsrc, int voff, int soff) {
     asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, %3 offen lds"
-                 :: "v"(voff), "s"(rsrc), "s"(lds), "s"(soff) : "memory");
+                 :: "v"(voff), "s"(rsrc), "s"(lds), "s"(soff) : "memory", "m0");
 }
 
 // Issue this wave's direct-to-LDS loads of K block kb into a stage.
@@ -163,30 +169,36 @@ __device__ __forceinline__ void dma4(uint32_t lds, i32x4 rsrc, int voff, int sof
 // end of the matrix load as zeros; the K block's byte offset (< K, so it
 // never carries a valid row's access past its own row) goes into the scalar
 // offset.
+// Only tile loads q_lo <= q < q_hi are issued, and the two scale loads only
+// with `scales` (the caller spreads one stage's loads over its MFMA rows).
 template <class C>
 __device__ __forceinline__ void issue_stage(uint8_t* stage, i32x4 rsrc_a, i32x4 rsrc_b, i32x4 rsrc_xs,
                                             i32x4 rsrc_ws, int lane_off_a, int lane_off_b, int q_stride,
-                                            int xs_off, int64_t kb, int wave, int lane) {
+                                            int xs_off, int64_t kb, int wave, int lane,
+                                            int q_lo = 0, int q_hi = C::kLoadsPerWave, bool scales = true) {
     const int k_off = __builtin_amdgcn_readfirstlane((int)(kb * kRowBytes));
     const uint32_t base = lds_address(stage);
+    if (scales) {
+        // Token scales xs[m0 + kXsLanes * w + l, kb], lanes l < kXsLanes only
+        // (the dword form writes M0 + 4 * lane for every active lane).
+        if (lane < C::kXsLanes)
+            dma4(__builtin_amdgcn_readfirstlane(base + C::kOffXs + 4 * C::kXsLanes * wave), rsrc_xs, xs_off,
+                 __builtin_amdgcn_readfirstlane((int)(kb * 4)));
+        // This wave's weight scale ws[nb, kb], lane 0 only.
+        if (lane == 0)
+            dma4(__builtin_amdgcn_readfirstlane(base + C::kOffWs + 4 * wave), rsrc_ws, 0,
+                 __builtin_amdgcn_readfirstlane((int)(kb * 4)));
+    }
 #pragma unroll
     for (int q = 0; q < C::kLoadsPerWave; ++q) {
+        if (q < q_lo || q >= q_hi) continue;
         const uint32_t lds = __builtin_amdgcn_readfirstlane(base + kRowsPerLoad * (C::kWaves * q + wave) * kRowBytes);
         if (q < C::kLoadsA) {
-            dma16(lds, rsrc_a, lane_off_a + q * q_stride, k_off);
+            dma16(lds, rsrc_a, lane_off_a, __builtin_amdgcn_readfirstlane(q * q_stride), k_off);
         } else {
-            dma16(lds, rsrc_b, lane_off_b + (q - C::kLoadsA) * q_stride, k_off);
+            dma16(lds, rsrc_b, lane_off_b, __builtin_amdgcn_readfirstlane((q - C::kLoadsA) * q_stride), k_off);
         }
     }
-    // Token scales xs[m0 + kXsLanes * w + l, kb], lanes l < kXsLanes only (the
-    // dword form writes M0 + 4 * lane for every active lane).
-    if (lane < C::kXsLanes)
-        dma4(__builtin_amdgcn_readfirstlane(base + C::kOffXs + 4 * C::kXsLanes * wave), rsrc_xs, xs_off,
-             __builtin_amdgcn_readfirstlane((int)(kb * 4)));
-    // This wave's weight scale ws[nb, kb], lane 0 only.
-    if (lane == 0)
-        dma4(__builtin_amdgcn_readfirstlane(base + C::kOffWs + 4 * wave), rsrc_ws, 0,
-             __builtin_amdgcn_readfirstlane((int)(kb * 4)));
 }
 
 // Workgroup barrier without the memory fence of __syncthreads(): that fence
@@ -309,7 +321,10 @@ __global__ __launch_bounds__(C::kThreads, 1) void w8a8_tile_kernel(
     // i+1's MFMAs, so the matrix core and the VALU work on different rows.
     // The token fragments and the scales of the block are read first; the
     // weight fragments are streamed one row ahead.
-    auto compute = [&](const uint8_t* stage) {
+    // `fill` (when not null) is the stage that receives block fill_kb; its
+    // loads are issued between the MFMA rows, so a wave never waits for the
+    // memory pipeline to accept a whole stage before it starts multiplying.
+    auto compute = [&](const uint8_t* stage, auto refill, uint8_t* fill, int64_t fill_kb) {
         const float wsc = reinterpret_cast<const float*>(stage + C::kOffWs)[wave];
         const float* xs_lds = reinterpret_cast<const float*>(stage + C::kOffXs);
         float sc[C::kTj];
@@ -325,6 +340,10 @@ __global__ __launch_bounds__(C::kThreads, 1) void w8a8_tile_kernel(
             const int c = i & 1;
 #pragma unroll
             for (int j = 0; j < C::kTj; ++j) tmp[c][j] = mfma_e4m3_16x16x128(af, bf[j], zero);
+            if constexpr (decltype(refill)::value)
+                issue_stage<C>(fill, rsrc_a, rsrc_b, rsrc_xs, rsrc_ws, lane_off_a, lane_off_b, q_stride, xs_off,
+                               fill_kb, wave, lane, i * C::kLoadsPerWave / C::kTi,
+                               (i + 1) * C::kLoadsPerWave / C::kTi, false);
             if (i + 1 < C::kTi) af = read_frag<true>(stage, a_base + a_row(i + 1, r), g);
             if (i > 0) {
 #pragma unroll
@@ -348,19 +367,30 @@ __global__ __launch_bounds__(C::kThreads, 1) void w8a8_tile_kernel(
         if (p < nkb)
             issue_stage<C>(stage(p), rsrc_a, rsrc_b, rsrc_xs, rsrc_ws, lane_off_a, lane_off_b, q_stride, xs_off, kb0 + p, wave,
                            lane);
-    for (int64_t b = 0; b < nkb; ++b) {
-        // This wave's loads of block b are done (those of the younger blocks
-        // b+1 .. b+S-2 that exist may stay in flight), and so are its LDS
-        // reads of block b-1.  After the barrier every wave's block b is in
-        // LDS and no wave reads the stage of block b-1, which receives block
-        // b+S-1.
+    // Steady state: blocks whose stage is refilled with block b + S - 1,
+    // then the last S - 1 blocks with no refill (two loops, so the
+    // accumulators never meet a branch between two copies of the MFMA code).
+    // At the top of each block: this wave's loads of block b are done (those
+    // of the younger blocks b+1 .. b+S-2 that exist may stay in flight), and
+    // so are its LDS reads of block b-1.  After the barrier every wave's
+    // block b is in LDS and no wave reads the stage of block b-1, which
+    // receives block b+S-1.
+    const int64_t steady = nkb - (C::kStages - 1) > 0 ? nkb - (C::kStages - 1) : 0;
+    for (int64_t b = 0; b < steady; ++b) {
+        wait_stage<C>(C::kStages - 2);
+        stage_barrier();
+        // The scale loads of the refill block first (two short
+        // instructions), its tile loads between the MFMA rows.
+        uint8_t* fill = stage(b + C::kStages - 1);
+        issue_stage<C>(fill, rsrc_a, rsrc_b, rsrc_xs, rsrc_ws, lane_off_a, lane_off_b, q_stride, xs_off,
+                       kb0 + b + C::kStages - 1, wave, lane, 0, 0, true);
+        compute(stage(b), std::true_type{}, fill, kb0 + b + C::kStages - 1);
+    }
+    for (int64_t b = steady; b < nkb; ++b) {
         const int64_t left = nkb - 1 - b;
         wait_stage<C>(left < C::kStages - 2 ? (int)left : C::kStages - 2);
         stage_barrier();
-        if (b + C::kStages - 1 < nkb)
-            issue_stage<C>(stage(b + C::kStages - 1), rsrc_a, rsrc_b, rsrc_xs, rsrc_ws, lane_off_a, lane_off_b, q_stride, xs_off,
-                           kb0 + b + C::kStages - 1, wave, lane);
-        compute(stage(b));
+        compute(stage(b), std::false_type{}, nullptr, 0);
     }
 
     // By a_row(), the lane holds, for token m = m0 + kWaveM wm + 16 j + r,
