@@ -2,8 +2,10 @@
 """Benchmark of the blockwise-scaled FP8 GEMM hot path on one MI355X.
 
 Workloads (synthetic, seeded; inputs resident in HBM before timing starts):
-  decode   (default) o_proj decode, M=1, N=K=4096.  One step = 1x128
-           activation quantisation + W8A8 GEMM + W8A16 GEMM (bf16 activations).
+  decode   (default) o_proj decode, M=1, N=K=4096.  One step = W8A8 GEMM
+           with its 1x128 activation quantisation fused (bf16 activations in)
+           + W8A16 GEMM (bf16 activations).  --unfused runs the quantiser as
+           its own kernel before the W8A8 GEMM instead.
            Weights rotate over --copies distinct copies so no call finds its
            weights in a cache.  Headline: step HBM GB/s (algorithmic bytes).
   prefill  o_proj prefill, M=N=K=4096, 1% outlier channels.  One step =
@@ -52,6 +54,8 @@ def parse():
     p.add_argument("--copies", type=int, default=32, help="distinct weight copies rotated per call")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--unfused", action="store_true",
+                   help="decode: separate quantiser + W8A8 GEMM instead of the fused call")
     p.add_argument("--copy-probe", action="store_true",
                    help="before the workload, copy a 96 MiB buffer 5 times (calibrates HBM byte counters)")
     return p.parse_args()
@@ -65,6 +69,11 @@ def bytes_quant(M, K):
 
 def bytes_w8a8(M, N, K):
     return N * K + 4 * ((N + 127) // 128) * (K // 128) + M * K + 4 * M * ((K + 127) // 128) + 2 * M * N
+
+
+def bytes_quant_w8a8(M, N, K):
+    """Fused quantise + W8A8: 16-bit activations in, no code round trip."""
+    return N * K + 4 * ((N + 127) // 128) * (K // 128) + 2 * M * K + 2 * M * N
 
 
 def bytes_w8a16(M, N, K):
@@ -206,6 +215,7 @@ def bench_decode(torch, bfp8, inputs, args):
     y8 = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
     y16 = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
     ws8 = bfp8.make_workspace(bfp8.OP_GEMM_W8A8_BLK128, M, N, K)
+    wsq = bfp8.make_workspace(bfp8.OP_QUANT_GEMM_W8A8_BLK128, M, N, K)
     ws16 = bfp8.make_workspace(bfp8.OP_GEMM_W8A16_BLK128, M, N, K)
     C = len(copies)
 
@@ -213,27 +223,37 @@ def bench_decode(torch, bfp8, inputs, args):
         a = copies[i % C]
         bfp8.bfp8_gemm_w8a8_blk128(xq, xs, a[0], a[1], y8, ws8)
 
+    def quant_w8a8(i):
+        a = copies[i % C]
+        bfp8.bfp8_quant_gemm_w8a8_blk128(x, a[0], a[1], y8, wsq)
+
     def w8a16(i):
         b = copies[(i + C // 2) % C]
         bfp8.bfp8_gemm_w8a16_blk128(x, b[0], b[1], y16, ws16)
 
-    phases = [("quant_act_1x128", lambda i: bfp8.bfp8_quantize_act_1x128(x, xq, xs)),
-              ("gemm_w8a8_blk128", w8a8), ("gemm_w8a16_blk128", w8a16)]
+    if args.unfused:
+        phases = [("quant_act_1x128", lambda i: bfp8.bfp8_quantize_act_1x128(x, xq, xs)),
+                  ("gemm_w8a8_blk128", w8a8), ("gemm_w8a16_blk128", w8a16)]
+    else:
+        phases = [("quant_gemm_w8a8_blk128", quant_w8a8), ("gemm_w8a16_blk128", w8a16)]
     names = [n for n, _ in phases]
     ms, wall, kern, timing = run_steps(torch, phases, args.steps, args.warmup)
     nbytes = {"quant_act_1x128": bytes_quant(M, K), "gemm_w8a8_blk128": bytes_w8a8(M, N, K),
-              "gemm_w8a16_blk128": bytes_w8a16(M, N, K)}
+              "quant_gemm_w8a8_blk128": bytes_quant_w8a8(M, N, K), "gemm_w8a16_blk128": bytes_w8a16(M, N, K)}
+    nbytes = {n: nbytes[n] for n in names}
     for n in names:
         kern[n]["alg_bytes"] = nbytes[n]
         kern[n]["GBps"] = nbytes[n] / (kern[n]["avg_us"] * 1e3)
         kern[n]["hbm_frac"] = kern[n]["GBps"] / HBM_PEAK_GBS
     step_bytes = sum(nbytes.values())
-    dom = max(["gemm_w8a8_blk128", "gemm_w8a16_blk128"], key=lambda n: kern[n]["avg_us"])
+    dom = max([n for n in names if n != "quant_act_1x128"], key=lambda n: kern[n]["avg_us"])
     roof = {"kernel": dom, "bound": "hbm", "achieved": kern[dom]["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": kern[dom]["GBps"] / HBM_PEAK_GBS, "traffic": measured_traffic("decode", dom),
+            "frac": kern[dom]["GBps"] / HBM_PEAK_GBS, "traffic": measured_traffic("decode_unfused" if args.unfused else "decode", dom),
             "alg_bytes": nbytes[dom]}
     result = {"value": step_bytes / (ms * 1e6), "unit": "GB/s", "ms_per_step": ms, "dtype": "e4m3,bf16",
-              "config": {"workload": "o_proj decode: 1x128 act quant + W8A8 blk128 + W8A16 blk128 (bf16 x)",
+              "config": {"workload": ("o_proj decode: 1x128 act quant + W8A8 blk128 + W8A16 blk128 (bf16 x)"
+                                      if args.unfused else
+                                      "o_proj decode: W8A8 blk128 with fused 1x128 act quant + W8A16 blk128 (bf16 x)"),
                          "M": M, "N": N, "K": K, "weight_copies": C, "out_dtype": "bf16",
                          "step_alg_bytes": step_bytes},
               "roofline": roof, "kernels": kern, "wall_s": wall, "timing": timing}

@@ -11,8 +11,8 @@ import torch
 from ._lib import (  # noqa: F401
     BFP8_BF16, BFP8_F16, BFP8_F32, Bfp8Error, LIB_PATH, SIGNATURES, STATUS_NAMES,
     OP_QUANT_ACT_1X128, OP_QUANT_WEIGHT_128X128, OP_GEMM_W8A8_BLK128, OP_GEMM_W8A16_BLK128,
-    OP_GEMM_W8A16_BLK32_UE8M0,
-    load, bfp8_quantize_act_1x128, bfp8_quantize_weight_128x128, bfp8_gemm_w8a8_blk128,
+    OP_GEMM_W8A16_BLK32_UE8M0, OP_QUANT_GEMM_W8A8_BLK128,
+    load, bfp8_quantize_act_1x128, bfp8_quantize_weight_128x128, bfp8_gemm_w8a8_blk128, bfp8_quant_gemm_w8a8_blk128,
     bfp8_gemm_w8a16_blk128, bfp8_gemm_w8a16_blk32_ue8m0, bfp8_prepare_blk32_ue8m0,
     bfp8_workspace_bytes, bfp8_get_limits, bfp8_status_string,
 )
@@ -50,6 +50,16 @@ def gemm_w8a8(xq, xs, wq, ws, out_dtype=torch.bfloat16, workspace=None):
     if workspace is None:
         workspace = make_workspace(OP_GEMM_W8A8_BLK128, M, N, xq.shape[1], xq.device)
     bfp8_gemm_w8a8_blk128(xq, xs, wq, ws, y, workspace)
+    return y
+
+
+def quant_gemm_w8a8(x, wq, ws, out_dtype=torch.bfloat16, workspace=None):
+    """16-bit activations in: 1x128 quantisation and the W8A8 GEMM in one call."""
+    M, N = x.shape[0], wq.shape[0]
+    y = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    if workspace is None:
+        workspace = make_workspace(OP_QUANT_GEMM_W8A8_BLK128, M, N, x.shape[1], x.device)
+    bfp8_quant_gemm_w8a8_blk128(x, wq, ws, y, workspace)
     return y
 
 

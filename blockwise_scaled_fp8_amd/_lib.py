@@ -23,6 +23,7 @@ OP_QUANT_WEIGHT_128X128 = 1
 OP_GEMM_W8A8_BLK128 = 2
 OP_GEMM_W8A16_BLK128 = 3
 OP_GEMM_W8A16_BLK32_UE8M0 = 4
+OP_QUANT_GEMM_W8A8_BLK128 = 5
 STATUS_NAMES = {
     0: "BFP8_OK", 1: "BFP8_E_NULL", 2: "BFP8_E_SHAPE", 3: "BFP8_E_DTYPE", 4: "BFP8_E_ALIGN",
     5: "BFP8_E_WORKSPACE", 6: "BFP8_E_NAN_CODE", 7: "BFP8_E_SCALE_NOT_POW2", 8: "BFP8_E_SCALE_WINDOW",
@@ -35,6 +36,7 @@ SIGNATURES = {
     "bfp8_quantize_act_1x128": (_I, [_P, _I, _I64, _I64, _P, _P, _P]),
     "bfp8_quantize_weight_128x128": (_I, [_P, _I, _I64, _I64, _P, _P, _P]),
     "bfp8_gemm_w8a8_blk128": (_I, [_P, _P, _P, _P, _P, _I, _I64, _I64, _I64, _P, _SZ, _P]),
+    "bfp8_quant_gemm_w8a8_blk128": (_I, [_P, _I, _P, _P, _P, _I, _I64, _I64, _I64, _P, _SZ, _P]),
     "bfp8_gemm_w8a16_blk128": (_I, [_P, _I, _P, _P, _P, _I, _I64, _I64, _I64, _P, _SZ, _P]),
     "bfp8_gemm_w8a16_blk32_ue8m0": (_I, [_P, _I, _P, _P, _P, _I, _I64, _I64, _I64, _P, _SZ, _P]),
     "bfp8_prepare_blk32_ue8m0": (_I, [_P, _P, _I64, _I64, _P, ctypes.POINTER(_I64)]),
@@ -109,6 +111,15 @@ def bfp8_gemm_w8a8_blk128(xq, xs, wq, ws, y, workspace=None):
     wsp, wsb = _ws(workspace)
     _check(load().bfp8_gemm_w8a8_blk128(_ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), _ptr(y), _dtype_code(y),
                                         M, N, K, wsp, wsb, _stream()), "bfp8_gemm_w8a8_blk128")
+
+
+def bfp8_quant_gemm_w8a8_blk128(x, wq, ws, y, workspace=None):
+    M, K = x.shape
+    N = wq.shape[0]
+    wsp, wsb = _ws(workspace)
+    _check(load().bfp8_quant_gemm_w8a8_blk128(_ptr(x), _dtype_code(x), _ptr(wq), _ptr(ws), _ptr(y),
+                                              _dtype_code(y), M, N, K, wsp, wsb, _stream()),
+           "bfp8_quant_gemm_w8a8_blk128")
 
 
 def bfp8_gemm_w8a16_blk128(x, wq, ws, y, workspace=None):

@@ -62,9 +62,44 @@ bfp8_status bfp8_quantize_weight_128x128(const void* w, int w_dtype, int64_t N, 
     return launched(launch_quant_weight_128x128(w, w_dtype == BFP8_BF16, N, K, wq, ws, as_stream(stream)));
 }
 
+}  // extern "C"
+
+namespace {
+
+size_t round256(size_t v) { return (v + 255) / 256 * 256; }
+
+// W8A8 workspace for codes input: the streaming plan's for M <= kStreamMaxM,
+// the tiled kernels' above.
+size_t w8a8_workspace(int64_t M, int64_t N, int64_t K) {
+    if (M <= kStreamMaxM) return stream_workspace_bytes(plan_stream(M, N, K));
+    return K <= kTileMaxK ? tile_workspace_bytes(M, N, K) : 0;
+}
+
+// Workspace of the fused quantise + W8A8 call above kFusedQuantMaxM, where
+// the codes are staged: [W8A8 workspace | xq codes M*K | xs scales M*K/128],
+// each part 256-byte aligned, the zero-initialised counters first.
+struct QuantGemmParts {
+    size_t gemm, xq, xs, total;
+};
+QuantGemmParts quant_gemm_parts(int64_t M, int64_t N, int64_t K) {
+    QuantGemmParts p;
+    p.gemm = round256(w8a8_workspace(M, N, K));
+    p.xq = round256((size_t)(M * K));
+    p.xs = round256((size_t)(M * (K / 128)) * sizeof(float));
+    p.total = p.gemm + p.xq + p.xs;
+    return p;
+}
+
+}  // namespace
+
+extern "C" {
+
 size_t bfp8_workspace_bytes(int op, int64_t M, int64_t N, int64_t K) {
     if (M < 1 || N < 16 || K < 128) return 0;
     switch (op) {
+        case BFP8_OP_QUANT_GEMM_W8A8_BLK128:
+            if (M <= kFusedQuantMaxM) return stream_workspace_bytes(plan_stream(M, N, K));
+            return K <= kTileMaxK ? quant_gemm_parts(M, N, K).total : 0;
         case BFP8_OP_GEMM_W8A8_BLK128:
             if (M > kStreamMaxM) return K <= kTileMaxK ? tile_workspace_bytes(M, N, K) : 0;
             return stream_workspace_bytes(plan_stream(M, N, K));
@@ -90,6 +125,32 @@ bfp8_status bfp8_gemm_w8a8_blk128(const uint8_t* xq, const float* xs, const uint
     // The tiled kernels address a 256-row slab of W through 32-bit offsets.
     if (K > kTileMaxK) return BFP8_E_SHAPE;
     return launched(launch_w8a8_tile(xq, xs, wq, ws, y, y_dtype, M, N, K, workspace, as_stream(stream)));
+}
+
+bfp8_status bfp8_quant_gemm_w8a8_blk128(const void* x, int x_dtype, const uint8_t* wq, const float* ws,
+                                        void* y, int y_dtype, int64_t M, int64_t N, int64_t K,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
+    if (!x || !wq || !ws || !y) return BFP8_E_NULL;
+    const size_t need = (dim_ok(M, 1) && dim_ok(N, 16) && dim_ok(K, 128))
+                            ? bfp8_workspace_bytes(BFP8_OP_QUANT_GEMM_W8A8_BLK128, M, N, K) : 0;
+    bfp8_status st = check_gemm(x, wq, ws, y, y_dtype, M, N, K, 16, need, workspace, workspace_bytes);
+    if (st != BFP8_OK) return st;
+    if (!is16(x_dtype)) return BFP8_E_DTYPE;
+    if (M <= kFusedQuantMaxM)
+        return launched(launch_w8a8_stream_quant(x, x_dtype == BFP8_BF16, wq, ws, y, y_dtype, M, N, K, workspace,
+                                                 as_stream(stream)));
+    if (K > kTileMaxK) return BFP8_E_SHAPE;
+    if (M * ((K + 2047) / 2048) >= kMaxDim) return BFP8_E_SHAPE;    // quantiser grid
+    const QuantGemmParts parts = quant_gemm_parts(M, N, K);
+    char* base = static_cast<char*>(workspace);
+    uint8_t* xq = reinterpret_cast<uint8_t*>(base + parts.gemm);
+    float* xs = reinterpret_cast<float*>(base + parts.gemm + parts.xq);
+    void* gemm_ws = parts.gemm ? workspace : nullptr;
+    hipError_t e = launch_quant_act_1x128(x, x_dtype == BFP8_BF16, M, K, xq, xs, as_stream(stream));
+    if (e != hipSuccess) return BFP8_E_LAUNCH;
+    if (M <= kStreamMaxM)
+        return launched(launch_w8a8_stream(xq, xs, wq, ws, y, y_dtype, M, N, K, gemm_ws, as_stream(stream)));
+    return launched(launch_w8a8_tile(xq, xs, wq, ws, y, y_dtype, M, N, K, gemm_ws, as_stream(stream)));
 }
 
 bfp8_status bfp8_gemm_w8a16_blk128(const void* x, int x_dtype, const uint8_t* wq, const float* ws,
@@ -165,6 +226,7 @@ bfp8_status bfp8_get_limits(int op, int64_t* k_multiple, int64_t* n_multiple, in
         case BFP8_OP_QUANT_ACT_1X128: k = 8; n = 1; ms = 0; break;
         case BFP8_OP_QUANT_WEIGHT_128X128: k = 8; n = 1; ms = 0; break;
         case BFP8_OP_GEMM_W8A8_BLK128: k = 128; n = 16; ms = kStreamMaxM; break;
+        case BFP8_OP_QUANT_GEMM_W8A8_BLK128: k = 128; n = 16; ms = kStreamMaxM; break;
         case BFP8_OP_GEMM_W8A16_BLK128: k = 128; n = 16; ms = INT32_MAX; break;
         case BFP8_OP_GEMM_W8A16_BLK32_UE8M0: k = 128; n = 32; ms = INT32_MAX; break;
         default: return BFP8_E_OP;

@@ -42,6 +42,13 @@ hipError_t launch_w8a8_tile(const uint8_t* xq, const float* xs, const uint8_t* w
 hipError_t launch_w8a8_stream(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
                               void* y, int y_dtype, int64_t M, int64_t N, int64_t K,
                               void* workspace, hipStream_t stream);
+// Largest M for which the W8A8 streaming kernel quantises its 16-bit
+// activations itself; above it the fused call runs the quantiser first.
+constexpr int64_t kFusedQuantMaxM = 8;
+// Streaming W8A8 that quantises its 16-bit activations itself (M <= kFusedQuantMaxM).
+hipError_t launch_w8a8_stream_quant(const void* x, bool x_bf16, const uint8_t* wq, const float* ws,
+                                    void* y, int y_dtype, int64_t M, int64_t N, int64_t K,
+                                    void* workspace, hipStream_t stream);
 hipError_t launch_w8a16_blk128_stream(const void* x, bool x_bf16, const uint8_t* wq, const float* ws,
                                       void* y, int y_dtype, int64_t M, int64_t N, int64_t K,
                                       void* workspace, hipStream_t stream);

@@ -61,7 +61,7 @@ constexpr int kW8A8Chunk = 4;   // 128-K blocks per wave with loads in flight to
 // Lane (r, g) supplies weight row n0 + r and token m0 + r; of each 128-K
 // block it holds the 16-byte chunks g and g + 4 (K offsets 16g and 64 + 16g),
 // the same for both MFMA operands.  Each load instruction then reads whole
-// 64-byte halves of 16 weight rows.  The eight waves take interleaved 128-K
+// 64-byte halves of 16 weight rows.  The waves take interleaved 128-K
 // blocks, so at any time a workgroup reads adjacent blocks of its rows.
 __global__ __launch_bounds__(kStreamThreads) void w8a8_stream_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ xs,
@@ -130,6 +130,139 @@ __global__ __launch_bounds__(kStreamThreads) void w8a8_stream_kernel(
     stream_finish(acc, red, y, y_dtype, M, N, nt, mt, splits, split, n_tiles, partials, counters);
 }
 
+// ------------------------------------------- activation quant fused in ----
+// The same streaming GEMM for M <= kFusedQuantMaxM with 16-bit activations
+// in: each wave quantises, for every 128-K block it multiplies, the block's
+// 1x128 groups of the (at most 8) tokens itself ([ADA] "What's next": the
+// activation quant moved into the GEMM, removing a launch and the code
+// round trip at decode).  The 64 lanes split the padded token count Mp
+// (1, 2, 4 or 8) evenly: 64/Mp lanes per token, 2 Mp values per lane, so no
+// lane quantises padding when M is small.  The group maximum is a
+// butterfly over the token's lanes; scale, quotients and codes use the
+// quantiser's own arithmetic (quantize_v), so codes, scales and results are
+// bit-identical to bfp8_quantize_act_1x128 followed by the codes kernel.
+// The codes go through a per-wave LDS scratch into the MFMA operand layout.
+constexpr int kFusedChunk = 2;
+
+template <int NW>
+__device__ __forceinline__ void load_words(const uint16_t* p, uint32_t (&w)[NW]) {
+    if constexpr (NW == 1) {
+        w[0] = *reinterpret_cast<const uint32_t*>(p);
+    } else if constexpr (NW == 2) {
+        const uint2 v = *reinterpret_cast<const uint2*>(p);
+        w[0] = v.x;
+        w[1] = v.y;
+    } else {
+#pragma unroll
+        for (int i = 0; i < NW / 4; ++i) {
+            const u32x4 v = load_16B(p + 8 * i);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w[4 * i + e] = v[e];
+        }
+    }
+}
+
+template <int NB>
+__device__ __forceinline__ void store_codes(uint8_t* p, const uint32_t (&c)[(NB + 3) / 4]) {
+    if constexpr (NB == 2) {
+        *reinterpret_cast<uint16_t*>(p) = (uint16_t)c[0];
+    } else if constexpr (NB == 4) {
+        *reinterpret_cast<uint32_t*>(p) = c[0];
+    } else if constexpr (NB == 8) {
+        *reinterpret_cast<uint2*>(p) = make_uint2(c[0], c[1]);
+    } else {
+        *reinterpret_cast<u32x4*>(p) = u32x4{c[0], c[1], c[2], c[3]};
+    }
+}
+
+template <bool kBf16, int kMp>
+__global__ __launch_bounds__(kStreamThreads) void w8a8_stream_quant_kernel(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq, const float* __restrict__ ws,
+    void* __restrict__ y, int y_dtype, int64_t M, int64_t N, int64_t K,
+    int64_t n_tiles, int64_t splits, int64_t kb_per_split,
+    float* __restrict__ partials, uint32_t* __restrict__ counters) {
+    constexpr int kL = kWave / kMp;          // lanes per token
+    constexpr int kV = 128 / kL;             // values per lane (2 Mp)
+    __shared__ float red[kStreamWaves * 256];
+    __shared__ __attribute__((aligned(16))) uint8_t xcode[kStreamWaves][kFusedChunk][kMp][128];
+    const int64_t nt = blockIdx.x, split = blockIdx.y;
+    const int64_t KB = K / 128;
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int r = lane & 15, g = lane >> 4;
+    const int64_t kb_begin = split * kb_per_split;
+    const int64_t kb_end = kb_begin + kb_per_split < KB ? kb_begin + kb_per_split : KB;
+
+    // Quantiser role: token qt, values [qp * kV, qp * kV + kV) of each block.
+    const int qt = lane / kL, qp = lane % kL;
+    const bool qt_ok = qt < M;
+    const uint16_t* xrow = x + (qt_ok ? qt : 0) * K + qp * kV;
+    // MFMA role: weight row n0 + r, token r (rows r >= kMp are padding).
+    const bool r_ok = r < kMp;
+    const uint8_t* wrow = wq + (nt * 16 + r) * K + g * 16;
+    const float* ws_row = ws + (nt * 16 / 128) * KB;
+
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int64_t kb0 = kb_begin + wave; kb0 < kb_end; kb0 += kStreamWaves * kFusedChunk) {
+        uint32_t raw[kFusedChunk][kV / 2];
+        u32x4 wa[kFusedChunk][2];
+#pragma unroll
+        for (int c = 0; c < kFusedChunk; ++c) {
+            const int64_t kb = kb0 + c * kStreamWaves;
+            if (kb < kb_end) {
+                if (qt_ok) {
+                    load_words<kV / 2>(xrow + kb * 128, raw[c]);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < kV / 2; ++i) raw[c][i] = 0u;
+                }
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < kFusedChunk; ++c) {
+            const int64_t kb = kb0 + c * kStreamWaves;
+            if (kb < kb_end) {
+                wa[c][0] = load_16B(wrow + kb * 128);
+                wa[c][1] = load_16B(wrow + kb * 128 + 64);
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < kFusedChunk; ++c) {
+            const int64_t kb = kb0 + c * kStreamWaves;
+            if (kb < kb_end) {
+                float v[kV];
+                float amax = 0.0f;
+#pragma unroll
+                for (int i = 0; i < kV / 2; ++i) {
+                    v[2 * i] = kBf16 ? bf16_bits_to_float(raw[c][i] & 0xFFFFu) : f16_bits_to_float(raw[c][i] & 0xFFFFu);
+                    v[2 * i + 1] = kBf16 ? bf16_bits_to_float(raw[c][i] >> 16) : f16_bits_to_float(raw[c][i] >> 16);
+                    amax = fmaxf(amax, fmaxf(fabsf(v[2 * i]), fabsf(v[2 * i + 1])));
+                }
+#pragma unroll
+                for (int off = kL / 2; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
+                const float s = amax / 448.0f;
+                uint32_t codes[(kV + 3) / 4];
+                quantize_v<kV>(v, s, codes);
+                store_codes<kV>(&xcode[wave][c][qt][qp * kV], codes);
+                // This MFMA lane's token scale, from the first lane of token r.
+                const float s_r = __shfl(s, (r_ok ? r : 0) * kL, kWave);
+                const float sc = r_ok ? s_r * ws_row[kb] : 0.0f;
+                u32x4 b0 = {0u, 0u, 0u, 0u}, b1 = {0u, 0u, 0u, 0u};
+                if (r_ok) {
+                    b0 = *reinterpret_cast<const u32x4*>(&xcode[wave][c][r][16 * g]);
+                    b1 = *reinterpret_cast<const u32x4*>(&xcode[wave][c][r][64 + 16 * g]);
+                }
+                const i32x8 a = __builtin_bit_cast(i32x8, __builtin_shufflevector(wa[c][0], wa[c][1], 0, 1, 2, 3, 4, 5, 6, 7));
+                const i32x8 b = __builtin_bit_cast(i32x8, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7));
+                const f32x4 blk = mfma_e4m3_16x16x128(a, b, zero);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(blk[i], sc, acc[i]);
+            }
+        }
+    }
+    stream_finish(acc, red, y, y_dtype, M, N, nt, 0, splits, split, n_tiles, partials, counters);
+}
+
 hipError_t launch_w8a8_stream(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
                               void* y, int y_dtype, int64_t M, int64_t N, int64_t K,
                               void* workspace, hipStream_t stream) {
@@ -140,6 +273,40 @@ hipError_t launch_w8a8_stream(const uint8_t* xq, const float* xs, const uint8_t*
     hipLaunchKernelGGL(w8a8_stream_kernel, dim3((unsigned)p.n_tiles, (unsigned)p.splits, (unsigned)p.m_tiles),
                        dim3(kStreamThreads), 0, stream, xq, xs, wq, ws, y, y_dtype, M, N, K,
                        p.n_tiles, p.splits, p.kb_per_split, partials, counters);
+    return hipGetLastError();
+}
+
+template <bool kBf16>
+static void launch_quant_mp(int mp, dim3 grid, hipStream_t stream, const void* x, const uint8_t* wq, const float* ws,
+                            void* y, int y_dtype, int64_t M, int64_t N, int64_t K, const StreamPlan& p,
+                            float* partials, uint32_t* counters) {
+    const uint16_t* xh = static_cast<const uint16_t*>(x);
+#define BFP8_LAUNCH_MP(MP)                                                                                    \
+    hipLaunchKernelGGL((w8a8_stream_quant_kernel<kBf16, MP>), grid, dim3(kStreamThreads), 0, stream, xh, wq, ws, \
+                       y, y_dtype, M, N, K, p.n_tiles, p.splits, p.kb_per_split, partials, counters)
+    switch (mp) {
+        case 1: BFP8_LAUNCH_MP(1); break;
+        case 2: BFP8_LAUNCH_MP(2); break;
+        case 4: BFP8_LAUNCH_MP(4); break;
+        default: BFP8_LAUNCH_MP(8); break;
+    }
+#undef BFP8_LAUNCH_MP
+}
+
+hipError_t launch_w8a8_stream_quant(const void* x, bool x_bf16, const uint8_t* wq, const float* ws,
+                                    void* y, int y_dtype, int64_t M, int64_t N, int64_t K,
+                                    void* workspace, hipStream_t stream) {
+    const StreamPlan p = plan_stream(M, N, K);
+    uint32_t* counters;
+    float* partials;
+    stream_workspace_parts(p, workspace, counters, partials);
+    const dim3 grid((unsigned)p.n_tiles, (unsigned)p.splits, 1u);
+    const int mp = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8;
+    if (x_bf16) {
+        launch_quant_mp<true>(mp, grid, stream, x, wq, ws, y, y_dtype, M, N, K, p, partials, counters);
+    } else {
+        launch_quant_mp<false>(mp, grid, stream, x, wq, ws, y, y_dtype, M, N, K, p, partials, counters);
+    }
     return hipGetLastError();
 }
 

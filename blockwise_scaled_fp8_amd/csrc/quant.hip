@@ -19,37 +19,6 @@
 
 namespace bfp8 {
 
-// Quantise 8 values against scale s; returns the 8 codes packed in K order.
-// A zero group (s == 0) gives code 0x00 everywhere.
-__device__ __forceinline__ void quantize8(const float v[8], float s, uint32_t& lo, uint32_t& hi) {
-    const QuotientBy div(s);
-    float q[8];
-    // The IEEE fallback (scales outside [2^-90, 2^100]) is taken by the whole
-    // wave when any lane needs it, so the common path has no divergence.
-    if (__any(div.ieee)) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) q[i] = fabsf(v[i]) / s;
-    } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) q[i] = div.abs_quotient(v[i]);
-    }
-    uint32_t c[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-        c[i] = (s == 0.0f) ? 0u : (e4m3_encode(q[i]) | ((__float_as_uint(v[i]) >> 24) & 0x80u));
-    lo = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
-    hi = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
-}
-
-__device__ __forceinline__ void unpack8(u32x4 raw, bool bf16, float v[8]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t w = raw[i];
-        v[2 * i] = bf16 ? bf16_bits_to_float(w & 0xFFFFu) : f16_bits_to_float(w & 0xFFFFu);
-        v[2 * i + 1] = bf16 ? bf16_bits_to_float(w >> 16) : f16_bits_to_float(w >> 16);
-    }
-}
-
 constexpr int kQuantActThreads = 256;
 
 // Grid: one workgroup per (row, run of 16 groups); 16 threads per group,

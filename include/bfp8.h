@@ -68,7 +68,8 @@ enum {
     BFP8_OP_QUANT_WEIGHT_128X128 = 1,
     BFP8_OP_GEMM_W8A8_BLK128 = 2,
     BFP8_OP_GEMM_W8A16_BLK128 = 3,
-    BFP8_OP_GEMM_W8A16_BLK32_UE8M0 = 4
+    BFP8_OP_GEMM_W8A16_BLK32_UE8M0 = 4,
+    BFP8_OP_QUANT_GEMM_W8A8_BLK128 = 5
 };
 
 /*
@@ -122,6 +123,27 @@ bfp8_status bfp8_gemm_w8a8_blk128(const uint8_t* xq, const float* xs,
                                   const uint8_t* wq, const float* ws,
                                   void* y, int y_dtype, int64_t M, int64_t N, int64_t K,
                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Activation quantisation fused with the W8A8 blockwise GEMM ([ADA] "What's
+ * next": the 1x128 activation quant moved into the GEMM; at decode it
+ * removes a launch and the round trip of the codes through memory).
+ * Computes exactly bfp8_quantize_act_1x128 followed by bfp8_gemm_w8a8_blk128
+ * on the same arguments: the same codes, scales and per-block promotion, so
+ * y is bit-identical to that pair of calls.
+ *   x   [M, K] bf16 or fp16 (x_dtype BFP8_BF16 / BFP8_F16), device.
+ *   wq, ws, y, y_dtype: as for bfp8_gemm_w8a8_blk128.
+ *   workspace: at least bfp8_workspace_bytes(BFP8_OP_QUANT_GEMM_W8A8_BLK128,
+ *       M, N, K) bytes, zero-filled before its first use, left ready for the
+ *       next call; calls that overlap in time must not share one.  For M <= 8
+ *       the streaming kernel quantises in registers; above that the codes and
+ *       scales are staged in the workspace by the 1x128 quantiser.
+ * Requires M >= 1, N >= 16, N % 16 == 0, K >= 128, K % 128 == 0.
+ */
+bfp8_status bfp8_quant_gemm_w8a8_blk128(const void* x, int x_dtype,
+                                        const uint8_t* wq, const float* ws,
+                                        void* y, int y_dtype, int64_t M, int64_t N, int64_t K,
+                                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * W8A16 blockwise GEMM: 16-bit activations, E4M3 weights expanded to 16 bits

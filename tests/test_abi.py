@@ -41,7 +41,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared()
-    assert len(names) == 9
+    assert len(names) == 10
     assert sorted(_lib.SIGNATURES) == names
     nm = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], stdout=subprocess.PIPE, text=True).stdout
     exported = set(re.findall(r" T (bfp8_\w+)", nm))
@@ -61,6 +61,32 @@ def test_limits(lib):
     assert w8a8 == {"k_multiple": 128, "n_multiple": 16, "align_bytes": 16, "m_stream_max": 16}
     assert bfp8.bfp8_get_limits(bfp8.OP_GEMM_W8A16_BLK32_UE8M0)["n_multiple"] == 32
     assert lib.bfp8_get_limits(77, None, None, None, None) == 10
+
+
+def test_quant_gemm_workspace_and_limits(lib):
+    op = bfp8.OP_QUANT_GEMM_W8A8_BLK128
+    # quantised in registers (M <= 8): the W8A8 split-K plan only
+    for M, N, K in [(1, 4096, 4096), (8, 1024, 4096), (4, 512, 512)]:
+        assert bfp8.bfp8_workspace_bytes(op, M, N, K) == bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, M, N, K)
+    # staged codes: W8A8 workspace + M*K codes + M*K/128 scales, each 256-aligned
+    r = lambda v: (v + 255) // 256 * 256
+    for M, N, K in [(4096, 4096, 4096), (64, 4096, 4096), (17, 384, 640), (9, 1024, 4096), (16, 4096, 4096)]:
+        t = bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, M, N, K)
+        assert bfp8.bfp8_workspace_bytes(op, M, N, K) == r(t) + r(M * K) + r(4 * M * (K // 128))
+    assert bfp8.bfp8_get_limits(op)["m_stream_max"] == 16
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((0, 0, B, C, Y, 0, 4, 512, 512, None, 0, None), 1),          # null x
+    ((A, 2, B, C, Y, 0, 4, 512, 512, None, 0, None), 3),          # fp32 activations
+    ((A, 0, B, C, Y, 0, 4, 520, 512, None, 0, None), 2),          # N % 16
+    ((A, 0, B, C, Y, 0, 4, 512, 500, None, 0, None), 2),          # K % 128
+    ((A, 0, B, C, Y, 0, 64, 512, 512, None, 0, None), 5),         # codes need a workspace above M = 8
+    ((A, 0, B, C, Y, 0, 12, 512, 512, None, 0, None), 5),
+    ((A, 0, B, C, MISALIGNED, 0, 4, 512, 512, None, 0, None), 4),
+])
+def test_quant_gemm_validation(lib, args, expect):
+    assert lib.bfp8_quant_gemm_w8a8_blk128(*args) == expect
 
 
 def test_workspace_sizes(lib):

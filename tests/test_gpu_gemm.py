@@ -109,6 +109,39 @@ def test_w8a8_large_tile_ragged_sampled(gpu_lib):
     assert_fp32_bar(y32[rows], y0, "256x256 ragged sampled rows")
 
 
+@pytest.mark.parametrize("xdtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("M,N,K", [(1, 4096, 4096), (2, 1024, 4096), (3, 512, 640), (4, 384, 12288),
+                                   (5, 1024, 4096), (8, 512, 1024), (9, 512, 640), (16, 1024, 4096),
+                                   (17, 384, 640), (64, 1024, 4096), (300, 1040, 1024)])
+def test_quant_gemm_equals_quantise_then_gemm(gpu_lib, M, N, K, xdtype):
+    """The fused call is bit-identical to bfp8_quantize_act_1x128 followed by
+    bfp8_gemm_w8a8_blk128 (fp32 and 16-bit outputs), and meets the oracle bar.
+    bf16 cases include a zero row and rows whose group scales lie outside
+    [2^-90, 2^100] (the quantiser's IEEE-division path)."""
+    say("quant+w8a8", xdtype, f"M={M} N={N} K={K}")
+    x = inputs.activations(M, K, workload=900 + M, stream=K, outliers=True, dtype=xdtype).float()
+    if xdtype == torch.bfloat16 and M >= 3:
+        x[0] = 0.0
+        x[1] *= 2.0 ** -100
+        x[2] *= 2.0 ** 110
+    x = x.to(xdtype)
+    wq, ws = oracle.quantize_weight_128x128(f32(inputs.weights_bf16(N, K, workload=900 + N, stream=K)))
+    wqd, wsd, xd = dev(wq), dev(ws), x.cuda()
+    xq, xs = bfp8.quantize_act(xd)
+    wsb = workspace(bfp8.OP_QUANT_GEMM_W8A8_BLK128, M, N, K)
+    for out in (torch.float32, torch.bfloat16):
+        ref = run_w8a8(xq, xs, wqd, wsd, out)
+        y = torch.empty((M, N), dtype=out, device="cuda")
+        bfp8.bfp8_quant_gemm_w8a8_blk128(xd, wqd, wsd, y, wsb)
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16 if out != torch.float32 else torch.int32),
+                           ref.view(torch.int16 if out != torch.float32 else torch.int32)), out
+        if out == torch.float32:
+            q0, s0 = oracle.quantize_act_1x128(f32(x))
+            np.testing.assert_array_equal(xq.cpu().numpy(), q0)
+            assert_fp32_bar(y, oracle.gemm_w8a8_blk128(q0, s0, wq, ws), f"quant+w8a8 M={M}")
+
+
 def test_w8a8_decode_oproj_full(gpu_lib):
     """Decode o_proj M=1, N=K=4096: full oracle."""
     _w8a8_check(1, 4096, 4096, 1, what="o_proj decode")
