@@ -133,9 +133,11 @@ __global__ __launch_bounds__(kStreamThreads) void w8a8_stream_kernel(
 // ------------------------------------------- activation quant fused in ----
 // The same streaming GEMM for M <= kFusedQuantMaxM with 16-bit activations
 // in: each wave quantises, for every 128-K block it multiplies, the block's
-// 1x128 groups of the (at most 8) tokens itself ([ADA] "What's next": the
-// activation quant moved into the GEMM, removing a launch and the code
-// round trip at decode).  The 64 lanes split the padded token count Mp
+// 1x128 groups of the (at most 8) tokens itself.  [ADA] "Results on the L4"
+// counts the activation quantisation inside the kernel's time, and "What's
+// not good yet" names batch-1 decode, memory-bound, as the remaining gap;
+// fusing removes a launch and the codes' round trip through memory there.
+// The 64 lanes split the padded token count Mp
 // (1, 2, 4 or 8) evenly: 64/Mp lanes per token, 2 Mp values per lane, so no
 // lane quantises padding when M is small.  The group maximum is a
 // butterfly over the token's lanes; scale, quotients and codes use the

@@ -125,9 +125,10 @@ bfp8_status bfp8_gemm_w8a8_blk128(const uint8_t* xq, const float* xs,
                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Activation quantisation fused with the W8A8 blockwise GEMM ([ADA] "What's
- * next": the 1x128 activation quant moved into the GEMM; at decode it
- * removes a launch and the round trip of the codes through memory).
+ * Activation quantisation fused with the W8A8 blockwise GEMM.  [ADA]
+ * "Results on the L4" counts the activation quantisation inside the GEMM's
+ * time and "What's not good yet" names batch-1 decode as the gap; fusing
+ * removes a launch and the codes' round trip through memory at decode.
  * Computes exactly bfp8_quantize_act_1x128 followed by bfp8_gemm_w8a8_blk128
  * on the same arguments: the same codes, scales and per-block promotion, so
  * y is bit-identical to that pair of calls.
