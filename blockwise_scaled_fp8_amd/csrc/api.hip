@@ -27,7 +27,7 @@ bfp8_status check_gemm(const void* a, const void* b, const void* c, const void* 
                        const void* workspace, size_t workspace_bytes) {
     if (!a || !b || !c || !y) return BFP8_E_NULL;
     if (!dim_ok(M, 1) || !dim_ok(N, n_mult) || !dim_ok(K, 128)) return BFP8_E_SHAPE;
-    if (N % n_mult != 0 || K % 128 != 0) return BFP8_E_SHAPE;
+    if (N % n_mult != 0 || K % 128 != 0 || K > kTileMaxK) return BFP8_E_SHAPE;
     if (M * K >= ((int64_t)1 << 40) || N * K >= ((int64_t)1 << 40)) return BFP8_E_SHAPE;
     if (!is_out(y_dtype)) return BFP8_E_DTYPE;
     if (!aligned(a) || !aligned(b) || !aligned(c) || !aligned(y)) return BFP8_E_ALIGN;

@@ -15,8 +15,8 @@ namespace bfp8 {
 constexpr int64_t kStreamMaxM = BFP8_STREAM_MAX_M;
 // Rows of W covered by one streaming workgroup (one MFMA row tile).
 constexpr int64_t kStreamRows = 16;
-// Largest K of the tiled W8A8 kernels (256 rows x K bytes must fit the
-// 32-bit per-lane offsets of their buffer loads).
+// Largest K of every GEMM: the tiled kernels address 256 rows x K bytes and
+// the streaming kernels 16 rows x K bytes through 32-bit buffer offsets.
 constexpr int64_t kTileMaxK = (int64_t)1 << 23;
 // Workspace bytes of the tiled W8A8 kernels (split-K partial tiles and tile
 // counters; 0 when the shape is not split).

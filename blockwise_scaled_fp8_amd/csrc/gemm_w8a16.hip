@@ -60,7 +60,7 @@ __global__ __launch_bounds__(kStreamThreads) void w8a16_blk128_stream_kernel(
     __shared__ float red[kStreamWaves * 256];
     const int64_t nt = blockIdx.x, split = blockIdx.y, mt = blockIdx.z;
     const int64_t KB = K / 128;
-    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
     const int r = lane & 15, g = lane >> 4;
     const int64_t n = nt * 16 + r;
     const int64_t m = mt * 16 + r;
@@ -78,15 +78,18 @@ __global__ __launch_bounds__(kStreamThreads) void w8a16_blk128_stream_kernel(
     const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
     for (int64_t kb0 = kb_begin + wave; kb0 < kb_end; kb0 += kStreamWaves * kW8A16Chunk) {
         u32x4 wa[kW8A16Chunk][2], xb[kW8A16Chunk][4];
-        // Activations first (from L2), then the weight stream.
+        float wsv[kW8A16Chunk];
+        // Activations and weight scales first (from L2), then the weight
+        // stream; every load is issued before any wait (rows past M read row
+        // 0 and are zeroed by a select at use, so no load is in a divergent
+        // branch).
 #pragma unroll
         for (int c = 0; c < kW8A16Chunk; ++c) {
             const int64_t kb = kb0 + c * kStreamWaves;
             if (kb < kb_end) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    xb[c][j] = m_ok ? load_16B(xrow + kb * 128 + (j < 2 ? 8 * j : 64 + 8 * (j - 2)))
-                                    : u32x4{0u, 0u, 0u, 0u};
+                for (int j = 0; j < 4; ++j) xb[c][j] = load_16B(xrow + kb * 128 + (j < 2 ? 8 * j : 64 + 8 * (j - 2)));
+                wsv[c] = ws_row[kb];
             }
         }
 #pragma unroll
@@ -97,6 +100,7 @@ __global__ __launch_bounds__(kStreamThreads) void w8a16_blk128_stream_kernel(
                 wa[c][1] = load_16B(wrow + kb * 128 + 64);
             }
         }
+        asm volatile("" ::: "memory");   // compiler-only: all loads above before the first wait
 #pragma unroll
         for (int c = 0; c < kW8A16Chunk; ++c) {
             const int64_t kb = kb0 + c * kStreamWaves;
@@ -107,9 +111,10 @@ __global__ __launch_bounds__(kStreamThreads) void w8a16_blk128_stream_kernel(
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const u32x4 a = decode8<kXBf16>(q[2 * j], q[2 * j + 1]);
-                    blk = kXBf16 ? mfma_bf16_16x16x32(a, xb[c][j], blk) : mfma_f16_16x16x32(a, xb[c][j], blk);
+                    const u32x4 xv = m_ok ? xb[c][j] : u32x4{0u, 0u, 0u, 0u};
+                    blk = kXBf16 ? mfma_bf16_16x16x32(a, xv, blk) : mfma_f16_16x16x32(a, xv, blk);
                 }
-                const float sc = ws_row[kb] * bias_fold;
+                const float sc = wsv[c] * bias_fold;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(blk[i], sc, acc[i]);
             }
@@ -126,7 +131,7 @@ __global__ __launch_bounds__(kStreamThreads) void w8a16_blk32_stream_kernel(
     __shared__ float red[kStreamWaves * 256];
     const int64_t nt = blockIdx.x, split = blockIdx.y, mt = blockIdx.z;
     const int64_t KB = K / 128, K32 = K / 32;
-    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
     const int r = lane & 15, g = lane >> 4;
     const int64_t n = nt * 16 + r;
     const int64_t m = mt * 16 + r;
@@ -144,15 +149,14 @@ __global__ __launch_bounds__(kStreamThreads) void w8a16_blk32_stream_kernel(
     for (int64_t kb0 = kb_begin + wave; kb0 < kb_end; kb0 += kStreamWaves * kW8A16Chunk) {
         u32x4 wa[kW8A16Chunk][2], xb[kW8A16Chunk][4];
         uint32_t ebyte[kW8A16Chunk][2];
-        // Activations and scale bytes first (from L2), then the weight stream.
+        // Activations and scale bytes first (from L2), then the weight stream;
+        // every load is issued before any wait (rows past M: see above).
 #pragma unroll
         for (int c = 0; c < kW8A16Chunk; ++c) {
             const int64_t kb = kb0 + c * kStreamWaves;
             if (kb < kb_end) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    xb[c][j] = m_ok ? load_16B(xrow + kb * 128 + (j < 2 ? 8 * j : 64 + 8 * (j - 2)))
-                                    : u32x4{0u, 0u, 0u, 0u};
+                for (int j = 0; j < 4; ++j) xb[c][j] = load_16B(xrow + kb * 128 + (j < 2 ? 8 * j : 64 + 8 * (j - 2)));
                 ebyte[c][0] = erow[kb * 4];
                 ebyte[c][1] = erow[kb * 4 + 2];
             }
@@ -165,6 +169,7 @@ __global__ __launch_bounds__(kStreamThreads) void w8a16_blk32_stream_kernel(
                 wa[c][1] = load_16B(wrow + kb * 128 + 64);
             }
         }
+        asm volatile("" ::: "memory");   // compiler-only: all loads above before the first wait
 #pragma unroll
         for (int c = 0; c < kW8A16Chunk; ++c) {
             const int64_t kb = kb0 + c * kStreamWaves;
@@ -184,7 +189,7 @@ __global__ __launch_bounds__(kStreamThreads) void w8a16_blk32_stream_kernel(
                     const f16x2 factor = j < 2 ? factor0 : factor1;
                     const u32x4 a = {scale_f16x2(d0, factor), scale_f16x2(d1, factor),
                                      scale_f16x2(d2, factor), scale_f16x2(d3, factor)};
-                    acc = mfma_f16_16x16x32(a, xb[c][j], acc);
+                    acc = mfma_f16_16x16x32(a, m_ok ? xb[c][j] : u32x4{0u, 0u, 0u, 0u}, acc);
                 }
             }
         }

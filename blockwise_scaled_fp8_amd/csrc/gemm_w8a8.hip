@@ -56,13 +56,20 @@ size_t stream_workspace_bytes(const StreamPlan& p) {
 }
 
 // =================================================================== stream
-constexpr int kW8A8Chunk = 4;   // 128-K blocks per wave with loads in flight together
 
 // Lane (r, g) supplies weight row n0 + r and token m0 + r; of each 128-K
 // block it holds the 16-byte chunks g and g + 4 (K offsets 16g and 64 + 16g),
-// the same for both MFMA operands.  Each load instruction then reads whole
-// 64-byte halves of 16 weight rows.  The waves take interleaved 128-K
-// blocks, so at any time a workgroup reads adjacent blocks of its rows.
+// the same for both MFMA operands.  The waves take interleaved 128-K blocks,
+// so at any time a workgroup reads adjacent blocks of its rows.
+//
+// Every load of a chunk is issued before anything waits on one: token rows
+// and scales first (L2), then the weights (HBM).  Token rows past M are read
+// from row 0 (a valid address) and zeroed by a select afterwards, so no
+// load sits in a lane-divergent branch; such branches made the compiler wait
+// for each block's token loads before issuing the next block's, serialising
+// four L2 round trips ahead of the weight stream (measured 0.7 us).
+constexpr int kStreamChunk = 4;   // 128-K blocks per wave with loads in flight together
+
 __global__ __launch_bounds__(kStreamThreads) void w8a8_stream_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ xs,
     const uint8_t* __restrict__ wq, const float* __restrict__ ws,
@@ -72,58 +79,57 @@ __global__ __launch_bounds__(kStreamThreads) void w8a8_stream_kernel(
     __shared__ float red[kStreamWaves * 256];
     const int64_t nt = blockIdx.x, split = blockIdx.y, mt = blockIdx.z;
     const int64_t KB = K / 128;
-    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
     const int r = lane & 15, g = lane >> 4;
 
-    const int64_t n = nt * 16 + r;                 // weight row supplied by this lane
     const int64_t m = mt * 16 + r;                 // token supplied by this lane (and its output column)
     const bool m_ok = m < M;
     const int64_t kb_begin = split * kb_per_split;
     const int64_t kb_end = kb_begin + kb_per_split < KB ? kb_begin + kb_per_split : KB;
 
-    const uint8_t* wrow = wq + n * K + g * 16;
+    const uint8_t* wrow = wq + (nt * 16 + r) * K + g * 16;
     const uint8_t* xrow = xq + (m_ok ? m : 0) * K + g * 16;
     const float* ws_row = ws + (nt * 16 / 128) * KB;
     const float* xs_row = xs + (m_ok ? m : 0) * KB;
 
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
     const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int64_t kb0 = kb_begin + wave; kb0 < kb_end; kb0 += kStreamWaves * kW8A8Chunk) {
-        u32x4 wa[kW8A8Chunk][2], xb[kW8A8Chunk][2];
-        float sc[kW8A8Chunk];
-        // Token codes and scales first: they come from L2 and their latency
-        // then hides under the weight stream instead of trailing it.
+    const u32x4 zero4 = {0u, 0u, 0u, 0u};
+    for (int64_t kb0 = kb_begin + wave; kb0 < kb_end; kb0 += kStreamWaves * kStreamChunk) {
+        u32x4 wa[kStreamChunk][2], xb[kStreamChunk][2];
+        float xsv[kStreamChunk], wsv[kStreamChunk];
 #pragma unroll
-        for (int c = 0; c < kW8A8Chunk; ++c) {
+        for (int c = 0; c < kStreamChunk; ++c) {
             const int64_t kb = kb0 + c * kStreamWaves;
             if (kb < kb_end) {
-                if (m_ok) {
-                    xb[c][0] = load_16B(xrow + kb * 128);
-                    xb[c][1] = load_16B(xrow + kb * 128 + 64);
-                    sc[c] = xs_row[kb] * ws_row[kb];
-                } else {
-                    xb[c][0] = xb[c][1] = u32x4{0u, 0u, 0u, 0u};
-                    sc[c] = 0.0f;
-                }
+                xb[c][0] = load_16B(xrow + kb * 128);
+                xb[c][1] = load_16B(xrow + kb * 128 + 64);
+                xsv[c] = xs_row[kb];
+                wsv[c] = ws_row[kb];
             }
         }
 #pragma unroll
-        for (int c = 0; c < kW8A8Chunk; ++c) {
+        for (int c = 0; c < kStreamChunk; ++c) {
             const int64_t kb = kb0 + c * kStreamWaves;
             if (kb < kb_end) {
                 wa[c][0] = load_16B(wrow + kb * 128);
                 wa[c][1] = load_16B(wrow + kb * 128 + 64);
             }
         }
+        // Compiler-only barrier: keeps every load above issued before the
+        // first wait below (the scheduler otherwise sinks some of them).
+        asm volatile("" ::: "memory");
 #pragma unroll
-        for (int c = 0; c < kW8A8Chunk; ++c) {
+        for (int c = 0; c < kStreamChunk; ++c) {
             const int64_t kb = kb0 + c * kStreamWaves;
             if (kb < kb_end) {
+                const u32x4 x0 = m_ok ? xb[c][0] : zero4, x1 = m_ok ? xb[c][1] : zero4;
+                const float sc = m_ok ? xsv[c] * wsv[c] : 0.0f;
                 const i32x8 a = __builtin_bit_cast(i32x8, __builtin_shufflevector(wa[c][0], wa[c][1], 0, 1, 2, 3, 4, 5, 6, 7));
-                const i32x8 b = __builtin_bit_cast(i32x8, __builtin_shufflevector(xb[c][0], xb[c][1], 0, 1, 2, 3, 4, 5, 6, 7));
+                const i32x8 b = __builtin_bit_cast(i32x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
                 const f32x4 blk = mfma_e4m3_16x16x128(a, b, zero);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(blk[i], sc[c], acc[i]);
+                for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(blk[i], sc, acc[i]);
             }
         }
     }
@@ -187,9 +193,10 @@ __global__ __launch_bounds__(kStreamThreads) void w8a8_stream_quant_kernel(
     constexpr int kV = 128 / kL;             // values per lane (2 Mp)
     __shared__ float red[kStreamWaves * 256];
     __shared__ __attribute__((aligned(16))) uint8_t xcode[kStreamWaves][kFusedChunk][kMp][128];
+    __shared__ __attribute__((aligned(1024))) uint8_t wslab[kStreamWaves][kFusedChunk][kSlabBytes];
     const int64_t nt = blockIdx.x, split = blockIdx.y;
     const int64_t KB = K / 128;
-    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
     const int r = lane & 15, g = lane >> 4;
     const int64_t kb_begin = split * kb_per_split;
     const int64_t kb_end = kb_begin + kb_per_split < KB ? kb_begin + kb_per_split : KB;
@@ -200,7 +207,8 @@ __global__ __launch_bounds__(kStreamThreads) void w8a8_stream_quant_kernel(
     const uint16_t* xrow = x + (qt_ok ? qt : 0) * K + qp * kV;
     // MFMA role: weight row n0 + r, token r (rows r >= kMp are padding).
     const bool r_ok = r < kMp;
-    const uint8_t* wrow = wq + (nt * 16 + r) * K + g * 16;
+    const i32x4 rsrc_w = buffer_rsrc(wq + nt * 16 * K, (uint32_t)(16 * K));
+    const int lane_off_w = slab_lane_offset(lane, K);
     const float* ws_row = ws + (nt * 16 / 128) * KB;
 
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -212,28 +220,30 @@ __global__ __launch_bounds__(kStreamThreads) void w8a8_stream_quant_kernel(
         for (int c = 0; c < kFusedChunk; ++c) {
             const int64_t kb = kb0 + c * kStreamWaves;
             if (kb < kb_end) {
-                if (qt_ok) {
-                    load_words<kV / 2>(xrow + kb * 128, raw[c]);
-                } else {
-#pragma unroll
-                    for (int i = 0; i < kV / 2; ++i) raw[c][i] = 0u;
-                }
+                load_words<kV / 2>(xrow + kb * 128, raw[c]);   // rows past M read row 0, zeroed below
             }
         }
 #pragma unroll
         for (int c = 0; c < kFusedChunk; ++c) {
             const int64_t kb = kb0 + c * kStreamWaves;
-            if (kb < kb_end) {
-                wa[c][0] = load_16B(wrow + kb * 128);
-                wa[c][1] = load_16B(wrow + kb * 128 + 64);
-            }
+            if (kb < kb_end) slab_issue(wslab[wave][c], rsrc_w, lane_off_w, K, kb);
         }
+        float wsv[kFusedChunk];
+#pragma unroll
+        for (int c = 0; c < kFusedChunk; ++c) {
+            const int64_t kb = kb0 + c * kStreamWaves;
+            if (kb < kb_end) wsv[c] = ws_row[kb];
+        }
+        wait_all_loads();
 #pragma unroll
         for (int c = 0; c < kFusedChunk; ++c) {
             const int64_t kb = kb0 + c * kStreamWaves;
             if (kb < kb_end) {
+                slab_read(wslab[wave][c], r, g, wa[c][0], wa[c][1]);
                 float v[kV];
                 float amax = 0.0f;
+#pragma unroll
+                for (int i = 0; i < kV / 2; ++i) raw[c][i] = qt_ok ? raw[c][i] : 0u;
 #pragma unroll
                 for (int i = 0; i < kV / 2; ++i) {
                     v[2 * i] = kBf16 ? bf16_bits_to_float(raw[c][i] & 0xFFFFu) : f16_bits_to_float(raw[c][i] & 0xFFFFu);
@@ -248,7 +258,7 @@ __global__ __launch_bounds__(kStreamThreads) void w8a8_stream_quant_kernel(
                 store_codes<kV>(&xcode[wave][c][qt][qp * kV], codes);
                 // This MFMA lane's token scale, from the first lane of token r.
                 const float s_r = __shfl(s, (r_ok ? r : 0) * kL, kWave);
-                const float sc = r_ok ? s_r * ws_row[kb] : 0.0f;
+                const float sc = r_ok ? s_r * wsv[c] : 0.0f;
                 u32x4 b0 = {0u, 0u, 0u, 0u}, b1 = {0u, 0u, 0u, 0u};
                 if (r_ok) {
                     b0 = *reinterpret_cast<const u32x4*>(&xcode[wave][c][r][16 * g]);

@@ -42,6 +42,41 @@ inline void stream_workspace_parts(const StreamPlan& p, void* ws, uint32_t*& cou
     partials = reinterpret_cast<float*>(static_cast<char*>(ws) + stream_counter_bytes(p));
 }
 
+// ------------------------------------------------------ weight slabs ----
+// The 16 weight rows of one 128-K block (2 KB), staged in LDS with two
+// direct-to-LDS loads of whole 128-byte lines (8 rows each): a load
+// instruction then covers 8 full cache lines instead of 16 half lines,
+// which a read probe measured at 3.99 vs 4.64 us for 16 MiB.  Lane l of
+// each load fetches row l/8 (+ 8), chunk (l%8) ^ (row & 7); the MFMA
+// operand of lane (r, g) is then chunks g and g + 4 of row r, read back at
+// positions c ^ (r & 7) (16 consecutive rows: conflict-free).
+constexpr int kSlabBytes = 16 * 128;
+
+// Lane offset of this lane's slab loads inside a 16-row window of W.
+__device__ __forceinline__ int slab_lane_offset(int lane, int64_t K) {
+    return (int)((lane >> 3) * K) + (((lane & 7) ^ ((lane >> 3) & 7)) << 4);
+}
+
+// Issue the two loads of block kb of the 16 rows that `rsrc` covers.
+__device__ __forceinline__ void slab_issue(uint8_t* slab, i32x4 rsrc, int lane_off, int64_t K, int64_t kb) {
+    const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_address(slab));
+    const int k_off = __builtin_amdgcn_readfirstlane((int)(kb * 128));
+    dma16(lds, rsrc, lane_off, 0, k_off);
+    dma16(lds + 1024, rsrc, lane_off, __builtin_amdgcn_readfirstlane((int)(8 * K)), k_off);
+}
+
+// Wait for every outstanding vector-memory load of this wave (the slab
+// loads are invisible to the compiler's own waits); also a compiler
+// barrier, so no LDS read of a slab moves above it.
+__device__ __forceinline__ void wait_all_loads() {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+__device__ __forceinline__ void slab_read(const uint8_t* slab, int r, int g, u32x4& lo, u32x4& hi) {
+    lo = *reinterpret_cast<const u32x4*>(slab + r * 128 + ((g ^ (r & 7)) << 4));
+    hi = *reinterpret_cast<const u32x4*>(slab + r * 128 + (((g + 4) ^ (r & 7)) << 4));
+}
+
 __device__ __forceinline__ void store_out(void* y, int y_dtype, int64_t idx, float v) {
     if (y_dtype == 2) {
         static_cast<float*>(y)[idx] = v;

@@ -117,7 +117,7 @@ bfp8_status bfp8_quantize_weight_128x128(const void* w, int w_dtype, int64_t N, 
  *       BFP8_OP_GEMM_W8A8_BLK128, M, N, K) bytes (may be NULL when that is 0).
  *       It must be zero-filled before its first use; every call leaves it
  *       ready for the next.  Calls that overlap in time must not share one.
- * Requires M >= 1, N >= 16, N % 16 == 0, K >= 128, K % 128 == 0.
+ * Requires M >= 1, N >= 16, N % 16 == 0, K >= 128, K % 128 == 0, K <= 2^23.
  */
 bfp8_status bfp8_gemm_w8a8_blk128(const uint8_t* xq, const float* xs,
                                   const uint8_t* wq, const float* ws,
@@ -139,7 +139,7 @@ bfp8_status bfp8_gemm_w8a8_blk128(const uint8_t* xq, const float* xs,
  *       next call; calls that overlap in time must not share one.  For M <= 8
  *       the streaming kernel quantises in registers; above that the codes and
  *       scales are staged in the workspace by the 1x128 quantiser.
- * Requires M >= 1, N >= 16, N % 16 == 0, K >= 128, K % 128 == 0.
+ * Requires M >= 1, N >= 16, N % 16 == 0, K >= 128, K % 128 == 0, K <= 2^23.
  */
 bfp8_status bfp8_quant_gemm_w8a8_blk128(const void* x, int x_dtype,
                                         const uint8_t* wq, const float* ws,
@@ -155,7 +155,7 @@ bfp8_status bfp8_quant_gemm_w8a8_blk128(const void* x, int x_dtype,
  *   Y[m, n] = sum_kb ws[n / 128, kb] * sum over k in kb of x[m, k] * E4M3(wq[n, k])
  *   x   [M, K] bf16 or fp16, wq [N, K] E4M3, ws [ceil(N/128), K/128] fp32.
  *   y   [M, N] in y_dtype (BF16 / F16 / F32); workspace as for W8A8.
- * Requires M >= 1, N % 16 == 0, K % 128 == 0.
+ * Requires M >= 1, N % 16 == 0, K % 128 == 0, K <= 2^23.
  */
 bfp8_status bfp8_gemm_w8a16_blk128(const void* x, int x_dtype,
                                    const uint8_t* wq, const float* ws,
@@ -173,7 +173,7 @@ bfp8_status bfp8_gemm_w8a16_blk128(const void* x, int x_dtype,
  *   e8m0  [N/32, K/32] bytes E, produced by bfp8_prepare_blk32_ue8m0
  *         (trusted: E must lie in [113, 134]).
  *   y     [M, N] in y_dtype (F16 / BF16 / F32); workspace as for W8A8.
- * Requires M >= 1, N % 32 == 0, K % 128 == 0.
+ * Requires M >= 1, N % 32 == 0, K % 128 == 0, K <= 2^23.
  */
 bfp8_status bfp8_gemm_w8a16_blk32_ue8m0(const void* x, int x_dtype,
                                         const uint8_t* wq, const uint8_t* e8m0,

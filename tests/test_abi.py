@@ -139,7 +139,8 @@ def _w8a8(M=4, N=512, K=512, y_dtype=0, xq=A, ws_ptr=C, y=Y, workspace=None, wby
     (dict(y_dtype=7), 3),
     (dict(y=MISALIGNED), 4),
     (dict(M=1, N=1024, K=4096), 5),                   # split-K plan needs a workspace
-    (dict(M=64, N=256, K=(1 << 23) + 128), 2),        # tiled kernel's K limit
+    (dict(M=64, N=256, K=(1 << 23) + 128), 2),        # K limit (tiled kernel)
+    (dict(M=1, N=256, K=(1 << 23) + 128), 2),         # K limit (streaming kernel)
     (dict(M=100, N=1024, K=4096), 5),                 # mid-M split-K plan needs a workspace
 ])
 def test_w8a8_validation(lib, kw, expect):
