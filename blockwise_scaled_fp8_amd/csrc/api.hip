@@ -68,10 +68,10 @@ namespace {
 
 size_t round256(size_t v) { return (v + 255) / 256 * 256; }
 
-// W8A8 workspace for codes input: the streaming plan's for M <= kStreamMaxM,
-// the tiled kernels' above.
+// W8A8 workspace for codes input: the streaming plan's or the tiled kernels'
+// (w8a8_streams decides).
 size_t w8a8_workspace(int64_t M, int64_t N, int64_t K) {
-    if (M <= kStreamMaxM) return stream_workspace_bytes(plan_stream(M, N, K));
+    if (w8a8_streams(M, N, K)) return stream_workspace_bytes(plan_stream_w8a8(M, N, K));
     return K <= kTileMaxK ? tile_workspace_bytes(M, N, K) : 0;
 }
 
@@ -101,8 +101,7 @@ size_t bfp8_workspace_bytes(int op, int64_t M, int64_t N, int64_t K) {
             if (M <= kFusedQuantMaxM) return stream_workspace_bytes(plan_stream(M, N, K));
             return K <= kTileMaxK ? quant_gemm_parts(M, N, K).total : 0;
         case BFP8_OP_GEMM_W8A8_BLK128:
-            if (M > kStreamMaxM) return K <= kTileMaxK ? tile_workspace_bytes(M, N, K) : 0;
-            return stream_workspace_bytes(plan_stream(M, N, K));
+            return w8a8_workspace(M, N, K);
         case BFP8_OP_GEMM_W8A16_BLK128:
         case BFP8_OP_GEMM_W8A16_BLK32_UE8M0:
             return stream_workspace_bytes(plan_stream(M, N, K));
@@ -120,10 +119,8 @@ bfp8_status bfp8_gemm_w8a8_blk128(const uint8_t* xq, const float* xs, const uint
     bfp8_status st = check_gemm(xq, wq, ws, y, y_dtype, M, N, K, 16, need, workspace, workspace_bytes);
     if (st != BFP8_OK) return st;
     if (!aligned(xs)) return BFP8_E_ALIGN;
-    if (M <= kStreamMaxM)
+    if (w8a8_streams(M, N, K))
         return launched(launch_w8a8_stream(xq, xs, wq, ws, y, y_dtype, M, N, K, workspace, as_stream(stream)));
-    // The tiled kernels address a 256-row slab of W through 32-bit offsets.
-    if (K > kTileMaxK) return BFP8_E_SHAPE;
     return launched(launch_w8a8_tile(xq, xs, wq, ws, y, y_dtype, M, N, K, workspace, as_stream(stream)));
 }
 
@@ -148,7 +145,7 @@ bfp8_status bfp8_quant_gemm_w8a8_blk128(const void* x, int x_dtype, const uint8_
     void* gemm_ws = parts.gemm ? workspace : nullptr;
     hipError_t e = launch_quant_act_1x128(x, x_dtype == BFP8_BF16, M, K, xq, xs, as_stream(stream));
     if (e != hipSuccess) return BFP8_E_LAUNCH;
-    if (M <= kStreamMaxM)
+    if (w8a8_streams(M, N, K))
         return launched(launch_w8a8_stream(xq, xs, wq, ws, y, y_dtype, M, N, K, gemm_ws, as_stream(stream)));
     return launched(launch_w8a8_tile(xq, xs, wq, ws, y, y_dtype, M, N, K, gemm_ws, as_stream(stream)));
 }

@@ -8,11 +8,20 @@
 
 namespace bfp8 {
 
-// Largest M served by the weight-streaming (decode) kernel of W8A8.
+// Largest M that the W8A8 codes path always serves with the weight-streaming
+// kernel.
 #ifndef BFP8_STREAM_MAX_M
 #define BFP8_STREAM_MAX_M 16
 #endif
 constexpr int64_t kStreamMaxM = BFP8_STREAM_MAX_M;
+// W8A8 dispatch (codes in), from the projection sweep: the streaming kernel
+// for M <= 16, and with two 16-token tiles per workgroup for M <= 32 on
+// projections of at most 2^24 weights (4096 x 4096: 10.5 vs 12.2 us tiled;
+// 1024 x 4096: 8.4 vs 9.8 us), the tiled kernels otherwise (12288 x 4096 at
+// M = 32: 22.4 us tiled vs 28.2 us streamed).
+inline bool w8a8_streams(int64_t M, int64_t N, int64_t K) {
+    return M <= kStreamMaxM || (M <= 2 * kStreamMaxM && N * K <= ((int64_t)1 << 24));
+}
 // Rows of W covered by one streaming workgroup (one MFMA row tile).
 constexpr int64_t kStreamRows = 16;
 // Largest K of every GEMM: the tiled kernels address 256 rows x K bytes and
@@ -22,12 +31,16 @@ constexpr int64_t kTileMaxK = (int64_t)1 << 23;
 // counters; 0 when the shape is not split).
 size_t tile_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
-// Split-K plan of a streaming kernel: `splits` workgroups share one
-// (16-row, 16-token) output tile, each covering `kb_per_split` 128-K blocks.
+// Split-K plan of a streaming kernel: a workgroup covers 16 weight rows and
+// `mt_per_wg` 16-token tiles; `splits` workgroups share one such block of
+// output tiles, each covering `kb_per_split` 128-K blocks.  Counters and
+// partial tiles are kept per 16x16 output tile.
 struct StreamPlan {
-    int64_t n_tiles, m_tiles, splits, kb_per_split;
+    int64_t n_tiles, m_tiles, mt_per_wg, splits, kb_per_split;
 };
-StreamPlan plan_stream(int64_t M, int64_t N, int64_t K);
+StreamPlan plan_stream(int64_t M, int64_t N, int64_t K, int64_t mt_per_wg = 1);
+// The W8A8 codes kernel's plan: 1 or 2 token tiles per workgroup by M.
+StreamPlan plan_stream_w8a8(int64_t M, int64_t N, int64_t K);
 // Workspace bytes of a streaming plan: tile counters, then fp32 partial tiles.
 size_t stream_workspace_bytes(const StreamPlan& p);
 

@@ -34,19 +34,24 @@
 namespace bfp8 {
 
 // ===================================================================== plan
-StreamPlan plan_stream(int64_t M, int64_t N, int64_t K) {
+StreamPlan plan_stream(int64_t M, int64_t N, int64_t K, int64_t mt_per_wg) {
     StreamPlan p;
     p.n_tiles = N / kStreamRows;
     p.m_tiles = (M + 15) / 16;
+    p.mt_per_wg = mt_per_wg;
     const int64_t KB = K / 128;
     // Enough workgroups to give each of the 256 CUs one, while at least half
     // of a workgroup's waves still get a 128-K block.
-    const int64_t tiles = p.n_tiles * p.m_tiles;
+    const int64_t tiles = p.n_tiles * ((p.m_tiles + mt_per_wg - 1) / mt_per_wg);
     int64_t splits = 1;
     while (tiles * splits < 256 && 2 * (KB / (splits * 2)) >= kStreamWaves) splits *= 2;
     p.splits = splits;
     p.kb_per_split = (KB + splits - 1) / splits;
     return p;
+}
+
+StreamPlan plan_stream_w8a8(int64_t M, int64_t N, int64_t K) {
+    return plan_stream(M, N, K, M <= 16 ? 1 : 2);
 }
 
 size_t stream_workspace_bytes(const StreamPlan& p) {
@@ -68,48 +73,64 @@ size_t stream_workspace_bytes(const StreamPlan& p) {
 // load sits in a lane-divergent branch; such branches made the compiler wait
 // for each block's token loads before issuing the next block's, serialising
 // four L2 round trips ahead of the weight stream (measured 0.7 us).
-constexpr int kStreamChunk = 4;   // 128-K blocks per wave with loads in flight together
-
+//
+// One or two 16-token tiles per workgroup (kMT): with two, the weights are
+// read once for 32 tokens, each wave issuing two MFMAs per block on the same
+// weight fragment, and two blocks per wave (not four) are kept in flight so
+// the registers stay within 128 at sixteen waves.
+template <int kMT>
 __global__ __launch_bounds__(kStreamThreads) void w8a8_stream_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ xs,
     const uint8_t* __restrict__ wq, const float* __restrict__ ws,
     void* __restrict__ y, int y_dtype, int64_t M, int64_t N, int64_t K,
     int64_t n_tiles, int64_t splits, int64_t kb_per_split,
     float* __restrict__ partials, uint32_t* __restrict__ counters) {
+    constexpr int kChunk = kMT == 1 ? 4 : 2;      // 128-K blocks per wave with loads in flight together
     __shared__ float red[kStreamWaves * 256];
-    const int64_t nt = blockIdx.x, split = blockIdx.y, mt = blockIdx.z;
+    const int64_t nt = blockIdx.x, split = blockIdx.y, mt0 = blockIdx.z * kMT;
     const int64_t KB = K / 128;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
     const int r = lane & 15, g = lane >> 4;
 
-    const int64_t m = mt * 16 + r;                 // token supplied by this lane (and its output column)
-    const bool m_ok = m < M;
     const int64_t kb_begin = split * kb_per_split;
     const int64_t kb_end = kb_begin + kb_per_split < KB ? kb_begin + kb_per_split : KB;
 
     const uint8_t* wrow = wq + (nt * 16 + r) * K + g * 16;
-    const uint8_t* xrow = xq + (m_ok ? m : 0) * K + g * 16;
     const float* ws_row = ws + (nt * 16 / 128) * KB;
-    const float* xs_row = xs + (m_ok ? m : 0) * KB;
+    bool m_ok[kMT];
+    const uint8_t* xrow[kMT];
+    const float* xs_row[kMT];
+#pragma unroll
+    for (int t = 0; t < kMT; ++t) {
+        const int64_t m = (mt0 + t) * 16 + r;     // token supplied by this lane for tile t
+        m_ok[t] = m < M;
+        xrow[t] = xq + (m_ok[t] ? m : 0) * K + g * 16;
+        xs_row[t] = xs + (m_ok[t] ? m : 0) * KB;
+    }
 
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    f32x4 acc[kMT];
+#pragma unroll
+    for (int t = 0; t < kMT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
     const u32x4 zero4 = {0u, 0u, 0u, 0u};
-    for (int64_t kb0 = kb_begin + wave; kb0 < kb_end; kb0 += kStreamWaves * kStreamChunk) {
-        u32x4 wa[kStreamChunk][2], xb[kStreamChunk][2];
-        float xsv[kStreamChunk], wsv[kStreamChunk];
+    for (int64_t kb0 = kb_begin + wave; kb0 < kb_end; kb0 += kStreamWaves * kChunk) {
+        u32x4 wa[kChunk][2], xb[kChunk][kMT][2];
+        float xsv[kChunk][kMT], wsv[kChunk];
 #pragma unroll
-        for (int c = 0; c < kStreamChunk; ++c) {
+        for (int c = 0; c < kChunk; ++c) {
             const int64_t kb = kb0 + c * kStreamWaves;
             if (kb < kb_end) {
-                xb[c][0] = load_16B(xrow + kb * 128);
-                xb[c][1] = load_16B(xrow + kb * 128 + 64);
-                xsv[c] = xs_row[kb];
+#pragma unroll
+                for (int t = 0; t < kMT; ++t) {
+                    xb[c][t][0] = load_16B(xrow[t] + kb * 128);
+                    xb[c][t][1] = load_16B(xrow[t] + kb * 128 + 64);
+                    xsv[c][t] = xs_row[t][kb];
+                }
                 wsv[c] = ws_row[kb];
             }
         }
 #pragma unroll
-        for (int c = 0; c < kStreamChunk; ++c) {
+        for (int c = 0; c < kChunk; ++c) {
             const int64_t kb = kb0 + c * kStreamWaves;
             if (kb < kb_end) {
                 wa[c][0] = load_16B(wrow + kb * 128);
@@ -120,20 +141,30 @@ __global__ __launch_bounds__(kStreamThreads) void w8a8_stream_kernel(
         // first wait below (the scheduler otherwise sinks some of them).
         asm volatile("" ::: "memory");
 #pragma unroll
-        for (int c = 0; c < kStreamChunk; ++c) {
+        for (int c = 0; c < kChunk; ++c) {
             const int64_t kb = kb0 + c * kStreamWaves;
             if (kb < kb_end) {
-                const u32x4 x0 = m_ok ? xb[c][0] : zero4, x1 = m_ok ? xb[c][1] : zero4;
-                const float sc = m_ok ? xsv[c] * wsv[c] : 0.0f;
                 const i32x8 a = __builtin_bit_cast(i32x8, __builtin_shufflevector(wa[c][0], wa[c][1], 0, 1, 2, 3, 4, 5, 6, 7));
-                const i32x8 b = __builtin_bit_cast(i32x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
-                const f32x4 blk = mfma_e4m3_16x16x128(a, b, zero);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(blk[i], sc, acc[i]);
+                for (int t = 0; t < kMT; ++t) {
+                    const u32x4 x0 = m_ok[t] ? xb[c][t][0] : zero4, x1 = m_ok[t] ? xb[c][t][1] : zero4;
+                    const float sc = m_ok[t] ? xsv[c][t] * wsv[c] : 0.0f;
+                    const i32x8 b = __builtin_bit_cast(i32x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
+                    const f32x4 blk = mfma_e4m3_16x16x128(a, b, zero);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[t][i] = __builtin_fmaf(blk[i], sc, acc[t][i]);
+                }
             }
         }
     }
-    stream_finish(acc, red, y, y_dtype, M, N, nt, mt, splits, split, n_tiles, partials, counters);
+    // One reduction per live token tile (tiles wholly past M are skipped:
+    // their counters do not exist); a barrier separates the uses of `red`.
+#pragma unroll
+    for (int t = 0; t < kMT; ++t) {
+        if ((mt0 + t) * 16 >= M) break;
+        if (t > 0) __syncthreads();
+        stream_finish(acc[t], red, y, y_dtype, M, N, nt, mt0 + t, splits, split, n_tiles, partials, counters);
+    }
 }
 
 // ------------------------------------------- activation quant fused in ----
@@ -278,13 +309,20 @@ __global__ __launch_bounds__(kStreamThreads) void w8a8_stream_quant_kernel(
 hipError_t launch_w8a8_stream(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
                               void* y, int y_dtype, int64_t M, int64_t N, int64_t K,
                               void* workspace, hipStream_t stream) {
-    const StreamPlan p = plan_stream(M, N, K);
+    const StreamPlan p = plan_stream_w8a8(M, N, K);
     uint32_t* counters;
     float* partials;
     stream_workspace_parts(p, workspace, counters, partials);
-    hipLaunchKernelGGL(w8a8_stream_kernel, dim3((unsigned)p.n_tiles, (unsigned)p.splits, (unsigned)p.m_tiles),
-                       dim3(kStreamThreads), 0, stream, xq, xs, wq, ws, y, y_dtype, M, N, K,
-                       p.n_tiles, p.splits, p.kb_per_split, partials, counters);
+    const dim3 grid((unsigned)p.n_tiles, (unsigned)p.splits, (unsigned)((p.m_tiles + p.mt_per_wg - 1) / p.mt_per_wg));
+#define BFP8_LAUNCH_MT(MT)                                                                                      \
+    hipLaunchKernelGGL(w8a8_stream_kernel<MT>, grid, dim3(kStreamThreads), 0, stream, xq, xs, wq, ws, y, y_dtype, M, \
+                       N, K, p.n_tiles, p.splits, p.kb_per_split, partials, counters)
+    if (p.mt_per_wg == 1) {
+        BFP8_LAUNCH_MT(1);
+    } else {
+        BFP8_LAUNCH_MT(2);
+    }
+#undef BFP8_LAUNCH_MT
     return hipGetLastError();
 }
 

@@ -209,8 +209,10 @@ size_t bfp8_workspace_bytes(int op, int64_t M, int64_t N, int64_t K);
  *   k_multiple    K must be a multiple of this.
  *   n_multiple    N must be a multiple of this.
  *   align_bytes   required alignment of every device pointer.
- *   m_stream_max  largest M served by the weight-streaming decode kernel
- *                 (larger M goes to the tiled MFMA kernel where one exists).
+ *   m_stream_max  largest M always served by the weight-streaming decode
+ *                 kernel.  W8A8 also streams M <= 2 * m_stream_max when
+ *                 N * K <= 2^24 (measured faster there); other M go to the
+ *                 tiled MFMA kernels.  W8A16 always streams.
  * Any output pointer may be NULL.
  */
 bfp8_status bfp8_get_limits(int op, int64_t* k_multiple, int64_t* n_multiple,

@@ -95,8 +95,13 @@ def test_workspace_sizes(lib):
     assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 1, 1024, 4096) > 0
     assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 4096, 1024, 4096) == 0   # 128x128 tiles
     assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 4096, 4096, 4096) == 0   # 256x256 tiles
-    # mid M: 64-token tiles, K split 8 ways -> counters + 8 fp32 partial tiles per output tile
-    assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 64, 4096, 4096) == 256 + 32 * 8 * 128 * 64 * 4
+    # M = 32 on a 1024 x 4096 projection streams two token tiles per workgroup:
+    # 64 workgroups, K split 4 ways -> counters + partials per 16x16 tile
+    assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 32, 1024, 4096) == 512 + 64 * 2 * 4 * 256 * 4
+    # ... while 12288 x 4096 at M = 32 is tiled (128x64 tiles, K split 4 ways)
+    assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 32, 12288, 4096) == 512 + 96 * 4 * 128 * 64 * 4
+    # mid M: 64x128 tiles, K split 4 ways -> counters + 4 fp32 partial tiles per output tile
+    assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 100, 4096, 4096) == 256 + 64 * 4 * 64 * 128 * 4
     assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 64, 384, 640) == 0      # K too short to split
     assert bfp8.bfp8_workspace_bytes(bfp8.OP_QUANT_ACT_1X128, 1, 4096, 4096) == 0
 

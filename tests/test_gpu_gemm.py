@@ -45,7 +45,7 @@ def test_w8a8_workload0(gpu_lib):
     _w8a8_check(4, 512, 512, 0, what="workload 0")
 
 
-@pytest.mark.parametrize("M", [1, 2, 3, 5, 8, 15, 16, 17, 31, 64, 129, 200])
+@pytest.mark.parametrize("M", [1, 2, 3, 5, 8, 15, 16, 17, 24, 31, 32, 33, 48, 63, 64, 65, 129, 200])
 def test_w8a8_across_the_stream_tile_threshold(gpu_lib, M):
     _w8a8_check(M, 384, 640, 300 + M, what="threshold")
 
@@ -57,7 +57,7 @@ def test_w8a8_weight_scale_rows_straddle(gpu_lib, M, N):
     _w8a8_check(M, N, 256, 400 + N + M, what="straddle")
 
 
-@pytest.mark.parametrize("M", [1, 4, 16])
+@pytest.mark.parametrize("M", [1, 4, 16, 24, 32])
 def test_w8a8_split_k_narrow_projection(gpu_lib, M):
     """k/v-shaped N=1024, K=4096 takes the split-K plan; run twice (counters re-arm)."""
     assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, M, 1024, 4096) > 0
@@ -73,7 +73,8 @@ def test_w8a8_split_k_narrow_projection(gpu_lib, M):
 
 
 @pytest.mark.parametrize("M,N,K,shape", [
-    (40, 1024, 4096, "128x64, 8 splits"),
+    (40, 2048, 4096, "128x64, 8 splits"),
+    (65, 1024, 4096, "64x128, 8 splits"),
     (100, 1024, 4096, "64x128, 8 splits"),
     (200, 2048, 2176, "64x128, 4 splits, last split shorter"),
     (300, 1040, 1024, "64x128, 2 splits, ragged N"),
