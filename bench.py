@@ -12,6 +12,9 @@ Workloads (synthetic, seeded; inputs resident in HBM before timing starts):
            activation quantisation + W8A8 GEMM.  Headline: TFLOP/s.
   blk32    block-32 UE8M0 weight-only GEMM, N=4096, K=7168, M=--m (default 1).
            Headline: HBM GB/s.
+  w8a16    W8A16 blk128 GEMM alone, N=K=4096, bf16 activations, M=--m
+           (default 4096; M > 16 runs the tiled MFMA kernel).  Headline:
+           TFLOP/s against the bf16 MFMA peak (HBM GB/s for M <= 16).
   sweep    W8A8 over the projections (N x K) 4096x4096, 1024x4096, 12288x4096,
            4096x12288 and M in {1, 2, 4, 8, 16, 32, 64, 128, 512, 4096}; weights
            rotate over copies totalling >= 512 MiB per shape.  Per point: GEMM
@@ -49,7 +52,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", choices=["decode", "prefill", "blk32", "sweep"], default="decode")
+    p.add_argument("--workload", choices=["decode", "prefill", "blk32", "w8a16", "sweep"], default="decode")
     p.add_argument("--m", type=int, default=None, help="token count for blk32 / decode")
     p.add_argument("--copies", type=int, default=32, help="distinct weight copies rotated per call")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -355,6 +358,48 @@ def bench_blk32(torch, bfp8, inputs, args):
     return result
 
 
+def bench_w8a16(torch, bfp8, inputs, args):
+    M = args.m or 4096
+    N = K = 4096
+    x = inputs.activations(M, K, workload=2, stream=0, outliers=True).cuda()
+    wq, ws = bfp8.quantize_weight(inputs.workload(2)["w"].cuda())
+    ncopy = 32 if M <= 16 else 4
+    copies = [(wq.clone(), ws.clone()) for _ in range(ncopy)]
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    wsb = bfp8.make_workspace(bfp8.OP_GEMM_W8A16_BLK128, M, N, K)
+
+    def gemm(i):
+        a = copies[i % len(copies)]
+        bfp8.bfp8_gemm_w8a16_blk128(x, a[0], a[1], y, wsb)
+
+    name = "gemm_w8a16_blk128"
+    ms, wall, kern, timing = run_steps(torch, [(name, gemm)], args.steps, args.warmup)
+    k = kern[name]
+    nb, flops = bytes_w8a16(M, N, K), 2.0 * M * N * K
+    k["alg_bytes"], k["TFLOPs"], k["GBps"] = nb, flops / (k["avg_us"] * 1e6), nb / (k["avg_us"] * 1e3)
+    if M <= 16:
+        roof = {"kernel": name, "bound": "hbm", "achieved": k["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": k["GBps"] / HBM_PEAK_GBS, "traffic": None, "alg_bytes": nb}
+        value, unit = nb / (ms * 1e6), "GB/s"
+    else:
+        roof = {"kernel": name, "bound": "mfma", "achieved": k["TFLOPs"], "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": k["TFLOPs"] / BF16_PEAK_TFLOPS, "traffic": None, "alg_bytes": nb}
+        value, unit = flops / (ms * 1e9), "TFLOP/s"
+    result = {"value": value, "unit": unit, "ms_per_step": ms, "dtype": "e4m3,bf16",
+              "config": {"workload": "W8A16 blk128 GEMM, bf16 x with 1% outlier channels", "M": M, "N": N, "K": K,
+                         "weight_copies": ncopy, "out_dtype": "bf16"},
+              "roofline": roof, "kernels": kern, "wall_s": wall, "timing": timing}
+    if not args.no_cpu_baseline:
+        import oracle
+        rows = min(M, 8)
+        xh = x[:rows].float().cpu().numpy()
+        wq_h, ws_h = wq.cpu().numpy(), ws.cpu().numpy()
+        result["cpu_baseline"] = cpu_baseline(lambda: oracle.gemm_w8a16_blk128(xh, wq_h, ws_h), args.cpu_seconds,
+                                              2.0 * rows * N * K / (1e12 if M > 16 else 1.0) if M > 16 else
+                                              bytes_w8a16(rows, N, K) / 1e9, unit, f"{rows} of {M} token rows")
+    return result
+
+
 def bench_sweep(torch, bfp8, inputs, args):
     import math
     points = []
@@ -415,7 +460,8 @@ def main():
     bfp8.load()
     if args.copy_probe:
         copy_probe(torch)
-    fn = {"decode": bench_decode, "prefill": bench_prefill, "blk32": bench_blk32, "sweep": bench_sweep}[args.workload]
+    fn = {"decode": bench_decode, "prefill": bench_prefill, "blk32": bench_blk32, "w8a16": bench_w8a16,
+          "sweep": bench_sweep}[args.workload]
     r = fn(torch, bfp8, inputs, args)
     line = {"metric": METRIC, "value": r["value"], "unit": r["unit"], "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": r["ms_per_step"], "higher_is_better": True, "scaling": "weak",

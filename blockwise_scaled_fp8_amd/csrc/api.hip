@@ -103,6 +103,8 @@ size_t bfp8_workspace_bytes(int op, int64_t M, int64_t N, int64_t K) {
         case BFP8_OP_GEMM_W8A8_BLK128:
             return w8a8_workspace(M, N, K);
         case BFP8_OP_GEMM_W8A16_BLK128:
+            if (M > kStreamMaxM) return K <= kTileMaxK ? tile16_workspace_bytes(M, N, K) : 0;
+            return stream_workspace_bytes(plan_stream(M, N, K));
         case BFP8_OP_GEMM_W8A16_BLK32_UE8M0:
             return stream_workspace_bytes(plan_stream(M, N, K));
         default:
@@ -159,7 +161,9 @@ bfp8_status bfp8_gemm_w8a16_blk128(const void* x, int x_dtype, const uint8_t* wq
     bfp8_status st = check_gemm(x, wq, ws, y, y_dtype, M, N, K, 16, need, workspace, workspace_bytes);
     if (st != BFP8_OK) return st;
     if (!is16(x_dtype)) return BFP8_E_DTYPE;
-    if ((M + 15) / 16 > 65535) return BFP8_E_SHAPE;         // grid.z limit
+    if (M > kStreamMaxM)     // tiled MFMA kernel, weights widened in registers
+        return launched(launch_w8a16_tile(x, x_dtype == BFP8_BF16, wq, ws, y, y_dtype, M, N, K, workspace,
+                                          as_stream(stream)));
     return launched(launch_w8a16_blk128_stream(x, x_dtype == BFP8_BF16, wq, ws, y, y_dtype, M, N, K,
                                                workspace, as_stream(stream)));
 }
@@ -224,7 +228,7 @@ bfp8_status bfp8_get_limits(int op, int64_t* k_multiple, int64_t* n_multiple, in
         case BFP8_OP_QUANT_WEIGHT_128X128: k = 8; n = 1; ms = 0; break;
         case BFP8_OP_GEMM_W8A8_BLK128: k = 128; n = 16; ms = kStreamMaxM; break;
         case BFP8_OP_QUANT_GEMM_W8A8_BLK128: k = 128; n = 16; ms = kStreamMaxM; break;
-        case BFP8_OP_GEMM_W8A16_BLK128: k = 128; n = 16; ms = INT32_MAX; break;
+        case BFP8_OP_GEMM_W8A16_BLK128: k = 128; n = 16; ms = kStreamMaxM; break;
         case BFP8_OP_GEMM_W8A16_BLK32_UE8M0: k = 128; n = 32; ms = INT32_MAX; break;
         default: return BFP8_E_OP;
     }

@@ -30,6 +30,8 @@ constexpr int64_t kTileMaxK = (int64_t)1 << 23;
 // Workspace bytes of the tiled W8A8 kernels (split-K partial tiles and tile
 // counters; 0 when the shape is not split).
 size_t tile_workspace_bytes(int64_t M, int64_t N, int64_t K);
+// Workspace bytes of the tiled W8A16 kernels.
+size_t tile16_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 // Split-K plan of a streaming kernel: a workgroup covers 16 weight rows and
 // `mt_per_wg` 16-token tiles; `splits` workgroups share one such block of
@@ -62,6 +64,8 @@ constexpr int64_t kFusedQuantMaxM = 8;
 hipError_t launch_w8a8_stream_quant(const void* x, bool x_bf16, const uint8_t* wq, const float* ws,
                                     void* y, int y_dtype, int64_t M, int64_t N, int64_t K,
                                     void* workspace, hipStream_t stream);
+hipError_t launch_w8a16_tile(const void* x, bool x_bf16, const uint8_t* wq, const float* ws, void* y,
+                             int y_dtype, int64_t M, int64_t N, int64_t K, void* workspace, hipStream_t stream);
 hipError_t launch_w8a16_blk128_stream(const void* x, bool x_bf16, const uint8_t* wq, const float* ws,
                                       void* y, int y_dtype, int64_t M, int64_t N, int64_t K,
                                       void* workspace, hipStream_t stream);

@@ -47,22 +47,31 @@ constexpr int kRowBytes = 128;                          // one 128-K block of on
 constexpr int kRowsPerLoad = kWave * 16 / kRowBytes;    // 8 rows per 16-byte load instruction
 constexpr int kCUs = 256;
 
-template <int BN_, int BM_, int WAVES_N, int WAVES_M, bool SPLIT>
+// Token operand of a tile configuration: E4M3 codes with 1x128 scales
+// (W8A8), or 16-bit activations with E4M3 weights widened in registers
+// (W8A16, bf16 or fp16).
+enum TileX { kTileCodes = 0, kTileBf16 = 1, kTileF16 = 2 };
+
+template <int BN_, int BM_, int WAVES_N, int WAVES_M, bool SPLIT, int X_ = kTileCodes>
 struct TileCfg {
     static constexpr int BN = BN_, BM = BM_;
+    static constexpr int X = X_;
+    static constexpr bool kX16 = X_ != kTileCodes;  // 16-bit token rows, no token scales
     static constexpr bool kSplit = SPLIT;           // plans for this shape may split K
     static constexpr int kWavesN = WAVES_N, kWavesM = WAVES_M;
     static constexpr int kWaves = kWavesN * kWavesM;
     static constexpr int kThreads = kWaves * kWave;
     static constexpr int kWaveN = BN / kWavesN, kWaveM = BM / kWavesM;   // per-wave tile
     static constexpr int kTi = kWaveN / 16, kTj = kWaveM / 16;
+    static constexpr int kBRowBytes = kX16 ? 256 : kRowBytes;           // token row bytes per 128-K block
+    static constexpr int kBRowsPerLoad = kWave * 16 / kBRowBytes;       // token rows per load instruction
     static constexpr int kStageA = BN * kRowBytes;
-    static constexpr int kStageB = BM * kRowBytes;
-    static constexpr int kLoadsPerWave = (BN + BM) / (kRowsPerLoad * kWaves);   // tile loads per wave per stage
-    static constexpr int kLoadsA = BN / (kRowsPerLoad * kWaves);               // of which weight rows
-    static constexpr int kXsLanes = BM / kWaves;                               // token scales per wave
+    static constexpr int kStageB = BM * kBRowBytes;
+    static constexpr int kLoadsA = BN / (kRowsPerLoad * kWaves);        // weight-row loads per wave per stage
+    static constexpr int kLoadsPerWave = kLoadsA + BM / (kBRowsPerLoad * kWaves);
+    static constexpr int kXsLanes = kX16 ? 0 : BM / kWaves;             // token scales per wave
     static constexpr int kOffXs = kStageA + kStageB;
-    static constexpr int kOffWs = kOffXs + BM * 4;
+    static constexpr int kOffWs = kOffXs + (kX16 ? 0 : BM * 4);
     static constexpr int kStageBytes = kOffWs + kWaves * 4;
     static constexpr int kStageStride = (kStageBytes + 1023) / 1024 * 1024;
     // As many LDS stages as fit, up to six: blocks kb+1 .. kb+S-1 are in
@@ -71,11 +80,11 @@ struct TileCfg {
     // prefetch to keep enough bytes in flight per CU.
     static constexpr int kStages = (160 * 1024 - 256) / kStageStride < 6 ? (160 * 1024 - 256) / kStageStride : 6;
     // Vector-memory instructions one stage adds per wave: tile loads, the
-    // token scales and the weight scale.
-    static constexpr int kVmemPerStage = kLoadsPerWave + 2;
+    // token scales (W8A8 only) and the weight scale.
+    static constexpr int kVmemPerStage = kLoadsPerWave + (kX16 ? 1 : 2);
     static_assert(kStages * kStageStride <= 160 * 1024, "LDS budget");
-    static_assert(BN % (kRowsPerLoad * kWaves) == 0 && BM % (kRowsPerLoad * kWaves) == 0, "load split");
-    static_assert(kXsLanes >= 1 && kXsLanes <= kWave, "token-scale loads");
+    static_assert(BN % (kRowsPerLoad * kWaves) == 0 && BM % (kBRowsPerLoad * kWaves) == 0, "load split");
+    static_assert(kX16 || (kXsLanes >= 1 && kXsLanes <= kWave), "token-scale loads");
     static_assert(128 % kWaveN == 0 || kWaveN % 128 == 0, "one weight-scale row per wave");
     static_assert(kTi >= 1 && kTj >= 1 && kStages >= 2 && (kStages - 2) * kVmemPerStage < 64, "wave tile");
 };
@@ -84,6 +93,10 @@ using Cfg256 = TileCfg<256, 256, 2, 4, false>;    // wave tile 128 n x 64 m, 2 s
 using Cfg128 = TileCfg<128, 128, 2, 4, false>;    // 64 x 32, 4 stages
 using Cfg64x128 = TileCfg<64, 128, 2, 4, true>;   // 32 x 32, 6 stages
 using Cfg128x64 = TileCfg<128, 64, 4, 2, true>;   // 32 x 32, 6 stages
+// W8A16 (16-bit activations): wave tiles 32 x 64 and 32 x 32 (four waves
+// across the weight rows, so each decoded weight fragment feeds kTj MFMAs).
+template <int X> using Cfg16_128 = TileCfg<128, 128, 4, 2, true, X>;   // 3 stages
+template <int X> using Cfg16_64 = TileCfg<128, 64, 4, 2, true, X>;     // 4 stages
 
 // s_waitcnt vmcnt(N) lgkmcnt(0) (expcnt not waited for).
 template <int N>
@@ -114,6 +127,10 @@ __device__ __forceinline__ void wait_stage(int younger) {
 __device__ __forceinline__ int swz_a_bits(int row) { return ((row >> 1) & 1) | (((row >> 3) & 3) << 1); }
 __device__ __forceinline__ int swz_a(int row, int c) { return row * kRowBytes + ((c ^ swz_a_bits(row)) << 4); }
 __device__ __forceinline__ int swz_b(int row, int c) { return row * kRowBytes + ((c ^ (row & 7)) << 4); }
+// 16-bit token rows are 256 bytes (16 chunks) per block: chunk c of row R at
+// position c ^ (R & 15), so 16 consecutive rows read at one chunk hit 16
+// distinct bank groups.
+__device__ __forceinline__ int swz_b16(int row, int c) { return row * 256 + ((c ^ (row & 15)) << 4); }
 
 // Weight row (local to the wave's kWaveN rows) behind MFMA row rho of the
 // wave's weight tile i.  Chosen so that the MFMA output lane group g (rows
@@ -137,17 +154,22 @@ __device__ __forceinline__ int a_row(int i, int rho) {
 // offset.
 // Only tile loads q_lo <= q < q_hi are issued, and the two scale loads only
 // with `scales` (the caller spreads one stage's loads over its MFMA rows).
+//
+// 16-bit token rows (W8A16) are 256 bytes per block: a load instruction then
+// covers 4 rows (lane l: row 4*(W q + w) + l/16, chunk position l%16), and
+// the K block's offset in them is kb * 256.
 template <class C>
 __device__ __forceinline__ void issue_stage(uint8_t* stage, i32x4 rsrc_a, i32x4 rsrc_b, i32x4 rsrc_xs,
                                             i32x4 rsrc_ws, int lane_off_a, int lane_off_b, int q_stride,
-                                            int xs_off, int64_t kb, int wave, int lane,
+                                            int q_stride_b, int xs_off, int64_t kb, int wave, int lane,
                                             int q_lo = 0, int q_hi = C::kLoadsPerWave, bool scales = true) {
     const int k_off = __builtin_amdgcn_readfirstlane((int)(kb * kRowBytes));
+    const int k_off_b = __builtin_amdgcn_readfirstlane((int)(kb * C::kBRowBytes));
     const uint32_t base = lds_address(stage);
     if (scales) {
         // Token scales xs[m0 + kXsLanes * w + l, kb], lanes l < kXsLanes only
         // (the dword form writes M0 + 4 * lane for every active lane).
-        if (lane < C::kXsLanes)
+        if (!C::kX16 && lane < C::kXsLanes)
             dma4(__builtin_amdgcn_readfirstlane(base + C::kOffXs + 4 * C::kXsLanes * wave), rsrc_xs, xs_off,
                  __builtin_amdgcn_readfirstlane((int)(kb * 4)));
         // This wave's weight scale ws[nb, kb], lane 0 only.
@@ -162,7 +184,7 @@ __device__ __forceinline__ void issue_stage(uint8_t* stage, i32x4 rsrc_a, i32x4 
         if (q < C::kLoadsA) {
             dma16(lds, rsrc_a, lane_off_a, __builtin_amdgcn_readfirstlane(q * q_stride), k_off);
         } else {
-            dma16(lds, rsrc_b, lane_off_b, __builtin_amdgcn_readfirstlane((q - C::kLoadsA) * q_stride), k_off);
+            dma16(lds, rsrc_b, lane_off_b, __builtin_amdgcn_readfirstlane((q - C::kLoadsA) * q_stride_b), k_off_b);
         }
     }
 }
@@ -236,7 +258,7 @@ __device__ __forceinline__ void store8(void* y, int y_dtype, int64_t idx, f32x4 
 // `counters` one uint32 per output tile (zero on entry, re-armed on exit).
 template <class C>
 __global__ __launch_bounds__(C::kThreads, 1) void w8a8_tile_kernel(
-    const uint8_t* __restrict__ xq, const float* __restrict__ xs,
+    const void* __restrict__ xin, const float* __restrict__ xs,
     const uint8_t* __restrict__ wq, const float* __restrict__ ws,
     void* __restrict__ y, int y_dtype, int64_t M, int64_t N, int64_t K,
     int64_t tiles_n, int64_t tiles_m, int64_t splits, int64_t kb_per_split,
@@ -258,13 +280,23 @@ __global__ __launch_bounds__(C::kThreads, 1) void w8a8_tile_kernel(
     // token-scale rows; rows past N or M lie outside them and load as zeros.
     const int64_t rows_a = N - n0 < C::BN ? N - n0 : C::BN;
     const int64_t rows_b = M - m0 < C::BM ? M - m0 : C::BM;
+    // Token operand: E4M3 codes (1 byte) or 16-bit activations (2 bytes).
+    constexpr int64_t kXBytes = C::kX16 ? 2 : 1;
+    const uint8_t* xbase = static_cast<const uint8_t*>(xin);
     const i32x4 rsrc_a = buffer_rsrc(wq + n0 * K, (uint32_t)(rows_a * K));
-    const i32x4 rsrc_b = buffer_rsrc(xq + m0 * K, (uint32_t)(rows_b * K));
-    const i32x4 rsrc_xs = buffer_rsrc(xs + m0 * KB, (uint32_t)(rows_b * KB * 4));
+    const i32x4 rsrc_b = buffer_rsrc(xbase + m0 * K * kXBytes, (uint32_t)(rows_b * K * kXBytes));
+    const i32x4 rsrc_xs = C::kX16 ? rsrc_b : buffer_rsrc(xs + m0 * KB, (uint32_t)(rows_b * KB * 4));
     const int dma_row = 8 * wave + (lane >> 3);     // stage row of this lane's first load, minus 8 W q
     const int lane_off_a = (int)(dma_row * K) + (((lane & 7) ^ swz_a_bits(dma_row)) << 4);
-    const int lane_off_b = (int)(dma_row * K) + (((lane & 7) ^ (dma_row & 7)) << 4);
+    int lane_off_b;
+    if constexpr (C::kX16) {
+        const int row16 = 4 * wave + (lane >> 4);   // 16-bit token row of this lane's first load
+        lane_off_b = (int)(row16 * K * 2) + (((lane & 15) ^ (row16 & 15)) << 4);
+    } else {
+        lane_off_b = (int)(dma_row * K) + (((lane & 7) ^ (dma_row & 7)) << 4);
+    }
     const int q_stride = (int)(kRowsPerLoad * C::kWaves * K);
+    const int q_stride_b = (int)(C::kBRowsPerLoad * C::kWaves * K * kXBytes);
     const int xs_off = (int)((C::kXsLanes * wave + lane) * KB * 4);
 
     // Weight scales: one row of ws per wave (its weight rows share it).
@@ -291,6 +323,61 @@ __global__ __launch_bounds__(C::kThreads, 1) void w8a8_tile_kernel(
     // loads are issued between the MFMA rows, so a wave never waits for the
     // memory pipeline to accept a whole stage before it starts multiplying.
     auto compute = [&](const uint8_t* stage, auto refill, uint8_t* fill, int64_t fill_kb) {
+      if constexpr (C::kX16) {
+        // W8A16: per 16x16 tile and block, four 16x16x32 MFMAs on weights
+        // widened in registers (decode8: the E4M3 bias difference, 2^120 for
+        // bf16 and 2^8 for fp16, is folded into the block scale).  MFMA jj
+        // of lane (r, g) takes K positions 16(g + 4(jj/2)) + 8(jj%2) .. +7:
+        // weight bytes from chunks g and g + 4 of the fp8 row, and the
+        // 16-bit token chunks 2g, 2g+1, 2g+8, 2g+9 of the 256-byte row.
+        constexpr float kBiasFold = C::X == kTileBf16 ? 0x1p120f : 0x1p8f;
+        const float wsc = reinterpret_cast<const float*>(stage + C::kOffWs)[wave] * kBiasFold;
+        u32x4 bfr[C::kTj][4];
+#pragma unroll
+        for (int j = 0; j < C::kTj; ++j) {
+            const int row = C::kWaveM * wm + 16 * j + r;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+                bfr[j][jj] = *reinterpret_cast<const u32x4*>(
+                    stage + C::kStageA + swz_b16(row, 2 * g + 8 * (jj >> 1) + (jj & 1)));
+        }
+        f32x4 tmp[2][C::kTj];
+        i32x8 af = read_frag<true>(stage, a_base + a_row(0, r), g);
+#pragma unroll
+        for (int i = 0; i < C::kTi; ++i) {
+            const int c = i & 1;
+            const u32x4 aop[4] = {decode8<C::X == kTileBf16>((uint32_t)af[0], (uint32_t)af[1]),
+                                  decode8<C::X == kTileBf16>((uint32_t)af[2], (uint32_t)af[3]),
+                                  decode8<C::X == kTileBf16>((uint32_t)af[4], (uint32_t)af[5]),
+                                  decode8<C::X == kTileBf16>((uint32_t)af[6], (uint32_t)af[7])};
+            if (i + 1 < C::kTi) af = read_frag<true>(stage, a_base + a_row(i + 1, r), g);
+#pragma unroll
+            for (int j = 0; j < C::kTj; ++j) {
+                f32x4 blk = zero;
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj)
+                    blk = C::X == kTileBf16 ? mfma_bf16_16x16x32(aop[jj], bfr[j][jj], blk)
+                                            : mfma_f16_16x16x32(aop[jj], bfr[j][jj], blk);
+                tmp[c][j] = blk;
+            }
+            if constexpr (decltype(refill)::value)
+                issue_stage<C>(fill, rsrc_a, rsrc_b, rsrc_xs, rsrc_ws, lane_off_a, lane_off_b, q_stride, q_stride_b,
+                               xs_off, fill_kb, wave, lane, i * C::kLoadsPerWave / C::kTi,
+                               (i + 1) * C::kLoadsPerWave / C::kTi, false);
+            if (i > 0) {
+#pragma unroll
+                for (int j = 0; j < C::kTj; ++j)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        acc[i - 1][j][e] = __builtin_fmaf(tmp[c ^ 1][j][e], wsc, acc[i - 1][j][e]);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < C::kTj; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                acc[C::kTi - 1][j][e] = __builtin_fmaf(tmp[(C::kTi - 1) & 1][j][e], wsc, acc[C::kTi - 1][j][e]);
+      } else {
         const float wsc = reinterpret_cast<const float*>(stage + C::kOffWs)[wave];
         const float* xs_lds = reinterpret_cast<const float*>(stage + C::kOffXs);
         float sc[C::kTj];
@@ -307,8 +394,8 @@ __global__ __launch_bounds__(C::kThreads, 1) void w8a8_tile_kernel(
 #pragma unroll
             for (int j = 0; j < C::kTj; ++j) tmp[c][j] = mfma_e4m3_16x16x128(af, bf[j], zero);
             if constexpr (decltype(refill)::value)
-                issue_stage<C>(fill, rsrc_a, rsrc_b, rsrc_xs, rsrc_ws, lane_off_a, lane_off_b, q_stride, xs_off,
-                               fill_kb, wave, lane, i * C::kLoadsPerWave / C::kTi,
+                issue_stage<C>(fill, rsrc_a, rsrc_b, rsrc_xs, rsrc_ws, lane_off_a, lane_off_b, q_stride, q_stride_b,
+                               xs_off, fill_kb, wave, lane, i * C::kLoadsPerWave / C::kTi,
                                (i + 1) * C::kLoadsPerWave / C::kTi, false);
             if (i + 1 < C::kTi) af = read_frag<true>(stage, a_base + a_row(i + 1, r), g);
             if (i > 0) {
@@ -324,6 +411,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void w8a8_tile_kernel(
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 acc[C::kTi - 1][j][e] = __builtin_fmaf(tmp[(C::kTi - 1) & 1][j][e], sc[j], acc[C::kTi - 1][j][e]);
+      }
     };
 
     auto stage = [&](int64_t b) { return stages + (int)(b % C::kStages) * C::kStageStride; };
@@ -331,7 +419,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void w8a8_tile_kernel(
 #pragma unroll
     for (int p = 0; p + 1 < C::kStages; ++p)
         if (p < nkb)
-            issue_stage<C>(stage(p), rsrc_a, rsrc_b, rsrc_xs, rsrc_ws, lane_off_a, lane_off_b, q_stride, xs_off, kb0 + p, wave,
+            issue_stage<C>(stage(p), rsrc_a, rsrc_b, rsrc_xs, rsrc_ws, lane_off_a, lane_off_b, q_stride, q_stride_b, xs_off, kb0 + p, wave,
                            lane);
     // Steady state: blocks whose stage is refilled with block b + S - 1,
     // then the last S - 1 blocks with no refill (two loops, so the
@@ -348,7 +436,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void w8a8_tile_kernel(
         // The scale loads of the refill block first (two short
         // instructions), its tile loads between the MFMA rows.
         uint8_t* fill = stage(b + C::kStages - 1);
-        issue_stage<C>(fill, rsrc_a, rsrc_b, rsrc_xs, rsrc_ws, lane_off_a, lane_off_b, q_stride, xs_off,
+        issue_stage<C>(fill, rsrc_a, rsrc_b, rsrc_xs, rsrc_ws, lane_off_a, lane_off_b, q_stride, q_stride_b, xs_off,
                        kb0 + b + C::kStages - 1, wave, lane, 0, 0, true);
         compute(stage(b), std::true_type{}, fill, kb0 + b + C::kStages - 1);
     }
@@ -443,7 +531,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void w8a8_tile_kernel(
 
 namespace {
 
-enum class TileShape { k256, k128, k64x128, k128x64 };
+enum class TileShape { k256, k128, k64x128, k128x64, k16_128, k16_64 };
 
 struct TilePlan {
     TileShape shape;
@@ -454,7 +542,7 @@ TilePlan make_plan(TileShape s, int64_t bn, int64_t bm, int64_t M, int64_t N, in
     TilePlan p{s, bn, bm, (N + bn - 1) / bn, (M + bm - 1) / bm, 1, 0};
     const int64_t KB = K / 128;
     int64_t splits = 1;
-    if (s == TileShape::k64x128 || s == TileShape::k128x64) {
+    if (s == TileShape::k64x128 || s == TileShape::k128x64 || s == TileShape::k16_128 || s == TileShape::k16_64) {
         // About one workgroup per CU, each with at least 4 K blocks.
         while (p.tiles_n * p.tiles_m * splits < kCUs && KB / (splits * 2) >= 4) splits *= 2;
     }
@@ -472,12 +560,20 @@ TilePlan plan_tile(int64_t M, int64_t N, int64_t K) {
     return make_plan(TileShape::k64x128, 64, 128, M, N, K);
 }
 
+// W8A16 (16-bit activations, M > 16): 128 weight rows x 128 tokens (64
+// tokens for M <= 64), K split when that leaves the CUs short of
+// workgroups.
+TilePlan plan_tile16(int64_t M, int64_t N, int64_t K) {
+    if (M <= 64) return make_plan(TileShape::k16_64, 128, 64, M, N, K);
+    return make_plan(TileShape::k16_128, 128, 128, M, N, K);
+}
+
 size_t counter_bytes(const TilePlan& p) {
     return ((size_t)(p.tiles_n * p.tiles_m) * sizeof(uint32_t) + 255) / 256 * 256;
 }
 
 template <class C>
-void launch(const TilePlan& p, const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws, void* y,
+void launch(const TilePlan& p, const void* xq, const float* xs, const uint8_t* wq, const float* ws, void* y,
             int y_dtype, int64_t M, int64_t N, int64_t K, float* partials, uint32_t* counters,
             hipStream_t stream) {
     const dim3 grid((unsigned)(p.tiles_n * p.tiles_m * p.splits));
@@ -487,22 +583,47 @@ void launch(const TilePlan& p, const uint8_t* xq, const float* xs, const uint8_t
 
 }  // namespace
 
-size_t tile_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-    const TilePlan p = plan_tile(M, N, K);
+static size_t plan_workspace_bytes(const TilePlan& p) {
     if (p.splits == 1) return 0;
     return counter_bytes(p) + (size_t)(p.tiles_n * p.tiles_m * p.splits * p.bn * p.bm) * sizeof(float);
+}
+
+size_t tile_workspace_bytes(int64_t M, int64_t N, int64_t K) { return plan_workspace_bytes(plan_tile(M, N, K)); }
+
+size_t tile16_workspace_bytes(int64_t M, int64_t N, int64_t K) { return plan_workspace_bytes(plan_tile16(M, N, K)); }
+
+static void split_parts(const TilePlan& p, void* workspace, uint32_t*& counters, float*& partials) {
+    counters = nullptr;
+    partials = nullptr;
+    if (p.splits > 1) {
+        counters = static_cast<uint32_t*>(workspace);
+        partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + counter_bytes(p));
+    }
+}
+
+hipError_t launch_w8a16_tile(const void* x, bool x_bf16, const uint8_t* wq, const float* ws, void* y,
+                             int y_dtype, int64_t M, int64_t N, int64_t K, void* workspace, hipStream_t stream) {
+    const TilePlan p = plan_tile16(M, N, K);
+    uint32_t* counters;
+    float* partials;
+    split_parts(p, workspace, counters, partials);
+    if (p.shape == TileShape::k16_64) {
+        if (x_bf16) launch<Cfg16_64<kTileBf16>>(p, x, nullptr, wq, ws, y, y_dtype, M, N, K, partials, counters, stream);
+        else launch<Cfg16_64<kTileF16>>(p, x, nullptr, wq, ws, y, y_dtype, M, N, K, partials, counters, stream);
+    } else {
+        if (x_bf16) launch<Cfg16_128<kTileBf16>>(p, x, nullptr, wq, ws, y, y_dtype, M, N, K, partials, counters, stream);
+        else launch<Cfg16_128<kTileF16>>(p, x, nullptr, wq, ws, y, y_dtype, M, N, K, partials, counters, stream);
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_w8a8_tile(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
                             void* y, int y_dtype, int64_t M, int64_t N, int64_t K, void* workspace,
                             hipStream_t stream) {
     const TilePlan p = plan_tile(M, N, K);
-    uint32_t* counters = nullptr;
-    float* partials = nullptr;
-    if (p.splits > 1) {
-        counters = static_cast<uint32_t*>(workspace);
-        partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + counter_bytes(p));
-    }
+    uint32_t* counters;
+    float* partials;
+    split_parts(p, workspace, counters, partials);
     switch (p.shape) {
         case TileShape::k256:
             launch<Cfg256>(p, xq, xs, wq, ws, y, y_dtype, M, N, K, partials, counters, stream);
@@ -515,6 +636,8 @@ hipError_t launch_w8a8_tile(const uint8_t* xq, const float* xs, const uint8_t* w
             break;
         case TileShape::k128x64:
             launch<Cfg128x64>(p, xq, xs, wq, ws, y, y_dtype, M, N, K, partials, counters, stream);
+            break;
+        default:
             break;
     }
     return hipGetLastError();

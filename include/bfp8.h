@@ -154,7 +154,11 @@ bfp8_status bfp8_quant_gemm_w8a8_blk128(const void* x, int x_dtype,
  * once per 128 K values).
  *   Y[m, n] = sum_kb ws[n / 128, kb] * sum over k in kb of x[m, k] * E4M3(wq[n, k])
  *   x   [M, K] bf16 or fp16, wq [N, K] E4M3, ws [ceil(N/128), K/128] fp32.
- *   y   [M, N] in y_dtype (BF16 / F16 / F32); workspace as for W8A8.
+ *   y   [M, N] in y_dtype (BF16 / F16 / F32); workspace as for W8A8 (sized
+ *       by bfp8_workspace_bytes(BFP8_OP_GEMM_W8A16_BLK128, M, N, K)).
+ * M <= 16 streams the weights (decode); larger M runs a tiled MFMA kernel
+ * that widens each weight fragment once per wave and reuses it for up to 64
+ * tokens ([3090] §4.4: at prefill the weight-only cost is a few percent).
  * Requires M >= 1, N % 16 == 0, K % 128 == 0, K <= 2^23.
  */
 bfp8_status bfp8_gemm_w8a16_blk128(const void* x, int x_dtype,
@@ -212,7 +216,8 @@ size_t bfp8_workspace_bytes(int op, int64_t M, int64_t N, int64_t K);
  *   m_stream_max  largest M always served by the weight-streaming decode
  *                 kernel.  W8A8 also streams M <= 2 * m_stream_max when
  *                 N * K <= 2^24 (measured faster there); other M go to the
- *                 tiled MFMA kernels.  W8A16 always streams.
+ *                 tiled MFMA kernels.  W8A16 blk128 streams M <= m_stream_max
+ *                 and uses its tiled MFMA kernel above; blk32 always streams.
  * Any output pointer may be NULL.
  */
 bfp8_status bfp8_get_limits(int op, int64_t* k_multiple, int64_t* n_multiple,

@@ -60,6 +60,7 @@ def test_limits(lib):
     w8a8 = bfp8.bfp8_get_limits(bfp8.OP_GEMM_W8A8_BLK128)
     assert w8a8 == {"k_multiple": 128, "n_multiple": 16, "align_bytes": 16, "m_stream_max": 16}
     assert bfp8.bfp8_get_limits(bfp8.OP_GEMM_W8A16_BLK32_UE8M0)["n_multiple"] == 32
+    assert bfp8.bfp8_get_limits(bfp8.OP_GEMM_W8A16_BLK128)["m_stream_max"] == 16
     assert lib.bfp8_get_limits(77, None, None, None, None) == 10
 
 

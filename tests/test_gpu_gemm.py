@@ -196,7 +196,7 @@ def test_w8a8_deterministic(gpu_lib):
 # ------------------------------------------------------------ W8A16 blk128 ----
 
 @pytest.mark.parametrize("xdtype", [torch.bfloat16, torch.float16])
-@pytest.mark.parametrize("M", [1, 2, 4, 8, 16, 33])
+@pytest.mark.parametrize("M", [1, 2, 4, 8, 16, 17, 33, 64, 65, 130])
 def test_w8a16_blk128(gpu_lib, M, xdtype):
     N, K = 512, 1024
     say("w8a16 blk128", M, xdtype)
@@ -224,6 +224,55 @@ def test_w8a16_blk128_one_hot_all_codes_exact(gpu_lib, xdtype):
         y = run_w8a16(x.cuda(), dev(wq), dev(ws), torch.float32)
         expect = oracle.e4m3_decode(wq[:, k]) * ws[np.arange(N) // 128, k // 128]
         np.testing.assert_array_equal(y.cpu().numpy(), np.broadcast_to(expect, (M, N)))
+
+
+@pytest.mark.parametrize("xdtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("M,N,K", [(40, 1024, 4096), (100, 1040, 4096), (300, 2048, 2176)])
+def test_w8a16_tile_split_k(gpu_lib, M, N, K, xdtype):
+    """Tiled W8A16 with ragged M/N tiles and split K (workspace), run twice on
+    one workspace: bar met, second run bit-identical."""
+    say("w8a16 tile", xdtype, f"M={M} N={N} K={K}")
+    x = inputs.activations(M, K, workload=620 + M, stream=K, outliers=True, dtype=xdtype)
+    wq, ws = oracle.quantize_weight_128x128(f32(inputs.weights_bf16(N, K, workload=620 + N, stream=K)))
+    y0 = oracle.gemm_w8a16_blk128(f32(x), wq, ws)
+    xd, wqd, wsd = x.cuda(), dev(wq), dev(ws)
+    wsb = workspace(bfp8.OP_GEMM_W8A16_BLK128, M, N, K)
+    y1 = run_w8a16(xd, wqd, wsd, torch.float32, wsb)
+    assert_fp32_bar(y1, y0, f"w8a16 tile M={M}")
+    y2 = run_w8a16(xd, wqd, wsd, torch.float32, wsb)
+    assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
+    y16 = run_w8a16(xd, wqd, wsd, xdtype, wsb)
+    assert_16bit_bar(y16, y1, y0, "bf16" if xdtype == torch.bfloat16 else "f16", f"w8a16 tile M={M}")
+
+
+@pytest.mark.parametrize("xdtype", [torch.bfloat16, torch.float16])
+def test_w8a16_tile_one_hot_all_codes_exact(gpu_lib, xdtype):
+    """Tiled path (M = 48): x one-hot 1.0 gives E4M3(wq[n, k]) * ws exactly."""
+    N, K, M = 256, 256, 48
+    wq = np.zeros((N, K), np.uint8)
+    wq[:254, :] = FINITE_CODES[:, None]
+    ws = np.array([[0.5, 2.0], [0.25, 4.0]], np.float32)
+    for k in (0, 37, 130, 255):
+        say("w8a16 tile one-hot", xdtype, k)
+        x = torch.zeros((M, K), dtype=xdtype)
+        x[:, k] = 1.0
+        y = run_w8a16(x.cuda(), dev(wq), dev(ws), torch.float32)
+        expect = oracle.e4m3_decode(wq[:, k]) * ws[np.arange(N) // 128, k // 128]
+        np.testing.assert_array_equal(y.cpu().numpy(), np.broadcast_to(expect, (M, N)))
+
+
+@pytest.mark.parametrize("xdtype", [torch.bfloat16, torch.float16])
+def test_w8a16_prefill_oproj_sampled(gpu_lib, xdtype):
+    """M = N = K = 4096 W8A16 with 1% outlier channels: full GPU run, 48 rows checked."""
+    say("w8a16 prefill", xdtype)
+    x = inputs.activations(4096, 4096, workload=2, stream=0, outliers=True, dtype=xdtype)
+    w = inputs.workload(2)["w"]
+    wq_d, ws_d = bfp8.quantize_weight(w.cuda())
+    y32 = run_w8a16(x.cuda(), wq_d, ws_d, torch.float32)
+    rows = np.concatenate([np.random.default_rng(5).choice(4096, 40, replace=False), np.arange(4088, 4096)])
+    wq, ws = oracle.quantize_weight_128x128(f32(w))
+    y0 = oracle.gemm_w8a16_blk128(f32(x[rows]), wq, ws)
+    assert_fp32_bar(y32[rows], y0, "w8a16 prefill sampled rows")
 
 
 def test_w8a16_blk128_decode_oproj_full(gpu_lib):
