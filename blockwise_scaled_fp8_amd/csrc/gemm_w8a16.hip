@@ -123,6 +123,93 @@ __global__ __launch_bounds__(kStreamThreads) void w8a16_blk128_stream_kernel(
     stream_finish(acc, red, y, y_dtype, M, N, nt, mt, splits, split, n_tiles, partials, counters);
 }
 
+// M <= 8 (padded token count Mp = 1, 2, 4 or 8): the weights come through
+// LDS slabs as whole 128-byte lines, and the block's token rows as
+// direct-to-LDS dword loads (one per token row and block), all issued
+// before the first wait.  Per wave and block that is two weight loads and
+// Mp token loads, where the register-operand kernel above issues two
+// half-line weight loads and four 16-byte token loads per lane (sixteen
+// lanes of one token column reading the same row when M = 1).  Lanes past
+// the token count read row 0 and are zeroed by a select.
+constexpr int kW8A16LdsMaxM = 8;
+constexpr int kW8A16LdsChunk = 2;
+
+template <bool kXBf16, int kMp>
+__global__ __launch_bounds__(kStreamThreads) void w8a16_blk128_stream_lds_kernel(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq, const float* __restrict__ ws,
+    void* __restrict__ y, int y_dtype, int64_t M, int64_t N, int64_t K,
+    int64_t n_tiles, int64_t splits, int64_t kb_per_split,
+    float* __restrict__ partials, uint32_t* __restrict__ counters) {
+    __shared__ float red[kStreamWaves * 256];
+    __shared__ __attribute__((aligned(16))) uint8_t xrows[kStreamWaves][kW8A16LdsChunk][kMp * kXRowStride];
+    __shared__ __attribute__((aligned(1024))) uint8_t wslab[kStreamWaves][kW8A16LdsChunk][kSlabBytes];
+    const int64_t nt = blockIdx.x, split = blockIdx.y;
+    const int64_t KB = K / 128;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
+    const int r = lane & 15, g = lane >> 4;
+    const bool r_ok = r < kMp;
+    const int r_row = r_ok ? r : 0;
+    const int64_t kb_begin = split * kb_per_split;
+    const int64_t kb_end = kb_begin + kb_per_split < KB ? kb_begin + kb_per_split : KB;
+
+    const i32x4 rsrc_w = buffer_rsrc(wq + nt * 16 * K, (uint32_t)(16 * K));
+    const i32x4 rsrc_x = buffer_rsrc(x, (uint32_t)(M * K * 2));
+    const int lane_off_w = slab_lane_offset(lane, K);
+    const float* ws_row = ws + (nt * 16 / 128) * KB;
+    const float bias_fold = kXBf16 ? 0x1p120f : 0x1p8f;
+
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+    const u32x4 z4 = {0u, 0u, 0u, 0u};
+    for (int64_t kb0 = kb_begin + wave; kb0 < kb_end; kb0 += kStreamWaves * kW8A16LdsChunk) {
+        float wsv[kW8A16LdsChunk];
+#pragma unroll
+        for (int c = 0; c < kW8A16LdsChunk; ++c) {
+            const int64_t kb = kb0 + c * kStreamWaves;
+            if (kb < kb_end) wsv[c] = ws_row[kb];
+        }
+#pragma unroll
+        for (int c = 0; c < kW8A16LdsChunk; ++c) {
+            const int64_t kb = kb0 + c * kStreamWaves;
+            if (kb < kb_end) xrows_issue<kMp>(xrows[wave][c], rsrc_x, lane, K, kb);
+        }
+#pragma unroll
+        for (int c = 0; c < kW8A16LdsChunk; ++c) {
+            const int64_t kb = kb0 + c * kStreamWaves;
+            if (kb < kb_end) slab_issue(wslab[wave][c], rsrc_w, lane_off_w, K, kb);
+        }
+        wait_vmcnt<0>();
+#pragma unroll
+        for (int c = 0; c < kW8A16LdsChunk; ++c) {
+            const int64_t kb = kb0 + c * kStreamWaves;
+            if (kb < kb_end) {
+                u32x4 wa0, wa1;
+                slab_read(wslab[wave][c], r, g, wa0, wa1);
+                const uint32_t q[8] = {wa0[0], wa0[1], wa0[2], wa0[3], wa1[0], wa1[1], wa1[2], wa1[3]};
+                // MFMA j takes K offsets 16 g + 8 j (j < 2) and 64 + 16 g + 8 (j - 2):
+                // bytes 32 g + 16 j and 128 + 32 g + 16 (j - 2) of the token row.
+                const uint8_t* row = xrows[wave][c] + r_row * kXRowStride + 32 * g;
+                u32x4 xv[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    xv[j] = *reinterpret_cast<const u32x4*>(row + (j < 2 ? 16 * j : 128 + 16 * (j - 2)));
+                    xv[j] = r_ok ? xv[j] : z4;
+                }
+                f32x4 blk = zero;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const u32x4 a = decode8<kXBf16>(q[2 * j], q[2 * j + 1]);
+                    blk = kXBf16 ? mfma_bf16_16x16x32(a, xv[j], blk) : mfma_f16_16x16x32(a, xv[j], blk);
+                }
+                const float sc = wsv[c] * bias_fold;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(blk[i], sc, acc[i]);
+            }
+        }
+    }
+    stream_finish(acc, red, y, y_dtype, M, N, nt, 0, splits, split, n_tiles, partials, counters);
+}
+
 __global__ __launch_bounds__(kStreamThreads) void w8a16_blk32_stream_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq, const uint8_t* __restrict__ e8m0,
     void* __restrict__ y, int y_dtype, int64_t M, int64_t N, int64_t K,
@@ -205,6 +292,30 @@ hipError_t launch_w8a16_blk128_stream(const void* x, bool x_bf16, const uint8_t*
     float* partials;
     stream_workspace_parts(p, workspace, counters, partials);
     const dim3 grid((unsigned)p.n_tiles, (unsigned)p.splits, (unsigned)p.m_tiles);
+    if (M <= kW8A16LdsMaxM) {
+        const int mp = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8;
+        const uint16_t* xh = static_cast<const uint16_t*>(x);
+#define BFP8_LAUNCH_LDS(BF, MP)                                                                                \
+    hipLaunchKernelGGL((w8a16_blk128_stream_lds_kernel<BF, MP>), grid, dim3(kStreamThreads), 0, stream, xh, wq, ws, \
+                       y, y_dtype, M, N, K, p.n_tiles, p.splits, p.kb_per_split, partials, counters)
+        if (x_bf16) {
+            switch (mp) {
+                case 1: BFP8_LAUNCH_LDS(true, 1); break;
+                case 2: BFP8_LAUNCH_LDS(true, 2); break;
+                case 4: BFP8_LAUNCH_LDS(true, 4); break;
+                default: BFP8_LAUNCH_LDS(true, 8); break;
+            }
+        } else {
+            switch (mp) {
+                case 1: BFP8_LAUNCH_LDS(false, 1); break;
+                case 2: BFP8_LAUNCH_LDS(false, 2); break;
+                case 4: BFP8_LAUNCH_LDS(false, 4); break;
+                default: BFP8_LAUNCH_LDS(false, 8); break;
+            }
+        }
+#undef BFP8_LAUNCH_LDS
+        return hipGetLastError();
+    }
     if (x_bf16) {
         hipLaunchKernelGGL(w8a16_blk128_stream_kernel<true>, grid, dim3(kStreamThreads), 0, stream,
                            static_cast<const uint16_t*>(x), wq, ws, y, y_dtype, M, N, K,

@@ -174,17 +174,25 @@ __global__ __launch_bounds__(kStreamThreads) void w8a8_stream_kernel(
 // counts the activation quantisation inside the kernel's time, and "What's
 // not good yet" names batch-1 decode, memory-bound, as the remaining gap;
 // fusing removes a launch and the codes' round trip through memory there.
-// The 64 lanes split the padded token count Mp
-// (1, 2, 4 or 8) evenly: 64/Mp lanes per token, 2 Mp values per lane, so no
-// lane quantises padding when M is small.  The group maximum is a
-// butterfly over the token's lanes; scale, quotients and codes use the
-// quantiser's own arithmetic (quantize_v), so codes, scales and results are
-// bit-identical to bfp8_quantize_act_1x128 followed by the codes kernel.
-// The codes go through a per-wave LDS scratch into the MFMA operand layout.
+//
+// Load order per wave: the weight scales, then the block's token rows
+// (direct-to-LDS dword loads, 256 bytes per token row; rows past M lie
+// outside the buffer descriptor and read as zeros), then the weight slabs.
+// Loads complete in issue order, so the wave waits for its token rows with
+// the weight loads still in flight and quantises while the weights stream
+// from HBM; only the MFMA and the promotion are left for after the weights
+// arrive.  The 64 lanes split the padded token count Mp (1, 2, 4 or 8)
+// evenly: 64/Mp lanes per token, 2 Mp values per lane, so no lane quantises
+// padding when M is small.  The group maximum is a butterfly over the
+// token's lanes; scale, quotients and codes use the quantiser's own
+// arithmetic (quantize_v), so codes, scales and results are bit-identical to
+// bfp8_quantize_act_1x128 followed by the codes kernel.  The codes overwrite
+// the first 128 bytes of their token row in LDS (a wave's LDS accesses run in
+// issue order, and every lane has read its values before any lane writes),
+// and are read back in the MFMA operand layout.
 constexpr int kFusedChunk = 2;
-
 template <int NW>
-__device__ __forceinline__ void load_words(const uint16_t* p, uint32_t (&w)[NW]) {
+__device__ __forceinline__ void read_words(const uint8_t* p, uint32_t (&w)[NW]) {
     if constexpr (NW == 1) {
         w[0] = *reinterpret_cast<const uint32_t*>(p);
     } else if constexpr (NW == 2) {
@@ -194,7 +202,7 @@ __device__ __forceinline__ void load_words(const uint16_t* p, uint32_t (&w)[NW])
     } else {
 #pragma unroll
         for (int i = 0; i < NW / 4; ++i) {
-            const u32x4 v = load_16B(p + 8 * i);
+            const u32x4 v = *reinterpret_cast<const u32x4*>(p + 16 * i);
 #pragma unroll
             for (int e = 0; e < 4; ++e) w[4 * i + e] = v[e];
         }
@@ -214,6 +222,36 @@ __device__ __forceinline__ void store_codes(uint8_t* p, const uint32_t (&c)[(NB 
     }
 }
 
+// Maximum over each token's kL lanes (aligned groups of 8, 16, 32 or 64):
+// DPP within rows of 16 lanes, then the row maxima read as scalars.
+template <int kL>
+__device__ __forceinline__ float token_max(float v) {
+    if constexpr (kL <= 16) {
+        return group_max_dpp<kL>(v);
+    } else {
+        v = group_max_dpp<16>(v);
+        const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+        const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+        const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+        const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+        if constexpr (kL == 64) return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+        else return (threadIdx.x & 32) ? fmaxf(r2, r3) : fmaxf(r0, r1);
+    }
+}
+
+// Value v of token t's first lane (lane t * 64 / kMp), for token t = `tok`.
+template <int kMp>
+__device__ __forceinline__ float token_value(float v, int tok) {
+    constexpr int kL = kWave / kMp;
+    float out = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+#pragma unroll
+    for (int t = 1; t < kMp; ++t) {
+        const float vt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), t * kL));
+        out = tok == t ? vt : out;
+    }
+    return out;
+}
+
 template <bool kBf16, int kMp>
 __global__ __launch_bounds__(kStreamThreads) void w8a8_stream_quant_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq, const float* __restrict__ ws,
@@ -222,8 +260,9 @@ __global__ __launch_bounds__(kStreamThreads) void w8a8_stream_quant_kernel(
     float* __restrict__ partials, uint32_t* __restrict__ counters) {
     constexpr int kL = kWave / kMp;          // lanes per token
     constexpr int kV = 128 / kL;             // values per lane (2 Mp)
+    static_assert(kFusedChunk == 2, "the token-row wait counts two slab loads per block");
     __shared__ float red[kStreamWaves * 256];
-    __shared__ __attribute__((aligned(16))) uint8_t xcode[kStreamWaves][kFusedChunk][kMp][128];
+    __shared__ __attribute__((aligned(16))) uint8_t xrows[kStreamWaves][kFusedChunk][kMp * kXRowStride];
     __shared__ __attribute__((aligned(1024))) uint8_t wslab[kStreamWaves][kFusedChunk][kSlabBytes];
     const int64_t nt = blockIdx.x, split = blockIdx.y;
     const int64_t KB = K / 128;
@@ -234,70 +273,83 @@ __global__ __launch_bounds__(kStreamThreads) void w8a8_stream_quant_kernel(
 
     // Quantiser role: token qt, values [qp * kV, qp * kV + kV) of each block.
     const int qt = lane / kL, qp = lane % kL;
-    const bool qt_ok = qt < M;
-    const uint16_t* xrow = x + (qt_ok ? qt : 0) * K + qp * kV;
     // MFMA role: weight row n0 + r, token r (rows r >= kMp are padding).
     const bool r_ok = r < kMp;
+    const int r_row = r_ok ? r : 0;
     const i32x4 rsrc_w = buffer_rsrc(wq + nt * 16 * K, (uint32_t)(16 * K));
+    const i32x4 rsrc_x = buffer_rsrc(x, (uint32_t)(M * K * 2));
     const int lane_off_w = slab_lane_offset(lane, K);
     const float* ws_row = ws + (nt * 16 / 128) * KB;
 
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
     const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
     for (int64_t kb0 = kb_begin + wave; kb0 < kb_end; kb0 += kStreamWaves * kFusedChunk) {
-        uint32_t raw[kFusedChunk][kV / 2];
-        u32x4 wa[kFusedChunk][2];
-#pragma unroll
-        for (int c = 0; c < kFusedChunk; ++c) {
-            const int64_t kb = kb0 + c * kStreamWaves;
-            if (kb < kb_end) {
-                load_words<kV / 2>(xrow + kb * 128, raw[c]);   // rows past M read row 0, zeroed below
-            }
-        }
-#pragma unroll
-        for (int c = 0; c < kFusedChunk; ++c) {
-            const int64_t kb = kb0 + c * kStreamWaves;
-            if (kb < kb_end) slab_issue(wslab[wave][c], rsrc_w, lane_off_w, K, kb);
-        }
+        const bool two = kb0 + kStreamWaves < kb_end;     // wave-uniform: blocks kb0 and kb0 + 16
+        // The previous pass's LDS accesses of these buffers are complete
+        // before new loads are aimed at them.
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         float wsv[kFusedChunk];
 #pragma unroll
         for (int c = 0; c < kFusedChunk; ++c) {
             const int64_t kb = kb0 + c * kStreamWaves;
             if (kb < kb_end) wsv[c] = ws_row[kb];
         }
-        wait_all_loads();
+#pragma unroll
+        for (int c = 0; c < kFusedChunk; ++c) {
+            const int64_t kb = kb0 + c * kStreamWaves;
+            if (kb < kb_end) xrows_issue<kMp>(xrows[wave][c], rsrc_x, lane, K, kb);
+        }
+#pragma unroll
+        for (int c = 0; c < kFusedChunk; ++c) {
+            const int64_t kb = kb0 + c * kStreamWaves;
+            if (kb < kb_end) slab_issue(wslab[wave][c], rsrc_w, lane_off_w, K, kb);
+        }
+        // Token rows in: the two slab loads per block issued after them may
+        // still be in flight.
+        if (two) wait_vmcnt<4>();
+        else wait_vmcnt<2>();
+        float s_r[kFusedChunk];
 #pragma unroll
         for (int c = 0; c < kFusedChunk; ++c) {
             const int64_t kb = kb0 + c * kStreamWaves;
             if (kb < kb_end) {
-                slab_read(wslab[wave][c], r, g, wa[c][0], wa[c][1]);
+                uint8_t* row = xrows[wave][c] + qt * kXRowStride;
+                uint32_t raw[kV / 2];
+                read_words<kV / 2>(row + qp * kV * 2, raw);
                 float v[kV];
                 float amax = 0.0f;
 #pragma unroll
-                for (int i = 0; i < kV / 2; ++i) raw[c][i] = qt_ok ? raw[c][i] : 0u;
-#pragma unroll
                 for (int i = 0; i < kV / 2; ++i) {
-                    v[2 * i] = kBf16 ? bf16_bits_to_float(raw[c][i] & 0xFFFFu) : f16_bits_to_float(raw[c][i] & 0xFFFFu);
-                    v[2 * i + 1] = kBf16 ? bf16_bits_to_float(raw[c][i] >> 16) : f16_bits_to_float(raw[c][i] >> 16);
+                    v[2 * i] = kBf16 ? bf16_bits_to_float(raw[i] & 0xFFFFu) : f16_bits_to_float(raw[i] & 0xFFFFu);
+                    v[2 * i + 1] = kBf16 ? bf16_bits_to_float(raw[i] >> 16) : f16_bits_to_float(raw[i] >> 16);
                     amax = fmaxf(amax, fmaxf(fabsf(v[2 * i]), fabsf(v[2 * i + 1])));
                 }
-#pragma unroll
-                for (int off = kL / 2; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
+                amax = token_max<kL>(amax);
                 const float s = amax / 448.0f;
                 uint32_t codes[(kV + 3) / 4];
                 quantize_v<kV>(v, s, codes);
-                store_codes<kV>(&xcode[wave][c][qt][qp * kV], codes);
+                store_codes<kV>(row + qp * kV, codes);
                 // This MFMA lane's token scale, from the first lane of token r.
-                const float s_r = __shfl(s, (r_ok ? r : 0) * kL, kWave);
-                const float sc = r_ok ? s_r * wsv[c] : 0.0f;
-                u32x4 b0 = {0u, 0u, 0u, 0u}, b1 = {0u, 0u, 0u, 0u};
-                if (r_ok) {
-                    b0 = *reinterpret_cast<const u32x4*>(&xcode[wave][c][r][16 * g]);
-                    b1 = *reinterpret_cast<const u32x4*>(&xcode[wave][c][r][64 + 16 * g]);
-                }
-                const i32x8 a = __builtin_bit_cast(i32x8, __builtin_shufflevector(wa[c][0], wa[c][1], 0, 1, 2, 3, 4, 5, 6, 7));
+                s_r[c] = token_value<kMp>(s, r_row);
+            }
+        }
+        wait_vmcnt<0>();   // weight slabs in (the weight scales are used only after this)
+#pragma unroll
+        for (int c = 0; c < kFusedChunk; ++c) {
+            const int64_t kb = kb0 + c * kStreamWaves;
+            if (kb < kb_end) {
+                u32x4 wa0, wa1;
+                slab_read(wslab[wave][c], r, g, wa0, wa1);
+                const uint8_t* row = xrows[wave][c] + r_row * kXRowStride;
+                u32x4 b0 = *reinterpret_cast<const u32x4*>(row + 16 * g);
+                u32x4 b1 = *reinterpret_cast<const u32x4*>(row + 64 + 16 * g);
+                const u32x4 z4 = {0u, 0u, 0u, 0u};
+                b0 = r_ok ? b0 : z4;
+                b1 = r_ok ? b1 : z4;
+                const i32x8 a = __builtin_bit_cast(i32x8, __builtin_shufflevector(wa0, wa1, 0, 1, 2, 3, 4, 5, 6, 7));
                 const i32x8 b = __builtin_bit_cast(i32x8, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7));
                 const f32x4 blk = mfma_e4m3_16x16x128(a, b, zero);
+                const float sc = r_ok ? s_r[c] * wsv[c] : 0.0f;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(blk[i], sc, acc[i]);
             }

@@ -77,6 +77,36 @@ __device__ __forceinline__ void slab_read(const uint8_t* slab, int r, int g, u32
     hi = *reinterpret_cast<const u32x4*>(slab + r * 128 + (((g + 4) ^ (r & 7)) << 4));
 }
 
+// ------------------------------------------------------ token rows ----
+// The token rows of one 128-K block staged in LDS by direct-to-LDS dword
+// loads: 256 bytes (128 16-bit values) per token, rows padded to
+// kXRowStride bytes so that the same column of consecutive rows falls in
+// distinct banks.  The loads are issued before a block's weight slabs, so
+// (loads complete in issue order) a wave can wait for its token rows while
+// the weights are still in flight.
+constexpr int kXRowStride = 272;   // 256-byte token rows, padded: rows of one column land in distinct banks
+
+// Direct-to-LDS loads of the kMp token rows of block kb into `rows` (one
+// dword per lane per row).  Rows at or past M lie past the descriptor's
+// range and load as zeros.
+template <int kMp>
+__device__ __forceinline__ void xrows_issue(uint8_t* rows, i32x4 rsrc_x, int lane, int64_t K, int64_t kb) {
+    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_address(rows));
+    const int k_off = __builtin_amdgcn_readfirstlane((int)(kb * 256));
+#pragma unroll
+    for (int t = 0; t < kMp; ++t)
+        dma4(__builtin_amdgcn_readfirstlane(base + t * kXRowStride), rsrc_x, (int)(t * K * 2) + 4 * lane, k_off);
+}
+
+// s_waitcnt vmcnt(N) alone; also a compiler barrier for memory accesses.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N == 0 || N == 2 || N == 4, "wait counts used here");
+    if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    else if constexpr (N == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+}
+
 __device__ __forceinline__ void store_out(void* y, int y_dtype, int64_t idx, float v) {
     if (y_dtype == 2) {
         static_cast<float*>(y)[idx] = v;
