@@ -52,7 +52,7 @@ constexpr int kCUs = 256;
 // (W8A16, bf16 or fp16).
 enum TileX { kTileCodes = 0, kTileBf16 = 1, kTileF16 = 2 };
 
-template <int BN_, int BM_, int WAVES_N, int WAVES_M, bool SPLIT, int X_ = kTileCodes>
+template <int BN_, int BM_, int WAVES_N, int WAVES_M, bool SPLIT, int X_ = kTileCodes, int FILL_ROWS_ = 0>
 struct TileCfg {
     static constexpr int BN = BN_, BM = BM_;
     static constexpr int X = X_;
@@ -82,6 +82,10 @@ struct TileCfg {
     // Vector-memory instructions one stage adds per wave: tile loads, the
     // token scales (W8A8 only) and the weight scale.
     static constexpr int kVmemPerStage = kLoadsPerWave + (kX16 ? 1 : 2);
+    // The refill loads of a block are spread over its first kFillRows MFMA
+    // rows (row i issues tile loads fill_lo(i) .. fill_lo(i + 1) - 1).
+    static constexpr int kFillRows = FILL_ROWS_ > 0 && FILL_ROWS_ < kTi ? FILL_ROWS_ : kTi;
+    static constexpr int fill_lo(int i) { return (i < kFillRows ? i : kFillRows) * kLoadsPerWave / kFillRows; }
     static_assert(kStages * kStageStride <= 160 * 1024, "LDS budget");
     static_assert(BN % (kRowsPerLoad * kWaves) == 0 && BM % (kBRowsPerLoad * kWaves) == 0, "load split");
     static_assert(kX16 || (kXsLanes >= 1 && kXsLanes <= kWave), "token-scale loads");
@@ -89,7 +93,11 @@ struct TileCfg {
     static_assert(kTi >= 1 && kTj >= 1 && kStages >= 2 && (kStages - 2) * kVmemPerStage < 64, "wave tile");
 };
 
-using Cfg256 = TileCfg<256, 256, 2, 4, false>;    // wave tile 128 n x 64 m, 2 stages
+// With two stages the next block's loads have only the current block's
+// compute to land in: they are issued over its first four MFMA rows (of
+// eight), not all eight, so the last of them is not issued just before the
+// wait at the top of the next block (3% at M = N = K = 4096, random data).
+using Cfg256 = TileCfg<256, 256, 2, 4, false, kTileCodes, 4>;    // wave tile 128 n x 64 m, 2 stages
 using Cfg128 = TileCfg<128, 128, 2, 4, false>;    // 64 x 32, 4 stages
 using Cfg64x128 = TileCfg<64, 128, 2, 4, true>;   // 32 x 32, 6 stages
 using Cfg128x64 = TileCfg<128, 64, 4, 2, true>;   // 32 x 32, 6 stages
@@ -362,8 +370,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void w8a8_tile_kernel(
             }
             if constexpr (decltype(refill)::value)
                 issue_stage<C>(fill, rsrc_a, rsrc_b, rsrc_xs, rsrc_ws, lane_off_a, lane_off_b, q_stride, q_stride_b,
-                               xs_off, fill_kb, wave, lane, i * C::kLoadsPerWave / C::kTi,
-                               (i + 1) * C::kLoadsPerWave / C::kTi, false);
+                               xs_off, fill_kb, wave, lane, C::fill_lo(i), C::fill_lo(i + 1), false);
             if (i > 0) {
 #pragma unroll
                 for (int j = 0; j < C::kTj; ++j)
@@ -395,8 +402,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void w8a8_tile_kernel(
             for (int j = 0; j < C::kTj; ++j) tmp[c][j] = mfma_e4m3_16x16x128(af, bf[j], zero);
             if constexpr (decltype(refill)::value)
                 issue_stage<C>(fill, rsrc_a, rsrc_b, rsrc_xs, rsrc_ws, lane_off_a, lane_off_b, q_stride, q_stride_b,
-                               xs_off, fill_kb, wave, lane, i * C::kLoadsPerWave / C::kTi,
-                               (i + 1) * C::kLoadsPerWave / C::kTi, false);
+                               xs_off, fill_kb, wave, lane, C::fill_lo(i), C::fill_lo(i + 1), false);
             if (i + 1 < C::kTi) af = read_frag<true>(stage, a_base + a_row(i + 1, r), g);
             if (i > 0) {
 #pragma unroll
