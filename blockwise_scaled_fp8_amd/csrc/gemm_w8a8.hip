@@ -167,6 +167,103 @@ __global__ __launch_bounds__(kStreamThreads) void w8a8_stream_kernel(
     }
 }
 
+// M <= 16 (padded token count Mp = 1, 2, 4, 8 or 16): the same product
+// with both operands staged in LDS.  The weights arrive as whole 128-byte
+// lines in per-wave slabs; the block's token rows (128 code bytes each) by
+// direct-to-LDS dword loads, two rows per load, lane l of a load fetching
+// the dword that belongs at LDS position 4 l of the two 128-byte rows with
+// the slab's chunk swizzle (chunk c of row R at position c ^ (R & 7)), so the
+// MFMA operand reads back with slab_read.  Rows past M lie outside the
+// buffer descriptor and read as zeros.  Per wave and block that is two
+// weight loads and Mp / 2 token loads (one for Mp = 1), against two
+// half-line weight loads and two 16-byte token loads per lane in the kernel
+// above; the token scales stay register loads (one dword per lane).
+template <int kMp>
+__device__ __forceinline__ void code_rows_issue(uint8_t* rows, i32x4 rsrc_x, int lane, int64_t K, int64_t kb) {
+    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_address(rows));
+    const int k_off = __builtin_amdgcn_readfirstlane((int)(kb * 128));
+    const int p = (lane & 31) >> 2;   // 16-byte chunk position inside the row
+#pragma unroll
+    for (int i = 0; i < (kMp + 1) / 2; ++i) {
+        const int row = 2 * i + (lane >> 5);
+        const int voff = (int)(row * K) + 16 * (p ^ (row & 7)) + 4 * (lane & 3);
+        dma4(__builtin_amdgcn_readfirstlane(base + 256 * i), rsrc_x, voff, k_off);
+    }
+}
+
+constexpr int kCodesLdsChunk = 2;
+
+template <int kMp>
+__global__ __launch_bounds__(kStreamThreads) void w8a8_stream_lds_kernel(
+    const uint8_t* __restrict__ xq, const float* __restrict__ xs,
+    const uint8_t* __restrict__ wq, const float* __restrict__ ws,
+    void* __restrict__ y, int y_dtype, int64_t M, int64_t N, int64_t K,
+    int64_t n_tiles, int64_t splits, int64_t kb_per_split,
+    float* __restrict__ partials, uint32_t* __restrict__ counters) {
+    constexpr int kRowsBytes = (kMp + 1) / 2 * 256;
+    __shared__ float red[kStreamWaves * 256];
+    __shared__ __attribute__((aligned(1024))) uint8_t xrows[kStreamWaves][kCodesLdsChunk][kRowsBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t wslab[kStreamWaves][kCodesLdsChunk][kSlabBytes];
+    const int64_t nt = blockIdx.x, split = blockIdx.y;
+    const int64_t KB = K / 128;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
+    const int r = lane & 15, g = lane >> 4;
+    const bool r_ok = r < kMp && r < M;
+    const int r_row = r < kMp ? r : 0;
+    const int64_t kb_begin = split * kb_per_split;
+    const int64_t kb_end = kb_begin + kb_per_split < KB ? kb_begin + kb_per_split : KB;
+
+    const i32x4 rsrc_w = buffer_rsrc(wq + nt * 16 * K, (uint32_t)(16 * K));
+    const i32x4 rsrc_x = buffer_rsrc(xq, (uint32_t)(M * K));
+    const int lane_off_w = slab_lane_offset(lane, K);
+    const float* ws_row = ws + (nt * 16 / 128) * KB;
+    const float* xs_row = xs + (r_ok ? r : 0) * KB;   // rows past M read row 0, zeroed at use
+
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+    const u32x4 z4 = {0u, 0u, 0u, 0u};
+    for (int64_t kb0 = kb_begin + wave; kb0 < kb_end; kb0 += kStreamWaves * kCodesLdsChunk) {
+        float xsv[kCodesLdsChunk], wsv[kCodesLdsChunk];
+#pragma unroll
+        for (int c = 0; c < kCodesLdsChunk; ++c) {
+            const int64_t kb = kb0 + c * kStreamWaves;
+            if (kb < kb_end) {
+                xsv[c] = xs_row[kb];
+                wsv[c] = ws_row[kb];
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < kCodesLdsChunk; ++c) {
+            const int64_t kb = kb0 + c * kStreamWaves;
+            if (kb < kb_end) code_rows_issue<kMp>(xrows[wave][c], rsrc_x, lane, K, kb);
+        }
+#pragma unroll
+        for (int c = 0; c < kCodesLdsChunk; ++c) {
+            const int64_t kb = kb0 + c * kStreamWaves;
+            if (kb < kb_end) slab_issue(wslab[wave][c], rsrc_w, lane_off_w, K, kb);
+        }
+        wait_vmcnt<0>();
+#pragma unroll
+        for (int c = 0; c < kCodesLdsChunk; ++c) {
+            const int64_t kb = kb0 + c * kStreamWaves;
+            if (kb < kb_end) {
+                u32x4 wa0, wa1, b0, b1;
+                slab_read(wslab[wave][c], r, g, wa0, wa1);
+                slab_read(xrows[wave][c], r_row, g, b0, b1);
+                b0 = r_ok ? b0 : z4;
+                b1 = r_ok ? b1 : z4;
+                const i32x8 a = __builtin_bit_cast(i32x8, __builtin_shufflevector(wa0, wa1, 0, 1, 2, 3, 4, 5, 6, 7));
+                const i32x8 b = __builtin_bit_cast(i32x8, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7));
+                const f32x4 blk = mfma_e4m3_16x16x128(a, b, zero);
+                const float sc = r_ok ? xsv[c] * wsv[c] : 0.0f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(blk[i], sc, acc[i]);
+            }
+        }
+    }
+    stream_finish(acc, red, y, y_dtype, M, N, nt, 0, splits, split, n_tiles, partials, counters);
+}
+
 // ------------------------------------------- activation quant fused in ----
 // The same streaming GEMM for M <= kFusedQuantMaxM with 16-bit activations
 // in: each wave quantises, for every 128-K block it multiplies, the block's
@@ -366,6 +463,20 @@ hipError_t launch_w8a8_stream(const uint8_t* xq, const float* xs, const uint8_t*
     float* partials;
     stream_workspace_parts(p, workspace, counters, partials);
     const dim3 grid((unsigned)p.n_tiles, (unsigned)p.splits, (unsigned)((p.m_tiles + p.mt_per_wg - 1) / p.mt_per_wg));
+    if (M <= 16) {
+#define BFP8_LAUNCH_LDS(MP)                                                                                    \
+    hipLaunchKernelGGL(w8a8_stream_lds_kernel<MP>, grid, dim3(kStreamThreads), 0, stream, xq, xs, wq, ws, y, y_dtype, \
+                       M, N, K, p.n_tiles, p.splits, p.kb_per_split, partials, counters)
+        switch (M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16) {
+            case 1: BFP8_LAUNCH_LDS(1); break;
+            case 2: BFP8_LAUNCH_LDS(2); break;
+            case 4: BFP8_LAUNCH_LDS(4); break;
+            case 8: BFP8_LAUNCH_LDS(8); break;
+            default: BFP8_LAUNCH_LDS(16); break;
+        }
+#undef BFP8_LAUNCH_LDS
+        return hipGetLastError();
+    }
 #define BFP8_LAUNCH_MT(MT)                                                                                      \
     hipLaunchKernelGGL(w8a8_stream_kernel<MT>, grid, dim3(kStreamThreads), 0, stream, xq, xs, wq, ws, y, y_dtype, M, \
                        N, K, p.n_tiles, p.splits, p.kb_per_split, partials, counters)
