@@ -21,19 +21,18 @@
 // e in [-14, 7] ([SM70] "Exactness"), so the MFMA sees exactly the weights
 // of a load-time fp16 dequantisation and accumulates in fp32 across all K.
 //
-// Both kernels stream the weights like the W8A8 decode kernel: one
+// The kernels here stream the weights like the W8A8 decode kernel: one
 // workgroup per 16 weight rows (and per split of K), 16 tokens on the MFMA
-// column axis; M > 16 is served by more token tiles, each streaming the
-// weights again.
+// column axis, sixteen waves taking interleaved 128-K blocks.  W8A16 blk128
+// with M > 16 runs the tiled MFMA kernel instead (gemm_w8a8_tile.hip); blk32
+// with M > 16 is served by more token tiles, each streaming the weights again.
 //
 // Operand mapping: within a 128-K block, lane l (row/column l % 16, slot
 // g = l / 16) holds the 16-byte weight chunks g and g + 4 of its row (K
-// offsets 16 g and 64 + 16 g), so each load instruction reads whole 64-byte
-// halves of 16 rows.  MFMA j (j = 0..3) takes 8 of those 32 values: K
-// offsets 16 g + 8 j for j < 2 and 64 + 16 g + 8 (j - 2) for j >= 2; the
-// activation operand of MFMA j is loaded with the same mapping, so the
-// contraction covers each K index once.  The eight waves take interleaved
-// 128-K blocks, so at any time a workgroup reads adjacent blocks of its rows.
+// offsets 16 g and 64 + 16 g).  MFMA j (j = 0..3) takes 8 of those 32
+// values: K offsets 16 g + 8 j for j < 2 and 64 + 16 g + 8 (j - 2) for
+// j >= 2; the activation operand of MFMA j is loaded with the same mapping,
+// so the contraction covers each K index once.
 
 #include "bfp8_device.hpp"
 #include "bfp8_launch.hpp"
@@ -49,166 +48,7 @@ __device__ __forceinline__ uint32_t scale_f16x2(uint32_t v, f16x2 factor) {
     return __builtin_bit_cast(uint32_t, p);
 }
 
-constexpr int kW8A16Chunk = 4;   // 128-K blocks per wave with loads in flight together
-
-template <bool kXBf16>
-__global__ __launch_bounds__(kStreamThreads) void w8a16_blk128_stream_kernel(
-    const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq, const float* __restrict__ ws,
-    void* __restrict__ y, int y_dtype, int64_t M, int64_t N, int64_t K,
-    int64_t n_tiles, int64_t splits, int64_t kb_per_split,
-    float* __restrict__ partials, uint32_t* __restrict__ counters) {
-    __shared__ float red[kStreamWaves * 256];
-    const int64_t nt = blockIdx.x, split = blockIdx.y, mt = blockIdx.z;
-    const int64_t KB = K / 128;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
-    const int r = lane & 15, g = lane >> 4;
-    const int64_t n = nt * 16 + r;
-    const int64_t m = mt * 16 + r;
-    const bool m_ok = m < M;
-    const int64_t kb_begin = split * kb_per_split;
-    const int64_t kb_end = kb_begin + kb_per_split < KB ? kb_begin + kb_per_split : KB;
-
-    const uint8_t* wrow = wq + n * K + g * 16;
-    const uint16_t* xrow = x + (m_ok ? m : 0) * K + g * 16;
-    const float* ws_row = ws + (nt * 16 / 128) * KB;
-    // Exponent-bias difference between E4M3 and the 16-bit type, folded into the scale.
-    const float bias_fold = kXBf16 ? 0x1p120f : 0x1p8f;
-
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int64_t kb0 = kb_begin + wave; kb0 < kb_end; kb0 += kStreamWaves * kW8A16Chunk) {
-        u32x4 wa[kW8A16Chunk][2], xb[kW8A16Chunk][4];
-        float wsv[kW8A16Chunk];
-        // Activations and weight scales first (from L2), then the weight
-        // stream; every load is issued before any wait (rows past M read row
-        // 0 and are zeroed by a select at use, so no load is in a divergent
-        // branch).
-#pragma unroll
-        for (int c = 0; c < kW8A16Chunk; ++c) {
-            const int64_t kb = kb0 + c * kStreamWaves;
-            if (kb < kb_end) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) xb[c][j] = load_16B(xrow + kb * 128 + (j < 2 ? 8 * j : 64 + 8 * (j - 2)));
-                wsv[c] = ws_row[kb];
-            }
-        }
-#pragma unroll
-        for (int c = 0; c < kW8A16Chunk; ++c) {
-            const int64_t kb = kb0 + c * kStreamWaves;
-            if (kb < kb_end) {
-                wa[c][0] = load_16B(wrow + kb * 128);
-                wa[c][1] = load_16B(wrow + kb * 128 + 64);
-            }
-        }
-        asm volatile("" ::: "memory");   // compiler-only: all loads above before the first wait
-#pragma unroll
-        for (int c = 0; c < kW8A16Chunk; ++c) {
-            const int64_t kb = kb0 + c * kStreamWaves;
-            if (kb < kb_end) {
-                const uint32_t q[8] = {wa[c][0][0], wa[c][0][1], wa[c][0][2], wa[c][0][3],
-                                       wa[c][1][0], wa[c][1][1], wa[c][1][2], wa[c][1][3]};
-                f32x4 blk = zero;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const u32x4 a = decode8<kXBf16>(q[2 * j], q[2 * j + 1]);
-                    const u32x4 xv = m_ok ? xb[c][j] : u32x4{0u, 0u, 0u, 0u};
-                    blk = kXBf16 ? mfma_bf16_16x16x32(a, xv, blk) : mfma_f16_16x16x32(a, xv, blk);
-                }
-                const float sc = wsv[c] * bias_fold;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(blk[i], sc, acc[i]);
-            }
-        }
-    }
-    stream_finish(acc, red, y, y_dtype, M, N, nt, mt, splits, split, n_tiles, partials, counters);
-}
-
-// M <= 8 (padded token count Mp = 1, 2, 4 or 8): the weights come through
-// LDS slabs as whole 128-byte lines, and the block's token rows as
-// direct-to-LDS dword loads (one per token row and block), all issued
-// before the first wait.  Per wave and block that is two weight loads and
-// Mp token loads, where the register-operand kernel above issues two
-// half-line weight loads and four 16-byte token loads per lane (sixteen
-// lanes of one token column reading the same row when M = 1).  Lanes past
-// the token count read row 0 and are zeroed by a select.
-constexpr int kW8A16LdsMaxM = 8;
-constexpr int kW8A16LdsChunk = 2;
-
-template <bool kXBf16, int kMp>
-__global__ __launch_bounds__(kStreamThreads) void w8a16_blk128_stream_lds_kernel(
-    const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq, const float* __restrict__ ws,
-    void* __restrict__ y, int y_dtype, int64_t M, int64_t N, int64_t K,
-    int64_t n_tiles, int64_t splits, int64_t kb_per_split,
-    float* __restrict__ partials, uint32_t* __restrict__ counters) {
-    __shared__ float red[kStreamWaves * 256];
-    __shared__ __attribute__((aligned(16))) uint8_t xrows[kStreamWaves][kW8A16LdsChunk][kMp * kXRowStride];
-    __shared__ __attribute__((aligned(1024))) uint8_t wslab[kStreamWaves][kW8A16LdsChunk][kSlabBytes];
-    const int64_t nt = blockIdx.x, split = blockIdx.y;
-    const int64_t KB = K / 128;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
-    const int r = lane & 15, g = lane >> 4;
-    const bool r_ok = r < kMp;
-    const int r_row = r_ok ? r : 0;
-    const int64_t kb_begin = split * kb_per_split;
-    const int64_t kb_end = kb_begin + kb_per_split < KB ? kb_begin + kb_per_split : KB;
-
-    const i32x4 rsrc_w = buffer_rsrc(wq + nt * 16 * K, (uint32_t)(16 * K));
-    const i32x4 rsrc_x = buffer_rsrc(x, (uint32_t)(M * K * 2));
-    const int lane_off_w = slab_lane_offset(lane, K);
-    const float* ws_row = ws + (nt * 16 / 128) * KB;
-    const float bias_fold = kXBf16 ? 0x1p120f : 0x1p8f;
-
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
-    const u32x4 z4 = {0u, 0u, 0u, 0u};
-    for (int64_t kb0 = kb_begin + wave; kb0 < kb_end; kb0 += kStreamWaves * kW8A16LdsChunk) {
-        float wsv[kW8A16LdsChunk];
-#pragma unroll
-        for (int c = 0; c < kW8A16LdsChunk; ++c) {
-            const int64_t kb = kb0 + c * kStreamWaves;
-            if (kb < kb_end) wsv[c] = ws_row[kb];
-        }
-#pragma unroll
-        for (int c = 0; c < kW8A16LdsChunk; ++c) {
-            const int64_t kb = kb0 + c * kStreamWaves;
-            if (kb < kb_end) xrows_issue<kMp>(xrows[wave][c], rsrc_x, lane, K, kb);
-        }
-#pragma unroll
-        for (int c = 0; c < kW8A16LdsChunk; ++c) {
-            const int64_t kb = kb0 + c * kStreamWaves;
-            if (kb < kb_end) slab_issue(wslab[wave][c], rsrc_w, lane_off_w, K, kb);
-        }
-        wait_vmcnt<0>();
-#pragma unroll
-        for (int c = 0; c < kW8A16LdsChunk; ++c) {
-            const int64_t kb = kb0 + c * kStreamWaves;
-            if (kb < kb_end) {
-                u32x4 wa0, wa1;
-                slab_read(wslab[wave][c], r, g, wa0, wa1);
-                const uint32_t q[8] = {wa0[0], wa0[1], wa0[2], wa0[3], wa1[0], wa1[1], wa1[2], wa1[3]};
-                // MFMA j takes K offsets 16 g + 8 j (j < 2) and 64 + 16 g + 8 (j - 2):
-                // bytes 32 g + 16 j and 128 + 32 g + 16 (j - 2) of the token row.
-                const uint8_t* row = xrows[wave][c] + r_row * kXRowStride + 32 * g;
-                u32x4 xv[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    xv[j] = *reinterpret_cast<const u32x4*>(row + (j < 2 ? 16 * j : 128 + 16 * (j - 2)));
-                    xv[j] = r_ok ? xv[j] : z4;
-                }
-                f32x4 blk = zero;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const u32x4 a = decode8<kXBf16>(q[2 * j], q[2 * j + 1]);
-                    blk = kXBf16 ? mfma_bf16_16x16x32(a, xv[j], blk) : mfma_f16_16x16x32(a, xv[j], blk);
-                }
-                const float sc = wsv[c] * bias_fold;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(blk[i], sc, acc[i]);
-            }
-        }
-    }
-    stream_finish(acc, red, y, y_dtype, M, N, nt, 0, splits, split, n_tiles, partials, counters);
-}
+constexpr int kW8A16Chunk = 4;   // 128-K blocks per wave with loads in flight together (blk32, M > 16)
 
 __global__ __launch_bounds__(kStreamThreads) void w8a16_blk32_stream_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq, const uint8_t* __restrict__ e8m0,
@@ -284,6 +124,205 @@ __global__ __launch_bounds__(kStreamThreads) void w8a16_blk32_stream_kernel(
     stream_finish(acc, red, y, y_dtype, M, N, nt, mt, splits, split, n_tiles, partials, counters);
 }
 
+// M <= 16 (padded token count Mp = 1, 2, 4, 8 or 16): the weights come
+// through LDS slabs as whole 128-byte lines (two loads of eight full lines
+// per block, where register loads in the MFMA layout read sixteen half
+// lines), and for Mp <= 8 the block's token rows as direct-to-LDS dword
+// loads (one per token row and block), all issued before the first wait.
+// Per wave and block that is two weight loads and Mp token loads, where
+// register token loads take four 16-byte loads per lane (sixteen lanes of
+// one token column reading the same row when M = 1).  With Mp = 16 every
+// lane carries a live token row, so the token loads stay register loads
+// (and sixteen 256-byte rows per block would not fit beside the slabs).
+// Lanes past the token count read row 0 and are zeroed by a select.
+constexpr int kW8A16LdsMaxM = 16;
+constexpr int kW8A16LdsChunk = 2;
+
+template <bool kXBf16, int kMp>
+__global__ __launch_bounds__(kStreamThreads) void w8a16_blk128_stream_lds_kernel(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq, const float* __restrict__ ws,
+    void* __restrict__ y, int y_dtype, int64_t M, int64_t N, int64_t K,
+    int64_t n_tiles, int64_t splits, int64_t kb_per_split,
+    float* __restrict__ partials, uint32_t* __restrict__ counters) {
+    constexpr bool kRegX = kMp == 16;   // sixteen live token rows: register loads, no LDS rows
+    __shared__ float red[kStreamWaves * 256];
+    __shared__ __attribute__((aligned(16))) uint8_t xrows[kStreamWaves][kW8A16LdsChunk][kRegX ? 16 : kMp * kXRowStride];
+    __shared__ __attribute__((aligned(1024))) uint8_t wslab[kStreamWaves][kW8A16LdsChunk][kSlabBytes];
+    const int64_t nt = blockIdx.x, split = blockIdx.y;
+    const int64_t KB = K / 128;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
+    const int r = lane & 15, g = lane >> 4;
+    const bool r_ok = r < kMp && r < M;
+    const int r_row = r < kMp ? r : 0;
+    // Register path: lane (r, g) reads its K slices of token r straight
+    // from memory (rows past M read row 0, zeroed by the select).
+    const uint16_t* xreg = x + (r_ok ? r : 0) * K + g * 16;
+    const int64_t kb_begin = split * kb_per_split;
+    const int64_t kb_end = kb_begin + kb_per_split < KB ? kb_begin + kb_per_split : KB;
+
+    const i32x4 rsrc_w = buffer_rsrc(wq + nt * 16 * K, (uint32_t)(16 * K));
+    const i32x4 rsrc_x = buffer_rsrc(x, (uint32_t)(M * K * 2));
+    const int lane_off_w = slab_lane_offset(lane, K);
+    const float* ws_row = ws + (nt * 16 / 128) * KB;
+    const float bias_fold = kXBf16 ? 0x1p120f : 0x1p8f;
+
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+    const u32x4 z4 = {0u, 0u, 0u, 0u};
+    for (int64_t kb0 = kb_begin + wave; kb0 < kb_end; kb0 += kStreamWaves * kW8A16LdsChunk) {
+        float wsv[kW8A16LdsChunk];
+        u32x4 xr[kW8A16LdsChunk][4];
+#pragma unroll
+        for (int c = 0; c < kW8A16LdsChunk; ++c) {
+            const int64_t kb = kb0 + c * kStreamWaves;
+            if (kb < kb_end) {
+                wsv[c] = ws_row[kb];
+                if constexpr (kRegX) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) xr[c][j] = load_16B(xreg + kb * 128 + (j < 2 ? 8 * j : 64 + 8 * (j - 2)));
+                }
+            }
+        }
+        if constexpr (!kRegX) {
+#pragma unroll
+            for (int c = 0; c < kW8A16LdsChunk; ++c) {
+                const int64_t kb = kb0 + c * kStreamWaves;
+                if (kb < kb_end) xrows_issue<kMp>(xrows[wave][c], rsrc_x, lane, K, kb);
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < kW8A16LdsChunk; ++c) {
+            const int64_t kb = kb0 + c * kStreamWaves;
+            if (kb < kb_end) slab_issue(wslab[wave][c], rsrc_w, lane_off_w, K, kb);
+        }
+        wait_vmcnt<0>();
+#pragma unroll
+        for (int c = 0; c < kW8A16LdsChunk; ++c) {
+            const int64_t kb = kb0 + c * kStreamWaves;
+            if (kb < kb_end) {
+                u32x4 wa0, wa1;
+                slab_read(wslab[wave][c], r, g, wa0, wa1);
+                const uint32_t q[8] = {wa0[0], wa0[1], wa0[2], wa0[3], wa1[0], wa1[1], wa1[2], wa1[3]};
+                // MFMA j takes K offsets 16 g + 8 j (j < 2) and 64 + 16 g + 8 (j - 2):
+                // bytes 32 g + 16 j and 128 + 32 g + 16 (j - 2) of the token row.
+                const uint8_t* row = xrows[wave][c] + r_row * kXRowStride + 32 * g;
+                u32x4 xv[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if constexpr (kRegX) xv[j] = xr[c][j];
+                    else xv[j] = *reinterpret_cast<const u32x4*>(row + (j < 2 ? 16 * j : 128 + 16 * (j - 2)));
+                    xv[j] = r_ok ? xv[j] : z4;
+                }
+                f32x4 blk = zero;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const u32x4 a = decode8<kXBf16>(q[2 * j], q[2 * j + 1]);
+                    blk = kXBf16 ? mfma_bf16_16x16x32(a, xv[j], blk) : mfma_f16_16x16x32(a, xv[j], blk);
+                }
+                const float sc = wsv[c] * bias_fold;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(blk[i], sc, acc[i]);
+            }
+        }
+    }
+    stream_finish(acc, red, y, y_dtype, M, N, nt, 0, splits, split, n_tiles, partials, counters);
+}
+
+// blk32 for M <= 16, staged like w8a16_blk128_stream_lds_kernel: weight
+// lines through LDS slabs, the block's fp16 token rows by direct-to-LDS
+// loads for Mp <= 8 (register loads for Mp = 16), issued before the first
+// wait; the scale bytes stay register loads.  The exact fp16 scaling and the accumulation across all K are those
+// of the kernel above.
+template <int kMp>
+__global__ __launch_bounds__(kStreamThreads) void w8a16_blk32_stream_lds_kernel(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq, const uint8_t* __restrict__ e8m0,
+    void* __restrict__ y, int y_dtype, int64_t M, int64_t N, int64_t K,
+    int64_t n_tiles, int64_t splits, int64_t kb_per_split,
+    float* __restrict__ partials, uint32_t* __restrict__ counters) {
+    constexpr bool kRegX = kMp == 16;   // sixteen live token rows: register loads, no LDS rows
+    __shared__ float red[kStreamWaves * 256];
+    __shared__ __attribute__((aligned(16))) uint8_t xrows[kStreamWaves][kW8A16LdsChunk][kRegX ? 16 : kMp * kXRowStride];
+    __shared__ __attribute__((aligned(1024))) uint8_t wslab[kStreamWaves][kW8A16LdsChunk][kSlabBytes];
+    const int64_t nt = blockIdx.x, split = blockIdx.y;
+    const int64_t KB = K / 128, K32 = K / 32;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
+    const int r = lane & 15, g = lane >> 4;
+    const bool r_ok = r < kMp && r < M;
+    const int r_row = r < kMp ? r : 0;
+    const uint16_t* xreg = x + (r_ok ? r : 0) * K + g * 16;
+    const int64_t n = nt * 16 + r;
+    const int64_t kb_begin = split * kb_per_split;
+    const int64_t kb_end = kb_begin + kb_per_split < KB ? kb_begin + kb_per_split : KB;
+
+    const i32x4 rsrc_w = buffer_rsrc(wq + nt * 16 * K, (uint32_t)(16 * K));
+    const i32x4 rsrc_x = buffer_rsrc(x, (uint32_t)(M * K * 2));
+    const int lane_off_w = slab_lane_offset(lane, K);
+    // Chunk g of block kb lies in 32x32 tile (n / 32, 4 kb + g / 2), chunk
+    // g + 4 in tile (n / 32, 4 kb + 2 + g / 2).
+    const uint8_t* erow = e8m0 + (n / 32) * K32 + (g >> 1);
+
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    const u32x4 z4 = {0u, 0u, 0u, 0u};
+    for (int64_t kb0 = kb_begin + wave; kb0 < kb_end; kb0 += kStreamWaves * kW8A16LdsChunk) {
+        uint32_t ebyte[kW8A16LdsChunk][2];
+        u32x4 xr[kW8A16LdsChunk][4];
+#pragma unroll
+        for (int c = 0; c < kW8A16LdsChunk; ++c) {
+            const int64_t kb = kb0 + c * kStreamWaves;
+            if (kb < kb_end) {
+                ebyte[c][0] = erow[kb * 4];
+                ebyte[c][1] = erow[kb * 4 + 2];
+                if constexpr (kRegX) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) xr[c][j] = load_16B(xreg + kb * 128 + (j < 2 ? 8 * j : 64 + 8 * (j - 2)));
+                }
+            }
+        }
+        if constexpr (!kRegX) {
+#pragma unroll
+            for (int c = 0; c < kW8A16LdsChunk; ++c) {
+                const int64_t kb = kb0 + c * kStreamWaves;
+                if (kb < kb_end) xrows_issue<kMp>(xrows[wave][c], rsrc_x, lane, K, kb);
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < kW8A16LdsChunk; ++c) {
+            const int64_t kb = kb0 + c * kStreamWaves;
+            if (kb < kb_end) slab_issue(wslab[wave][c], rsrc_w, lane_off_w, K, kb);
+        }
+        wait_vmcnt<0>();
+#pragma unroll
+        for (int c = 0; c < kW8A16LdsChunk; ++c) {
+            const int64_t kb = kb0 + c * kStreamWaves;
+            if (kb < kb_end) {
+                u32x4 wa0, wa1;
+                slab_read(wslab[wave][c], r, g, wa0, wa1);
+                const uint32_t q[8] = {wa0[0], wa0[1], wa0[2], wa0[3], wa1[0], wa1[1], wa1[2], wa1[3]};
+                const uint8_t* row = xrows[wave][c] + r_row * kXRowStride + 32 * g;
+                // 2^(E - 127 + 8) as fp16: exponent field E - 104 (see the kernel above).
+                const uint32_t f0 = (ebyte[c][0] - 104u) << 10, f1 = (ebyte[c][1] - 104u) << 10;
+                const f16x2 factor0 = __builtin_bit_cast(f16x2, f0 | (f0 << 16));
+                const f16x2 factor1 = __builtin_bit_cast(f16x2, f1 | (f1 << 16));
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    u32x4 xv;
+                    if constexpr (kRegX) xv = xr[c][j];
+                    else xv = *reinterpret_cast<const u32x4*>(row + (j < 2 ? 16 * j : 128 + 16 * (j - 2)));
+                    xv = r_ok ? xv : z4;
+                    uint32_t d0, d1, d2, d3;
+                    e4m3x4_to_f16x4(q[2 * j], d0, d1);
+                    e4m3x4_to_f16x4(q[2 * j + 1], d2, d3);
+                    const f16x2 factor = j < 2 ? factor0 : factor1;
+                    const u32x4 a = {scale_f16x2(d0, factor), scale_f16x2(d1, factor),
+                                     scale_f16x2(d2, factor), scale_f16x2(d3, factor)};
+                    acc = mfma_f16_16x16x32(a, xv, acc);
+                }
+            }
+        }
+    }
+    stream_finish(acc, red, y, y_dtype, M, N, nt, 0, splits, split, n_tiles, partials, counters);
+}
+
 hipError_t launch_w8a16_blk128_stream(const void* x, bool x_bf16, const uint8_t* wq, const float* ws,
                                       void* y, int y_dtype, int64_t M, int64_t N, int64_t K,
                                       void* workspace, hipStream_t stream) {
@@ -293,7 +332,7 @@ hipError_t launch_w8a16_blk128_stream(const void* x, bool x_bf16, const uint8_t*
     stream_workspace_parts(p, workspace, counters, partials);
     const dim3 grid((unsigned)p.n_tiles, (unsigned)p.splits, (unsigned)p.m_tiles);
     if (M <= kW8A16LdsMaxM) {
-        const int mp = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8;
+        const int mp = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16;
         const uint16_t* xh = static_cast<const uint16_t*>(x);
 #define BFP8_LAUNCH_LDS(BF, MP)                                                                                \
     hipLaunchKernelGGL((w8a16_blk128_stream_lds_kernel<BF, MP>), grid, dim3(kStreamThreads), 0, stream, xh, wq, ws, \
@@ -303,29 +342,22 @@ hipError_t launch_w8a16_blk128_stream(const void* x, bool x_bf16, const uint8_t*
                 case 1: BFP8_LAUNCH_LDS(true, 1); break;
                 case 2: BFP8_LAUNCH_LDS(true, 2); break;
                 case 4: BFP8_LAUNCH_LDS(true, 4); break;
-                default: BFP8_LAUNCH_LDS(true, 8); break;
+                case 8: BFP8_LAUNCH_LDS(true, 8); break;
+                default: BFP8_LAUNCH_LDS(true, 16); break;
             }
         } else {
             switch (mp) {
                 case 1: BFP8_LAUNCH_LDS(false, 1); break;
                 case 2: BFP8_LAUNCH_LDS(false, 2); break;
                 case 4: BFP8_LAUNCH_LDS(false, 4); break;
-                default: BFP8_LAUNCH_LDS(false, 8); break;
+                case 8: BFP8_LAUNCH_LDS(false, 8); break;
+                default: BFP8_LAUNCH_LDS(false, 16); break;
             }
         }
 #undef BFP8_LAUNCH_LDS
         return hipGetLastError();
     }
-    if (x_bf16) {
-        hipLaunchKernelGGL(w8a16_blk128_stream_kernel<true>, grid, dim3(kStreamThreads), 0, stream,
-                           static_cast<const uint16_t*>(x), wq, ws, y, y_dtype, M, N, K,
-                           p.n_tiles, p.splits, p.kb_per_split, partials, counters);
-    } else {
-        hipLaunchKernelGGL(w8a16_blk128_stream_kernel<false>, grid, dim3(kStreamThreads), 0, stream,
-                           static_cast<const uint16_t*>(x), wq, ws, y, y_dtype, M, N, K,
-                           p.n_tiles, p.splits, p.kb_per_split, partials, counters);
-    }
-    return hipGetLastError();
+    return hipErrorInvalidValue;   // M > 16 runs the tiled kernel (launch_w8a16_tile)
 }
 
 hipError_t launch_w8a16_blk32_stream(const void* x, const uint8_t* wq, const uint8_t* e8m0,
@@ -335,6 +367,22 @@ hipError_t launch_w8a16_blk32_stream(const void* x, const uint8_t* wq, const uin
     uint32_t* counters;
     float* partials;
     stream_workspace_parts(p, workspace, counters, partials);
+    if (M <= kW8A16LdsMaxM) {
+        const dim3 grid((unsigned)p.n_tiles, (unsigned)p.splits, 1u);
+        const uint16_t* xh = static_cast<const uint16_t*>(x);
+#define BFP8_LAUNCH_LDS32(MP)                                                                                   \
+    hipLaunchKernelGGL(w8a16_blk32_stream_lds_kernel<MP>, grid, dim3(kStreamThreads), 0, stream, xh, wq, e8m0, y, \
+                       y_dtype, M, N, K, p.n_tiles, p.splits, p.kb_per_split, partials, counters)
+        switch (M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16) {
+            case 1: BFP8_LAUNCH_LDS32(1); break;
+            case 2: BFP8_LAUNCH_LDS32(2); break;
+            case 4: BFP8_LAUNCH_LDS32(4); break;
+            case 8: BFP8_LAUNCH_LDS32(8); break;
+            default: BFP8_LAUNCH_LDS32(16); break;
+        }
+#undef BFP8_LAUNCH_LDS32
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(w8a16_blk32_stream_kernel, dim3((unsigned)p.n_tiles, (unsigned)p.splits, (unsigned)p.m_tiles),
                        dim3(kStreamThreads), 0, stream, static_cast<const uint16_t*>(x), wq, e8m0, y, y_dtype,
                        M, N, K, p.n_tiles, p.splits, p.kb_per_split, partials, counters);

@@ -196,7 +196,7 @@ def test_w8a8_deterministic(gpu_lib):
 # ------------------------------------------------------------ W8A16 blk128 ----
 
 @pytest.mark.parametrize("xdtype", [torch.bfloat16, torch.float16])
-@pytest.mark.parametrize("M", [1, 2, 4, 8, 16, 17, 33, 64, 65, 130])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 12, 16, 17, 33, 64, 65, 130])
 def test_w8a16_blk128(gpu_lib, M, xdtype):
     N, K = 512, 1024
     say("w8a16 blk128", M, xdtype)
@@ -299,7 +299,7 @@ def _blk32_inputs(M, N, K, wid, lo=-14, hi=7):
     return x, wq, e8.numpy()
 
 
-@pytest.mark.parametrize("M", [1, 2, 4, 8, 16])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 8, 12, 16])
 def test_blk32_block32_workload_shape(gpu_lib, M):
     """N=4096, K=7168 block-32 weights, e uniform on [-14, 7]."""
     say("blk32", M)
