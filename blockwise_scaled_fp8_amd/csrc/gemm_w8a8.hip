@@ -424,7 +424,7 @@ __global__ __launch_bounds__(kStreamThreads) void w8a8_stream_quant_kernel(
                 amax = token_max<kL>(amax);
                 const float s = amax / 448.0f;
                 uint32_t codes[(kV + 3) / 4];
-                quantize_v<kV>(v, s, codes);
+                quantize_v<kV>(v, raw, s, codes);
                 store_codes<kV>(row + qp * kV, codes);
                 // This MFMA lane's token scale, from the first lane of token r.
                 s_r[c] = token_value<kMp>(s, r_row);

@@ -26,19 +26,19 @@ constexpr int kQuantActThreads = 256;
 __global__ __launch_bounds__(kQuantActThreads) void quant_act_1x128_kernel(
     const uint16_t* __restrict__ x, int bf16, int64_t M, int64_t K, int64_t G, int64_t blocks_per_row,
     uint8_t* __restrict__ xq, float* __restrict__ xs) {
-    const int64_t m = blockIdx.x / blocks_per_row;               // uniform per workgroup
-    const int64_t g = (blockIdx.x - m * blocks_per_row) * (kQuantActThreads / 16) + (threadIdx.x >> 4);
+    // 32-bit index arithmetic (the launcher keeps the grid below 2^32): the
+    // 64-bit division took some fifty scalar instructions per wave.
+    const uint32_t mb = (uint32_t)blockIdx.x / (uint32_t)blocks_per_row;   // uniform per workgroup
+    const int64_t m = mb;
+    const int64_t g = (int64_t)((uint32_t)blockIdx.x - mb * (uint32_t)blocks_per_row) * (kQuantActThreads / 16) +
+                      (threadIdx.x >> 4);
     const int lane16 = threadIdx.x & 15;
     const int64_t col = g * 128 + lane16 * 8;
     const bool valid = g < G && col < K;            // K % 8 == 0: a chunk is all in or all out
 
+    const u32x4 raw = valid ? load_16B(x + m * K + col) : u32x4{0u, 0u, 0u, 0u};
     float v[8];
-    if (valid) {
-        unpack8(load_16B(x + m * K + col), bf16 != 0, v);
-    } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = 0.0f;
-    }
+    unpack8(raw, bf16 != 0, v);
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
@@ -46,7 +46,7 @@ __global__ __launch_bounds__(kQuantActThreads) void quant_act_1x128_kernel(
 
     const float s = amax / 448.0f;
     uint32_t lo, hi;
-    quantize8(v, s, lo, hi);
+    quantize8(v, raw, s, lo, hi);
     if (valid) {
         *reinterpret_cast<uint2*>(xq + m * K + col) = make_uint2(lo, hi);
         if (lane16 == 0) xs[m * G + g] = s;
@@ -67,16 +67,13 @@ __global__ __launch_bounds__(kQuantWThreads) void quant_weight_128x128_kernel(
     const bool col_ok = col < K;
 
     float v[8][8];
+    u32x4 raw[8];
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int64_t row = nb * 128 + (t >> 4) + 16 * i;
-        if (col_ok && row < N) {
-            unpack8(load_16B(w + row * K + col), bf16 != 0, v[i]);
-        } else {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) v[i][j] = 0.0f;
-        }
+        raw[i] = col_ok && row < N ? load_16B(w + row * K + col) : u32x4{0u, 0u, 0u, 0u};
+        unpack8(raw[i], bf16 != 0, v[i]);
 #pragma unroll
         for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[i][j]));
     }
@@ -90,7 +87,7 @@ __global__ __launch_bounds__(kQuantWThreads) void quant_weight_128x128_kernel(
     for (int i = 0; i < 8; ++i) {
         const int64_t row = nb * 128 + (t >> 4) + 16 * i;
         uint32_t lo, hi;
-        quantize8(v[i], s, lo, hi);
+        quantize8(v[i], raw[i], s, lo, hi);
         if (col_ok && row < N) *reinterpret_cast<uint2*>(wq + row * K + col) = make_uint2(lo, hi);
     }
     if (t == 0) ws[nb * KB + kb] = s;
@@ -100,6 +97,7 @@ hipError_t launch_quant_act_1x128(const void* x, bool bf16, int64_t M, int64_t K
                                   uint8_t* xq, float* xs, hipStream_t stream) {
     const int64_t G = (K + 127) / 128;
     const int64_t blocks_per_row = (G + kQuantActThreads / 16 - 1) / (kQuantActThreads / 16);
+    if (M * blocks_per_row >= (int64_t(1) << 32)) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(quant_act_1x128_kernel, dim3((unsigned)(M * blocks_per_row)), dim3(kQuantActThreads), 0,
                        stream, static_cast<const uint16_t*>(x), (int)bf16, M, K, G, blocks_per_row, xq, xs);
     return hipGetLastError();
