@@ -86,6 +86,12 @@ struct TileCfg {
     // rows (row i issues tile loads fill_lo(i) .. fill_lo(i + 1) - 1).
     static constexpr int kFillRows = FILL_ROWS_ > 0 && FILL_ROWS_ < kTi ? FILL_ROWS_ : kTi;
     static constexpr int fill_lo(int i) { return (i < kFillRows ? i : kFillRows) * kLoadsPerWave / kFillRows; }
+    // W8A16 with many token tiles per wave: token fragments are streamed one
+    // tile column at a time (all of them would not fit in registers) and the
+    // widened weight rows are kept for the whole block.
+    static constexpr bool kJOuter = kX16 && kTj > 4;
+    static constexpr int kFillCols = kTj / 2;   // j-outer: refill loads over the first half of the columns
+    static constexpr int fill_lo_j(int j) { return (j < kFillCols ? j : kFillCols) * kLoadsPerWave / kFillCols; }
     static_assert(kStages * kStageStride <= 160 * 1024, "LDS budget");
     static_assert(BN % (kRowsPerLoad * kWaves) == 0 && BM % (kBRowsPerLoad * kWaves) == 0, "load split");
     static_assert(kX16 || (kXsLanes >= 1 && kXsLanes <= kWave), "token-scale loads");
@@ -105,6 +111,10 @@ using Cfg128x64 = TileCfg<128, 64, 4, 2, true>;   // 32 x 32, 6 stages
 // across the weight rows, so each decoded weight fragment feeds kTj MFMAs).
 template <int X> using Cfg16_128 = TileCfg<128, 128, 4, 2, true, X>;   // 3 stages
 template <int X> using Cfg16_64 = TileCfg<128, 64, 4, 2, true, X>;     // 4 stages
+// Large M: 256 weight rows x 128 tokens, eight waves stacked along the
+// weight rows (wave tile 32 x 128), so each widened weight fragment feeds
+// eight token tiles; two stages.
+template <int X> using Cfg16_256 = TileCfg<256, 128, 8, 1, false, X>;
 
 // s_waitcnt vmcnt(N) lgkmcnt(0) (expcnt not waited for).
 template <int N>
@@ -331,7 +341,64 @@ __global__ __launch_bounds__(C::kThreads, 1) void w8a8_tile_kernel(
     // loads are issued between the MFMA rows, so a wave never waits for the
     // memory pipeline to accept a whole stage before it starts multiplying.
     auto compute = [&](const uint8_t* stage, auto refill, uint8_t* fill, int64_t fill_kb) {
-      if constexpr (C::kX16) {
+      if constexpr (C::kJOuter) {
+        // The kTi weight rows of the block are widened once (aop), then each
+        // token tile column j is read (one ahead) and multiplied by every row;
+        // the promotion of column j - 1 follows the MFMAs of column j.
+        constexpr float kBiasFold = C::X == kTileBf16 ? 0x1p120f : 0x1p8f;
+        const float wsc = reinterpret_cast<const float*>(stage + C::kOffWs)[wave] * kBiasFold;
+        u32x4 aop[C::kTi][4];
+#pragma unroll
+        for (int i = 0; i < C::kTi; ++i) {
+            const i32x8 af = read_frag<true>(stage, a_base + a_row(i, r), g);
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+                aop[i][jj] = decode8<C::X == kTileBf16>((uint32_t)af[2 * jj], (uint32_t)af[2 * jj + 1]);
+        }
+        auto read_b = [&](int j, u32x4 (&b)[4]) {
+            const int row = C::kWaveM * wm + 16 * j + r;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+                b[jj] = *reinterpret_cast<const u32x4*>(stage + C::kStageA +
+                                                        swz_b16(row, 2 * g + 8 * (jj >> 1) + (jj & 1)));
+        };
+        u32x4 bcur[4], bnext[4];
+        read_b(0, bcur);
+        f32x4 tmp[2][C::kTi];
+#pragma unroll
+        for (int j = 0; j < C::kTj; ++j) {
+            const int c = j & 1;
+            if (j + 1 < C::kTj) read_b(j + 1, bnext);
+#pragma unroll
+            for (int i = 0; i < C::kTi; ++i) {
+                f32x4 blk = zero;
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj)
+                    blk = C::X == kTileBf16 ? mfma_bf16_16x16x32(aop[i][jj], bcur[jj], blk)
+                                            : mfma_f16_16x16x32(aop[i][jj], bcur[jj], blk);
+                tmp[c][i] = blk;
+            }
+            if constexpr (decltype(refill)::value)
+                issue_stage<C>(fill, rsrc_a, rsrc_b, rsrc_xs, rsrc_ws, lane_off_a, lane_off_b, q_stride, q_stride_b,
+                               xs_off, fill_kb, wave, lane, C::fill_lo_j(j), C::fill_lo_j(j + 1), false);
+            if (j > 0) {
+#pragma unroll
+                for (int i = 0; i < C::kTi; ++i)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        acc[i][j - 1][e] = __builtin_fmaf(tmp[c ^ 1][i][e], wsc, acc[i][j - 1][e]);
+            }
+            if (j + 1 < C::kTj) {
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) bcur[jj] = bnext[jj];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < C::kTi; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                acc[i][C::kTj - 1][e] = __builtin_fmaf(tmp[(C::kTj - 1) & 1][i][e], wsc, acc[i][C::kTj - 1][e]);
+      } else if constexpr (C::kX16) {
         // W8A16: per 16x16 tile and block, four 16x16x32 MFMAs on weights
         // widened in registers (decode8: the E4M3 bias difference, 2^120 for
         // bf16 and 2^8 for fp16, is folded into the block scale).  MFMA jj
@@ -537,7 +604,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void w8a8_tile_kernel(
 
 namespace {
 
-enum class TileShape { k256, k128, k64x128, k128x64, k16_128, k16_64 };
+enum class TileShape { k256, k128, k64x128, k128x64, k16_256, k16_128, k16_64 };
 
 struct TilePlan {
     TileShape shape;
@@ -570,6 +637,8 @@ TilePlan plan_tile(int64_t M, int64_t N, int64_t K) {
 // tokens for M <= 64), K split when that leaves the CUs short of
 // workgroups.
 TilePlan plan_tile16(int64_t M, int64_t N, int64_t K) {
+    const TilePlan big = make_plan(TileShape::k16_256, 256, 128, M, N, K);
+    if (big.tiles_n * big.tiles_m >= kCUs) return big;
     if (M <= 64) return make_plan(TileShape::k16_64, 128, 64, M, N, K);
     return make_plan(TileShape::k16_128, 128, 128, M, N, K);
 }
@@ -613,7 +682,10 @@ hipError_t launch_w8a16_tile(const void* x, bool x_bf16, const uint8_t* wq, cons
     uint32_t* counters;
     float* partials;
     split_parts(p, workspace, counters, partials);
-    if (p.shape == TileShape::k16_64) {
+    if (p.shape == TileShape::k16_256) {
+        if (x_bf16) launch<Cfg16_256<kTileBf16>>(p, x, nullptr, wq, ws, y, y_dtype, M, N, K, partials, counters, stream);
+        else launch<Cfg16_256<kTileF16>>(p, x, nullptr, wq, ws, y, y_dtype, M, N, K, partials, counters, stream);
+    } else if (p.shape == TileShape::k16_64) {
         if (x_bf16) launch<Cfg16_64<kTileBf16>>(p, x, nullptr, wq, ws, y, y_dtype, M, N, K, partials, counters, stream);
         else launch<Cfg16_64<kTileF16>>(p, x, nullptr, wq, ws, y, y_dtype, M, N, K, partials, counters, stream);
     } else {

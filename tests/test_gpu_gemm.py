@@ -262,6 +262,38 @@ def test_w8a16_tile_one_hot_all_codes_exact(gpu_lib, xdtype):
 
 
 @pytest.mark.parametrize("xdtype", [torch.bfloat16, torch.float16])
+def test_w8a16_tile_large_ragged(gpu_lib, xdtype):
+    """The 256 x 128 W8A16 tile (chosen once it gives 256 tiles) with a ragged
+    last weight tile (N = 4112) and a ragged last token tile (M = 2000)."""
+    M, N, K = 2000, 4112, 1024
+    say("w8a16 tile large", xdtype)
+    x = inputs.activations(M, K, workload=640, stream=1, outliers=True, dtype=xdtype)
+    wq, ws = oracle.quantize_weight_128x128(f32(inputs.weights_bf16(N, K, workload=641)))
+    y0 = oracle.gemm_w8a16_blk128(f32(x), wq, ws)
+    xd, wqd, wsd = x.cuda(), dev(wq), dev(ws)
+    y32 = run_w8a16(xd, wqd, wsd, torch.float32)
+    assert_fp32_bar(y32, y0, "w8a16 tile large")
+    y16 = run_w8a16(xd, wqd, wsd, xdtype)
+    assert_16bit_bar(y16, y32, y0, "bf16" if xdtype == torch.bfloat16 else "f16", "w8a16 tile large")
+
+
+@pytest.mark.parametrize("xdtype", [torch.bfloat16, torch.float16])
+def test_w8a16_tile_large_one_hot_all_codes_exact(gpu_lib, xdtype):
+    """256 x 128 tile path (M = 2048, N = 4096): x one-hot 1.0 gives
+    E4M3(wq[n, k]) * ws exactly, every finite code in every weight tile."""
+    M, N, K = 2048, 4096, 256
+    wq = FINITE_CODES[np.arange(N) % 254][:, None].repeat(K, axis=1).astype(np.uint8)
+    ws = np.where((np.arange(N // 128)[:, None] + np.arange(K // 128)[None, :]) % 2 == 0, 0.5, 4.0).astype(np.float32)
+    for k in (3, 200):
+        say("w8a16 tile large one-hot", xdtype, k)
+        x = torch.zeros((M, K), dtype=xdtype)
+        x[:, k] = 1.0
+        y = run_w8a16(x.cuda(), dev(wq), dev(ws), torch.float32)
+        expect = oracle.e4m3_decode(wq[:, k]) * ws[np.arange(N) // 128, k // 128]
+        np.testing.assert_array_equal(y.cpu().numpy(), np.broadcast_to(expect, (M, N)))
+
+
+@pytest.mark.parametrize("xdtype", [torch.bfloat16, torch.float16])
 def test_w8a16_prefill_oproj_sampled(gpu_lib, xdtype):
     """M = N = K = 4096 W8A16 with 1% outlier channels: full GPU run, 48 rows checked."""
     say("w8a16 prefill", xdtype)
