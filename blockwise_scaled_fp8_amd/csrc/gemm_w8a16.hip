@@ -137,6 +137,7 @@ __global__ __launch_bounds__(kStreamThreads) void w8a16_blk32_stream_kernel(
 // Lanes past the token count read row 0 and are zeroed by a select.
 constexpr int kW8A16LdsMaxM = 16;
 constexpr int kW8A16LdsChunk = 2;
+static_assert(kW8A16LdsChunk == 2, "wait_block counts two blocks per pass");
 
 template <bool kXBf16, int kMp>
 __global__ __launch_bounds__(kStreamThreads) void w8a16_blk128_stream_lds_kernel(
@@ -195,11 +196,12 @@ __global__ __launch_bounds__(kStreamThreads) void w8a16_blk128_stream_lds_kernel
             const int64_t kb = kb0 + c * kStreamWaves;
             if (kb < kb_end) slab_issue(wslab[wave][c], rsrc_w, lane_off_w, K, kb);
         }
-        wait_vmcnt<0>();
+        const bool two = kb0 + kStreamWaves < kb_end;     // wave-uniform
 #pragma unroll
         for (int c = 0; c < kW8A16LdsChunk; ++c) {
             const int64_t kb = kb0 + c * kStreamWaves;
             if (kb < kb_end) {
+                wait_block(c, two);
                 u32x4 wa0, wa1;
                 slab_read(wslab[wave][c], r, g, wa0, wa1);
                 const uint32_t q[8] = {wa0[0], wa0[1], wa0[2], wa0[3], wa1[0], wa1[1], wa1[2], wa1[3]};
@@ -290,11 +292,12 @@ __global__ __launch_bounds__(kStreamThreads) void w8a16_blk32_stream_lds_kernel(
             const int64_t kb = kb0 + c * kStreamWaves;
             if (kb < kb_end) slab_issue(wslab[wave][c], rsrc_w, lane_off_w, K, kb);
         }
-        wait_vmcnt<0>();
+        const bool two = kb0 + kStreamWaves < kb_end;     // wave-uniform
 #pragma unroll
         for (int c = 0; c < kW8A16LdsChunk; ++c) {
             const int64_t kb = kb0 + c * kStreamWaves;
             if (kb < kb_end) {
+                wait_block(c, two);
                 u32x4 wa0, wa1;
                 slab_read(wslab[wave][c], r, g, wa0, wa1);
                 const uint32_t q[8] = {wa0[0], wa0[1], wa0[2], wa0[3], wa1[0], wa1[1], wa1[2], wa1[3]};

@@ -192,6 +192,7 @@ __device__ __forceinline__ void code_rows_issue(uint8_t* rows, i32x4 rsrc_x, int
 }
 
 constexpr int kCodesLdsChunk = 2;
+static_assert(kCodesLdsChunk == 2, "wait_block counts two blocks per pass");
 
 template <int kMp>
 __global__ __launch_bounds__(kStreamThreads) void w8a8_stream_lds_kernel(
@@ -242,11 +243,12 @@ __global__ __launch_bounds__(kStreamThreads) void w8a8_stream_lds_kernel(
             const int64_t kb = kb0 + c * kStreamWaves;
             if (kb < kb_end) slab_issue(wslab[wave][c], rsrc_w, lane_off_w, K, kb);
         }
-        wait_vmcnt<0>();
+        const bool two = kb0 + kStreamWaves < kb_end;     // wave-uniform
 #pragma unroll
         for (int c = 0; c < kCodesLdsChunk; ++c) {
             const int64_t kb = kb0 + c * kStreamWaves;
             if (kb < kb_end) {
+                wait_block(c, two);
                 u32x4 wa0, wa1, b0, b1;
                 slab_read(wslab[wave][c], r, g, wa0, wa1);
                 slab_read(xrows[wave][c], r_row, g, b0, b1);
@@ -430,11 +432,11 @@ __global__ __launch_bounds__(kStreamThreads) void w8a8_stream_quant_kernel(
                 s_r[c] = token_value<kMp>(s, r_row);
             }
         }
-        wait_vmcnt<0>();   // weight slabs in (the weight scales are used only after this)
 #pragma unroll
         for (int c = 0; c < kFusedChunk; ++c) {
             const int64_t kb = kb0 + c * kStreamWaves;
             if (kb < kb_end) {
+                wait_block(c, two);   // this block's weight slabs in (its weight scale is used only after this)
                 u32x4 wa0, wa1;
                 slab_read(wslab[wave][c], r, g, wa0, wa1);
                 const uint8_t* row = xrows[wave][c] + r_row * kXRowStride;

@@ -107,6 +107,16 @@ __device__ __forceinline__ void wait_vmcnt() {
     else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
 }
 
+// A pass of a streaming kernel issues its loads block by block (token rows
+// of both blocks, then the weight slabs of block 0, then those of block 1).
+// Loads complete in issue order, so block 0 is in once at most the two slab
+// loads of block 1 are outstanding: the wave multiplies block 0 while block
+// 1 is still arriving.  `two`: this pass has a block 1 (wave-uniform).
+__device__ __forceinline__ void wait_block(int c, bool two) {
+    if (c == 0 && two) wait_vmcnt<2>();
+    else wait_vmcnt<0>();
+}
+
 __device__ __forceinline__ void store_out(void* y, int y_dtype, int64_t idx, float v) {
     if (y_dtype == 2) {
         static_cast<float*>(y)[idx] = v;
