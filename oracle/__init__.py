@@ -26,6 +26,7 @@ Modules:
   quant   1x128 activation quantiser and 128x128 weight quantiser
   gemm    W8A8 blk128, W8A16 blk128 and W8A16 blk32-UE8M0 products
   ue8m0   load-time validation of power-of-two block scales
+  dequant load-time blockwise dequantisation (the fallback for refused layers)
   compare the tolerance bar used by the parity tests
 
 Every function is pinned by tests in ``tests/test_oracle_*.py`` against facts
@@ -37,6 +38,7 @@ from .e4m3 import e4m3_decode, e4m3_encode, E4M3_MAX, E4M3_NAN_CODES
 from .quant import quantize_act_1x128, quantize_weight_128x128
 from .gemm import gemm_w8a8_blk128, gemm_w8a16_blk128, gemm_w8a16_blk32_ue8m0
 from .ue8m0 import prepare_blk32_ue8m0, Refusal
+from .dequant import dequantize_weight, round_bf16, round_f16
 from .compare import gemm_error, check_gemm_fp32, check_gemm_16bit
 
 __all__ = [
@@ -44,5 +46,6 @@ __all__ = [
     "quantize_act_1x128", "quantize_weight_128x128",
     "gemm_w8a8_blk128", "gemm_w8a16_blk128", "gemm_w8a16_blk32_ue8m0",
     "prepare_blk32_ue8m0", "Refusal",
+    "dequantize_weight", "round_bf16", "round_f16",
     "gemm_error", "check_gemm_fp32", "check_gemm_16bit",
 ]

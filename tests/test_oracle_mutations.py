@@ -95,3 +95,36 @@ def test_blk32_mistake_is_caught(monkeypatch):
     monkeypatch.setattr(pins_gemm, "gemm_w8a16_blk32_ue8m0", _blk32_bias_off_by_one)
     with pytest.raises(AssertionError):
         pins_gemm.test_blk32_exact_rational()
+
+
+def _dequant_transposed_scales(wq, scales, block):
+    # scale of block (kb, nb) instead of (nb, kb): a plausible indexing slip
+    wq = np.asarray(wq, np.uint8)
+    N, K = wq.shape
+    out = np.empty((N, K), np.float32)
+    for n in range(N):
+        for k in range(K):
+            i, j = k // block, n // block
+            s = scales[i, j] if i < scales.shape[0] and j < scales.shape[1] else scales[0, 0]
+            out[n, k] = np.float32(e4m3_decode(wq[n, k])) * s
+    return out
+
+
+def _dequant_rounded_twice(wq, scales, block):
+    # product formed in bf16 arithmetic (rounded operands) instead of one fp32 rounding
+    from oracle import dequantize_weight, round_bf16
+    return round_bf16(dequantize_weight(wq, round_bf16(scales), block))
+
+
+@pytest.mark.parametrize("bad", [_dequant_transposed_scales, _dequant_rounded_twice])
+def test_dequant_mistakes_are_caught(monkeypatch, bad):
+    import tests.test_oracle_dequant as pins_dq
+    monkeypatch.setattr(pins_dq, "dequantize_weight", bad)
+    failures = 0
+    for pin in (lambda: pins_dq.test_block_map(32, 96, 160), lambda: pins_dq.test_block_map(128, 200, 264),
+                pins_dq.test_single_fp32_rounding, pins_dq.test_round_trip_of_the_weight_quantiser):
+        try:
+            pin()
+        except AssertionError:
+            failures += 1
+    assert failures >= 1
