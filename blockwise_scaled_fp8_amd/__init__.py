@@ -12,7 +12,8 @@ from ._lib import (  # noqa: F401
     BFP8_BF16, BFP8_F16, BFP8_F32, Bfp8Error, LIB_PATH, SIGNATURES, STATUS_NAMES,
     OP_QUANT_ACT_1X128, OP_QUANT_WEIGHT_128X128, OP_GEMM_W8A8_BLK128, OP_GEMM_W8A16_BLK128,
     OP_GEMM_W8A16_BLK32_UE8M0, OP_QUANT_GEMM_W8A8_BLK128,
-    load, bfp8_quantize_act_1x128, bfp8_quantize_weight_128x128, bfp8_gemm_w8a8_blk128, bfp8_quant_gemm_w8a8_blk128,
+    load, bfp8_quantize_act_1x128, bfp8_quantize_weight_128x128, bfp8_dequantize_weight,
+    bfp8_gemm_w8a8_blk128, bfp8_quant_gemm_w8a8_blk128,
     bfp8_gemm_w8a16_blk128, bfp8_gemm_w8a16_blk32_ue8m0, bfp8_prepare_blk32_ue8m0,
     bfp8_workspace_bytes, bfp8_get_limits, bfp8_status_string,
 )
@@ -42,6 +43,14 @@ def quantize_weight(w):
     ws = torch.empty(((N + 127) // 128, (K + 127) // 128), dtype=torch.float32, device=w.device)
     bfp8_quantize_weight_128x128(w, wq, ws)
     return wq, ws
+
+
+def dequantize_weight(wq, scales, block, out_dtype=torch.bfloat16):
+    """wq [N, K] E4M3 codes with fp32 block scales (block 32 or 128) ->
+    weights [N, K] in out_dtype (load-time fallback; see include/bfp8.h)."""
+    w = torch.empty(wq.shape, dtype=out_dtype, device=wq.device)
+    bfp8_dequantize_weight(wq, scales, block, w)
+    return w
 
 
 def gemm_w8a8(xq, xs, wq, ws, out_dtype=torch.bfloat16, workspace=None):

@@ -35,6 +35,7 @@ _P, _I, _I64, _SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size
 SIGNATURES = {
     "bfp8_quantize_act_1x128": (_I, [_P, _I, _I64, _I64, _P, _P, _P]),
     "bfp8_quantize_weight_128x128": (_I, [_P, _I, _I64, _I64, _P, _P, _P]),
+    "bfp8_dequantize_weight": (_I, [_P, _P, _I64, _P, _I, _I64, _I64, _P]),
     "bfp8_gemm_w8a8_blk128": (_I, [_P, _P, _P, _P, _P, _I, _I64, _I64, _I64, _P, _SZ, _P]),
     "bfp8_quant_gemm_w8a8_blk128": (_I, [_P, _I, _P, _P, _P, _I, _I64, _I64, _I64, _P, _SZ, _P]),
     "bfp8_gemm_w8a16_blk128": (_I, [_P, _I, _P, _P, _P, _I, _I64, _I64, _I64, _P, _SZ, _P]),
@@ -103,6 +104,12 @@ def bfp8_quantize_weight_128x128(w, wq, ws):
     N, K = w.shape
     _check(load().bfp8_quantize_weight_128x128(_ptr(w), _dtype_code(w), N, K, _ptr(wq), _ptr(ws), _stream()),
            "bfp8_quantize_weight_128x128")
+
+
+def bfp8_dequantize_weight(wq, scales, block, w):
+    N, K = wq.shape
+    _check(load().bfp8_dequantize_weight(_ptr(wq), _ptr(scales), block, _ptr(w), _dtype_code(w), N, K, _stream()),
+           "bfp8_dequantize_weight")
 
 
 def bfp8_gemm_w8a8_blk128(xq, xs, wq, ws, y, workspace=None):

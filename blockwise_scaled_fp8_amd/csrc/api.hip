@@ -62,6 +62,17 @@ bfp8_status bfp8_quantize_weight_128x128(const void* w, int w_dtype, int64_t N, 
     return launched(launch_quant_weight_128x128(w, w_dtype == BFP8_BF16, N, K, wq, ws, as_stream(stream)));
 }
 
+bfp8_status bfp8_dequantize_weight(const uint8_t* wq, const float* scales, int64_t block, void* w, int w_dtype,
+                                   int64_t N, int64_t K, void* stream) {
+    if (!wq || !scales || !w) return BFP8_E_NULL;
+    if (block != 32 && block != 128) return BFP8_E_SHAPE;
+    if (!dim_ok(N, 1) || !dim_ok(K, 8) || K % 8 != 0 || N * K >= ((int64_t)1 << 40)) return BFP8_E_SHAPE;
+    if (N * ((K + 2047) / 2048) >= kMaxDim) return BFP8_E_SHAPE;   // one workgroup per row and 2048 columns
+    if (!is_out(w_dtype)) return BFP8_E_DTYPE;
+    if (!aligned(wq) || !aligned(scales) || !aligned(w)) return BFP8_E_ALIGN;
+    return launched(launch_dequant_weight(wq, scales, (int)block, w, w_dtype, N, K, as_stream(stream)));
+}
+
 }  // extern "C"
 
 namespace {

@@ -50,6 +50,8 @@ hipError_t launch_quant_act_1x128(const void* x, bool bf16, int64_t M, int64_t K
                                   uint8_t* xq, float* xs, hipStream_t stream);
 hipError_t launch_quant_weight_128x128(const void* w, bool bf16, int64_t N, int64_t K,
                                        uint8_t* wq, float* ws, hipStream_t stream);
+hipError_t launch_dequant_weight(const uint8_t* wq, const float* scales, int block, void* w, int w_dtype,
+                                 int64_t N, int64_t K, hipStream_t stream);
 
 hipError_t launch_w8a8_tile(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
                             void* y, int y_dtype, int64_t M, int64_t N, int64_t K, void* workspace,

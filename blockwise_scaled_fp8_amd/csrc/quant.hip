@@ -93,6 +93,54 @@ __global__ __launch_bounds__(kQuantWThreads) void quant_weight_128x128_kernel(
     if (t == 0) ws[nb * KB + kb] = s;
 }
 
+// Load-time blockwise dequantisation: w = RN_out(fl32(E4M3(q) * s)) with one
+// fp32 scale per B x B block (B = 32 or 128), the fallback for layers whose
+// 32x32 scales the block-32 packer refuses ([SM70] "Exactness").  One thread
+// per 8 consecutive weights of a row (one 8-byte code load, one 16-byte
+// store for 16-bit outputs, two for fp32); the 8 share one block scale since
+// B is a multiple of 8.  The E4M3 decode is gfx950's fp8 -> fp32 conversion
+// (exact: every finite E4M3 value is an fp32 value; NaN codes give NaN).
+constexpr int kDequantThreads = 256;
+
+__global__ __launch_bounds__(kDequantThreads) void dequant_weight_kernel(
+    const uint8_t* __restrict__ wq, const float* __restrict__ scales, int block, void* __restrict__ w,
+    int w_dtype, int64_t N, int64_t K, int64_t blocks_per_row) {
+    const uint32_t n32 = (uint32_t)blockIdx.x / (uint32_t)blocks_per_row;   // uniform per workgroup
+    const int64_t n = n32;
+    const int64_t k = ((int64_t)((uint32_t)blockIdx.x - n32 * (uint32_t)blocks_per_row) * kDequantThreads +
+                       threadIdx.x) * 8;
+    if (k >= K) return;
+    const int64_t KBs = (K + block - 1) / block;
+    const float s = scales[(n / block) * KBs + k / block];
+    const uint2 q = *reinterpret_cast<const uint2*>(wq + n * K + k);
+    // The conversion's byte select is an immediate.
+    const float p[8] = {__builtin_amdgcn_cvt_f32_fp8((int)q.x, 0) * s, __builtin_amdgcn_cvt_f32_fp8((int)q.x, 1) * s,
+                        __builtin_amdgcn_cvt_f32_fp8((int)q.x, 2) * s, __builtin_amdgcn_cvt_f32_fp8((int)q.x, 3) * s,
+                        __builtin_amdgcn_cvt_f32_fp8((int)q.y, 0) * s, __builtin_amdgcn_cvt_f32_fp8((int)q.y, 1) * s,
+                        __builtin_amdgcn_cvt_f32_fp8((int)q.y, 2) * s, __builtin_amdgcn_cvt_f32_fp8((int)q.y, 3) * s};
+    const int64_t idx = n * K + k;
+    if (w_dtype == 2) {
+        float* out = static_cast<float*>(w) + idx;
+        *reinterpret_cast<f32x4*>(out) = f32x4{p[0], p[1], p[2], p[3]};
+        *reinterpret_cast<f32x4*>(out + 4) = f32x4{p[4], p[5], p[6], p[7]};
+    } else {
+        uint32_t h[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) h[i] = w_dtype == 0 ? float_to_bf16_bits(p[i]) : float_to_f16_bits(p[i]);
+        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(w) + idx) =
+            u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+    }
+}
+
+hipError_t launch_dequant_weight(const uint8_t* wq, const float* scales, int block, void* w, int w_dtype,
+                                 int64_t N, int64_t K, hipStream_t stream) {
+    const int64_t blocks_per_row = (K / 8 + kDequantThreads - 1) / kDequantThreads;
+    if (N * blocks_per_row >= (int64_t(1) << 32)) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(dequant_weight_kernel, dim3((unsigned)(N * blocks_per_row)), dim3(kDequantThreads), 0, stream,
+                       wq, scales, block, w, w_dtype, N, K, blocks_per_row);
+    return hipGetLastError();
+}
+
 hipError_t launch_quant_act_1x128(const void* x, bool bf16, int64_t M, int64_t K,
                                   uint8_t* xq, float* xs, hipStream_t stream) {
     const int64_t G = (K + 127) / 128;

@@ -104,6 +104,29 @@ bfp8_status bfp8_quantize_weight_128x128(const void* w, int w_dtype, int64_t N, 
                                          uint8_t* wq, float* ws, void* stream);
 
 /*
+ * Blockwise weight dequantisation at load time: the fallback for a layer
+ * whose 32x32 scales bfp8_prepare_blk32_ue8m0 refuses ([SM70] "Exactness":
+ * only power-of-two scales in [2^-14, 2^7] keep the block-32 weights exact in
+ * fp16; other layers are dequantised once when loaded).  Per-step
+ * dequantisation is what the pages warn against ([ARC] "Route-2 handover"),
+ * so this is meant for load time: dequantise, then requantise the result with
+ * bfp8_quantize_weight_128x128 and run the blk128 GEMMs on it.
+ *   wq      [N, K] E4M3 codes, device.
+ *   scales  [ceil(N/block), ceil(K/block)] fp32, row-major, device (any
+ *           values; no window or power-of-two rule applies here).
+ *   block   32 or 128.
+ *   w       [N, K] in w_dtype (BFP8_BF16, BFP8_F16 or BFP8_F32), device, written.
+ * w[n, k] = RN(fl32(E4M3(wq[n, k]) * scales[n / block, k / block])): the fp32
+ * product rounded to nearest even to w_dtype (fp32 output is the product).
+ * NaN codes (0x7F, 0xFF) give NaN.  Requires N >= 1, K >= 8, K % 8 == 0 (edge
+ * blocks may be ragged); pointers 16-byte aligned.  Asynchronous on `stream`;
+ * errors: BFP8_E_NULL, BFP8_E_SHAPE (including a block other than 32 or 128),
+ * BFP8_E_DTYPE, BFP8_E_ALIGN, BFP8_E_LAUNCH.
+ */
+bfp8_status bfp8_dequantize_weight(const uint8_t* wq, const float* scales, int64_t block, void* w, int w_dtype,
+                                   int64_t N, int64_t K, void* stream);
+
+/*
  * W8A8 blockwise GEMM ([ADA] "The starting point" and "The fix"; [ARC]
  * "What this adds"):
  *   for each 128-wide K block kb:

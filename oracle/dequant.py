@@ -55,5 +55,7 @@ def round_bf16(x):
 
 
 def round_f16(x):
-    """Nearest-even fp16 value of each fp32 value (numpy's IEEE conversion)."""
-    return np.asarray(x, dtype=np.float32).astype(np.float16)
+    """Nearest-even fp16 value of each fp32 value (numpy's IEEE conversion;
+    magnitudes past the fp16 range become infinities)."""
+    with np.errstate(over="ignore"):
+        return np.asarray(x, dtype=np.float32).astype(np.float16)

@@ -41,7 +41,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared()
-    assert len(names) == 10
+    assert len(names) == 11
     assert sorted(_lib.SIGNATURES) == names
     nm = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], stdout=subprocess.PIPE, text=True).stdout
     exported = set(re.findall(r" T (bfp8_\w+)", nm))
@@ -128,6 +128,20 @@ def test_quantize_act_validation(lib, args, expect):
 ])
 def test_quantize_weight_validation(lib, args, expect):
     assert lib.bfp8_quantize_weight_128x128(*args) == expect
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((0, B, 32, C, 0, 64, 64, None), 1),             # null codes
+    ((A, 0, 32, C, 0, 64, 64, None), 1),             # null scales
+    ((A, B, 32, 0, 0, 64, 64, None), 1),             # null output
+    ((A, B, 64, C, 0, 64, 64, None), 2),             # block other than 32 or 128
+    ((A, B, 32, C, 0, 0, 64, None), 2),              # N = 0
+    ((A, B, 128, C, 0, 64, 12, None), 2),            # K % 8
+    ((A, B, 32, C, 7, 64, 64, None), 3),             # output dtype
+    ((A, B, 32, MISALIGNED, 1, 64, 64, None), 4),    # misaligned output
+])
+def test_dequantize_weight_validation(lib, args, expect):
+    assert lib.bfp8_dequantize_weight(*args) == expect
 
 
 def _w8a8(M=4, N=512, K=512, y_dtype=0, xq=A, ws_ptr=C, y=Y, workspace=None, wbytes=0):

@@ -132,3 +132,67 @@ def test_quant_deterministic(gpu_lib):
     b = bfp8.quantize_act(x)
     torch.cuda.synchronize()
     assert torch.equal(a[0], b[0]) and torch.equal(a[1].view(torch.int32), b[1].view(torch.int32))
+
+
+# ------------------------------------------------- load-time dequantisation ----
+
+def _dq_case(wq, scales, block, what):
+    wq_d, s_d = torch.from_numpy(wq).cuda(), torch.from_numpy(scales).cuda()
+    p = oracle.dequantize_weight(wq, scales, block)
+    expect = {torch.float32: p, torch.bfloat16: oracle.round_bf16(p), torch.float16: oracle.round_f16(p)}
+    for dt, ref in expect.items():
+        say("dequant", what, block, dt)
+        got = bfp8.dequantize_weight(wq_d, s_d, block, dt).float().cpu().numpy()
+        ref = np.asarray(ref, np.float32)
+        nan = np.isnan(ref)
+        np.testing.assert_array_equal(np.isnan(got), nan, err_msg=f"{what} {dt} NaN positions")
+        np.testing.assert_array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32), err_msg=f"{what} {dt}")
+
+
+@pytest.mark.parametrize("block,N,K", [(32, 96, 160), (128, 200, 264), (32, 64, 8), (128, 130, 1000)])
+def test_dequantize_weight_bit_exact(gpu_lib, block, N, K):
+    """Every code (NaN codes included), scales of every magnitude and
+    significand (powers of two in and out of the [SM70] window, values with
+    full 24-bit significands), ragged edge blocks; outputs overflowing fp16
+    included."""
+    rng = np.random.default_rng(block * 1000 + N + K)
+    wq = rng.integers(0, 256, size=(N, K), dtype=np.uint8)
+    wq[0, :min(K, 256)] = np.arange(min(K, 256), dtype=np.uint8)
+    nb, kb = -(-N // block), -(-K // block)
+    scales = (np.exp2(rng.uniform(-40, 12, size=(nb, kb))) * rng.uniform(1, 2, size=(nb, kb))).astype(np.float32)
+    scales.flat[0] = 2.0 ** -20          # a power of two below the window
+    _dq_case(wq, scales, block, f"N={N} K={K}")
+
+
+def test_dequantize_weight_block32_workload_shape(gpu_lib):
+    """The block-32 layer shape, N = 4096, K = 7168, with scales that are not
+    powers of two (the layers the packer refuses)."""
+    rng = np.random.default_rng(3)
+    wq = inputs.block32_codes(4096, 7168, workload=3).numpy()
+    scales = (np.exp2(rng.integers(-14, 8, size=(128, 224))) * rng.uniform(1, 2, size=(128, 224))).astype(np.float32)
+    _dq_case(wq, scales, 32, "block-32 layer")
+
+
+def test_refused_layer_falls_back_to_blk128(gpu_lib):
+    """A block-32 layer with a scale outside the window: the packer refuses it;
+    dequantised to bf16 and requantised to 128x128 tiles on the GPU it matches
+    the oracle's same chain bit for bit, and the W8A16 blk128 GEMM on it meets
+    the bar against the oracle."""
+    N, K, M = 512, 1024, 4
+    wq = inputs.block32_codes(N, K, workload=31).numpy()
+    s = inputs.block32_scales(N, K, workload=31).numpy()
+    s[3, 5] = 2.0 ** 9                                          # outside [2^-14, 2^7]
+    st, e8, bad = bfp8.bfp8_prepare_blk32_ue8m0(torch.from_numpy(wq), torch.from_numpy(s))
+    assert (st, e8, bad) == (8, None, 3 * (K // 32) + 5)        # BFP8_E_SCALE_WINDOW at scale [3, 5]
+    say("fallback: dequant + requant")
+    w_bf16 = bfp8.dequantize_weight(torch.from_numpy(wq).cuda(), torch.from_numpy(s).cuda(), 32, torch.bfloat16)
+    wq2, ws2 = bfp8.quantize_weight(w_bf16)
+    ref_w = oracle.round_bf16(oracle.dequantize_weight(wq, s, 32))
+    ref_q, ref_s = oracle.quantize_weight_128x128(ref_w)
+    np.testing.assert_array_equal(wq2.cpu().numpy(), ref_q)
+    np.testing.assert_array_equal(ws2.cpu().numpy().view(np.uint32), ref_s.view(np.uint32))
+    x = inputs.activations(M, K, workload=31, dtype=torch.bfloat16)
+    y = bfp8.gemm_w8a16(x.cuda(), wq2, ws2, out_dtype=torch.float32)
+    y0 = oracle.gemm_w8a16_blk128(f32(x), ref_q, ref_s)
+    ok, err = oracle.check_gemm_fp32(y.cpu().numpy(), y0)
+    assert ok, err
