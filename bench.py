@@ -27,7 +27,10 @@ of each), with one HIP event pair per kernel on the stream the kernels run
 on; per-kernel durations are those phase times over K.  The roofline object
 reports the dominant kernel's algorithmic bytes (or FLOPs) per launch over
 its average duration.  The cpu_baseline object times the CPU oracle on a
-bounded sample of the same workload.
+bounded sample of the same workload.  For decode, timing.graph also gives
+the time per step of one rotation cycle of steps captured as a HIP graph and
+replayed (kernels in step order, gaps included, no host launch cost;
+--no-graph skips it).
 
 Prints exactly one JSON line on stdout.
 """
@@ -57,6 +60,7 @@ def parse():
     p.add_argument("--copies", type=int, default=32, help="distinct weight copies rotated per call")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-graph", action="store_true", help="decode: skip the HIP graph replay timing")
     p.add_argument("--unfused", action="store_true",
                    help="decode: separate quantiser + W8A8 GEMM instead of the fused call")
     p.add_argument("--copy-probe", action="store_true",
@@ -204,6 +208,34 @@ def cpu_baseline(fn, seconds, unit_per_call, unit, sample):
 
 
 # --------------------------------------------------------------- workloads ----
+def graph_timing(torch, phases, steps_per_graph, replays):
+    """One rotation cycle of decode steps (every phase of every step, in step
+    order) captured as a HIP graph and replayed: the wall-clock time per step
+    including the gaps between kernels, with no host launch cost."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(2):
+            for _, fn in phases:
+                fn(i)
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(steps_per_graph):
+            for _, fn in phases:
+                fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(replays):
+        g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) * 1e3 / (replays * steps_per_graph)
+    return {"us_per_step": us, "steps_per_replay": steps_per_graph, "replays": replays}
+
+
 def bench_decode(torch, bfp8, inputs, args):
     M = args.m or 1
     N = K = 4096
@@ -260,6 +292,9 @@ def bench_decode(torch, bfp8, inputs, args):
                          "M": M, "N": N, "K": K, "weight_copies": C, "out_dtype": "bf16",
                          "step_alg_bytes": step_bytes},
               "roofline": roof, "kernels": kern, "wall_s": wall, "timing": timing}
+
+    if not args.no_graph:
+        result["timing"]["graph"] = graph_timing(torch, phases, C, max(1, args.steps // C))
 
     if not args.no_cpu_baseline:
         import oracle

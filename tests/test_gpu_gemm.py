@@ -210,6 +210,19 @@ def test_w8a16_blk128(gpu_lib, M, xdtype):
     assert_16bit_bar(y16, y32, y0, "bf16" if xdtype == torch.bfloat16 else "f16", f"w8a16 M={M}")
 
 
+@pytest.mark.parametrize("M", [1, 3, 16])
+def test_w8a16_blk128_long_k(gpu_lib, M):
+    """K = 12288 on 4096 rows: six 128-K blocks per wave, two passes of up to
+    four blocks with the cross-wave sum in the slab memory."""
+    N, K = 4096, 12288
+    say("w8a16 long K", M)
+    x = inputs.activations(M, K, workload=650 + M, dtype=torch.bfloat16)
+    wq, ws = oracle.quantize_weight_128x128(f32(inputs.weights_bf16(N, K, workload=651)))
+    y0 = oracle.gemm_w8a16_blk128(f32(x), wq, ws)
+    y32 = run_w8a16(x.cuda(), dev(wq), dev(ws), torch.float32)
+    assert_fp32_bar(y32, y0, f"w8a16 long K M={M}")
+
+
 @pytest.mark.parametrize("xdtype", [torch.bfloat16, torch.float16])
 def test_w8a16_blk128_one_hot_all_codes_exact(gpu_lib, xdtype):
     """x one-hot 1.0: Y[:, n] = E4M3(wq[n, k]) * ws exactly, subnormal codes included."""
