@@ -61,6 +61,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-graph", action="store_true", help="decode: skip the HIP graph replay timing")
+    p.add_argument("--smi", action="store_true",
+                   help="record rocm-smi power and clock readings before and after the run in device.smi")
     p.add_argument("--unfused", action="store_true",
                    help="decode: separate quantiser + W8A8 GEMM instead of the fused call")
     p.add_argument("--copy-probe", action="store_true",
@@ -152,16 +154,43 @@ def run_steps(torch, phases, steps, warmup):
     (all `steps` launches of the first kernel, then of the second, ...), which
     is the same work in an order that keeps every data dependency (each phase
     only reads what earlier phases wrote), with one event pair per phase on
-    the launch stream.  A spin kernel queued right before the timed region
-    keeps the GPU busy while the host enqueues every timed launch, so the
-    events see back-to-back GPU execution, not host launch latency.  Returns
-    ms per step and per-kernel average microseconds per launch."""
+    the launch stream.  When the host enqueues a step faster than the GPU runs
+    it, a second round of warmup steps is queued right before the timed ones
+    (the GPU stays busy from the warmup into the timed region, at the clock the
+    warmup reached); otherwise a spin kernel queued right before the timed
+    region keeps the GPU busy while the host enqueues every timed launch, so
+    the events see back-to-back GPU execution, not host launch latency.
+    Returns ms per step and per-kernel average microseconds per launch."""
     t0 = time.perf_counter()
     for i in range(warmup):
         for _, launch in phases:
             launch(i)
+    t_host = time.perf_counter() - t0
     torch.cuda.synchronize()
     host_per_step = (time.perf_counter() - t0) / max(warmup, 1)
+    enqueue_per_step = t_host / max(warmup, 1)
+    # GPU-bound steps (the host enqueues a step in well under the GPU's time
+    # for it): the warmup runs straight into the timed region with no idle
+    # gap, so the timed steps start at the clock the warmup reached.
+    if warmup >= 10 and enqueue_per_step < 0.5 * host_per_step:
+        for i in range(warmup):
+            for _, launch in phases:
+                launch(i)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)]
+        t_enq = time.perf_counter()
+        ev[0].record()
+        for p, (_, launch) in enumerate(phases):
+            for s in range(steps):
+                launch(warmup + s)
+            ev[p + 1].record()
+        enqueue_ms = (time.perf_counter() - t_enq) * 1e3
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t_enq
+        kern = {name: {"avg_us": 1e3 * ev[p].elapsed_time(ev[p + 1]) / steps} for p, (name, _) in enumerate(phases)}
+        return ev[0].elapsed_time(ev[-1]) / steps, wall, kern, {
+            "head_start_ms": 0.0, "host_enqueue_ms": enqueue_ms, "gpu_ahead": True,
+            "method": "per-kernel phases of back-to-back launches, HIP events; GPU-bound, so the warmup runs "
+                      "straight into the timed region (no idle gap)"}
     cyc_per_ms = _sleep_cycles_per_ms(torch)
     head_ms = 1.5 * host_per_step * steps * 1e3 + 5.0
     for attempt in range(3):
@@ -482,11 +511,28 @@ def bench_sweep(torch, bfp8, inputs, args):
             "kernels": {"points": points}, "timing": {"method": "per-kernel phases of back-to-back launches, HIP events"}}
 
 
+def smi_sample():
+    """Power and clock readings of the GPU from rocm-smi (a child process), or
+    the reason there are none."""
+    import subprocess
+    try:
+        p = subprocess.run(["rocm-smi", "--showpower", "--showclocks", "--json"], stdout=subprocess.PIPE,
+                           stderr=subprocess.PIPE, text=True, timeout=30)
+        data = json.loads(p.stdout)
+    except Exception as e:   # tool missing, refused or unparsable: say so instead
+        return {"error": f"{type(e).__name__}: {e}"[:200]}
+    out = {}
+    for card, vals in data.items():
+        if isinstance(vals, dict):
+            out[card] = {k: v for k, v in vals.items() if any(w in k.lower() for w in ("power", "clk", "clock"))}
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the path has no multi-GPU form in this build)", file=sys.stderr)
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported "
+              "(the library has no multi-GPU path)", file=sys.stderr)
         sys.exit(2)
     import torch
     import blockwise_scaled_fp8_amd as bfp8
@@ -497,12 +543,18 @@ def main():
         copy_probe(torch)
     fn = {"decode": bench_decode, "prefill": bench_prefill, "blk32": bench_blk32, "w8a16": bench_w8a16,
           "sweep": bench_sweep}[args.workload]
+    smi_before = smi_sample() if args.smi else None
     r = fn(torch, bfp8, inputs, args)
+    device = {"name": torch.cuda.get_device_name(0),
+              "arch": getattr(torch.cuda.get_device_properties(0), "gcnArchName", ""),
+              "compute_units": torch.cuda.get_device_properties(0).multi_processor_count}
+    if args.smi:
+        device["smi"] = {"before": smi_before, "after": smi_sample()}
     line = {"metric": METRIC, "value": r["value"], "unit": r["unit"], "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": r["ms_per_step"], "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": r["dtype"], "data": "synthetic", "config": r["config"],
             "roofline": r["roofline"], "cpu_baseline": r.get("cpu_baseline"), "kernels": r["kernels"],
-            "timing": r["timing"], "device": torch.cuda.get_device_name(0)}
+            "timing": r["timing"], "device": device}
     print(json.dumps(line), flush=True)
 
 
