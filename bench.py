@@ -487,7 +487,7 @@ def bench_sweep(torch, bfp8, inputs, args):
 
             phases = [("quant_act_1x128", lambda i, x=x, xq=xq, xs=xs: bfp8.bfp8_quantize_act_1x128(x, xq, xs)),
                       ("gemm_w8a8_blk128", gemm)]
-            ms, wall, kern, timing = run_steps(torch, phases, steps, 3)
+            ms, wall, kern, timing = run_steps(torch, phases, steps, max(3, args.warmup))
             g_us = kern["gemm_w8a8_blk128"]["avg_us"]
             nbytes, flops = bytes_w8a8(M, N, K), 2.0 * M * N * K
             roof_us = max(nbytes / (HBM_PEAK_GBS * 1e3), flops / (FP8_PEAK_TFLOPS * 1e6))
