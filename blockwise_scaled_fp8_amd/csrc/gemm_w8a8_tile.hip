@@ -25,10 +25,10 @@
 // (lanes 16g..16g+15) takes chunks g and g + 4 of the row, the same for both
 // operands, so the contraction is over the same 128 K values.
 //
-// Tile shapes ([ADA] "One tile doesn't fit all M"): the largest of 256x256
-// and 128x128 that still gives at least one workgroup per CU; below that,
-// 64x128 (or 128x64 for M <= 64) with K split over several workgroups so
-// that about one workgroup per CU exists.  Split partial tiles go to the
+// Tile shapes ([ADA] "One tile doesn't fit all M"): 256x256, 256x128 or
+// 128x128 by estimated time (plan_tile) among those that occupy most CUs;
+// below that, 64x128 (or 128x64 for M <= 64) with K split over several
+// workgroups so that about one workgroup per CU exists.  Split partial tiles go to the
 // workspace in fp32 and the last workgroup of a tile sums them in split
 // order (no float atomics, identical from run to run), with the same
 // fence-free hand-off as the streaming kernels.
@@ -105,6 +105,7 @@ struct TileCfg {
 // wait at the top of the next block (3% at M = N = K = 4096, random data).
 using Cfg256 = TileCfg<256, 256, 2, 4, false, kTileCodes, 4>;    // wave tile 128 n x 64 m, 2 stages
 using Cfg128 = TileCfg<128, 128, 2, 4, false>;    // 64 x 32, 4 stages
+using Cfg256x128 = TileCfg<256, 128, 4, 2, false>;   // 64 x 64, 3 stages
 using Cfg64x128 = TileCfg<64, 128, 2, 4, true>;   // 32 x 32, 6 stages
 using Cfg128x64 = TileCfg<128, 64, 4, 2, true>;   // 32 x 32, 6 stages
 // W8A16 (16-bit activations): wave tiles 32 x 64 and 32 x 32 (four waves
@@ -604,7 +605,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void w8a8_tile_kernel(
 
 namespace {
 
-enum class TileShape { k256, k128, k64x128, k128x64, k16_256, k16_128, k16_64 };
+enum class TileShape { k256, k256x128, k128, k64x128, k128x64, k16_256, k16_128, k16_64 };
 
 struct TilePlan {
     TileShape shape;
@@ -624,11 +625,28 @@ TilePlan make_plan(TileShape s, int64_t bn, int64_t bm, int64_t M, int64_t N, in
     return p;
 }
 
+// Large tiles: the shape with the least estimated time among those that
+// occupy at least three quarters of the CUs, time = rounds of kCUs tiles x
+// the time of one tile.  Relative tile times at N = K = 4096 (measured):
+// 256x256 1, 256x128 0.64, 128x128 0.4 (the larger tiles read fewer bytes
+// per MFMA from L2 and LDS).  Below that, the split-K shapes.
 TilePlan plan_tile(int64_t M, int64_t N, int64_t K) {
-    const TilePlan big = make_plan(TileShape::k256, 256, 256, M, N, K);
-    if (big.tiles_n * big.tiles_m >= kCUs) return big;
-    const TilePlan mid = make_plan(TileShape::k128, 128, 128, M, N, K);
-    if (mid.tiles_n * mid.tiles_m >= kCUs) return mid;
+    const TilePlan cand[3] = {make_plan(TileShape::k256, 256, 256, M, N, K),
+                              make_plan(TileShape::k256x128, 256, 128, M, N, K),
+                              make_plan(TileShape::k128, 128, 128, M, N, K)};
+    constexpr double kTileTime[3] = {1.0, 0.64, 0.4};
+    int best = -1;
+    double best_cost = 0.0;
+    for (int c = 0; c < 3; ++c) {
+        const int64_t tiles = cand[c].tiles_n * cand[c].tiles_m;
+        if (4 * tiles < 3 * kCUs) continue;
+        const double cost = (double)((tiles + kCUs - 1) / kCUs) * kTileTime[c];
+        if (best < 0 || cost < best_cost) {
+            best = c;
+            best_cost = cost;
+        }
+    }
+    if (best >= 0) return cand[best];
     if (M <= 64) return make_plan(TileShape::k128x64, 128, 64, M, N, K);
     return make_plan(TileShape::k64x128, 64, 128, M, N, K);
 }
@@ -705,6 +723,9 @@ hipError_t launch_w8a8_tile(const uint8_t* xq, const float* xs, const uint8_t* w
     switch (p.shape) {
         case TileShape::k256:
             launch<Cfg256>(p, xq, xs, wq, ws, y, y_dtype, M, N, K, partials, counters, stream);
+            break;
+        case TileShape::k256x128:
+            launch<Cfg256x128>(p, xq, xs, wq, ws, y, y_dtype, M, N, K, partials, counters, stream);
             break;
         case TileShape::k128:
             launch<Cfg128>(p, xq, xs, wq, ws, y, y_dtype, M, N, K, partials, counters, stream);
