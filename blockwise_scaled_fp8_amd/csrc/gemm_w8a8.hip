@@ -67,26 +67,30 @@ size_t stream_workspace_bytes(const StreamPlan& p) {
 // the same for both MFMA operands.  The waves take interleaved 128-K blocks,
 // so at any time a workgroup reads adjacent blocks of its rows.
 //
-// Every load of a chunk is issued before anything waits on one: token rows
-// and scales first (L2), then the weights (HBM).  Token rows past M are read
-// from row 0 (a valid address) and zeroed by a select afterwards, so no
-// load sits in a lane-divergent branch; such branches made the compiler wait
-// for each block's token loads before issuing the next block's, serialising
-// four L2 round trips ahead of the weight stream (measured 0.7 us).
-//
-// One or two 16-token tiles per workgroup (kMT): with two, the weights are
-// read once for 32 tokens, each wave issuing two MFMAs per block on the same
-// weight fragment, and two blocks per wave (not four) are kept in flight so
-// the registers stay within 128 at sixteen waves.
-template <int kMT>
-__global__ __launch_bounds__(kStreamThreads) void w8a8_stream_kernel(
+// 16 < M <= 32 on projections small enough that one pass over the weights
+// for 32 tokens beats the tiled kernels (w8a8_streams): two 16-token tiles
+// per workgroup, each wave issuing two MFMAs per block on the same weight
+// fragment.  The weights come through per-wave LDS slabs as whole 128-byte
+// lines; the token codes stay register loads (every lane carries a live
+// token row of one of the tiles).  Every load of a pass is issued before
+// anything waits on one: token rows and scales first (L2), then the weight
+// slabs.  Token rows past M are read from row 0 (a valid address) and zeroed
+// by a select afterwards, so no load sits in a lane-divergent branch; such
+// branches made the compiler wait for each block's token loads before
+// issuing the next block's, serialising four L2 round trips ahead of the
+// weight stream (measured 0.7 us).
+constexpr int kStream2Chunk = 2;
+static_assert(kStream2Chunk == 2, "wait_block counts two blocks per pass");
+
+__global__ __launch_bounds__(kStreamThreads) void w8a8_stream2_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ xs,
     const uint8_t* __restrict__ wq, const float* __restrict__ ws,
     void* __restrict__ y, int y_dtype, int64_t M, int64_t N, int64_t K,
     int64_t n_tiles, int64_t splits, int64_t kb_per_split,
     float* __restrict__ partials, uint32_t* __restrict__ counters) {
-    constexpr int kChunk = kMT == 1 ? 4 : 2;      // 128-K blocks per wave with loads in flight together
+    constexpr int kMT = 2, kChunk = kStream2Chunk;
     __shared__ float red[kStreamWaves * 256];
+    __shared__ __attribute__((aligned(1024))) uint8_t wslab[kStreamWaves][kChunk][kSlabBytes];
     const int64_t nt = blockIdx.x, split = blockIdx.y, mt0 = blockIdx.z * kMT;
     const int64_t KB = K / 128;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
@@ -95,7 +99,8 @@ __global__ __launch_bounds__(kStreamThreads) void w8a8_stream_kernel(
     const int64_t kb_begin = split * kb_per_split;
     const int64_t kb_end = kb_begin + kb_per_split < KB ? kb_begin + kb_per_split : KB;
 
-    const uint8_t* wrow = wq + (nt * 16 + r) * K + g * 16;
+    const i32x4 rsrc_w = buffer_rsrc(wq + nt * 16 * K, (uint32_t)(16 * K));
+    const int lane_off_w = slab_lane_offset(lane, K);
     const float* ws_row = ws + (nt * 16 / 128) * KB;
     bool m_ok[kMT];
     const uint8_t* xrow[kMT];
@@ -114,7 +119,7 @@ __global__ __launch_bounds__(kStreamThreads) void w8a8_stream_kernel(
     const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
     const u32x4 zero4 = {0u, 0u, 0u, 0u};
     for (int64_t kb0 = kb_begin + wave; kb0 < kb_end; kb0 += kStreamWaves * kChunk) {
-        u32x4 wa[kChunk][2], xb[kChunk][kMT][2];
+        u32x4 xb[kChunk][kMT][2];
         float xsv[kChunk][kMT], wsv[kChunk];
 #pragma unroll
         for (int c = 0; c < kChunk; ++c) {
@@ -132,19 +137,17 @@ __global__ __launch_bounds__(kStreamThreads) void w8a8_stream_kernel(
 #pragma unroll
         for (int c = 0; c < kChunk; ++c) {
             const int64_t kb = kb0 + c * kStreamWaves;
-            if (kb < kb_end) {
-                wa[c][0] = load_16B(wrow + kb * 128);
-                wa[c][1] = load_16B(wrow + kb * 128 + 64);
-            }
+            if (kb < kb_end) slab_issue(wslab[wave][c], rsrc_w, lane_off_w, K, kb);
         }
-        // Compiler-only barrier: keeps every load above issued before the
-        // first wait below (the scheduler otherwise sinks some of them).
-        asm volatile("" ::: "memory");
+        const bool two = kb0 + kStreamWaves < kb_end;     // wave-uniform
 #pragma unroll
         for (int c = 0; c < kChunk; ++c) {
             const int64_t kb = kb0 + c * kStreamWaves;
             if (kb < kb_end) {
-                const i32x8 a = __builtin_bit_cast(i32x8, __builtin_shufflevector(wa[c][0], wa[c][1], 0, 1, 2, 3, 4, 5, 6, 7));
+                wait_block(c, two);
+                u32x4 wa0, wa1;
+                slab_read(wslab[wave][c], r, g, wa0, wa1);
+                const i32x8 a = __builtin_bit_cast(i32x8, __builtin_shufflevector(wa0, wa1, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
                 for (int t = 0; t < kMT; ++t) {
                     const u32x4 x0 = m_ok[t] ? xb[c][t][0] : zero4, x1 = m_ok[t] ? xb[c][t][1] : zero4;
@@ -479,15 +482,9 @@ hipError_t launch_w8a8_stream(const uint8_t* xq, const float* xs, const uint8_t*
 #undef BFP8_LAUNCH_LDS
         return hipGetLastError();
     }
-#define BFP8_LAUNCH_MT(MT)                                                                                      \
-    hipLaunchKernelGGL(w8a8_stream_kernel<MT>, grid, dim3(kStreamThreads), 0, stream, xq, xs, wq, ws, y, y_dtype, M, \
-                       N, K, p.n_tiles, p.splits, p.kb_per_split, partials, counters)
-    if (p.mt_per_wg == 1) {
-        BFP8_LAUNCH_MT(1);
-    } else {
-        BFP8_LAUNCH_MT(2);
-    }
-#undef BFP8_LAUNCH_MT
+    if (p.mt_per_wg != 2) return hipErrorInvalidValue;   // M > 16 streams two token tiles per workgroup
+    hipLaunchKernelGGL(w8a8_stream2_kernel, grid, dim3(kStreamThreads), 0, stream, xq, xs, wq, ws, y, y_dtype, M, N,
+                       K, p.n_tiles, p.splits, p.kb_per_split, partials, counters);
     return hipGetLastError();
 }
 
