@@ -48,8 +48,10 @@ __device__ __forceinline__ uint32_t scale_f16x2(uint32_t v, f16x2 factor) {
     return __builtin_bit_cast(uint32_t, p);
 }
 
-constexpr int kW8A16Chunk = 4;   // 128-K blocks per wave with loads in flight together (blk32, M > 16)
+constexpr int kW8A16Chunk = 4;   // 128-K blocks per wave with loads in flight together
 
+// blk32 with M > 16: one 16-token tile per workgroup (grid z), register
+// loads for weights and tokens.
 __global__ __launch_bounds__(kStreamThreads) void w8a16_blk32_stream_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq, const uint8_t* __restrict__ e8m0,
     void* __restrict__ y, int y_dtype, int64_t M, int64_t N, int64_t K,
@@ -233,8 +235,8 @@ __global__ __launch_bounds__(kStreamThreads) void w8a16_blk128_stream_lds_kernel
 // blk32 for M <= 16, staged like w8a16_blk128_stream_lds_kernel: weight
 // lines through LDS slabs, the block's fp16 token rows by direct-to-LDS
 // loads for Mp <= 8 (register loads for Mp = 16), issued before the first
-// wait; the scale bytes stay register loads.  The exact fp16 scaling and the accumulation across all K are those
-// of the kernel above.
+// wait; the scale bytes stay register loads.  The exact fp16 scaling and
+// the accumulation across all K are those of w8a16_blk32_stream_kernel.
 template <int kMp>
 __global__ __launch_bounds__(kStreamThreads) void w8a16_blk32_stream_lds_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq, const uint8_t* __restrict__ e8m0,
@@ -302,7 +304,7 @@ __global__ __launch_bounds__(kStreamThreads) void w8a16_blk32_stream_lds_kernel(
                 slab_read(wslab[wave][c], r, g, wa0, wa1);
                 const uint32_t q[8] = {wa0[0], wa0[1], wa0[2], wa0[3], wa1[0], wa1[1], wa1[2], wa1[3]};
                 const uint8_t* row = xrows[wave][c] + r_row * kXRowStride + 32 * g;
-                // 2^(E - 127 + 8) as fp16: exponent field E - 104 (see the kernel above).
+                // 2^(E - 127 + 8) as fp16: exponent field E - 104 (as in w8a16_blk32_stream_kernel).
                 const uint32_t f0 = (ebyte[c][0] - 104u) << 10, f1 = (ebyte[c][1] - 104u) << 10;
                 const f16x2 factor0 = __builtin_bit_cast(f16x2, f0 | (f0 << 16));
                 const f16x2 factor1 = __builtin_bit_cast(f16x2, f1 | (f1 << 16));

@@ -240,7 +240,8 @@ size_t bfp8_workspace_bytes(int op, int64_t M, int64_t N, int64_t K);
  *                 kernel.  W8A8 also streams M <= 2 * m_stream_max when
  *                 N * K <= 2^24 (measured faster there); other M go to the
  *                 tiled MFMA kernels.  W8A16 blk128 streams M <= m_stream_max
- *                 and uses its tiled MFMA kernel above; blk32 always streams.
+ *                 and uses its tiled MFMA kernel for larger M; blk32 always
+ *                 streams.
  * Any output pointer may be NULL.
  */
 bfp8_status bfp8_get_limits(int op, int64_t* k_multiple, int64_t* n_multiple,
