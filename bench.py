@@ -350,10 +350,11 @@ def bench_prefill(torch, bfp8, inputs, args):
     xq = torch.empty((M, K), dtype=torch.uint8, device="cuda")
     xs = torch.empty((M, K // 128), dtype=torch.float32, device="cuda")
     y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    wsp = bfp8.make_workspace(bfp8.OP_GEMM_W8A8_BLK128, M, N, K)
 
     def gemm(i):
         a = copies[i % len(copies)]
-        bfp8.bfp8_gemm_w8a8_blk128(xq, xs, a[0], a[1], y)
+        bfp8.bfp8_gemm_w8a8_blk128(xq, xs, a[0], a[1], y, wsp)
 
     phases = [("quant_act_1x128", lambda i: bfp8.bfp8_quantize_act_1x128(x, xq, xs)), ("gemm_w8a8_blk128", gemm)]
     ms, wall, kern, timing = run_steps(torch, phases, args.steps, args.warmup)

@@ -79,14 +79,29 @@ namespace {
 
 size_t round256(size_t v) { return (v + 255) / 256 * 256; }
 
-// W8A8 workspace for codes input: the streaming plan's or the tiled kernels'
-// (w8a8_streams decides).
+// W8A8 workspace for codes input: the streaming plan's, none for the wide
+// kernel, or the tiled kernels' (w8a8_streams and w8a8_wide decide).
 size_t w8a8_workspace(int64_t M, int64_t N, int64_t K) {
-    if (w8a8_streams(M, N, K)) return stream_workspace_bytes(plan_stream_w8a8(M, N, K));
+    if (w8a8_streams(M, N, K)) return stream_workspace_bytes(plan_stream(M, N, K));
+    if (w8a8_wide(M, N, K)) return 0;
     return K <= kTileMaxK ? tile_workspace_bytes(M, N, K) : 0;
 }
 
-// Workspace of the fused quantise + W8A8 call above kFusedQuantMaxM, where
+// The W8A8 codes kernels by M (workspace already checked).
+hipError_t launch_w8a8(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws, void* y,
+                       int y_dtype, int64_t M, int64_t N, int64_t K, void* workspace, hipStream_t stream) {
+    if (w8a8_streams(M, N, K)) return launch_w8a8_stream(xq, xs, wq, ws, y, y_dtype, M, N, K, workspace, stream);
+    if (w8a8_wide(M, N, K)) return launch_w8a8_wide(xq, xs, wq, ws, y, y_dtype, M, N, K, stream);
+    return launch_w8a8_tile(xq, xs, wq, ws, y, y_dtype, M, N, K, workspace, stream);
+}
+
+// The fused quantise + W8A8 call quantises inside the streaming kernel when
+// the codes call would stream (so both give the same bits), M permitting.
+bool quantises_in_registers(int64_t M, int64_t N, int64_t K) {
+    return M <= kFusedQuantMaxM && w8a8_streams(M, N, K);
+}
+
+// Workspace of the fused quantise + W8A8 call when it does not, where
 // the codes are staged: [W8A8 workspace | xq codes M*K | xs scales M*K/128],
 // each part 256-byte aligned, the zero-initialised counters first.
 struct QuantGemmParts {
@@ -109,7 +124,7 @@ size_t bfp8_workspace_bytes(int op, int64_t M, int64_t N, int64_t K) {
     if (M < 1 || N < 16 || K < 128) return 0;
     switch (op) {
         case BFP8_OP_QUANT_GEMM_W8A8_BLK128:
-            if (M <= kFusedQuantMaxM) return stream_workspace_bytes(plan_stream(M, N, K));
+            if (quantises_in_registers(M, N, K)) return stream_workspace_bytes(plan_stream(M, N, K));
             return K <= kTileMaxK ? quant_gemm_parts(M, N, K).total : 0;
         case BFP8_OP_GEMM_W8A8_BLK128:
             return w8a8_workspace(M, N, K);
@@ -132,9 +147,7 @@ bfp8_status bfp8_gemm_w8a8_blk128(const uint8_t* xq, const float* xs, const uint
     bfp8_status st = check_gemm(xq, wq, ws, y, y_dtype, M, N, K, 16, need, workspace, workspace_bytes);
     if (st != BFP8_OK) return st;
     if (!aligned(xs)) return BFP8_E_ALIGN;
-    if (w8a8_streams(M, N, K))
-        return launched(launch_w8a8_stream(xq, xs, wq, ws, y, y_dtype, M, N, K, workspace, as_stream(stream)));
-    return launched(launch_w8a8_tile(xq, xs, wq, ws, y, y_dtype, M, N, K, workspace, as_stream(stream)));
+    return launched(launch_w8a8(xq, xs, wq, ws, y, y_dtype, M, N, K, workspace, as_stream(stream)));
 }
 
 bfp8_status bfp8_quant_gemm_w8a8_blk128(const void* x, int x_dtype, const uint8_t* wq, const float* ws,
@@ -146,7 +159,7 @@ bfp8_status bfp8_quant_gemm_w8a8_blk128(const void* x, int x_dtype, const uint8_
     bfp8_status st = check_gemm(x, wq, ws, y, y_dtype, M, N, K, 16, need, workspace, workspace_bytes);
     if (st != BFP8_OK) return st;
     if (!is16(x_dtype)) return BFP8_E_DTYPE;
-    if (M <= kFusedQuantMaxM)
+    if (quantises_in_registers(M, N, K))
         return launched(launch_w8a8_stream_quant(x, x_dtype == BFP8_BF16, wq, ws, y, y_dtype, M, N, K, workspace,
                                                  as_stream(stream)));
     if (K > kTileMaxK) return BFP8_E_SHAPE;
@@ -158,9 +171,7 @@ bfp8_status bfp8_quant_gemm_w8a8_blk128(const void* x, int x_dtype, const uint8_
     void* gemm_ws = parts.gemm ? workspace : nullptr;
     hipError_t e = launch_quant_act_1x128(x, x_dtype == BFP8_BF16, M, K, xq, xs, as_stream(stream));
     if (e != hipSuccess) return BFP8_E_LAUNCH;
-    if (w8a8_streams(M, N, K))
-        return launched(launch_w8a8_stream(xq, xs, wq, ws, y, y_dtype, M, N, K, gemm_ws, as_stream(stream)));
-    return launched(launch_w8a8_tile(xq, xs, wq, ws, y, y_dtype, M, N, K, gemm_ws, as_stream(stream)));
+    return launched(launch_w8a8(xq, xs, wq, ws, y, y_dtype, M, N, K, gemm_ws, as_stream(stream)));
 }
 
 bfp8_status bfp8_gemm_w8a16_blk128(const void* x, int x_dtype, const uint8_t* wq, const float* ws,

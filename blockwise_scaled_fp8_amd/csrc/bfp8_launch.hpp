@@ -10,23 +10,12 @@ namespace bfp8 {
 
 // Largest M that the W8A8 codes path always serves with the weight-streaming
 // kernel.
-#ifndef BFP8_STREAM_MAX_M
-#define BFP8_STREAM_MAX_M 16
-#endif
-constexpr int64_t kStreamMaxM = BFP8_STREAM_MAX_M;
-// W8A8 dispatch (codes in), from the projection sweep: the streaming kernel
-// for M <= 16, and with two 16-token tiles per workgroup for M <= 32 on
-// projections of at most 2^24 weights (4096 x 4096: 10.5 vs 12.2 us tiled;
-// 1024 x 4096: 8.4 vs 9.8 us), the tiled kernels otherwise (12288 x 4096 at
-// M = 32: 22.4 us tiled vs 28.2 us streamed).
-inline bool w8a8_streams(int64_t M, int64_t N, int64_t K) {
-    return M <= kStreamMaxM || (M <= 2 * kStreamMaxM && N * K <= ((int64_t)1 << 24));
-}
-// Rows of W covered by one streaming workgroup (one MFMA row tile).
-constexpr int64_t kStreamRows = 16;
+constexpr int64_t kStreamMaxM = 16;   // one 16-token MFMA column tile
 // Largest K of every GEMM: the tiled kernels address 256 rows x K bytes and
 // the streaming kernels 16 rows x K bytes through 32-bit buffer offsets.
 constexpr int64_t kTileMaxK = (int64_t)1 << 23;
+// Rows of W covered by one streaming workgroup (one MFMA row tile).
+constexpr int64_t kStreamRows = 16;
 // Workspace bytes of the tiled W8A8 kernels (split-K partial tiles and tile
 // counters; 0 when the shape is not split).
 size_t tile_workspace_bytes(int64_t M, int64_t N, int64_t K);
@@ -34,15 +23,32 @@ size_t tile_workspace_bytes(int64_t M, int64_t N, int64_t K);
 size_t tile16_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 // Split-K plan of a streaming kernel: a workgroup covers 16 weight rows and
-// `mt_per_wg` 16-token tiles; `splits` workgroups share one such block of
-// output tiles, each covering `kb_per_split` 128-K blocks.  Counters and
-// partial tiles are kept per 16x16 output tile.
+// one 16-token tile; `splits` workgroups share one output tile, each
+// covering `kb_per_split` 128-K blocks.  Counters and partial tiles are kept
+// per 16x16 output tile.
 struct StreamPlan {
-    int64_t n_tiles, m_tiles, mt_per_wg, splits, kb_per_split;
+    int64_t n_tiles, m_tiles, splits, kb_per_split;
 };
-StreamPlan plan_stream(int64_t M, int64_t N, int64_t K, int64_t mt_per_wg = 1);
-// The W8A8 codes kernel's plan: 1 or 2 token tiles per workgroup by M.
-StreamPlan plan_stream_w8a8(int64_t M, int64_t N, int64_t K);
+StreamPlan plan_stream(int64_t M, int64_t N, int64_t K);
+
+// W8A8 dispatch (codes in), from the projection sweep:
+//  * the streaming kernel for M <= 16 when it needs no split of K (at least
+//    256 weight-row tiles), or when N < 1024;
+//  * the wide kernel (all tokens per workgroup, no split) for the other
+//    M <= 32, and for M <= 64 on projections of at most 2^24 weights.
+//    Measured: 1024 x 4096 at M = 1 / 16: 4.3 / 4.4 us against 5.3 / 5.5 us
+//    streamed with K split 4 ways; at M = 32: 4096 x 4096 6.7 us,
+//    1024 x 4096 4.9 us, 12288 x 4096 18.9 us, against 11.6, 9.8 and 22.5 us
+//    tiled; at M = 64: 4096 x 4096 9.5 vs 12.1 us, 1024 x 4096 7.3 vs
+//    10.3 us, while 12288 x 4096 is faster tiled (25.1 vs 28.5 us);
+//  * the tiled kernels otherwise.
+inline bool w8a8_streams(int64_t M, int64_t N, int64_t K) {
+    return M <= kStreamMaxM && (N < 1024 || K > kTileMaxK || plan_stream(M, N, K).splits == 1);
+}
+inline bool w8a8_wide(int64_t M, int64_t N, int64_t K) {
+    if (K > kTileMaxK || w8a8_streams(M, N, K)) return false;
+    return M <= 2 * kStreamMaxM || (M <= 4 * kStreamMaxM && N * K <= ((int64_t)1 << 24));
+}
 // Workspace bytes of a streaming plan: tile counters, then fp32 partial tiles.
 size_t stream_workspace_bytes(const StreamPlan& p);
 
@@ -56,6 +62,9 @@ hipError_t launch_dequant_weight(const uint8_t* wq, const float* scales, int blo
 hipError_t launch_w8a8_tile(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
                             void* y, int y_dtype, int64_t M, int64_t N, int64_t K, void* workspace,
                             hipStream_t stream);
+// 1 <= M <= 64, N a multiple of 16, K <= kTileMaxK; needs no workspace.
+hipError_t launch_w8a8_wide(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
+                            void* y, int y_dtype, int64_t M, int64_t N, int64_t K, hipStream_t stream);
 hipError_t launch_w8a8_stream(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
                               void* y, int y_dtype, int64_t M, int64_t N, int64_t K,
                               void* workspace, hipStream_t stream);

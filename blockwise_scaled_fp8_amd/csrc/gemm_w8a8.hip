@@ -21,11 +21,13 @@
 // 128-aligned tile), never once per workgroup of arbitrary width ([ADA]
 // "The fix", the latent-bug paragraph).
 //
-// Two kernels, chosen by M ([ADA] "One tile doesn't fit all M"):
-//   * stream (M <= 16): weight streaming.  One workgroup per 16 weight rows
+// Three kernels, chosen by M ([ADA] "One tile doesn't fit all M"):
+//   * stream (M <= 16, see w8a8_streams): weight streaming.  One workgroup per 16 weight rows
 //     (and per split of K), sixteen waves each holding its 128-K blocks of
 //     weight loads in flight, tokens padded to 16 on the MFMA column axis.
-//   * tile (M > 16): in gemm_w8a8_tile.hip.
+//   * wide (M <= 64, see w8a8_wide): one workgroup per 16 weight rows and
+//     all tokens over all of K, eight waves with private LDS rings.
+//   * tile (larger M): in gemm_w8a8_tile.hip.
 
 #include "bfp8_device.hpp"
 #include "bfp8_launch.hpp"
@@ -34,24 +36,19 @@
 namespace bfp8 {
 
 // ===================================================================== plan
-StreamPlan plan_stream(int64_t M, int64_t N, int64_t K, int64_t mt_per_wg) {
+StreamPlan plan_stream(int64_t M, int64_t N, int64_t K) {
     StreamPlan p;
     p.n_tiles = N / kStreamRows;
     p.m_tiles = (M + 15) / 16;
-    p.mt_per_wg = mt_per_wg;
     const int64_t KB = K / 128;
     // Enough workgroups to give each of the 256 CUs one, while at least half
     // of a workgroup's waves still get a 128-K block.
-    const int64_t tiles = p.n_tiles * ((p.m_tiles + mt_per_wg - 1) / mt_per_wg);
+    const int64_t tiles = p.n_tiles * p.m_tiles;
     int64_t splits = 1;
     while (tiles * splits < 256 && 2 * (KB / (splits * 2)) >= kStreamWaves) splits *= 2;
     p.splits = splits;
     p.kb_per_split = (KB + splits - 1) / splits;
     return p;
-}
-
-StreamPlan plan_stream_w8a8(int64_t M, int64_t N, int64_t K) {
-    return plan_stream(M, N, K, M <= 16 ? 1 : 2);
 }
 
 size_t stream_workspace_bytes(const StreamPlan& p) {
@@ -67,109 +64,6 @@ size_t stream_workspace_bytes(const StreamPlan& p) {
 // the same for both MFMA operands.  The waves take interleaved 128-K blocks,
 // so at any time a workgroup reads adjacent blocks of its rows.
 //
-// 16 < M <= 32 on projections small enough that one pass over the weights
-// for 32 tokens beats the tiled kernels (w8a8_streams): two 16-token tiles
-// per workgroup, each wave issuing two MFMAs per block on the same weight
-// fragment.  The weights come through per-wave LDS slabs as whole 128-byte
-// lines; the token codes stay register loads (every lane carries a live
-// token row of one of the tiles).  Every load of a pass is issued before
-// anything waits on one: token rows and scales first (L2), then the weight
-// slabs.  Token rows past M are read from row 0 (a valid address) and zeroed
-// by a select afterwards, so no load sits in a lane-divergent branch; such
-// branches made the compiler wait for each block's token loads before
-// issuing the next block's, serialising four L2 round trips ahead of the
-// weight stream (measured 0.7 us).
-constexpr int kStream2Chunk = 2;
-static_assert(kStream2Chunk == 2, "wait_block counts two blocks per pass");
-
-__global__ __launch_bounds__(kStreamThreads) void w8a8_stream2_kernel(
-    const uint8_t* __restrict__ xq, const float* __restrict__ xs,
-    const uint8_t* __restrict__ wq, const float* __restrict__ ws,
-    void* __restrict__ y, int y_dtype, int64_t M, int64_t N, int64_t K,
-    int64_t n_tiles, int64_t splits, int64_t kb_per_split,
-    float* __restrict__ partials, uint32_t* __restrict__ counters) {
-    constexpr int kMT = 2, kChunk = kStream2Chunk;
-    __shared__ float red[kStreamWaves * 256];
-    __shared__ __attribute__((aligned(1024))) uint8_t wslab[kStreamWaves][kChunk][kSlabBytes];
-    const int64_t nt = blockIdx.x, split = blockIdx.y, mt0 = blockIdx.z * kMT;
-    const int64_t KB = K / 128;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
-    const int r = lane & 15, g = lane >> 4;
-
-    const int64_t kb_begin = split * kb_per_split;
-    const int64_t kb_end = kb_begin + kb_per_split < KB ? kb_begin + kb_per_split : KB;
-
-    const i32x4 rsrc_w = buffer_rsrc(wq + nt * 16 * K, (uint32_t)(16 * K));
-    const int lane_off_w = slab_lane_offset(lane, K);
-    const float* ws_row = ws + (nt * 16 / 128) * KB;
-    bool m_ok[kMT];
-    const uint8_t* xrow[kMT];
-    const float* xs_row[kMT];
-#pragma unroll
-    for (int t = 0; t < kMT; ++t) {
-        const int64_t m = (mt0 + t) * 16 + r;     // token supplied by this lane for tile t
-        m_ok[t] = m < M;
-        xrow[t] = xq + (m_ok[t] ? m : 0) * K + g * 16;
-        xs_row[t] = xs + (m_ok[t] ? m : 0) * KB;
-    }
-
-    f32x4 acc[kMT];
-#pragma unroll
-    for (int t = 0; t < kMT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
-    const u32x4 zero4 = {0u, 0u, 0u, 0u};
-    for (int64_t kb0 = kb_begin + wave; kb0 < kb_end; kb0 += kStreamWaves * kChunk) {
-        u32x4 xb[kChunk][kMT][2];
-        float xsv[kChunk][kMT], wsv[kChunk];
-#pragma unroll
-        for (int c = 0; c < kChunk; ++c) {
-            const int64_t kb = kb0 + c * kStreamWaves;
-            if (kb < kb_end) {
-#pragma unroll
-                for (int t = 0; t < kMT; ++t) {
-                    xb[c][t][0] = load_16B(xrow[t] + kb * 128);
-                    xb[c][t][1] = load_16B(xrow[t] + kb * 128 + 64);
-                    xsv[c][t] = xs_row[t][kb];
-                }
-                wsv[c] = ws_row[kb];
-            }
-        }
-#pragma unroll
-        for (int c = 0; c < kChunk; ++c) {
-            const int64_t kb = kb0 + c * kStreamWaves;
-            if (kb < kb_end) slab_issue(wslab[wave][c], rsrc_w, lane_off_w, K, kb);
-        }
-        const bool two = kb0 + kStreamWaves < kb_end;     // wave-uniform
-#pragma unroll
-        for (int c = 0; c < kChunk; ++c) {
-            const int64_t kb = kb0 + c * kStreamWaves;
-            if (kb < kb_end) {
-                wait_block(c, two);
-                u32x4 wa0, wa1;
-                slab_read(wslab[wave][c], r, g, wa0, wa1);
-                const i32x8 a = __builtin_bit_cast(i32x8, __builtin_shufflevector(wa0, wa1, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-                for (int t = 0; t < kMT; ++t) {
-                    const u32x4 x0 = m_ok[t] ? xb[c][t][0] : zero4, x1 = m_ok[t] ? xb[c][t][1] : zero4;
-                    const float sc = m_ok[t] ? xsv[c][t] * wsv[c] : 0.0f;
-                    const i32x8 b = __builtin_bit_cast(i32x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
-                    const f32x4 blk = mfma_e4m3_16x16x128(a, b, zero);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) acc[t][i] = __builtin_fmaf(blk[i], sc, acc[t][i]);
-                }
-            }
-        }
-    }
-    // One reduction per live token tile (tiles wholly past M are skipped:
-    // their counters do not exist); a barrier separates the uses of `red`.
-#pragma unroll
-    for (int t = 0; t < kMT; ++t) {
-        if ((mt0 + t) * 16 >= M) break;
-        if (t > 0) __syncthreads();
-        stream_finish(acc[t], red, y, y_dtype, M, N, nt, mt0 + t, splits, split, n_tiles, partials, counters);
-    }
-}
-
 // M <= 16 (padded token count Mp = 1, 2, 4, 8 or 16): the same product
 // with both operands staged in LDS.  The weights arrive as whole 128-byte
 // lines in per-wave slabs; the block's token rows (128 code bytes each) by
@@ -460,15 +354,171 @@ __global__ __launch_bounds__(kStreamThreads) void w8a8_stream_quant_kernel(
     stream_finish(acc, red, y, y_dtype, M, N, nt, 0, splits, split, n_tiles, partials, counters);
 }
 
+// ------------------------------------------------------------ wide stream ----
+// M <= 64 (see w8a8_wide): one workgroup per 16 weight rows and all tokens
+// (kT = 2 or 4 16-token tiles), over all of K, so the weights are read once
+// and no split-K hand-off is needed.  Eight waves: wave w takes token tiles
+// 2 tg, 2 tg + 1 (tg = w % G, G = kT / 2 groups) and the 128-K blocks kw,
+// kw + KW, ... (kw = w / G, KW = 8 / G).  Each wave owns a ring of three
+// LDS slots; a slot holds one block: the 16 weight rows (2 KB), the wave's
+// 32 token rows (4 KB), their token scales and the weight scale, brought in
+// by direct-to-LDS loads of whole 128-byte lines (a load instruction covers
+// eight full lines; register loads of MFMA fragments touch sixteen half
+// lines each, which a read probe measured at half the throughput from L2).
+// A wave multiplies block j
+// while blocks j+1 and j+2 are in flight and refills the slot as soon as it
+// has read block j's operands; the slots are private, so there is no barrier
+// until the end, where the KW partial tiles of every token tile are summed
+// in LDS in K order.
+constexpr int kWideWaves = 8;
+constexpr int kWideThreads = kWideWaves * kWave;
+constexpr int kWideSlots = 3;
+constexpr int kWideOffX = kSlabBytes;                   // 32 token rows
+constexpr int kWideOffXs = kWideOffX + 32 * 128;        // 64 token scales (lanes >= 32 load padding)
+constexpr int kWideOffWs = kWideOffXs + 64 * 4;         // weight scale
+constexpr int kWideSlot = (kWideOffWs + 4 + 255) / 256 * 256;
+constexpr int kWideVmem = 2 + 4 + 1 + 1;                 // load instructions per block
+static_assert(kWideWaves * kWideSlots * kWideSlot <= 160 * 1024, "LDS ring");
+
+template <int Y>
+__device__ __forceinline__ void wide_wait_n() {
+    constexpr int n = Y * kWideVmem;
+    __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+template <int kT>
+__global__ __launch_bounds__(kWideThreads, 1) void w8a8_wide_kernel(
+    const uint8_t* __restrict__ xq, const float* __restrict__ xs,
+    const uint8_t* __restrict__ wq, const float* __restrict__ ws,
+    void* __restrict__ y, int y_dtype, int64_t M, int64_t N, int64_t K) {
+    constexpr int G = kT / 2, KW = kWideWaves / G;
+    static_assert(kT == 2 || kT == 4, "token tiles");
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[kWideWaves * kWideSlots * kWideSlot];
+    const int64_t nt = blockIdx.x;
+    const int KB = (int)(K / 128);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
+    const int tg = wave % G, kw = wave / G;
+    const int r = lane & 15, g = lane >> 4;
+    const int64_t m0 = 32 * tg;                       // first token of this wave's tiles
+
+    const i32x4 rsrc_w = buffer_rsrc(wq + nt * 16 * K, (uint32_t)(16 * K));
+    // Token rows and scales from row m0 on; rows at or past M load as zeros.
+    const int64_t rows_x = M - m0 > 0 ? M - m0 : 0;
+    const i32x4 rsrc_x = buffer_rsrc(xq + m0 * K, (uint32_t)(rows_x * K));
+    const i32x4 rsrc_xs = buffer_rsrc(xs + m0 * KB, (uint32_t)(rows_x * KB * 4));
+    const i32x4 rsrc_ws = buffer_rsrc(ws + (nt * 16 / 128) * KB, (uint32_t)(KB * 4));
+    const int lane_off = slab_lane_offset(lane, K);   // row lane/8, chunk (lane%8) ^ (lane/8)
+    const int xs_off = lane * KB * 4;
+    uint8_t* my_ring = ring + wave * kWideSlots * kWideSlot;
+
+    auto issue = [&](int slot, int kb) {
+        const uint32_t base = __builtin_amdgcn_readfirstlane(lds_address(my_ring + slot * kWideSlot));
+        const int k_off = __builtin_amdgcn_readfirstlane(kb * 128);
+        const int row8 = __builtin_amdgcn_readfirstlane((int)(8 * K));
+        dma16(base, rsrc_w, lane_off, 0, k_off);
+        dma16(base + 1024, rsrc_w, lane_off, row8, k_off);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            dma16(base + kWideOffX + 1024 * q, rsrc_x, lane_off, __builtin_amdgcn_readfirstlane((int)(8 * q * K)), k_off);
+        dma4(base + kWideOffXs, rsrc_xs, xs_off, __builtin_amdgcn_readfirstlane(kb * 4));
+        if (lane == 0) dma4(base + kWideOffWs, rsrc_ws, 0, __builtin_amdgcn_readfirstlane(kb * 4));
+    };
+
+    const int nj = kw < KB ? (KB - 1 - kw) / KW + 1 : 0;   // blocks of this wave
+#pragma unroll
+    for (int s = 0; s < kWideSlots; ++s)
+        if (s < nj) issue(s, kw + KW * s);
+
+    f32x4 acc[2];
+    acc[0] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    acc[1] = acc[0];
+    const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+    int slot = 0;
+    for (int j = 0; j < nj; ++j) {
+        // Block j is complete once at most the loads of the (up to two)
+        // younger blocks are outstanding (loads retire in issue order).
+        const int younger = nj - 1 - j;
+        if (younger >= 2) wide_wait_n<2>();
+        else if (younger == 1) wide_wait_n<1>();
+        else wide_wait_n<0>();
+        asm volatile("" ::: "memory");
+        const uint8_t* sl = my_ring + slot * kWideSlot;
+        u32x4 a0, a1, b0[2], b1[2];
+        slab_read(sl, r, g, a0, a1);
+        float xsv[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            slab_read(sl + kWideOffX + t * 2048, r, g, b0[t], b1[t]);
+            xsv[t] = reinterpret_cast<const float*>(sl + kWideOffXs)[16 * t + r];
+        }
+        const float wsv = *reinterpret_cast<const float*>(sl + kWideOffWs);
+        // Every operand of block j is in registers before the slot is refilled.
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        if (j + kWideSlots < nj) issue(slot, kw + KW * (j + kWideSlots));
+        const i32x8 a = __builtin_bit_cast(i32x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const i32x8 b = __builtin_bit_cast(i32x8, __builtin_shufflevector(b0[t], b1[t], 0, 1, 2, 3, 4, 5, 6, 7));
+            const f32x4 blk = mfma_e4m3_16x16x128(a, b, zero);
+            const float sc = xsv[t] * wsv;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[t][i] = __builtin_fmaf(blk[i], sc, acc[t][i]);
+        }
+        slot = slot + 1 == kWideSlots ? 0 : slot + 1;
+    }
+
+    // Sum the KW partial tiles of every token tile in K order.  Every
+    // wave's loads are done (its last wait was vmcnt(0)); the barrier
+    // orders the reuse of the ring.
+    __syncthreads();
+    float* red = reinterpret_cast<float*>(ring);
+    // Slot of (token tile tt = 2 tg + t, K lane kw): ((kw * kT + tt) * 64 + lane) * 4 floats.
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+        *reinterpret_cast<f32x4*>(red + ((kw * kT + 2 * tg + t) * kWave + lane) * 4) = acc[t];
+    __syncthreads();
+    // Thread x: lane L = x % 64 of token tiles tt = x / 64, x / 64 + 8, ...
+    const int L = threadIdx.x % kWave, rr = L & 15, gg = L >> 4;
+    for (int tt = threadIdx.x / kWave; tt < kT; tt += kWideWaves) {
+        f32x4 v = *reinterpret_cast<const f32x4*>(red + (tt * kWave + L) * 4);
+#pragma unroll
+        for (int w = 1; w < KW; ++w) v += *reinterpret_cast<const f32x4*>(red + ((w * kT + tt) * kWave + L) * 4);
+        const int64_t m = 16 * tt + rr;
+        if (m < M) {
+            const int64_t idx = m * N + nt * 16 + 4 * gg;
+            if (y_dtype == 2) {
+                *reinterpret_cast<f32x4*>(static_cast<float*>(y) + idx) = v;
+            } else {
+                uint32_t h[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) h[i] = y_dtype == 0 ? float_to_bf16_bits(v[i]) : float_to_f16_bits(v[i]);
+                *reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + idx) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+            }
+        }
+    }
+}
+
+hipError_t launch_w8a8_wide(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
+                            void* y, int y_dtype, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+    if (M < 1 || M > 64 || N % 16 != 0 || K > kTileMaxK) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)(N / 16));
+    if (M <= 32)
+        hipLaunchKernelGGL(w8a8_wide_kernel<2>, grid, dim3(kWideThreads), 0, stream, xq, xs, wq, ws, y, y_dtype, M, N, K);
+    else
+        hipLaunchKernelGGL(w8a8_wide_kernel<4>, grid, dim3(kWideThreads), 0, stream, xq, xs, wq, ws, y, y_dtype, M, N, K);
+    return hipGetLastError();
+}
+
 hipError_t launch_w8a8_stream(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
                               void* y, int y_dtype, int64_t M, int64_t N, int64_t K,
                               void* workspace, hipStream_t stream) {
-    const StreamPlan p = plan_stream_w8a8(M, N, K);
+    if (M > kStreamMaxM) return hipErrorInvalidValue;
+    const StreamPlan p = plan_stream(M, N, K);
     uint32_t* counters;
     float* partials;
     stream_workspace_parts(p, workspace, counters, partials);
-    const dim3 grid((unsigned)p.n_tiles, (unsigned)p.splits, (unsigned)((p.m_tiles + p.mt_per_wg - 1) / p.mt_per_wg));
-    if (M <= 16) {
+    const dim3 grid((unsigned)p.n_tiles, (unsigned)p.splits, 1u);
+    {
 #define BFP8_LAUNCH_LDS(MP)                                                                                    \
     hipLaunchKernelGGL(w8a8_stream_lds_kernel<MP>, grid, dim3(kStreamThreads), 0, stream, xq, xs, wq, ws, y, y_dtype, \
                        M, N, K, p.n_tiles, p.splits, p.kb_per_split, partials, counters)
@@ -480,11 +530,7 @@ hipError_t launch_w8a8_stream(const uint8_t* xq, const float* xs, const uint8_t*
             default: BFP8_LAUNCH_LDS(16); break;
         }
 #undef BFP8_LAUNCH_LDS
-        return hipGetLastError();
     }
-    if (p.mt_per_wg != 2) return hipErrorInvalidValue;   // M > 16 streams two token tiles per workgroup
-    hipLaunchKernelGGL(w8a8_stream2_kernel, grid, dim3(kStreamThreads), 0, stream, xq, xs, wq, ws, y, y_dtype, M, N,
-                       K, p.n_tiles, p.splits, p.kb_per_split, partials, counters);
     return hipGetLastError();
 }
 

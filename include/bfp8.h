@@ -160,8 +160,9 @@ bfp8_status bfp8_gemm_w8a8_blk128(const uint8_t* xq, const float* xs,
  *   workspace: at least bfp8_workspace_bytes(BFP8_OP_QUANT_GEMM_W8A8_BLK128,
  *       M, N, K) bytes, zero-filled before its first use, left ready for the
  *       next call; calls that overlap in time must not share one.  For M <= 8
- *       the streaming kernel quantises in registers; above that the codes and
- *       scales are staged in the workspace by the 1x128 quantiser.
+ *       where bfp8_gemm_w8a8_blk128 uses the weight-streaming kernel, that
+ *       kernel quantises in registers; otherwise the codes and scales are
+ *       staged in the workspace by the 1x128 quantiser.
  * Requires M >= 1, N >= 16, N % 16 == 0, K >= 128, K % 128 == 0, K <= 2^23.
  */
 bfp8_status bfp8_quant_gemm_w8a8_blk128(const void* x, int x_dtype,
@@ -236,12 +237,14 @@ size_t bfp8_workspace_bytes(int op, int64_t M, int64_t N, int64_t K);
  *   k_multiple    K must be a multiple of this.
  *   n_multiple    N must be a multiple of this.
  *   align_bytes   required alignment of every device pointer.
- *   m_stream_max  largest M always served by the weight-streaming decode
- *                 kernel.  W8A8 also streams M <= 2 * m_stream_max when
- *                 N * K <= 2^24 (measured faster there); other M go to the
- *                 tiled MFMA kernels.  W8A16 blk128 streams M <= m_stream_max
- *                 and uses its tiled MFMA kernel for larger M; blk32 always
- *                 streams.
+ *   m_stream_max  largest M served by the weight-streaming decode kernel
+ *                 (W8A8 streams it when K needs no split across workgroups,
+ *                 or N < 1024).  W8A8 uses a kernel that reads all tokens per
+ *                 16-row weight tile for the other M <= 2 * m_stream_max, and
+ *                 for M <= 4 * m_stream_max when N * K <= 2^24 (measured
+ *                 faster there), the tiled MFMA kernels otherwise.  W8A16
+ *                 blk128 streams M <= m_stream_max and uses its tiled MFMA
+ *                 kernel for larger M; blk32 always streams.
  * Any output pointer may be NULL.
  */
 bfp8_status bfp8_get_limits(int op, int64_t* k_multiple, int64_t* n_multiple,
