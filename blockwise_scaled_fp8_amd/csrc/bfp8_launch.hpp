@@ -34,20 +34,22 @@ StreamPlan plan_stream(int64_t M, int64_t N, int64_t K);
 // W8A8 dispatch (codes in), from the projection sweep:
 //  * the streaming kernel for M <= 16 when it needs no split of K (at least
 //    256 weight-row tiles), or when N < 1024;
-//  * the wide kernel (all tokens per workgroup, no split) for the other
-//    M <= 32, and for M <= 64 on projections of at most 2^24 weights.
-//    Measured: 1024 x 4096 at M = 1 / 16: 4.3 / 4.4 us against 5.3 / 5.5 us
-//    streamed with K split 4 ways; at M = 32: 4096 x 4096 6.7 us,
-//    1024 x 4096 4.9 us, 12288 x 4096 18.9 us, against 11.6, 9.8 and 22.5 us
-//    tiled; at M = 64: 4096 x 4096 9.5 vs 12.1 us, 1024 x 4096 7.3 vs
-//    10.3 us, while 12288 x 4096 is faster tiled (25.1 vs 28.5 us);
+//  * the all-token kernel (launch_w8a8_wide: every token per workgroup, no
+//    split) for the other M <= 32, and for M <= 128 when K <= 4096;
+//    measured (us): 1024 x 4096 at M = 1 / 16: 4.3 / 4.4 against 5.3 / 5.5
+//    streamed with K split 4 ways; at M = 32: 4096 x 4096 6.7, 1024 x 4096
+//    4.9, 12288 x 4096 16.5, 4096 x 12288 17.1 against 11.6, 9.8, 22.5 and
+//    17.8 tiled; at M = 64: 4096 x 4096 9.7 vs 12.1, 1024 x 4096 7.3 vs
+//    10.3, 12288 x 4096 24.1 vs 24.8; at M = 128: 4096 x 4096 11.7 vs 14.6,
+//    1024 x 4096 7.5 vs 11.5, 12288 x 4096 34.2 vs 34.5; with K = 12288
+//    and M >= 64 the tiled kernels win (M = 64: 19.2 vs 29.0 us);
 //  * the tiled kernels otherwise.
 inline bool w8a8_streams(int64_t M, int64_t N, int64_t K) {
     return M <= kStreamMaxM && (N < 1024 || K > kTileMaxK || plan_stream(M, N, K).splits == 1);
 }
 inline bool w8a8_wide(int64_t M, int64_t N, int64_t K) {
     if (K > kTileMaxK || w8a8_streams(M, N, K)) return false;
-    return M <= 2 * kStreamMaxM || (M <= 4 * kStreamMaxM && N * K <= ((int64_t)1 << 24));
+    return M <= 2 * kStreamMaxM || (M <= 8 * kStreamMaxM && K <= 4096);
 }
 // Workspace bytes of a streaming plan: tile counters, then fp32 partial tiles.
 size_t stream_workspace_bytes(const StreamPlan& p);
@@ -62,7 +64,7 @@ hipError_t launch_dequant_weight(const uint8_t* wq, const float* scales, int blo
 hipError_t launch_w8a8_tile(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
                             void* y, int y_dtype, int64_t M, int64_t N, int64_t K, void* workspace,
                             hipStream_t stream);
-// 1 <= M <= 64, N a multiple of 16, K <= kTileMaxK; needs no workspace.
+// 1 <= M <= 128, N a multiple of 16, K <= kTileMaxK; needs no workspace.
 hipError_t launch_w8a8_wide(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
                             void* y, int y_dtype, int64_t M, int64_t N, int64_t K, hipStream_t stream);
 hipError_t launch_w8a8_stream(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,

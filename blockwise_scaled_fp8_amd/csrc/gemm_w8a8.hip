@@ -355,58 +355,69 @@ __global__ __launch_bounds__(kStreamThreads) void w8a8_stream_quant_kernel(
 }
 
 // ------------------------------------------------------------ wide stream ----
-// M <= 64 (see w8a8_wide): one workgroup per 16 weight rows and all tokens
-// (kT = 2 or 4 16-token tiles), over all of K, so the weights are read once
-// and no split-K hand-off is needed.  Eight waves: wave w takes token tiles
-// 2 tg, 2 tg + 1 (tg = w % G, G = kT / 2 groups) and the 128-K blocks kw,
-// kw + KW, ... (kw = w / G, KW = 8 / G).  Each wave owns a ring of three
-// LDS slots; a slot holds one block: the 16 weight rows (2 KB), the wave's
-// 32 token rows (4 KB), their token scales and the weight scale, brought in
-// by direct-to-LDS loads of whole 128-byte lines (a load instruction covers
-// eight full lines; register loads of MFMA fragments touch sixteen half
-// lines each, which a read probe measured at half the throughput from L2).
-// A wave multiplies block j
-// while blocks j+1 and j+2 are in flight and refills the slot as soon as it
-// has read block j's operands; the slots are private, so there is no barrier
-// until the end, where the KW partial tiles of every token tile are summed
-// in LDS in K order.
+// All-token kernel (see w8a8_wide for where it is used): a workgroup owns
+// 16 kR weight rows (kR = 1 or 2 MFMA row tiles) and 16 kT tokens (kT = 2
+// or 4 token tiles; grid.y covers M above that) over all of K, so the
+// weights are read once and no split-K hand-off is needed.  Eight waves:
+// wave w takes token tiles 2 tg, 2 tg + 1 (tg = w % G, G = kT / 2) and the
+// 128-K blocks kw, kw + KW, ... (kw = w / G, KW = 8 / G).  Each wave owns a
+// ring of LDS slots (three for kR = 1, two for kR = 2); a slot holds one
+// block: the workgroup's 16 kR weight rows, the wave's 32 token rows, their
+// token scales and the weight scale, brought in by direct-to-LDS loads of
+// whole 128-byte lines (a load instruction covers eight full lines; register
+// loads of MFMA fragments touch sixteen half lines each, which a read probe
+// measured at half the throughput from L2).  A wave multiplies block j while
+// the younger blocks of its ring are in flight and refills the slot as soon
+// as it has read block j's operands; the slots are private, so there is no
+// barrier until the end, where the KW partial tiles of every output tile are
+// summed in LDS in K order.
 constexpr int kWideWaves = 8;
 constexpr int kWideThreads = kWideWaves * kWave;
-constexpr int kWideSlots = 3;
-constexpr int kWideOffX = kSlabBytes;                   // 32 token rows
-constexpr int kWideOffXs = kWideOffX + 32 * 128;        // 64 token scales (lanes >= 32 load padding)
-constexpr int kWideOffWs = kWideOffXs + 64 * 4;         // weight scale
-constexpr int kWideSlot = (kWideOffWs + 4 + 255) / 256 * 256;
-constexpr int kWideVmem = 2 + 4 + 1 + 1;                 // load instructions per block
-static_assert(kWideWaves * kWideSlots * kWideSlot <= 160 * 1024, "LDS ring");
+template <int kR>
+struct WideSlot {
+    static constexpr int kOffX = kR * kSlabBytes;                 // 32 token rows
+    static constexpr int kOffXs = kOffX + 32 * 128;               // 64 token scales (lanes >= 32 load padding)
+    static constexpr int kOffWs = kOffXs + 64 * 4;                // weight scale
+    static constexpr int kBytes = (kOffWs + 4 + 255) / 256 * 256;
+    static constexpr int kSlotsFit = 160 * 1024 / (kWideWaves * kBytes);
+    static constexpr int kSlots = kSlotsFit > 3 ? 3 : kSlotsFit;
+    static constexpr int kVmem = 2 * kR + 4 + 1 + 1;             // load instructions per block
+    static_assert(kSlots >= 2, "LDS ring");
+};
 
-template <int Y>
+template <int V, int Y>
 __device__ __forceinline__ void wide_wait_n() {
-    constexpr int n = Y * kWideVmem;
+    constexpr int n = Y * V;
     __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-template <int kT>
+template <int kR, int kT>
 __global__ __launch_bounds__(kWideThreads, 1) void w8a8_wide_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ xs,
     const uint8_t* __restrict__ wq, const float* __restrict__ ws,
     void* __restrict__ y, int y_dtype, int64_t M, int64_t N, int64_t K) {
     constexpr int G = kT / 2, KW = kWideWaves / G;
-    static_assert(kT == 2 || kT == 4, "token tiles");
+    using SL = WideSlot<kR>;
+    constexpr int kWideSlots = SL::kSlots, kWideSlot = SL::kBytes;
+    constexpr int kWideOffX = SL::kOffX, kWideOffXs = SL::kOffXs, kWideOffWs = SL::kOffWs;
+    static_assert(kT == 2 || kT == 4 || kT == 8, "token tiles");
     __shared__ __attribute__((aligned(1024))) uint8_t ring[kWideWaves * kWideSlots * kWideSlot];
-    const int64_t nt = blockIdx.x;
+    const int64_t nt = blockIdx.x;            // 16 kR weight rows
+    const int64_t mg = blockIdx.y;            // 16 kT tokens
     const int KB = (int)(K / 128);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
     const int tg = wave % G, kw = wave / G;
     const int r = lane & 15, g = lane >> 4;
-    const int64_t m0 = 32 * tg;                       // first token of this wave's tiles
+    const int64_t m0 = 16 * kT * mg + 32 * tg;        // first token of this wave's tiles
+    const int64_t n0 = 16 * kR * nt;
+    const int64_t rows_w = N - n0 < 16 * kR ? N - n0 : 16 * kR;
 
-    const i32x4 rsrc_w = buffer_rsrc(wq + nt * 16 * K, (uint32_t)(16 * K));
+    const i32x4 rsrc_w = buffer_rsrc(wq + n0 * K, (uint32_t)(rows_w * K));
     // Token rows and scales from row m0 on; rows at or past M load as zeros.
     const int64_t rows_x = M - m0 > 0 ? M - m0 : 0;
     const i32x4 rsrc_x = buffer_rsrc(xq + m0 * K, (uint32_t)(rows_x * K));
     const i32x4 rsrc_xs = buffer_rsrc(xs + m0 * KB, (uint32_t)(rows_x * KB * 4));
-    const i32x4 rsrc_ws = buffer_rsrc(ws + (nt * 16 / 128) * KB, (uint32_t)(KB * 4));
+    const i32x4 rsrc_ws = buffer_rsrc(ws + (n0 / 128) * KB, (uint32_t)(KB * 4));
     const int lane_off = slab_lane_offset(lane, K);   // row lane/8, chunk (lane%8) ^ (lane/8)
     const int xs_off = lane * KB * 4;
     uint8_t* my_ring = ring + wave * kWideSlots * kWideSlot;
@@ -414,9 +425,9 @@ __global__ __launch_bounds__(kWideThreads, 1) void w8a8_wide_kernel(
     auto issue = [&](int slot, int kb) {
         const uint32_t base = __builtin_amdgcn_readfirstlane(lds_address(my_ring + slot * kWideSlot));
         const int k_off = __builtin_amdgcn_readfirstlane(kb * 128);
-        const int row8 = __builtin_amdgcn_readfirstlane((int)(8 * K));
-        dma16(base, rsrc_w, lane_off, 0, k_off);
-        dma16(base + 1024, rsrc_w, lane_off, row8, k_off);
+#pragma unroll
+        for (int q = 0; q < 2 * kR; ++q)
+            dma16(base + 1024 * q, rsrc_w, lane_off, __builtin_amdgcn_readfirstlane((int)(8 * q * K)), k_off);
 #pragma unroll
         for (int q = 0; q < 4; ++q)
             dma16(base + kWideOffX + 1024 * q, rsrc_x, lane_off, __builtin_amdgcn_readfirstlane((int)(8 * q * K)), k_off);
@@ -429,22 +440,23 @@ __global__ __launch_bounds__(kWideThreads, 1) void w8a8_wide_kernel(
     for (int s = 0; s < kWideSlots; ++s)
         if (s < nj) issue(s, kw + KW * s);
 
-    f32x4 acc[2];
-    acc[0] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    acc[1] = acc[0];
+    f32x4 acc[kR][2];
+#pragma unroll
+    for (int i = 0; i < kR; ++i) acc[i][0] = acc[i][1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
     int slot = 0;
     for (int j = 0; j < nj; ++j) {
         // Block j is complete once at most the loads of the (up to two)
         // younger blocks are outstanding (loads retire in issue order).
         const int younger = nj - 1 - j;
-        if (younger >= 2) wide_wait_n<2>();
-        else if (younger == 1) wide_wait_n<1>();
-        else wide_wait_n<0>();
+        if (kWideSlots > 2 && younger >= 2) wide_wait_n<SL::kVmem, (kWideSlots > 2 ? 2 : 1)>();
+        else if (younger >= 1) wide_wait_n<SL::kVmem, 1>();
+        else wide_wait_n<SL::kVmem, 0>();
         asm volatile("" ::: "memory");
         const uint8_t* sl = my_ring + slot * kWideSlot;
-        u32x4 a0, a1, b0[2], b1[2];
-        slab_read(sl, r, g, a0, a1);
+        u32x4 a0[kR], a1[kR], b0[2], b1[2];
+#pragma unroll
+        for (int i = 0; i < kR; ++i) slab_read(sl + i * kSlabBytes, r, g, a0[i], a1[i]);
         float xsv[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
@@ -455,14 +467,17 @@ __global__ __launch_bounds__(kWideThreads, 1) void w8a8_wide_kernel(
         // Every operand of block j is in registers before the slot is refilled.
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         if (j + kWideSlots < nj) issue(slot, kw + KW * (j + kWideSlots));
-        const i32x8 a = __builtin_bit_cast(i32x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const i32x8 b = __builtin_bit_cast(i32x8, __builtin_shufflevector(b0[t], b1[t], 0, 1, 2, 3, 4, 5, 6, 7));
-            const f32x4 blk = mfma_e4m3_16x16x128(a, b, zero);
-            const float sc = xsv[t] * wsv;
+        for (int i = 0; i < kR; ++i) {
+            const i32x8 a = __builtin_bit_cast(i32x8, __builtin_shufflevector(a0[i], a1[i], 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[t][i] = __builtin_fmaf(blk[i], sc, acc[t][i]);
+            for (int t = 0; t < 2; ++t) {
+                const i32x8 b = __builtin_bit_cast(i32x8, __builtin_shufflevector(b0[t], b1[t], 0, 1, 2, 3, 4, 5, 6, 7));
+                const f32x4 blk = mfma_e4m3_16x16x128(a, b, zero);
+                const float sc = xsv[t] * wsv;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[i][t][e] = __builtin_fmaf(blk[e], sc, acc[i][t][e]);
+            }
         }
         slot = slot + 1 == kWideSlots ? 0 : slot + 1;
     }
@@ -472,20 +487,26 @@ __global__ __launch_bounds__(kWideThreads, 1) void w8a8_wide_kernel(
     // orders the reuse of the ring.
     __syncthreads();
     float* red = reinterpret_cast<float*>(ring);
-    // Slot of (token tile tt = 2 tg + t, K lane kw): ((kw * kT + tt) * 64 + lane) * 4 floats.
+    // Slot of (row tile i, token tile tt = 2 tg + t, K lane kw):
+    // (((kw * kR + i) * kT + tt) * 64 + lane) * 4 floats.
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-        *reinterpret_cast<f32x4*>(red + ((kw * kT + 2 * tg + t) * kWave + lane) * 4) = acc[t];
+    for (int i = 0; i < kR; ++i)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+            *reinterpret_cast<f32x4*>(red + (((kw * kR + i) * kT + 2 * tg + t) * kWave + lane) * 4) = acc[i][t];
     __syncthreads();
-    // Thread x: lane L = x % 64 of token tiles tt = x / 64, x / 64 + 8, ...
+    // Thread x: lane L = x % 64 of output tiles u = x / 64, x / 64 + 8, ...
+    // (u = i * kT + tt).
     const int L = threadIdx.x % kWave, rr = L & 15, gg = L >> 4;
-    for (int tt = threadIdx.x / kWave; tt < kT; tt += kWideWaves) {
-        f32x4 v = *reinterpret_cast<const f32x4*>(red + (tt * kWave + L) * 4);
+    for (int u = threadIdx.x / kWave; u < kR * kT; u += kWideWaves) {
+        f32x4 v = *reinterpret_cast<const f32x4*>(red + (u * kWave + L) * 4);
 #pragma unroll
-        for (int w = 1; w < KW; ++w) v += *reinterpret_cast<const f32x4*>(red + ((w * kT + tt) * kWave + L) * 4);
-        const int64_t m = 16 * tt + rr;
-        if (m < M) {
-            const int64_t idx = m * N + nt * 16 + 4 * gg;
+        for (int w = 1; w < KW; ++w) v += *reinterpret_cast<const f32x4*>(red + ((w * kR * kT + u) * kWave + L) * 4);
+        const int i = u / kT, tt = u % kT;
+        const int64_t m = 16 * kT * mg + 16 * tt + rr;
+        const int64_t n = n0 + 16 * i + 4 * gg;
+        if (m < M && n < N) {
+            const int64_t idx = m * N + n;
             if (y_dtype == 2) {
                 *reinterpret_cast<f32x4*>(static_cast<float*>(y) + idx) = v;
             } else {
@@ -498,14 +519,39 @@ __global__ __launch_bounds__(kWideThreads, 1) void w8a8_wide_kernel(
     }
 }
 
+// Configuration of the all-token kernel for M (16 kT tokens per workgroup
+// row, kT = 2 or 4) and N: two 16-row weight tiles per workgroup when that
+// still leaves at least 256 workgroups (each workgroup then reads half the
+// token bytes per output), one otherwise.
+struct WideShape {
+    int kr, kt;
+    unsigned groups_n, groups_m;
+};
+static WideShape wide_shape(int64_t M, int64_t N) {
+    WideShape w;
+    w.kt = M <= 32 ? 2 : 4;
+    w.groups_m = (unsigned)((M + 16 * w.kt - 1) / (16 * w.kt));
+    w.kr = (N + 31) / 32 * w.groups_m >= 256 ? 2 : 1;
+    w.groups_n = (unsigned)((N + 16 * w.kr - 1) / (16 * w.kr));
+    return w;
+}
+
 hipError_t launch_w8a8_wide(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
                             void* y, int y_dtype, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
-    if (M < 1 || M > 64 || N % 16 != 0 || K > kTileMaxK) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)(N / 16));
-    if (M <= 32)
-        hipLaunchKernelGGL(w8a8_wide_kernel<2>, grid, dim3(kWideThreads), 0, stream, xq, xs, wq, ws, y, y_dtype, M, N, K);
-    else
-        hipLaunchKernelGGL(w8a8_wide_kernel<4>, grid, dim3(kWideThreads), 0, stream, xq, xs, wq, ws, y, y_dtype, M, N, K);
+    if (M < 1 || M > 128 || N % 16 != 0 || K > kTileMaxK) return hipErrorInvalidValue;
+    const WideShape w = wide_shape(M, N);
+    const dim3 grid(w.groups_n, w.groups_m);
+#define BFP8_LAUNCH_WIDE(R, T)                                                                                 \
+    hipLaunchKernelGGL((w8a8_wide_kernel<R, T>), grid, dim3(kWideThreads), 0, stream, xq, xs, wq, ws, y, y_dtype, \
+                       M, N, K)
+    if (w.kr == 1) {
+        if (w.kt == 2) BFP8_LAUNCH_WIDE(1, 2);
+        else BFP8_LAUNCH_WIDE(1, 4);
+    } else {
+        if (w.kt == 2) BFP8_LAUNCH_WIDE(2, 2);
+        else BFP8_LAUNCH_WIDE(2, 4);
+    }
+#undef BFP8_LAUNCH_WIDE
     return hipGetLastError();
 }
 

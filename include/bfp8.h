@@ -240,8 +240,8 @@ size_t bfp8_workspace_bytes(int op, int64_t M, int64_t N, int64_t K);
  *   m_stream_max  largest M served by the weight-streaming decode kernel
  *                 (W8A8 streams it when K needs no split across workgroups,
  *                 or N < 1024).  W8A8 uses a kernel that reads all tokens per
- *                 16-row weight tile for the other M <= 2 * m_stream_max, and
- *                 for M <= 4 * m_stream_max when N * K <= 2^24 (measured
+ *                 16- or 32-row weight tile for the other M <= 2 * m_stream_max,
+ *                 and for M <= 8 * m_stream_max when K <= 4096 (measured
  *                 faster there), the tiled MFMA kernels otherwise.  W8A16
  *                 blk128 streams M <= m_stream_max and uses its tiled MFMA
  *                 kernel for larger M; blk32 always streams.

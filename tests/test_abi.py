@@ -106,10 +106,12 @@ def test_workspace_sizes(lib):
     assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 32, 1024, 4096) == 0
     assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 32, 12288, 4096) == 0
     assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 64, 4096, 4096) == 0
-    # ... while 12288 x 4096 at M = 64 is tiled (128x64 tiles, K split 4 ways)
-    assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 64, 12288, 4096) == 512 + 96 * 4 * 128 * 64 * 4
+    assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 64, 12288, 4096) == 0
+    # ... while 4096 x 12288 at M = 64 is tiled (128x64 tiles, K split 8 ways)
+    assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 64, 4096, 12288) == 256 + 32 * 8 * 128 * 64 * 4
     # mid M: 64x128 tiles, K split 4 ways -> counters + 4 fp32 partial tiles per output tile
-    assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 100, 4096, 4096) == 256 + 64 * 4 * 64 * 128 * 4
+    assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 100, 4096, 8192) == 256 + 64 * 4 * 64 * 128 * 4
+    assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 100, 4096, 4096) == 0    # all-token kernel
     assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 64, 384, 640) == 0      # K too short to split
     assert bfp8.bfp8_workspace_bytes(bfp8.OP_QUANT_ACT_1X128, 1, 4096, 4096) == 0
 
@@ -168,7 +170,7 @@ def _w8a8(M=4, N=512, K=512, y_dtype=0, xq=A, ws_ptr=C, y=Y, workspace=None, wby
     (dict(M=1, N=512, K=4096), 5),                    # split-K plan needs a workspace
     (dict(M=64, N=256, K=(1 << 23) + 128), 2),        # K limit (tiled kernel)
     (dict(M=1, N=256, K=(1 << 23) + 128), 2),         # K limit (streaming kernel)
-    (dict(M=100, N=1024, K=4096), 5),                 # mid-M split-K plan needs a workspace
+    (dict(M=100, N=1024, K=8192), 5),                 # mid-M split-K plan needs a workspace
 ])
 def test_w8a8_validation(lib, kw, expect):
     assert lib.bfp8_gemm_w8a8_blk128(*_w8a8(**kw)) == expect

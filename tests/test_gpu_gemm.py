@@ -74,20 +74,23 @@ def test_w8a8_split_k_narrow_projection(gpu_lib, M):
 
 @pytest.mark.parametrize("M,N,K", [(1, 1024, 4096), (5, 2048, 4096), (16, 1024, 4096), (17, 1024, 4096),
                                    (24, 1024, 4096), (32, 4096, 4096), (33, 4096, 4096), (50, 1024, 4096),
-                                   (64, 4096, 4096), (32, 12288, 256), (20, 16, 8192)])
+                                   (64, 4096, 4096), (32, 12288, 256), (20, 16, 8192), (20, 8208, 256),
+                                   (65, 8192, 512), (100, 4096, 1024), (128, 1040, 2048)])
 def test_w8a8_wide_all_tokens(gpu_lib, M, N, K):
-    """The kernel that holds every token per 16-row weight tile (no
-    workspace): M <= 16 where streaming would split K, and 16 < M <= 64;
-    ragged M inside the last token tile, a single 16-row weight tile, and K
-    spread unevenly over the eight waves' rings."""
+    """The kernel that holds every token per 16- or 32-row weight tile (no
+    workspace): M <= 16 where streaming would split K, 16 < M <= 32, and
+    M <= 128 with K <= 4096; ragged M inside the last token tile and in a
+    second token group, a single 16-row weight tile, a 32-row tile with only
+    16 live rows (N = 8208), and K spread unevenly over the eight waves'
+    rings."""
     assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, M, N, K) == 0
     _w8a8_check(M, N, K, 900 + M, what="wide")
 
 
 @pytest.mark.parametrize("M,N,K,shape", [
-    (40, 8192, 4096, "128x64, 4 splits"),
-    (65, 1024, 4096, "64x128, 8 splits"),
-    (100, 1024, 4096, "64x128, 8 splits"),
+    (40, 8192, 8192, "128x64, 4 splits"),
+    (65, 1024, 8192, "64x128, 16 splits"),
+    (100, 1024, 8192, "64x128, 16 splits"),
     (200, 2048, 2176, "64x128, 4 splits, last split shorter"),
     (300, 1040, 1024, "64x128, 2 splits, ragged N"),
     (1000, 4096, 1024, "128x128"),
