@@ -129,6 +129,7 @@ size_t bfp8_workspace_bytes(int op, int64_t M, int64_t N, int64_t K) {
         case BFP8_OP_GEMM_W8A8_BLK128:
             return w8a8_workspace(M, N, K);
         case BFP8_OP_GEMM_W8A16_BLK128:
+            if (w8a16_wide(M, N, K)) return 0;
             if (M > kStreamMaxM) return K <= kTileMaxK ? tile16_workspace_bytes(M, N, K) : 0;
             return stream_workspace_bytes(plan_stream(M, N, K));
         case BFP8_OP_GEMM_W8A16_BLK32_UE8M0:
@@ -183,6 +184,8 @@ bfp8_status bfp8_gemm_w8a16_blk128(const void* x, int x_dtype, const uint8_t* wq
     bfp8_status st = check_gemm(x, wq, ws, y, y_dtype, M, N, K, 16, need, workspace, workspace_bytes);
     if (st != BFP8_OK) return st;
     if (!is16(x_dtype)) return BFP8_E_DTYPE;
+    if (w8a16_wide(M, N, K))   // every token per workgroup, weights widened in registers
+        return launched(launch_w8a16_wide(x, x_dtype == BFP8_BF16, wq, ws, y, y_dtype, M, N, K, as_stream(stream)));
     if (M > kStreamMaxM)     // tiled MFMA kernel, weights widened in registers
         return launched(launch_w8a16_tile(x, x_dtype == BFP8_BF16, wq, ws, y, y_dtype, M, N, K, workspace,
                                           as_stream(stream)));

@@ -79,6 +79,20 @@ hipError_t launch_w8a8_stream_quant(const void* x, bool x_bf16, const uint8_t* w
                                     void* workspace, hipStream_t stream);
 hipError_t launch_w8a16_tile(const void* x, bool x_bf16, const uint8_t* wq, const float* ws, void* y,
                              int y_dtype, int64_t M, int64_t N, int64_t K, void* workspace, hipStream_t stream);
+// W8A16 blk128 dispatch: the streaming kernel for M <= 16; the all-token
+// kernel (launch_w8a16_wide) for 16 < M <= 32 and for M <= 64 on at most
+// 2^24 weights, both with K <= 4096 (measured, us: M = 17 / 32 on
+// 4096 x 4096 8.0 / 8.6 against 13.3 / 13.4 tiled, M = 64 12.7 vs 14.0;
+// 1024 x 4096 M = 64 10.1 vs 11.4; 12288 x 4096 M = 32 25.4 vs 26.9; the
+// tiled kernel wins at 4096 x 12288 from M = 32 and on 12288 x 4096 from
+// M = 64); the tiled kernel otherwise.
+inline bool w8a16_wide(int64_t M, int64_t N, int64_t K) {
+    return M > kStreamMaxM && K <= 4096 &&
+           (M <= 2 * kStreamMaxM || (M <= 4 * kStreamMaxM && N * K <= ((int64_t)1 << 24)));
+}
+// 1 <= M <= 64, N a multiple of 16, K <= kTileMaxK; needs no workspace.
+hipError_t launch_w8a16_wide(const void* x, bool x_bf16, const uint8_t* wq, const float* ws, void* y, int y_dtype,
+                             int64_t M, int64_t N, int64_t K, hipStream_t stream);
 hipError_t launch_w8a16_blk128_stream(const void* x, bool x_bf16, const uint8_t* wq, const float* ws,
                                       void* y, int y_dtype, int64_t M, int64_t N, int64_t K,
                                       void* workspace, hipStream_t stream);

@@ -328,6 +328,163 @@ __global__ __launch_bounds__(kStreamThreads) void w8a16_blk32_stream_lds_kernel(
     stream_finish(acc, red, y, y_dtype, M, N, nt, 0, splits, split, n_tiles, partials, counters);
 }
 
+// ------------------------------------------------- W8A16 all-token kernel ----
+// The W8A16 blk128 product with every token per workgroup (see w8a16_wide
+// for where it is used): a workgroup owns 16 weight rows and 16 kT tokens
+// (kT = 2 or 4 token tiles) over all of K, so the weights are read once and
+// nothing is split across workgroups.  Eight waves: wave w takes token tile tg = w % kT and
+// the 128-K blocks kw, kw + KW, ... (kw = w / kT, KW = 8 / kT).  Each wave owns
+// a ring of three LDS slots; a slot holds one block: the 16 weight rows
+// (2 KB, E4M3), the wave's 16 token rows (16-bit, 256 bytes each) and the
+// weight scale, all by direct-to-LDS 16-byte loads of whole lines.  Token
+// row R of a tile keeps its 16-byte chunk c at position c ^ sw(R), sw(R) =
+// ((R & 3) << 2) | (R >> 2), so the 16 rows of one MFMA read hit 16 distinct
+// bank groups.  The weights are widened in registers (decode8) and feed four
+// 16x16x32 MFMAs per block; the exponent-bias difference is folded into the
+// block scale, as in the streaming kernel.
+constexpr int kW16WideWaves = 8;
+constexpr int kW16WideThreads = kW16WideWaves * kWave;
+constexpr int kW16WideSlots = 3;
+constexpr int kW16OffX = kSlabBytes;                      // 16 token rows x 256 bytes
+constexpr int kW16OffWs = kW16OffX + 16 * 256;
+constexpr int kW16Slot = (kW16OffWs + 4 + 255) / 256 * 256;
+constexpr int kW16Vmem = 2 + 4 + 1;                        // load instructions per block
+static_assert(kW16WideWaves * kW16WideSlots * kW16Slot <= 160 * 1024, "LDS ring");
+
+template <int Y>
+__device__ __forceinline__ void w16_wait_n() {
+    constexpr int n = Y * kW16Vmem;
+    __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+__device__ __forceinline__ int w16_sw(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+
+template <bool kXBf16, int kT>
+__global__ __launch_bounds__(kW16WideThreads, 1) void w8a16_wide_kernel(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq, const float* __restrict__ ws,
+    void* __restrict__ y, int y_dtype, int64_t M, int64_t N, int64_t K) {
+    constexpr int KW = kW16WideWaves / kT;
+    static_assert(kT == 2 || kT == 4, "token tiles");
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[kW16WideWaves * kW16WideSlots * kW16Slot];
+    const int64_t nt = blockIdx.x, mg = blockIdx.y;
+    const int KB = (int)(K / 128);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
+    const int tg = wave % kT, kw = wave / kT;
+    const int r = lane & 15, g = lane >> 4;
+    const int64_t m0 = 16 * kT * mg + 16 * tg;         // first token of this wave's tile
+
+    const i32x4 rsrc_w = buffer_rsrc(wq + nt * 16 * K, (uint32_t)(16 * K));
+    const int64_t rows_x = M - m0 > 0 ? (M - m0 < 16 ? M - m0 : 16) : 0;
+    const i32x4 rsrc_x = buffer_rsrc(x + m0 * K, (uint32_t)(rows_x * K * 2));
+    const i32x4 rsrc_ws = buffer_rsrc(ws + (nt * 16 / 128) * KB, (uint32_t)(KB * 4));
+    const int lane_off_w = slab_lane_offset(lane, K);
+    // Token-row loads: instruction q covers rows 4q .. 4q + 3; lane l fills
+    // position l % 16 of row 4q + l / 16 with logical chunk (l % 16) ^ sw(row).
+    int x_off[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int row = 4 * q + (lane >> 4);
+        x_off[q] = (int)(row * K * 2) + (((lane & 15) ^ w16_sw(row)) << 4);
+    }
+    uint8_t* my_ring = ring + wave * kW16WideSlots * kW16Slot;
+    const float bias_fold = kXBf16 ? 0x1p120f : 0x1p8f;
+
+    auto issue = [&](int slot, int kb) {
+        const uint32_t base = __builtin_amdgcn_readfirstlane(lds_address(my_ring + slot * kW16Slot));
+        const int k_off = __builtin_amdgcn_readfirstlane(kb * 128);
+        const int k_off_x = __builtin_amdgcn_readfirstlane(kb * 256);
+        dma16(base, rsrc_w, lane_off_w, 0, k_off);
+        dma16(base + 1024, rsrc_w, lane_off_w, __builtin_amdgcn_readfirstlane((int)(8 * K)), k_off);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) dma16(base + kW16OffX + 1024 * q, rsrc_x, x_off[q], 0, k_off_x);
+        if (lane == 0) dma4(base + kW16OffWs, rsrc_ws, 0, __builtin_amdgcn_readfirstlane(kb * 4));
+    };
+
+    const int nj = kw < KB ? (KB - 1 - kw) / KW + 1 : 0;
+#pragma unroll
+    for (int s = 0; s < kW16WideSlots; ++s)
+        if (s < nj) issue(s, kw + KW * s);
+
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+    const int sw = w16_sw(r);
+    int slot = 0;
+    for (int j = 0; j < nj; ++j) {
+        const int younger = nj - 1 - j;
+        if (younger >= 2) w16_wait_n<2>();
+        else if (younger == 1) w16_wait_n<1>();
+        else w16_wait_n<0>();
+        asm volatile("" ::: "memory");
+        const uint8_t* sl = my_ring + slot * kW16Slot;
+        u32x4 wa0, wa1;
+        slab_read(sl, r, g, wa0, wa1);
+        // MFMA i takes K offsets 16 g + 8 i (i < 2) and 64 + 16 g + 8 (i - 2):
+        // 16-bit chunks 2 g + i and 8 + 2 g + (i - 2) of the token row.
+        u32x4 xv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int c = i < 2 ? 2 * g + i : 8 + 2 * g + (i - 2);
+            xv[i] = *reinterpret_cast<const u32x4*>(sl + kW16OffX + r * 256 + ((c ^ sw) << 4));
+        }
+        const float wsv = *reinterpret_cast<const float*>(sl + kW16OffWs);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        if (j + kW16WideSlots < nj) issue(slot, kw + KW * (j + kW16WideSlots));
+        const uint32_t q8[8] = {wa0[0], wa0[1], wa0[2], wa0[3], wa1[0], wa1[1], wa1[2], wa1[3]};
+        f32x4 blk = zero;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const u32x4 a = decode8<kXBf16>(q8[2 * i], q8[2 * i + 1]);
+            blk = kXBf16 ? mfma_bf16_16x16x32(a, xv[i], blk) : mfma_f16_16x16x32(a, xv[i], blk);
+        }
+        const float sc = wsv * bias_fold;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(blk[e], sc, acc[e]);
+        slot = slot + 1 == kW16WideSlots ? 0 : slot + 1;
+    }
+
+    __syncthreads();
+    float* red = reinterpret_cast<float*>(ring);
+    *reinterpret_cast<f32x4*>(red + ((kw * kT + tg) * kWave + lane) * 4) = acc;
+    __syncthreads();
+    const int L = threadIdx.x % kWave, rr = L & 15, gg = L >> 4;
+    for (int tt = threadIdx.x / kWave; tt < kT; tt += kW16WideWaves) {
+        f32x4 v = *reinterpret_cast<const f32x4*>(red + (tt * kWave + L) * 4);
+#pragma unroll
+        for (int w = 1; w < KW; ++w) v += *reinterpret_cast<const f32x4*>(red + ((w * kT + tt) * kWave + L) * 4);
+        const int64_t m = 16 * kT * mg + 16 * tt + rr;
+        if (m < M) {
+            const int64_t idx = m * N + nt * 16 + 4 * gg;
+            if (y_dtype == 2) {
+                *reinterpret_cast<f32x4*>(static_cast<float*>(y) + idx) = v;
+            } else {
+                uint32_t h[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) h[e] = y_dtype == 0 ? float_to_bf16_bits(v[e]) : float_to_f16_bits(v[e]);
+                *reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + idx) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+            }
+        }
+    }
+}
+
+hipError_t launch_w8a16_wide(const void* x, bool x_bf16, const uint8_t* wq, const float* ws, void* y, int y_dtype,
+                             int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+    if (M < 1 || M > 64 || N % 16 != 0 || K > kTileMaxK) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)(N / 16));
+    const uint16_t* xh = static_cast<const uint16_t*>(x);
+#define BFP8_LAUNCH_W16(B, T)                                                                                \
+    hipLaunchKernelGGL((w8a16_wide_kernel<B, T>), grid, dim3(kW16WideThreads), 0, stream, xh, wq, ws, y, y_dtype, \
+                       M, N, K)
+    if (x_bf16) {
+        if (M <= 32) BFP8_LAUNCH_W16(true, 2);
+        else BFP8_LAUNCH_W16(true, 4);
+    } else {
+        if (M <= 32) BFP8_LAUNCH_W16(false, 2);
+        else BFP8_LAUNCH_W16(false, 4);
+    }
+#undef BFP8_LAUNCH_W16
+    return hipGetLastError();
+}
+
 hipError_t launch_w8a16_blk128_stream(const void* x, bool x_bf16, const uint8_t* wq, const float* ws,
                                       void* y, int y_dtype, int64_t M, int64_t N, int64_t K,
                                       void* workspace, hipStream_t stream) {

@@ -226,6 +226,24 @@ def test_w8a16_blk128(gpu_lib, M, xdtype):
     assert_16bit_bar(y16, y32, y0, "bf16" if xdtype == torch.bfloat16 else "f16", f"w8a16 M={M}")
 
 
+@pytest.mark.parametrize("xdtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("M,N,K", [(17, 1024, 4096), (32, 4096, 4096), (50, 1024, 4096), (64, 4096, 4096),
+                                   (24, 12288, 512), (20, 16, 4096)])
+def test_w8a16_all_tokens(gpu_lib, M, N, K, xdtype):
+    """16 < M <= 64 with K <= 4096: every token per 16-row weight tile, no
+    workspace; ragged M, a single weight tile, K spread over the waves."""
+    assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A16_BLK128, M, N, K) == 0
+    say("w8a16 all-token", xdtype, f"M={M} N={N} K={K}")
+    x = inputs.activations(M, K, workload=640 + M, stream=K, outliers=True, dtype=xdtype)
+    wq, ws = oracle.quantize_weight_128x128(f32(inputs.weights_bf16(N, K, workload=640 + N, stream=K)))
+    y0 = oracle.gemm_w8a16_blk128(f32(x), wq, ws)
+    xd, wqd, wsd = x.cuda(), dev(wq), dev(ws)
+    y32 = run_w8a16(xd, wqd, wsd, torch.float32)
+    assert_fp32_bar(y32, y0, f"w8a16 all-token M={M}")
+    y16 = run_w8a16(xd, wqd, wsd, xdtype)
+    assert_16bit_bar(y16, y32, y0, "bf16" if xdtype == torch.bfloat16 else "f16", f"w8a16 all-token M={M}")
+
+
 @pytest.mark.parametrize("M", [1, 3, 16])
 def test_w8a16_blk128_long_k(gpu_lib, M):
     """K = 12288 on 4096 rows: six 128-K blocks per wave, two passes of up to
@@ -240,14 +258,16 @@ def test_w8a16_blk128_long_k(gpu_lib, M):
 
 
 @pytest.mark.parametrize("xdtype", [torch.bfloat16, torch.float16])
-def test_w8a16_blk128_one_hot_all_codes_exact(gpu_lib, xdtype):
-    """x one-hot 1.0: Y[:, n] = E4M3(wq[n, k]) * ws exactly, subnormal codes included."""
-    N, K, M = 256, 256, 4
+@pytest.mark.parametrize("M", [4, 40])
+def test_w8a16_blk128_one_hot_all_codes_exact(gpu_lib, xdtype, M):
+    """x one-hot 1.0: Y[:, n] = E4M3(wq[n, k]) * ws exactly, subnormal codes
+    included (streaming kernel at M = 4, all-token kernel at M = 40)."""
+    N, K = 256, 256
     wq = np.zeros((N, K), np.uint8)
     wq[:254, :] = FINITE_CODES[:, None]
     ws = np.array([[0.5, 2.0], [0.25, 4.0]], np.float32)
     for k in (0, 100, 129, 255):
-        say("w8a16 one-hot", xdtype, k)
+        say("w8a16 one-hot", xdtype, M, k)
         x = torch.zeros((M, K), dtype=xdtype)
         x[:, k] = 1.0
         y = run_w8a16(x.cuda(), dev(wq), dev(ws), torch.float32)
@@ -256,7 +276,7 @@ def test_w8a16_blk128_one_hot_all_codes_exact(gpu_lib, xdtype):
 
 
 @pytest.mark.parametrize("xdtype", [torch.bfloat16, torch.float16])
-@pytest.mark.parametrize("M,N,K", [(40, 1024, 4096), (100, 1040, 4096), (300, 2048, 2176)])
+@pytest.mark.parametrize("M,N,K", [(40, 1024, 8192), (100, 1040, 4096), (300, 2048, 2176)])
 def test_w8a16_tile_split_k(gpu_lib, M, N, K, xdtype):
     """Tiled W8A16 with ragged M/N tiles and split K (workspace), run twice on
     one workspace: bar met, second run bit-identical."""
