@@ -57,7 +57,7 @@ __global__ __launch_bounds__(kStreamThreads) void w8a16_blk32_stream_kernel(
     void* __restrict__ y, int y_dtype, int64_t M, int64_t N, int64_t K,
     int64_t n_tiles, int64_t splits, int64_t kb_per_split,
     float* __restrict__ partials, uint32_t* __restrict__ counters) {
-    __shared__ float red[kStreamWaves * 256];
+    __shared__ float red[kStreamRedWords];
     const int64_t nt = blockIdx.x, split = blockIdx.y, mt = blockIdx.z;
     const int64_t KB = K / 128, K32 = K / 32;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
@@ -148,9 +148,9 @@ __global__ __launch_bounds__(kStreamThreads) void w8a16_blk128_stream_lds_kernel
     int64_t n_tiles, int64_t splits, int64_t kb_per_split,
     float* __restrict__ partials, uint32_t* __restrict__ counters) {
     constexpr bool kRegX = kMp == 16;   // sixteen live token rows: register loads, no LDS rows
-    __shared__ float red[kStreamWaves * 256];
     __shared__ __attribute__((aligned(16))) uint8_t xrows[kStreamWaves][kW8A16LdsChunk][kRegX ? 16 : kMp * kXRowStride];
     __shared__ __attribute__((aligned(1024))) uint8_t wslab[kStreamWaves][kW8A16LdsChunk][kSlabBytes];
+    float* red = slab_scratch(&wslab[0][0][0]);   // used after the last block only
     const int64_t nt = blockIdx.x, split = blockIdx.y;
     const int64_t KB = K / 128;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
@@ -229,6 +229,7 @@ __global__ __launch_bounds__(kStreamThreads) void w8a16_blk128_stream_lds_kernel
             }
         }
     }
+    __syncthreads();   // every wave is done with the slabs that red overlays
     stream_finish(acc, red, y, y_dtype, M, N, nt, 0, splits, split, n_tiles, partials, counters);
 }
 
@@ -244,9 +245,9 @@ __global__ __launch_bounds__(kStreamThreads) void w8a16_blk32_stream_lds_kernel(
     int64_t n_tiles, int64_t splits, int64_t kb_per_split,
     float* __restrict__ partials, uint32_t* __restrict__ counters) {
     constexpr bool kRegX = kMp == 16;   // sixteen live token rows: register loads, no LDS rows
-    __shared__ float red[kStreamWaves * 256];
     __shared__ __attribute__((aligned(16))) uint8_t xrows[kStreamWaves][kW8A16LdsChunk][kRegX ? 16 : kMp * kXRowStride];
     __shared__ __attribute__((aligned(1024))) uint8_t wslab[kStreamWaves][kW8A16LdsChunk][kSlabBytes];
+    float* red = slab_scratch(&wslab[0][0][0]);   // used after the last block only
     const int64_t nt = blockIdx.x, split = blockIdx.y;
     const int64_t KB = K / 128, K32 = K / 32;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
@@ -325,6 +326,7 @@ __global__ __launch_bounds__(kStreamThreads) void w8a16_blk32_stream_lds_kernel(
             }
         }
     }
+    __syncthreads();   // every wave is done with the slabs that red overlays
     stream_finish(acc, red, y, y_dtype, M, N, nt, 0, splits, split, n_tiles, partials, counters);
 }
 

@@ -99,9 +99,9 @@ __global__ __launch_bounds__(kStreamThreads) void w8a8_stream_lds_kernel(
     int64_t n_tiles, int64_t splits, int64_t kb_per_split,
     float* __restrict__ partials, uint32_t* __restrict__ counters) {
     constexpr int kRowsBytes = (kMp + 1) / 2 * 256;
-    __shared__ float red[kStreamWaves * 256];
     __shared__ __attribute__((aligned(1024))) uint8_t xrows[kStreamWaves][kCodesLdsChunk][kRowsBytes];
     __shared__ __attribute__((aligned(1024))) uint8_t wslab[kStreamWaves][kCodesLdsChunk][kSlabBytes];
+    float* red = slab_scratch(&wslab[0][0][0]);   // used after the last block only
     const int64_t nt = blockIdx.x, split = blockIdx.y;
     const int64_t KB = K / 128;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
@@ -160,6 +160,7 @@ __global__ __launch_bounds__(kStreamThreads) void w8a8_stream_lds_kernel(
             }
         }
     }
+    __syncthreads();   // every wave is done with the slabs that red overlays
     stream_finish(acc, red, y, y_dtype, M, N, nt, 0, splits, split, n_tiles, partials, counters);
 }
 
@@ -257,9 +258,9 @@ __global__ __launch_bounds__(kStreamThreads) void w8a8_stream_quant_kernel(
     constexpr int kL = kWave / kMp;          // lanes per token
     constexpr int kV = 128 / kL;             // values per lane (2 Mp)
     static_assert(kFusedChunk == 2, "the token-row wait counts two slab loads per block");
-    __shared__ float red[kStreamWaves * 256];
     __shared__ __attribute__((aligned(16))) uint8_t xrows[kStreamWaves][kFusedChunk][kMp * kXRowStride];
     __shared__ __attribute__((aligned(1024))) uint8_t wslab[kStreamWaves][kFusedChunk][kSlabBytes];
+    float* red = slab_scratch(&wslab[0][0][0]);   // used after the last block only
     const int64_t nt = blockIdx.x, split = blockIdx.y;
     const int64_t KB = K / 128;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
@@ -351,6 +352,7 @@ __global__ __launch_bounds__(kStreamThreads) void w8a8_stream_quant_kernel(
             }
         }
     }
+    __syncthreads();   // every wave is done with the slabs that red overlays
     stream_finish(acc, red, y, y_dtype, M, N, nt, 0, splits, split, n_tiles, partials, counters);
 }
 
