@@ -252,11 +252,15 @@ __device__ __forceinline__ void tile_of_block(int64_t b, int64_t tiles_n, int64_
 
 // Store eight consecutive outputs y[idx .. idx+7] (lo = the first four):
 // one 16-byte store for 16-bit outputs, two for fp32.  idx is a multiple of
-// 8 and, with N % 16 == 0, the eight lie in one row.
+// 8 and, with N % 16 == 0, the eight lie in one row.  Non-temporal stores:
+// the output is not read again by this kernel, and with every workgroup of
+// a one-round grid storing at the same time the streaming hint measured 2 %
+// faster at M = N = K = 4096 (69.8 -> 68.4 us; a store through LDS in whole
+// 128-byte lines measured no faster than these 64-byte row pieces).
 __device__ __forceinline__ void store8(void* y, int y_dtype, int64_t idx, f32x4 lo, f32x4 hi) {
     if (y_dtype == 2) {
-        *reinterpret_cast<f32x4*>(static_cast<float*>(y) + idx) = lo;
-        *reinterpret_cast<f32x4*>(static_cast<float*>(y) + idx + 4) = hi;
+        __builtin_nontemporal_store(lo, reinterpret_cast<f32x4*>(static_cast<float*>(y) + idx));
+        __builtin_nontemporal_store(hi, reinterpret_cast<f32x4*>(static_cast<float*>(y) + idx + 4));
     } else {
         uint32_t h[8];
 #pragma unroll
@@ -264,8 +268,9 @@ __device__ __forceinline__ void store8(void* y, int y_dtype, int64_t idx, f32x4 
             h[e] = y_dtype == 0 ? float_to_bf16_bits(lo[e]) : float_to_f16_bits(lo[e]);
             h[e + 4] = y_dtype == 0 ? float_to_bf16_bits(hi[e]) : float_to_f16_bits(hi[e]);
         }
-        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(y) + idx) =
-            u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+        __builtin_nontemporal_store(
+            u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)},
+            reinterpret_cast<u32x4*>(static_cast<uint16_t*>(y) + idx));
     }
 }
 
