@@ -27,7 +27,8 @@
 //
 // Tile shapes ([ADA] "One tile doesn't fit all M"): 256x256, 256x128 or
 // 128x128 by estimated time (plan_tile) among those that occupy most CUs;
-// below that, 64x128 (or 128x64 for M <= 64) with K split over several
+// below that, for long K 128x128 with four waves and K split 2 or 4 ways,
+// else 64x128 (or 128x64 for M <= 64) with K split over several
 // workgroups so that about one workgroup per CU exists.  Split partial tiles go to the
 // workspace in fp32 and the last workgroup of a tile sums them in split
 // order (no float atomics, identical from run to run), with the same
@@ -108,6 +109,9 @@ using Cfg128 = TileCfg<128, 128, 2, 4, false>;    // 64 x 32, 4 stages
 using Cfg256x128 = TileCfg<256, 128, 4, 2, false>;   // 64 x 64, 3 stages
 using Cfg64x128 = TileCfg<64, 128, 2, 4, true>;   // 32 x 32, 6 stages
 using Cfg128x64 = TileCfg<128, 64, 4, 2, true>;   // 32 x 32, 6 stages
+// Long K at mid M: 128 x 128 with four waves (wave tile 64 x 64, sixteen
+// MFMAs per block) and K split so that the tiles fill the CUs once.
+using Cfg128w4 = TileCfg<128, 128, 2, 2, true>;
 // W8A16 (16-bit activations): wave tiles 32 x 64 and 32 x 32 (four waves
 // across the weight rows, so each decoded weight fragment feeds kTj MFMAs).
 template <int X> using Cfg16_128 = TileCfg<128, 128, 4, 2, true, X>;   // 3 stages
@@ -610,7 +614,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void w8a8_tile_kernel(
 
 namespace {
 
-enum class TileShape { k256, k256x128, k128, k64x128, k128x64, k16_256, k16_128, k16_64 };
+enum class TileShape { k256, k256x128, k128, k64x128, k128x64, k128w4, k16_256, k16_128, k16_64 };
 
 struct TilePlan {
     TileShape shape;
@@ -621,7 +625,8 @@ TilePlan make_plan(TileShape s, int64_t bn, int64_t bm, int64_t M, int64_t N, in
     TilePlan p{s, bn, bm, (N + bn - 1) / bn, (M + bm - 1) / bm, 1, 0};
     const int64_t KB = K / 128;
     int64_t splits = 1;
-    if (s == TileShape::k64x128 || s == TileShape::k128x64 || s == TileShape::k16_128 || s == TileShape::k16_64) {
+    if (s == TileShape::k64x128 || s == TileShape::k128x64 || s == TileShape::k128w4 || s == TileShape::k16_128 ||
+        s == TileShape::k16_64) {
         // About one workgroup per CU, each with at least 4 K blocks.
         while (p.tiles_n * p.tiles_m * splits < kCUs && KB / (splits * 2) >= 4) splits *= 2;
     }
@@ -652,6 +657,16 @@ TilePlan plan_tile(int64_t M, int64_t N, int64_t K) {
         }
     }
     if (best >= 0) return cand[best];
+    // Long K (at least 64 blocks) with 64 or 128 tiles of 128 x 128: four
+    // waves per tile, K split 4 or 2 ways (measured at K = 12288, N = 4096:
+    // M = 256 33.9 vs 38.9 us, M = 512 48.3 vs 63.8 us; N = 2048, M = 512
+    // 32.2 vs 37.2 us; K = 8192, M = 512 36.9 vs 43.9 us; at K = 4096 and
+    // with 32 tiles, K split 8 ways, the small tiles stay ahead).
+    {
+        const int64_t tiles = cand[2].tiles_n * cand[2].tiles_m;
+        if (M > 128 && K >= 64 * 128 && (tiles == kCUs / 4 || tiles == kCUs / 2))
+            return make_plan(TileShape::k128w4, 128, 128, M, N, K);
+    }
     if (M <= 64) return make_plan(TileShape::k128x64, 128, 64, M, N, K);
     return make_plan(TileShape::k64x128, 64, 128, M, N, K);
 }
@@ -740,6 +755,9 @@ hipError_t launch_w8a8_tile(const uint8_t* xq, const float* xs, const uint8_t* w
             break;
         case TileShape::k128x64:
             launch<Cfg128x64>(p, xq, xs, wq, ws, y, y_dtype, M, N, K, partials, counters, stream);
+            break;
+        case TileShape::k128w4:
+            launch<Cfg128w4>(p, xq, xs, wq, ws, y, y_dtype, M, N, K, partials, counters, stream);
             break;
         default:
             break;

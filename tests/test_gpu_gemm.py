@@ -94,6 +94,8 @@ def test_w8a8_wide_all_tokens(gpu_lib, M, N, K):
     (200, 2048, 2176, "64x128, 4 splits, last split shorter"),
     (300, 1040, 1024, "64x128, 2 splits, ragged N"),
     (1000, 4096, 1024, "128x128"),
+    (400, 2048, 8192, "128x128 four waves, 4 splits, ragged M"),
+    (512, 4096, 8192, "128x128 four waves, 2 splits"),
     (2000, 4000, 1024, "256x128, ragged M and N"),
 ])
 def test_w8a8_tile_shapes_and_split_k(gpu_lib, M, N, K, shape):
