@@ -20,36 +20,48 @@
 namespace bfp8 {
 
 constexpr int kQuantActThreads = 256;
+constexpr int kQuantActRows = 2;   // token rows per thread
 
-// Grid: one workgroup per (row, run of 16 groups); 16 threads per group,
-// one thread per 8 input values.
+// Grid: one workgroup per (pair of rows, run of 16 groups); 16 threads per
+// group, one thread per 8 input values of each of its two rows.  Both rows'
+// loads are issued before either is quantised, and the codes are written
+// with non-temporal stores (nothing reads them again before the GEMM):
+// 11.4 -> 9.9 us at M = K = 4096 (one row per thread with ordinary stores
+// before; four or eight rows per thread, or non-temporal loads, were slower).
 __global__ __launch_bounds__(kQuantActThreads) void quant_act_1x128_kernel(
     const uint16_t* __restrict__ x, int bf16, int64_t M, int64_t K, int64_t G, int64_t blocks_per_row,
     uint8_t* __restrict__ xq, float* __restrict__ xs) {
     // 32-bit index arithmetic (the launcher keeps the grid below 2^32): the
     // 64-bit division took some fifty scalar instructions per wave.
     const uint32_t mb = (uint32_t)blockIdx.x / (uint32_t)blocks_per_row;   // uniform per workgroup
-    const int64_t m = mb;
+    const int64_t m0 = (int64_t)mb * kQuantActRows;
     const int64_t g = (int64_t)((uint32_t)blockIdx.x - mb * (uint32_t)blocks_per_row) * (kQuantActThreads / 16) +
                       (threadIdx.x >> 4);
     const int lane16 = threadIdx.x & 15;
     const int64_t col = g * 128 + lane16 * 8;
     const bool valid = g < G && col < K;            // K % 8 == 0: a chunk is all in or all out
 
-    const u32x4 raw = valid ? load_16B(x + m * K + col) : u32x4{0u, 0u, 0u, 0u};
-    float v[8];
-    unpack8(raw, bf16 != 0, v);
-    float amax = 0.0f;
+    u32x4 raw[kQuantActRows];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
-    amax = group16_max(amax);                       // all 16 lanes of a group are in one wave
+    for (int r = 0; r < kQuantActRows; ++r)
+        raw[r] = valid && m0 + r < M ? load_16B(x + (m0 + r) * K + col) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int r = 0; r < kQuantActRows; ++r) {
+        const int64_t m = m0 + r;
+        float v[8];
+        unpack8(raw[r], bf16 != 0, v);
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+        amax = group16_max(amax);                   // all 16 lanes of a group are in one wave
 
-    const float s = amax / 448.0f;
-    uint32_t lo, hi;
-    quantize8(v, raw, s, lo, hi);
-    if (valid) {
-        *reinterpret_cast<uint2*>(xq + m * K + col) = make_uint2(lo, hi);
-        if (lane16 == 0) xs[m * G + g] = s;
+        const float s = amax / 448.0f;
+        uint32_t lo, hi;
+        quantize8(v, raw[r], s, lo, hi);
+        if (valid && m < M) {
+            __builtin_nontemporal_store(u32x2{lo, hi}, reinterpret_cast<u32x2*>(xq + m * K + col));
+            if (lane16 == 0) xs[m * G + g] = s;
+        }
     }
 }
 
@@ -145,8 +157,9 @@ hipError_t launch_quant_act_1x128(const void* x, bool bf16, int64_t M, int64_t K
                                   uint8_t* xq, float* xs, hipStream_t stream) {
     const int64_t G = (K + 127) / 128;
     const int64_t blocks_per_row = (G + kQuantActThreads / 16 - 1) / (kQuantActThreads / 16);
-    if (M * blocks_per_row >= (int64_t(1) << 32)) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(quant_act_1x128_kernel, dim3((unsigned)(M * blocks_per_row)), dim3(kQuantActThreads), 0,
+    const int64_t row_blocks = (M + kQuantActRows - 1) / kQuantActRows;
+    if (row_blocks * blocks_per_row >= (int64_t(1) << 32)) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(quant_act_1x128_kernel, dim3((unsigned)(row_blocks * blocks_per_row)), dim3(kQuantActThreads), 0,
                        stream, static_cast<const uint16_t*>(x), (int)bf16, M, K, G, blocks_per_row, xq, xs);
     return hipGetLastError();
 }
