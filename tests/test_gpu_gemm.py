@@ -75,7 +75,8 @@ def test_w8a8_split_k_narrow_projection(gpu_lib, M):
 @pytest.mark.parametrize("M,N,K", [(1, 1024, 4096), (5, 2048, 4096), (16, 1024, 4096), (17, 1024, 4096),
                                    (24, 1024, 4096), (32, 4096, 4096), (33, 4096, 4096), (50, 1024, 4096),
                                    (64, 4096, 4096), (32, 12288, 256), (20, 16, 8192), (20, 8208, 256),
-                                   (65, 8192, 512), (100, 4096, 1024), (128, 1040, 2048)])
+                                   (65, 8192, 512), (100, 4096, 1024), (128, 1040, 2048), (20, 64, 128),
+                                   (128, 8192, 128)])
 def test_w8a8_wide_all_tokens(gpu_lib, M, N, K):
     """The kernel that holds every token per 16- or 32-row weight tile (no
     workspace): M <= 16 where streaming would split K, 16 < M <= 32, and
@@ -230,7 +231,7 @@ def test_w8a16_blk128(gpu_lib, M, xdtype):
 
 @pytest.mark.parametrize("xdtype", [torch.bfloat16, torch.float16])
 @pytest.mark.parametrize("M,N,K", [(17, 1024, 4096), (32, 4096, 4096), (50, 1024, 4096), (64, 4096, 4096),
-                                   (24, 12288, 512), (20, 16, 4096)])
+                                   (24, 12288, 512), (20, 16, 4096), (20, 64, 128)])
 def test_w8a16_all_tokens(gpu_lib, M, N, K, xdtype):
     """16 < M <= 64 with K <= 4096: every token per 16-row weight tile, no
     workspace; ragged M, a single weight tile, K spread over the waves."""
