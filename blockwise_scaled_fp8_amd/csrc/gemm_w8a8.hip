@@ -41,11 +41,18 @@ StreamPlan plan_stream(int64_t M, int64_t N, int64_t K) {
     p.n_tiles = N / kStreamRows;
     p.m_tiles = (M + 15) / 16;
     const int64_t KB = K / 128;
-    // Enough workgroups to give each of the 256 CUs one, while at least half
-    // of a workgroup's waves still get a 128-K block.
+    // K is split over workgroups only when it is long (more than 64 blocks,
+    // more than two passes of two blocks per wave): up to K = 8192 a single
+    // pass with every load in flight at once beats the split-K hand-off even
+    // with few workgroups (measured, us, K split vs not: N = 1024, K = 4096,
+    // M = 1 / 8 / 16: 5.4 / 5.6 / 5.8 vs 3.3 / 4.0 / 4.5; N = 512, M = 1:
+    // 4.7 vs 3.3; N = 1024, K = 8192: 6.2 vs 4.4), while at K = 12288 the
+    // serial passes cost more (N = 1024, M = 16: 7.5 vs 11.5).  Then: enough
+    // workgroups to give each of the 256 CUs one, while at least half of a
+    // workgroup's waves still get a 128-K block.
     const int64_t tiles = p.n_tiles * p.m_tiles;
     int64_t splits = 1;
-    while (tiles * splits < 256 && 2 * (KB / (splits * 2)) >= kStreamWaves) splits *= 2;
+    while (KB > 64 && tiles * splits < 256 && 2 * (KB / (splits * 2)) >= kStreamWaves) splits *= 2;
     p.splits = splits;
     p.kb_per_split = (KB + splits - 1) / splits;
     return p;

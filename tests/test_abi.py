@@ -67,15 +67,16 @@ def test_limits(lib):
 def test_quant_gemm_workspace_and_limits(lib):
     op = bfp8.OP_QUANT_GEMM_W8A8_BLK128
     # quantised in registers (M <= 8 where the codes call streams): the
-    # streaming kernel's split-K plan only (N = 512: counters of 32 16x16
-    # tiles, then 4 fp32 partial tiles each, K split 4 ways)
-    for M, N, K in [(1, 4096, 4096), (8, 512, 4096), (4, 512, 512)]:
+    # streaming kernel's split-K plan only (N = 512, K = 12288: counters of 32
+    # 16x16 tiles, then 8 fp32 partial tiles each, K split 8 ways)
+    for M, N, K in [(1, 4096, 4096), (8, 512, 12288), (4, 512, 512), (8, 1024, 4096)]:
         assert bfp8.bfp8_workspace_bytes(op, M, N, K) == bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, M, N, K)
-    assert bfp8.bfp8_workspace_bytes(op, 8, 512, 4096) == 256 + 32 * 4 * 256 * 4
+    assert bfp8.bfp8_workspace_bytes(op, 8, 512, 12288) == 256 + 32 * 8 * 256 * 4
+    assert bfp8.bfp8_workspace_bytes(op, 8, 1024, 4096) == 0     # K up to 8192 is never split
     # staged codes: W8A8 workspace + M*K codes + M*K/128 scales, each 256-aligned
     r = lambda v: (v + 255) // 256 * 256
     for M, N, K in [(4096, 4096, 4096), (64, 4096, 4096), (17, 384, 640), (9, 1024, 4096), (16, 4096, 4096),
-                    (8, 1024, 4096)]:
+                    (8, 1024, 12288)]:
         t = bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, M, N, K)
         assert bfp8.bfp8_workspace_bytes(op, M, N, K) == r(t) + r(M * K) + r(4 * M * (K // 128))
     assert bfp8.bfp8_get_limits(op)["m_stream_max"] == 16
@@ -97,8 +98,9 @@ def test_quant_gemm_validation(lib, args, expect):
 def test_workspace_sizes(lib):
     # o_proj decode needs no split-K; a narrow projection does
     assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 1, 4096, 4096) == 0
-    assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 1, 512, 4096) > 0
-    assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 1, 1024, 4096) == 0   # all-token kernel
+    assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 1, 512, 12288) > 0
+    assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 1, 1024, 4096) == 0   # K not split up to 8192
+    assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 1, 1024, 12288) == 0  # all-token kernel
     assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 4096, 1024, 4096) == 0   # 128x128 tiles
     assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 4096, 4096, 4096) == 0   # 256x256 tiles
     # 16 < M <= 32 (and M <= 64 on at most 2^24 weights): one workgroup per 16
@@ -167,7 +169,7 @@ def _w8a8(M=4, N=512, K=512, y_dtype=0, xq=A, ws_ptr=C, y=Y, workspace=None, wby
     (dict(K=0), 2),
     (dict(y_dtype=7), 3),
     (dict(y=MISALIGNED), 4),
-    (dict(M=1, N=512, K=4096), 5),                    # split-K plan needs a workspace
+    (dict(M=1, N=512, K=12288), 5),                   # split-K plan needs a workspace
     (dict(M=64, N=256, K=(1 << 23) + 128), 2),        # K limit (tiled kernel)
     (dict(M=1, N=256, K=(1 << 23) + 128), 2),         # K limit (streaming kernel)
     (dict(M=100, N=1024, K=8192), 5),                 # mid-M split-K plan needs a workspace
@@ -177,9 +179,9 @@ def test_w8a8_validation(lib, kw, expect):
 
 
 def test_w8a8_workspace_too_small(lib):
-    need = bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 1, 512, 4096)
-    assert lib.bfp8_gemm_w8a8_blk128(*_w8a8(M=1, N=512, K=4096, workspace=A, wbytes=need - 1)) == 5
-    assert lib.bfp8_gemm_w8a8_blk128(*_w8a8(M=1, N=512, K=4096, workspace=MISALIGNED, wbytes=need, y=0)) == 1
+    need = bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 1, 512, 12288)
+    assert lib.bfp8_gemm_w8a8_blk128(*_w8a8(M=1, N=512, K=12288, workspace=A, wbytes=need - 1)) == 5
+    assert lib.bfp8_gemm_w8a8_blk128(*_w8a8(M=1, N=512, K=12288, workspace=MISALIGNED, wbytes=need, y=0)) == 1
 
 
 @pytest.mark.parametrize("x_dtype,y_dtype,N,expect", [

@@ -59,12 +59,12 @@ def test_w8a8_weight_scale_rows_straddle(gpu_lib, M, N):
 
 @pytest.mark.parametrize("M", [1, 4, 16])
 def test_w8a8_split_k_narrow_projection(gpu_lib, M):
-    """N=512, K=4096 streams with K split over workgroups; run twice (counters re-arm)."""
-    assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, M, 512, 4096) > 0
-    xq, xs, wq, ws = _w8a8_inputs(M, 512, 4096, 500 + M)
+    """N=512, K=12288 streams with K split over workgroups; run twice (counters re-arm)."""
+    assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, M, 512, 12288) > 0
+    xq, xs, wq, ws = _w8a8_inputs(M, 512, 12288, 500 + M)
     y0 = oracle.gemm_w8a8_blk128(xq, xs, wq, ws)
     d = [dev(a) for a in (xq, xs, wq, ws)]
-    wsb = workspace(bfp8.OP_GEMM_W8A8_BLK128, M, 512, 4096)
+    wsb = workspace(bfp8.OP_GEMM_W8A8_BLK128, M, 512, 12288)
     say("w8a8 split-K", M)
     y1 = run_w8a8(*d, torch.float32, wsb)
     y2 = run_w8a8(*d, torch.float32, wsb)
@@ -72,7 +72,7 @@ def test_w8a8_split_k_narrow_projection(gpu_lib, M):
     assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 1024, 4096), (5, 2048, 4096), (16, 1024, 4096), (17, 1024, 4096),
+@pytest.mark.parametrize("M,N,K", [(1, 1024, 12288), (5, 2048, 12288), (16, 1024, 12288), (17, 1024, 4096),
                                    (24, 1024, 4096), (32, 4096, 4096), (33, 4096, 4096), (50, 1024, 4096),
                                    (64, 4096, 4096), (32, 12288, 256), (20, 16, 8192), (20, 8208, 256),
                                    (65, 8192, 512), (100, 4096, 1024), (128, 1040, 2048), (20, 64, 128),
@@ -429,7 +429,8 @@ def test_blk32_one_hot_all_codes_all_exponents_exact(gpu_lib, out):
 
 
 def test_blk32_split_k_and_determinism(gpu_lib):
-    M, N, K = 4, 1024, 7168
+    M, N, K = 4, 1024, 12288
+    assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A16_BLK32_UE8M0, M, N, K) > 0
     x, wq, e8 = _blk32_inputs(M, N, K, 31)
     y0 = oracle.gemm_w8a16_blk32_ue8m0(f32(x), wq, e8)
     wsb = workspace(bfp8.OP_GEMM_W8A16_BLK32_UE8M0, M, N, K)
