@@ -32,8 +32,8 @@ struct StreamPlan {
 StreamPlan plan_stream(int64_t M, int64_t N, int64_t K);
 
 // W8A8 dispatch (codes in), from the projection sweep:
-//  * the streaming kernel for M <= 16 when it needs no split of K (at least
-//    256 weight-row tiles), or when N < 1024;
+//  * the streaming kernel for M <= 16 when it needs no split of K, or when
+//    N < 1024, and for M <= 64 when its workgroups fit one round unsplit;
 //  * the all-token kernel (launch_w8a8_wide: every token per workgroup, no
 //    split) for the other M <= 32, and for M <= 128 when K <= 4096;
 //    measured (us): 1024 x 4096 at M = 1 / 16: 4.3 / 4.4 against 5.3 / 5.5
@@ -45,7 +45,15 @@ StreamPlan plan_stream(int64_t M, int64_t N, int64_t K);
 //    and M >= 64 the tiled kernels win (M = 64: 19.2 vs 29.0 us);
 //  * the tiled kernels otherwise.
 inline bool w8a8_streams(int64_t M, int64_t N, int64_t K) {
-    return M <= kStreamMaxM && (N < 1024 || K > kTileMaxK || plan_stream(M, N, K).splits == 1);
+    if (M <= kStreamMaxM) return N < 1024 || K > kTileMaxK || plan_stream(M, N, K).splits == 1;
+    // More than one token tile (one workgroup per weight-row tile and token
+    // tile, the weights read once per token tile): on small projections,
+    // where every such workgroup fits in one round on the CUs without a
+    // split of K (measured, us: 1024 x 4096, M = 32 / 64: 4.6 / 4.7 against
+    // 4.9 / 7.3 for the all-token kernel; at 4096 x 4096, M = 32, 9.7 vs 7.5).
+    if (M > 4 * kStreamMaxM || K > kTileMaxK) return false;
+    const StreamPlan p = plan_stream(M, N, K);
+    return p.splits == 1 && p.n_tiles * p.m_tiles <= 256;
 }
 inline bool w8a8_wide(int64_t M, int64_t N, int64_t K) {
     if (K > kTileMaxK || w8a8_streams(M, N, K)) return false;

@@ -22,7 +22,8 @@
 // "The fix", the latent-bug paragraph).
 //
 // Three kernels, chosen by M ([ADA] "One tile doesn't fit all M"):
-//   * stream (M <= 16, see w8a8_streams): weight streaming.  One workgroup per 16 weight rows
+//   * stream (M <= 16, or up to 64 on small projections; see w8a8_streams):
+//     weight streaming.  One workgroup per 16 weight rows and 16-token tile
 //     (and per split of K), sixteen waves each holding its 128-K blocks of
 //     weight loads in flight, tokens padded to 16 on the MFMA column axis.
 //   * wide (M <= 64, see w8a8_wide): one workgroup per 16 weight rows and
@@ -109,20 +110,22 @@ __global__ __launch_bounds__(kStreamThreads) void w8a8_stream_lds_kernel(
     __shared__ __attribute__((aligned(1024))) uint8_t xrows[kStreamWaves][kCodesLdsChunk][kRowsBytes];
     __shared__ __attribute__((aligned(1024))) uint8_t wslab[kStreamWaves][kCodesLdsChunk][kSlabBytes];
     float* red = slab_scratch(&wslab[0][0][0]);   // used after the last block only
-    const int64_t nt = blockIdx.x, split = blockIdx.y;
+    // Token tile mt = blockIdx.z: tokens m0 .. m0 + Mt - 1.
+    const int64_t nt = blockIdx.x, split = blockIdx.y, mt = blockIdx.z;
+    const int64_t m0 = 16 * mt, Mt = M - m0 < 16 ? M - m0 : 16;
     const int64_t KB = K / 128;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
     const int r = lane & 15, g = lane >> 4;
-    const bool r_ok = r < kMp && r < M;
+    const bool r_ok = r < kMp && r < Mt;
     const int r_row = r < kMp ? r : 0;
     const int64_t kb_begin = split * kb_per_split;
     const int64_t kb_end = kb_begin + kb_per_split < KB ? kb_begin + kb_per_split : KB;
 
     const i32x4 rsrc_w = buffer_rsrc(wq + nt * 16 * K, (uint32_t)(16 * K));
-    const i32x4 rsrc_x = buffer_rsrc(xq, (uint32_t)(M * K));
+    const i32x4 rsrc_x = buffer_rsrc(xq + m0 * K, (uint32_t)(Mt * K));
     const int lane_off_w = slab_lane_offset(lane, K);
     const float* ws_row = ws + (nt * 16 / 128) * KB;
-    const float* xs_row = xs + (r_ok ? r : 0) * KB;   // rows past M read row 0, zeroed at use
+    const float* xs_row = xs + (m0 + (r_ok ? r : 0)) * KB;   // rows past M read row m0, zeroed at use
 
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
     const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -168,7 +171,7 @@ __global__ __launch_bounds__(kStreamThreads) void w8a8_stream_lds_kernel(
         }
     }
     __syncthreads();   // every wave is done with the slabs that red overlays
-    stream_finish(acc, red, y, y_dtype, M, N, nt, 0, splits, split, n_tiles, partials, counters);
+    stream_finish(acc, red, y, y_dtype, M, N, nt, mt, splits, split, n_tiles, partials, counters);
 }
 
 // ------------------------------------------- activation quant fused in ----
@@ -567,12 +570,12 @@ hipError_t launch_w8a8_wide(const uint8_t* xq, const float* xs, const uint8_t* w
 hipError_t launch_w8a8_stream(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
                               void* y, int y_dtype, int64_t M, int64_t N, int64_t K,
                               void* workspace, hipStream_t stream) {
-    if (M > kStreamMaxM) return hipErrorInvalidValue;
     const StreamPlan p = plan_stream(M, N, K);
+    if (p.m_tiles > 65535) return hipErrorInvalidValue;
     uint32_t* counters;
     float* partials;
     stream_workspace_parts(p, workspace, counters, partials);
-    const dim3 grid((unsigned)p.n_tiles, (unsigned)p.splits, 1u);
+    const dim3 grid((unsigned)p.n_tiles, (unsigned)p.splits, (unsigned)p.m_tiles);   // one 16-token tile per z
     {
 #define BFP8_LAUNCH_LDS(MP)                                                                                    \
     hipLaunchKernelGGL(w8a8_stream_lds_kernel<MP>, grid, dim3(kStreamThreads), 0, stream, xq, xs, wq, ws, y, y_dtype, \

@@ -237,9 +237,12 @@ size_t bfp8_workspace_bytes(int op, int64_t M, int64_t N, int64_t K);
  *   k_multiple    K must be a multiple of this.
  *   n_multiple    N must be a multiple of this.
  *   align_bytes   required alignment of every device pointer.
- *   m_stream_max  largest M served by the weight-streaming decode kernel
- *                 (W8A8 streams it when K needs no split across workgroups,
- *                 or N < 1024).  W8A8 uses a kernel that reads all tokens per
+ *   m_stream_max  largest M always served by the weight-streaming decode
+ *                 kernel (W8A8 streams it when K needs no split across
+ *                 workgroups, or N < 1024; W8A8 also streams up to
+ *                 4 * m_stream_max, one workgroup per 16-token tile, when
+ *                 those workgroups fit one round on the CUs without a split
+ *                 of K).  W8A8 uses a kernel that reads all tokens per
  *                 16- or 32-row weight tile for the other M <= 2 * m_stream_max,
  *                 and for M <= 8 * m_stream_max when K <= 4096 (measured
  *                 faster there), the tiled MFMA kernels otherwise.  W8A16

@@ -76,14 +76,15 @@ def test_w8a8_split_k_narrow_projection(gpu_lib, M):
                                    (24, 1024, 4096), (32, 4096, 4096), (33, 4096, 4096), (50, 1024, 4096),
                                    (64, 4096, 4096), (32, 12288, 256), (20, 16, 8192), (20, 8208, 256),
                                    (65, 8192, 512), (100, 4096, 1024), (128, 1040, 2048), (20, 64, 128),
-                                   (128, 8192, 128)])
+                                   (128, 8192, 128), (64, 1024, 4096), (40, 2048, 1024), (61, 512, 8192)])
 def test_w8a8_wide_all_tokens(gpu_lib, M, N, K):
-    """The kernel that holds every token per 16- or 32-row weight tile (no
-    workspace): M <= 16 where streaming would split K, 16 < M <= 32, and
-    M <= 128 with K <= 4096; ragged M inside the last token tile and in a
-    second token group, a single 16-row weight tile, a 32-row tile with only
-    16 live rows (N = 8208), and K spread unevenly over the eight waves'
-    rings."""
+    """The paths that need no workspace for M <= 128: the kernel that holds
+    every token per 16- or 32-row weight tile (M <= 16 where streaming would
+    split K, 16 < M <= 32, M <= 128 with K <= 4096) and the streaming kernel
+    over 16-token tiles on small projections (grid.z, e.g. N = 1024 or 16 at
+    M <= 64); ragged M inside the last token tile and in a second token
+    group, a single 16-row weight tile, a 32-row tile with only 16 live rows
+    (N = 8208), and K spread unevenly over the waves."""
     assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, M, N, K) == 0
     _w8a8_check(M, N, K, 900 + M, what="wide")
 
