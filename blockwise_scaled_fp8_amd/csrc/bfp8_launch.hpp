@@ -35,14 +35,18 @@ StreamPlan plan_stream(int64_t M, int64_t N, int64_t K);
 //  * the streaming kernel for M <= 16 when it needs no split of K, or when
 //    N < 1024, and for M <= 64 when its workgroups fit one round unsplit;
 //  * the all-token kernel (launch_w8a8_wide: every token per workgroup, no
-//    split) for the other M <= 32, and for M <= 128 when K <= 4096;
+//    split) for the other M <= 32, and when K <= 4096 and M * N <= 2^19
+//    (M <= 128 at N = 4096, M <= 512 at N = 1024);
 //    measured (us): 1024 x 4096 at M = 1 / 16: 4.3 / 4.4 against 5.3 / 5.5
 //    streamed with K split 4 ways; at M = 32: 4096 x 4096 6.7, 1024 x 4096
 //    4.9, 12288 x 4096 16.5, 4096 x 12288 17.1 against 11.6, 9.8, 22.5 and
 //    17.8 tiled; at M = 64: 4096 x 4096 9.7 vs 12.1, 1024 x 4096 7.3 vs
 //    10.3, 12288 x 4096 24.1 vs 24.8; at M = 128: 4096 x 4096 11.7 vs 14.6,
-//    1024 x 4096 7.5 vs 11.5, 12288 x 4096 34.2 vs 34.5; with K = 12288
-//    and M >= 64 the tiled kernels win (M = 64: 19.2 vs 29.0 us);
+//    1024 x 4096 7.5 vs 11.5, 12288 x 4096 34.2 vs 34.5; 1024 x 4096 at
+//    M = 256 / 512 7.9 / 9.4 vs 11.8 / 12.9, 2048 x 4096 at M = 256 10.9 vs
+//    13.3, but 4096 x 4096 at M = 256 21.2 vs 18.0 and 2048 x 4096 at
+//    M = 512 19.4 vs 16.9; with K = 12288 and M >= 64 the tiled kernels win
+//    (M = 64: 19.2 vs 29.0 us);
 //  * the tiled kernels otherwise.
 inline bool w8a8_streams(int64_t M, int64_t N, int64_t K) {
     if (M <= kStreamMaxM) return N < 1024 || K > kTileMaxK || plan_stream(M, N, K).splits == 1;
@@ -57,7 +61,7 @@ inline bool w8a8_streams(int64_t M, int64_t N, int64_t K) {
 }
 inline bool w8a8_wide(int64_t M, int64_t N, int64_t K) {
     if (K > kTileMaxK || w8a8_streams(M, N, K)) return false;
-    return M <= 2 * kStreamMaxM || (M <= 8 * kStreamMaxM && K <= 4096);
+    return M <= 2 * kStreamMaxM || (K <= 4096 && M * N <= ((int64_t)1 << 19));
 }
 // Workspace bytes of a streaming plan: tile counters, then fp32 partial tiles.
 size_t stream_workspace_bytes(const StreamPlan& p);
@@ -72,7 +76,7 @@ hipError_t launch_dequant_weight(const uint8_t* wq, const float* scales, int blo
 hipError_t launch_w8a8_tile(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
                             void* y, int y_dtype, int64_t M, int64_t N, int64_t K, void* workspace,
                             hipStream_t stream);
-// 1 <= M <= 128, N a multiple of 16, K <= kTileMaxK; needs no workspace.
+// M >= 1, N a multiple of 16, K <= kTileMaxK; needs no workspace.
 hipError_t launch_w8a8_wide(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
                             void* y, int y_dtype, int64_t M, int64_t N, int64_t K, hipStream_t stream);
 hipError_t launch_w8a8_stream(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,

@@ -369,7 +369,7 @@ __global__ __launch_bounds__(kStreamThreads) void w8a8_stream_quant_kernel(
 // ------------------------------------------------------------ wide stream ----
 // All-token kernel (see w8a8_wide for where it is used): a workgroup owns
 // 16 kR weight rows (kR = 1 or 2 MFMA row tiles) and 16 kT tokens (kT = 2
-// or 4 token tiles; grid.y covers M above that) over all of K, so the
+// or 4 token tiles; grid.y covers the tokens beyond) over all of K, so the
 // weights are read once and no split-K hand-off is needed.  Eight waves:
 // wave w takes token tiles 2 tg, 2 tg + 1 (tg = w % G, G = kT / 2) and the
 // 128-K blocks kw, kw + KW, ... (kw = w / G, KW = 8 / G).  Each wave owns a
@@ -550,8 +550,9 @@ static WideShape wide_shape(int64_t M, int64_t N) {
 
 hipError_t launch_w8a8_wide(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
                             void* y, int y_dtype, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
-    if (M < 1 || M > 128 || N % 16 != 0 || K > kTileMaxK) return hipErrorInvalidValue;
+    if (M < 1 || N % 16 != 0 || K > kTileMaxK) return hipErrorInvalidValue;
     const WideShape w = wide_shape(M, N);
+    if (w.groups_m > 65535) return hipErrorInvalidValue;
     const dim3 grid(w.groups_n, w.groups_m);
 #define BFP8_LAUNCH_WIDE(R, T)                                                                                 \
     hipLaunchKernelGGL((w8a8_wide_kernel<R, T>), grid, dim3(kWideThreads), 0, stream, xq, xs, wq, ws, y, y_dtype, \

@@ -244,8 +244,8 @@ size_t bfp8_workspace_bytes(int op, int64_t M, int64_t N, int64_t K);
  *                 those workgroups fit one round on the CUs without a split
  *                 of K).  W8A8 uses a kernel that reads all tokens per
  *                 16- or 32-row weight tile for the other M <= 2 * m_stream_max,
- *                 and for M <= 8 * m_stream_max when K <= 4096 (measured
- *                 faster there), the tiled MFMA kernels otherwise.  W8A16
+ *                 and when K <= 4096 and M * N <= 2^19 (measured faster
+ *                 there), the tiled MFMA kernels otherwise.  W8A16
  *                 blk128 streams M <= m_stream_max and uses its tiled MFMA
  *                 kernel for larger M; blk32 always streams.
  * Any output pointer may be NULL.

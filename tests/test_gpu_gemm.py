@@ -76,7 +76,8 @@ def test_w8a8_split_k_narrow_projection(gpu_lib, M):
                                    (24, 1024, 4096), (32, 4096, 4096), (33, 4096, 4096), (50, 1024, 4096),
                                    (64, 4096, 4096), (32, 12288, 256), (20, 16, 8192), (20, 8208, 256),
                                    (65, 8192, 512), (100, 4096, 1024), (128, 1040, 2048), (20, 64, 128),
-                                   (128, 8192, 128), (64, 1024, 4096), (40, 2048, 1024), (61, 512, 8192)])
+                                   (128, 8192, 128), (64, 1024, 4096), (40, 2048, 1024), (61, 512, 8192),
+                                   (300, 1024, 2048), (512, 1024, 512)])
 def test_w8a8_wide_all_tokens(gpu_lib, M, N, K):
     """The paths that need no workspace for M <= 128: the kernel that holds
     every token per 16- or 32-row weight tile (M <= 16 where streaming would
@@ -93,8 +94,8 @@ def test_w8a8_wide_all_tokens(gpu_lib, M, N, K):
     (40, 8192, 8192, "128x64, 4 splits"),
     (65, 1024, 8192, "64x128, 16 splits"),
     (100, 1024, 8192, "64x128, 16 splits"),
-    (200, 2048, 2176, "64x128, 4 splits, last split shorter"),
-    (300, 1040, 1024, "64x128, 2 splits, ragged N"),
+    (200, 4096, 2176, "64x128, 2 splits, last split shorter"),
+    (300, 2064, 1024, "64x128, 2 splits, ragged N"),
     (1000, 4096, 1024, "128x128"),
     (400, 2048, 8192, "128x128 four waves, 4 splits, ragged M"),
     (512, 4096, 8192, "128x128 four waves, 2 splits"),
