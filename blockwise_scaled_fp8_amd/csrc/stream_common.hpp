@@ -75,13 +75,6 @@ __device__ __forceinline__ void slab_issue(uint8_t* slab, i32x4 rsrc, int lane_o
     dma16(lds + 1024, rsrc, lane_off, __builtin_amdgcn_readfirstlane((int)(8 * K)), k_off);
 }
 
-// Wait for every outstanding vector-memory load of this wave (the slab
-// loads are invisible to the compiler's own waits); also a compiler
-// barrier, so no LDS read of a slab moves above it.
-__device__ __forceinline__ void wait_all_loads() {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-}
-
 __device__ __forceinline__ void slab_read(const uint8_t* slab, int r, int g, u32x4& lo, u32x4& hi) {
     lo = *reinterpret_cast<const u32x4*>(slab + r * 128 + ((g ^ (r & 7)) << 4));
     hi = *reinterpret_cast<const u32x4*>(slab + r * 128 + (((g + 4) ^ (r & 7)) << 4));
