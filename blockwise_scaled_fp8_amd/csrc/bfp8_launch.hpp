@@ -92,17 +92,17 @@ hipError_t launch_w8a8_stream_quant(const void* x, bool x_bf16, const uint8_t* w
 hipError_t launch_w8a16_tile(const void* x, bool x_bf16, const uint8_t* wq, const float* ws, void* y,
                              int y_dtype, int64_t M, int64_t N, int64_t K, void* workspace, hipStream_t stream);
 // W8A16 blk128 dispatch: the streaming kernel for M <= 16; the all-token
-// kernel (launch_w8a16_wide) for 16 < M <= 32 and for M <= 64 on at most
-// 2^24 weights, both with K <= 4096 (measured, us: M = 17 / 32 on
-// 4096 x 4096 8.0 / 8.6 against 13.3 / 13.4 tiled, M = 64 12.7 vs 14.0;
-// 1024 x 4096 M = 64 10.1 vs 11.4; 12288 x 4096 M = 32 25.4 vs 26.9; the
-// tiled kernel wins at 4096 x 12288 from M = 32 and on 12288 x 4096 from
-// M = 64); the tiled kernel otherwise.
+// kernel (launch_w8a16_wide) for 16 < M <= 256 when K <= 4096 and either
+// M <= 32 or M * N <= 2^19; the tiled kernel otherwise.  Measured, us, all
+// with K = 4096: N = 4096 M = 32 / 64 / 128 9.6 / 11.9 / 17.8 against
+// 13.7 / 14.2 / 20.4 tiled; N = 1024 M = 64 / 128 / 256 7.0 / 7.5 / 9.8
+// against 11.5 / 17.0 / 18.1; N = 12288 M = 32 22.3 vs 26.3, while from
+// M = 64 there (27.5 vs 33.5) and from K = 12288 the tiled kernel wins.
 inline bool w8a16_wide(int64_t M, int64_t N, int64_t K) {
-    return M > kStreamMaxM && K <= 4096 &&
-           (M <= 2 * kStreamMaxM || (M <= 4 * kStreamMaxM && N * K <= ((int64_t)1 << 24)));
+    return M > kStreamMaxM && M <= 16 * kStreamMaxM && K <= 4096 &&
+           (M <= 2 * kStreamMaxM || M * N <= ((int64_t)1 << 19));
 }
-// 1 <= M <= 64, N a multiple of 16, K <= kTileMaxK; needs no workspace.
+// M >= 1, N a multiple of 16, K <= kTileMaxK; needs no workspace.
 hipError_t launch_w8a16_wide(const void* x, bool x_bf16, const uint8_t* wq, const float* ws, void* y, int y_dtype,
                              int64_t M, int64_t N, int64_t K, hipStream_t stream);
 hipError_t launch_w8a16_blk128_stream(const void* x, bool x_bf16, const uint8_t* wq, const float* ws,

@@ -332,40 +332,49 @@ __global__ __launch_bounds__(kStreamThreads) void w8a16_blk32_stream_lds_kernel(
 
 // ------------------------------------------------- W8A16 all-token kernel ----
 // The W8A16 blk128 product with every token per workgroup (see w8a16_wide
-// for where it is used): a workgroup owns 16 weight rows and 16 kT tokens
-// (kT = 2 or 4 token tiles) over all of K, so the weights are read once and
-// nothing is split across workgroups.  Eight waves: wave w takes token tile tg = w % kT and
-// the 128-K blocks kw, kw + KW, ... (kw = w / kT, KW = 8 / kT).  Each wave owns
-// a ring of three LDS slots; a slot holds one block: the 16 weight rows
-// (2 KB, E4M3), the wave's 16 token rows (16-bit, 256 bytes each) and the
-// weight scale, all by direct-to-LDS 16-byte loads of whole lines.  Token
-// row R of a tile keeps its 16-byte chunk c at position c ^ sw(R), sw(R) =
-// ((R & 3) << 2) | (R >> 2), so the 16 rows of one MFMA read hit 16 distinct
-// bank groups.  The weights are widened in registers (decode8) and feed four
-// 16x16x32 MFMAs per block; the exponent-bias difference is folded into the
-// block scale, as in the streaming kernel.
+// for where it is used): a workgroup owns 16 kR weight rows (kR = 1 or 2)
+// and 16 kT tokens (kT = 2 or 4 token tiles; grid.y walks further groups of
+// 16 kT tokens) over all of K, so nothing is split across workgroups.  Eight
+// waves: wave w takes token tile tg = w % kT and the 128-K blocks kw,
+// kw + KW, ... (kw = w / kT, KW = 8 / kT).  Each wave owns a ring of LDS
+// slots (three for kR = 1, two for kR = 2); a slot holds one block: the
+// 16 kR weight rows (2 KB each 16, E4M3), the wave's 16 token rows (16-bit,
+// 256 bytes each) and the weight scale, all by direct-to-LDS 16-byte loads
+// of whole lines.  Token row R of a tile keeps its 16-byte chunk c at
+// position c ^ sw(R), sw(R) = ((R & 3) << 2) | (R >> 2), so the 16 rows of
+// one MFMA read hit 16 distinct bank groups.  The weights are widened in
+// registers (decode8) and feed four 16x16x32 MFMAs per block and row tile;
+// the exponent-bias difference is folded into the block scale, as in the
+// streaming kernel.  The waves' partial sums meet in LDS once, at the end,
+// and are added in K-lane order.
 constexpr int kW16WideWaves = 8;
 constexpr int kW16WideThreads = kW16WideWaves * kWave;
-constexpr int kW16WideSlots = 3;
-constexpr int kW16OffX = kSlabBytes;                      // 16 token rows x 256 bytes
-constexpr int kW16OffWs = kW16OffX + 16 * 256;
-constexpr int kW16Slot = (kW16OffWs + 4 + 255) / 256 * 256;
-constexpr int kW16Vmem = 2 + 4 + 1;                        // load instructions per block
-static_assert(kW16WideWaves * kW16WideSlots * kW16Slot <= 160 * 1024, "LDS ring");
+template <int kR>
+struct W16Slot {
+    static constexpr int kOffX = kR * kSlabBytes;                  // 16 token rows x 256 bytes
+    static constexpr int kOffWs = kOffX + 16 * 256;
+    static constexpr int kBytes = (kOffWs + 4 + 255) / 256 * 256;
+    static constexpr int kSlotsFit = 160 * 1024 / (kW16WideWaves * kBytes);
+    static constexpr int kSlots = kSlotsFit > 3 ? 3 : kSlotsFit;
+    static constexpr int kVmem = 2 * kR + 4 + 1;                   // load instructions per block
+    static_assert(kSlots >= 2, "LDS ring");
+};
 
-template <int Y>
+template <int V, int Y>
 __device__ __forceinline__ void w16_wait_n() {
-    constexpr int n = Y * kW16Vmem;
+    constexpr int n = Y * V;
     __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
 __device__ __forceinline__ int w16_sw(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
 
-template <bool kXBf16, int kT>
+template <bool kXBf16, int kT, int kR>
 __global__ __launch_bounds__(kW16WideThreads, 1) void w8a16_wide_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq, const float* __restrict__ ws,
     void* __restrict__ y, int y_dtype, int64_t M, int64_t N, int64_t K) {
     constexpr int KW = kW16WideWaves / kT;
+    using SL = W16Slot<kR>;
+    constexpr int kW16WideSlots = SL::kSlots, kW16Slot = SL::kBytes, kW16OffX = SL::kOffX, kW16OffWs = SL::kOffWs;
     static_assert(kT == 2 || kT == 4, "token tiles");
     __shared__ __attribute__((aligned(1024))) uint8_t ring[kW16WideWaves * kW16WideSlots * kW16Slot];
     const int64_t nt = blockIdx.x, mg = blockIdx.y;
@@ -375,10 +384,12 @@ __global__ __launch_bounds__(kW16WideThreads, 1) void w8a16_wide_kernel(
     const int r = lane & 15, g = lane >> 4;
     const int64_t m0 = 16 * kT * mg + 16 * tg;         // first token of this wave's tile
 
-    const i32x4 rsrc_w = buffer_rsrc(wq + nt * 16 * K, (uint32_t)(16 * K));
+    const int64_t n0 = 16 * kR * nt;
+    const int64_t rows_w = N - n0 < 16 * kR ? N - n0 : 16 * kR;
+    const i32x4 rsrc_w = buffer_rsrc(wq + n0 * K, (uint32_t)(rows_w * K));
     const int64_t rows_x = M - m0 > 0 ? (M - m0 < 16 ? M - m0 : 16) : 0;
     const i32x4 rsrc_x = buffer_rsrc(x + m0 * K, (uint32_t)(rows_x * K * 2));
-    const i32x4 rsrc_ws = buffer_rsrc(ws + (nt * 16 / 128) * KB, (uint32_t)(KB * 4));
+    const i32x4 rsrc_ws = buffer_rsrc(ws + (n0 / 128) * KB, (uint32_t)(KB * 4));
     const int lane_off_w = slab_lane_offset(lane, K);
     // Token-row loads: instruction q covers rows 4q .. 4q + 3; lane l fills
     // position l % 16 of row 4q + l / 16 with logical chunk (l % 16) ^ sw(row).
@@ -395,8 +406,9 @@ __global__ __launch_bounds__(kW16WideThreads, 1) void w8a16_wide_kernel(
         const uint32_t base = __builtin_amdgcn_readfirstlane(lds_address(my_ring + slot * kW16Slot));
         const int k_off = __builtin_amdgcn_readfirstlane(kb * 128);
         const int k_off_x = __builtin_amdgcn_readfirstlane(kb * 256);
-        dma16(base, rsrc_w, lane_off_w, 0, k_off);
-        dma16(base + 1024, rsrc_w, lane_off_w, __builtin_amdgcn_readfirstlane((int)(8 * K)), k_off);
+#pragma unroll
+        for (int q = 0; q < 2 * kR; ++q)
+            dma16(base + 1024 * q, rsrc_w, lane_off_w, __builtin_amdgcn_readfirstlane((int)(8 * q * K)), k_off);
 #pragma unroll
         for (int q = 0; q < 4; ++q) dma16(base + kW16OffX + 1024 * q, rsrc_x, x_off[q], 0, k_off_x);
         if (lane == 0) dma4(base + kW16OffWs, rsrc_ws, 0, __builtin_amdgcn_readfirstlane(kb * 4));
@@ -407,19 +419,22 @@ __global__ __launch_bounds__(kW16WideThreads, 1) void w8a16_wide_kernel(
     for (int s = 0; s < kW16WideSlots; ++s)
         if (s < nj) issue(s, kw + KW * s);
 
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    f32x4 acc[kR];
+#pragma unroll
+    for (int i = 0; i < kR; ++i) acc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
     const int sw = w16_sw(r);
     int slot = 0;
     for (int j = 0; j < nj; ++j) {
         const int younger = nj - 1 - j;
-        if (younger >= 2) w16_wait_n<2>();
-        else if (younger == 1) w16_wait_n<1>();
-        else w16_wait_n<0>();
+        if (kW16WideSlots > 2 && younger >= 2) w16_wait_n<SL::kVmem, (kW16WideSlots > 2 ? 2 : 1)>();
+        else if (younger >= 1) w16_wait_n<SL::kVmem, 1>();
+        else w16_wait_n<SL::kVmem, 0>();
         asm volatile("" ::: "memory");
         const uint8_t* sl = my_ring + slot * kW16Slot;
-        u32x4 wa0, wa1;
-        slab_read(sl, r, g, wa0, wa1);
+        u32x4 wa0[kR], wa1[kR];
+#pragma unroll
+        for (int i = 0; i < kR; ++i) slab_read(sl + i * kSlabBytes, r, g, wa0[i], wa1[i]);
         // MFMA i takes K offsets 16 g + 8 i (i < 2) and 64 + 16 g + 8 (i - 2):
         // 16-bit chunks 2 g + i and 8 + 2 g + (i - 2) of the token row.
         u32x4 xv[4];
@@ -431,31 +446,39 @@ __global__ __launch_bounds__(kW16WideThreads, 1) void w8a16_wide_kernel(
         const float wsv = *reinterpret_cast<const float*>(sl + kW16OffWs);
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         if (j + kW16WideSlots < nj) issue(slot, kw + KW * (j + kW16WideSlots));
-        const uint32_t q8[8] = {wa0[0], wa0[1], wa0[2], wa0[3], wa1[0], wa1[1], wa1[2], wa1[3]};
-        f32x4 blk = zero;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const u32x4 a = decode8<kXBf16>(q8[2 * i], q8[2 * i + 1]);
-            blk = kXBf16 ? mfma_bf16_16x16x32(a, xv[i], blk) : mfma_f16_16x16x32(a, xv[i], blk);
-        }
         const float sc = wsv * bias_fold;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(blk[e], sc, acc[e]);
+        for (int rt = 0; rt < kR; ++rt) {
+            const uint32_t q8[8] = {wa0[rt][0], wa0[rt][1], wa0[rt][2], wa0[rt][3],
+                                    wa1[rt][0], wa1[rt][1], wa1[rt][2], wa1[rt][3]};
+            f32x4 blk = zero;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const u32x4 a = decode8<kXBf16>(q8[2 * i], q8[2 * i + 1]);
+                blk = kXBf16 ? mfma_bf16_16x16x32(a, xv[i], blk) : mfma_f16_16x16x32(a, xv[i], blk);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[rt][e] = __builtin_fmaf(blk[e], sc, acc[rt][e]);
+        }
         slot = slot + 1 == kW16WideSlots ? 0 : slot + 1;
     }
 
     __syncthreads();
     float* red = reinterpret_cast<float*>(ring);
-    *reinterpret_cast<f32x4*>(red + ((kw * kT + tg) * kWave + lane) * 4) = acc;
+#pragma unroll
+    for (int i = 0; i < kR; ++i)
+        *reinterpret_cast<f32x4*>(red + (((kw * kR + i) * kT + tg) * kWave + lane) * 4) = acc[i];
     __syncthreads();
     const int L = threadIdx.x % kWave, rr = L & 15, gg = L >> 4;
-    for (int tt = threadIdx.x / kWave; tt < kT; tt += kW16WideWaves) {
-        f32x4 v = *reinterpret_cast<const f32x4*>(red + (tt * kWave + L) * 4);
+    for (int u = threadIdx.x / kWave; u < kR * kT; u += kW16WideWaves) {
+        f32x4 v = *reinterpret_cast<const f32x4*>(red + (u * kWave + L) * 4);
 #pragma unroll
-        for (int w = 1; w < KW; ++w) v += *reinterpret_cast<const f32x4*>(red + ((w * kT + tt) * kWave + L) * 4);
+        for (int w = 1; w < KW; ++w) v += *reinterpret_cast<const f32x4*>(red + ((w * kR * kT + u) * kWave + L) * 4);
+        const int i = u / kT, tt = u % kT;
         const int64_t m = 16 * kT * mg + 16 * tt + rr;
-        if (m < M) {
-            const int64_t idx = m * N + nt * 16 + 4 * gg;
+        const int64_t n = n0 + 16 * i + 4 * gg;
+        if (m < M && n < N) {
+            const int64_t idx = m * N + n;
             if (y_dtype == 2) {
                 *reinterpret_cast<f32x4*>(static_cast<float*>(y) + idx) = v;
             } else {
@@ -468,21 +491,65 @@ __global__ __launch_bounds__(kW16WideThreads, 1) void w8a16_wide_kernel(
     }
 }
 
+// Configuration of the W8A16 all-token kernel: kR 16-row weight tiles and kT
+// 16-token tiles per workgroup.  Among (kR, kT) in {1, 2} x {2, 4} (kT at
+// most the token tiles M needs), the one with the fewest workgroups that
+// still gives at least 256 (one per CU), preferring two weight-row tiles on
+// a tie (each token byte then feeds twice the weights); with no such
+// candidate, the one with the most workgroups.  Measured (us, N x K, M):
+// 4096 x 4096: M = 32 (1, 2) 9.6 vs (2, 2) 11.4; M = 64 (2, 2) 11.9 vs
+// (1, 4) 14.0; M = 128 (2, 4) 17.8 vs (2, 2) 20.0 and 20.4 tiled;
+// 12288 x 4096, M = 32: (2, 2) 22.3 vs (1, 2) 25.1; 1024 x 4096: M = 64
+// (1, 2) 7.0 vs 11.5 tiled, M = 128 (1, 2) 7.5 vs 17.0, M = 256 (2, 2) 9.8
+// vs 18.1.
+struct W16Shape {
+    int kr, kt;
+    unsigned groups_n, groups_m;
+};
+static W16Shape w16_shape(int64_t M, int64_t N) {
+    const int64_t m_tiles = (M + 15) / 16;
+    W16Shape best{0, 0, 0, 0};
+    int64_t best_wg = -1;
+    bool best_full = false;
+    for (int kt : {2, 4}) {
+        if (kt > 2 && kt > m_tiles) continue;
+        for (int kr : {2, 1}) {
+            const int64_t gn = (N + 16 * kr - 1) / (16 * kr), gm = (M + 16 * kt - 1) / (16 * kt);
+            const int64_t wg = gn * gm;
+            const bool full = wg >= 256;
+            const bool better = best_wg < 0 || (full && !best_full) || (full && best_full && wg < best_wg) ||
+                                (!full && !best_full && wg > best_wg);
+            if (better) {
+                best = W16Shape{kr, kt, (unsigned)gn, (unsigned)gm};
+                best_wg = wg;
+                best_full = full;
+            }
+        }
+    }
+    return best;
+}
+
 hipError_t launch_w8a16_wide(const void* x, bool x_bf16, const uint8_t* wq, const float* ws, void* y, int y_dtype,
                              int64_t M, int64_t N, int64_t K, hipStream_t stream) {
-    if (M < 1 || M > 64 || N % 16 != 0 || K > kTileMaxK) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)(N / 16));
+    if (M < 1 || N % 16 != 0 || K > kTileMaxK) return hipErrorInvalidValue;
+    const W16Shape w = w16_shape(M, N);
+    if (w.groups_m > 65535) return hipErrorInvalidValue;
+    const dim3 grid(w.groups_n, w.groups_m);
     const uint16_t* xh = static_cast<const uint16_t*>(x);
-#define BFP8_LAUNCH_W16(B, T)                                                                                \
-    hipLaunchKernelGGL((w8a16_wide_kernel<B, T>), grid, dim3(kW16WideThreads), 0, stream, xh, wq, ws, y, y_dtype, \
+#define BFP8_LAUNCH_W16(B, T, R)                                                                                  \
+    hipLaunchKernelGGL((w8a16_wide_kernel<B, T, R>), grid, dim3(kW16WideThreads), 0, stream, xh, wq, ws, y, y_dtype, \
                        M, N, K)
+#define BFP8_LAUNCH_W16_KR(B, T)          \
+    if (w.kr == 1) BFP8_LAUNCH_W16(B, T, 1); \
+    else BFP8_LAUNCH_W16(B, T, 2);
     if (x_bf16) {
-        if (M <= 32) BFP8_LAUNCH_W16(true, 2);
-        else BFP8_LAUNCH_W16(true, 4);
+        if (w.kt == 2) { BFP8_LAUNCH_W16_KR(true, 2) }
+        else { BFP8_LAUNCH_W16_KR(true, 4) }
     } else {
-        if (M <= 32) BFP8_LAUNCH_W16(false, 2);
-        else BFP8_LAUNCH_W16(false, 4);
+        if (w.kt == 2) { BFP8_LAUNCH_W16_KR(false, 2) }
+        else { BFP8_LAUNCH_W16_KR(false, 4) }
     }
+#undef BFP8_LAUNCH_W16_KR
 #undef BFP8_LAUNCH_W16
     return hipGetLastError();
 }

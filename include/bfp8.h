@@ -246,8 +246,11 @@ size_t bfp8_workspace_bytes(int op, int64_t M, int64_t N, int64_t K);
  *                 16- or 32-row weight tile for the other M <= 2 * m_stream_max,
  *                 and when K <= 4096 and M * N <= 2^19 (measured faster
  *                 there), the tiled MFMA kernels otherwise.  W8A16
- *                 blk128 streams M <= m_stream_max and uses its tiled MFMA
- *                 kernel for larger M; blk32 always streams.
+ *                 blk128 streams M <= m_stream_max, reads all tokens per
+ *                 weight tile for m_stream_max < M <= 16 * m_stream_max
+ *                 when K <= 4096 and either M <= 2 * m_stream_max or
+ *                 M * N <= 2^19, and uses its tiled MFMA kernel
+ *                 otherwise; blk32 always streams.
  * Any output pointer may be NULL.
  */
 bfp8_status bfp8_get_limits(int op, int64_t* k_multiple, int64_t* n_multiple,

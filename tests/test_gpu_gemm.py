@@ -233,10 +233,14 @@ def test_w8a16_blk128(gpu_lib, M, xdtype):
 
 @pytest.mark.parametrize("xdtype", [torch.bfloat16, torch.float16])
 @pytest.mark.parametrize("M,N,K", [(17, 1024, 4096), (32, 4096, 4096), (50, 1024, 4096), (64, 4096, 4096),
-                                   (24, 12288, 512), (20, 16, 4096), (20, 64, 128)])
+                                   (24, 12288, 512), (20, 16, 4096), (20, 64, 128), (128, 4096, 4096),
+                                   (100, 4112, 1024), (256, 1024, 4096), (200, 1040, 1024)])
 def test_w8a16_all_tokens(gpu_lib, M, N, K, xdtype):
-    """16 < M <= 64 with K <= 4096: every token per 16-row weight tile, no
-    workspace; ragged M, a single weight tile, K spread over the waves."""
+    """16 < M <= 256 with K <= 4096: every token of a group per 16- or 32-row
+    weight tile, no workspace.  Covers one and two weight-row tiles per
+    workgroup (a half-filled last pair at N = 16 and 4112), two and four
+    token tiles, several token groups (grid.y) with a ragged last group and
+    an empty last tile (M = 100), and K spread over the waves."""
     assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A16_BLK128, M, N, K) == 0
     say("w8a16 all-token", xdtype, f"M={M} N={N} K={K}")
     x = inputs.activations(M, K, workload=640 + M, stream=K, outliers=True, dtype=xdtype)
@@ -281,7 +285,7 @@ def test_w8a16_blk128_one_hot_all_codes_exact(gpu_lib, xdtype, M):
 
 
 @pytest.mark.parametrize("xdtype", [torch.bfloat16, torch.float16])
-@pytest.mark.parametrize("M,N,K", [(40, 1024, 8192), (100, 1040, 4096), (300, 2048, 2176)])
+@pytest.mark.parametrize("M,N,K", [(40, 1024, 8192), (100, 1040, 8192), (300, 2048, 2176)])
 def test_w8a16_tile_split_k(gpu_lib, M, N, K, xdtype):
     """Tiled W8A16 with ragged M/N tiles and split K (workspace), run twice on
     one workspace: bar met, second run bit-identical."""
@@ -301,8 +305,8 @@ def test_w8a16_tile_split_k(gpu_lib, M, N, K, xdtype):
 
 @pytest.mark.parametrize("xdtype", [torch.bfloat16, torch.float16])
 def test_w8a16_tile_one_hot_all_codes_exact(gpu_lib, xdtype):
-    """Tiled path (M = 48): x one-hot 1.0 gives E4M3(wq[n, k]) * ws exactly."""
-    N, K, M = 256, 256, 48
+    """Tiled path (M = 300): x one-hot 1.0 gives E4M3(wq[n, k]) * ws exactly."""
+    N, K, M = 256, 256, 300
     wq = np.zeros((N, K), np.uint8)
     wq[:254, :] = FINITE_CODES[:, None]
     ws = np.array([[0.5, 2.0], [0.25, 4.0]], np.float32)
