@@ -31,22 +31,61 @@ struct StreamPlan {
 };
 StreamPlan plan_stream(int64_t M, int64_t N, int64_t K);
 
+// Shape of a launch of the all-token kernels (W8A8 and W8A16): kr 16-row
+// weight tiles and kt 16-token tiles per workgroup, groups_n x groups_m
+// workgroups.  Among (kr, kt) in {1, 2} x {2, 4} (kt = 4 only when M needs
+// at least four token tiles) it takes the one with the fewest workgroups
+// that still gives at least 256, one per CU, and two weight tiles on a tie
+// (each token byte then feeds twice the weights); with no such candidate,
+// the one with the most workgroups.  Measured over every (kr, kt), K = 4096,
+// 32 rotated weight copies, this picks the fastest at each point tried
+// (us, W8A8 / W8A16): 4096 x 4096 M = 32 (1, 2) 6.7 / 9.6, M = 48 (2, 2)
+// 7.8 against 9.4 for (1, 4), M = 64 (2, 2) 8.7 / 11.9 against 10.7 / 14.0,
+// M = 128 (2, 4) 12.5 / 17.8; 1024 x 4096 M = 128 (1, 2) 5.4 / 7.5 against
+// 7.5 / 10.4 for (1, 4), M = 256 (2, 2) 6.4 / 9.8, M = 512 (2, 4) 9.4;
+// 12288 x 4096 M = 32 (2, 2) - / 22.3.
+struct WideShape {
+    int kr, kt;
+    unsigned groups_n, groups_m;
+};
+inline WideShape wide_shape(int64_t M, int64_t N) {
+    const int64_t m_tiles = (M + 15) / 16;
+    WideShape best{1, 2, 0, 0};
+    int64_t best_wg = -1;
+    bool best_full = false;
+    for (int kt = 2; kt <= 4; kt += 2) {
+        if (kt > 2 && kt > m_tiles) continue;
+        for (int kr = 2; kr >= 1; --kr) {
+            const int64_t gn = (N + 16 * kr - 1) / (16 * kr), gm = (M + 16 * kt - 1) / (16 * kt);
+            const int64_t wg = gn * gm;
+            const bool full = wg >= 256;
+            const bool better = best_wg < 0 || (full && (!best_full || wg < best_wg)) || (!full && !best_full && wg > best_wg);
+            if (better) {
+                best = WideShape{kr, kt, (unsigned)gn, (unsigned)(gm > 65535 ? 65536 : gm)};
+                best_wg = wg;
+                best_full = full;
+            }
+        }
+    }
+    return best;
+}
+
 // W8A8 dispatch (codes in), from the projection sweep:
 //  * the streaming kernel for M <= 16 when it needs no split of K, or when
 //    N < 1024, and for M <= 64 when its workgroups fit one round unsplit;
-//  * the all-token kernel (launch_w8a8_wide: every token per workgroup, no
-//    split) for the other M <= 32, and when K <= 4096 and M * N <= 2^19
-//    (M <= 128 at N = 4096, M <= 512 at N = 1024);
-//    measured (us): 1024 x 4096 at M = 1 / 16: 4.3 / 4.4 against 5.3 / 5.5
-//    streamed with K split 4 ways; at M = 32: 4096 x 4096 6.7, 1024 x 4096
-//    4.9, 12288 x 4096 16.5, 4096 x 12288 17.1 against 11.6, 9.8, 22.5 and
-//    17.8 tiled; at M = 64: 4096 x 4096 9.7 vs 12.1, 1024 x 4096 7.3 vs
-//    10.3, 12288 x 4096 24.1 vs 24.8; at M = 128: 4096 x 4096 11.7 vs 14.6,
-//    1024 x 4096 7.5 vs 11.5, 12288 x 4096 34.2 vs 34.5; 1024 x 4096 at
-//    M = 256 / 512 7.9 / 9.4 vs 11.8 / 12.9, 2048 x 4096 at M = 256 10.9 vs
-//    13.3, but 4096 x 4096 at M = 256 21.2 vs 18.0 and 2048 x 4096 at
-//    M = 512 19.4 vs 16.9; with K = 12288 and M >= 64 the tiled kernels win
-//    (M = 64: 19.2 vs 29.0 us);
+//  * the all-token kernel (launch_w8a8_wide: every token of a 32- or
+//    64-token group per workgroup, no split) for the other M <= 32, and
+//    when K <= 4096 and M * N <= 2^19 (M <= 128 at N = 4096, M <= 512 at
+//    N = 1024); measured (us, 32 rotated weight copies): 1024 x 4096 at
+//    M = 1 / 16: 4.3 / 4.4 against 5.3 / 5.5 streamed with K split 4 ways;
+//    at M = 32: 4096 x 4096 6.7, 1024 x 4096 4.9, 12288 x 4096 16.5,
+//    4096 x 12288 17.1 against 11.6, 9.8, 22.5 and 17.8 tiled; 4096 x 4096
+//    at M = 48 / 64 / 96 / 128: 7.8 / 8.7 / 10.8 / 12.5 against 12.1 /
+//    12.7 / 13.5 / 14.3 tiled; 1024 x 4096 at M = 128 / 256 / 512: 5.4 /
+//    6.4 / 9.4 against 11.2 / 11.9 / 12.9; but 4096 x 4096 at M = 256 21.2
+//    vs 18.0 and 2048 x 4096 at M = 512 19.4 vs 16.9, 12288 x 4096 at
+//    M = 64 / 128 even (24.1 / 33.9 vs 24.3 / 33.8), and with K = 12288 and
+//    M >= 64 the tiled kernels win (M = 64: 19.2 vs 29.0 us);
 //  * the tiled kernels otherwise.
 inline bool w8a8_streams(int64_t M, int64_t N, int64_t K) {
     if (M <= kStreamMaxM) return N < 1024 || K > kTileMaxK || plan_stream(M, N, K).splits == 1;

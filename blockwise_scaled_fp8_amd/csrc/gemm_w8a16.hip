@@ -491,48 +491,10 @@ __global__ __launch_bounds__(kW16WideThreads, 1) void w8a16_wide_kernel(
     }
 }
 
-// Configuration of the W8A16 all-token kernel: kR 16-row weight tiles and kT
-// 16-token tiles per workgroup.  Among (kR, kT) in {1, 2} x {2, 4} (kT at
-// most the token tiles M needs), the one with the fewest workgroups that
-// still gives at least 256 (one per CU), preferring two weight-row tiles on
-// a tie (each token byte then feeds twice the weights); with no such
-// candidate, the one with the most workgroups.  Measured (us, N x K, M):
-// 4096 x 4096: M = 32 (1, 2) 9.6 vs (2, 2) 11.4; M = 64 (2, 2) 11.9 vs
-// (1, 4) 14.0; M = 128 (2, 4) 17.8 vs (2, 2) 20.0 and 20.4 tiled;
-// 12288 x 4096, M = 32: (2, 2) 22.3 vs (1, 2) 25.1; 1024 x 4096: M = 64
-// (1, 2) 7.0 vs 11.5 tiled, M = 128 (1, 2) 7.5 vs 17.0, M = 256 (2, 2) 9.8
-// vs 18.1.
-struct W16Shape {
-    int kr, kt;
-    unsigned groups_n, groups_m;
-};
-static W16Shape w16_shape(int64_t M, int64_t N) {
-    const int64_t m_tiles = (M + 15) / 16;
-    W16Shape best{0, 0, 0, 0};
-    int64_t best_wg = -1;
-    bool best_full = false;
-    for (int kt : {2, 4}) {
-        if (kt > 2 && kt > m_tiles) continue;
-        for (int kr : {2, 1}) {
-            const int64_t gn = (N + 16 * kr - 1) / (16 * kr), gm = (M + 16 * kt - 1) / (16 * kt);
-            const int64_t wg = gn * gm;
-            const bool full = wg >= 256;
-            const bool better = best_wg < 0 || (full && !best_full) || (full && best_full && wg < best_wg) ||
-                                (!full && !best_full && wg > best_wg);
-            if (better) {
-                best = W16Shape{kr, kt, (unsigned)gn, (unsigned)gm};
-                best_wg = wg;
-                best_full = full;
-            }
-        }
-    }
-    return best;
-}
-
 hipError_t launch_w8a16_wide(const void* x, bool x_bf16, const uint8_t* wq, const float* ws, void* y, int y_dtype,
                              int64_t M, int64_t N, int64_t K, hipStream_t stream) {
     if (M < 1 || N % 16 != 0 || K > kTileMaxK) return hipErrorInvalidValue;
-    const W16Shape w = w16_shape(M, N);
+    const WideShape w = wide_shape(M, N);
     if (w.groups_m > 65535) return hipErrorInvalidValue;
     const dim3 grid(w.groups_n, w.groups_m);
     const uint16_t* xh = static_cast<const uint16_t*>(x);

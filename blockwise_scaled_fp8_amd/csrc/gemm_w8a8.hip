@@ -531,23 +531,6 @@ __global__ __launch_bounds__(kWideThreads, 1) void w8a8_wide_kernel(
     }
 }
 
-// Configuration of the all-token kernel for M (16 kT tokens per workgroup
-// row, kT = 2 or 4) and N: two 16-row weight tiles per workgroup when that
-// still leaves at least 256 workgroups (each workgroup then reads half the
-// token bytes per output), one otherwise.
-struct WideShape {
-    int kr, kt;
-    unsigned groups_n, groups_m;
-};
-static WideShape wide_shape(int64_t M, int64_t N) {
-    WideShape w;
-    w.kt = M <= 32 ? 2 : 4;
-    w.groups_m = (unsigned)((M + 16 * w.kt - 1) / (16 * w.kt));
-    w.kr = (N + 31) / 32 * w.groups_m >= 256 ? 2 : 1;
-    w.groups_n = (unsigned)((N + 16 * w.kr - 1) / (16 * w.kr));
-    return w;
-}
-
 hipError_t launch_w8a8_wide(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
                             void* y, int y_dtype, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
     if (M < 1 || N % 16 != 0 || K > kTileMaxK) return hipErrorInvalidValue;

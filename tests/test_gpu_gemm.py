@@ -77,7 +77,7 @@ def test_w8a8_split_k_narrow_projection(gpu_lib, M):
                                    (64, 4096, 4096), (32, 12288, 256), (20, 16, 8192), (20, 8208, 256),
                                    (65, 8192, 512), (100, 4096, 1024), (128, 1040, 2048), (20, 64, 128),
                                    (128, 8192, 128), (64, 1024, 4096), (40, 2048, 1024), (61, 512, 8192),
-                                   (300, 1024, 2048), (512, 1024, 512)])
+                                   (300, 1024, 2048), (512, 1024, 512), (256, 1040, 1024)])
 def test_w8a8_wide_all_tokens(gpu_lib, M, N, K):
     """The paths that need no workspace for M <= 128: the kernel that holds
     every token per 16- or 32-row weight tile (M <= 16 where streaming would
