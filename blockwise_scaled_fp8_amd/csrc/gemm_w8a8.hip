@@ -425,8 +425,9 @@ __global__ __launch_bounds__(kWideThreads, 1) void w8a8_wide_kernel(
     const int64_t rows_w = N - n0 < 16 * kR ? N - n0 : 16 * kR;
 
     const i32x4 rsrc_w = buffer_rsrc(wq + n0 * K, (uint32_t)(rows_w * K));
-    // Token rows and scales from row m0 on; rows at or past M load as zeros.
-    const int64_t rows_x = M - m0 > 0 ? M - m0 : 0;
+    // The wave's 32 token rows and their scales from row m0 on; rows at or
+    // past M (and the padding scales of lanes 32..63) load as zeros.
+    const int64_t rows_x = M - m0 > 0 ? (M - m0 < 32 ? M - m0 : 32) : 0;
     const i32x4 rsrc_x = buffer_rsrc(xq + m0 * K, (uint32_t)(rows_x * K));
     const i32x4 rsrc_xs = buffer_rsrc(xs + m0 * KB, (uint32_t)(rows_x * KB * 4));
     const i32x4 rsrc_ws = buffer_rsrc(ws + (n0 / 128) * KB, (uint32_t)(KB * 4));
