@@ -79,9 +79,11 @@ namespace {
 
 size_t round256(size_t v) { return (v + 255) / 256 * 256; }
 
-// W8A8 workspace for codes input: the streaming plan's, none for the wide
-// kernel, or the tiled kernels' (w8a8_streams and w8a8_wide decide).
+// W8A8 workspace for codes input: none for one token (K <= 4096), the
+// streaming plan's, none for the wide kernel, or the tiled kernels'
+// (one_token, w8a8_streams and w8a8_wide decide).
 size_t w8a8_workspace(int64_t M, int64_t N, int64_t K) {
+    if (one_token(M, K)) return 0;
     if (w8a8_streams(M, N, K)) return stream_workspace_bytes(plan_stream(M, N, K));
     if (w8a8_wide(M, N, K)) return 0;
     return K <= kTileMaxK ? tile_workspace_bytes(M, N, K) : 0;
@@ -90,15 +92,17 @@ size_t w8a8_workspace(int64_t M, int64_t N, int64_t K) {
 // The W8A8 codes kernels by M (workspace already checked).
 hipError_t launch_w8a8(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws, void* y,
                        int y_dtype, int64_t M, int64_t N, int64_t K, void* workspace, hipStream_t stream) {
+    if (one_token(M, K)) return launch_w8a8_gemv(xq, xs, wq, ws, y, y_dtype, N, K, stream);
     if (w8a8_streams(M, N, K)) return launch_w8a8_stream(xq, xs, wq, ws, y, y_dtype, M, N, K, workspace, stream);
     if (w8a8_wide(M, N, K)) return launch_w8a8_wide(xq, xs, wq, ws, y, y_dtype, M, N, K, stream);
     return launch_w8a8_tile(xq, xs, wq, ws, y, y_dtype, M, N, K, workspace, stream);
 }
 
-// The fused quantise + W8A8 call quantises inside the streaming kernel when
-// the codes call would stream (so both give the same bits), M permitting.
+// The fused quantise + W8A8 call quantises inside the kernel when the codes
+// call would run the one-token kernel or stream (so both give the same
+// bits), M permitting.
 bool quantises_in_registers(int64_t M, int64_t N, int64_t K) {
-    return M <= kFusedQuantMaxM && w8a8_streams(M, N, K);
+    return one_token(M, K) || (M <= kFusedQuantMaxM && w8a8_streams(M, N, K));
 }
 
 // Workspace of the fused quantise + W8A8 call when it does not, where
@@ -124,12 +128,13 @@ size_t bfp8_workspace_bytes(int op, int64_t M, int64_t N, int64_t K) {
     if (M < 1 || N < 16 || K < 128) return 0;
     switch (op) {
         case BFP8_OP_QUANT_GEMM_W8A8_BLK128:
+            if (one_token(M, K)) return 0;
             if (quantises_in_registers(M, N, K)) return stream_workspace_bytes(plan_stream(M, N, K));
             return K <= kTileMaxK ? quant_gemm_parts(M, N, K).total : 0;
         case BFP8_OP_GEMM_W8A8_BLK128:
             return w8a8_workspace(M, N, K);
         case BFP8_OP_GEMM_W8A16_BLK128:
-            if (w8a16_wide(M, N, K)) return 0;
+            if (one_token(M, K) || w8a16_wide(M, N, K)) return 0;
             if (M > kStreamMaxM) return K <= kTileMaxK ? tile16_workspace_bytes(M, N, K) : 0;
             return stream_workspace_bytes(plan_stream(M, N, K));
         case BFP8_OP_GEMM_W8A16_BLK32_UE8M0:
@@ -160,6 +165,8 @@ bfp8_status bfp8_quant_gemm_w8a8_blk128(const void* x, int x_dtype, const uint8_
     bfp8_status st = check_gemm(x, wq, ws, y, y_dtype, M, N, K, 16, need, workspace, workspace_bytes);
     if (st != BFP8_OK) return st;
     if (!is16(x_dtype)) return BFP8_E_DTYPE;
+    if (one_token(M, K))
+        return launched(launch_w8a8_gemv_quant(x, x_dtype == BFP8_BF16, wq, ws, y, y_dtype, N, K, as_stream(stream)));
     if (quantises_in_registers(M, N, K))
         return launched(launch_w8a8_stream_quant(x, x_dtype == BFP8_BF16, wq, ws, y, y_dtype, M, N, K, workspace,
                                                  as_stream(stream)));
@@ -184,6 +191,8 @@ bfp8_status bfp8_gemm_w8a16_blk128(const void* x, int x_dtype, const uint8_t* wq
     bfp8_status st = check_gemm(x, wq, ws, y, y_dtype, M, N, K, 16, need, workspace, workspace_bytes);
     if (st != BFP8_OK) return st;
     if (!is16(x_dtype)) return BFP8_E_DTYPE;
+    if (one_token(M, K))       // one token: dot products on the vector ALUs
+        return launched(launch_w8a16_gemv(x, x_dtype == BFP8_BF16, wq, ws, y, y_dtype, N, K, as_stream(stream)));
     if (w8a16_wide(M, N, K))   // every token per workgroup, weights widened in registers
         return launched(launch_w8a16_wide(x, x_dtype == BFP8_BF16, wq, ws, y, y_dtype, M, N, K, as_stream(stream)));
     if (M > kStreamMaxM)     // tiled MFMA kernel, weights widened in registers

@@ -141,6 +141,20 @@ inline bool w8a16_wide(int64_t M, int64_t N, int64_t K) {
     return M > kStreamMaxM && M <= 16 * kStreamMaxM && K <= 4096 &&
            (M <= 2 * kStreamMaxM || M * N <= ((int64_t)1 << 19));
 }
+// One token with K <= 4096 (W8A8 codes, W8A8 with activations quantised in
+// the kernel, W8A16 blk128): dot-product kernels on the vector ALUs, no
+// workspace (launch_w8a8_gemv, launch_w8a8_gemv_quant, launch_w8a16_gemv).
+// Measured against the streaming MFMA kernels (us, 32 rotated weight
+// copies): N = K = 4096 W8A8 codes 5.23 vs 5.45, fused quantise + W8A8
+// 5.67 vs 5.82, W8A16 5.63 vs 5.69; 1024 x 4096 W8A8 3.33 vs 3.87, W8A16
+// 3.05 vs 3.96; 12288 x 4096 W8A8 10.3 vs 11.0, W8A16 10.8 vs 11.5.
+inline bool one_token(int64_t M, int64_t K) { return M == 1 && K <= 4096; }
+hipError_t launch_w8a8_gemv(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws, void* y,
+                            int y_dtype, int64_t N, int64_t K, hipStream_t stream);
+hipError_t launch_w8a8_gemv_quant(const void* x, bool x_bf16, const uint8_t* wq, const float* ws, void* y,
+                                  int y_dtype, int64_t N, int64_t K, hipStream_t stream);
+hipError_t launch_w8a16_gemv(const void* x, bool x_bf16, const uint8_t* wq, const float* ws, void* y, int y_dtype,
+                             int64_t N, int64_t K, hipStream_t stream);
 // M >= 1, N a multiple of 16, K <= kTileMaxK; needs no workspace.
 hipError_t launch_w8a16_wide(const void* x, bool x_bf16, const uint8_t* wq, const float* ws, void* y, int y_dtype,
                              int64_t M, int64_t N, int64_t K, hipStream_t stream);

@@ -21,7 +21,9 @@
 // e in [-14, 7] ([SM70] "Exactness"), so the MFMA sees exactly the weights
 // of a load-time fp16 dequantisation and accumulates in fp32 across all K.
 //
-// The kernels here stream the weights like the W8A8 decode kernel: one
+// M = 1 with K <= 4096 runs a plain dot-product kernel on the vector ALUs
+// (w8a16_gemv_kernel below).  The other kernels here stream the weights like
+// the W8A8 decode kernel: one
 // workgroup per 16 weight rows (and per split of K), 16 tokens on the MFMA
 // column axis, sixteen waves taking interleaved 128-K blocks.  W8A16 blk128
 // with M > 16 runs the tiled MFMA kernel instead (gemm_w8a8_tile.hip); blk32
@@ -513,6 +515,117 @@ hipError_t launch_w8a16_wide(const void* x, bool x_bf16, const uint8_t* wq, cons
     }
 #undef BFP8_LAUNCH_W16_KR
 #undef BFP8_LAUNCH_W16
+    return hipGetLastError();
+}
+
+// ------------------------------------------------ W8A16 GEMV, M = 1 ----
+// One token (batch-1 decode) with K <= 4096 needs no matrix core: the work
+// is one dot product per weight row.  A wave owns kR weight rows.  Lane l
+// takes, in each 1 KB chunk c of a row, the 16 weight bytes at K offset
+// 1024 c + 16 l (one load instruction covers 8 whole 128-byte lines) and the
+// 16 matching activations, widens the E4M3 weights to fp32
+// (v_cvt_pk_f32_fp8, exact) and sums the 16 products in fp32.  Lanes 8 j ..
+// 8 j + 7 hold 128-K block 8 c + j: three lane exchanges give every one of
+// them the block's dot product, which is promoted once with the block's
+// weight scale (the per-block promotion of [ARC] "What this adds", here
+// without a matrix instruction).  The eight lane groups' promoted
+// sums are added at the end (three more exchanges) and lane 0 stores the
+// row.  Every load is issued before the first product; there is no LDS
+// staging and no barrier, so the cross-wave reduction of the streaming
+// kernel, about half a microsecond of a 5.7 us launch at N = K = 4096, is
+// gone (measured 5.50 vs 5.66 us there, 3.05 vs 3.96 us at N = 1024 and
+// 10.8 vs 11.5 us at N = 12288).  Lanes past K read zeros (their offsets
+// are moved past the descriptor's range).
+template <bool kXBf16>
+__device__ __forceinline__ float half_bits_to_f32(uint32_t h) {
+    if constexpr (kXBf16) return __builtin_bit_cast(float, h << 16);
+    else return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+template <bool kXBf16, int kR>
+__global__ __launch_bounds__(kGemvWaves * kWave) void w8a16_gemv_kernel(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq, const float* __restrict__ ws,
+    void* __restrict__ y, int y_dtype, int64_t N, int64_t K) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
+    const int64_t n0 = ((int64_t)blockIdx.x * kGemvWaves + wave) * kR;   // wave-uniform: scalar descriptors
+    if (n0 >= N) return;
+    const int KB = (int)(K / 128);
+    const int64_t rows = N - n0 < kR ? N - n0 : kR;
+    const int w_bytes = (int)(rows * K);
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void*)(wq + n0 * K), 0, w_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)x, 0, (int)(2 * K), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(ws + (n0 / 128) * KB), 0, KB * 4, 0x00020000);
+
+    i32x4 xv[kGemvMaxChunks][2], wv[kGemvMaxChunks][kR];
+    float wsv[kGemvMaxChunks];
+#pragma unroll
+    for (int c = 0; c < kGemvMaxChunks; ++c) {
+        const int k = 1024 * c + 16 * lane;
+        xv[c][0] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, 2 * k, 0, 0));
+        xv[c][1] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, 2 * k + 16, 0, 0));
+        wsv[c] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * (k / 128), 0, 0));
+    }
+#pragma unroll
+    for (int c = 0; c < kGemvMaxChunks; ++c) {
+        const int k = 1024 * c + 16 * lane;
+#pragma unroll
+        for (int r = 0; r < kR; ++r) {
+            const int off = k < K ? (int)(r * K) + k : w_bytes;
+            wv[c][r] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, 0));
+        }
+    }
+    // Keep every load ahead of the arithmetic: the scheduler would otherwise
+    // sink the later chunks' loads below the first chunk's products.
+    __builtin_amdgcn_sched_barrier(0);
+
+    float acc[kR];
+#pragma unroll
+    for (int r = 0; r < kR; ++r) acc[r] = 0.0f;
+#pragma unroll
+    for (int c = 0; c < kGemvMaxChunks; ++c) {
+        // Chunks past K hold zeros only (every lane's loads lie past its
+        // descriptor), so they add nothing and need no branch.
+        float xf[16];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t u = (uint32_t)xv[c][h][i];
+                xf[8 * h + 2 * i] = half_bits_to_f32<kXBf16>(u & 0xFFFFu);
+                xf[8 * h + 2 * i + 1] = half_bits_to_f32<kXBf16>(u >> 16);
+            }
+#pragma unroll
+        for (int r = 0; r < kR; ++r) {
+            float wf[16];
+            e4m3x16_to_f32(wv[c][r], wf);
+            acc[r] = __builtin_fmaf(block_dot16(xf, wf), wsv[c], acc[r]);
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < kR; ++r) {
+        const float v = group_sum8(acc[r]);
+        if (lane == 0 && r < rows) store_out(y, y_dtype, n0 + r, v);
+    }
+}
+
+hipError_t launch_w8a16_gemv(const void* x, bool x_bf16, const uint8_t* wq, const float* ws, void* y, int y_dtype,
+                             int64_t N, int64_t K, hipStream_t stream) {
+    if (N % 16 != 0 || K > kGemvMaxK) return hipErrorInvalidValue;
+    // Two rows per wave when that still leaves at least 256 workgroups.
+    const int kr = N >= 2048 ? 2 : 1;
+    const dim3 grid((unsigned)((N + kGemvWaves * kr - 1) / (kGemvWaves * kr)));
+    const uint16_t* xh = static_cast<const uint16_t*>(x);
+#define BFP8_LAUNCH_GEMV(B, R) \
+    hipLaunchKernelGGL((w8a16_gemv_kernel<B, R>), grid, dim3(kGemvWaves * kWave), 0, stream, xh, wq, ws, y, y_dtype, N, K)
+    if (x_bf16) {
+        if (kr == 2) BFP8_LAUNCH_GEMV(true, 2);
+        else BFP8_LAUNCH_GEMV(true, 1);
+    } else {
+        if (kr == 2) BFP8_LAUNCH_GEMV(false, 2);
+        else BFP8_LAUNCH_GEMV(false, 1);
+    }
+#undef BFP8_LAUNCH_GEMV
     return hipGetLastError();
 }
 

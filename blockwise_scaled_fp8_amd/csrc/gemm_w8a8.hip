@@ -552,6 +552,212 @@ hipError_t launch_w8a8_wide(const uint8_t* xq, const float* xs, const uint8_t* w
     return hipGetLastError();
 }
 
+// ------------------------------------------------ W8A8 GEMV, M = 1 ----
+// One token with K <= 4096 (batch-1 decode): the dot products run on the
+// vector ALUs, laid out as in the W8A16 one-token kernel (stream_common.hpp:
+// lane l covers K offsets 1024 c + 16 l of every 1 KB chunk c of its weight
+// rows).  Each lane widens its 16 activation codes and 16 weight codes to
+// fp32 (exact), block_dot16 gives the 128-K block's dot product to the 8
+// lanes of the block, and the block is promoted once with
+// xs[kb] * ws[n / 128, kb] ([ADA] "Scale promotion"; [ARC] "What this
+// adds").  All loads are issued before the first product; there is no LDS
+// and no barrier.  gemv_row_dot is that arithmetic for one row; the kernel
+// that quantises its own activations calls it too, so the fused call and
+// quantise-then-GEMM give the same bits.
+template <int kR>
+__device__ __forceinline__ void gemv_rows(const float (&xf)[kGemvMaxChunks][16], const float (&sx)[kGemvMaxChunks],
+                                          const i32x4 (&wv)[kGemvMaxChunks][kR], const float (&wsv)[kGemvMaxChunks],
+                                          float (&acc)[kR]) {
+#pragma unroll
+    for (int r = 0; r < kR; ++r) acc[r] = 0.0f;
+#pragma unroll
+    for (int c = 0; c < kGemvMaxChunks; ++c) {
+        const float sc = sx[c] * wsv[c];
+#pragma unroll
+        for (int r = 0; r < kR; ++r) {
+            float wf[16];
+            e4m3x16_to_f32(wv[c][r], wf);
+            acc[r] = __builtin_fmaf(block_dot16(xf[c], wf), sc, acc[r]);
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < kR; ++r) acc[r] = group_sum8(acc[r]);
+}
+
+// Issue the loads of the kR weight rows from row n0 and of their weight
+// scales, chunk by chunk; lanes past K read zeros.
+template <int kR>
+__device__ __forceinline__ void gemv_load_weights(const uint8_t* wq, const float* ws, int64_t n0, int64_t rows,
+                                                  int64_t K, int lane, i32x4 (&wv)[kGemvMaxChunks][kR],
+                                                  float (&wsv)[kGemvMaxChunks]) {
+    const int KB = (int)(K / 128);
+    const int w_bytes = (int)(rows * K);
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void*)(wq + n0 * K), 0, w_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(ws + (n0 / 128) * KB), 0, KB * 4, 0x00020000);
+#pragma unroll
+    for (int c = 0; c < kGemvMaxChunks; ++c)
+        wsv[c] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * ((1024 * c + 16 * lane) / 128), 0, 0));
+#pragma unroll
+    for (int c = 0; c < kGemvMaxChunks; ++c) {
+        const int k = 1024 * c + 16 * lane;
+#pragma unroll
+        for (int r = 0; r < kR; ++r) {
+            const int off = k < K ? (int)(r * K) + k : w_bytes;
+            wv[c][r] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, 0));
+        }
+    }
+}
+
+template <int kR>
+__global__ __launch_bounds__(kGemvWaves * kWave) void w8a8_gemv_kernel(
+    const uint8_t* __restrict__ xq, const float* __restrict__ xs, const uint8_t* __restrict__ wq,
+    const float* __restrict__ ws, void* __restrict__ y, int y_dtype, int64_t N, int64_t K) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
+    const int64_t n0 = ((int64_t)blockIdx.x * kGemvWaves + wave) * kR;   // wave-uniform: scalar descriptors
+    if (n0 >= N) return;
+    const int KB = (int)(K / 128);
+    const int64_t rows = N - n0 < kR ? N - n0 : kR;
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)xq, 0, (int)K, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rxs = __builtin_amdgcn_make_buffer_rsrc((void*)xs, 0, KB * 4, 0x00020000);
+    i32x4 xv[kGemvMaxChunks], wv[kGemvMaxChunks][kR];
+    float sx[kGemvMaxChunks], wsv[kGemvMaxChunks];
+#pragma unroll
+    for (int c = 0; c < kGemvMaxChunks; ++c) {
+        const int k = 1024 * c + 16 * lane;
+        xv[c] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, k, 0, 0));
+        sx[c] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rxs, 4 * (k / 128), 0, 0));
+    }
+    gemv_load_weights<kR>(wq, ws, n0, rows, K, lane, wv, wsv);
+    // Keep every load ahead of the arithmetic: the scheduler would otherwise
+    // sink the later chunks' loads below the first chunk's products.
+    __builtin_amdgcn_sched_barrier(0);
+    float xf[kGemvMaxChunks][16];
+#pragma unroll
+    for (int c = 0; c < kGemvMaxChunks; ++c) e4m3x16_to_f32(xv[c], xf[c]);
+    float acc[kR];
+    gemv_rows<kR>(xf, sx, wv, wsv, acc);
+#pragma unroll
+    for (int r = 0; r < kR; ++r)
+        if (lane == 0 && r < rows) store_out(y, y_dtype, n0 + r, acc[r]);
+}
+
+// The same product from 16-bit activations, quantised once per workgroup:
+// kW waves, one weight row each.  Wave w quantises activations
+// [4096 w / kW, 4096 (w + 1) / kW), V = 64 / kW consecutive values per lane,
+// so a 1x128 group spans 128 / V lanes; their maximum (lane exchanges),
+// scale amax / 448 and codes (quantize_v, the quantiser's own arithmetic)
+// equal bfp8_quantize_act_1x128's bit for bit.  Codes and scales go to LDS;
+// after one barrier every wave reads back its lanes' 16 codes per chunk and
+// runs gemv_rows.  The weight loads are issued first, so the quantisation
+// runs while they stream.
+template <bool kXBf16, int kW>
+__global__ __launch_bounds__(kW * kWave) void w8a8_gemv_quant_kernel(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq, const float* __restrict__ ws,
+    void* __restrict__ y, int y_dtype, int64_t N, int64_t K) {
+    constexpr int V = 64 / kW;              // activations per lane
+    constexpr int kGroupLanes = 128 / V;
+    static_assert(V == 4 || V == 8 || V == 16, "values per lane");
+    __shared__ __attribute__((aligned(16))) uint8_t codes_lds[kGemvMaxK];
+    __shared__ float scale_lds[kGemvMaxK / 128];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
+    const int64_t n0 = (int64_t)blockIdx.x * kW + wave;    // wave-uniform; < N since kW divides N
+
+    // This wave's share of the activations first (values past K load as
+    // zeros: their groups get scale 0 and code 0), then its weight row: loads
+    // complete in issue order, so the quantisation waits only for the former.
+    const int i0 = (kGemvMaxK / kW) * wave + V * lane;
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)x, 0, (int)(2 * K), 0x00020000);
+    uint32_t raw[V / 2];
+    if constexpr (V == 4) {
+        const i32x2 t = __builtin_bit_cast(i32x2, __builtin_amdgcn_raw_buffer_load_b64(rx, 2 * i0, 0, 0));
+        raw[0] = (uint32_t)t[0];
+        raw[1] = (uint32_t)t[1];
+    } else {
+#pragma unroll
+        for (int h = 0; h < V / 8; ++h) {
+            const i32x4 t = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, 2 * i0 + 16 * h, 0, 0));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) raw[4 * h + j] = (uint32_t)t[j];
+        }
+    }
+    // Every wave's activation loads go out before any wave's weight loads
+    // (a bare barrier: it waits for no load), so the activations do not
+    // queue behind the weights in the memory system.
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    i32x4 wv[kGemvMaxChunks][1];
+    float wsv[kGemvMaxChunks];
+    gemv_load_weights<1>(wq, ws, n0, 1, K, lane, wv, wsv);
+    __builtin_amdgcn_sched_barrier(0);   // keep the weight loads ahead of the quantisation
+
+    float v[V];
+#pragma unroll
+    for (int j = 0; j < V / 2; ++j) {
+        v[2 * j] = kXBf16 ? bf16_bits_to_float(raw[j] & 0xFFFFu) : f16_bits_to_float(raw[j] & 0xFFFFu);
+        v[2 * j + 1] = kXBf16 ? bf16_bits_to_float(raw[j] >> 16) : f16_bits_to_float(raw[j] >> 16);
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < V; ++j) amax = fmaxf(amax, fabsf(v[j]));
+#pragma unroll
+    for (int off = 1; off < kGroupLanes; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
+    const float s = amax / 448.0f;
+    uint32_t q[V / 4];
+    quantize_v<V>(v, raw, s, q);
+#pragma unroll
+    for (int j = 0; j < V / 4; ++j) reinterpret_cast<uint32_t*>(codes_lds + i0)[j] = q[j];
+    if (lane % kGroupLanes == 0) scale_lds[i0 / 128] = s;
+    __syncthreads();
+
+    float xf[kGemvMaxChunks][16], sx[kGemvMaxChunks];
+#pragma unroll
+    for (int c = 0; c < kGemvMaxChunks; ++c) {
+        const int k = 1024 * c + 16 * lane;
+        e4m3x16_to_f32(*reinterpret_cast<const i32x4*>(codes_lds + k), xf[c]);
+        // Lanes past K: their weights are zero; take scale 0 so that no
+        // stale value enters the promotion.
+        sx[c] = k < K ? scale_lds[k / 128] : 0.0f;
+    }
+    float acc[1];
+    gemv_rows<1>(xf, sx, wv, wsv, acc);
+    if (lane == 0) store_out(y, y_dtype, n0, acc[0]);
+}
+
+hipError_t launch_w8a8_gemv(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws, void* y,
+                            int y_dtype, int64_t N, int64_t K, hipStream_t stream) {
+    if (N % 16 != 0 || K > kGemvMaxK) return hipErrorInvalidValue;
+    // Two rows per wave only for the largest projections (measured, us:
+    // 4096 x 4096 5.28 one row vs 5.53 two; 12288 x 4096 11.2 vs 10.9).
+    const int kr = N >= 8192 ? 2 : 1;
+    const dim3 grid((unsigned)((N + kGemvWaves * kr - 1) / (kGemvWaves * kr)));
+    if (kr == 2)
+        hipLaunchKernelGGL((w8a8_gemv_kernel<2>), grid, dim3(kGemvWaves * kWave), 0, stream, xq, xs, wq, ws, y,
+                           y_dtype, N, K);
+    else
+        hipLaunchKernelGGL((w8a8_gemv_kernel<1>), grid, dim3(kGemvWaves * kWave), 0, stream, xq, xs, wq, ws, y,
+                           y_dtype, N, K);
+    return hipGetLastError();
+}
+
+hipError_t launch_w8a8_gemv_quant(const void* x, bool x_bf16, const uint8_t* wq, const float* ws, void* y,
+                                  int y_dtype, int64_t N, int64_t K, hipStream_t stream) {
+    if (N % 16 != 0 || K > kGemvMaxK) return hipErrorInvalidValue;   // every wave owns a row
+    const uint16_t* xh = static_cast<const uint16_t*>(x);
+    // Sixteen rows per workgroup where that still gives 256 workgroups, else four.
+    if (N >= 16 * 256) {
+        const dim3 grid((unsigned)(N / 16));
+        if (x_bf16) hipLaunchKernelGGL((w8a8_gemv_quant_kernel<true, 16>), grid, dim3(16 * kWave), 0, stream, xh, wq, ws, y, y_dtype, N, K);
+        else hipLaunchKernelGGL((w8a8_gemv_quant_kernel<false, 16>), grid, dim3(16 * kWave), 0, stream, xh, wq, ws, y, y_dtype, N, K);
+    } else {
+        const dim3 grid((unsigned)(N / 4));
+        if (x_bf16) hipLaunchKernelGGL((w8a8_gemv_quant_kernel<true, 4>), grid, dim3(4 * kWave), 0, stream, xh, wq, ws, y, y_dtype, N, K);
+        else hipLaunchKernelGGL((w8a8_gemv_quant_kernel<false, 4>), grid, dim3(4 * kWave), 0, stream, xh, wq, ws, y, y_dtype, N, K);
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_w8a8_stream(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
                               void* y, int y_dtype, int64_t M, int64_t N, int64_t K,
                               void* workspace, hipStream_t stream) {

@@ -52,6 +52,51 @@ inline void stream_workspace_parts(const StreamPlan& p, void* ws, uint32_t*& cou
     partials = reinterpret_cast<float*>(static_cast<char*>(ws) + stream_counter_bytes(p));
 }
 
+// ------------------------------------------- one-token dot products ----
+// Shared by the W8A8 and W8A16 kernels for M = 1 (K <= kGemvMaxK): four
+// waves per workgroup, lane l of a wave covering K offsets 1024 c + 16 l of
+// each 1 KB chunk c of its weight rows.
+constexpr int kGemvWaves = 4;
+constexpr int kGemvMaxChunks = 4;
+constexpr int64_t kGemvMaxK = 1024 * kGemvMaxChunks;
+
+// The 16 E4M3 codes of v (K order) widened to fp32; exact for every finite code.
+__device__ __forceinline__ void e4m3x16_to_f32(i32x4 v, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(v[i], false), hi = __builtin_amdgcn_cvt_pk_f32_fp8(v[i], true);
+        f[4 * i] = lo[0];
+        f[4 * i + 1] = lo[1];
+        f[4 * i + 2] = hi[0];
+        f[4 * i + 3] = hi[1];
+    }
+}
+
+// Sum of x[i] * w[i] over one lane's 16 values, then over the 8 lanes of its
+// 128-K block (lanes 8 j .. 8 j + 7): every lane of the group returns the
+// block's dot product, in one fixed order.
+__device__ __forceinline__ float block_dot16(const float* x, const float* w) {
+    float d0 = 0.0f, d1 = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+        d0 = __builtin_fmaf(x[i], w[i], d0);
+        d1 = __builtin_fmaf(x[i + 1], w[i + 1], d1);
+    }
+    float d = d0 + d1;
+    d += __shfl_xor(d, 1, kWave);
+    d += __shfl_xor(d, 2, kWave);
+    d += __shfl_xor(d, 4, kWave);
+    return d;
+}
+
+// Sum of the eight block groups' promoted sums of a lane (lanes 8 apart).
+__device__ __forceinline__ float group_sum8(float v) {
+    v += __shfl_xor(v, 8, kWave);
+    v += __shfl_xor(v, 16, kWave);
+    v += __shfl_xor(v, 32, kWave);
+    return v;
+}
+
 // ------------------------------------------------------ weight slabs ----
 // The 16 weight rows of one 128-K block (2 KB), staged in LDS with two
 // direct-to-LDS loads of whole 128-byte lines (8 rows each): a load

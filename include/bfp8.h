@@ -159,10 +159,11 @@ bfp8_status bfp8_gemm_w8a8_blk128(const uint8_t* xq, const float* xs,
  *   wq, ws, y, y_dtype: as for bfp8_gemm_w8a8_blk128.
  *   workspace: at least bfp8_workspace_bytes(BFP8_OP_QUANT_GEMM_W8A8_BLK128,
  *       M, N, K) bytes, zero-filled before its first use, left ready for the
- *       next call; calls that overlap in time must not share one.  For M <= 8
- *       where bfp8_gemm_w8a8_blk128 uses the weight-streaming kernel, that
- *       kernel quantises in registers; otherwise the codes and scales are
- *       staged in the workspace by the 1x128 quantiser.
+ *       next call; calls that overlap in time must not share one.  For M = 1
+ *       with K <= 4096 (the one-token kernel; no workspace) and for M <= 8
+ *       where bfp8_gemm_w8a8_blk128 uses the weight-streaming kernel, the
+ *       kernel quantises the activations itself; otherwise the codes and
+ *       scales are staged in the workspace by the 1x128 quantiser.
  * Requires M >= 1, N >= 16, N % 16 == 0, K >= 128, K % 128 == 0, K <= 2^23.
  */
 bfp8_status bfp8_quant_gemm_w8a8_blk128(const void* x, int x_dtype,
@@ -180,8 +181,10 @@ bfp8_status bfp8_quant_gemm_w8a8_blk128(const void* x, int x_dtype,
  *   x   [M, K] bf16 or fp16, wq [N, K] E4M3, ws [ceil(N/128), K/128] fp32.
  *   y   [M, N] in y_dtype (BF16 / F16 / F32); workspace as for W8A8 (sized
  *       by bfp8_workspace_bytes(BFP8_OP_GEMM_W8A16_BLK128, M, N, K)).
- * M <= 16 streams the weights (decode); larger M runs a tiled MFMA kernel
- * that widens each weight fragment once per wave and reuses it for up to 64
+ * M = 1 with K <= 4096 runs a dot-product kernel on the vector ALUs (the
+ * weights widened to fp32); M <= 16 otherwise streams the weights (decode);
+ * larger M reads all tokens per weight tile or runs a tiled MFMA kernel that
+ * widens each weight fragment once per wave and reuses it for up to 64
  * tokens ([3090] §4.4: at prefill the weight-only cost is a few percent).
  * Requires M >= 1, N % 16 == 0, K % 128 == 0, K <= 2^23.
  */
@@ -238,7 +241,9 @@ size_t bfp8_workspace_bytes(int op, int64_t M, int64_t N, int64_t K);
  *   n_multiple    N must be a multiple of this.
  *   align_bytes   required alignment of every device pointer.
  *   m_stream_max  largest M always served by the weight-streaming decode
- *                 kernel (W8A8 streams it when K needs no split across
+ *                 kernels (one token with K <= 4096 runs a dot-product
+ *                 kernel on the vector ALUs instead, for every blk128 GEMM
+ *                 and the fused call; W8A8 streams when K needs no split across
  *                 workgroups, or N < 1024; W8A8 also streams up to
  *                 4 * m_stream_max, one workgroup per 16-token tile, when
  *                 those workgroups fit one round on the CUs without a split

@@ -50,6 +50,16 @@ def test_w8a8_across_the_stream_tile_threshold(gpu_lib, M):
     _w8a8_check(M, 384, 640, 300 + M, what="threshold")
 
 
+@pytest.mark.parametrize("N,K", [(16, 128), (16, 1152), (64, 4096), (1024, 4096), (2064, 1024), (4096, 3968),
+                                 (12288, 2048)])
+def test_w8a8_one_token(gpu_lib, N, K):
+    """M = 1 with K <= 4096: the vector-ALU dot-product kernel (one or two
+    weight rows per wave), with K of one block, K ending inside a 1 KB chunk
+    and shorter than the four chunks the kernel reads; no workspace."""
+    assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 1, N, K) == 0
+    _w8a8_check(1, N, K, 450 + N + K // 128, what="one token")
+
+
 @pytest.mark.parametrize("N", [16, 48, 144, 272])
 @pytest.mark.parametrize("M", [4, 40])
 def test_w8a8_weight_scale_rows_straddle(gpu_lib, M, N):
@@ -132,20 +142,26 @@ def test_w8a8_large_tile_ragged_sampled(gpu_lib):
 
 
 @pytest.mark.parametrize("xdtype", [torch.bfloat16, torch.float16])
-@pytest.mark.parametrize("M,N,K", [(1, 4096, 4096), (2, 1024, 4096), (3, 512, 640), (4, 384, 12288),
+@pytest.mark.parametrize("M,N,K", [(1, 4096, 4096), (1, 16, 128), (1, 1024, 1152), (1, 2064, 3968),
+                                   (1, 512, 4224), (2, 1024, 4096), (3, 512, 640), (4, 384, 12288),
                                    (5, 1024, 4096), (8, 512, 1024), (9, 512, 640), (16, 1024, 4096),
                                    (17, 384, 640), (64, 1024, 4096), (300, 1040, 1024)])
 def test_quant_gemm_equals_quantise_then_gemm(gpu_lib, M, N, K, xdtype):
     """The fused call is bit-identical to bfp8_quantize_act_1x128 followed by
     bfp8_gemm_w8a8_blk128 (fp32 and 16-bit outputs), and meets the oracle bar.
-    bf16 cases include a zero row and rows whose group scales lie outside
-    [2^-90, 2^100] (the quantiser's IEEE-division path)."""
+    bf16 cases include a zero row (a zero group at M = 1) and rows (groups)
+    whose scales lie outside [2^-90, 2^100] (the quantiser's IEEE-division
+    path)."""
     say("quant+w8a8", xdtype, f"M={M} N={N} K={K}")
     x = inputs.activations(M, K, workload=900 + M, stream=K, outliers=True, dtype=xdtype).float()
     if xdtype == torch.bfloat16 and M >= 3:
         x[0] = 0.0
         x[1] *= 2.0 ** -100
         x[2] *= 2.0 ** 110
+    if xdtype == torch.bfloat16 and M == 1 and K >= 512:
+        x[0, :128] = 0.0
+        x[0, 256:384] *= 2.0 ** -100
+        x[0, 384:512] *= 2.0 ** 110
     x = x.to(xdtype)
     wq, ws = oracle.quantize_weight_128x128(f32(inputs.weights_bf16(N, K, workload=900 + N, stream=K)))
     wqd, wsd, xd = dev(wq), dev(ws), x.cuda()
@@ -189,10 +205,10 @@ def test_w8a8_prefill_oproj_sampled(gpu_lib):
     assert_16bit_bar(y16[rows], y32[rows], y0, "bf16", "prefill sampled rows")
 
 
-@pytest.mark.parametrize("M", [3, 48])
+@pytest.mark.parametrize("M", [1, 3, 48])
 def test_w8a8_one_hot_all_codes_exact(gpu_lib, M):
     """xq one-hot 1.0 at column k, unit scales: Y[:, n] = E4M3(wq[n, k]) exactly,
-    for every finite code (stream and tile kernels)."""
+    for every finite code (one-token, stream and all-token kernels)."""
     N, K = 256, 256
     wq = np.zeros((N, K), np.uint8)
     wq[:254, :] = FINITE_CODES[:, None]
@@ -232,6 +248,27 @@ def test_w8a16_blk128(gpu_lib, M, xdtype):
 
 
 @pytest.mark.parametrize("xdtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("N,K", [(16, 128), (16, 1152), (64, 4096), (1024, 4096), (2064, 1024), (4096, 4096),
+                                 (4096, 3968), (12288, 2048)])
+def test_w8a16_gemv_one_token(gpu_lib, N, K, xdtype):
+    """M = 1 with K <= 4096: the vector-ALU dot-product kernel, one or two
+    weight rows per wave; a K of one block, K ending inside a 1 KB chunk
+    (1152, 3968) and shorter than the four chunks the kernel always reads,
+    N of one workgroup; all three output types."""
+    say("w8a16 gemv", xdtype, f"N={N} K={K}")
+    assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A16_BLK128, 1, N, K) == 0
+    x = inputs.activations(1, K, workload=660 + N, stream=K, outliers=True, dtype=xdtype)
+    wq, ws = oracle.quantize_weight_128x128(f32(inputs.weights_bf16(N, K, workload=661, stream=K)))
+    y0 = oracle.gemm_w8a16_blk128(f32(x), wq, ws)
+    xd, wqd, wsd = x.cuda(), dev(wq), dev(ws)
+    y32 = run_w8a16(xd, wqd, wsd, torch.float32)
+    assert_fp32_bar(y32, y0, f"w8a16 gemv N={N} K={K}")
+    for out in (torch.bfloat16, torch.float16):
+        y16 = run_w8a16(xd, wqd, wsd, out)
+        assert_16bit_bar(y16, y32, y0, "bf16" if out == torch.bfloat16 else "f16", f"w8a16 gemv N={N} K={K}")
+
+
+@pytest.mark.parametrize("xdtype", [torch.bfloat16, torch.float16])
 @pytest.mark.parametrize("M,N,K", [(17, 1024, 4096), (32, 4096, 4096), (50, 1024, 4096), (64, 4096, 4096),
                                    (24, 12288, 512), (20, 16, 4096), (20, 64, 128), (128, 4096, 4096),
                                    (100, 4112, 1024), (256, 1024, 4096), (200, 1040, 1024)])
@@ -267,10 +304,11 @@ def test_w8a16_blk128_long_k(gpu_lib, M):
 
 
 @pytest.mark.parametrize("xdtype", [torch.bfloat16, torch.float16])
-@pytest.mark.parametrize("M", [4, 40])
+@pytest.mark.parametrize("M", [1, 4, 40])
 def test_w8a16_blk128_one_hot_all_codes_exact(gpu_lib, xdtype, M):
     """x one-hot 1.0: Y[:, n] = E4M3(wq[n, k]) * ws exactly, subnormal codes
-    included (streaming kernel at M = 4, all-token kernel at M = 40)."""
+    included (vector-ALU kernel at M = 1, streaming kernel at M = 4,
+    all-token kernel at M = 40)."""
     N, K = 256, 256
     wq = np.zeros((N, K), np.uint8)
     wq[:254, :] = FINITE_CODES[:, None]
