@@ -103,8 +103,8 @@ def test_workspace_sizes(lib):
     assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 1, 1024, 12288) == 0  # all-token kernel
     assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 4096, 1024, 4096) == 0   # 128x128 tiles
     assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 4096, 4096, 4096) == 0   # 256x256 tiles
-    # 16 < M <= 32 (and M <= 64 on at most 2^24 weights): one workgroup per 16
-    # weight rows holds every token over all of K, no workspace
+    # 16 < M <= 32, and M * N <= 2^19 with K <= 4096: one workgroup per 16 or
+    # 32 weight rows holds every token of its group over all of K, no workspace
     assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 32, 1024, 4096) == 0
     assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 32, 12288, 4096) == 0
     assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 64, 4096, 4096) == 0
@@ -117,6 +117,15 @@ def test_workspace_sizes(lib):
     assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 100, 4096, 4096) == 0    # all-token kernel
     assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 64, 384, 640) == 0      # K too short to split
     assert bfp8.bfp8_workspace_bytes(bfp8.OP_QUANT_ACT_1X128, 1, 4096, 4096) == 0
+    # one token with K <= 4096 runs the dot-product kernels, which need none,
+    # for every blk128 GEMM and the fused call (staged codes otherwise need room)
+    for op in (bfp8.OP_GEMM_W8A8_BLK128, bfp8.OP_QUANT_GEMM_W8A8_BLK128, bfp8.OP_GEMM_W8A16_BLK128):
+        for n, k in ((16, 128), (1024, 4096), (12288, 4096), (2064, 3968)):
+            assert bfp8.bfp8_workspace_bytes(op, 1, n, k) == 0, (op, n, k)
+    # past K = 4096 one token streams, the fused call quantising in registers:
+    # its workspace is the codes call's split-K workspace
+    assert bfp8.bfp8_workspace_bytes(bfp8.OP_QUANT_GEMM_W8A8_BLK128, 1, 512, 12288) == \
+        bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 1, 512, 12288) > 0
 
 
 @pytest.mark.parametrize("args,expect", [
