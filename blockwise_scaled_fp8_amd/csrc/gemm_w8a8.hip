@@ -701,8 +701,7 @@ __global__ __launch_bounds__(kW * kWave) void w8a8_gemv_quant_kernel(
     float amax = 0.0f;
 #pragma unroll
     for (int j = 0; j < V; ++j) amax = fmaxf(amax, fabsf(v[j]));
-#pragma unroll
-    for (int off = 1; off < kGroupLanes; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
+    amax = group_max<kGroupLanes>(amax);
     const float s = amax / 448.0f;
     uint32_t q[V / 4];
     quantize_v<V>(v, raw, s, q);

@@ -21,6 +21,8 @@
 // reads complete partial tiles.
 #pragma once
 
+#include <type_traits>
+
 #include "bfp8_device.hpp"
 #include "bfp8_launch.hpp"
 
@@ -72,9 +74,19 @@ __device__ __forceinline__ void e4m3x16_to_f32(i32x4 v, float* f) {
     }
 }
 
+// v plus the value of the lane given by DPP control `ctl` (a lane move
+// inside the ALU, no LDS round trip).
+template <int ctl>
+__device__ __forceinline__ float add_dpp(float v) {
+    return v + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), ctl, 0xF, 0xF, false));
+}
+
 // Sum of x[i] * w[i] over one lane's 16 values, then over the 8 lanes of its
 // 128-K block (lanes 8 j .. 8 j + 7): every lane of the group returns the
-// block's dot product, in one fixed order.
+// block's dot product, in one fixed order.  The lane sums pair lanes i ^ 1,
+// then i ^ 2 (quad permutes), then the other quad of the eight (half-row
+// mirror: after the first two steps every lane of a quad holds the same
+// value, so lane 7 - i stands for lane i ^ 4).
 __device__ __forceinline__ float block_dot16(const float* x, const float* w) {
     float d0 = 0.0f, d1 = 0.0f;
 #pragma unroll
@@ -83,15 +95,33 @@ __device__ __forceinline__ float block_dot16(const float* x, const float* w) {
         d1 = __builtin_fmaf(x[i + 1], w[i + 1], d1);
     }
     float d = d0 + d1;
-    d += __shfl_xor(d, 1, kWave);
-    d += __shfl_xor(d, 2, kWave);
-    d += __shfl_xor(d, 4, kWave);
+    d = add_dpp<0xB1>(d);    // quad_perm [1, 0, 3, 2]: lane i ^ 1
+    d = add_dpp<0x4E>(d);    // quad_perm [2, 3, 0, 1]: lane i ^ 2
+    d = add_dpp<0x141>(d);   // row_half_mirror: the other quad
     return d;
+}
+
+// Maximum over aligned groups of kLanes lanes (2 .. 64): lane moves inside
+// the ALU up to 16 lanes (the half-row mirror and row rotation stand for
+// i ^ 4 and i ^ 8 once the smaller groups agree), LDS permutes beyond.
+template <int kLanes>
+__device__ __forceinline__ float group_max(float v) {
+    auto max_dpp = [](float a, auto ctl) {
+        return fmaxf(a, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, a), decltype(ctl)::value,
+                                                                          0xF, 0xF, false)));
+    };
+    if constexpr (kLanes > 1) v = max_dpp(v, std::integral_constant<int, 0xB1>{});
+    if constexpr (kLanes > 2) v = max_dpp(v, std::integral_constant<int, 0x4E>{});
+    if constexpr (kLanes > 4) v = max_dpp(v, std::integral_constant<int, 0x141>{});
+    if constexpr (kLanes > 8) v = max_dpp(v, std::integral_constant<int, 0x128>{});
+    if constexpr (kLanes > 16) v = fmaxf(v, __shfl_xor(v, 16, kWave));
+    if constexpr (kLanes > 32) v = fmaxf(v, __shfl_xor(v, 32, kWave));
+    return v;
 }
 
 // Sum of the eight block groups' promoted sums of a lane (lanes 8 apart).
 __device__ __forceinline__ float group_sum8(float v) {
-    v += __shfl_xor(v, 8, kWave);
+    v = add_dpp<0x128>(v);   // row_ror 8: lane i ^ 8 within its row of 16
     v += __shfl_xor(v, 16, kWave);
     v += __shfl_xor(v, 32, kWave);
     return v;
