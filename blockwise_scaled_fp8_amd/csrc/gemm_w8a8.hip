@@ -744,16 +744,12 @@ hipError_t launch_w8a8_gemv_quant(const void* x, bool x_bf16, const uint8_t* wq,
                                   int y_dtype, int64_t N, int64_t K, hipStream_t stream) {
     if (N % 16 != 0 || K > kGemvMaxK) return hipErrorInvalidValue;   // every wave owns a row
     const uint16_t* xh = static_cast<const uint16_t*>(x);
-    // Sixteen rows per workgroup where that still gives 256 workgroups, else four.
-    if (N >= 16 * 256) {
-        const dim3 grid((unsigned)(N / 16));
-        if (x_bf16) hipLaunchKernelGGL((w8a8_gemv_quant_kernel<true, 16>), grid, dim3(16 * kWave), 0, stream, xh, wq, ws, y, y_dtype, N, K);
-        else hipLaunchKernelGGL((w8a8_gemv_quant_kernel<false, 16>), grid, dim3(16 * kWave), 0, stream, xh, wq, ws, y, y_dtype, N, K);
-    } else {
-        const dim3 grid((unsigned)(N / 4));
-        if (x_bf16) hipLaunchKernelGGL((w8a8_gemv_quant_kernel<true, 4>), grid, dim3(4 * kWave), 0, stream, xh, wq, ws, y, y_dtype, N, K);
-        else hipLaunchKernelGGL((w8a8_gemv_quant_kernel<false, 4>), grid, dim3(4 * kWave), 0, stream, xh, wq, ws, y, y_dtype, N, K);
-    }
+    // Four waves (rows) per workgroup: each wave quantises a quarter of the
+    // token, 16 values per lane, its group maximum all in lane moves (measured
+    // 5.29 vs 5.43 us for sixteen waves at N = K = 4096, even at N = 12288).
+    const dim3 grid((unsigned)(N / 4));
+    if (x_bf16) hipLaunchKernelGGL((w8a8_gemv_quant_kernel<true, 4>), grid, dim3(4 * kWave), 0, stream, xh, wq, ws, y, y_dtype, N, K);
+    else hipLaunchKernelGGL((w8a8_gemv_quant_kernel<false, 4>), grid, dim3(4 * kWave), 0, stream, xh, wq, ws, y, y_dtype, N, K);
     return hipGetLastError();
 }
 
