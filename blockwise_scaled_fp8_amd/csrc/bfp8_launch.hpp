@@ -146,7 +146,7 @@ inline bool w8a16_wide(int64_t M, int64_t N, int64_t K) {
 // workspace (launch_w8a8_gemv, launch_w8a8_gemv_quant, launch_w8a16_gemv).
 // Measured against the streaming MFMA kernels (us, 32 rotated weight
 // copies): N = K = 4096 W8A8 codes 5.02 vs 5.45, fused quantise + W8A8
-// 5.49 vs 5.82, W8A16 5.33 vs 5.69; 1024 x 4096 W8A8 3.08 vs 3.87;
+// 5.35 vs 5.82, W8A16 5.33-5.42 vs 5.69; 1024 x 4096 W8A8 3.08 vs 3.87;
 // 12288 x 4096 W8A8 9.97 vs 11.0.
 inline bool one_token(int64_t M, int64_t K) { return M == 1 && K <= 4096; }
 hipError_t launch_w8a8_gemv(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws, void* y,

@@ -533,9 +533,10 @@ hipError_t launch_w8a16_wide(const void* x, bool x_bf16, const uint8_t* wq, cons
 // row.  Every load is issued before the first product; there is no LDS
 // staging and no barrier, so the cross-wave reduction of the streaming
 // kernel, about half a microsecond of a 5.7 us launch at N = K = 4096, is
-// gone (measured 5.50 vs 5.66 us there, 3.05 vs 3.96 us at N = 1024 and
-// 10.8 vs 11.5 us at N = 12288).  Lanes past K read zeros (their offsets
-// are moved past the descriptor's range).
+// gone (measured 5.33-5.42 vs 5.69 us there, 3.00 vs 3.96 us at N = 1024
+// and 11.1 vs 11.5 us at N = 12288).  The lane sums use DPP lane moves
+// (block_dot16, group_sum8).  Lanes past K read zeros (their offsets are
+// moved past the descriptor's range).
 template <bool kXBf16>
 __device__ __forceinline__ float half_bits_to_f32(uint32_t h) {
     if constexpr (kXBf16) return __builtin_bit_cast(float, h << 16);
