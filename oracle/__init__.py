@@ -31,7 +31,12 @@ Modules:
 
 Every function is pinned by tests in ``tests/test_oracle_*.py`` against facts
 the pages or mathematics fix (bitwise identities, brute force, exact rational
-arithmetic, library special cases); none is "parity unpinned".
+arithmetic, library special cases); the tolerance bar in ``compare`` is pinned
+by hand-computed error measures, arrays just inside and just outside each
+bound, and half-ulps checked against the 16-bit formats' bit patterns
+(``tests/test_oracle_compare.py``).  Planted mistakes in copies of these
+functions make a pin fail (``tests/test_oracle_mutations.py``).  No function
+is "parity unpinned".
 """
 
 from .e4m3 import e4m3_decode, e4m3_encode, E4M3_MAX, E4M3_NAN_CODES

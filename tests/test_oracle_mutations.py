@@ -128,3 +128,133 @@ def test_dequant_mistakes_are_caught(monkeypatch, bad):
         except AssertionError:
             failures += 1
     assert failures >= 1
+
+
+# ------------------------------------------------------- the tolerance bar ----
+
+def _error_rms_over_output(y, y0):
+    from oracle import gemm_error
+    e = gemm_error(y, y0)
+    e["rms_ref"] = float(np.sqrt(np.mean(np.asarray(y, np.float64) ** 2)))
+    return e
+
+
+def _error_rel_over_output(y, y0):
+    from oracle import gemm_error
+    e = gemm_error(y, y0)
+    d = np.asarray(y, np.float64) - np.asarray(y0, np.float64)
+    e["rel_frob"] = float(np.linalg.norm(d)) / float(np.linalg.norm(np.asarray(y, np.float64)))
+    return e
+
+
+def _error_mean_not_max(y, y0):
+    from oracle import gemm_error
+    e = gemm_error(y, y0)
+    e["max_abs_err"] = float(np.mean(np.abs(np.asarray(y, np.float64) - np.asarray(y0, np.float64))))
+    return e
+
+
+@pytest.mark.parametrize("bad", [_error_rms_over_output, _error_rel_over_output, _error_mean_not_max])
+def test_error_measure_mistakes_are_caught(monkeypatch, bad):
+    import tests.test_oracle_compare as pins_cmp
+    monkeypatch.setattr(pins_cmp, "gemm_error", bad)
+    failures = 0
+    for pin in (pins_cmp.test_gemm_error_hand_computed, pins_cmp.test_gemm_error_rms_is_over_the_reference,
+                pins_cmp.test_gemm_error_uses_the_largest_element_error):
+        try:
+            pin()
+        except AssertionError:
+            failures += 1
+    assert failures >= 1
+
+
+def _fp32_bar_constants(max_frac, rel):
+    def check(y, y0):
+        from oracle import gemm_error
+        e = gemm_error(y, y0)
+        return e["max_abs_err"] <= max_frac * e["rms_ref"] and e["rel_frob"] <= rel, e
+    return check
+
+
+@pytest.mark.parametrize("bad", [_fp32_bar_constants(1e-3, 4e-3), _fp32_bar_constants(2e-2, 4e-3),
+                                 _fp32_bar_constants(1e-2, 4e-2), _fp32_bar_constants(1e-2, 2e-3)])
+def test_fp32_bar_constant_mistakes_are_caught(monkeypatch, bad):
+    import tests.test_oracle_compare as pins_cmp
+    monkeypatch.setattr(pins_cmp, "check_gemm_fp32", bad)
+    failures = 0
+    for factor, ok in ((1 - 1e-6, True), (1 + 1e-6, False)):
+        for pin in (pins_cmp.test_fp32_max_error_bound_flips, pins_cmp.test_fp32_relative_bound_flips):
+            try:
+                pin(factor, ok)
+            except AssertionError:
+                failures += 1
+    assert failures >= 1
+
+
+def _half_ulp_full_ulp(y0, mant_bits, min_exp):
+    from oracle.compare import _half_ulp
+    return 2.0 * _half_ulp(y0, mant_bits, min_exp)
+
+
+def _half_ulp_no_subnormal_floor(y0, mant_bits, min_exp):
+    a = np.abs(np.asarray(y0, np.float64))
+    _, ex = np.frexp(np.where(a > 0, a, 1.0))
+    return np.exp2((ex - 1 - mant_bits).astype(np.float64)) / 2.0
+
+
+def _half_ulp_exponent_off_by_one(y0, mant_bits, min_exp):
+    from oracle.compare import _half_ulp
+    return _half_ulp(y0, mant_bits - 1, min_exp)
+
+
+@pytest.mark.parametrize("bad", [_half_ulp_full_ulp, _half_ulp_no_subnormal_floor, _half_ulp_exponent_off_by_one])
+def test_half_ulp_mistakes_are_caught(monkeypatch, bad):
+    import tests.test_oracle_compare as pins_cmp
+    monkeypatch.setattr(pins_cmp, "_half_ulp", bad)
+    failures = 0
+    for pin in (pins_cmp.test_half_ulp_f16_every_finite_value, pins_cmp.test_half_ulp_bf16_normals_and_subnormals,
+                pins_cmp.test_half_ulp_between_representable_values):
+        try:
+            pin()
+        except AssertionError:
+            failures += 1
+    assert failures >= 1
+
+
+def _16bit_without_half_ulp(y, y0, fmt):
+    from oracle import check_gemm_fp32
+    return check_gemm_fp32(y, y0)
+
+
+def _16bit_without_relative_bound(y, y0, fmt):
+    from oracle import gemm_error
+    from oracle.compare import _half_ulp
+    mant_bits, min_exp = {"bf16": (7, -126), "f16": (10, -14)}[fmt]
+    e = gemm_error(y, y0)
+    bound = 1e-2 * e["rms_ref"] + _half_ulp(y0, mant_bits, min_exp)
+    return bool(np.all(np.abs(np.asarray(y, np.float64) - np.asarray(y0, np.float64)) <= bound)), e
+
+
+def _16bit_formats_swapped(y, y0, fmt):
+    from oracle import check_gemm_16bit
+    return check_gemm_16bit(y, y0, "f16" if fmt == "bf16" else "bf16")
+
+
+@pytest.mark.parametrize("bad", [_16bit_without_half_ulp, _16bit_without_relative_bound, _16bit_formats_swapped])
+def test_16bit_bar_mistakes_are_caught(monkeypatch, bad):
+    import tests.test_oracle_compare as pins_cmp
+    monkeypatch.setattr(pins_cmp, "check_gemm_16bit", bad)
+    failures = 0
+    pins = [lambda fmt=fmt: pins_cmp.test_16bit_rounded_result_passes_where_the_bare_bar_fails(fmt)
+            for fmt in ("bf16", "f16")]
+    pins += [lambda fmt=fmt: pins_cmp.test_16bit_one_ulp_off_fails(fmt) for fmt in ("bf16", "f16")]
+    pins += [lambda fmt=fmt, f=f, ok=ok: pins_cmp.test_16bit_per_element_bound_flips(fmt, f, ok)
+             for fmt in ("bf16", "f16") for f, ok in ((1 - 1e-6, True), (1 + 1e-6, False))]
+    pins += [lambda fmt=fmt, f=f, ok=ok: pins_cmp.test_16bit_relative_bound_flips(fmt, f, ok)
+             for fmt in ("bf16", "f16") for f, ok in ((1 - 1e-6, True), (1 + 1e-6, False))]
+    for pin in pins:
+        try:
+            pin()
+        except AssertionError:
+            failures += 1
+    assert failures >= 1
