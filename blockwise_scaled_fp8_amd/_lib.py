@@ -6,6 +6,13 @@ computation runs in the library's HIP kernels.  Work is enqueued on the
 current torch stream.  A missing library raises at load time; a nonzero
 status raises Bfp8Error with the library's status text.  There is no
 fallback of any kind.
+
+The C functions take bare pointers and cannot see buffer sizes, so before
+each call the binding checks what only it can: every tensor lives on the
+current GPU (host tensors for the host-only packer), is contiguous, has the
+dtype the C argument expects, and has the shape that M, N and K (taken from
+the first operands) imply.  A mismatch raises Bfp8Error before anything is
+enqueued.  Arithmetic and kernel choice stay in the library.
 """
 
 import ctypes
@@ -50,10 +57,15 @@ _lib = None
 
 
 class Bfp8Error(RuntimeError):
-    def __init__(self, status, where):
+    """A nonzero status from the library, or an argument the binding refused
+    before calling it (then `detail` says which and why)."""
+
+    def __init__(self, status, where, detail=None):
         self.status = status
         self.name = STATUS_NAMES.get(status, str(status))
-        super().__init__(f"{where}: {self.name}: {load().bfp8_status_string(status).decode()}")
+        self.detail = detail
+        text = detail if detail is not None else load().bfp8_status_string(status).decode()
+        super().__init__(f"{where}: {self.name}: {text}")
 
 
 def load():
@@ -81,6 +93,61 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+_E_NULL, _E_SHAPE, _E_DTYPE = 1, 2, 3
+_U8, _F32 = (torch.uint8,), (torch.float32,)
+_X16 = (torch.bfloat16, torch.float16)
+_OUT = (torch.bfloat16, torch.float16, torch.float32)
+
+
+def _cdiv(a, b):
+    return -(-a // b)
+
+
+def _arg(where, name, t, dtypes, shape=None, ndim=None):
+    """Refuse a tensor argument that the C call cannot take: missing, of the
+    wrong dtype, not contiguous, or of a shape other than the one the call's
+    sizes imply.  Where it lives is checked afterwards by _placed, once every
+    argument has passed these checks."""
+    if t is None:
+        raise Bfp8Error(_E_NULL, where, f"{name} is None")
+    if not isinstance(t, torch.Tensor):
+        raise Bfp8Error(_E_NULL, where, f"{name} is not a torch tensor")
+    if t.dtype not in dtypes:
+        raise Bfp8Error(_E_DTYPE, where, f"{name} has dtype {t.dtype}, expected one of {list(dtypes)}")
+    if ndim is not None and t.dim() != ndim:
+        raise Bfp8Error(_E_SHAPE, where, f"{name} must be {ndim}-D, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise Bfp8Error(_E_SHAPE, where, f"{name} is not contiguous (strides {t.stride()})")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise Bfp8Error(_E_SHAPE, where, f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _placed(where, device=True, **tensors):
+    """Every tensor on the current GPU (device=True) or in host memory."""
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if device:
+            if not t.is_cuda:
+                raise Bfp8Error(_E_NULL, where, f"{name} is on {t.device}, not on the GPU")
+            if t.device.index != torch.cuda.current_device():
+                raise Bfp8Error(_E_NULL, where, f"{name} is on {t.device}, the current device is "
+                                                f"cuda:{torch.cuda.current_device()}")
+        elif t.device.type != "cpu":
+            raise Bfp8Error(_E_NULL, where, f"{name} must be a host tensor, got {t.device}")
+
+
+def _mat(where, name, t, dtypes):
+    """A 2-D operand whose shape defines sizes; returns its (rows, cols)."""
+    _arg(where, name, t, dtypes, ndim=2)
+    return t.shape
+
+
+def _workspace_arg(where, workspace):
+    if workspace is not None:
+        _arg(where, "workspace", workspace, _U8)
+
+
 def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
@@ -95,63 +162,105 @@ def _ws(workspace):
 
 
 def bfp8_quantize_act_1x128(x, xq, xs):
-    M, K = x.shape
-    _check(load().bfp8_quantize_act_1x128(_ptr(x), _dtype_code(x), M, K, _ptr(xq), _ptr(xs), _stream()),
-           "bfp8_quantize_act_1x128")
+    w = "bfp8_quantize_act_1x128"
+    M, K = _mat(w, "x", x, _X16)
+    _arg(w, "xq", xq, _U8, (M, K))
+    _arg(w, "xs", xs, _F32, (M, _cdiv(K, 128)))
+    _placed(w, x=x, xq=xq, xs=xs)
+    _check(load().bfp8_quantize_act_1x128(_ptr(x), _dtype_code(x), M, K, _ptr(xq), _ptr(xs), _stream()), w)
 
 
-def bfp8_quantize_weight_128x128(w, wq, ws):
-    N, K = w.shape
-    _check(load().bfp8_quantize_weight_128x128(_ptr(w), _dtype_code(w), N, K, _ptr(wq), _ptr(ws), _stream()),
-           "bfp8_quantize_weight_128x128")
+def bfp8_quantize_weight_128x128(w_, wq, ws):
+    w = "bfp8_quantize_weight_128x128"
+    N, K = _mat(w, "w", w_, _X16)
+    _arg(w, "wq", wq, _U8, (N, K))
+    _arg(w, "ws", ws, _F32, (_cdiv(N, 128), _cdiv(K, 128)))
+    _placed(w, w=w_, wq=wq, ws=ws)
+    _check(load().bfp8_quantize_weight_128x128(_ptr(w_), _dtype_code(w_), N, K, _ptr(wq), _ptr(ws), _stream()), w)
 
 
-def bfp8_dequantize_weight(wq, scales, block, w):
-    N, K = wq.shape
-    _check(load().bfp8_dequantize_weight(_ptr(wq), _ptr(scales), block, _ptr(w), _dtype_code(w), N, K, _stream()),
-           "bfp8_dequantize_weight")
+def bfp8_dequantize_weight(wq, scales, block, w_):
+    w = "bfp8_dequantize_weight"
+    N, K = _mat(w, "wq", wq, _U8)
+    if block not in (32, 128):
+        raise Bfp8Error(_E_SHAPE, w, f"block must be 32 or 128, got {block}")
+    _arg(w, "scales", scales, _F32, (_cdiv(N, block), _cdiv(K, block)))
+    _arg(w, "w", w_, _OUT, (N, K))
+    _placed(w, wq=wq, scales=scales, w=w_)
+    _check(load().bfp8_dequantize_weight(_ptr(wq), _ptr(scales), block, _ptr(w_), _dtype_code(w_), N, K, _stream()),
+           w)
+
+
+def _weights_blk128(w, wq, ws, K):
+    N, Kw = _mat(w, "wq", wq, _U8)
+    if Kw != K:
+        raise Bfp8Error(_E_SHAPE, w, f"wq has K = {Kw}, the activations have K = {K}")
+    _arg(w, "ws", ws, _F32, (_cdiv(N, 128), _cdiv(K, 128)))
+    return N
 
 
 def bfp8_gemm_w8a8_blk128(xq, xs, wq, ws, y, workspace=None):
-    M, K = xq.shape
-    N = wq.shape[0]
+    w = "bfp8_gemm_w8a8_blk128"
+    M, K = _mat(w, "xq", xq, _U8)
+    _arg(w, "xs", xs, _F32, (M, _cdiv(K, 128)))
+    N = _weights_blk128(w, wq, ws, K)
+    _arg(w, "y", y, _OUT, (M, N))
+    _workspace_arg(w, workspace)
+    _placed(w, xq=xq, xs=xs, wq=wq, ws=ws, y=y, workspace=workspace)
     wsp, wsb = _ws(workspace)
     _check(load().bfp8_gemm_w8a8_blk128(_ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), _ptr(y), _dtype_code(y),
-                                        M, N, K, wsp, wsb, _stream()), "bfp8_gemm_w8a8_blk128")
+                                        M, N, K, wsp, wsb, _stream()), w)
 
 
 def bfp8_quant_gemm_w8a8_blk128(x, wq, ws, y, workspace=None):
-    M, K = x.shape
-    N = wq.shape[0]
+    w = "bfp8_quant_gemm_w8a8_blk128"
+    M, K = _mat(w, "x", x, _X16)
+    N = _weights_blk128(w, wq, ws, K)
+    _arg(w, "y", y, _OUT, (M, N))
+    _workspace_arg(w, workspace)
+    _placed(w, x=x, wq=wq, ws=ws, y=y, workspace=workspace)
     wsp, wsb = _ws(workspace)
     _check(load().bfp8_quant_gemm_w8a8_blk128(_ptr(x), _dtype_code(x), _ptr(wq), _ptr(ws), _ptr(y),
-                                              _dtype_code(y), M, N, K, wsp, wsb, _stream()),
-           "bfp8_quant_gemm_w8a8_blk128")
+                                              _dtype_code(y), M, N, K, wsp, wsb, _stream()), w)
 
 
 def bfp8_gemm_w8a16_blk128(x, wq, ws, y, workspace=None):
-    M, K = x.shape
-    N = wq.shape[0]
+    w = "bfp8_gemm_w8a16_blk128"
+    M, K = _mat(w, "x", x, _X16)
+    N = _weights_blk128(w, wq, ws, K)
+    _arg(w, "y", y, _OUT, (M, N))
+    _workspace_arg(w, workspace)
+    _placed(w, x=x, wq=wq, ws=ws, y=y, workspace=workspace)
     wsp, wsb = _ws(workspace)
     _check(load().bfp8_gemm_w8a16_blk128(_ptr(x), _dtype_code(x), _ptr(wq), _ptr(ws), _ptr(y), _dtype_code(y),
-                                         M, N, K, wsp, wsb, _stream()), "bfp8_gemm_w8a16_blk128")
+                                         M, N, K, wsp, wsb, _stream()), w)
 
 
 def bfp8_gemm_w8a16_blk32_ue8m0(x, wq, e8m0, y, workspace=None):
-    M, K = x.shape
-    N = wq.shape[0]
+    w = "bfp8_gemm_w8a16_blk32_ue8m0"
+    M, K = _mat(w, "x", x, _X16)
+    N, Kw = _mat(w, "wq", wq, _U8)
+    if Kw != K:
+        raise Bfp8Error(_E_SHAPE, w, f"wq has K = {Kw}, the activations have K = {K}")
+    _arg(w, "e8m0", e8m0, _U8, (_cdiv(N, 32), _cdiv(K, 32)))
+    _arg(w, "y", y, _OUT, (M, N))
+    _workspace_arg(w, workspace)
+    _placed(w, x=x, wq=wq, e8m0=e8m0, y=y, workspace=workspace)
     wsp, wsb = _ws(workspace)
     _check(load().bfp8_gemm_w8a16_blk32_ue8m0(_ptr(x), _dtype_code(x), _ptr(wq), _ptr(e8m0), _ptr(y),
-                                              _dtype_code(y), M, N, K, wsp, wsb, _stream()),
-           "bfp8_gemm_w8a16_blk32_ue8m0")
+                                              _dtype_code(y), M, N, K, wsp, wsb, _stream()), w)
 
 
 def bfp8_prepare_blk32_ue8m0(wq_host, scale_host):
     """Host tensors in, (status, e8m0 uint8 host tensor or None, bad_index) out;
     refusals are returned, not raised, so callers can act on the index."""
+    w = "bfp8_prepare_blk32_ue8m0"
     wq_host = wq_host.contiguous()
     scale_host = scale_host.contiguous()
+    _arg(w, "wq_host", wq_host, _U8, ndim=2)
     N, K = wq_host.shape
+    _arg(w, "scale_host", scale_host, _F32, (_cdiv(N, 32), _cdiv(K, 32)))
+    _placed(w, device=False, wq_host=wq_host, scale_host=scale_host)
     out = torch.empty((N // 32, K // 32), dtype=torch.uint8)
     bad = ctypes.c_int64(-1)
     st = load().bfp8_prepare_blk32_ue8m0(_ptr(wq_host), _ptr(scale_host), N, K, _ptr(out), ctypes.byref(bad))
