@@ -50,8 +50,17 @@ SIGNATURES = {
     "bfp8_prepare_blk32_ue8m0": (_I, [_P, _P, _I64, _I64, _P, ctypes.POINTER(_I64)]),
     "bfp8_workspace_bytes": (_SZ, [_I, _I64, _I64, _I64]),
     "bfp8_get_limits": (_I, [_I] + [ctypes.POINTER(_I64)] * 4),
+    "bfp8_get_plan": (_I, [_I, _I64, _I64, _I64, _P]),
+    "bfp8_kernel_name": (ctypes.c_char_p, [_I]),
     "bfp8_status_string": (ctypes.c_char_p, [_I]),
 }
+
+
+class Plan(ctypes.Structure):
+    """struct bfp8_plan of include/bfp8.h."""
+    _fields_ = [("kernel", ctypes.c_int32), ("quant_kernel", ctypes.c_int32), ("tile_n", ctypes.c_int32),
+                ("tile_m", ctypes.c_int32), ("waves", ctypes.c_int32), ("splits", ctypes.c_int32),
+                ("workgroups", ctypes.c_int64), ("workspace_bytes", ctypes.c_uint64)]
 
 _lib = None
 
@@ -276,6 +285,21 @@ def bfp8_get_limits(op):
     _check(load().bfp8_get_limits(op, *[ctypes.byref(v) for v in vals]), "bfp8_get_limits")
     return {"k_multiple": vals[0].value, "n_multiple": vals[1].value,
             "align_bytes": vals[2].value, "m_stream_max": vals[3].value}
+
+
+def bfp8_get_plan(op, M, N, K):
+    """The launch plan the library uses for op at M x N x K, as a dict with
+    the kernel's name (host only, no GPU needed)."""
+    p = Plan()
+    _check(load().bfp8_get_plan(op, M, N, K, ctypes.byref(p)), "bfp8_get_plan")
+    out = {f: getattr(p, f) for f, _ in Plan._fields_}
+    out["kernel_name"] = bfp8_kernel_name(p.kernel)
+    out["quant_kernel_name"] = bfp8_kernel_name(p.quant_kernel)
+    return out
+
+
+def bfp8_kernel_name(kernel):
+    return load().bfp8_kernel_name(kernel).decode()
 
 
 def bfp8_status_string(status):

@@ -89,20 +89,54 @@ size_t w8a8_workspace(int64_t M, int64_t N, int64_t K) {
     return K <= kTileMaxK ? tile_workspace_bytes(M, N, K) : 0;
 }
 
-// The W8A8 codes kernels by M (workspace already checked).
-hipError_t launch_w8a8(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws, void* y,
-                       int y_dtype, int64_t M, int64_t N, int64_t K, void* workspace, hipStream_t stream) {
-    if (one_token(M, K)) return launch_w8a8_gemv(xq, xs, wq, ws, y, y_dtype, N, K, stream);
-    if (w8a8_streams(M, N, K)) return launch_w8a8_stream(xq, xs, wq, ws, y, y_dtype, M, N, K, workspace, stream);
-    if (w8a8_wide(M, N, K)) return launch_w8a8_wide(xq, xs, wq, ws, y, y_dtype, M, N, K, stream);
-    return launch_w8a8_tile(xq, xs, wq, ws, y, y_dtype, M, N, K, workspace, stream);
-}
-
 // The fused quantise + W8A8 call quantises inside the kernel when the codes
 // call would run the one-token kernel or stream (so both give the same
 // bits), M permitting.
 bool quantises_in_registers(int64_t M, int64_t N, int64_t K) {
     return one_token(M, K) || (M <= kFusedQuantMaxM && w8a8_streams(M, N, K));
+}
+
+// The kernel each GEMM op runs for a shape: the one routing rule behind the
+// launches below and bfp8_get_plan.  For the fused quantise + W8A8 op
+// outside the in-kernel range this is the W8A8 kernel that follows the
+// staged quantiser.
+int route(int op, int64_t M, int64_t N, int64_t K) {
+    switch (op) {
+        case BFP8_OP_QUANT_GEMM_W8A8_BLK128:
+            if (one_token(M, K)) return BFP8_KERNEL_W8A8_GEMV_QUANT;
+            if (quantises_in_registers(M, N, K)) return BFP8_KERNEL_W8A8_STREAM_QUANT;
+            return route(BFP8_OP_GEMM_W8A8_BLK128, M, N, K);
+        case BFP8_OP_GEMM_W8A8_BLK128:
+            if (one_token(M, K)) return BFP8_KERNEL_W8A8_GEMV;
+            if (w8a8_streams(M, N, K)) return BFP8_KERNEL_W8A8_STREAM;
+            if (w8a8_wide(M, N, K)) return BFP8_KERNEL_W8A8_WIDE;
+            return BFP8_KERNEL_W8A8_TILE;
+        case BFP8_OP_GEMM_W8A16_BLK128:
+            if (one_token(M, K)) return BFP8_KERNEL_W8A16_GEMV;
+            if (w8a16_wide(M, N, K)) return BFP8_KERNEL_W8A16_WIDE;
+            if (M > kStreamMaxM) return BFP8_KERNEL_W8A16_TILE;
+            return BFP8_KERNEL_W8A16_STREAM;
+        case BFP8_OP_GEMM_W8A16_BLK32_UE8M0:
+            return M <= kStreamMaxM ? BFP8_KERNEL_BLK32_STREAM_LDS : BFP8_KERNEL_BLK32_STREAM;
+        case BFP8_OP_QUANT_ACT_1X128:
+            return BFP8_KERNEL_QUANT_ACT;
+        case BFP8_OP_QUANT_WEIGHT_128X128:
+            return BFP8_KERNEL_QUANT_WEIGHT;
+        default:
+            return BFP8_KERNEL_NONE;
+    }
+}
+
+// The W8A8 codes kernels by M (workspace already checked).
+hipError_t launch_w8a8(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws, void* y,
+                       int y_dtype, int64_t M, int64_t N, int64_t K, void* workspace, hipStream_t stream) {
+    switch (route(BFP8_OP_GEMM_W8A8_BLK128, M, N, K)) {
+        case BFP8_KERNEL_W8A8_GEMV: return launch_w8a8_gemv(xq, xs, wq, ws, y, y_dtype, N, K, stream);
+        case BFP8_KERNEL_W8A8_STREAM:
+            return launch_w8a8_stream(xq, xs, wq, ws, y, y_dtype, M, N, K, workspace, stream);
+        case BFP8_KERNEL_W8A8_WIDE: return launch_w8a8_wide(xq, xs, wq, ws, y, y_dtype, M, N, K, stream);
+        default: return launch_w8a8_tile(xq, xs, wq, ws, y, y_dtype, M, N, K, workspace, stream);
+    }
 }
 
 // Workspace of the fused quantise + W8A8 call when it does not, where
@@ -165,9 +199,10 @@ bfp8_status bfp8_quant_gemm_w8a8_blk128(const void* x, int x_dtype, const uint8_
     bfp8_status st = check_gemm(x, wq, ws, y, y_dtype, M, N, K, 16, need, workspace, workspace_bytes);
     if (st != BFP8_OK) return st;
     if (!is16(x_dtype)) return BFP8_E_DTYPE;
-    if (one_token(M, K))
+    const int kernel = route(BFP8_OP_QUANT_GEMM_W8A8_BLK128, M, N, K);
+    if (kernel == BFP8_KERNEL_W8A8_GEMV_QUANT)
         return launched(launch_w8a8_gemv_quant(x, x_dtype == BFP8_BF16, wq, ws, y, y_dtype, N, K, as_stream(stream)));
-    if (quantises_in_registers(M, N, K))
+    if (kernel == BFP8_KERNEL_W8A8_STREAM_QUANT)
         return launched(launch_w8a8_stream_quant(x, x_dtype == BFP8_BF16, wq, ws, y, y_dtype, M, N, K, workspace,
                                                  as_stream(stream)));
     if (K > kTileMaxK) return BFP8_E_SHAPE;
@@ -191,15 +226,18 @@ bfp8_status bfp8_gemm_w8a16_blk128(const void* x, int x_dtype, const uint8_t* wq
     bfp8_status st = check_gemm(x, wq, ws, y, y_dtype, M, N, K, 16, need, workspace, workspace_bytes);
     if (st != BFP8_OK) return st;
     if (!is16(x_dtype)) return BFP8_E_DTYPE;
-    if (one_token(M, K))       // one token: dot products on the vector ALUs
-        return launched(launch_w8a16_gemv(x, x_dtype == BFP8_BF16, wq, ws, y, y_dtype, N, K, as_stream(stream)));
-    if (w8a16_wide(M, N, K))   // every token per workgroup, weights widened in registers
-        return launched(launch_w8a16_wide(x, x_dtype == BFP8_BF16, wq, ws, y, y_dtype, M, N, K, as_stream(stream)));
-    if (M > kStreamMaxM)     // tiled MFMA kernel, weights widened in registers
-        return launched(launch_w8a16_tile(x, x_dtype == BFP8_BF16, wq, ws, y, y_dtype, M, N, K, workspace,
-                                          as_stream(stream)));
-    return launched(launch_w8a16_blk128_stream(x, x_dtype == BFP8_BF16, wq, ws, y, y_dtype, M, N, K,
-                                               workspace, as_stream(stream)));
+    const bool bf = x_dtype == BFP8_BF16;
+    switch (route(BFP8_OP_GEMM_W8A16_BLK128, M, N, K)) {
+        case BFP8_KERNEL_W8A16_GEMV:    // one token: dot products on the vector ALUs
+            return launched(launch_w8a16_gemv(x, bf, wq, ws, y, y_dtype, N, K, as_stream(stream)));
+        case BFP8_KERNEL_W8A16_WIDE:    // every token per workgroup, weights widened in registers
+            return launched(launch_w8a16_wide(x, bf, wq, ws, y, y_dtype, M, N, K, as_stream(stream)));
+        case BFP8_KERNEL_W8A16_TILE:    // tiled MFMA kernel, weights widened in registers
+            return launched(launch_w8a16_tile(x, bf, wq, ws, y, y_dtype, M, N, K, workspace, as_stream(stream)));
+        default:
+            return launched(launch_w8a16_blk128_stream(x, bf, wq, ws, y, y_dtype, M, N, K, workspace,
+                                                       as_stream(stream)));
+    }
 }
 
 bfp8_status bfp8_gemm_w8a16_blk32_ue8m0(const void* x, int x_dtype, const uint8_t* wq, const uint8_t* e8m0,
@@ -219,7 +257,9 @@ bfp8_status bfp8_prepare_blk32_ue8m0(const uint8_t* wq_host, const float* scale_
                                      uint8_t* e8m0_host, int64_t* bad_index) {
     if (bad_index) *bad_index = -1;
     if (!wq_host || !scale_host || !e8m0_host || !bad_index) return BFP8_E_NULL;
-    if (N < 32 || K < 32 || N % 32 != 0 || K % 32 != 0 || N >= kMaxDim || K >= kMaxDim) return BFP8_E_SHAPE;
+    // N in 32-row tiles; K in whole 128-K blocks, the unit the block-32 GEMM
+    // streams (so a layer this packer accepts is one the GEMM accepts).
+    if (N < 32 || K < 128 || N % 32 != 0 || K % 128 != 0 || N >= kMaxDim || K >= kMaxDim) return BFP8_E_SHAPE;
     const int64_t count = N * K;
     for (int64_t i = 0; i < count; ++i) {
         if ((wq_host[i] & 0x7F) == 0x7F) {
@@ -271,6 +311,110 @@ bfp8_status bfp8_get_limits(int op, int64_t* k_multiple, int64_t* n_multiple, in
     if (align_bytes) *align_bytes = kAlign;
     if (m_stream_max) *m_stream_max = ms;
     return BFP8_OK;
+}
+
+bfp8_status bfp8_get_plan(int op, int64_t M, int64_t N, int64_t K, bfp8_plan* plan) {
+    if (!plan) return BFP8_E_NULL;
+    if (op < BFP8_OP_QUANT_ACT_1X128 || op > BFP8_OP_QUANT_GEMM_W8A8_BLK128) return BFP8_E_OP;
+    bfp8_plan p;
+    memset(&p, 0, sizeof(p));
+    p.kernel = route(op, M, N, K);
+    p.splits = 1;
+    if (op == BFP8_OP_QUANT_ACT_1X128 || op == BFP8_OP_QUANT_WEIGHT_128X128) {
+        // The quantisers take their own shape rules (N stands for the weight rows).
+        const int64_t rows = op == BFP8_OP_QUANT_ACT_1X128 ? M : N;
+        if (!dim_ok(rows, 1) || !dim_ok(K, 8) || K % 8 != 0 || rows * K >= ((int64_t)1 << 40)) return BFP8_E_SHAPE;
+        p.tile_n = op == BFP8_OP_QUANT_ACT_1X128 ? 0 : 128;
+        p.waves = kQuantLaunchWaves;
+        p.workgroups = op == BFP8_OP_QUANT_ACT_1X128 ? quant_act_workgroups(rows, K)
+                                                     : ((rows + 127) / 128) * ((K + 127) / 128);
+        *plan = p;
+        return BFP8_OK;
+    }
+    const int64_t n_mult = op == BFP8_OP_GEMM_W8A16_BLK32_UE8M0 ? 32 : 16;
+    if (!dim_ok(M, 1) || !dim_ok(N, n_mult) || !dim_ok(K, 128) || N % n_mult != 0 || K % 128 != 0 ||
+        K > kTileMaxK || M * K >= ((int64_t)1 << 40) || N * K >= ((int64_t)1 << 40))
+        return BFP8_E_SHAPE;
+    if (op == BFP8_OP_GEMM_W8A16_BLK32_UE8M0 && (M + 15) / 16 > 65535) return BFP8_E_SHAPE;
+    p.workspace_bytes = bfp8_workspace_bytes(op, M, N, K);
+    if (op == BFP8_OP_QUANT_GEMM_W8A8_BLK128 && p.kernel != BFP8_KERNEL_W8A8_GEMV_QUANT &&
+        p.kernel != BFP8_KERNEL_W8A8_STREAM_QUANT)
+        p.quant_kernel = BFP8_KERNEL_QUANT_ACT;
+    switch (p.kernel) {
+        case BFP8_KERNEL_W8A8_GEMV:
+        case BFP8_KERNEL_W8A16_GEMV: {
+            const int kr = gemv_rows_per_wave(N);
+            p.tile_n = kGemvLaunchWaves * kr;
+            p.tile_m = 1;
+            p.waves = kGemvLaunchWaves;
+            p.workgroups = (N + p.tile_n - 1) / p.tile_n;
+            break;
+        }
+        case BFP8_KERNEL_W8A8_GEMV_QUANT:
+            p.tile_n = 4;
+            p.tile_m = 1;
+            p.waves = 4;
+            p.workgroups = N / 4;
+            break;
+        case BFP8_KERNEL_W8A8_STREAM:
+        case BFP8_KERNEL_W8A8_STREAM_QUANT:
+        case BFP8_KERNEL_W8A16_STREAM:
+        case BFP8_KERNEL_BLK32_STREAM_LDS:
+        case BFP8_KERNEL_BLK32_STREAM: {
+            const StreamPlan sp = plan_stream(M, N, K);
+            p.tile_n = (int)kStreamRows;
+            p.tile_m = 16;
+            p.waves = kStreamLaunchWaves;
+            p.splits = (int)sp.splits;
+            const bool z_tiles = p.kernel == BFP8_KERNEL_W8A8_STREAM || p.kernel == BFP8_KERNEL_BLK32_STREAM;
+            p.workgroups = sp.n_tiles * sp.splits * (z_tiles ? sp.m_tiles : 1);
+            break;
+        }
+        case BFP8_KERNEL_W8A8_WIDE:
+        case BFP8_KERNEL_W8A16_WIDE: {
+            const WideShape w = wide_shape(M, N);
+            p.tile_n = 16 * w.kr;
+            p.tile_m = 16 * w.kt;
+            p.waves = kWideLaunchWaves;
+            p.workgroups = (int64_t)w.groups_n * w.groups_m;
+            break;
+        }
+        case BFP8_KERNEL_W8A8_TILE:
+        case BFP8_KERNEL_W8A16_TILE: {
+            const TileInfo t = p.kernel == BFP8_KERNEL_W8A8_TILE ? tile_info(M, N, K) : tile16_info(M, N, K);
+            p.tile_n = t.tile_n;
+            p.tile_m = t.tile_m;
+            p.waves = t.waves;
+            p.splits = (int)t.splits;
+            p.workgroups = t.tiles * t.splits;
+            break;
+        }
+        default:
+            return BFP8_E_OP;
+    }
+    *plan = p;
+    return BFP8_OK;
+}
+
+const char* bfp8_kernel_name(int kernel) {
+    switch (kernel) {
+        case BFP8_KERNEL_NONE: return "none";
+        case BFP8_KERNEL_QUANT_ACT: return "quant_act_1x128";
+        case BFP8_KERNEL_QUANT_WEIGHT: return "quant_weight_128x128";
+        case BFP8_KERNEL_W8A8_GEMV: return "w8a8_gemv";
+        case BFP8_KERNEL_W8A8_GEMV_QUANT: return "w8a8_gemv_quant";
+        case BFP8_KERNEL_W8A8_STREAM: return "w8a8_stream";
+        case BFP8_KERNEL_W8A8_STREAM_QUANT: return "w8a8_stream_quant";
+        case BFP8_KERNEL_W8A8_WIDE: return "w8a8_wide";
+        case BFP8_KERNEL_W8A8_TILE: return "w8a8_tile";
+        case BFP8_KERNEL_W8A16_GEMV: return "w8a16_gemv";
+        case BFP8_KERNEL_W8A16_STREAM: return "w8a16_stream";
+        case BFP8_KERNEL_W8A16_WIDE: return "w8a16_wide";
+        case BFP8_KERNEL_W8A16_TILE: return "w8a16_tile";
+        case BFP8_KERNEL_BLK32_STREAM_LDS: return "blk32_stream_lds";
+        case BFP8_KERNEL_BLK32_STREAM: return "blk32_stream";
+        default: return "unknown kernel";
+    }
 }
 
 const char* bfp8_status_string(bfp8_status s) {

@@ -21,6 +21,14 @@ constexpr int64_t kStreamRows = 16;
 size_t tile_workspace_bytes(int64_t M, int64_t N, int64_t K);
 // Workspace bytes of the tiled W8A16 kernels.
 size_t tile16_workspace_bytes(int64_t M, int64_t N, int64_t K);
+// The tiled kernels' choice for a shape (the same planner the launches use):
+// workgroup tile (weight rows x tokens), waves, tiles and K splits.
+struct TileInfo {
+    int tile_n, tile_m, waves;
+    int64_t tiles, splits;
+};
+TileInfo tile_info(int64_t M, int64_t N, int64_t K);     // W8A8 codes
+TileInfo tile16_info(int64_t M, int64_t N, int64_t K);   // W8A16 (16-bit tokens)
 
 // Split-K plan of a streaming kernel: a workgroup covers 16 weight rows and
 // one 16-token tile; `splits` workgroups share one output tile, each
@@ -149,6 +157,17 @@ inline bool w8a16_wide(int64_t M, int64_t N, int64_t K) {
 // 5.35 vs 5.82, W8A16 5.33-5.42 vs 5.69; 1024 x 4096 W8A8 3.08 vs 3.87;
 // 12288 x 4096 W8A8 9.97 vs 11.0.
 inline bool one_token(int64_t M, int64_t K) { return M == 1 && K <= 4096; }
+// Weight rows per wave of the one-token kernels: two only for the largest
+// projections (measured, us, one row vs two: W8A8 4096 x 4096 5.28 vs 5.53,
+// 12288 x 4096 11.2 vs 10.9; W8A16 2048 x 4096 3.81 vs 3.87, 4096 x 4096
+// 5.34 vs 5.35, 12288 x 4096 11.3 vs 11.1).
+inline int gemv_rows_per_wave(int64_t N) { return N >= 8192 ? 2 : 1; }
+constexpr int kGemvLaunchWaves = 4;    // waves per workgroup of the one-token kernels
+constexpr int kStreamLaunchWaves = 16;  // waves per workgroup of the streaming kernels
+constexpr int kWideLaunchWaves = 8;     // waves per workgroup of the all-token kernels
+constexpr int kQuantLaunchWaves = 4;    // waves per workgroup of the quantisers
+// Workgroups of the 1x128 activation quantiser's grid.
+int64_t quant_act_workgroups(int64_t M, int64_t K);
 hipError_t launch_w8a8_gemv(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws, void* y,
                             int y_dtype, int64_t N, int64_t K, hipStream_t stream);
 hipError_t launch_w8a8_gemv_quant(const void* x, bool x_bf16, const uint8_t* wq, const float* ws, void* y,

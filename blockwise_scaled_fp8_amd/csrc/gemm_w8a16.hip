@@ -350,6 +350,7 @@ __global__ __launch_bounds__(kStreamThreads) void w8a16_blk32_stream_lds_kernel(
 // streaming kernel.  The waves' partial sums meet in LDS once, at the end,
 // and are added in K-lane order.
 constexpr int kW16WideWaves = 8;
+static_assert(kW16WideWaves == kWideLaunchWaves, "plan and launch agree");
 constexpr int kW16WideThreads = kW16WideWaves * kWave;
 template <int kR>
 struct W16Slot {
@@ -613,10 +614,7 @@ __global__ __launch_bounds__(kGemvWaves * kWave) void w8a16_gemv_kernel(
 hipError_t launch_w8a16_gemv(const void* x, bool x_bf16, const uint8_t* wq, const float* ws, void* y, int y_dtype,
                              int64_t N, int64_t K, hipStream_t stream) {
     if (N % 16 != 0 || K > kGemvMaxK) return hipErrorInvalidValue;
-    // Two rows per wave only for the largest projections (measured, us:
-    // 2048 x 4096 3.81 one row vs 3.87 two, 4096 x 4096 5.34 vs 5.35,
-    // 12288 x 4096 11.3 vs 11.1).
-    const int kr = N >= 8192 ? 2 : 1;
+    const int kr = gemv_rows_per_wave(N);
     const dim3 grid((unsigned)((N + kGemvWaves * kr - 1) / (kGemvWaves * kr)));
     const uint16_t* xh = static_cast<const uint16_t*>(x);
 #define BFP8_LAUNCH_GEMV(B, R) \

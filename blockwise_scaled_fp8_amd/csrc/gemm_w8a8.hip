@@ -384,6 +384,7 @@ __global__ __launch_bounds__(kStreamThreads) void w8a8_stream_quant_kernel(
 // barrier until the end, where the KW partial tiles of every output tile are
 // summed in LDS in K order.
 constexpr int kWideWaves = 8;
+static_assert(kWideWaves == kWideLaunchWaves, "plan and launch agree");
 constexpr int kWideThreads = kWideWaves * kWave;
 template <int kR>
 struct WideSlot {
@@ -727,9 +728,8 @@ __global__ __launch_bounds__(kW * kWave) void w8a8_gemv_quant_kernel(
 hipError_t launch_w8a8_gemv(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws, void* y,
                             int y_dtype, int64_t N, int64_t K, hipStream_t stream) {
     if (N % 16 != 0 || K > kGemvMaxK) return hipErrorInvalidValue;
-    // Two rows per wave only for the largest projections (measured, us:
-    // 4096 x 4096 5.28 one row vs 5.53 two; 12288 x 4096 11.2 vs 10.9).
-    const int kr = N >= 8192 ? 2 : 1;
+    static_assert(kGemvWaves == kGemvLaunchWaves, "plan and launch agree");
+    const int kr = gemv_rows_per_wave(N);
     const dim3 grid((unsigned)((N + kGemvWaves * kr - 1) / (kGemvWaves * kr)));
     if (kr == 2)
         hipLaunchKernelGGL((w8a8_gemv_kernel<2>), grid, dim3(kGemvWaves * kWave), 0, stream, xq, xs, wq, ws, y,

@@ -703,6 +703,27 @@ static size_t plan_workspace_bytes(const TilePlan& p) {
 
 size_t tile_workspace_bytes(int64_t M, int64_t N, int64_t K) { return plan_workspace_bytes(plan_tile(M, N, K)); }
 
+static int waves_of(TileShape s) {
+    switch (s) {
+        case TileShape::k256: return Cfg256::kWaves;
+        case TileShape::k256x128: return Cfg256x128::kWaves;
+        case TileShape::k128: return Cfg128::kWaves;
+        case TileShape::k64x128: return Cfg64x128::kWaves;
+        case TileShape::k128x64: return Cfg128x64::kWaves;
+        case TileShape::k128w4: return Cfg128w4::kWaves;
+        case TileShape::k16_256: return Cfg16_256<kTileBf16>::kWaves;
+        case TileShape::k16_128: return Cfg16_128<kTileBf16>::kWaves;
+        default: return Cfg16_64<kTileBf16>::kWaves;
+    }
+}
+
+static TileInfo info_of(const TilePlan& p) {
+    return TileInfo{(int)p.bn, (int)p.bm, waves_of(p.shape), p.tiles_n * p.tiles_m, p.splits};
+}
+
+TileInfo tile_info(int64_t M, int64_t N, int64_t K) { return info_of(plan_tile(M, N, K)); }
+TileInfo tile16_info(int64_t M, int64_t N, int64_t K) { return info_of(plan_tile16(M, N, K)); }
+
 size_t tile16_workspace_bytes(int64_t M, int64_t N, int64_t K) { return plan_workspace_bytes(plan_tile16(M, N, K)); }
 
 static void split_parts(const TilePlan& p, void* workspace, uint32_t*& counters, float*& partials) {

@@ -153,6 +153,14 @@ hipError_t launch_dequant_weight(const uint8_t* wq, const float* scales, int blo
     return hipGetLastError();
 }
 
+static_assert(kQuantActThreads == kQuantLaunchWaves * kWave && kQuantWThreads == kQuantLaunchWaves * kWave,
+              "plan and launch agree");
+
+int64_t quant_act_workgroups(int64_t M, int64_t K) {
+    const int64_t G = (K + 127) / 128;
+    return ((M + kQuantActRows - 1) / kQuantActRows) * ((G + kQuantActThreads / 16 - 1) / (kQuantActThreads / 16));
+}
+
 hipError_t launch_quant_act_1x128(const void* x, bool bf16, int64_t M, int64_t K,
                                   uint8_t* xq, float* xs, hipStream_t stream) {
     const int64_t G = (K + 127) / 128;

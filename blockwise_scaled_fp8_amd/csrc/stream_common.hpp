@@ -29,6 +29,7 @@
 namespace bfp8 {
 
 constexpr int kStreamWaves = 16;
+static_assert(kStreamWaves == kStreamLaunchWaves, "plan and launch agree");
 constexpr int kStreamThreads = kStreamWaves * kWave;
 // Words of the cross-wave reduction scratch (stream_finish): one 16x16 fp32
 // tile per wave and the split-K arrival word.

@@ -224,7 +224,10 @@ bfp8_status bfp8_gemm_w8a16_blk32_ue8m0(const void* x, int x_dtype,
  *               then scales).
  * Returns BFP8_E_NAN_CODE, BFP8_E_SCALE_NOT_POW2 (zero, negative, infinite,
  * NaN or non-power-of-two scale) or BFP8_E_SCALE_WINDOW (2^e, e outside
- * [-14, 7]) on refusal.  Requires N, K >= 32 and multiples of 32.
+ * [-14, 7]) on refusal.  Requires N >= 32 with N % 32 == 0, and K >= 128
+ * with K % 128 == 0: the 32x32 tiles of the format, in whole 128-K blocks,
+ * the unit bfp8_gemm_w8a16_blk32_ue8m0 streams, so that every layer this
+ * packer accepts is one that GEMM accepts (BFP8_E_SHAPE otherwise).
  */
 bfp8_status bfp8_prepare_blk32_ue8m0(const uint8_t* wq_host, const float* scale_host,
                                      int64_t N, int64_t K, uint8_t* e8m0_host,
@@ -260,6 +263,59 @@ size_t bfp8_workspace_bytes(int op, int64_t M, int64_t N, int64_t K);
  */
 bfp8_status bfp8_get_limits(int op, int64_t* k_multiple, int64_t* n_multiple,
                             int64_t* align_bytes, int64_t* m_stream_max);
+
+/*
+ * Kernels a call can run, as reported by bfp8_get_plan.  One tile does not
+ * fit every M ([ADA] "One tile doesn't fit all M"; [SM70] "How it works":
+ * GEMV-style kernels for a few tokens, matrix-core tiles above), so each
+ * GEMM picks one of these by M, N and K.
+ */
+enum {
+    BFP8_KERNEL_NONE = 0,
+    BFP8_KERNEL_QUANT_ACT = 1,          /* 1x128 activation quantiser */
+    BFP8_KERNEL_QUANT_WEIGHT = 2,       /* 128x128 weight quantiser */
+    BFP8_KERNEL_W8A8_GEMV = 3,          /* one token, codes in: dot products on the vector ALUs */
+    BFP8_KERNEL_W8A8_GEMV_QUANT = 4,    /* one token, 16-bit in, quantised inside the kernel */
+    BFP8_KERNEL_W8A8_STREAM = 5,        /* weight-streaming MFMA kernel, 16-token tiles, codes in */
+    BFP8_KERNEL_W8A8_STREAM_QUANT = 6,  /* weight-streaming MFMA kernel, quantised inside the kernel */
+    BFP8_KERNEL_W8A8_WIDE = 7,          /* all tokens of a group per 16/32-row weight tile */
+    BFP8_KERNEL_W8A8_TILE = 8,          /* tiled MFMA kernel */
+    BFP8_KERNEL_W8A16_GEMV = 9,         /* one token: dot products on the vector ALUs */
+    BFP8_KERNEL_W8A16_STREAM = 10,      /* weight-streaming MFMA kernel */
+    BFP8_KERNEL_W8A16_WIDE = 11,        /* all tokens of a group per weight tile */
+    BFP8_KERNEL_W8A16_TILE = 12,        /* tiled MFMA kernel, weights widened in registers */
+    BFP8_KERNEL_BLK32_STREAM_LDS = 13,  /* block-32, M <= 16: weights through LDS slabs */
+    BFP8_KERNEL_BLK32_STREAM = 14,      /* block-32, M > 16: one 16-token tile per workgroup */
+    BFP8_KERNEL_COUNT = 15
+};
+
+/* A call's launch plan (filled by bfp8_get_plan). */
+typedef struct bfp8_plan {
+    int32_t kernel;         /* BFP8_KERNEL_* of the op's main kernel */
+    int32_t quant_kernel;   /* BFP8_KERNEL_QUANT_ACT when the fused quantise + W8A8 call runs
+                               the quantiser as its own launch first, else BFP8_KERNEL_NONE */
+    int32_t tile_n;         /* weight rows (output columns) per workgroup tile */
+    int32_t tile_m;         /* tokens per workgroup tile, padded (0 for the quantisers) */
+    int32_t waves;          /* 64-lane waves per workgroup */
+    int32_t splits;         /* workgroups that share one output tile over K (1: K not split) */
+    int64_t workgroups;     /* workgroups in the main kernel's grid */
+    uint64_t workspace_bytes; /* = bfp8_workspace_bytes(op, M, N, K) */
+} bfp8_plan;
+
+/*
+ * The launch plan of `op` for an M x N x K problem, from the same routing
+ * code the calls use, so a test can state which kernel it exercises and a
+ * caller can see the kernel and workspace a shape will get ([ARC]
+ * "Correctness guards": what a shape is served by is read from the library,
+ * not re-derived by the caller).  Host only, touches no GPU, allocates
+ * nothing.  Returns BFP8_E_NULL (plan NULL), BFP8_E_OP (unknown op) or
+ * BFP8_E_SHAPE when the call itself would refuse the sizes; `plan` is
+ * written only on success.
+ */
+bfp8_status bfp8_get_plan(int op, int64_t M, int64_t N, int64_t K, bfp8_plan* plan);
+
+/* Static name of a BFP8_KERNEL_* id ("unknown kernel" for others). */
+const char* bfp8_kernel_name(int kernel);
 
 /* Static, human-readable text for a status code. */
 const char* bfp8_status_string(bfp8_status status);

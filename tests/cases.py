@@ -1,0 +1,161 @@
+"""Shape tables of the GPU parity tests, each case with the kernel variant it
+is meant to exercise.
+
+The GPU tests take their parameters from here and assert, through
+bfp8_get_plan, that the library routes each case to the stated kernel.  The
+CPU suite (tests/test_plan.py) checks the same routing without a GPU and that
+the cases together reach every kernel variant the router can produce, so a
+dispatch threshold that moves a case off its kernel, or leaves a kernel with
+no parity case, fails the suite.
+
+A variant is the kernel's name; the all-token and tiled kernels add their
+workgroup tile and waves (":tile_n x tile_m w waves"), a plan that splits K
+adds "/split", and the fused quantise + W8A8 call that stages the codes
+through the quantiser first is prefixed "quant+".
+"""
+
+import blockwise_scaled_fp8_amd as bfp8
+
+W8A8 = bfp8.OP_GEMM_W8A8_BLK128
+QW8A8 = bfp8.OP_QUANT_GEMM_W8A8_BLK128
+W8A16 = bfp8.OP_GEMM_W8A16_BLK128
+BLK32 = bfp8.OP_GEMM_W8A16_BLK32_UE8M0
+
+
+def variant(op, M, N, K):
+    p = bfp8.bfp8_get_plan(op, M, N, K)
+    v = p["kernel_name"]
+    if "tile" in v or "wide" in v:
+        v += f":{p['tile_n']}x{p['tile_m']}w{p['waves']}"
+    if p["splits"] > 1:
+        v += "/split"
+    if p["quant_kernel"]:
+        v = "quant+" + v
+    return v
+
+
+def expect(op, M, N, K, want):
+    got = variant(op, M, N, K)
+    assert got == want, f"op {op} M={M} N={N} K={K} runs {got}, the case is meant for {want}"
+
+
+# ------------------------------------------------------------------ W8A8 ----
+# Threshold straddle on a small projection (N = 384, K = 640).
+W8A8_THRESHOLD = [(1, 384, 640, "w8a8_gemv")] + \
+    [(M, 384, 640, "w8a8_stream") for M in (2, 3, 5, 8, 15, 16, 17, 24, 31, 32, 33, 48, 63, 64)] + \
+    [(M, 384, 640, "w8a8_wide:16x32w8") for M in (65, 129, 200)]
+
+W8A8_ONE_TOKEN = [(1, N, K, "w8a8_gemv") for N, K in
+                  ((16, 128), (16, 1152), (64, 4096), (1024, 4096), (2064, 1024), (4096, 3968), (12288, 2048))]
+
+# N not a multiple of 128: tiles straddle weight-scale rows.
+W8A8_STRADDLE = [(M, N, 256, "w8a8_stream") for N in (16, 48, 144, 272) for M in (4, 40)]
+
+W8A8_SPLIT_K_STREAM = [(M, 512, 12288, "w8a8_stream/split") for M in (1, 4, 16)]
+
+# Paths that need no workspace for M <= 512 (all-token kernel, or the
+# streaming kernel over 16-token tiles on small projections).
+W8A8_NO_WORKSPACE = [
+    (1, 1024, 12288, "w8a8_wide:16x32w8"), (5, 2048, 12288, "w8a8_wide:16x32w8"),
+    (16, 1024, 12288, "w8a8_wide:16x32w8"), (17, 1024, 4096, "w8a8_stream"), (24, 1024, 4096, "w8a8_stream"),
+    (32, 4096, 4096, "w8a8_wide:16x32w8"), (33, 4096, 4096, "w8a8_wide:32x32w8"), (50, 1024, 4096, "w8a8_stream"),
+    (64, 4096, 4096, "w8a8_wide:32x32w8"), (32, 12288, 256, "w8a8_wide:32x32w8"), (20, 16, 8192, "w8a8_stream"),
+    (20, 8208, 256, "w8a8_wide:32x32w8"), (65, 8192, 512, "w8a8_tile:64x128w8"),
+    (100, 4096, 1024, "w8a8_wide:32x64w8"), (128, 1040, 2048, "w8a8_wide:16x32w8"), (20, 64, 128, "w8a8_stream"),
+    (128, 8192, 128, "w8a8_tile:64x128w8"), (64, 1024, 4096, "w8a8_stream"), (40, 2048, 1024, "w8a8_wide:16x32w8"),
+    (61, 512, 8192, "w8a8_stream"), (300, 1024, 2048, "w8a8_wide:32x32w8"), (512, 1024, 512, "w8a8_wide:32x64w8"),
+    (256, 1040, 1024, "w8a8_wide:16x64w8"),
+]
+
+# Every tiled configuration, ragged M and N tiles, split K.
+W8A8_TILE = [
+    (40, 8192, 8192, "w8a8_tile:128x64w8/split"),
+    (65, 1024, 8192, "w8a8_tile:64x128w8/split"),
+    (100, 1024, 8192, "w8a8_tile:64x128w8/split"),
+    (200, 4096, 2176, "w8a8_tile:64x128w8/split"),        # last split shorter
+    (300, 2064, 1024, "w8a8_tile:64x128w8/split"),        # ragged N
+    (1000, 4096, 1024, "w8a8_tile:128x128w8"),
+    (400, 2048, 8192, "w8a8_tile:128x128w4/split"),       # ragged M
+    (512, 4096, 8192, "w8a8_tile:128x128w4/split"),
+    (2000, 4000, 1024, "w8a8_tile:256x128w8"),            # ragged M and N
+    (48, 16384, 256, "w8a8_tile:128x64w8"),               # enough tiles: K not split
+]
+W8A8_LARGE_RAGGED = (4000, 4000, 384, "w8a8_tile:256x256w8")
+W8A8_DECODE_OPROJ = (1, 4096, 4096, "w8a8_gemv")
+W8A8_PREFILL_OPROJ = (4096, 4096, 4096, "w8a8_tile:256x256w8")
+W8A8_ONE_HOT = [(1, 256, 256, "w8a8_gemv"), (3, 256, 256, "w8a8_stream"), (48, 256, 256, "w8a8_stream")]
+W8A8_DETERMINISTIC = (64, 512, 1024, "w8a8_stream")
+
+# Fused quantise + W8A8 (bit-identical to quantise-then-GEMM).
+QUANT_W8A8 = [
+    (1, 4096, 4096, "w8a8_gemv_quant"), (1, 16, 128, "w8a8_gemv_quant"), (1, 1024, 1152, "w8a8_gemv_quant"),
+    (1, 2064, 3968, "w8a8_gemv_quant"), (1, 512, 4224, "w8a8_stream_quant"), (2, 1024, 4096, "w8a8_stream_quant"),
+    (3, 512, 640, "w8a8_stream_quant"), (4, 384, 12288, "w8a8_stream_quant/split"),
+    (5, 1024, 4096, "w8a8_stream_quant"), (8, 512, 1024, "w8a8_stream_quant"), (9, 512, 640, "quant+w8a8_stream"),
+    (16, 1024, 4096, "quant+w8a8_stream"), (17, 384, 640, "quant+w8a8_stream"), (64, 1024, 4096, "quant+w8a8_stream"),
+    (300, 1040, 1024, "quant+w8a8_wide:16x64w8"), (200, 4096, 2176, "quant+w8a8_tile:64x128w8/split"),
+]
+
+# ---------------------------------------------------------------- W8A16 ----
+W8A16_BY_M = [(1, 512, 1024, "w8a16_gemv")] + \
+    [(M, 512, 1024, "w8a16_stream") for M in (2, 3, 4, 5, 8, 12, 16)] + \
+    [(M, 512, 1024, "w8a16_wide:16x32w8") for M in (17, 33, 64, 65, 130)]
+W8A16_ONE_TOKEN = [(1, N, K, "w8a16_gemv") for N, K in
+                   ((16, 128), (16, 1152), (64, 4096), (1024, 4096), (2064, 1024), (4096, 4096), (4096, 3968),
+                    (12288, 2048))]
+W8A16_ALL_TOKENS = [
+    (17, 1024, 4096, "w8a16_wide:16x32w8"), (32, 4096, 4096, "w8a16_wide:16x32w8"),
+    (50, 1024, 4096, "w8a16_wide:16x32w8"), (64, 4096, 4096, "w8a16_wide:32x32w8"),
+    (24, 12288, 512, "w8a16_wide:32x32w8"), (20, 16, 4096, "w8a16_wide:32x32w8"), (20, 64, 128, "w8a16_wide:16x32w8"),
+    (128, 4096, 4096, "w8a16_wide:32x64w8"), (100, 4112, 1024, "w8a16_wide:32x64w8"),
+    (256, 1024, 4096, "w8a16_wide:32x32w8"), (200, 1040, 1024, "w8a16_wide:16x64w8"),
+]
+W8A16_LONG_K = [(M, 4096, 12288, "w8a16_stream") for M in (1, 3, 16)]
+W8A16_SPLIT_K_STREAM = [(4, 512, 12288, "w8a16_stream/split")]
+W8A16_ONE_HOT = [(1, 256, 256, "w8a16_gemv"), (4, 256, 256, "w8a16_stream"), (40, 256, 256, "w8a16_wide:16x32w8")]
+W8A16_TILE_SPLIT = [(40, 1024, 8192, "w8a16_tile:128x64w8/split"), (100, 1040, 8192, "w8a16_tile:128x128w8/split"),
+                    (300, 2048, 2176, "w8a16_tile:128x128w8/split"), (40, 16384, 512, "w8a16_tile:128x64w8")]
+W8A16_TILE_ONE_HOT = (300, 256, 256, "w8a16_tile:128x128w8")
+W8A16_TILE_LARGE_RAGGED = (2000, 4112, 1024, "w8a16_tile:256x128w8")
+W8A16_TILE_LARGE_ONE_HOT = (2048, 4096, 256, "w8a16_tile:256x128w8")
+W8A16_PREFILL_OPROJ = (4096, 4096, 4096, "w8a16_tile:256x128w8")
+W8A16_DECODE_OPROJ = (1, 4096, 4096, "w8a16_gemv")
+
+# ---------------------------------------------------------------- blk32 ----
+BLK32_WORKLOAD = [(M, 4096, 7168, "blk32_stream_lds") for M in (1, 2, 3, 4, 8, 12, 16)]
+# Above the streaming range ([SM70] "Results" times M = 32 ... 4096).
+BLK32_ABOVE_16 = [(M, 4096, 7168, "blk32_stream") for M in (17, 32, 64, 128, 512)]
+BLK32_WINDOW = (8, 512, 1024, "blk32_stream_lds")
+BLK32_ONE_HOT = (16, 704, 256, "blk32_stream_lds")
+BLK32_ONE_HOT_ABOVE_16 = (17, 704, 256, "blk32_stream")
+BLK32_SPLIT_K = (4, 1024, 12288, "blk32_stream_lds/split")
+BLK32_SPLIT_K_ABOVE_16 = (20, 512, 12288, "blk32_stream/split")
+
+
+def coverage_key(op, v):
+    """The fused call that stages the codes through the quantiser runs the
+    same W8A8 kernel as the codes call: its variants count as that call's
+    (a separate check asks for at least one staged case)."""
+    if op == QW8A8 and v.startswith("quant+"):
+        return (W8A8, v[len("quant+"):])
+    return (op, v)
+
+
+def all_cases():
+    """(op, M, N, K, variant) for every case above."""
+    out = []
+    tables = {
+        W8A8: [W8A8_THRESHOLD, W8A8_ONE_TOKEN, W8A8_STRADDLE, W8A8_SPLIT_K_STREAM, W8A8_NO_WORKSPACE, W8A8_TILE,
+               [W8A8_LARGE_RAGGED, W8A8_DECODE_OPROJ, W8A8_PREFILL_OPROJ, W8A8_DETERMINISTIC], W8A8_ONE_HOT],
+        QW8A8: [QUANT_W8A8],
+        W8A16: [W8A16_BY_M, W8A16_ONE_TOKEN, W8A16_ALL_TOKENS, W8A16_LONG_K, W8A16_SPLIT_K_STREAM, W8A16_ONE_HOT,
+                W8A16_TILE_SPLIT, [W8A16_TILE_ONE_HOT, W8A16_TILE_LARGE_RAGGED, W8A16_TILE_LARGE_ONE_HOT,
+                                   W8A16_PREFILL_OPROJ, W8A16_DECODE_OPROJ]],
+        BLK32: [BLK32_WORKLOAD, BLK32_ABOVE_16, [BLK32_WINDOW, BLK32_ONE_HOT, BLK32_ONE_HOT_ABOVE_16, BLK32_SPLIT_K,
+                                                 BLK32_SPLIT_K_ABOVE_16]],
+    }
+    for op, tabs in tables.items():
+        for tab in tabs:
+            for (M, N, K, v) in tab:
+                out.append((op, M, N, K, v))
+    return out

@@ -41,7 +41,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared()
-    assert len(names) == 11
+    assert len(names) == 13
     assert sorted(_lib.SIGNATURES) == names
     nm = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], stdout=subprocess.PIPE, text=True).stdout
     exported = set(re.findall(r" T (bfp8_\w+)", nm))
@@ -234,18 +234,18 @@ def test_prepare_accepts_full_window():
 @pytest.mark.parametrize("value", [3.0, 0.0, -1.0, -0.5, np.inf, -np.inf, np.nan, 1.5 * 2.0 ** -20,
                                    2.0 ** -15, 2.0 ** 8, 2.0 ** -130, 2.0 ** 100, 2.0 ** -14, 2.0 ** 7])
 def test_prepare_scale_refusals_match_oracle(value):
-    wq = np.zeros((64, 96), np.uint8)
-    s = np.ones((2, 3), np.float32)
+    wq = np.zeros((64, 128), np.uint8)
+    s = np.ones((2, 4), np.float32)
     s[1, 2] = value
     _both(wq, s)
 
 
-@pytest.mark.parametrize("pos", [(0, 0), (5, 17), (63, 95)])
+@pytest.mark.parametrize("pos", [(0, 0), (5, 17), (63, 127)])
 @pytest.mark.parametrize("code", [0x7F, 0xFF])
 def test_prepare_nan_code_refusals_match_oracle(pos, code):
-    wq = np.zeros((64, 96), np.uint8)
+    wq = np.zeros((64, 128), np.uint8)
     wq[pos] = code
-    s = np.full((2, 3), 3.0, np.float32)      # bad scales too: the codes are reported first
+    s = np.full((2, 4), 3.0, np.float32)      # bad scales too: the codes are reported first
     assert _both(wq, s) == 6
 
 
@@ -253,8 +253,15 @@ def test_prepare_validation(lib):
     bad = ctypes.c_int64(5)
     assert lib.bfp8_prepare_blk32_ue8m0(None, None, 32, 32, None, ctypes.byref(bad)) == 1
     assert bad.value == -1
-    buf = (ctypes.c_uint8 * 4096)()
-    assert lib.bfp8_prepare_blk32_ue8m0(buf, buf, 48, 32, buf, ctypes.byref(bad)) == 2
+    buf = (ctypes.c_uint8 * 16384)()
+    assert lib.bfp8_prepare_blk32_ue8m0(buf, buf, 48, 128, buf, ctypes.byref(bad)) == 2
+    # K must be whole 128-K blocks, the unit the block-32 GEMM streams, so that
+    # a layer the packer accepts is one the GEMM accepts
+    assert lib.bfp8_prepare_blk32_ue8m0(buf, buf, 64, 96, buf, ctypes.byref(bad)) == 2
+    assert lib.bfp8_gemm_w8a16_blk32_ue8m0(A, 1, B, C, Y, 1, 4, 64, 96, None, 0, None) == 2
+    k_mult = ctypes.c_int64(0)
+    assert lib.bfp8_get_limits(bfp8.OP_GEMM_W8A16_BLK32_UE8M0, ctypes.byref(k_mult), None, None, None) == 0
+    assert k_mult.value == 128
 
 
 # --------------------------------------------------------------- build ----

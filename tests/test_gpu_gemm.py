@@ -15,6 +15,8 @@ from blockwise_scaled_fp8_amd import inputs
 import oracle
 from tests.gpu_helpers import (FINITE_CODES, say, dev, f32, workspace, run_w8a8, run_w8a16, run_blk32,
                                assert_fp32_bar, assert_16bit_bar)
+from tests import cases
+from tests.cases import expect, W8A8, QW8A8, W8A16, BLK32
 
 pytestmark = pytest.mark.gpu
 
@@ -27,8 +29,10 @@ def _w8a8_inputs(M, N, K, wid, outliers=False):
     return xq, xs, wq, ws
 
 
-def _w8a8_check(M, N, K, wid, outliers=False, what=""):
-    say("w8a8", what, f"M={M} N={N} K={K}")
+def _w8a8_check(M, N, K, wid, outliers=False, what="", kernel=None):
+    say("w8a8", what, f"M={M} N={N} K={K}", kernel)
+    if kernel is not None:
+        expect(W8A8, M, N, K, kernel)
     xq, xs, wq, ws = _w8a8_inputs(M, N, K, wid, outliers)
     y0 = oracle.gemm_w8a8_blk128(xq, xs, wq, ws)
     d = [dev(a) for a in (xq, xs, wq, ws)]
@@ -42,34 +46,33 @@ def _w8a8_check(M, N, K, wid, outliers=False, what=""):
 
 
 def test_w8a8_workload0(gpu_lib):
-    _w8a8_check(4, 512, 512, 0, what="workload 0")
+    _w8a8_check(4, 512, 512, 0, what="workload 0", kernel="w8a8_stream")
 
 
-@pytest.mark.parametrize("M", [1, 2, 3, 5, 8, 15, 16, 17, 24, 31, 32, 33, 48, 63, 64, 65, 129, 200])
-def test_w8a8_across_the_stream_tile_threshold(gpu_lib, M):
-    _w8a8_check(M, 384, 640, 300 + M, what="threshold")
+@pytest.mark.parametrize("M,N,K,kernel", cases.W8A8_THRESHOLD)
+def test_w8a8_across_the_stream_tile_threshold(gpu_lib, M, N, K, kernel):
+    _w8a8_check(M, N, K, 300 + M, what="threshold", kernel=kernel)
 
 
-@pytest.mark.parametrize("N,K", [(16, 128), (16, 1152), (64, 4096), (1024, 4096), (2064, 1024), (4096, 3968),
-                                 (12288, 2048)])
-def test_w8a8_one_token(gpu_lib, N, K):
+@pytest.mark.parametrize("M,N,K,kernel", cases.W8A8_ONE_TOKEN)
+def test_w8a8_one_token(gpu_lib, M, N, K, kernel):
     """M = 1 with K <= 4096: the vector-ALU dot-product kernel (one or two
     weight rows per wave), with K of one block, K ending inside a 1 KB chunk
     and shorter than the four chunks the kernel reads; no workspace."""
     assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 1, N, K) == 0
-    _w8a8_check(1, N, K, 450 + N + K // 128, what="one token")
+    _w8a8_check(1, N, K, 450 + N + K // 128, what="one token", kernel=kernel)
 
 
-@pytest.mark.parametrize("N", [16, 48, 144, 272])
-@pytest.mark.parametrize("M", [4, 40])
-def test_w8a8_weight_scale_rows_straddle(gpu_lib, M, N):
+@pytest.mark.parametrize("M,N,K,kernel", cases.W8A8_STRADDLE)
+def test_w8a8_weight_scale_rows_straddle(gpu_lib, M, N, K, kernel):
     """N not a multiple of 128: tiles straddle or subdivide a 128-row weight-scale block."""
-    _w8a8_check(M, N, 256, 400 + N + M, what="straddle")
+    _w8a8_check(M, N, K, 400 + N + M, what="straddle", kernel=kernel)
 
 
-@pytest.mark.parametrize("M", [1, 4, 16])
-def test_w8a8_split_k_narrow_projection(gpu_lib, M):
+@pytest.mark.parametrize("M,N,K,kernel", cases.W8A8_SPLIT_K_STREAM)
+def test_w8a8_split_k_narrow_projection(gpu_lib, M, N, K, kernel):
     """N=512, K=12288 streams with K split over workgroups; run twice (counters re-arm)."""
+    expect(W8A8, M, N, K, kernel)
     assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, M, 512, 12288) > 0
     xq, xs, wq, ws = _w8a8_inputs(M, 512, 12288, 500 + M)
     y0 = oracle.gemm_w8a8_blk128(xq, xs, wq, ws)
@@ -82,13 +85,8 @@ def test_w8a8_split_k_narrow_projection(gpu_lib, M):
     assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 1024, 12288), (5, 2048, 12288), (16, 1024, 12288), (17, 1024, 4096),
-                                   (24, 1024, 4096), (32, 4096, 4096), (33, 4096, 4096), (50, 1024, 4096),
-                                   (64, 4096, 4096), (32, 12288, 256), (20, 16, 8192), (20, 8208, 256),
-                                   (65, 8192, 512), (100, 4096, 1024), (128, 1040, 2048), (20, 64, 128),
-                                   (128, 8192, 128), (64, 1024, 4096), (40, 2048, 1024), (61, 512, 8192),
-                                   (300, 1024, 2048), (512, 1024, 512), (256, 1040, 1024)])
-def test_w8a8_wide_all_tokens(gpu_lib, M, N, K):
+@pytest.mark.parametrize("M,N,K,kernel", cases.W8A8_NO_WORKSPACE)
+def test_w8a8_wide_all_tokens(gpu_lib, M, N, K, kernel):
     """The paths that need no workspace for M <= 128: the kernel that holds
     every token per 16- or 32-row weight tile (M <= 16 where streaming would
     split K, 16 < M <= 32, M <= 128 with K <= 4096) and the streaming kernel
@@ -97,25 +95,16 @@ def test_w8a8_wide_all_tokens(gpu_lib, M, N, K):
     group, a single 16-row weight tile, a 32-row tile with only 16 live rows
     (N = 8208), and K spread unevenly over the waves."""
     assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, M, N, K) == 0
-    _w8a8_check(M, N, K, 900 + M, what="wide")
+    _w8a8_check(M, N, K, 900 + M, what="wide", kernel=kernel)
 
 
-@pytest.mark.parametrize("M,N,K,shape", [
-    (40, 8192, 8192, "128x64, 4 splits"),
-    (65, 1024, 8192, "64x128, 16 splits"),
-    (100, 1024, 8192, "64x128, 16 splits"),
-    (200, 4096, 2176, "64x128, 2 splits, last split shorter"),
-    (300, 2064, 1024, "64x128, 2 splits, ragged N"),
-    (1000, 4096, 1024, "128x128"),
-    (400, 2048, 8192, "128x128 four waves, 4 splits, ragged M"),
-    (512, 4096, 8192, "128x128 four waves, 2 splits"),
-    (2000, 4000, 1024, "256x128, ragged M and N"),
-])
+@pytest.mark.parametrize("M,N,K,shape", cases.W8A8_TILE)
 def test_w8a8_tile_shapes_and_split_k(gpu_lib, M, N, K, shape):
     """Every tiled configuration, with ragged M and N tiles and split K; the
     split plans run twice on one workspace (counters re-arm) and must repeat
     bit for bit."""
     say("w8a8 tile", shape, f"M={M} N={N} K={K}")
+    expect(W8A8, M, N, K, shape)
     xq, xs, wq, ws = _w8a8_inputs(M, N, K, 700 + M)
     y0 = oracle.gemm_w8a8_blk128(xq, xs, wq, ws)
     d = [dev(a) for a in (xq, xs, wq, ws)]
@@ -132,8 +121,9 @@ def test_w8a8_tile_shapes_and_split_k(gpu_lib, M, N, K, shape):
 def test_w8a8_large_tile_ragged_sampled(gpu_lib):
     """256x256 tiles with ragged M and N (N straddles weight-scale rows):
     full GPU run, oracle on sampled rows including the last tile's."""
-    M, N, K = 4000, 4000, 384
+    M, N, K, kernel = cases.W8A8_LARGE_RAGGED
     say("w8a8 256x256 ragged", M, N, K)
+    expect(W8A8, M, N, K, kernel)
     xq, xs, wq, ws = _w8a8_inputs(M, N, K, 800)
     y32 = run_w8a8(*(dev(a) for a in (xq, xs, wq, ws)), torch.float32)
     rows = np.concatenate([np.random.default_rng(4).choice(3840, 24, replace=False), np.arange(3840, 4000, 5)])
@@ -142,17 +132,15 @@ def test_w8a8_large_tile_ragged_sampled(gpu_lib):
 
 
 @pytest.mark.parametrize("xdtype", [torch.bfloat16, torch.float16])
-@pytest.mark.parametrize("M,N,K", [(1, 4096, 4096), (1, 16, 128), (1, 1024, 1152), (1, 2064, 3968),
-                                   (1, 512, 4224), (2, 1024, 4096), (3, 512, 640), (4, 384, 12288),
-                                   (5, 1024, 4096), (8, 512, 1024), (9, 512, 640), (16, 1024, 4096),
-                                   (17, 384, 640), (64, 1024, 4096), (300, 1040, 1024)])
-def test_quant_gemm_equals_quantise_then_gemm(gpu_lib, M, N, K, xdtype):
+@pytest.mark.parametrize("M,N,K,kernel", cases.QUANT_W8A8)
+def test_quant_gemm_equals_quantise_then_gemm(gpu_lib, M, N, K, kernel, xdtype):
     """The fused call is bit-identical to bfp8_quantize_act_1x128 followed by
     bfp8_gemm_w8a8_blk128 (fp32 and 16-bit outputs), and meets the oracle bar.
     bf16 cases include a zero row (a zero group at M = 1) and rows (groups)
     whose scales lie outside [2^-90, 2^100] (the quantiser's IEEE-division
     path)."""
-    say("quant+w8a8", xdtype, f"M={M} N={N} K={K}")
+    say("quant+w8a8", xdtype, f"M={M} N={N} K={K}", kernel)
+    expect(QW8A8, M, N, K, kernel)
     x = inputs.activations(M, K, workload=900 + M, stream=K, outliers=True, dtype=xdtype).float()
     if xdtype == torch.bfloat16 and M >= 3:
         x[0] = 0.0
@@ -182,12 +170,14 @@ def test_quant_gemm_equals_quantise_then_gemm(gpu_lib, M, N, K, xdtype):
 
 def test_w8a8_decode_oproj_full(gpu_lib):
     """Decode o_proj M=1, N=K=4096: full oracle."""
-    _w8a8_check(1, 4096, 4096, 1, what="o_proj decode")
+    M, N, K, kernel = cases.W8A8_DECODE_OPROJ
+    _w8a8_check(M, N, K, 1, what="o_proj decode", kernel=kernel)
 
 
 def test_w8a8_prefill_oproj_sampled(gpu_lib):
     """Prefill o_proj M=N=K=4096 with 1% outlier channels: full GPU run, 64 rows checked."""
     say("w8a8 prefill full size")
+    expect(W8A8, *cases.W8A8_PREFILL_OPROJ)
     x = inputs.workload(2)["x"]
     w = inputs.workload(2)["w"]
     xq_d, xs_d = bfp8.quantize_act(x.cuda())
@@ -205,11 +195,11 @@ def test_w8a8_prefill_oproj_sampled(gpu_lib):
     assert_16bit_bar(y16[rows], y32[rows], y0, "bf16", "prefill sampled rows")
 
 
-@pytest.mark.parametrize("M", [1, 3, 48])
-def test_w8a8_one_hot_all_codes_exact(gpu_lib, M):
+@pytest.mark.parametrize("M,N,K,kernel", cases.W8A8_ONE_HOT)
+def test_w8a8_one_hot_all_codes_exact(gpu_lib, M, N, K, kernel):
     """xq one-hot 1.0 at column k, unit scales: Y[:, n] = E4M3(wq[n, k]) exactly,
-    for every finite code (one-token, stream and all-token kernels)."""
-    N, K = 256, 256
+    for every finite code (one-token and stream kernels)."""
+    expect(W8A8, M, N, K, kernel)
     wq = np.zeros((N, K), np.uint8)
     wq[:254, :] = FINITE_CODES[:, None]
     for k in (0, 77, 128, 255):
@@ -218,12 +208,14 @@ def test_w8a8_one_hot_all_codes_exact(gpu_lib, M):
         xq[:, k] = 0x38
         y = run_w8a8(dev(xq), dev(np.ones((M, 2), np.float32)), dev(wq), dev(np.ones((2, 2), np.float32)),
                      torch.float32)
-        expect = np.broadcast_to(oracle.e4m3_decode(wq[:, k]), (M, N))
-        np.testing.assert_array_equal(y.cpu().numpy(), expect)
+        want = np.broadcast_to(oracle.e4m3_decode(wq[:, k]), (M, N))
+        np.testing.assert_array_equal(y.cpu().numpy(), want)
 
 
 def test_w8a8_deterministic(gpu_lib):
-    xq, xs, wq, ws = _w8a8_inputs(64, 512, 1024, 11)
+    M, N, K, kernel = cases.W8A8_DETERMINISTIC
+    expect(W8A8, M, N, K, kernel)
+    xq, xs, wq, ws = _w8a8_inputs(M, N, K, 11)
     d = [dev(a) for a in (xq, xs, wq, ws)]
     a = run_w8a8(*d, torch.float32)
     b = run_w8a8(*d, torch.float32)
@@ -233,10 +225,10 @@ def test_w8a8_deterministic(gpu_lib):
 # ------------------------------------------------------------ W8A16 blk128 ----
 
 @pytest.mark.parametrize("xdtype", [torch.bfloat16, torch.float16])
-@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 12, 16, 17, 33, 64, 65, 130])
-def test_w8a16_blk128(gpu_lib, M, xdtype):
-    N, K = 512, 1024
-    say("w8a16 blk128", M, xdtype)
+@pytest.mark.parametrize("M,N,K,kernel", cases.W8A16_BY_M)
+def test_w8a16_blk128(gpu_lib, M, N, K, kernel, xdtype):
+    say("w8a16 blk128", M, xdtype, kernel)
+    expect(W8A16, M, N, K, kernel)
     x = inputs.activations(M, K, workload=600 + M, dtype=xdtype)
     wq, ws = oracle.quantize_weight_128x128(f32(inputs.weights_bf16(N, K, workload=600 + M)))
     y0 = oracle.gemm_w8a16_blk128(f32(x), wq, ws)
@@ -248,14 +240,14 @@ def test_w8a16_blk128(gpu_lib, M, xdtype):
 
 
 @pytest.mark.parametrize("xdtype", [torch.bfloat16, torch.float16])
-@pytest.mark.parametrize("N,K", [(16, 128), (16, 1152), (64, 4096), (1024, 4096), (2064, 1024), (4096, 4096),
-                                 (4096, 3968), (12288, 2048)])
-def test_w8a16_gemv_one_token(gpu_lib, N, K, xdtype):
+@pytest.mark.parametrize("M,N,K,kernel", cases.W8A16_ONE_TOKEN)
+def test_w8a16_gemv_one_token(gpu_lib, M, N, K, kernel, xdtype):
     """M = 1 with K <= 4096: the vector-ALU dot-product kernel, one or two
     weight rows per wave; a K of one block, K ending inside a 1 KB chunk
     (1152, 3968) and shorter than the four chunks the kernel always reads,
     N of one workgroup; all three output types."""
     say("w8a16 gemv", xdtype, f"N={N} K={K}")
+    expect(W8A16, M, N, K, kernel)
     assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A16_BLK128, 1, N, K) == 0
     x = inputs.activations(1, K, workload=660 + N, stream=K, outliers=True, dtype=xdtype)
     wq, ws = oracle.quantize_weight_128x128(f32(inputs.weights_bf16(N, K, workload=661, stream=K)))
@@ -269,10 +261,8 @@ def test_w8a16_gemv_one_token(gpu_lib, N, K, xdtype):
 
 
 @pytest.mark.parametrize("xdtype", [torch.bfloat16, torch.float16])
-@pytest.mark.parametrize("M,N,K", [(17, 1024, 4096), (32, 4096, 4096), (50, 1024, 4096), (64, 4096, 4096),
-                                   (24, 12288, 512), (20, 16, 4096), (20, 64, 128), (128, 4096, 4096),
-                                   (100, 4112, 1024), (256, 1024, 4096), (200, 1040, 1024)])
-def test_w8a16_all_tokens(gpu_lib, M, N, K, xdtype):
+@pytest.mark.parametrize("M,N,K,kernel", cases.W8A16_ALL_TOKENS)
+def test_w8a16_all_tokens(gpu_lib, M, N, K, kernel, xdtype):
     """16 < M <= 256 with K <= 4096: every token of a group per 16- or 32-row
     weight tile, no workspace.  Covers one and two weight-row tiles per
     workgroup (a half-filled last pair at N = 16 and 4112), two and four
@@ -280,6 +270,7 @@ def test_w8a16_all_tokens(gpu_lib, M, N, K, xdtype):
     an empty last tile (M = 100), and K spread over the waves."""
     assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A16_BLK128, M, N, K) == 0
     say("w8a16 all-token", xdtype, f"M={M} N={N} K={K}")
+    expect(W8A16, M, N, K, kernel)
     x = inputs.activations(M, K, workload=640 + M, stream=K, outliers=True, dtype=xdtype)
     wq, ws = oracle.quantize_weight_128x128(f32(inputs.weights_bf16(N, K, workload=640 + N, stream=K)))
     y0 = oracle.gemm_w8a16_blk128(f32(x), wq, ws)
@@ -290,26 +281,32 @@ def test_w8a16_all_tokens(gpu_lib, M, N, K, xdtype):
     assert_16bit_bar(y16, y32, y0, "bf16" if xdtype == torch.bfloat16 else "f16", f"w8a16 all-token M={M}")
 
 
-@pytest.mark.parametrize("M", [1, 3, 16])
-def test_w8a16_blk128_long_k(gpu_lib, M):
-    """K = 12288 on 4096 rows: six 128-K blocks per wave, two passes of up to
-    four blocks with the cross-wave sum in the slab memory."""
-    N, K = 4096, 12288
-    say("w8a16 long K", M)
+@pytest.mark.parametrize("M,N,K,kernel", cases.W8A16_LONG_K + cases.W8A16_SPLIT_K_STREAM)
+def test_w8a16_blk128_long_k(gpu_lib, M, N, K, kernel):
+    """K = 12288: six 128-K blocks per wave on 4096 rows (two passes of up to
+    four blocks, the cross-wave sum in the slab memory), and K split over
+    workgroups on 512 rows, run twice on one workspace (counters re-arm,
+    bit-identical)."""
+    say("w8a16 long K", M, N, kernel)
+    expect(W8A16, M, N, K, kernel)
     x = inputs.activations(M, K, workload=650 + M, dtype=torch.bfloat16)
     wq, ws = oracle.quantize_weight_128x128(f32(inputs.weights_bf16(N, K, workload=651)))
     y0 = oracle.gemm_w8a16_blk128(f32(x), wq, ws)
-    y32 = run_w8a16(x.cuda(), dev(wq), dev(ws), torch.float32)
+    wsb = workspace(bfp8.OP_GEMM_W8A16_BLK128, M, N, K)
+    assert (wsb is not None) == kernel.endswith("/split")
+    y32 = run_w8a16(x.cuda(), dev(wq), dev(ws), torch.float32, wsb)
     assert_fp32_bar(y32, y0, f"w8a16 long K M={M}")
+    y2 = run_w8a16(x.cuda(), dev(wq), dev(ws), torch.float32, wsb)
+    assert torch.equal(y32.view(torch.int32), y2.view(torch.int32))
 
 
 @pytest.mark.parametrize("xdtype", [torch.bfloat16, torch.float16])
-@pytest.mark.parametrize("M", [1, 4, 40])
-def test_w8a16_blk128_one_hot_all_codes_exact(gpu_lib, xdtype, M):
+@pytest.mark.parametrize("M,N,K,kernel", cases.W8A16_ONE_HOT)
+def test_w8a16_blk128_one_hot_all_codes_exact(gpu_lib, xdtype, M, N, K, kernel):
     """x one-hot 1.0: Y[:, n] = E4M3(wq[n, k]) * ws exactly, subnormal codes
     included (vector-ALU kernel at M = 1, streaming kernel at M = 4,
     all-token kernel at M = 40)."""
-    N, K = 256, 256
+    expect(W8A16, M, N, K, kernel)
     wq = np.zeros((N, K), np.uint8)
     wq[:254, :] = FINITE_CODES[:, None]
     ws = np.array([[0.5, 2.0], [0.25, 4.0]], np.float32)
@@ -318,16 +315,18 @@ def test_w8a16_blk128_one_hot_all_codes_exact(gpu_lib, xdtype, M):
         x = torch.zeros((M, K), dtype=xdtype)
         x[:, k] = 1.0
         y = run_w8a16(x.cuda(), dev(wq), dev(ws), torch.float32)
-        expect = oracle.e4m3_decode(wq[:, k]) * ws[np.arange(N) // 128, k // 128]
-        np.testing.assert_array_equal(y.cpu().numpy(), np.broadcast_to(expect, (M, N)))
+        want = oracle.e4m3_decode(wq[:, k]) * ws[np.arange(N) // 128, k // 128]
+        np.testing.assert_array_equal(y.cpu().numpy(), np.broadcast_to(want, (M, N)))
 
 
 @pytest.mark.parametrize("xdtype", [torch.bfloat16, torch.float16])
-@pytest.mark.parametrize("M,N,K", [(40, 1024, 8192), (100, 1040, 8192), (300, 2048, 2176)])
-def test_w8a16_tile_split_k(gpu_lib, M, N, K, xdtype):
+@pytest.mark.parametrize("M,N,K,kernel", cases.W8A16_TILE_SPLIT)
+def test_w8a16_tile_split_k(gpu_lib, M, N, K, kernel, xdtype):
     """Tiled W8A16 with ragged M/N tiles and split K (workspace), run twice on
-    one workspace: bar met, second run bit-identical."""
-    say("w8a16 tile", xdtype, f"M={M} N={N} K={K}")
+    one workspace: bar met, second run bit-identical (and one 128 x 64 plan
+    with enough tiles that K is not split)."""
+    say("w8a16 tile", xdtype, f"M={M} N={N} K={K}", kernel)
+    expect(W8A16, M, N, K, kernel)
     x = inputs.activations(M, K, workload=620 + M, stream=K, outliers=True, dtype=xdtype)
     wq, ws = oracle.quantize_weight_128x128(f32(inputs.weights_bf16(N, K, workload=620 + N, stream=K)))
     y0 = oracle.gemm_w8a16_blk128(f32(x), wq, ws)
@@ -344,7 +343,8 @@ def test_w8a16_tile_split_k(gpu_lib, M, N, K, xdtype):
 @pytest.mark.parametrize("xdtype", [torch.bfloat16, torch.float16])
 def test_w8a16_tile_one_hot_all_codes_exact(gpu_lib, xdtype):
     """Tiled path (M = 300): x one-hot 1.0 gives E4M3(wq[n, k]) * ws exactly."""
-    N, K, M = 256, 256, 300
+    M, N, K, kernel = cases.W8A16_TILE_ONE_HOT
+    expect(W8A16, M, N, K, kernel)
     wq = np.zeros((N, K), np.uint8)
     wq[:254, :] = FINITE_CODES[:, None]
     ws = np.array([[0.5, 2.0], [0.25, 4.0]], np.float32)
@@ -353,16 +353,17 @@ def test_w8a16_tile_one_hot_all_codes_exact(gpu_lib, xdtype):
         x = torch.zeros((M, K), dtype=xdtype)
         x[:, k] = 1.0
         y = run_w8a16(x.cuda(), dev(wq), dev(ws), torch.float32)
-        expect = oracle.e4m3_decode(wq[:, k]) * ws[np.arange(N) // 128, k // 128]
-        np.testing.assert_array_equal(y.cpu().numpy(), np.broadcast_to(expect, (M, N)))
+        want = oracle.e4m3_decode(wq[:, k]) * ws[np.arange(N) // 128, k // 128]
+        np.testing.assert_array_equal(y.cpu().numpy(), np.broadcast_to(want, (M, N)))
 
 
 @pytest.mark.parametrize("xdtype", [torch.bfloat16, torch.float16])
 def test_w8a16_tile_large_ragged(gpu_lib, xdtype):
     """The 256 x 128 W8A16 tile (chosen once it gives 256 tiles) with a ragged
     last weight tile (N = 4112) and a ragged last token tile (M = 2000)."""
-    M, N, K = 2000, 4112, 1024
+    M, N, K, kernel = cases.W8A16_TILE_LARGE_RAGGED
     say("w8a16 tile large", xdtype)
+    expect(W8A16, M, N, K, kernel)
     x = inputs.activations(M, K, workload=640, stream=1, outliers=True, dtype=xdtype)
     wq, ws = oracle.quantize_weight_128x128(f32(inputs.weights_bf16(N, K, workload=641)))
     y0 = oracle.gemm_w8a16_blk128(f32(x), wq, ws)
@@ -377,7 +378,8 @@ def test_w8a16_tile_large_ragged(gpu_lib, xdtype):
 def test_w8a16_tile_large_one_hot_all_codes_exact(gpu_lib, xdtype):
     """256 x 128 tile path (M = 2048, N = 4096): x one-hot 1.0 gives
     E4M3(wq[n, k]) * ws exactly, every finite code in every weight tile."""
-    M, N, K = 2048, 4096, 256
+    M, N, K, kernel = cases.W8A16_TILE_LARGE_ONE_HOT
+    expect(W8A16, M, N, K, kernel)
     wq = FINITE_CODES[np.arange(N) % 254][:, None].repeat(K, axis=1).astype(np.uint8)
     ws = np.where((np.arange(N // 128)[:, None] + np.arange(K // 128)[None, :]) % 2 == 0, 0.5, 4.0).astype(np.float32)
     for k in (3, 200):
@@ -385,14 +387,15 @@ def test_w8a16_tile_large_one_hot_all_codes_exact(gpu_lib, xdtype):
         x = torch.zeros((M, K), dtype=xdtype)
         x[:, k] = 1.0
         y = run_w8a16(x.cuda(), dev(wq), dev(ws), torch.float32)
-        expect = oracle.e4m3_decode(wq[:, k]) * ws[np.arange(N) // 128, k // 128]
-        np.testing.assert_array_equal(y.cpu().numpy(), np.broadcast_to(expect, (M, N)))
+        want = oracle.e4m3_decode(wq[:, k]) * ws[np.arange(N) // 128, k // 128]
+        np.testing.assert_array_equal(y.cpu().numpy(), np.broadcast_to(want, (M, N)))
 
 
 @pytest.mark.parametrize("xdtype", [torch.bfloat16, torch.float16])
 def test_w8a16_prefill_oproj_sampled(gpu_lib, xdtype):
     """M = N = K = 4096 W8A16 with 1% outlier channels: full GPU run, 48 rows checked."""
     say("w8a16 prefill", xdtype)
+    expect(W8A16, *cases.W8A16_PREFILL_OPROJ)
     x = inputs.activations(4096, 4096, workload=2, stream=0, outliers=True, dtype=xdtype)
     w = inputs.workload(2)["w"]
     wq_d, ws_d = bfp8.quantize_weight(w.cuda())
@@ -405,6 +408,7 @@ def test_w8a16_prefill_oproj_sampled(gpu_lib, xdtype):
 
 def test_w8a16_blk128_decode_oproj_full(gpu_lib):
     say("w8a16 o_proj decode")
+    expect(W8A16, *cases.W8A16_DECODE_OPROJ)
     x = inputs.workload(1)["x"]
     wq, ws = oracle.quantize_weight_128x128(f32(inputs.workload(1)["w"]))
     y0 = oracle.gemm_w8a16_blk128(f32(x), wq, ws)
@@ -427,11 +431,12 @@ def _blk32_inputs(M, N, K, wid, lo=-14, hi=7):
     return x, wq, e8.numpy()
 
 
-@pytest.mark.parametrize("M", [1, 2, 3, 4, 8, 12, 16])
-def test_blk32_block32_workload_shape(gpu_lib, M):
+@pytest.mark.parametrize("M,N,K,kernel", cases.BLK32_WORKLOAD)
+def test_blk32_block32_workload_shape(gpu_lib, M, N, K, kernel):
     """N=4096, K=7168 block-32 weights, e uniform on [-14, 7]."""
     say("blk32", M)
-    x, wq, e8 = _blk32_inputs(M, 4096, 7168, 3)
+    expect(BLK32, M, N, K, kernel)
+    x, wq, e8 = _blk32_inputs(M, N, K, 3)
     y0 = oracle.gemm_w8a16_blk32_ue8m0(f32(x), wq, e8)
     xd, wqd, e8d = x.cuda(), dev(wq), dev(e8)
     y32 = run_blk32(xd, wqd, e8d, torch.float32)
@@ -445,35 +450,44 @@ def test_blk32_block32_workload_shape(gpu_lib, M):
 @pytest.mark.parametrize("lo,hi", [(-14, -14), (7, 7)])
 def test_blk32_window_ends(gpu_lib, lo, hi):
     say("blk32 window end", lo)
-    x, wq, e8 = _blk32_inputs(8, 512, 1024, 30 + lo, lo=lo, hi=hi)
+    M, N, K, kernel = cases.BLK32_WINDOW
+    expect(BLK32, M, N, K, kernel)
+    x, wq, e8 = _blk32_inputs(M, N, K, 30 + lo, lo=lo, hi=hi)
     y0 = oracle.gemm_w8a16_blk32_ue8m0(f32(x), wq, e8)
     y32 = run_blk32(x.cuda(), dev(wq), dev(e8), torch.float32)
     assert_fp32_bar(y32, y0, f"blk32 e={lo}")
 
 
+@pytest.mark.parametrize("case", [cases.BLK32_ONE_HOT, cases.BLK32_ONE_HOT_ABOVE_16], ids=lambda c: c[3])
 @pytest.mark.parametrize("out", [torch.float32, torch.float16])
-def test_blk32_one_hot_all_codes_all_exponents_exact(gpu_lib, out):
+def test_blk32_one_hot_all_codes_all_exponents_exact(gpu_lib, out, case):
     """Every finite code times every window exponent is produced exactly
-    (fp16 subnormals at e = -14 included)."""
+    (fp16 subnormals at e = -14 included), by the streaming kernel of M <= 16
+    and by the one for M > 16 (M = 17: a full token tile and a second one
+    with a single live row)."""
     exps = np.arange(-14, 8)
-    N, K, M = 32 * exps.size, 256, 16
+    M, N, K, kernel = case
+    assert N == 32 * exps.size
+    expect(BLK32, M, N, K, kernel)
     wq = np.zeros((N, K), np.uint8)
     wq[:, :254] = FINITE_CODES[None, :]
     e8 = np.repeat((exps + 127).astype(np.uint8)[:, None], K // 32, axis=1)
     d = oracle.e4m3_decode(FINITE_CODES)
     for base in range(0, 256, M):
-        say("blk32 one-hot", out, base)
+        say("blk32 one-hot", out, M, base)
         x = torch.zeros((M, K), dtype=torch.float16)
-        ks = np.arange(base, base + M)
+        ks = np.arange(base, base + M) % K
         x[np.arange(M), ks] = 1.0
         y = run_blk32(x.cuda(), dev(wq), dev(e8), out).float().cpu().numpy()
         for row, k in enumerate(ks):
-            expect = (d[k] if k < 254 else 0.0) * np.exp2(exps.astype(np.float64))
-            np.testing.assert_array_equal(y[row].reshape(exps.size, 32), np.repeat(expect[:, None], 32, axis=1))
+            want = (d[k] if k < 254 else 0.0) * np.exp2(exps.astype(np.float64))
+            np.testing.assert_array_equal(y[row].reshape(exps.size, 32), np.repeat(want[:, None], 32, axis=1))
 
 
-def test_blk32_split_k_and_determinism(gpu_lib):
-    M, N, K = 4, 1024, 12288
+@pytest.mark.parametrize("case", [cases.BLK32_SPLIT_K, cases.BLK32_SPLIT_K_ABOVE_16], ids=lambda c: c[3])
+def test_blk32_split_k_and_determinism(gpu_lib, case):
+    M, N, K, kernel = case
+    expect(BLK32, M, N, K, kernel)
     assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A16_BLK32_UE8M0, M, N, K) > 0
     x, wq, e8 = _blk32_inputs(M, N, K, 31)
     y0 = oracle.gemm_w8a16_blk32_ue8m0(f32(x), wq, e8)
@@ -483,3 +497,25 @@ def test_blk32_split_k_and_determinism(gpu_lib):
     b = run_blk32(x.cuda(), dev(wq), dev(e8), torch.float32, wsb)
     assert_fp32_bar(a, y0, "blk32 split-K")
     assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+@pytest.mark.parametrize("M,N,K,kernel", cases.BLK32_ABOVE_16)
+def test_blk32_above_the_streaming_range(gpu_lib, M, N, K, kernel):
+    """M > 16 on the block-32 workload shape (N = 4096, K = 7168): one
+    16-token tile per workgroup, ragged last tile at M = 17; fp32 output
+    against the oracle (all rows up to M = 64, sampled rows above, the last
+    tile's rows always included) and fp16 output as RNE of the fp32 result."""
+    say("blk32 M > 16", M)
+    expect(BLK32, M, N, K, kernel)
+    x, wq, e8 = _blk32_inputs(M, N, K, 40 + M)
+    xd, wqd, e8d = x.cuda(), dev(wq), dev(e8)
+    y32 = run_blk32(xd, wqd, e8d, torch.float32)
+    yh = run_blk32(xd, wqd, e8d, torch.float16)
+    if M <= 64:
+        rows = np.arange(M)
+    else:
+        rows = np.unique(np.concatenate([np.random.default_rng(M).choice(M, 40, replace=False),
+                                         np.arange(M - 16, M)]))
+    y0 = oracle.gemm_w8a16_blk32_ue8m0(f32(x[rows]), wq, e8)
+    assert_fp32_bar(y32[rows], y0, f"blk32 M={M}")
+    assert_16bit_bar(yh[rows], y32[rows], y0, "f16", f"blk32 M={M}")
