@@ -57,8 +57,14 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", choices=["decode", "prefill", "blk32", "w8a16", "sweep"], default="decode")
     p.add_argument("--m", type=int, default=None, help="token count for blk32 / decode")
-    p.add_argument("--copies", type=int, default=32, help="distinct weight copies rotated per call")
-    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--copies", type=int, default=24,
+                   help="decode: distinct weight copies rotated per kernel (each kernel has its own set); "
+                        "other workloads: copies rotated per call")
+    p.add_argument("--cpu-seconds", type=float, default=8.0, help="per leg (one thread, all cores)")
+    p.add_argument("--no-extras", action="store_true",
+                   help="decode: skip the extra kernel lines (read floor, prefill GEMM, block-32 at M = 1)")
+    p.add_argument("--prefill-warm-ms", type=float, default=250.0,
+                   help="GPU time the prefill GEMM runs back to back before its timed launches (clock ramp)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-graph", action="store_true", help="decode: skip the HIP graph replay timing")
     p.add_argument("--smi", action="store_true",
@@ -216,14 +222,64 @@ def run_steps(torch, phases, steps, warmup):
                                      "method": "per-kernel phases of back-to-back launches, HIP events"}
 
 
+# ---------------------------------------------------------- cache reuse ----
+MALL_BYTES = 256 << 20      # MI355X Infinity Cache (memory-side, shared by all XCDs)
+
+
+def launch_order(phase_names, copies_of, warmup, steps, gpu_bound_rewarm=True):
+    """The (phase, copy) sequence run_steps issues: warmup steps in step
+    order (twice when the GPU-bound path queues a second warmup round), then
+    the timed steps phase by phase.  Returns the sequence and the position of
+    the first timed launch."""
+    seq = []
+    for _ in range(2 if gpu_bound_rewarm else 1):
+        for i in range(warmup):
+            seq += [(p, copies_of[p](i)) for p in phase_names]
+    timed = len(seq)
+    for p in phase_names:
+        seq += [(p, copies_of[p](warmup + s)) for s in range(steps)]
+    return seq, timed
+
+
+def min_reuse_bytes(seq, bytes_of, first=0):
+    """Smallest number of other weight bytes read between a read at position
+    >= `first` in `seq` and the previous read of the same buffer (None when
+    no such buffer is read twice)."""
+    last, total, best = {}, 0, None
+    for pos, (p, c) in enumerate(seq):
+        key = (p, c)
+        if key in last and pos >= first:
+            d = total - last[key]
+            best = d if best is None else min(best, d)
+        total += bytes_of[p]
+        last[key] = total
+    return best
+
+
+def assert_no_cache_reuse(order, bytes_of, what):
+    """No timed launch reads a weight copy that less than the last-level
+    cache's size of other weights has followed since its previous read."""
+    seq, timed = order
+    d = min_reuse_bytes(seq, bytes_of, timed)
+    assert d is None or d >= MALL_BYTES, (
+        f"{what}: a weight copy is re-read after only {d} bytes of other weights (< {MALL_BYTES}, the "
+        f"last-level cache): use more copies")
+    return d
+
+
 # ------------------------------------------------------------ CPU baseline ----
-def cpu_baseline(fn, seconds, unit_per_call, unit, sample):
-    import numpy as np  # noqa: F401
+def _cpu_share():
+    """Host cores this process may use: the affinity mask, capped by the
+    thread budget the environment sets (OMP_NUM_THREADS)."""
+    n = len(os.sched_getaffinity(0))
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        threads = 1
+        n = min(n, int(os.environ.get("OMP_NUM_THREADS", n)))
+    except ValueError:
+        pass
+    return max(1, n)
+
+
+def _time_calls(fn, seconds):
     calls = 0
     t0 = time.perf_counter()
     while True:
@@ -231,9 +287,135 @@ def cpu_baseline(fn, seconds, unit_per_call, unit, sample):
         calls += 1
         el = time.perf_counter() - t0
         if el >= seconds:
-            break
-    return {"value": unit_per_call * calls / el, "unit": unit, "cores": threads, "kind": "oracle",
-            "sample": f"{sample}; {calls} calls in {el:.1f} s; numpy float64, BLAS threads={threads}"}
+            return calls, el
+
+
+def cpu_baseline(fn, seconds, unit_per_call, unit, sample):
+    """The oracle as it stands, timed on the host: once with one BLAS thread
+    and once with every core of this process's share; `value` is the
+    all-core figure."""
+    from threadpoolctl import threadpool_limits
+    nproc = len(os.sched_getaffinity(0))
+    share = _cpu_share()
+    with threadpool_limits(limits=1):
+        c1, t1 = _time_calls(fn, seconds)
+    with threadpool_limits(limits=share):
+        cn, tn = _time_calls(fn, seconds)
+    return {"value": unit_per_call * cn / tn, "unit": unit, "cores": share, "kind": "oracle",
+            "sample": f"{sample}; {cn} calls in {tn:.1f} s with {share} BLAS threads, {c1} calls in {t1:.1f} s "
+                      f"with 1; numpy float64",
+            "one_core": {"value": unit_per_call * c1 / t1, "cores": 1}, "nproc": nproc}
+
+
+# ------------------------------------------------------- extra kernel lines ----
+def timed_after_ramp(torch, launch, steps, warm_ms):
+    """Run `launch` back to back for about `warm_ms` of GPU time (the clock
+    ramps up under sustained load), then time `steps` more launches queued
+    right behind them with one HIP event pair, with no idle gap in between."""
+    for i in range(5):
+        launch(i)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(20):
+        launch(5 + i)
+    b.record()
+    torch.cuda.synchronize()
+    est_us = 1e3 * a.elapsed_time(b) / 20
+    n_warm = max(20, int(warm_ms * 1e3 / max(est_us, 1e-3)))
+    for i in range(n_warm):
+        launch(25 + i)
+    a.record()
+    for s in range(steps):
+        launch(25 + n_warm + s)
+    b.record()
+    torch.cuda.synchronize()
+    return 1e3 * a.elapsed_time(b) / steps, n_warm, n_warm * est_us / 1e3
+
+
+def read_floor(torch, buffers, nbytes, steps, warmup):
+    """Per-launch time of the streaming-read probe over rotated buffers (the
+    best of 4, 8 and 16 loads per thread)."""
+    import ctypes
+    from blockwise_scaled_fp8_amd.build import PROBE_LIB
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.bfp8_read_probe.restype = ctypes.c_int
+    lib.bfp8_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.bfp8_probe_workgroups.restype = ctypes.c_int64
+    lib.bfp8_probe_workgroups.argtypes = [ctypes.c_int64, ctypes.c_int]
+    sink = torch.empty(int(lib.bfp8_probe_workgroups(nbytes, 4)), dtype=torch.int32, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    best = None
+    for loads in (4, 8, 16):
+        def launch(i, loads=loads):
+            rc = lib.bfp8_read_probe(ctypes.c_void_p(buffers[i % len(buffers)].data_ptr()), nbytes, loads,
+                                     ctypes.c_void_p(sink.data_ptr()), stream)
+            assert rc == 0, rc
+        _, _, kern, _ = run_steps(torch, [("read", launch)], steps, warmup)
+        us = kern["read"]["avg_us"]
+        if best is None or us < best[0]:
+            best = (us, loads)
+    return {"avg_us": best[0], "alg_bytes": nbytes, "GBps": nbytes / (best[0] * 1e3),
+            "hbm_frac": nbytes / (best[0] * 1e3) / HBM_PEAK_GBS, "loads_per_thread": best[1],
+            "what": "plain 16-byte streaming read of the same rotated weight copies, one dword written per workgroup; "
+                    "best of 4/8/16 loads per thread"}
+
+
+def extra_prefill(torch, bfp8, inputs, args):
+    """The prefill GEMM (M = N = K = 4096, codes in) after the clock has
+    ramped: run back to back for --prefill-warm-ms of GPU time first."""
+    M = N = K = 4096
+    data = inputs.workload(2, M=M)
+    xq, xs = bfp8.quantize_act(data["x"].cuda())
+    wq, ws = bfp8.quantize_weight(data["w"].cuda())
+    copies = [(wq.clone(), ws.clone()) for _ in range(4)]
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    wsp = bfp8.make_workspace(bfp8.OP_GEMM_W8A8_BLK128, M, N, K)
+
+    def gemm(i):
+        a = copies[i % len(copies)]
+        bfp8.bfp8_gemm_w8a8_blk128(xq, xs, a[0], a[1], y, wsp)
+
+    us, n_warm, warm_ms = timed_after_ramp(torch, gemm, 200, args.prefill_warm_ms)
+    flops = 2.0 * M * N * K
+    out = {"avg_us": us, "TFLOPs": flops / (us * 1e6), "mfma_frac": flops / (us * 1e6) / FP8_PEAK_TFLOPS,
+           "alg_bytes": bytes_w8a8(M, N, K), "M": M, "N": N, "K": K,
+           "kernel": bfp8.bfp8_get_plan(bfp8.OP_GEMM_W8A8_BLK128, M, N, K)["kernel_name"],
+           "ramp": f"{n_warm} launches (~{warm_ms:.0f} ms of GPU time) back to back before 200 timed launches, "
+                   f"no idle gap: the clock ramps up over the first ~20 ms of sustained load"}
+    if args.smi:
+        for i in range(int(1000e3 / us)):       # ~1 s of queued work: sample the clock under it
+            gemm(i)
+        out["smi_under_load"] = smi_sample()
+        torch.cuda.synchronize()
+    del copies, y, wsp
+    return out
+
+
+def extra_blk32(torch, bfp8, inputs, args, M=1):
+    N, K = 4096, 7168
+    x = inputs.activations(M, K, workload=3, dtype=torch.float16).cuda()
+    wq_h = inputs.block32_codes(N, K, workload=3)
+    st, e8_h, bad = bfp8.bfp8_prepare_blk32_ue8m0(wq_h, inputs.block32_scales(N, K, workload=3))
+    assert st == 0, (st, bad)
+    nb = bytes_blk32(M, N, K)
+    ncopy = 12
+    copies = [(wq_h.cuda(), e8_h.cuda()) for _ in range(ncopy)]
+    assert_no_cache_reuse(launch_order(["g"], {"g": lambda i: i % ncopy}, args.warmup, args.steps), {"g": N * K},
+                          "block-32")
+    y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    wsb = bfp8.make_workspace(bfp8.OP_GEMM_W8A16_BLK32_UE8M0, M, N, K)
+
+    def gemm(i):
+        a = copies[i % ncopy]
+        bfp8.bfp8_gemm_w8a16_blk32_ue8m0(x, a[0], a[1], y, wsb)
+
+    _, _, kern, _ = run_steps(torch, [("g", gemm)], args.steps, args.warmup)
+    us = kern["g"]["avg_us"]
+    del copies
+    return {"avg_us": us, "alg_bytes": nb, "GBps": nb / (us * 1e3), "hbm_frac": nb / (us * 1e3) / HBM_PEAK_GBS,
+            "M": M, "N": N, "K": K, "weight_copies": ncopy,
+            "kernel": bfp8.bfp8_get_plan(bfp8.OP_GEMM_W8A16_BLK32_UE8M0, M, N, K)["kernel_name"]}
 
 
 # --------------------------------------------------------------- workloads ----
@@ -272,7 +454,12 @@ def bench_decode(torch, bfp8, inputs, args):
     x = data["x"].cuda()
     w = data["w"].cuda()
     wq0, ws0 = bfp8.quantize_weight(w)
-    copies = [(wq0.clone(), ws0.clone()) for _ in range(args.copies)]
+    # Each kernel rotates over its own set of weight copies, so no copy is
+    # read again before more than the last-level cache's size of other
+    # weights has streamed through (checked below for the exact launch order).
+    C = args.copies
+    copies8 = [(wq0.clone(), ws0.clone()) for _ in range(C)]
+    copies16 = [(wq0.clone(), ws0.clone()) for _ in range(C)]
     del w
     xq = torch.empty((M, K), dtype=torch.uint8, device="cuda")
     xs = torch.empty((M, K // 128), dtype=torch.float32, device="cuda")
@@ -281,18 +468,17 @@ def bench_decode(torch, bfp8, inputs, args):
     ws8 = bfp8.make_workspace(bfp8.OP_GEMM_W8A8_BLK128, M, N, K)
     wsq = bfp8.make_workspace(bfp8.OP_QUANT_GEMM_W8A8_BLK128, M, N, K)
     ws16 = bfp8.make_workspace(bfp8.OP_GEMM_W8A16_BLK128, M, N, K)
-    C = len(copies)
 
     def w8a8(i):
-        a = copies[i % C]
+        a = copies8[i % C]
         bfp8.bfp8_gemm_w8a8_blk128(xq, xs, a[0], a[1], y8, ws8)
 
     def quant_w8a8(i):
-        a = copies[i % C]
+        a = copies8[i % C]
         bfp8.bfp8_quant_gemm_w8a8_blk128(x, a[0], a[1], y8, wsq)
 
     def w8a16(i):
-        b = copies[(i + C // 2) % C]
+        b = copies16[i % C]
         bfp8.bfp8_gemm_w8a16_blk128(x, b[0], b[1], y16, ws16)
 
     if args.unfused:
@@ -301,6 +487,12 @@ def bench_decode(torch, bfp8, inputs, args):
     else:
         phases = [("quant_gemm_w8a8_blk128", quant_w8a8), ("gemm_w8a16_blk128", w8a16)]
     names = [n for n, _ in phases]
+    set_of = {"quant_act_1x128": None, "gemm_w8a8_blk128": "w8", "quant_gemm_w8a8_blk128": "w8",
+              "gemm_w8a16_blk128": "w16"}
+    weight_phases = [n for n in names if set_of[n]]
+    seq, timed = launch_order(weight_phases, {n: (lambda i: i % C) for n in weight_phases}, args.warmup, args.steps)
+    seq = [(set_of[p], c) for p, c in seq]
+    reuse = assert_no_cache_reuse((seq, timed), {"w8": N * K, "w16": N * K}, "decode")
     ms, wall, kern, timing = run_steps(torch, phases, args.steps, args.warmup)
     nbytes = {"quant_act_1x128": bytes_quant(M, K), "gemm_w8a8_blk128": bytes_w8a8(M, N, K),
               "quant_gemm_w8a8_blk128": bytes_quant_w8a8(M, N, K), "gemm_w8a16_blk128": bytes_w8a16(M, N, K)}
@@ -318,12 +510,25 @@ def bench_decode(torch, bfp8, inputs, args):
               "config": {"workload": ("o_proj decode: 1x128 act quant + W8A8 blk128 + W8A16 blk128 (bf16 x)"
                                       if args.unfused else
                                       "o_proj decode: W8A8 blk128 with fused 1x128 act quant + W8A16 blk128 (bf16 x)"),
-                         "M": M, "N": N, "K": K, "weight_copies": C, "out_dtype": "bf16",
+                         "M": M, "N": N, "K": K, "weight_copies": 2 * C, "out_dtype": "bf16",
                          "step_alg_bytes": step_bytes},
               "roofline": roof, "kernels": kern, "wall_s": wall, "timing": timing}
+    result["timing"]["weight_rotation"] = (
+        f"{C} copies per GEMM kernel ({2 * C} in all, 16 MiB each); fewest other weight bytes between two reads "
+        f"of one copy in this run's launch order: {reuse} (last-level cache {MALL_BYTES})")
 
     if not args.no_graph:
         result["timing"]["graph"] = graph_timing(torch, phases, C, max(1, args.steps // C))
+
+    if not args.no_extras:
+        floor = read_floor(torch, [a[0] for a in copies8], N * K, args.steps, args.warmup)
+        for n in names:
+            if set_of[n]:
+                kern[n]["vs_read_floor"] = kern[n]["avg_us"] / floor["avg_us"]
+        kern["read_floor"] = floor
+        kern["prefill_gemm_w8a8_blk128"] = extra_prefill(torch, bfp8, inputs, args)
+        torch.cuda.empty_cache()
+        kern["blk32_m1"] = extra_blk32(torch, bfp8, inputs, args, M=1)
 
     if not args.no_cpu_baseline:
         import oracle

@@ -45,15 +45,25 @@ def _run(cmd):
     return p
 
 
-def build(verbose=False):
-    """Compile every HIP source for gfx950 into libbfp8.so (always recompiles)."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC] + COMMON_FLAGS + ["-shared", "-o", tmp] + srcs
-    p = _run(cmd)
-    os.replace(tmp, LIB)
+# The benchmark's streaming-read probe: a separate library, not part of the
+# GEMM library's C ABI.
+PROBE_SOURCES = ["read_probe.hip"]
+PROBE_LIB = os.path.join(PKG, "libbfp8_probe.so")
+
+
+def _link(sources, out, verbose):
+    tmp = out + ".tmp"
+    p = _run([HIPCC] + COMMON_FLAGS + ["-shared", "-o", tmp] + [os.path.join(CSRC, s) for s in sources])
+    os.replace(tmp, out)
     if verbose:
         sys.stderr.write(p.stderr)
+
+
+def build(verbose=False):
+    """Compile every HIP source for gfx950 into libbfp8.so, and the read
+    probe into libbfp8_probe.so (always recompiles)."""
+    _link(SOURCES, LIB, verbose)
+    _link(PROBE_SOURCES, PROBE_LIB, verbose)
     return LIB
 
 
