@@ -13,7 +13,7 @@ from ._lib import (  # noqa: F401
     OP_QUANT_ACT_1X128, OP_QUANT_WEIGHT_128X128, OP_GEMM_W8A8_BLK128, OP_GEMM_W8A16_BLK128,
     OP_GEMM_W8A16_BLK32_UE8M0, OP_QUANT_GEMM_W8A8_BLK128,
     load, bfp8_quantize_act_1x128, bfp8_quantize_weight_128x128, bfp8_dequantize_weight,
-    bfp8_gemm_w8a8_blk128, bfp8_quant_gemm_w8a8_blk128,
+    bfp8_gemm_w8a8_blk128, bfp8_gemm_w8a8_blk128_noalloc, bfp8_quant_gemm_w8a8_blk128, NOALLOC_SCRATCH_BYTES,
     bfp8_gemm_w8a16_blk128, bfp8_gemm_w8a16_blk32_ue8m0, bfp8_prepare_blk32_ue8m0,
     bfp8_workspace_bytes, bfp8_get_limits, bfp8_get_plan, bfp8_kernel_name, bfp8_status_string,
 )

@@ -23,7 +23,8 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libbfp8.so")
 
-# Values of the C enums in include/bfp8.h.
+# Values of the C enums and constants in include/bfp8.h.
+NOALLOC_SCRATCH_BYTES = (16 << 20) + 4096
 BFP8_BF16, BFP8_F16, BFP8_F32 = 0, 1, 2
 OP_QUANT_ACT_1X128 = 0
 OP_QUANT_WEIGHT_128X128 = 1
@@ -44,6 +45,7 @@ SIGNATURES = {
     "bfp8_quantize_weight_128x128": (_I, [_P, _I, _I64, _I64, _P, _P, _P]),
     "bfp8_dequantize_weight": (_I, [_P, _P, _I64, _P, _I, _I64, _I64, _P]),
     "bfp8_gemm_w8a8_blk128": (_I, [_P, _P, _P, _P, _P, _I, _I64, _I64, _I64, _P, _SZ, _P]),
+    "bfp8_gemm_w8a8_blk128_noalloc": (_I, [_P, _P, _P, _P, _P, _I, _I64, _I64, _I64, _P]),
     "bfp8_quant_gemm_w8a8_blk128": (_I, [_P, _I, _P, _P, _P, _I, _I64, _I64, _I64, _P, _SZ, _P]),
     "bfp8_gemm_w8a16_blk128": (_I, [_P, _I, _P, _P, _P, _I, _I64, _I64, _I64, _P, _SZ, _P]),
     "bfp8_gemm_w8a16_blk32_ue8m0": (_I, [_P, _I, _P, _P, _P, _I, _I64, _I64, _I64, _P, _SZ, _P]),
@@ -219,6 +221,20 @@ def bfp8_gemm_w8a8_blk128(xq, xs, wq, ws, y, workspace=None):
     wsp, wsb = _ws(workspace)
     _check(load().bfp8_gemm_w8a8_blk128(_ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), _ptr(y), _dtype_code(y),
                                         M, N, K, wsp, wsb, _stream()), w)
+
+
+def bfp8_gemm_w8a8_blk128_noalloc(xq, xs, wq, ws, y):
+    """bfp8_gemm_w8a8_blk128 with the library's own per-GPU scratch as the
+    workspace (for callers that cannot allocate; calls on one GPU must not
+    overlap in time)."""
+    w = "bfp8_gemm_w8a8_blk128_noalloc"
+    M, K = _mat(w, "xq", xq, _U8)
+    _arg(w, "xs", xs, _F32, (M, _cdiv(K, 128)))
+    N = _weights_blk128(w, wq, ws, K)
+    _arg(w, "y", y, _OUT, (M, N))
+    _placed(w, xq=xq, xs=xs, wq=wq, ws=ws, y=y)
+    _check(load().bfp8_gemm_w8a8_blk128_noalloc(_ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), _ptr(y), _dtype_code(y),
+                                                M, N, K, _stream()), w)
 
 
 def bfp8_quant_gemm_w8a8_blk128(x, wq, ws, y, workspace=None):

@@ -4,8 +4,12 @@
 #include <math.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "bfp8.h"
 #include "bfp8_launch.hpp"
+#include "stream_common.hpp"
 
 using namespace bfp8;
 
@@ -188,6 +192,91 @@ bfp8_status bfp8_gemm_w8a8_blk128(const uint8_t* xq, const float* xs, const uint
     if (st != BFP8_OK) return st;
     if (!aligned(xs)) return BFP8_E_ALIGN;
     return launched(launch_w8a8(xq, xs, wq, ws, y, y_dtype, M, N, K, workspace, as_stream(stream)));
+}
+
+}  // extern "C"
+
+// ------------------------------------------------ allocation-free variant ----
+// bfp8_gemm_w8a8_blk128_noalloc takes its workspace from this array: one
+// copy per GPU, held by the loaded library until the process ends.  Host code
+// never uses the array's name as a device address (in host code it names a
+// host-side stand-in); the device address comes from hipGetSymbolAddress,
+// once per device, and only that pointer is passed to kernels.
+namespace {
+
+static __device__ __attribute__((aligned(256))) uint8_t scratch[BFP8_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The scratch address on the current device (set up on its first use).
+hipError_t scratch_on_current_device(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    void* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            if (!p) return hipErrorInvalidSymbol;
+            g_scratch[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return hipSuccess;
+}
+
+// Clears n dwords with vector stores (a kernel, not a memset, so the call
+// can be captured into a HIP graph).
+__global__ __launch_bounds__(256) void clear_words_kernel(uint32_t* __restrict__ p, uint32_t n) {
+    for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < n; i += gridDim.x * 256u) p[i] = 0u;
+}
+
+// Leading workspace bytes of the W8A8 codes call that must be zero when it
+// starts: the split-K tile counters of its plan (0 when it does not split K).
+size_t w8a8_counter_bytes(int64_t M, int64_t N, int64_t K) {
+    switch (route(BFP8_OP_GEMM_W8A8_BLK128, M, N, K)) {
+        case BFP8_KERNEL_W8A8_STREAM: {
+            const StreamPlan p = plan_stream(M, N, K);
+            return p.splits > 1 ? stream_counter_bytes(p) : 0;
+        }
+        case BFP8_KERNEL_W8A8_TILE:
+            return tile_counter_bytes(M, N, K);
+        default:
+            return 0;
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+bfp8_status bfp8_gemm_w8a8_blk128_noalloc(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
+                                          void* y, int y_dtype, int64_t M, int64_t N, int64_t K, void* stream) {
+    if (!xq || !xs || !wq || !ws || !y) return BFP8_E_NULL;
+    const size_t need = (dim_ok(M, 1) && dim_ok(N, 16) && dim_ok(K, 128))
+                            ? bfp8_workspace_bytes(BFP8_OP_GEMM_W8A8_BLK128, M, N, K) : 0;
+    bfp8_status st = check_gemm(xq, wq, ws, y, y_dtype, M, N, K, 16, 0, nullptr, 0);
+    if (st != BFP8_OK) return st;
+    if (!aligned(xs)) return BFP8_E_ALIGN;
+    if (need > BFP8_NOALLOC_SCRATCH_BYTES) return BFP8_E_WORKSPACE;
+    void* work = nullptr;
+    if (need > 0) {
+        if (scratch_on_current_device(&work) != hipSuccess) return BFP8_E_LAUNCH;
+        const size_t counters = w8a8_counter_bytes(M, N, K);
+        if (counters > 0) {
+            const uint32_t words = (uint32_t)(counters / 4);
+            hipLaunchKernelGGL(clear_words_kernel, dim3((words + 255) / 256), dim3(256), 0, as_stream(stream),
+                               static_cast<uint32_t*>(work), words);
+            if (hipGetLastError() != hipSuccess) return BFP8_E_LAUNCH;
+        }
+    }
+    return launched(launch_w8a8(xq, xs, wq, ws, y, y_dtype, M, N, K, work, as_stream(stream)));
 }
 
 bfp8_status bfp8_quant_gemm_w8a8_blk128(const void* x, int x_dtype, const uint8_t* wq, const float* ws,

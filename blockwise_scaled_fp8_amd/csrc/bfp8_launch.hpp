@@ -21,6 +21,9 @@ constexpr int64_t kStreamRows = 16;
 size_t tile_workspace_bytes(int64_t M, int64_t N, int64_t K);
 // Workspace bytes of the tiled W8A16 kernels.
 size_t tile16_workspace_bytes(int64_t M, int64_t N, int64_t K);
+// Leading bytes of the tiled W8A8 workspace that hold the zero-initialised
+// tile counters (0 when the plan does not split K).
+size_t tile_counter_bytes(int64_t M, int64_t N, int64_t K);
 // The tiled kernels' choice for a shape (the same planner the launches use):
 // workgroup tile (weight rows x tokens), waves, tiles and K splits.
 struct TileInfo {

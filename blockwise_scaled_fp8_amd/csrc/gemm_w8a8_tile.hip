@@ -726,6 +726,11 @@ TileInfo tile16_info(int64_t M, int64_t N, int64_t K) { return info_of(plan_tile
 
 size_t tile16_workspace_bytes(int64_t M, int64_t N, int64_t K) { return plan_workspace_bytes(plan_tile16(M, N, K)); }
 
+size_t tile_counter_bytes(int64_t M, int64_t N, int64_t K) {
+    const TilePlan p = plan_tile(M, N, K);
+    return p.splits > 1 ? counter_bytes(p) : 0;
+}
+
 static void split_parts(const TilePlan& p, void* workspace, uint32_t*& counters, float*& partials) {
     counters = nullptr;
     partials = nullptr;

@@ -148,6 +148,32 @@ bfp8_status bfp8_gemm_w8a8_blk128(const uint8_t* xq, const float* xs,
                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The W8A8 blockwise GEMM for callers that cannot allocate: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, kernels and results (bit for bit) as bfp8_gemm_w8a8_blk128,
+ * without the workspace arguments: the library keeps one device array of
+ * BFP8_NOALLOC_SCRATCH_BYTES per GPU (static device memory, held from the
+ * library's first use on that GPU until the process ends) and uses it as
+ * the workspace.  The call allocates nothing and calls no allocating
+ * routine; on its first call on a GPU it looks up that GPU's copy of the
+ * array (hipGetSymbolAddress, no allocation).  When the plan splits K it
+ * first clears the plan's tile counters with a small kernel on `stream`
+ * (no memset, so the call can be captured into a graph).
+ * Every call on one GPU shares that GPU's array: calls that may overlap in
+ * time on one GPU (other streams, other threads, graphs replayed
+ * concurrently) race and must be serialised by the caller.
+ * Shapes whose workspace (bfp8_workspace_bytes(BFP8_OP_GEMM_W8A8_BLK128,
+ * M, N, K)) exceeds BFP8_NOALLOC_SCRATCH_BYTES return BFP8_E_WORKSPACE (the
+ * planners keep every shape within it: at most 16 MiB + 512 bytes).
+ * Other errors as for bfp8_gemm_w8a8_blk128; BFP8_E_LAUNCH also when the
+ * array cannot be located on the current device.
+ */
+#define BFP8_NOALLOC_SCRATCH_BYTES ((size_t)(16u << 20) + 4096u)
+bfp8_status bfp8_gemm_w8a8_blk128_noalloc(const uint8_t* xq, const float* xs,
+                                          const uint8_t* wq, const float* ws,
+                                          void* y, int y_dtype, int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
  * Activation quantisation fused with the W8A8 blockwise GEMM.  [ADA]
  * "Results on the L4" counts the activation quantisation inside the GEMM's
  * time and "What's not good yet" names batch-1 decode as the gap; fusing

@@ -41,7 +41,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared()
-    assert len(names) == 13
+    assert len(names) == 14
     assert sorted(_lib.SIGNATURES) == names
     nm = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], stdout=subprocess.PIPE, text=True).stdout
     exported = set(re.findall(r" T (bfp8_\w+)", nm))
@@ -274,3 +274,35 @@ def test_kernels_have_no_scratch_and_no_spills():
         assert r["ScratchSize [bytes/lane]"] == 0, name
         assert r["VGPRs Spill"] == 0 and r["SGPRs Spill"] == 0, name
         assert r["LDS Size [bytes/block]"] <= 160 * 1024, name
+
+
+# ------------------------------------------------ allocation-free W8A8 ----
+
+def test_noalloc_scratch_size_matches_the_header():
+    text = open(HEADER).read()
+    assert "#define BFP8_NOALLOC_SCRATCH_BYTES ((size_t)(16u << 20) + 4096u)" in text
+    assert bfp8.NOALLOC_SCRATCH_BYTES == (16 << 20) + 4096
+
+
+def test_noalloc_scratch_covers_every_planned_workspace():
+    """The planners keep every W8A8 workspace within the static scratch, so
+    the allocation-free call serves every shape the workspace call does."""
+    import itertools
+    worst = 0
+    for M, N, K in itertools.product(list(range(1, 70)) + [96, 128, 129, 200, 256, 300, 400, 512, 768, 1000, 1024,
+                                                           2048, 4096, 8192],
+                                     [16, 64, 256, 512, 1024, 2048, 4096, 8192, 12288, 16384, 65536],
+                                     [128, 512, 1024, 2048, 4096, 8192, 12288, 16384, 65536]):
+        worst = max(worst, bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, M, N, K))
+    assert 0 < worst <= bfp8.NOALLOC_SCRATCH_BYTES
+
+
+@pytest.mark.parametrize("args,expect", [
+    (dict(xq=0), 1), (dict(y=0), 1), (dict(M=0), 2), (dict(N=24), 2), (dict(K=200), 2), (dict(y_dtype=7), 3),
+    (dict(y=MISALIGNED), 4), (dict(xs=MISALIGNED), 4),
+])
+def test_noalloc_validation(lib, args, expect):
+    a = dict(xq=A, xs=B, wq=C, ws=B, y=Y, y_dtype=0, M=4, N=256, K=512)
+    a.update(args)
+    assert lib.bfp8_gemm_w8a8_blk128_noalloc(a["xq"], a["xs"], a["wq"], a["ws"], a["y"], a["y_dtype"], a["M"],
+                                            a["N"], a["K"], None) == expect
