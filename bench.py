@@ -63,6 +63,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=8.0, help="per leg (one thread, all cores)")
     p.add_argument("--no-extras", action="store_true",
                    help="decode: skip the extra kernel lines (read floor, prefill GEMM, block-32 at M = 1)")
+    p.add_argument("--sweep-warm-ms", type=float, default=40.0,
+                   help="sweep: GPU time each point's GEMM runs back to back before its timed launches")
     p.add_argument("--prefill-warm-ms", type=float, default=250.0,
                    help="GPU time the prefill GEMM runs back to back before its timed launches (clock ramp)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -309,28 +311,38 @@ def cpu_baseline(fn, seconds, unit_per_call, unit, sample):
 
 # ------------------------------------------------------- extra kernel lines ----
 def timed_after_ramp(torch, launch, steps, warm_ms):
-    """Run `launch` back to back for about `warm_ms` of GPU time (the clock
-    ramps up under sustained load), then time `steps` more launches queued
-    right behind them with one HIP event pair, with no idle gap in between."""
+    """Run `launch` back to back for about `warm_ms` (the clock ramps up under
+    sustained load), then time `steps` more launches with one HIP event pair,
+    queued right behind the warm ones.  When the host enqueues a launch more
+    slowly than the GPU runs it, a spin kernel queued between the two keeps
+    the GPU busy while the host enqueues the timed launches, so the events see
+    back-to-back GPU execution rather than the host's launch rate.  Returns
+    (us per launch, warm launches, warm ms)."""
     for i in range(5):
         launch(i)
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
     a.record()
     for i in range(20):
         launch(5 + i)
     b.record()
+    host_us = (time.perf_counter() - t0) * 1e6 / 20
     torch.cuda.synchronize()
     est_us = 1e3 * a.elapsed_time(b) / 20
-    n_warm = max(20, int(warm_ms * 1e3 / max(est_us, 1e-3)))
+    gpu_bound = host_us < 0.5 * est_us
+    cyc_per_ms = None if gpu_bound else _sleep_cycles_per_ms(torch)
+    n_warm = max(20, int(warm_ms * 1e3 / max(est_us, host_us, 1e-3)))
     for i in range(n_warm):
         launch(25 + i)
+    if not gpu_bound:
+        torch.cuda._sleep(int((1.5 * host_us * steps / 1e3 + 2.0) * cyc_per_ms))
     a.record()
     for s in range(steps):
         launch(25 + n_warm + s)
     b.record()
     torch.cuda.synchronize()
-    return 1e3 * a.elapsed_time(b) / steps, n_warm, n_warm * est_us / 1e3
+    return 1e3 * a.elapsed_time(b) / steps, n_warm, n_warm * max(est_us, host_us) / 1e3
 
 
 def read_floor(torch, buffers, nbytes, steps, warmup):
@@ -672,6 +684,14 @@ def bench_w8a16(torch, bfp8, inputs, args):
     return result
 
 
+def cases_variant(bfp8, M, N, K):
+    p = bfp8.bfp8_get_plan(bfp8.OP_GEMM_W8A8_BLK128, M, N, K)
+    v = p["kernel_name"]
+    if "tile" in v or "wide" in v:
+        v += f":{p['tile_n']}x{p['tile_m']}w{p['waves']}"
+    return v + (f"/split{p['splits']}" if p["splits"] > 1 else "")
+
+
 def bench_sweep(torch, bfp8, inputs, args):
     import math
     points = []
@@ -693,13 +713,16 @@ def bench_sweep(torch, bfp8, inputs, args):
                 a = copies[i % len(copies)]
                 bfp8.bfp8_gemm_w8a8_blk128(xq, xs, a[0], a[1], y, wsb)
 
-            phases = [("quant_act_1x128", lambda i, x=x, xq=xq, xs=xs: bfp8.bfp8_quantize_act_1x128(x, xq, xs)),
-                      ("gemm_w8a8_blk128", gemm)]
-            ms, wall, kern, timing = run_steps(torch, phases, steps, max(3, args.warmup))
-            g_us = kern["gemm_w8a8_blk128"]["avg_us"]
+            phases = [("quant_act_1x128", lambda i, x=x, xq=xq, xs=xs: bfp8.bfp8_quantize_act_1x128(x, xq, xs))]
+            _, _, kern, _ = run_steps(torch, phases, steps, max(3, args.warmup))
+            bfp8.bfp8_quantize_act_1x128(x, xq, xs)
+            # The GEMM after a time-based ramp (the clock needs ~20 ms of load),
+            # rotating over the copies from the first launch on.
+            g_us, _, _ = timed_after_ramp(torch, gemm, steps, args.sweep_warm_ms)
             nbytes, flops = bytes_w8a8(M, N, K), 2.0 * M * N * K
             roof_us = max(nbytes / (HBM_PEAK_GBS * 1e3), flops / (FP8_PEAK_TFLOPS * 1e6))
-            points.append({"N": N, "K": K, "M": M, "gemm_us": g_us, "quant_us": kern["quant_act_1x128"]["avg_us"],
+            points.append({"N": N, "K": K, "M": M, "kernel": cases_variant(bfp8, M, N, K),
+                           "gemm_us": g_us, "quant_us": kern["quant_act_1x128"]["avg_us"],
                            "TFLOPs": flops / (g_us * 1e6), "GBps": nbytes / (g_us * 1e3),
                            "bound": "hbm" if nbytes / (HBM_PEAK_GBS * 1e3) >= flops / (FP8_PEAK_TFLOPS * 1e6) else "mfma",
                            "roofline_frac": roof_us / g_us, "copies": len(copies)})
@@ -716,7 +739,9 @@ def bench_sweep(torch, bfp8, inputs, args):
             "roofline": {"kernel": "gemm_w8a8_blk128", "bound": worst["bound"], "achieved": worst["roofline_frac"],
                          "peak": 1.0, "unit": "fraction", "frac": worst["roofline_frac"], "traffic": None,
                          "note": "worst point of the sweep"},
-            "kernels": {"points": points}, "timing": {"method": "per-kernel phases of back-to-back launches, HIP events"}}
+            "kernels": {"points": points},
+            "timing": {"method": f"GEMM: back-to-back launches for ~{args.sweep_warm_ms:.0f} ms of GPU time, then "
+                                 f"the timed ones with no gap (HIP events); quantiser: per-kernel phases"}}
 
 
 def smi_sample():

@@ -83,16 +83,6 @@ namespace {
 
 size_t round256(size_t v) { return (v + 255) / 256 * 256; }
 
-// W8A8 workspace for codes input: none for one token (K <= 4096), the
-// streaming plan's, none for the wide kernel, or the tiled kernels'
-// (one_token, w8a8_streams and w8a8_wide decide).
-size_t w8a8_workspace(int64_t M, int64_t N, int64_t K) {
-    if (one_token(M, K)) return 0;
-    if (w8a8_streams(M, N, K)) return stream_workspace_bytes(plan_stream(M, N, K));
-    if (w8a8_wide(M, N, K)) return 0;
-    return K <= kTileMaxK ? tile_workspace_bytes(M, N, K) : 0;
-}
-
 // The fused quantise + W8A8 call quantises inside the kernel when the codes
 // call would run the one-token kernel or stream (so both give the same
 // bits), M permitting.
@@ -121,6 +111,7 @@ int route(int op, int64_t M, int64_t N, int64_t K) {
             if (M > kStreamMaxM) return BFP8_KERNEL_W8A16_TILE;
             return BFP8_KERNEL_W8A16_STREAM;
         case BFP8_OP_GEMM_W8A16_BLK32_UE8M0:
+            if (one_token(M, K)) return BFP8_KERNEL_BLK32_GEMV;
             return M <= kStreamMaxM ? BFP8_KERNEL_BLK32_STREAM_LDS : BFP8_KERNEL_BLK32_STREAM;
         case BFP8_OP_QUANT_ACT_1X128:
             return BFP8_KERNEL_QUANT_ACT;
@@ -129,6 +120,31 @@ int route(int op, int64_t M, int64_t N, int64_t K) {
         default:
             return BFP8_KERNEL_NONE;
     }
+}
+
+
+// Workspace of the kernel route() picks (the launches use the same route,
+// so the size always matches what the launched kernel uses): the streaming
+// or tiled plan's split-K counters and partial tiles, none otherwise.
+size_t kernel_workspace(int kernel, int64_t M, int64_t N, int64_t K) {
+    switch (kernel) {
+        case BFP8_KERNEL_W8A8_STREAM:
+        case BFP8_KERNEL_W8A8_STREAM_QUANT:
+        case BFP8_KERNEL_W8A16_STREAM:
+        case BFP8_KERNEL_BLK32_STREAM_LDS:
+        case BFP8_KERNEL_BLK32_STREAM:
+            return stream_workspace_bytes(plan_stream(M, N, K));
+        case BFP8_KERNEL_W8A8_TILE:
+            return K <= kTileMaxK ? tile_workspace_bytes(M, N, K) : 0;
+        case BFP8_KERNEL_W8A16_TILE:
+            return K <= kTileMaxK ? tile16_workspace_bytes(M, N, K) : 0;
+        default:
+            return 0;
+    }
+}
+
+size_t w8a8_workspace(int64_t M, int64_t N, int64_t K) {
+    return kernel_workspace(route(BFP8_OP_GEMM_W8A8_BLK128, M, N, K), M, N, K);
 }
 
 // The W8A8 codes kernels by M (workspace already checked).
@@ -165,18 +181,16 @@ extern "C" {
 size_t bfp8_workspace_bytes(int op, int64_t M, int64_t N, int64_t K) {
     if (M < 1 || N < 16 || K < 128) return 0;
     switch (op) {
-        case BFP8_OP_QUANT_GEMM_W8A8_BLK128:
-            if (one_token(M, K)) return 0;
-            if (quantises_in_registers(M, N, K)) return stream_workspace_bytes(plan_stream(M, N, K));
-            return K <= kTileMaxK ? quant_gemm_parts(M, N, K).total : 0;
+        case BFP8_OP_QUANT_GEMM_W8A8_BLK128: {
+            const int kernel = route(op, M, N, K);
+            if (kernel == BFP8_KERNEL_W8A8_GEMV_QUANT || kernel == BFP8_KERNEL_W8A8_STREAM_QUANT)
+                return kernel_workspace(kernel, M, N, K);
+            return K <= kTileMaxK ? quant_gemm_parts(M, N, K).total : 0;   // codes staged by the quantiser
+        }
         case BFP8_OP_GEMM_W8A8_BLK128:
-            return w8a8_workspace(M, N, K);
         case BFP8_OP_GEMM_W8A16_BLK128:
-            if (one_token(M, K) || w8a16_wide(M, N, K)) return 0;
-            if (M > kStreamMaxM) return K <= kTileMaxK ? tile16_workspace_bytes(M, N, K) : 0;
-            return stream_workspace_bytes(plan_stream(M, N, K));
         case BFP8_OP_GEMM_W8A16_BLK32_UE8M0:
-            return stream_workspace_bytes(plan_stream(M, N, K));
+            return kernel_workspace(route(op, M, N, K), M, N, K);
         default:
             return 0;
     }
@@ -339,6 +353,8 @@ bfp8_status bfp8_gemm_w8a16_blk32_ue8m0(const void* x, int x_dtype, const uint8_
     if (st != BFP8_OK) return st;
     if (x_dtype != BFP8_F16) return BFP8_E_DTYPE;
     if ((M + 15) / 16 > 65535) return BFP8_E_SHAPE;
+    if (route(BFP8_OP_GEMM_W8A16_BLK32_UE8M0, M, N, K) == BFP8_KERNEL_BLK32_GEMV)
+        return launched(launch_w8a16_blk32_gemv(x, wq, e8m0, y, y_dtype, N, K, as_stream(stream)));
     return launched(launch_w8a16_blk32_stream(x, wq, e8m0, y, y_dtype, M, N, K, workspace, as_stream(stream)));
 }
 
@@ -431,7 +447,8 @@ bfp8_status bfp8_get_plan(int op, int64_t M, int64_t N, int64_t K, bfp8_plan* pl
         p.quant_kernel = BFP8_KERNEL_QUANT_ACT;
     switch (p.kernel) {
         case BFP8_KERNEL_W8A8_GEMV:
-        case BFP8_KERNEL_W8A16_GEMV: {
+        case BFP8_KERNEL_W8A16_GEMV:
+        case BFP8_KERNEL_BLK32_GEMV: {
             const int kr = gemv_rows_per_wave(N);
             p.tile_n = kGemvLaunchWaves * kr;
             p.tile_m = 1;
@@ -502,6 +519,7 @@ const char* bfp8_kernel_name(int kernel) {
         case BFP8_KERNEL_W8A16_TILE: return "w8a16_tile";
         case BFP8_KERNEL_BLK32_STREAM_LDS: return "blk32_stream_lds";
         case BFP8_KERNEL_BLK32_STREAM: return "blk32_stream";
+        case BFP8_KERNEL_BLK32_GEMV: return "blk32_gemv";
         default: return "unknown kernel";
     }
 }

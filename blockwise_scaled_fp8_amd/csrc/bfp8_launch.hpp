@@ -159,7 +159,13 @@ inline bool w8a16_wide(int64_t M, int64_t N, int64_t K) {
 // copies): N = K = 4096 W8A8 codes 5.02 vs 5.45, fused quantise + W8A8
 // 5.35 vs 5.82, W8A16 5.33-5.42 vs 5.69; 1024 x 4096 W8A8 3.08 vs 3.87;
 // 12288 x 4096 W8A8 9.97 vs 11.0.
-inline bool one_token(int64_t M, int64_t K) { return M == 1 && K <= 4096; }
+// The one-token kernels are built for K up to kOneTokenMaxK, but serve
+// K <= kOneTokenRouteK: above it the streaming kernels measured faster
+// (us, 32 rotated weight copies: 4096 x 12288 W8A8 11.0 streamed vs 11.3;
+// block-32 4096 x 7168 8.2 vs 8.5).
+constexpr int64_t kOneTokenMaxK = 16384;
+constexpr int64_t kOneTokenRouteK = 4096;
+inline bool one_token(int64_t M, int64_t K) { return M == 1 && K <= kOneTokenRouteK; }
 // Weight rows per wave of the one-token kernels: two only for the largest
 // projections (measured, us, one row vs two: W8A8 4096 x 4096 5.28 vs 5.53,
 // 12288 x 4096 11.2 vs 10.9; W8A16 2048 x 4096 3.81 vs 3.87, 4096 x 4096
@@ -183,6 +189,9 @@ hipError_t launch_w8a16_wide(const void* x, bool x_bf16, const uint8_t* wq, cons
 hipError_t launch_w8a16_blk128_stream(const void* x, bool x_bf16, const uint8_t* wq, const float* ws,
                                       void* y, int y_dtype, int64_t M, int64_t N, int64_t K,
                                       void* workspace, hipStream_t stream);
+// One token, block-32 weights (K <= kOneTokenMaxK, N a multiple of 32): dot products on the vector ALUs.
+hipError_t launch_w8a16_blk32_gemv(const void* x, const uint8_t* wq, const uint8_t* e8m0, void* y, int y_dtype,
+                                   int64_t N, int64_t K, hipStream_t stream);
 hipError_t launch_w8a16_blk32_stream(const void* x, const uint8_t* wq, const uint8_t* e8m0,
                                      void* y, int y_dtype, int64_t M, int64_t N, int64_t K,
                                      void* workspace, hipStream_t stream);

@@ -544,7 +544,7 @@ __device__ __forceinline__ float half_bits_to_f32(uint32_t h) {
     else return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
 }
 
-template <bool kXBf16, int kR>
+template <bool kXBf16, int kR, int kC>
 __global__ __launch_bounds__(kGemvWaves * kWave) void w8a16_gemv_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq, const float* __restrict__ ws,
     void* __restrict__ y, int y_dtype, int64_t N, int64_t K) {
@@ -559,17 +559,17 @@ __global__ __launch_bounds__(kGemvWaves * kWave) void w8a16_gemv_kernel(
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc((void*)(ws + (n0 / 128) * KB), 0, KB * 4, 0x00020000);
 
-    i32x4 xv[kGemvMaxChunks][2], wv[kGemvMaxChunks][kR];
-    float wsv[kGemvMaxChunks];
+    i32x4 xv[kC][2], wv[kC][kR];
+    float wsv[kC];
 #pragma unroll
-    for (int c = 0; c < kGemvMaxChunks; ++c) {
+    for (int c = 0; c < kC; ++c) {
         const int k = 1024 * c + 16 * lane;
         xv[c][0] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, 2 * k, 0, 0));
         xv[c][1] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, 2 * k + 16, 0, 0));
         wsv[c] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * (k / 128), 0, 0));
     }
 #pragma unroll
-    for (int c = 0; c < kGemvMaxChunks; ++c) {
+    for (int c = 0; c < kC; ++c) {
         const int k = 1024 * c + 16 * lane;
 #pragma unroll
         for (int r = 0; r < kR; ++r) {
@@ -585,7 +585,7 @@ __global__ __launch_bounds__(kGemvWaves * kWave) void w8a16_gemv_kernel(
 #pragma unroll
     for (int r = 0; r < kR; ++r) acc[r] = 0.0f;
 #pragma unroll
-    for (int c = 0; c < kGemvMaxChunks; ++c) {
+    for (int c = 0; c < kC; ++c) {
         // Chunks past K hold zeros only (every lane's loads lie past its
         // descriptor), so they add nothing and need no branch.
         float xf[16];
@@ -611,22 +611,135 @@ __global__ __launch_bounds__(kGemvWaves * kWave) void w8a16_gemv_kernel(
     }
 }
 
+// Block-32 UE8M0 weights, one token ([SM70] "How it works": a GEMV for the
+// fewest tokens): the one-token layout above with fp16 activations.  A
+// lane's 16 weights of a chunk lie in one 32-wide K tile (16 divides 32), so
+// they share one scale 2^e: the lane's 16 products of exact fp32 values
+// (E4M3 widened, fp16 widened) are summed in fp32 and multiplied once by
+// 2^e, which is exact; the lane totals are summed over the wave in one fixed
+// order.  The scale byte E (e = E - 127) of lane l in chunk c is
+// e8m0[n / 32, 32 c + l / 2].
+template <int kR, int kC>
+__global__ __launch_bounds__(kGemvWaves * kWave) void w8a16_blk32_gemv_kernel(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq, const uint8_t* __restrict__ e8m0,
+    void* __restrict__ y, int y_dtype, int64_t N, int64_t K) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
+    const int64_t n0 = ((int64_t)blockIdx.x * kGemvWaves + wave) * kR;   // wave-uniform: scalar descriptors
+    if (n0 >= N) return;
+    const int K32 = (int)(K / 32);
+    const int64_t rows = N - n0 < kR ? N - n0 : kR;
+    const int w_bytes = (int)(rows * K);
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void*)(wq + n0 * K), 0, w_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)x, 0, (int)(2 * K), 0x00020000);
+    // The kR rows lie in one 32-row scale tile (kR divides 32 and n0 is a multiple of kR).
+    const __amdgpu_buffer_rsrc_t re =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(e8m0 + (n0 / 32) * K32), 0, K32, 0x00020000);
+
+    i32x4 xv[kC][2], wv[kC][kR];
+    uint32_t eb[kC];
+#pragma unroll
+    for (int c = 0; c < kC; ++c) {
+        const int k = 1024 * c + 16 * lane;
+        xv[c][0] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, 2 * k, 0, 0));
+        xv[c][1] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, 2 * k + 16, 0, 0));
+        eb[c] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(re, k / 32, 0, 0);
+    }
+#pragma unroll
+    for (int c = 0; c < kC; ++c) {
+        const int k = 1024 * c + 16 * lane;
+#pragma unroll
+        for (int r = 0; r < kR; ++r) {
+            const int off = k < K ? (int)(r * K) + k : w_bytes;
+            wv[c][r] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, 0));
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);   // every load ahead of the arithmetic
+
+    float acc[kR];
+#pragma unroll
+    for (int r = 0; r < kR; ++r) acc[r] = 0.0f;
+#pragma unroll
+    for (int c = 0; c < kC; ++c) {
+        float xf[16];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t u = (uint32_t)xv[c][h][i];
+                xf[8 * h + 2 * i] = half_bits_to_f32<false>(u & 0xFFFFu);
+                xf[8 * h + 2 * i + 1] = half_bits_to_f32<false>(u >> 16);
+            }
+        // 2^(E - 127) as fp32 (E in [113, 134]: a normal number).  Lanes
+        // past K read E = 0 and zero weights: the factor is then 0.
+        const float scale = __builtin_bit_cast(float, eb[c] << 23);
+#pragma unroll
+        for (int r = 0; r < kR; ++r) {
+            float wf[16];
+            e4m3x16_to_f32(wv[c][r], wf);
+            float d0 = 0.0f, d1 = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 16; i += 2) {
+                d0 = __builtin_fmaf(xf[i], wf[i], d0);
+                d1 = __builtin_fmaf(xf[i + 1], wf[i + 1], d1);
+            }
+            acc[r] = __builtin_fmaf(d0 + d1, scale, acc[r]);
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < kR; ++r) {
+        const float v = wave_sum(acc[r]);
+        if (lane == 0 && r < rows) store_out(y, y_dtype, n0 + r, v);
+    }
+}
+
 hipError_t launch_w8a16_gemv(const void* x, bool x_bf16, const uint8_t* wq, const float* ws, void* y, int y_dtype,
                              int64_t N, int64_t K, hipStream_t stream) {
     if (N % 16 != 0 || K > kGemvMaxK) return hipErrorInvalidValue;
     const int kr = gemv_rows_per_wave(N);
     const dim3 grid((unsigned)((N + kGemvWaves * kr - 1) / (kGemvWaves * kr)));
     const uint16_t* xh = static_cast<const uint16_t*>(x);
-#define BFP8_LAUNCH_GEMV(B, R) \
-    hipLaunchKernelGGL((w8a16_gemv_kernel<B, R>), grid, dim3(kGemvWaves * kWave), 0, stream, xh, wq, ws, y, y_dtype, N, K)
-    if (x_bf16) {
-        if (kr == 2) BFP8_LAUNCH_GEMV(true, 2);
-        else BFP8_LAUNCH_GEMV(true, 1);
-    } else {
-        if (kr == 2) BFP8_LAUNCH_GEMV(false, 2);
-        else BFP8_LAUNCH_GEMV(false, 1);
+#define BFP8_LAUNCH_GEMV(B, R, C)                                                                              \
+    hipLaunchKernelGGL((w8a16_gemv_kernel<B, R, C>), grid, dim3(kGemvWaves * kWave), 0, stream, xh, wq, ws, y, \
+                       y_dtype, N, K)
+#define BFP8_LAUNCH_GEMV_C(B, R)                    \
+    switch (gemv_chunks(K)) {                        \
+        case 4: BFP8_LAUNCH_GEMV(B, R, 4); break;   \
+        case 8: BFP8_LAUNCH_GEMV(B, R, 8); break;   \
+        case 12: BFP8_LAUNCH_GEMV(B, R, 12); break; \
+        default: BFP8_LAUNCH_GEMV(B, R, 16); break; \
     }
+    if (x_bf16) {
+        if (kr == 2) { BFP8_LAUNCH_GEMV_C(true, 2) }
+        else { BFP8_LAUNCH_GEMV_C(true, 1) }
+    } else {
+        if (kr == 2) { BFP8_LAUNCH_GEMV_C(false, 2) }
+        else { BFP8_LAUNCH_GEMV_C(false, 1) }
+    }
+#undef BFP8_LAUNCH_GEMV_C
 #undef BFP8_LAUNCH_GEMV
+    return hipGetLastError();
+}
+
+hipError_t launch_w8a16_blk32_gemv(const void* x, const uint8_t* wq, const uint8_t* e8m0, void* y, int y_dtype,
+                                   int64_t N, int64_t K, hipStream_t stream) {
+    if (N % 32 != 0 || K > kGemvMaxK) return hipErrorInvalidValue;
+    const int kr = gemv_rows_per_wave(N);
+    const dim3 grid((unsigned)((N + kGemvWaves * kr - 1) / (kGemvWaves * kr)));
+    const uint16_t* xh = static_cast<const uint16_t*>(x);
+#define BFP8_LAUNCH_GEMV32(R, C)                                                                                    \
+    hipLaunchKernelGGL((w8a16_blk32_gemv_kernel<R, C>), grid, dim3(kGemvWaves * kWave), 0, stream, xh, wq, e8m0, y, \
+                       y_dtype, N, K)
+#define BFP8_LAUNCH_GEMV32_C(R)                    \
+    switch (gemv_chunks(K)) {                       \
+        case 4: BFP8_LAUNCH_GEMV32(R, 4); break;   \
+        case 8: BFP8_LAUNCH_GEMV32(R, 8); break;   \
+        case 12: BFP8_LAUNCH_GEMV32(R, 12); break; \
+        default: BFP8_LAUNCH_GEMV32(R, 16); break; \
+    }
+    if (kr == 2) { BFP8_LAUNCH_GEMV32_C(2) }
+    else { BFP8_LAUNCH_GEMV32_C(1) }
+#undef BFP8_LAUNCH_GEMV32_C
+#undef BFP8_LAUNCH_GEMV32
     return hipGetLastError();
 }
 
@@ -636,7 +749,7 @@ hipError_t launch_w8a16_blk128_stream(const void* x, bool x_bf16, const uint8_t*
     const StreamPlan p = plan_stream(M, N, K);
     uint32_t* counters;
     float* partials;
-    stream_workspace_parts(p, workspace, counters, partials);
+    if (!stream_workspace_parts(p, workspace, counters, partials)) return hipErrorInvalidValue;
     const dim3 grid((unsigned)p.n_tiles, (unsigned)p.splits, (unsigned)p.m_tiles);
     if (M <= kW8A16LdsMaxM) {
         const int mp = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16;
@@ -673,7 +786,7 @@ hipError_t launch_w8a16_blk32_stream(const void* x, const uint8_t* wq, const uin
     const StreamPlan p = plan_stream(M, N, K);
     uint32_t* counters;
     float* partials;
-    stream_workspace_parts(p, workspace, counters, partials);
+    if (!stream_workspace_parts(p, workspace, counters, partials)) return hipErrorInvalidValue;
     if (M <= kW8A16LdsMaxM) {
         const dim3 grid((unsigned)p.n_tiles, (unsigned)p.splits, 1u);
         const uint16_t* xh = static_cast<const uint16_t*>(x);

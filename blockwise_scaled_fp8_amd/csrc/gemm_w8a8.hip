@@ -554,25 +554,24 @@ hipError_t launch_w8a8_wide(const uint8_t* xq, const float* xs, const uint8_t* w
 }
 
 // ------------------------------------------------ W8A8 GEMV, M = 1 ----
-// One token with K <= 4096 (batch-1 decode): the dot products run on the
+// One token with K <= 16384 (batch-1 decode): the dot products run on the
 // vector ALUs, laid out as in the W8A16 one-token kernel (stream_common.hpp:
 // lane l covers K offsets 1024 c + 16 l of every 1 KB chunk c of its weight
-// rows).  Each lane widens its 16 activation codes and 16 weight codes to
-// fp32 (exact), block_dot16 gives the 128-K block's dot product to the 8
-// lanes of the block, and the block is promoted once with
-// xs[kb] * ws[n / 128, kb] ([ADA] "Scale promotion"; [ARC] "What this
-// adds").  All loads are issued before the first product; there is no LDS
-// and no barrier.  gemv_row_dot is that arithmetic for one row; the kernel
-// that quantises its own activations calls it too, so the fused call and
-// quantise-then-GEMM give the same bits.
-template <int kR>
-__device__ __forceinline__ void gemv_rows(const float (&xf)[kGemvMaxChunks][16], const float (&sx)[kGemvMaxChunks],
-                                          const i32x4 (&wv)[kGemvMaxChunks][kR], const float (&wsv)[kGemvMaxChunks],
-                                          float (&acc)[kR]) {
+// rows, kC chunks).  Each lane widens its 16 activation codes and 16 weight
+// codes to fp32 (exact), block_dot16 gives the 128-K block's dot product to
+// the 8 lanes of the block, and the block is promoted once with
+// xs[kb] * ws[n / 128, kb] ([ADA] "The fix"; [ARC] "What this adds").  All
+// loads are issued before the first product; there is no LDS and no
+// barrier.  gemv_rows is that arithmetic; the kernel that quantises its own
+// activations calls it too, so the fused call and quantise-then-GEMM give
+// the same bits.
+template <int kR, int kC>
+__device__ __forceinline__ void gemv_rows(const float (&xf)[kC][16], const float (&sx)[kC],
+                                          const i32x4 (&wv)[kC][kR], const float (&wsv)[kC], float (&acc)[kR]) {
 #pragma unroll
     for (int r = 0; r < kR; ++r) acc[r] = 0.0f;
 #pragma unroll
-    for (int c = 0; c < kGemvMaxChunks; ++c) {
+    for (int c = 0; c < kC; ++c) {
         const float sc = sx[c] * wsv[c];
 #pragma unroll
         for (int r = 0; r < kR; ++r) {
@@ -587,20 +586,19 @@ __device__ __forceinline__ void gemv_rows(const float (&xf)[kGemvMaxChunks][16],
 
 // Issue the loads of the kR weight rows from row n0 and of their weight
 // scales, chunk by chunk; lanes past K read zeros.
-template <int kR>
+template <int kR, int kC>
 __device__ __forceinline__ void gemv_load_weights(const uint8_t* wq, const float* ws, int64_t n0, int64_t rows,
-                                                  int64_t K, int lane, i32x4 (&wv)[kGemvMaxChunks][kR],
-                                                  float (&wsv)[kGemvMaxChunks]) {
+                                                  int64_t K, int lane, i32x4 (&wv)[kC][kR], float (&wsv)[kC]) {
     const int KB = (int)(K / 128);
     const int w_bytes = (int)(rows * K);
     const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void*)(wq + n0 * K), 0, w_bytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc((void*)(ws + (n0 / 128) * KB), 0, KB * 4, 0x00020000);
 #pragma unroll
-    for (int c = 0; c < kGemvMaxChunks; ++c)
+    for (int c = 0; c < kC; ++c)
         wsv[c] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * ((1024 * c + 16 * lane) / 128), 0, 0));
 #pragma unroll
-    for (int c = 0; c < kGemvMaxChunks; ++c) {
+    for (int c = 0; c < kC; ++c) {
         const int k = 1024 * c + 16 * lane;
 #pragma unroll
         for (int r = 0; r < kR; ++r) {
@@ -610,7 +608,7 @@ __device__ __forceinline__ void gemv_load_weights(const uint8_t* wq, const float
     }
 }
 
-template <int kR>
+template <int kR, int kC>
 __global__ __launch_bounds__(kGemvWaves * kWave) void w8a8_gemv_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ xs, const uint8_t* __restrict__ wq,
     const float* __restrict__ ws, void* __restrict__ y, int y_dtype, int64_t N, int64_t K) {
@@ -621,65 +619,63 @@ __global__ __launch_bounds__(kGemvWaves * kWave) void w8a8_gemv_kernel(
     const int64_t rows = N - n0 < kR ? N - n0 : kR;
     const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)xq, 0, (int)K, 0x00020000);
     const __amdgpu_buffer_rsrc_t rxs = __builtin_amdgcn_make_buffer_rsrc((void*)xs, 0, KB * 4, 0x00020000);
-    i32x4 xv[kGemvMaxChunks], wv[kGemvMaxChunks][kR];
-    float sx[kGemvMaxChunks], wsv[kGemvMaxChunks];
+    i32x4 xv[kC], wv[kC][kR];
+    float sx[kC], wsv[kC];
 #pragma unroll
-    for (int c = 0; c < kGemvMaxChunks; ++c) {
+    for (int c = 0; c < kC; ++c) {
         const int k = 1024 * c + 16 * lane;
         xv[c] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, k, 0, 0));
         sx[c] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rxs, 4 * (k / 128), 0, 0));
     }
-    gemv_load_weights<kR>(wq, ws, n0, rows, K, lane, wv, wsv);
+    gemv_load_weights<kR, kC>(wq, ws, n0, rows, K, lane, wv, wsv);
     // Keep every load ahead of the arithmetic: the scheduler would otherwise
     // sink the later chunks' loads below the first chunk's products.
     __builtin_amdgcn_sched_barrier(0);
-    float xf[kGemvMaxChunks][16];
+    float xf[kC][16];
 #pragma unroll
-    for (int c = 0; c < kGemvMaxChunks; ++c) e4m3x16_to_f32(xv[c], xf[c]);
+    for (int c = 0; c < kC; ++c) e4m3x16_to_f32(xv[c], xf[c]);
     float acc[kR];
-    gemv_rows<kR>(xf, sx, wv, wsv, acc);
+    gemv_rows<kR, kC>(xf, sx, wv, wsv, acc);
 #pragma unroll
     for (int r = 0; r < kR; ++r)
         if (lane == 0 && r < rows) store_out(y, y_dtype, n0 + r, acc[r]);
 }
 
 // The same product from 16-bit activations, quantised once per workgroup:
-// kW waves, one weight row each.  Wave w quantises activations
-// [4096 w / kW, 4096 (w + 1) / kW), V = 64 / kW consecutive values per lane,
-// so a 1x128 group spans 128 / V lanes; their maximum (lane exchanges),
-// scale amax / 448 and codes (quantize_v, the quantiser's own arithmetic)
-// equal bfp8_quantize_act_1x128's bit for bit.  Codes and scales go to LDS;
-// after one barrier every wave reads back its lanes' 16 codes per chunk and
-// runs gemv_rows.  The weight loads are issued first, so the quantisation
-// runs while they stream.
-template <bool kXBf16, int kW>
+// kW waves, one weight row each.  The token is quantised in rounds of 4096
+// values: in round t, wave w quantises activations 4096 t + 1024 w ..
+// + 1023, V = 16 consecutive values per lane, so a 1x128 group spans 8
+// lanes; their maximum (lane moves), scale amax / 448 and codes
+// (quantize_v, the quantiser's own arithmetic) equal bfp8_quantize_act_1x128's
+// bit for bit.  Codes and scales go to LDS; after one barrier every wave
+// reads back its lanes' 16 codes per chunk and runs gemv_rows.  The weight
+// loads are issued first, so the quantisation runs while they stream.
+template <bool kXBf16, int kW, int kC>
 __global__ __launch_bounds__(kW * kWave) void w8a8_gemv_quant_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq, const float* __restrict__ ws,
     void* __restrict__ y, int y_dtype, int64_t N, int64_t K) {
-    constexpr int V = 64 / kW;              // activations per lane
+    constexpr int V = 16;                   // activations per lane per round
     constexpr int kGroupLanes = 128 / V;
-    static_assert(V == 4 || V == 8 || V == 16, "values per lane");
-    __shared__ __attribute__((aligned(16))) uint8_t codes_lds[kGemvMaxK];
-    __shared__ float scale_lds[kGemvMaxK / 128];
+    constexpr int kRounds = kC / 4;         // 4096 values per round
+    static_assert(kW * V * kWave == 4096 && kC % 4 == 0, "one round covers four chunks");
+    __shared__ __attribute__((aligned(16))) uint8_t codes_lds[1024 * kC];
+    __shared__ float scale_lds[8 * kC];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
     const int64_t n0 = (int64_t)blockIdx.x * kW + wave;    // wave-uniform; < N since kW divides N
 
     // This wave's share of the activations first (values past K load as
     // zeros: their groups get scale 0 and code 0), then its weight row: loads
     // complete in issue order, so the quantisation waits only for the former.
-    const int i0 = (kGemvMaxK / kW) * wave + V * lane;
     const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)x, 0, (int)(2 * K), 0x00020000);
-    uint32_t raw[V / 2];
-    if constexpr (V == 4) {
-        const i32x2 t = __builtin_bit_cast(i32x2, __builtin_amdgcn_raw_buffer_load_b64(rx, 2 * i0, 0, 0));
-        raw[0] = (uint32_t)t[0];
-        raw[1] = (uint32_t)t[1];
-    } else {
+    uint32_t raw[kRounds][V / 2];
+#pragma unroll
+    for (int t = 0; t < kRounds; ++t) {
+        const int i0 = 4096 * t + (4096 / kW) * wave + V * lane;
 #pragma unroll
         for (int h = 0; h < V / 8; ++h) {
-            const i32x4 t = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, 2 * i0 + 16 * h, 0, 0));
+            const i32x4 u = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, 2 * i0 + 16 * h, 0, 0));
 #pragma unroll
-            for (int j = 0; j < 4; ++j) raw[4 * h + j] = (uint32_t)t[j];
+            for (int j = 0; j < 4; ++j) raw[t][4 * h + j] = (uint32_t)u[j];
         }
     }
     // Every wave's activation loads go out before any wave's weight loads
@@ -688,32 +684,36 @@ __global__ __launch_bounds__(kW * kWave) void w8a8_gemv_quant_kernel(
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    i32x4 wv[kGemvMaxChunks][1];
-    float wsv[kGemvMaxChunks];
-    gemv_load_weights<1>(wq, ws, n0, 1, K, lane, wv, wsv);
+    i32x4 wv[kC][1];
+    float wsv[kC];
+    gemv_load_weights<1, kC>(wq, ws, n0, 1, K, lane, wv, wsv);
     __builtin_amdgcn_sched_barrier(0);   // keep the weight loads ahead of the quantisation
 
-    float v[V];
 #pragma unroll
-    for (int j = 0; j < V / 2; ++j) {
-        v[2 * j] = kXBf16 ? bf16_bits_to_float(raw[j] & 0xFFFFu) : f16_bits_to_float(raw[j] & 0xFFFFu);
-        v[2 * j + 1] = kXBf16 ? bf16_bits_to_float(raw[j] >> 16) : f16_bits_to_float(raw[j] >> 16);
+    for (int t = 0; t < kRounds; ++t) {
+        const int i0 = 4096 * t + (4096 / kW) * wave + V * lane;
+        float v[V];
+#pragma unroll
+        for (int j = 0; j < V / 2; ++j) {
+            v[2 * j] = kXBf16 ? bf16_bits_to_float(raw[t][j] & 0xFFFFu) : f16_bits_to_float(raw[t][j] & 0xFFFFu);
+            v[2 * j + 1] = kXBf16 ? bf16_bits_to_float(raw[t][j] >> 16) : f16_bits_to_float(raw[t][j] >> 16);
+        }
+        float amax = 0.0f;
+#pragma unroll
+        for (int j = 0; j < V; ++j) amax = fmaxf(amax, fabsf(v[j]));
+        amax = group_max<kGroupLanes>(amax);
+        const float s = amax / 448.0f;
+        uint32_t q[V / 4];
+        quantize_v<V>(v, raw[t], s, q);
+#pragma unroll
+        for (int j = 0; j < V / 4; ++j) reinterpret_cast<uint32_t*>(codes_lds + i0)[j] = q[j];
+        if (lane % kGroupLanes == 0) scale_lds[i0 / 128] = s;
     }
-    float amax = 0.0f;
-#pragma unroll
-    for (int j = 0; j < V; ++j) amax = fmaxf(amax, fabsf(v[j]));
-    amax = group_max<kGroupLanes>(amax);
-    const float s = amax / 448.0f;
-    uint32_t q[V / 4];
-    quantize_v<V>(v, raw, s, q);
-#pragma unroll
-    for (int j = 0; j < V / 4; ++j) reinterpret_cast<uint32_t*>(codes_lds + i0)[j] = q[j];
-    if (lane % kGroupLanes == 0) scale_lds[i0 / 128] = s;
     __syncthreads();
 
-    float xf[kGemvMaxChunks][16], sx[kGemvMaxChunks];
+    float xf[kC][16], sx[kC];
 #pragma unroll
-    for (int c = 0; c < kGemvMaxChunks; ++c) {
+    for (int c = 0; c < kC; ++c) {
         const int k = 1024 * c + 16 * lane;
         e4m3x16_to_f32(*reinterpret_cast<const i32x4*>(codes_lds + k), xf[c]);
         // Lanes past K: their weights are zero; take scale 0 so that no
@@ -721,7 +721,7 @@ __global__ __launch_bounds__(kW * kWave) void w8a8_gemv_quant_kernel(
         sx[c] = k < K ? scale_lds[k / 128] : 0.0f;
     }
     float acc[1];
-    gemv_rows<1>(xf, sx, wv, wsv, acc);
+    gemv_rows<1, kC>(xf, sx, wv, wsv, acc);
     if (lane == 0) store_out(y, y_dtype, n0, acc[0]);
 }
 
@@ -731,12 +731,20 @@ hipError_t launch_w8a8_gemv(const uint8_t* xq, const float* xs, const uint8_t* w
     static_assert(kGemvWaves == kGemvLaunchWaves, "plan and launch agree");
     const int kr = gemv_rows_per_wave(N);
     const dim3 grid((unsigned)((N + kGemvWaves * kr - 1) / (kGemvWaves * kr)));
-    if (kr == 2)
-        hipLaunchKernelGGL((w8a8_gemv_kernel<2>), grid, dim3(kGemvWaves * kWave), 0, stream, xq, xs, wq, ws, y,
-                           y_dtype, N, K);
-    else
-        hipLaunchKernelGGL((w8a8_gemv_kernel<1>), grid, dim3(kGemvWaves * kWave), 0, stream, xq, xs, wq, ws, y,
-                           y_dtype, N, K);
+#define BFP8_LAUNCH_GEMV8(R, C)                                                                                    \
+    hipLaunchKernelGGL((w8a8_gemv_kernel<R, C>), grid, dim3(kGemvWaves * kWave), 0, stream, xq, xs, wq, ws, y, \
+                       y_dtype, N, K)
+#define BFP8_LAUNCH_GEMV8_C(R)                    \
+    switch (gemv_chunks(K)) {                      \
+        case 4: BFP8_LAUNCH_GEMV8(R, 4); break;   \
+        case 8: BFP8_LAUNCH_GEMV8(R, 8); break;   \
+        case 12: BFP8_LAUNCH_GEMV8(R, 12); break; \
+        default: BFP8_LAUNCH_GEMV8(R, 16); break; \
+    }
+    if (kr == 2) { BFP8_LAUNCH_GEMV8_C(2) }
+    else { BFP8_LAUNCH_GEMV8_C(1) }
+#undef BFP8_LAUNCH_GEMV8_C
+#undef BFP8_LAUNCH_GEMV8
     return hipGetLastError();
 }
 
@@ -744,12 +752,25 @@ hipError_t launch_w8a8_gemv_quant(const void* x, bool x_bf16, const uint8_t* wq,
                                   int y_dtype, int64_t N, int64_t K, hipStream_t stream) {
     if (N % 16 != 0 || K > kGemvMaxK) return hipErrorInvalidValue;   // every wave owns a row
     const uint16_t* xh = static_cast<const uint16_t*>(x);
-    // Four waves (rows) per workgroup: each wave quantises a quarter of the
-    // token, 16 values per lane, its group maximum all in lane moves (measured
-    // 5.29 vs 5.43 us for sixteen waves at N = K = 4096, even at N = 12288).
+    // Four waves (rows) per workgroup: each wave quantises a quarter of each
+    // 4096 values, 16 values per lane, its group maximum all in lane moves
+    // (measured 5.29 vs 5.43 us for sixteen waves at N = K = 4096, even at
+    // N = 12288).
     const dim3 grid((unsigned)(N / 4));
-    if (x_bf16) hipLaunchKernelGGL((w8a8_gemv_quant_kernel<true, 4>), grid, dim3(4 * kWave), 0, stream, xh, wq, ws, y, y_dtype, N, K);
-    else hipLaunchKernelGGL((w8a8_gemv_quant_kernel<false, 4>), grid, dim3(4 * kWave), 0, stream, xh, wq, ws, y, y_dtype, N, K);
+#define BFP8_LAUNCH_GEMVQ(B, C)                                                                                    \
+    hipLaunchKernelGGL((w8a8_gemv_quant_kernel<B, 4, C>), grid, dim3(4 * kWave), 0, stream, xh, wq, ws, y, y_dtype, \
+                       N, K)
+#define BFP8_LAUNCH_GEMVQ_C(B)                    \
+    switch (gemv_chunks(K)) {                      \
+        case 4: BFP8_LAUNCH_GEMVQ(B, 4); break;   \
+        case 8: BFP8_LAUNCH_GEMVQ(B, 8); break;   \
+        case 12: BFP8_LAUNCH_GEMVQ(B, 12); break; \
+        default: BFP8_LAUNCH_GEMVQ(B, 16); break; \
+    }
+    if (x_bf16) { BFP8_LAUNCH_GEMVQ_C(true) }
+    else { BFP8_LAUNCH_GEMVQ_C(false) }
+#undef BFP8_LAUNCH_GEMVQ_C
+#undef BFP8_LAUNCH_GEMVQ
     return hipGetLastError();
 }
 
@@ -760,7 +781,7 @@ hipError_t launch_w8a8_stream(const uint8_t* xq, const float* xs, const uint8_t*
     if (p.m_tiles > 65535) return hipErrorInvalidValue;
     uint32_t* counters;
     float* partials;
-    stream_workspace_parts(p, workspace, counters, partials);
+    if (!stream_workspace_parts(p, workspace, counters, partials)) return hipErrorInvalidValue;
     const dim3 grid((unsigned)p.n_tiles, (unsigned)p.splits, (unsigned)p.m_tiles);   // one 16-token tile per z
     {
 #define BFP8_LAUNCH_LDS(MP)                                                                                    \
@@ -801,7 +822,7 @@ hipError_t launch_w8a8_stream_quant(const void* x, bool x_bf16, const uint8_t* w
     const StreamPlan p = plan_stream(M, N, K);
     uint32_t* counters;
     float* partials;
-    stream_workspace_parts(p, workspace, counters, partials);
+    if (!stream_workspace_parts(p, workspace, counters, partials)) return hipErrorInvalidValue;
     const dim3 grid((unsigned)p.n_tiles, (unsigned)p.splits, 1u);
     const int mp = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8;
     if (x_bf16) {

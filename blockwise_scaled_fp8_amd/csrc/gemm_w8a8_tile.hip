@@ -105,13 +105,10 @@ struct TileCfg {
 // eight), not all eight, so the last of them is not issued just before the
 // wait at the top of the next block (3% at M = N = K = 4096, random data).
 using Cfg256 = TileCfg<256, 256, 2, 4, false, kTileCodes, 4>;    // wave tile 128 n x 64 m, 2 stages
-using Cfg128 = TileCfg<128, 128, 2, 4, false>;    // 64 x 32, 4 stages
+using Cfg128 = TileCfg<128, 128, 2, 4, true>;     // 64 x 32, 4 stages
 using Cfg256x128 = TileCfg<256, 128, 4, 2, false>;   // 64 x 64, 3 stages
 using Cfg64x128 = TileCfg<64, 128, 2, 4, true>;   // 32 x 32, 6 stages
 using Cfg128x64 = TileCfg<128, 64, 4, 2, true>;   // 32 x 32, 6 stages
-// Long K at mid M: 128 x 128 with four waves (wave tile 64 x 64, sixteen
-// MFMAs per block) and K split so that the tiles fill the CUs once.
-using Cfg128w4 = TileCfg<128, 128, 2, 2, true>;
 // W8A16 (16-bit activations): wave tiles 32 x 64 and 32 x 32 (four waves
 // across the weight rows, so each decoded weight fragment feeds kTj MFMAs).
 template <int X> using Cfg16_128 = TileCfg<128, 128, 4, 2, true, X>;   // 3 stages
@@ -589,22 +586,29 @@ __global__ __launch_bounds__(C::kThreads, 1) void w8a8_tile_kernel(
         for (int i = 0; i < C::kTi; ++i)
 #pragma unroll
             for (int j = 0; j < C::kTj; ++j) acc[i][j] = zero;
-        for (int64_t s0 = 0; s0 < splits; s0 += kChunk) {
-            i32x4 v[kChunk][kSlots];
+        // kGroup slots at a time (at most 8 x kChunk loads in flight: the
+        // partials of a whole large tile would not fit in registers), each
+        // summed over the splits in split order.
+        constexpr int kGroup = kSlots < 8 ? kSlots : 8;
+        static_assert(kSlots % kGroup == 0, "slot groups");
 #pragma unroll
-            for (int u = 0; u < kChunk; ++u) {
-                if (s0 + u >= splits) continue;
+        for (int g0 = 0; g0 < kSlots; g0 += kGroup) {
+            for (int64_t s0 = 0; s0 < splits; s0 += kChunk) {
+                i32x4 v[kChunk][kGroup];
 #pragma unroll
-                for (int slot = 0; slot < kSlots; ++slot)
-                    v[u][slot] = __builtin_amdgcn_raw_buffer_load_b128(prs, slot_off(s0 + u, slot), 0, kSc1);
-            }
+                for (int u = 0; u < kChunk; ++u) {
+                    if (s0 + u >= splits) continue;
 #pragma unroll
-            for (int u = 0; u < kChunk; ++u) {
-                if (s0 + u >= splits) continue;
+                    for (int q = 0; q < kGroup; ++q)
+                        v[u][q] = __builtin_amdgcn_raw_buffer_load_b128(prs, slot_off(s0 + u, g0 + q), 0, kSc1);
+                }
 #pragma unroll
-                for (int i = 0; i < C::kTi; ++i)
+                for (int u = 0; u < kChunk; ++u) {
+                    if (s0 + u >= splits) continue;
 #pragma unroll
-                    for (int j = 0; j < C::kTj; ++j) acc[i][j] += __builtin_bit_cast(f32x4, v[u][i * C::kTj + j]);
+                    for (int q = 0; q < kGroup; ++q)
+                        acc[(g0 + q) / C::kTj][(g0 + q) % C::kTj] += __builtin_bit_cast(f32x4, v[u][q]);
+                }
             }
         }
         store_tile();
@@ -614,7 +618,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void w8a8_tile_kernel(
 
 namespace {
 
-enum class TileShape { k256, k256x128, k128, k64x128, k128x64, k128w4, k16_256, k16_128, k16_64 };
+enum class TileShape { k256, k256x128, k128, k64x128, k128x64, k16_256, k16_128, k16_64 };
 
 struct TilePlan {
     TileShape shape;
@@ -625,8 +629,7 @@ TilePlan make_plan(TileShape s, int64_t bn, int64_t bm, int64_t M, int64_t N, in
     TilePlan p{s, bn, bm, (N + bn - 1) / bn, (M + bm - 1) / bm, 1, 0};
     const int64_t KB = K / 128;
     int64_t splits = 1;
-    if (s == TileShape::k64x128 || s == TileShape::k128x64 || s == TileShape::k128w4 || s == TileShape::k16_128 ||
-        s == TileShape::k16_64) {
+    if (s == TileShape::k16_128 || s == TileShape::k16_64) {
         // About one workgroup per CU, each with at least 4 K blocks.
         while (p.tiles_n * p.tiles_m * splits < kCUs && KB / (splits * 2) >= 4) splits *= 2;
     }
@@ -635,40 +638,69 @@ TilePlan make_plan(TileShape s, int64_t bn, int64_t bm, int64_t M, int64_t N, in
     return p;
 }
 
-// Large tiles: the shape with the least estimated time among those that
-// occupy at least three quarters of the CUs, time = rounds of kCUs tiles x
-// the time of one tile.  Relative tile times at N = K = 4096 (measured):
-// 256x256 1, 256x128 0.64, 128x128 0.4 (the larger tiles read fewer bytes
-// per MFMA from L2 and LDS).  Below that, the split-K shapes.
+// W8A8 tile plan by estimated time ([ADA] "One tile doesn't fit all M"):
+// among every shape and K split (1, 2, 4, 8 or 16, at least four 128-K
+// blocks per split), the least of
+//   rounds x blocks per split x t_block(shape) + (split ? t_split : 0),
+// rounds = ceil(workgroups / 256 CUs).  t_block is the measured time of one
+// 128-K block of one workgroup at the sustained clock (us; it is nearly the
+// same whatever the tile, most of it fixed cost per block, so larger tiles
+// pay it for more outputs): 256x256 2.03, 256x128 1.46, 128x128 0.90,
+// 64x128 and 128x64 0.77 (a four-wave 128x128 variant with 64 x 64 wave
+// tiles measured the same as the eight-wave one, within 5%).  t_split
+// is the hand-off of the partial tiles (written through to memory, summed
+// by the last workgroup of a tile): 3.4 us + 0.021 us per KB the last
+// workgroup reads (splits x the tile in fp32), fitted to measured split
+// plans (64 KB: 4.7-5.1 us, 128 KB: 6.1-6.6 us, 512 KB: 14 us).  Split
+// plans are kept to one round of workgroups and 16 MiB of partial tiles.
+// Measured against the rules this replaces (us, N x K, M): 4096 x 4096
+// M = 512 24.6 -> 21.3 (128x128 split 2), M = 256 17.4 -> 16.3 (128x64
+// split 2); 12288 x 4096 M = 64 23.9 -> 17.4 (128x64 split 2, 192
+// workgroups instead of 384), M = 128 33.4 -> 22.5 (128x128 split 2).
+namespace {
+struct ShapeCost {
+    TileShape shape;
+    int bn, bm;
+    bool split_ok;
+    double block_us;
+};
+constexpr ShapeCost kW8A8Shapes[] = {
+    {TileShape::k256, 256, 256, false, 2.03},   {TileShape::k256x128, 256, 128, false, 1.46},
+    {TileShape::k128, 128, 128, true, 0.90},
+    {TileShape::k64x128, 64, 128, true, 0.77},  {TileShape::k128x64, 128, 64, true, 0.77},
+};
+constexpr int64_t kMaxPartialBytes = (int64_t)16 << 20;
+
+TilePlan split_plan(const ShapeCost& c, int64_t M, int64_t N, int64_t K, int64_t splits) {
+    TilePlan p{c.shape, c.bn, c.bm, (N + c.bn - 1) / c.bn, (M + c.bm - 1) / c.bm, 1, 0};
+    const int64_t KB = K / 128;
+    p.kb_per_split = (KB + splits - 1) / splits;
+    p.splits = (KB + p.kb_per_split - 1) / p.kb_per_split;
+    return p;
+}
+}  // namespace
+
 TilePlan plan_tile(int64_t M, int64_t N, int64_t K) {
-    const TilePlan cand[3] = {make_plan(TileShape::k256, 256, 256, M, N, K),
-                              make_plan(TileShape::k256x128, 256, 128, M, N, K),
-                              make_plan(TileShape::k128, 128, 128, M, N, K)};
-    constexpr double kTileTime[3] = {1.0, 0.64, 0.4};
-    int best = -1;
-    double best_cost = 0.0;
-    for (int c = 0; c < 3; ++c) {
-        const int64_t tiles = cand[c].tiles_n * cand[c].tiles_m;
-        if (4 * tiles < 3 * kCUs) continue;
-        const double cost = (double)((tiles + kCUs - 1) / kCUs) * kTileTime[c];
-        if (best < 0 || cost < best_cost) {
-            best = c;
-            best_cost = cost;
+    const int64_t KB = K / 128;
+    TilePlan best{};
+    double best_cost = -1.0;
+    for (const ShapeCost& c : kW8A8Shapes) {
+        for (int64_t splits = 1; splits <= 16; splits *= 2) {
+            if (splits > 1 && (!c.split_ok || (KB + splits - 1) / splits < 4)) break;
+            const TilePlan p = split_plan(c, M, N, K, splits);
+            if (splits > 1 && p.splits != splits) break;
+            const int64_t wgs = p.tiles_n * p.tiles_m * p.splits;
+            const int64_t tile_bytes = (int64_t)c.bn * c.bm * 4;
+            if (p.splits > 1 && (wgs > kCUs || wgs * tile_bytes > kMaxPartialBytes)) continue;
+            double cost = (double)((wgs + kCUs - 1) / kCUs) * (double)p.kb_per_split * c.block_us;
+            if (p.splits > 1) cost += 3.4 + 0.021 * (double)(p.splits * tile_bytes) / 1024.0;
+            if (best_cost < 0.0 || cost < best_cost) {
+                best = p;
+                best_cost = cost;
+            }
         }
     }
-    if (best >= 0) return cand[best];
-    // Long K (at least 64 blocks) with 64 or 128 tiles of 128 x 128: four
-    // waves per tile, K split 4 or 2 ways (measured at K = 12288, N = 4096:
-    // M = 256 33.9 vs 38.9 us, M = 512 48.3 vs 63.8 us; N = 2048, M = 512
-    // 32.2 vs 37.2 us; K = 8192, M = 512 36.9 vs 43.9 us; at K = 4096 and
-    // with 32 tiles, K split 8 ways, the small tiles stay ahead).
-    {
-        const int64_t tiles = cand[2].tiles_n * cand[2].tiles_m;
-        if (M > 128 && K >= 64 * 128 && (tiles == kCUs / 4 || tiles == kCUs / 2))
-            return make_plan(TileShape::k128w4, 128, 128, M, N, K);
-    }
-    if (M <= 64) return make_plan(TileShape::k128x64, 128, 64, M, N, K);
-    return make_plan(TileShape::k64x128, 64, 128, M, N, K);
+    return best;
 }
 
 // W8A16 (16-bit activations, M > 16): 128 weight rows x 128 tokens (64
@@ -710,7 +742,6 @@ static int waves_of(TileShape s) {
         case TileShape::k128: return Cfg128::kWaves;
         case TileShape::k64x128: return Cfg64x128::kWaves;
         case TileShape::k128x64: return Cfg128x64::kWaves;
-        case TileShape::k128w4: return Cfg128w4::kWaves;
         case TileShape::k16_256: return Cfg16_256<kTileBf16>::kWaves;
         case TileShape::k16_128: return Cfg16_128<kTileBf16>::kWaves;
         default: return Cfg16_64<kTileBf16>::kWaves;
@@ -731,13 +762,17 @@ size_t tile_counter_bytes(int64_t M, int64_t N, int64_t K) {
     return p.splits > 1 ? counter_bytes(p) : 0;
 }
 
-static void split_parts(const TilePlan& p, void* workspace, uint32_t*& counters, float*& partials) {
+// Counters and partial tiles of a split plan inside the workspace; false
+// (launch nothing) when the plan splits K and no workspace was given.
+static bool split_parts(const TilePlan& p, void* workspace, uint32_t*& counters, float*& partials) {
     counters = nullptr;
     partials = nullptr;
     if (p.splits > 1) {
+        if (!workspace) return false;
         counters = static_cast<uint32_t*>(workspace);
         partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + counter_bytes(p));
     }
+    return true;
 }
 
 hipError_t launch_w8a16_tile(const void* x, bool x_bf16, const uint8_t* wq, const float* ws, void* y,
@@ -745,7 +780,7 @@ hipError_t launch_w8a16_tile(const void* x, bool x_bf16, const uint8_t* wq, cons
     const TilePlan p = plan_tile16(M, N, K);
     uint32_t* counters;
     float* partials;
-    split_parts(p, workspace, counters, partials);
+    if (!split_parts(p, workspace, counters, partials)) return hipErrorInvalidValue;
     if (p.shape == TileShape::k16_256) {
         if (x_bf16) launch<Cfg16_256<kTileBf16>>(p, x, nullptr, wq, ws, y, y_dtype, M, N, K, partials, counters, stream);
         else launch<Cfg16_256<kTileF16>>(p, x, nullptr, wq, ws, y, y_dtype, M, N, K, partials, counters, stream);
@@ -765,7 +800,7 @@ hipError_t launch_w8a8_tile(const uint8_t* xq, const float* xs, const uint8_t* w
     const TilePlan p = plan_tile(M, N, K);
     uint32_t* counters;
     float* partials;
-    split_parts(p, workspace, counters, partials);
+    if (!split_parts(p, workspace, counters, partials)) return hipErrorInvalidValue;
     switch (p.shape) {
         case TileShape::k256:
             launch<Cfg256>(p, xq, xs, wq, ws, y, y_dtype, M, N, K, partials, counters, stream);
@@ -781,9 +816,6 @@ hipError_t launch_w8a8_tile(const uint8_t* xq, const float* xs, const uint8_t* w
             break;
         case TileShape::k128x64:
             launch<Cfg128x64>(p, xq, xs, wq, ws, y, y_dtype, M, N, K, partials, counters, stream);
-            break;
-        case TileShape::k128w4:
-            launch<Cfg128w4>(p, xq, xs, wq, ws, y, y_dtype, M, N, K, partials, counters, stream);
             break;
         default:
             break;

@@ -47,21 +47,30 @@ __device__ __forceinline__ float* slab_scratch(uint8_t* slabs) { return reinterp
 inline size_t stream_counter_bytes(const StreamPlan& p) {
     return ((size_t)(p.n_tiles * p.m_tiles) * sizeof(uint32_t) + 255) / 256 * 256;
 }
-inline void stream_workspace_parts(const StreamPlan& p, void* ws, uint32_t*& counters, float*& partials) {
+// Counters and partial tiles of a split plan inside the workspace; false
+// (the caller launches nothing) when the plan splits K and no workspace was
+// given.
+inline bool stream_workspace_parts(const StreamPlan& p, void* ws, uint32_t*& counters, float*& partials) {
     counters = nullptr;
     partials = nullptr;
-    if (p.splits == 1) return;
+    if (p.splits == 1) return true;
+    if (!ws) return false;
     counters = static_cast<uint32_t*>(ws);
     partials = reinterpret_cast<float*>(static_cast<char*>(ws) + stream_counter_bytes(p));
+    return true;
 }
 
 // ------------------------------------------- one-token dot products ----
 // Shared by the W8A8 and W8A16 kernels for M = 1 (K <= kGemvMaxK): four
 // waves per workgroup, lane l of a wave covering K offsets 1024 c + 16 l of
-// each 1 KB chunk c of its weight rows.
+// each 1 KB chunk c of its weight rows.  The kernels are instantiated for
+// kC = 4, 8, 12 or 16 chunks (gemv_chunks: the fewest covering K), and issue
+// every load of all kC chunks before the first product.
 constexpr int kGemvWaves = 4;
-constexpr int kGemvMaxChunks = 4;
+constexpr int kGemvMaxChunks = 16;
 constexpr int64_t kGemvMaxK = 1024 * kGemvMaxChunks;
+static_assert(kGemvMaxK == kOneTokenMaxK, "routing and kernels agree");
+inline int gemv_chunks(int64_t K) { return K <= 4096 ? 4 : K <= 8192 ? 8 : K <= 12288 ? 12 : 16; }
 
 // The 16 E4M3 codes of v (K order) widened to fp32; exact for every finite code.
 __device__ __forceinline__ void e4m3x16_to_f32(i32x4 v, float* f) {
@@ -126,6 +135,15 @@ __device__ __forceinline__ float group_sum8(float v) {
     v += __shfl_xor(v, 16, kWave);
     v += __shfl_xor(v, 32, kWave);
     return v;
+}
+
+// Sum over all 64 lanes in one fixed order (pairs, quads, eights by lane
+// moves, then group_sum8); every lane returns the total.
+__device__ __forceinline__ float wave_sum(float v) {
+    v = add_dpp<0xB1>(v);
+    v = add_dpp<0x4E>(v);
+    v = add_dpp<0x141>(v);
+    return group_sum8(v);
 }
 
 // ------------------------------------------------------ weight slabs ----

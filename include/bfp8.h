@@ -312,7 +312,8 @@ enum {
     BFP8_KERNEL_W8A16_TILE = 12,        /* tiled MFMA kernel, weights widened in registers */
     BFP8_KERNEL_BLK32_STREAM_LDS = 13,  /* block-32, M <= 16: weights through LDS slabs */
     BFP8_KERNEL_BLK32_STREAM = 14,      /* block-32, M > 16: one 16-token tile per workgroup */
-    BFP8_KERNEL_COUNT = 15
+    BFP8_KERNEL_BLK32_GEMV = 15,        /* block-32, one token: dot products on the vector ALUs */
+    BFP8_KERNEL_COUNT = 16
 };
 
 /* A call's launch plan (filled by bfp8_get_plan). */

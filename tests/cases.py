@@ -73,12 +73,13 @@ W8A8_TILE = [
     (65, 1024, 8192, "w8a8_tile:64x128w8/split"),
     (100, 1024, 8192, "w8a8_tile:64x128w8/split"),
     (200, 4096, 2176, "w8a8_tile:64x128w8/split"),        # last split shorter
-    (300, 2064, 1024, "w8a8_tile:64x128w8/split"),        # ragged N
+    (66, 2064, 8192, "w8a8_tile:64x128w8/split"),         # ragged N and M
+    (300, 2064, 1024, "w8a8_tile:64x128w8"),              # ragged N, K not split
     (1000, 4096, 1024, "w8a8_tile:128x128w8"),
-    (400, 2048, 8192, "w8a8_tile:128x128w4/split"),       # ragged M
-    (512, 4096, 8192, "w8a8_tile:128x128w4/split"),
+    (400, 2048, 8192, "w8a8_tile:128x128w8/split"),       # ragged M
+    (512, 4096, 8192, "w8a8_tile:128x128w8/split"),
     (2000, 4000, 1024, "w8a8_tile:256x128w8"),            # ragged M and N
-    (48, 16384, 256, "w8a8_tile:128x64w8"),               # enough tiles: K not split
+    (388, 4112, 512, "w8a8_tile:128x64w8"),               # ragged M and N, K not split
 ]
 W8A8_LARGE_RAGGED = (4000, 4000, 384, "w8a8_tile:256x256w8")
 W8A8_DECODE_OPROJ = (1, 4096, 4096, "w8a8_gemv")
@@ -123,6 +124,11 @@ W8A16_DECODE_OPROJ = (1, 4096, 4096, "w8a16_gemv")
 
 # ---------------------------------------------------------------- blk32 ----
 BLK32_WORKLOAD = [(M, 4096, 7168, "blk32_stream_lds") for M in (1, 2, 3, 4, 8, 12, 16)]
+# One token with K <= 4096: the dot-product kernel on the vector ALUs (one and
+# two rows per wave, K of one block and K ending inside a 1 KB chunk).
+BLK32_ONE_TOKEN = [(1, 4096, 4096, "blk32_gemv"), (1, 32, 128, "blk32_gemv"), (1, 8192, 1152, "blk32_gemv"),
+                   (1, 1024, 3968, "blk32_gemv")]
+BLK32_ONE_HOT_ONE_TOKEN = (1, 704, 256, "blk32_gemv")
 # Above the streaming range ([SM70] "Results" times M = 32 ... 4096).
 BLK32_ABOVE_16 = [(M, 4096, 7168, "blk32_stream") for M in (17, 32, 64, 128, 512)]
 BLK32_WINDOW = (8, 512, 1024, "blk32_stream_lds")
@@ -151,8 +157,9 @@ def all_cases():
         W8A16: [W8A16_BY_M, W8A16_ONE_TOKEN, W8A16_ALL_TOKENS, W8A16_LONG_K, W8A16_SPLIT_K_STREAM, W8A16_ONE_HOT,
                 W8A16_TILE_SPLIT, [W8A16_TILE_ONE_HOT, W8A16_TILE_LARGE_RAGGED, W8A16_TILE_LARGE_ONE_HOT,
                                    W8A16_PREFILL_OPROJ, W8A16_DECODE_OPROJ]],
-        BLK32: [BLK32_WORKLOAD, BLK32_ABOVE_16, [BLK32_WINDOW, BLK32_ONE_HOT, BLK32_ONE_HOT_ABOVE_16, BLK32_SPLIT_K,
-                                                 BLK32_SPLIT_K_ABOVE_16]],
+        BLK32: [BLK32_WORKLOAD, BLK32_ONE_TOKEN, BLK32_ABOVE_16,
+                [BLK32_WINDOW, BLK32_ONE_HOT, BLK32_ONE_HOT_ABOVE_16, BLK32_ONE_HOT_ONE_TOKEN, BLK32_SPLIT_K,
+                 BLK32_SPLIT_K_ABOVE_16]],
     }
     for op, tabs in tables.items():
         for tab in tabs:

@@ -108,9 +108,9 @@ def test_workspace_sizes(lib):
     assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 32, 1024, 4096) == 0
     assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 32, 12288, 4096) == 0
     assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 64, 4096, 4096) == 0
-    # ... while 12288 x 4096 at M = 64 is tiled (128x64 tiles, K split 4 ways),
-    # and so is 4096 x 12288 (K split 8 ways)
-    assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 64, 12288, 4096) == 512 + 96 * 4 * 128 * 64 * 4
+    # ... while 12288 x 4096 at M = 64 is tiled (128x64 tiles, K split 2 ways:
+    # 192 workgroups in one round), and so is 4096 x 12288 (K split 8 ways)
+    assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 64, 12288, 4096) == 512 + 96 * 2 * 128 * 64 * 4
     assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 64, 4096, 12288) == 256 + 32 * 8 * 128 * 64 * 4
     # mid M: 64x128 tiles, K split 4 ways -> counters + 4 fp32 partial tiles per output tile
     assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 100, 4096, 8192) == 256 + 64 * 4 * 64 * 128 * 4

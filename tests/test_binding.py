@@ -46,10 +46,11 @@ def refused(fn, status, *args, **kw):
     ("y", t((M, 2 * N), BF)[:, ::2], "BFP8_E_SHAPE"),   # strided view
     ("y", None, "BFP8_E_NULL"),
 ])
-def test_w8a8_refusals(name, bad, status):
+@pytest.mark.parametrize("fn", [bfp8.bfp8_gemm_w8a8_blk128, bfp8.bfp8_gemm_w8a8_blk128_noalloc])
+def test_w8a8_refusals(name, bad, status, fn):
     a = good_w8a8()
     a[name] = bad
-    refused(bfp8.bfp8_gemm_w8a8_blk128, status, a["xq"], a["xs"], a["wq"], a["ws"], a["y"])
+    refused(fn, status, a["xq"], a["xs"], a["wq"], a["ws"], a["y"])
 
 
 def test_w8a8_host_tensors_refused():
@@ -129,7 +130,8 @@ def test_every_entry_point_with_tensor_arguments_checks_them():
     """Each C function that takes buffers is reached only through a binding
     function that refuses bad tensors (the refusal tests above cover them)."""
     covered = {"bfp8_quantize_act_1x128", "bfp8_quantize_weight_128x128", "bfp8_dequantize_weight",
-               "bfp8_gemm_w8a8_blk128", "bfp8_quant_gemm_w8a8_blk128", "bfp8_gemm_w8a16_blk128",
+               "bfp8_gemm_w8a8_blk128", "bfp8_gemm_w8a8_blk128_noalloc", "bfp8_quant_gemm_w8a8_blk128",
+               "bfp8_gemm_w8a16_blk128",
                "bfp8_gemm_w8a16_blk32_ue8m0", "bfp8_prepare_blk32_ue8m0"}
     pointer_args = {n for n, (_, args) in _lib.SIGNATURES.items() if args.count(_lib._P) >= 2}
     assert pointer_args <= covered, pointer_args - covered

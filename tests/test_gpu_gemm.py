@@ -447,6 +447,22 @@ def test_blk32_block32_workload_shape(gpu_lib, M, N, K, kernel):
     assert ok, e
 
 
+@pytest.mark.parametrize("M,N,K,kernel", cases.BLK32_ONE_TOKEN)
+def test_blk32_one_token(gpu_lib, M, N, K, kernel):
+    """One token with K <= 4096: the vector-ALU kernel (two rows per wave at
+    N = 8192), e uniform on [-14, 7]; fp32 output against the oracle, fp16
+    output as RNE of the fp32 result."""
+    say("blk32 one token", N, K)
+    expect(BLK32, M, N, K, kernel)
+    x, wq, e8 = _blk32_inputs(M, N, K, 60 + K // 128)
+    y0 = oracle.gemm_w8a16_blk32_ue8m0(f32(x), wq, e8)
+    xd, wqd, e8d = x.cuda(), dev(wq), dev(e8)
+    y32 = run_blk32(xd, wqd, e8d, torch.float32)
+    assert_fp32_bar(y32, y0, f"blk32 one token N={N} K={K}")
+    yh = run_blk32(xd, wqd, e8d, torch.float16)
+    assert_16bit_bar(yh, y32, y0, "f16", f"blk32 one token N={N} K={K}")
+
+
 @pytest.mark.parametrize("lo,hi", [(-14, -14), (7, 7)])
 def test_blk32_window_ends(gpu_lib, lo, hi):
     say("blk32 window end", lo)
@@ -458,13 +474,15 @@ def test_blk32_window_ends(gpu_lib, lo, hi):
     assert_fp32_bar(y32, y0, f"blk32 e={lo}")
 
 
-@pytest.mark.parametrize("case", [cases.BLK32_ONE_HOT, cases.BLK32_ONE_HOT_ABOVE_16], ids=lambda c: c[3])
+@pytest.mark.parametrize("case", [cases.BLK32_ONE_HOT, cases.BLK32_ONE_HOT_ABOVE_16, cases.BLK32_ONE_HOT_ONE_TOKEN],
+                         ids=lambda c: c[3])
 @pytest.mark.parametrize("out", [torch.float32, torch.float16])
 def test_blk32_one_hot_all_codes_all_exponents_exact(gpu_lib, out, case):
     """Every finite code times every window exponent is produced exactly
-    (fp16 subnormals at e = -14 included), by the streaming kernel of M <= 16
-    and by the one for M > 16 (M = 17: a full token tile and a second one
-    with a single live row)."""
+    (fp16 subnormals at e = -14 included), by the streaming kernel of M <= 16,
+    by the one for M > 16 (M = 17: a full token tile and a second one with a
+    single live row) and by the one-token kernel (M = 1: one column k per
+    call)."""
     exps = np.arange(-14, 8)
     M, N, K, kernel = case
     assert N == 32 * exps.size

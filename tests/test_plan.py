@@ -48,7 +48,7 @@ def test_every_reachable_kernel_variant_has_a_parity_case():
     assert any("/split" in c[4] for c in staged) and any("/split" not in c[4] for c in staged)
     # and the sweep reaches every kernel id the router knows of
     ids = {bfp8.bfp8_get_plan(op, M, N, K)["kernel"] for op, M, N, K in _sweep()}
-    assert ids == set(range(3, 15)), sorted(ids)
+    assert ids == set(range(3, 16)), sorted(ids)
 
 
 def test_plan_agrees_with_workspace_bytes_and_grid():
@@ -73,7 +73,8 @@ def test_routing_rules_read_off_the_plan():
         if op == cases.W8A16 and M <= 16 and not (M == 1 and K <= 4096):
             assert name == "w8a16_stream"
         if op == cases.BLK32:
-            assert name == ("blk32_stream_lds" if M <= 16 else "blk32_stream")
+            want = "blk32_gemv" if M == 1 and K <= 4096 else "blk32_stream_lds" if M <= 16 else "blk32_stream"
+            assert name == want, (M, N, K, name)
         if op == cases.QW8A8 and name.endswith("_quant"):
             assert M == 1 or M <= 8
 
@@ -101,6 +102,6 @@ def test_quantiser_plans():
 
 
 def test_kernel_names():
-    names = [bfp8.bfp8_kernel_name(k) for k in range(15)]
-    assert len(set(names)) == 15 and "unknown kernel" not in names
+    names = [bfp8.bfp8_kernel_name(k) for k in range(16)]
+    assert len(set(names)) == 16 and "unknown kernel" not in names
     assert bfp8.bfp8_kernel_name(99) == "unknown kernel"
