@@ -4,22 +4,20 @@
 // There is no MFMA that multiplies a 16-bit operand by an FP8 operand, so
 // with 16-bit activations the weights are widened to the activations' type
 // and the bf16/fp16 MFMA runs ([3090] §2: mixed operand types do not exist
-// in one matrix instruction).  The widening is exact and costs a few integer
-// operations per weight ([3090] §4.1; [SM70] "How it works"); at decode
-// sizes the kernels are bound by streaming the weights from HBM, and the
-// integer work hides under the loads ([3090] §4.3).
+// in one matrix instruction).  The widening is exact and takes one gfx950
+// conversion instruction per two weights (widen8); at decode sizes the
+// kernels are bound by streaming the weights from HBM, and the widening
+// hides under the loads ([3090] §4.3).
 //
-// blk128: weights with one fp32 scale per 128x128 tile.  The weights are
-// decoded to bf16 (value * 2^-120) or fp16 (value * 2^-8); the bias
-// difference is folded into the block scale, so the per-block promotion is
-// one FMA per output: acc += P * (ws * 2^120) or (ws * 2^8) ([3090] §4.1;
-// [ARC] "What this adds").
+// blk128: weights with one fp32 scale per 128x128 tile, widened to their
+// exact bf16 or fp16 values, so the per-block promotion is one FMA per
+// output: acc += P * ws ([ARC] "What this adds").
 //
 // blk32 (UE8M0): weights with one power-of-two scale 2^e per 32x32 tile.
-// Each decoded fp16 weight (value * 2^-8) is multiplied by 2^(e+8) with a
-// packed fp16 multiply; the product value * 2^e is an exact fp16 number for
-// e in [-14, 7] ([SM70] "Exactness"), so the MFMA sees exactly the weights
-// of a load-time fp16 dequantisation and accumulates in fp32 across all K.
+// The conversion applies 2^e itself: each weight becomes the fp16 number
+// value * 2^e, exact for e in [-14, 7] ([SM70] "Exactness"), so the MFMA
+// sees exactly the weights of a load-time fp16 dequantisation and
+// accumulates in fp32 across all K.
 //
 // M = 1 with K <= 4096 runs a plain dot-product kernel on the vector ALUs
 // (w8a16_gemv_kernel below).  The other kernels here stream the weights like
@@ -42,13 +40,10 @@
 
 namespace bfp8 {
 
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-
-// Two fp16 values (one dword) times a packed fp16 factor: one v_pk_mul_f16.
-__device__ __forceinline__ uint32_t scale_f16x2(uint32_t v, f16x2 factor) {
-    const f16x2 p = __builtin_bit_cast(f16x2, v) * factor;
-    return __builtin_bit_cast(uint32_t, p);
-}
+// The UE8M0 byte E of a 32x32 weight tile as the fp32 scale 2^(E - 127)
+// (the byte is an fp32 exponent field; prepared weights have E in
+// [113, 134]).
+__device__ __forceinline__ float ue8m0_scale(uint32_t E) { return __builtin_bit_cast(float, E << 23); }
 
 constexpr int kW8A16Chunk = 4;   // 128-K blocks per wave with loads in flight together
 
@@ -105,21 +100,14 @@ __global__ __launch_bounds__(kStreamThreads) void w8a16_blk32_stream_kernel(
         for (int c = 0; c < kW8A16Chunk; ++c) {
             const int64_t kb = kb0 + c * kStreamWaves;
             if (kb < kb_end) {
-                // 2^(E - 127 + 8) as fp16: exponent field (E - 119) + 15 = E - 104, in [9, 30]
-                // for E in [113, 134]; both halves of the packed factor.
-                const uint32_t f0 = (ebyte[c][0] - 104u) << 10, f1 = (ebyte[c][1] - 104u) << 10;
-                const f16x2 factor0 = __builtin_bit_cast(f16x2, f0 | (f0 << 16));
-                const f16x2 factor1 = __builtin_bit_cast(f16x2, f1 | (f1 << 16));
+                // MFMAs 0, 1 take K offsets below 64 (the first 32x32 tile of the
+                // block for this lane's slot), MFMAs 2, 3 the second.
+                const float e0 = ue8m0_scale(ebyte[c][0]), e1 = ue8m0_scale(ebyte[c][1]);
                 const uint32_t q[8] = {wa[c][0][0], wa[c][0][1], wa[c][0][2], wa[c][0][3],
                                        wa[c][1][0], wa[c][1][1], wa[c][1][2], wa[c][1][3]};
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    uint32_t d0, d1, d2, d3;
-                    e4m3x4_to_f16x4(q[2 * j], d0, d1);
-                    e4m3x4_to_f16x4(q[2 * j + 1], d2, d3);
-                    const f16x2 factor = j < 2 ? factor0 : factor1;
-                    const u32x4 a = {scale_f16x2(d0, factor), scale_f16x2(d1, factor),
-                                     scale_f16x2(d2, factor), scale_f16x2(d3, factor)};
+                    const u32x4 a = widen8<false>(q[2 * j], q[2 * j + 1], j < 2 ? e0 : e1);
                     acc = mfma_f16_16x16x32(a, m_ok ? xb[c][j] : u32x4{0u, 0u, 0u, 0u}, acc);
                 }
             }
@@ -169,7 +157,6 @@ __global__ __launch_bounds__(kStreamThreads) void w8a16_blk128_stream_lds_kernel
     const i32x4 rsrc_x = buffer_rsrc(x, (uint32_t)(M * K * 2));
     const int lane_off_w = slab_lane_offset(lane, K);
     const float* ws_row = ws + (nt * 16 / 128) * KB;
-    const float bias_fold = kXBf16 ? 0x1p120f : 0x1p8f;
 
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
     const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -222,10 +209,10 @@ __global__ __launch_bounds__(kStreamThreads) void w8a16_blk128_stream_lds_kernel
                 f32x4 blk = zero;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const u32x4 a = decode8<kXBf16>(q[2 * j], q[2 * j + 1]);
+                    const u32x4 a = widen8<kXBf16>(q[2 * j], q[2 * j + 1]);
                     blk = kXBf16 ? mfma_bf16_16x16x32(a, xv[j], blk) : mfma_f16_16x16x32(a, xv[j], blk);
                 }
-                const float sc = wsv[c] * bias_fold;
+                const float sc = wsv[c];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(blk[i], sc, acc[i]);
             }
@@ -307,22 +294,14 @@ __global__ __launch_bounds__(kStreamThreads) void w8a16_blk32_stream_lds_kernel(
                 slab_read(wslab[wave][c], r, g, wa0, wa1);
                 const uint32_t q[8] = {wa0[0], wa0[1], wa0[2], wa0[3], wa1[0], wa1[1], wa1[2], wa1[3]};
                 const uint8_t* row = xrows[wave][c] + r_row * kXRowStride + 32 * g;
-                // 2^(E - 127 + 8) as fp16: exponent field E - 104 (as in w8a16_blk32_stream_kernel).
-                const uint32_t f0 = (ebyte[c][0] - 104u) << 10, f1 = (ebyte[c][1] - 104u) << 10;
-                const f16x2 factor0 = __builtin_bit_cast(f16x2, f0 | (f0 << 16));
-                const f16x2 factor1 = __builtin_bit_cast(f16x2, f1 | (f1 << 16));
+                const float e0 = ue8m0_scale(ebyte[c][0]), e1 = ue8m0_scale(ebyte[c][1]);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     u32x4 xv;
                     if constexpr (kRegX) xv = xr[c][j];
                     else xv = *reinterpret_cast<const u32x4*>(row + (j < 2 ? 16 * j : 128 + 16 * (j - 2)));
                     xv = r_ok ? xv : z4;
-                    uint32_t d0, d1, d2, d3;
-                    e4m3x4_to_f16x4(q[2 * j], d0, d1);
-                    e4m3x4_to_f16x4(q[2 * j + 1], d2, d3);
-                    const f16x2 factor = j < 2 ? factor0 : factor1;
-                    const u32x4 a = {scale_f16x2(d0, factor), scale_f16x2(d1, factor),
-                                     scale_f16x2(d2, factor), scale_f16x2(d3, factor)};
+                    const u32x4 a = widen8<false>(q[2 * j], q[2 * j + 1], j < 2 ? e0 : e1);
                     acc = mfma_f16_16x16x32(a, xv, acc);
                 }
             }
@@ -345,10 +324,9 @@ __global__ __launch_bounds__(kStreamThreads) void w8a16_blk32_stream_lds_kernel(
 // of whole lines.  Token row R of a tile keeps its 16-byte chunk c at
 // position c ^ sw(R), sw(R) = ((R & 3) << 2) | (R >> 2), so the 16 rows of
 // one MFMA read hit 16 distinct bank groups.  The weights are widened in
-// registers (decode8) and feed four 16x16x32 MFMAs per block and row tile;
-// the exponent-bias difference is folded into the block scale, as in the
-// streaming kernel.  The waves' partial sums meet in LDS once, at the end,
-// and are added in K-lane order.
+// registers (widen8) and feed four 16x16x32 MFMAs per block and row tile,
+// promoted with the block scale as in the streaming kernel.  The waves'
+// partial sums meet in LDS once, at the end, and are added in K-lane order.
 constexpr int kW16WideWaves = 8;
 static_assert(kW16WideWaves == kWideLaunchWaves, "plan and launch agree");
 constexpr int kW16WideThreads = kW16WideWaves * kWave;
@@ -403,7 +381,6 @@ __global__ __launch_bounds__(kW16WideThreads, 1) void w8a16_wide_kernel(
         x_off[q] = (int)(row * K * 2) + (((lane & 15) ^ w16_sw(row)) << 4);
     }
     uint8_t* my_ring = ring + wave * kW16WideSlots * kW16Slot;
-    const float bias_fold = kXBf16 ? 0x1p120f : 0x1p8f;
 
     auto issue = [&](int slot, int kb) {
         const uint32_t base = __builtin_amdgcn_readfirstlane(lds_address(my_ring + slot * kW16Slot));
@@ -449,7 +426,7 @@ __global__ __launch_bounds__(kW16WideThreads, 1) void w8a16_wide_kernel(
         const float wsv = *reinterpret_cast<const float*>(sl + kW16OffWs);
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         if (j + kW16WideSlots < nj) issue(slot, kw + KW * (j + kW16WideSlots));
-        const float sc = wsv * bias_fold;
+        const float sc = wsv;
 #pragma unroll
         for (int rt = 0; rt < kR; ++rt) {
             const uint32_t q8[8] = {wa0[rt][0], wa0[rt][1], wa0[rt][2], wa0[rt][3],
@@ -457,7 +434,7 @@ __global__ __launch_bounds__(kW16WideThreads, 1) void w8a16_wide_kernel(
             f32x4 blk = zero;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const u32x4 a = decode8<kXBf16>(q8[2 * i], q8[2 * i + 1]);
+                const u32x4 a = widen8<kXBf16>(q8[2 * i], q8[2 * i + 1]);
                 blk = kXBf16 ? mfma_bf16_16x16x32(a, xv[i], blk) : mfma_f16_16x16x32(a, xv[i], blk);
             }
 #pragma unroll
@@ -671,7 +648,7 @@ __global__ __launch_bounds__(kGemvWaves * kWave) void w8a16_blk32_gemv_kernel(
             }
         // 2^(E - 127) as fp32 (E in [113, 134]: a normal number).  Lanes
         // past K read E = 0 and zero weights: the factor is then 0.
-        const float scale = __builtin_bit_cast(float, eb[c] << 23);
+        const float scale = ue8m0_scale(eb[c]);
 #pragma unroll
         for (int r = 0; r < kR; ++r) {
             float wf[16];

@@ -352,15 +352,14 @@ __global__ __launch_bounds__(C::kThreads, 1) void w8a8_tile_kernel(
         // The kTi weight rows of the block are widened once (aop), then each
         // token tile column j is read (one ahead) and multiplied by every row;
         // the promotion of column j - 1 follows the MFMAs of column j.
-        constexpr float kBiasFold = C::X == kTileBf16 ? 0x1p120f : 0x1p8f;
-        const float wsc = reinterpret_cast<const float*>(stage + C::kOffWs)[wave] * kBiasFold;
+        const float wsc = reinterpret_cast<const float*>(stage + C::kOffWs)[wave];
         u32x4 aop[C::kTi][4];
 #pragma unroll
         for (int i = 0; i < C::kTi; ++i) {
             const i32x8 af = read_frag<true>(stage, a_base + a_row(i, r), g);
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj)
-                aop[i][jj] = decode8<C::X == kTileBf16>((uint32_t)af[2 * jj], (uint32_t)af[2 * jj + 1]);
+                aop[i][jj] = widen8<C::X == kTileBf16>((uint32_t)af[2 * jj], (uint32_t)af[2 * jj + 1]);
         }
         auto read_b = [&](int j, u32x4 (&b)[4]) {
             const int row = C::kWaveM * wm + 16 * j + r;
@@ -407,13 +406,11 @@ __global__ __launch_bounds__(C::kThreads, 1) void w8a8_tile_kernel(
                 acc[i][C::kTj - 1][e] = __builtin_fmaf(tmp[(C::kTj - 1) & 1][i][e], wsc, acc[i][C::kTj - 1][e]);
       } else if constexpr (C::kX16) {
         // W8A16: per 16x16 tile and block, four 16x16x32 MFMAs on weights
-        // widened in registers (decode8: the E4M3 bias difference, 2^120 for
-        // bf16 and 2^8 for fp16, is folded into the block scale).  MFMA jj
+        // widened in registers to their exact 16-bit values (widen8).  MFMA jj
         // of lane (r, g) takes K positions 16(g + 4(jj/2)) + 8(jj%2) .. +7:
         // weight bytes from chunks g and g + 4 of the fp8 row, and the
         // 16-bit token chunks 2g, 2g+1, 2g+8, 2g+9 of the 256-byte row.
-        constexpr float kBiasFold = C::X == kTileBf16 ? 0x1p120f : 0x1p8f;
-        const float wsc = reinterpret_cast<const float*>(stage + C::kOffWs)[wave] * kBiasFold;
+        const float wsc = reinterpret_cast<const float*>(stage + C::kOffWs)[wave];
         u32x4 bfr[C::kTj][4];
 #pragma unroll
         for (int j = 0; j < C::kTj; ++j) {
@@ -428,10 +425,10 @@ __global__ __launch_bounds__(C::kThreads, 1) void w8a8_tile_kernel(
 #pragma unroll
         for (int i = 0; i < C::kTi; ++i) {
             const int c = i & 1;
-            const u32x4 aop[4] = {decode8<C::X == kTileBf16>((uint32_t)af[0], (uint32_t)af[1]),
-                                  decode8<C::X == kTileBf16>((uint32_t)af[2], (uint32_t)af[3]),
-                                  decode8<C::X == kTileBf16>((uint32_t)af[4], (uint32_t)af[5]),
-                                  decode8<C::X == kTileBf16>((uint32_t)af[6], (uint32_t)af[7])};
+            const u32x4 aop[4] = {widen8<C::X == kTileBf16>((uint32_t)af[0], (uint32_t)af[1]),
+                                  widen8<C::X == kTileBf16>((uint32_t)af[2], (uint32_t)af[3]),
+                                  widen8<C::X == kTileBf16>((uint32_t)af[4], (uint32_t)af[5]),
+                                  widen8<C::X == kTileBf16>((uint32_t)af[6], (uint32_t)af[7])};
             if (i + 1 < C::kTi) af = read_frag<true>(stage, a_base + a_row(i + 1, r), g);
 #pragma unroll
             for (int j = 0; j < C::kTj; ++j) {
