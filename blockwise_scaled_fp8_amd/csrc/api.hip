@@ -106,7 +106,7 @@ int route(int op, int64_t M, int64_t N, int64_t K) {
             if (w8a8_wide(M, N, K)) return BFP8_KERNEL_W8A8_WIDE;
             return BFP8_KERNEL_W8A8_TILE;
         case BFP8_OP_GEMM_W8A16_BLK128:
-            if (one_token(M, K)) return BFP8_KERNEL_W8A16_GEMV;
+            if (one_token_w8a16(M, K)) return BFP8_KERNEL_W8A16_GEMV;
             if (w8a16_wide(M, N, K)) return BFP8_KERNEL_W8A16_WIDE;
             if (M > kStreamMaxM) return BFP8_KERNEL_W8A16_TILE;
             return BFP8_KERNEL_W8A16_STREAM;
@@ -449,18 +449,18 @@ bfp8_status bfp8_get_plan(int op, int64_t M, int64_t N, int64_t K, bfp8_plan* pl
         case BFP8_KERNEL_W8A8_GEMV:
         case BFP8_KERNEL_W8A16_GEMV:
         case BFP8_KERNEL_BLK32_GEMV: {
-            const int kr = gemv_rows_per_wave(N);
+            const int kr = gemv_rows_per_wave(N, K);
             p.tile_n = kGemvLaunchWaves * kr;
             p.tile_m = 1;
             p.waves = kGemvLaunchWaves;
             p.workgroups = (N + p.tile_n - 1) / p.tile_n;
             break;
         }
-        case BFP8_KERNEL_W8A8_GEMV_QUANT:
-            p.tile_n = 4;
+        case BFP8_KERNEL_W8A8_GEMV_QUANT:   // one weight row per wave
+            p.tile_n = kGemvLaunchWaves;
             p.tile_m = 1;
-            p.waves = 4;
-            p.workgroups = N / 4;
+            p.waves = kGemvLaunchWaves;
+            p.workgroups = N / kGemvLaunchWaves;
             break;
         case BFP8_KERNEL_W8A8_STREAM:
         case BFP8_KERNEL_W8A8_STREAM_QUANT:

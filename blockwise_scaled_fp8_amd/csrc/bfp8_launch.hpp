@@ -152,26 +152,33 @@ inline bool w8a16_wide(int64_t M, int64_t N, int64_t K) {
     return M > kStreamMaxM && M <= 16 * kStreamMaxM && K <= 4096 &&
            (M <= 2 * kStreamMaxM || M * N <= ((int64_t)1 << 19));
 }
-// One token with K <= 4096 (W8A8 codes, W8A8 with activations quantised in
-// the kernel, W8A16 blk128): dot-product kernels on the vector ALUs, no
-// workspace (launch_w8a8_gemv, launch_w8a8_gemv_quant, launch_w8a16_gemv).
-// Measured against the streaming MFMA kernels (us, 32 rotated weight
-// copies): N = K = 4096 W8A8 codes 5.02 vs 5.45, fused quantise + W8A8
-// 5.35 vs 5.82, W8A16 5.33-5.42 vs 5.69; 1024 x 4096 W8A8 3.08 vs 3.87;
-// 12288 x 4096 W8A8 9.97 vs 11.0.
-// The one-token kernels are built for K up to kOneTokenMaxK, but serve
-// K <= kOneTokenRouteK: above it the streaming kernels measured faster
-// (us, 32 rotated weight copies: 4096 x 12288 W8A8 11.0 streamed vs 11.3;
-// block-32 4096 x 7168 8.2 vs 8.5).
+// One token (W8A8 codes, W8A8 with activations quantised in the kernel,
+// W8A16 blk128, block-32): dot-product kernels on the vector ALUs, no
+// workspace (launch_w8a8_gemv, launch_w8a8_gemv_quant, launch_w8a16_gemv,
+// launch_w8a16_blk32_gemv).  They are built for K up to kOneTokenMaxK and
+// serve the K where they measured faster than the streaming MFMA kernels
+// (us, at least 512 MB of rotated weight copies, after a clock ramp):
+//   N = K = 4096: W8A8 codes 5.14, fused 4.96, W8A16 5.01 (streaming
+//     kernels 5.45, 5.82, 5.69 when last compared);
+//   4096 x 7168: W8A8 codes 7.10 vs 7.68, W8A16 7.11 vs 7.70, block-32
+//     6.89 vs 7.65, fused 7.81 vs 7.66;
+//   4096 x 12288: W8A16 10.67 vs 10.92, but W8A8 codes 12.19 vs 10.82 and
+//     fused 14.17 vs 11.03.
+// So W8A8 and block-32 take them up to K = 8192, W8A16 up to 12288.  The
+// fused call keeps the codes call's range despite its 2 % loss at 7168: the
+// two must run the same kernel to give the same bits.
 constexpr int64_t kOneTokenMaxK = 16384;
-constexpr int64_t kOneTokenRouteK = 4096;
+constexpr int64_t kOneTokenRouteK = 8192;      // W8A8 (codes and fused), block-32
+constexpr int64_t kOneTokenRouteK16 = 12288;   // W8A16 blk128
 inline bool one_token(int64_t M, int64_t K) { return M == 1 && K <= kOneTokenRouteK; }
+inline bool one_token_w8a16(int64_t M, int64_t K) { return M == 1 && K <= kOneTokenRouteK16; }
 // Weight rows per wave of the one-token kernels: two only for the largest
 // projections (measured, us, one row vs two: W8A8 4096 x 4096 5.28 vs 5.53,
 // 12288 x 4096 11.2 vs 10.9; W8A16 2048 x 4096 3.81 vs 3.87, 4096 x 4096
-// 5.34 vs 5.35, 12288 x 4096 11.3 vs 11.1).
-inline int gemv_rows_per_wave(int64_t N) { return N >= 8192 ? 2 : 1; }
-constexpr int kGemvLaunchWaves = 4;    // waves per workgroup of the one-token kernels
+// 5.34 vs 5.35, 12288 x 4096 11.3 vs 11.1), and only up to K = 8192: two
+// rows of 12 or 16 chunks hold more loads in flight than registers.
+inline int gemv_rows_per_wave(int64_t N, int64_t K) { return N >= 8192 && K <= 8192 ? 2 : 1; }
+constexpr int kGemvLaunchWaves = 8;    // waves per workgroup of the one-token kernels
 constexpr int kStreamLaunchWaves = 16;  // waves per workgroup of the streaming kernels
 constexpr int kWideLaunchWaves = 8;     // waves per workgroup of the all-token kernels
 constexpr int kQuantLaunchWaves = 4;    // waves per workgroup of the quantisers

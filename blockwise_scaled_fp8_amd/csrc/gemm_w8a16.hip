@@ -501,8 +501,9 @@ hipError_t launch_w8a16_wide(const void* x, bool x_bf16, const uint8_t* wq, cons
 // is one dot product per weight row.  A wave owns kR weight rows.  Lane l
 // takes, in each 1 KB chunk c of a row, the 16 weight bytes at K offset
 // 1024 c + 16 l (one load instruction covers 8 whole 128-byte lines) and the
-// 16 matching activations, widens the E4M3 weights to fp32
-// (v_cvt_pk_f32_fp8, exact) and sums the 16 products in fp32.  Lanes 8 j ..
+// 16 matching activations, widens the E4M3 weights to the activations'
+// 16-bit type (exact) and sums the 16 products with v_dot2c (lane_dot16).
+// Lanes 8 j ..
 // 8 j + 7 hold 128-K block 8 c + j: three lane exchanges give every one of
 // them the block's dot product, which is promoted once with the block's
 // weight scale (the per-block promotion of [ARC] "What this adds", here
@@ -513,38 +514,39 @@ hipError_t launch_w8a16_wide(const void* x, bool x_bf16, const uint8_t* wq, cons
 // kernel, about half a microsecond of a 5.7 us launch at N = K = 4096, is
 // gone (measured 5.33-5.42 vs 5.69 us there, 3.00 vs 3.96 us at N = 1024
 // and 11.1 vs 11.5 us at N = 12288).  The lane sums use DPP lane moves
-// (block_dot16, group_sum8).  Lanes past K read zeros (their offsets are
+// (block_sum8, group_sum8).  Lanes past K read zeros (their offsets are
 // moved past the descriptor's range).
-template <bool kXBf16>
-__device__ __forceinline__ float half_bits_to_f32(uint32_t h) {
-    if constexpr (kXBf16) return __builtin_bit_cast(float, h << 16);
-    else return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+
+// A lane's 16 activations of a chunk (two 16-byte loads) as 8 pairs.
+__device__ __forceinline__ const uint32_t (&pairs(const i32x4 (&x)[2]))[8] {
+    return *reinterpret_cast<const uint32_t(*)[8]>(&x[0]);
 }
 
 template <bool kXBf16, int kR, int kC>
-__global__ __launch_bounds__(kGemvWaves * kWave) void w8a16_gemv_kernel(
+__global__ __launch_bounds__(kGemvThreads) void w8a16_gemv_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq, const float* __restrict__ ws,
     void* __restrict__ y, int y_dtype, int64_t N, int64_t K) {
+    constexpr int kU = kC / 4;   // 8 KB rounds of the 16-bit token (2 KB per chunk)
+    __shared__ __attribute__((aligned(16))) uint8_t x_lds[2048 * kC];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
     const int64_t n0 = ((int64_t)blockIdx.x * kGemvWaves + wave) * kR;   // wave-uniform: scalar descriptors
-    if (n0 >= N) return;
+    // The launch covers N exactly (N % 16 == 0); a wave past N would still
+    // take part in the token copy and the barrier, with empty descriptors.
+    const int64_t rows = n0 >= N ? 0 : N - n0 < kR ? N - n0 : kR;
+    const int64_t nb = rows > 0 ? n0 : 0;
     const int KB = (int)(K / 128);
-    const int64_t rows = N - n0 < kR ? N - n0 : kR;
     const int w_bytes = (int)(rows * K);
-    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void*)(wq + n0 * K), 0, w_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void*)(wq + nb * K), 0, w_bytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)x, 0, (int)(2 * K), 0x00020000);
     const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(ws + (n0 / 128) * KB), 0, KB * 4, 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc((void*)(ws + (nb / 128) * KB), 0, rows > 0 ? KB * 4 : 0, 0x00020000);
 
-    i32x4 xv[kC][2], wv[kC][kR];
+    i32x4 xr[kU], wv[kC][kR];
     float wsv[kC];
+    gemv_x_issue<kU>(rx, xr);
 #pragma unroll
-    for (int c = 0; c < kC; ++c) {
-        const int k = 1024 * c + 16 * lane;
-        xv[c][0] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, 2 * k, 0, 0));
-        xv[c][1] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, 2 * k + 16, 0, 0));
-        wsv[c] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * (k / 128), 0, 0));
-    }
+    for (int c = 0; c < kC; ++c)
+        wsv[c] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * ((1024 * c + 16 * lane) / 128), 0, 0));
 #pragma unroll
     for (int c = 0; c < kC; ++c) {
         const int k = 1024 * c + 16 * lane;
@@ -554,32 +556,25 @@ __global__ __launch_bounds__(kGemvWaves * kWave) void w8a16_gemv_kernel(
             wv[c][r] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, 0));
         }
     }
-    // Keep every load ahead of the arithmetic: the scheduler would otherwise
-    // sink the later chunks' loads below the first chunk's products.
+    // Keep every load ahead of the token copy and the arithmetic: the
+    // scheduler would otherwise sink the later chunks' loads below the
+    // first chunk's products.
     __builtin_amdgcn_sched_barrier(0);
+    gemv_x_store<kU>(x_lds, xr);
+    __syncthreads();
 
     float acc[kR];
 #pragma unroll
     for (int r = 0; r < kR; ++r) acc[r] = 0.0f;
 #pragma unroll
     for (int c = 0; c < kC; ++c) {
-        // Chunks past K hold zeros only (every lane's loads lie past its
-        // descriptor), so they add nothing and need no branch.
-        float xf[16];
+        // Lane l's 16 activations of chunk c: bytes 2048 c + 32 l .. + 31.
+        // Chunks past K hold zeros only (weights and token), so they add
+        // nothing and need no branch.
+        const i32x4 xv[2] = {gemv_x_read(x_lds, 128 * c + 2 * lane), gemv_x_read(x_lds, 128 * c + 2 * lane + 1)};
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t u = (uint32_t)xv[c][h][i];
-                xf[8 * h + 2 * i] = half_bits_to_f32<kXBf16>(u & 0xFFFFu);
-                xf[8 * h + 2 * i + 1] = half_bits_to_f32<kXBf16>(u >> 16);
-            }
-#pragma unroll
-        for (int r = 0; r < kR; ++r) {
-            float wf[16];
-            e4m3x16_to_f32(wv[c][r], wf);
-            acc[r] = __builtin_fmaf(block_dot16(xf, wf), wsv[c], acc[r]);
-        }
+        for (int r = 0; r < kR; ++r)
+            acc[r] = __builtin_fmaf(block_sum8(lane_dot16<kXBf16>(pairs(xv), wv[c][r])), wsv[c], acc[r]);
     }
 #pragma unroll
     for (int r = 0; r < kR; ++r) {
@@ -597,30 +592,28 @@ __global__ __launch_bounds__(kGemvWaves * kWave) void w8a16_gemv_kernel(
 // order.  The scale byte E (e = E - 127) of lane l in chunk c is
 // e8m0[n / 32, 32 c + l / 2].
 template <int kR, int kC>
-__global__ __launch_bounds__(kGemvWaves * kWave) void w8a16_blk32_gemv_kernel(
+__global__ __launch_bounds__(kGemvThreads) void w8a16_blk32_gemv_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq, const uint8_t* __restrict__ e8m0,
     void* __restrict__ y, int y_dtype, int64_t N, int64_t K) {
+    constexpr int kU = kC / 4;
+    __shared__ __attribute__((aligned(16))) uint8_t x_lds[2048 * kC];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
     const int64_t n0 = ((int64_t)blockIdx.x * kGemvWaves + wave) * kR;   // wave-uniform: scalar descriptors
-    if (n0 >= N) return;
+    const int64_t rows = n0 >= N ? 0 : N - n0 < kR ? N - n0 : kR;     // as in w8a16_gemv_kernel
+    const int64_t nb = rows > 0 ? n0 : 0;
     const int K32 = (int)(K / 32);
-    const int64_t rows = N - n0 < kR ? N - n0 : kR;
     const int w_bytes = (int)(rows * K);
-    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void*)(wq + n0 * K), 0, w_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void*)(wq + nb * K), 0, w_bytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)x, 0, (int)(2 * K), 0x00020000);
     // The kR rows lie in one 32-row scale tile (kR divides 32 and n0 is a multiple of kR).
     const __amdgpu_buffer_rsrc_t re =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(e8m0 + (n0 / 32) * K32), 0, K32, 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc((void*)(e8m0 + (nb / 32) * K32), 0, rows > 0 ? K32 : 0, 0x00020000);
 
-    i32x4 xv[kC][2], wv[kC][kR];
+    i32x4 xr[kU], wv[kC][kR];
     uint32_t eb[kC];
+    gemv_x_issue<kU>(rx, xr);
 #pragma unroll
-    for (int c = 0; c < kC; ++c) {
-        const int k = 1024 * c + 16 * lane;
-        xv[c][0] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, 2 * k, 0, 0));
-        xv[c][1] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, 2 * k + 16, 0, 0));
-        eb[c] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(re, k / 32, 0, 0);
-    }
+    for (int c = 0; c < kC; ++c) eb[c] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(re, (1024 * c + 16 * lane) / 32, 0, 0);
 #pragma unroll
     for (int c = 0; c < kC; ++c) {
         const int k = 1024 * c + 16 * lane;
@@ -630,37 +623,22 @@ __global__ __launch_bounds__(kGemvWaves * kWave) void w8a16_blk32_gemv_kernel(
             wv[c][r] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, 0));
         }
     }
-    __builtin_amdgcn_sched_barrier(0);   // every load ahead of the arithmetic
+    __builtin_amdgcn_sched_barrier(0);   // every load ahead of the token copy and the arithmetic
+    gemv_x_store<kU>(x_lds, xr);
+    __syncthreads();
 
     float acc[kR];
 #pragma unroll
     for (int r = 0; r < kR; ++r) acc[r] = 0.0f;
 #pragma unroll
     for (int c = 0; c < kC; ++c) {
-        float xf[16];
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t u = (uint32_t)xv[c][h][i];
-                xf[8 * h + 2 * i] = half_bits_to_f32<false>(u & 0xFFFFu);
-                xf[8 * h + 2 * i + 1] = half_bits_to_f32<false>(u >> 16);
-            }
-        // 2^(E - 127) as fp32 (E in [113, 134]: a normal number).  Lanes
-        // past K read E = 0 and zero weights: the factor is then 0.
+        const i32x4 xv[2] = {gemv_x_read(x_lds, 128 * c + 2 * lane), gemv_x_read(x_lds, 128 * c + 2 * lane + 1)};
+        // 2^(E - 127) (E in [113, 134]) goes into the widening: each weight
+        // becomes the fp16 number value * 2^e exactly.  Lanes past K read
+        // E = 0 and zero weights, which widen to zeros.
         const float scale = ue8m0_scale(eb[c]);
 #pragma unroll
-        for (int r = 0; r < kR; ++r) {
-            float wf[16];
-            e4m3x16_to_f32(wv[c][r], wf);
-            float d0 = 0.0f, d1 = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 16; i += 2) {
-                d0 = __builtin_fmaf(xf[i], wf[i], d0);
-                d1 = __builtin_fmaf(xf[i + 1], wf[i + 1], d1);
-            }
-            acc[r] = __builtin_fmaf(d0 + d1, scale, acc[r]);
-        }
+        for (int r = 0; r < kR; ++r) acc[r] += lane_dot16<false>(pairs(xv), wv[c][r], scale);
     }
 #pragma unroll
     for (int r = 0; r < kR; ++r) {
@@ -672,11 +650,11 @@ __global__ __launch_bounds__(kGemvWaves * kWave) void w8a16_blk32_gemv_kernel(
 hipError_t launch_w8a16_gemv(const void* x, bool x_bf16, const uint8_t* wq, const float* ws, void* y, int y_dtype,
                              int64_t N, int64_t K, hipStream_t stream) {
     if (N % 16 != 0 || K > kGemvMaxK) return hipErrorInvalidValue;
-    const int kr = gemv_rows_per_wave(N);
+    const int kr = gemv_rows_per_wave(N, K);
     const dim3 grid((unsigned)((N + kGemvWaves * kr - 1) / (kGemvWaves * kr)));
     const uint16_t* xh = static_cast<const uint16_t*>(x);
 #define BFP8_LAUNCH_GEMV(B, R, C)                                                                              \
-    hipLaunchKernelGGL((w8a16_gemv_kernel<B, R, C>), grid, dim3(kGemvWaves * kWave), 0, stream, xh, wq, ws, y, \
+    hipLaunchKernelGGL((w8a16_gemv_kernel<B, R, C>), grid, dim3(kGemvThreads), 0, stream, xh, wq, ws, y, \
                        y_dtype, N, K)
 #define BFP8_LAUNCH_GEMV_C(B, R)                    \
     switch (gemv_chunks(K)) {                        \
@@ -685,11 +663,12 @@ hipError_t launch_w8a16_gemv(const void* x, bool x_bf16, const uint8_t* wq, cons
         case 12: BFP8_LAUNCH_GEMV(B, R, 12); break; \
         default: BFP8_LAUNCH_GEMV(B, R, 16); break; \
     }
+    // Two rows per wave only with K <= 8192 (gemv_rows_per_wave): 4 or 8 chunks.
     if (x_bf16) {
-        if (kr == 2) { BFP8_LAUNCH_GEMV_C(true, 2) }
+        if (kr == 2) { if (gemv_chunks(K) == 4) BFP8_LAUNCH_GEMV(true, 2, 4); else BFP8_LAUNCH_GEMV(true, 2, 8); }
         else { BFP8_LAUNCH_GEMV_C(true, 1) }
     } else {
-        if (kr == 2) { BFP8_LAUNCH_GEMV_C(false, 2) }
+        if (kr == 2) { if (gemv_chunks(K) == 4) BFP8_LAUNCH_GEMV(false, 2, 4); else BFP8_LAUNCH_GEMV(false, 2, 8); }
         else { BFP8_LAUNCH_GEMV_C(false, 1) }
     }
 #undef BFP8_LAUNCH_GEMV_C
@@ -700,11 +679,11 @@ hipError_t launch_w8a16_gemv(const void* x, bool x_bf16, const uint8_t* wq, cons
 hipError_t launch_w8a16_blk32_gemv(const void* x, const uint8_t* wq, const uint8_t* e8m0, void* y, int y_dtype,
                                    int64_t N, int64_t K, hipStream_t stream) {
     if (N % 32 != 0 || K > kGemvMaxK) return hipErrorInvalidValue;
-    const int kr = gemv_rows_per_wave(N);
+    const int kr = gemv_rows_per_wave(N, K);
     const dim3 grid((unsigned)((N + kGemvWaves * kr - 1) / (kGemvWaves * kr)));
     const uint16_t* xh = static_cast<const uint16_t*>(x);
 #define BFP8_LAUNCH_GEMV32(R, C)                                                                                    \
-    hipLaunchKernelGGL((w8a16_blk32_gemv_kernel<R, C>), grid, dim3(kGemvWaves * kWave), 0, stream, xh, wq, e8m0, y, \
+    hipLaunchKernelGGL((w8a16_blk32_gemv_kernel<R, C>), grid, dim3(kGemvThreads), 0, stream, xh, wq, e8m0, y, \
                        y_dtype, N, K)
 #define BFP8_LAUNCH_GEMV32_C(R)                    \
     switch (gemv_chunks(K)) {                       \
@@ -713,7 +692,8 @@ hipError_t launch_w8a16_blk32_gemv(const void* x, const uint8_t* wq, const uint8
         case 12: BFP8_LAUNCH_GEMV32(R, 12); break; \
         default: BFP8_LAUNCH_GEMV32(R, 16); break; \
     }
-    if (kr == 2) { BFP8_LAUNCH_GEMV32_C(2) }
+    // Two rows per wave only with K <= 8192 (gemv_rows_per_wave): 4 or 8 chunks.
+    if (kr == 2) { if (gemv_chunks(K) == 4) BFP8_LAUNCH_GEMV32(2, 4); else BFP8_LAUNCH_GEMV32(2, 8); }
     else { BFP8_LAUNCH_GEMV32_C(1) }
 #undef BFP8_LAUNCH_GEMV32_C
 #undef BFP8_LAUNCH_GEMV32

@@ -557,16 +557,18 @@ hipError_t launch_w8a8_wide(const uint8_t* xq, const float* xs, const uint8_t* w
 // One token with K <= 16384 (batch-1 decode): the dot products run on the
 // vector ALUs, laid out as in the W8A16 one-token kernel (stream_common.hpp:
 // lane l covers K offsets 1024 c + 16 l of every 1 KB chunk c of its weight
-// rows, kC chunks).  Each lane widens its 16 activation codes and 16 weight
-// codes to fp32 (exact), block_dot16 gives the 128-K block's dot product to
-// the 8 lanes of the block, and the block is promoted once with
+// rows, kC chunks).  Each lane widens its 16 activation codes (once per
+// chunk, for all of its rows) and 16 weight codes to bf16 (exact), sums the
+// 16 products with v_dot2c (lane_dot16: a product of two E4M3 values is
+// exact in fp32), block_sum8 gives the 128-K block's dot product to the 8
+// lanes of the block, and the block is promoted once with
 // xs[kb] * ws[n / 128, kb] ([ADA] "The fix"; [ARC] "What this adds").  All
 // loads are issued before the first product; there is no LDS and no
 // barrier.  gemv_rows is that arithmetic; the kernel that quantises its own
 // activations calls it too, so the fused call and quantise-then-GEMM give
 // the same bits.
 template <int kR, int kC>
-__device__ __forceinline__ void gemv_rows(const float (&xf)[kC][16], const float (&sx)[kC],
+__device__ __forceinline__ void gemv_rows(const uint32_t (&xp)[kC][8], const float (&sx)[kC],
                                           const i32x4 (&wv)[kC][kR], const float (&wsv)[kC], float (&acc)[kR]) {
 #pragma unroll
     for (int r = 0; r < kR; ++r) acc[r] = 0.0f;
@@ -574,11 +576,7 @@ __device__ __forceinline__ void gemv_rows(const float (&xf)[kC][16], const float
     for (int c = 0; c < kC; ++c) {
         const float sc = sx[c] * wsv[c];
 #pragma unroll
-        for (int r = 0; r < kR; ++r) {
-            float wf[16];
-            e4m3x16_to_f32(wv[c][r], wf);
-            acc[r] = __builtin_fmaf(block_dot16(xf[c], wf), sc, acc[r]);
-        }
+        for (int r = 0; r < kR; ++r) acc[r] = __builtin_fmaf(block_sum8(lane_dot16<true>(xp[c], wv[c][r])), sc, acc[r]);
     }
 #pragma unroll
     for (int r = 0; r < kR; ++r) acc[r] = group_sum8(acc[r]);
@@ -609,33 +607,37 @@ __device__ __forceinline__ void gemv_load_weights(const uint8_t* wq, const float
 }
 
 template <int kR, int kC>
-__global__ __launch_bounds__(kGemvWaves * kWave) void w8a8_gemv_kernel(
+__global__ __launch_bounds__(kGemvThreads) void w8a8_gemv_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ xs, const uint8_t* __restrict__ wq,
     const float* __restrict__ ws, void* __restrict__ y, int y_dtype, int64_t N, int64_t K) {
+    constexpr int kU = (kC + 7) / 8;   // 8 KB rounds of the token's codes (1 KB per chunk)
+    __shared__ __attribute__((aligned(16))) uint8_t x_lds[8192 * kU];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
     const int64_t n0 = ((int64_t)blockIdx.x * kGemvWaves + wave) * kR;   // wave-uniform: scalar descriptors
-    if (n0 >= N) return;
+    // The launch covers N exactly (N % 16 == 0); a wave past N would still
+    // take part in the token copy and the barrier, reading no weights.
+    const int64_t rows = n0 >= N ? 0 : N - n0 < kR ? N - n0 : kR;
     const int KB = (int)(K / 128);
-    const int64_t rows = N - n0 < kR ? N - n0 : kR;
     const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)xq, 0, (int)K, 0x00020000);
     const __amdgpu_buffer_rsrc_t rxs = __builtin_amdgcn_make_buffer_rsrc((void*)xs, 0, KB * 4, 0x00020000);
-    i32x4 xv[kC], wv[kC][kR];
+    i32x4 xr[kU], wv[kC][kR];
     float sx[kC], wsv[kC];
+    gemv_x_issue<kU>(rx, xr);
 #pragma unroll
-    for (int c = 0; c < kC; ++c) {
-        const int k = 1024 * c + 16 * lane;
-        xv[c] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, k, 0, 0));
-        sx[c] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rxs, 4 * (k / 128), 0, 0));
-    }
-    gemv_load_weights<kR, kC>(wq, ws, n0, rows, K, lane, wv, wsv);
-    // Keep every load ahead of the arithmetic: the scheduler would otherwise
-    // sink the later chunks' loads below the first chunk's products.
+    for (int c = 0; c < kC; ++c)
+        sx[c] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rxs, 4 * ((1024 * c + 16 * lane) / 128), 0, 0));
+    gemv_load_weights<kR, kC>(wq, ws, rows > 0 ? n0 : 0, rows, K, lane, wv, wsv);
+    // Keep every load ahead of the token copy and the arithmetic: the
+    // scheduler would otherwise sink the later chunks' loads below the
+    // first chunk's products.
     __builtin_amdgcn_sched_barrier(0);
-    float xf[kC][16];
+    gemv_x_store<kU>(x_lds, xr);
+    __syncthreads();
+    uint32_t xp[kC][8];
 #pragma unroll
-    for (int c = 0; c < kC; ++c) e4m3x16_to_f32(xv[c], xf[c]);
+    for (int c = 0; c < kC; ++c) e4m3x16_to_bf16x2(gemv_x_read(x_lds, 64 * c + lane), xp[c]);
     float acc[kR];
-    gemv_rows<kR, kC>(xf, sx, wv, wsv, acc);
+    gemv_rows<kR, kC>(xp, sx, wv, wsv, acc);
 #pragma unroll
     for (int r = 0; r < kR; ++r)
         if (lane == 0 && r < rows) store_out(y, y_dtype, n0 + r, acc[r]);
@@ -654,10 +656,10 @@ template <bool kXBf16, int kW, int kC>
 __global__ __launch_bounds__(kW * kWave) void w8a8_gemv_quant_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq, const float* __restrict__ ws,
     void* __restrict__ y, int y_dtype, int64_t N, int64_t K) {
-    constexpr int V = 16;                   // activations per lane per round
+    constexpr int V = 4096 / (kW * kWave);  // activations per lane per round
     constexpr int kGroupLanes = 128 / V;
     constexpr int kRounds = kC / 4;         // 4096 values per round
-    static_assert(kW * V * kWave == 4096 && kC % 4 == 0, "one round covers four chunks");
+    static_assert((V == 8 || V == 16) && kW * V * kWave == 4096 && kC % 4 == 0, "one round covers four chunks");
     __shared__ __attribute__((aligned(16))) uint8_t codes_lds[1024 * kC];
     __shared__ float scale_lds[8 * kC];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
@@ -711,17 +713,18 @@ __global__ __launch_bounds__(kW * kWave) void w8a8_gemv_quant_kernel(
     }
     __syncthreads();
 
-    float xf[kC][16], sx[kC];
+    uint32_t xp[kC][8];
+    float sx[kC];
 #pragma unroll
     for (int c = 0; c < kC; ++c) {
         const int k = 1024 * c + 16 * lane;
-        e4m3x16_to_f32(*reinterpret_cast<const i32x4*>(codes_lds + k), xf[c]);
+        e4m3x16_to_bf16x2(*reinterpret_cast<const i32x4*>(codes_lds + k), xp[c]);
         // Lanes past K: their weights are zero; take scale 0 so that no
         // stale value enters the promotion.
         sx[c] = k < K ? scale_lds[k / 128] : 0.0f;
     }
     float acc[1];
-    gemv_rows<1, kC>(xf, sx, wv, wsv, acc);
+    gemv_rows<1, kC>(xp, sx, wv, wsv, acc);
     if (lane == 0) store_out(y, y_dtype, n0, acc[0]);
 }
 
@@ -729,10 +732,10 @@ hipError_t launch_w8a8_gemv(const uint8_t* xq, const float* xs, const uint8_t* w
                             int y_dtype, int64_t N, int64_t K, hipStream_t stream) {
     if (N % 16 != 0 || K > kGemvMaxK) return hipErrorInvalidValue;
     static_assert(kGemvWaves == kGemvLaunchWaves, "plan and launch agree");
-    const int kr = gemv_rows_per_wave(N);
+    const int kr = gemv_rows_per_wave(N, K);
     const dim3 grid((unsigned)((N + kGemvWaves * kr - 1) / (kGemvWaves * kr)));
 #define BFP8_LAUNCH_GEMV8(R, C)                                                                                    \
-    hipLaunchKernelGGL((w8a8_gemv_kernel<R, C>), grid, dim3(kGemvWaves * kWave), 0, stream, xq, xs, wq, ws, y, \
+    hipLaunchKernelGGL((w8a8_gemv_kernel<R, C>), grid, dim3(kGemvThreads), 0, stream, xq, xs, wq, ws, y, \
                        y_dtype, N, K)
 #define BFP8_LAUNCH_GEMV8_C(R)                    \
     switch (gemv_chunks(K)) {                      \
@@ -741,7 +744,8 @@ hipError_t launch_w8a8_gemv(const uint8_t* xq, const float* xs, const uint8_t* w
         case 12: BFP8_LAUNCH_GEMV8(R, 12); break; \
         default: BFP8_LAUNCH_GEMV8(R, 16); break; \
     }
-    if (kr == 2) { BFP8_LAUNCH_GEMV8_C(2) }
+    // Two rows per wave only with K <= 8192 (gemv_rows_per_wave): 4 or 8 chunks.
+    if (kr == 2) { if (gemv_chunks(K) == 4) BFP8_LAUNCH_GEMV8(2, 4); else BFP8_LAUNCH_GEMV8(2, 8); }
     else { BFP8_LAUNCH_GEMV8_C(1) }
 #undef BFP8_LAUNCH_GEMV8_C
 #undef BFP8_LAUNCH_GEMV8
@@ -752,13 +756,15 @@ hipError_t launch_w8a8_gemv_quant(const void* x, bool x_bf16, const uint8_t* wq,
                                   int y_dtype, int64_t N, int64_t K, hipStream_t stream) {
     if (N % 16 != 0 || K > kGemvMaxK) return hipErrorInvalidValue;   // every wave owns a row
     const uint16_t* xh = static_cast<const uint16_t*>(x);
-    // Four waves (rows) per workgroup: each wave quantises a quarter of each
-    // 4096 values, 16 values per lane, its group maximum all in lane moves
-    // (measured 5.29 vs 5.43 us for sixteen waves at N = K = 4096, even at
-    // N = 12288).
-    const dim3 grid((unsigned)(N / 4));
+    // Eight waves (rows) per workgroup: each wave quantises an eighth of each
+    // 4096 values, 8 values per lane, its group maximum all in lane moves.
+    // Every workgroup quantises the whole token, so fewer, larger workgroups
+    // do less of that work in all: N = K = 4096, 5.0-5.06 us against
+    // 5.25-5.29 for four waves (16 values per lane) and 5.43 for sixteen.
+    constexpr int kQW = kGemvWaves;
+    const dim3 grid((unsigned)(N / kQW));
 #define BFP8_LAUNCH_GEMVQ(B, C)                                                                                    \
-    hipLaunchKernelGGL((w8a8_gemv_quant_kernel<B, 4, C>), grid, dim3(4 * kWave), 0, stream, xh, wq, ws, y, y_dtype, \
+    hipLaunchKernelGGL((w8a8_gemv_quant_kernel<B, kQW, C>), grid, dim3(kQW * kWave), 0, stream, xh, wq, ws, y, y_dtype, \
                        N, K)
 #define BFP8_LAUNCH_GEMVQ_C(B)                    \
     switch (gemv_chunks(K)) {                      \

@@ -61,27 +61,86 @@ inline bool stream_workspace_parts(const StreamPlan& p, void* ws, uint32_t*& cou
 }
 
 // ------------------------------------------- one-token dot products ----
-// Shared by the W8A8 and W8A16 kernels for M = 1 (K <= kGemvMaxK): four
+// Shared by the W8A8 and W8A16 kernels for M = 1 (K <= kGemvMaxK): eight
 // waves per workgroup, lane l of a wave covering K offsets 1024 c + 16 l of
 // each 1 KB chunk c of its weight rows.  The kernels are instantiated for
 // kC = 4, 8, 12 or 16 chunks (gemv_chunks: the fewest covering K), and issue
-// every load of all kC chunks before the first product.
-constexpr int kGemvWaves = 4;
+// every load of all kC chunks before the first product.  The token is read
+// from memory once per workgroup and shared through LDS (gemv_x_issue,
+// gemv_x_store): with every wave reading all of it from L2, a 16-bit token
+// of K = 4096 moved twice the weights' bytes through the caches (W8A16
+// N = K = 4096: 5.25-5.35 us; the fused quantiser, which already shared its
+// codes this way, ran 5.0 us over the same weights).
+constexpr int kGemvWaves = 8;
 constexpr int kGemvMaxChunks = 16;
 constexpr int64_t kGemvMaxK = 1024 * kGemvMaxChunks;
 static_assert(kGemvMaxK == kOneTokenMaxK, "routing and kernels agree");
 inline int gemv_chunks(int64_t K) { return K <= 4096 ? 4 : K <= 8192 ? 8 : K <= 12288 ? 12 : 16; }
 
-// The 16 E4M3 codes of v (K order) widened to fp32; exact for every finite code.
-__device__ __forceinline__ void e4m3x16_to_f32(i32x4 v, float* f) {
+// The first kU * 8 KB of the token (descriptor rx; bytes past its range
+// load as zeros) copied into LDS by the workgroup: thread t loads the 16
+// bytes of unit t + 512 u (u < kU) in gemv_x_issue, before its weight
+// loads, and stores them in gemv_x_store, after them; a barrier follows.
+// Unit U sits at LDS unit U ^ ((U >> 4) & 1), so that a wave reading units
+// 2 l and then 2 l + 1 (a 16-bit chunk: 32 bytes per lane) hits 16
+// distinct bank groups per 16 lanes in each read.
+constexpr int kGemvThreads = kGemvWaves * kWave;
+__device__ __forceinline__ int gemv_x_unit(int u) { return u ^ ((u >> 4) & 1); }
+template <int kU>
+__device__ __forceinline__ void gemv_x_issue(__amdgpu_buffer_rsrc_t rx, i32x4 (&v)[kU]) {
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+        v[u] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                             rx, 16 * ((int)threadIdx.x + kGemvThreads * u), 0, 0));
+}
+template <int kU>
+__device__ __forceinline__ void gemv_x_store(uint8_t* x_lds, const i32x4 (&v)[kU]) {
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+        *reinterpret_cast<i32x4*>(x_lds + 16 * gemv_x_unit((int)threadIdx.x + kGemvThreads * u)) = v[u];
+}
+__device__ __forceinline__ i32x4 gemv_x_read(const uint8_t* x_lds, int unit) {
+    return *reinterpret_cast<const i32x4*>(x_lds + 16 * gemv_x_unit(unit));
+}
+
+// The 16 E4M3 codes of v (K order) widened to 8 bf16 pairs (pair d: K
+// offsets 2d, 2d + 1); exact for every finite code.
+__device__ __forceinline__ void e4m3x16_to_bf16x2(i32x4 v, uint32_t (&p)[8]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(v[i], false), hi = __builtin_amdgcn_cvt_pk_f32_fp8(v[i], true);
-        f[4 * i] = lo[0];
-        f[4 * i + 1] = lo[1];
-        f[4 * i + 2] = hi[0];
-        f[4 * i + 3] = hi[1];
+        p[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)v[i], 1.0f, false));
+        p[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)v[i], 1.0f, true));
     }
+}
+
+// One lane's 16 products of a chunk: xp[d] holds two 16-bit values (bf16
+// or fp16, K offsets 2d and 2d + 1), w 16 E4M3 weights (byte b: K offset
+// b), each widened exactly to the same 16-bit type and multiplied by
+// `scale` (a power of two).  Two v_dot2c chains over alternate pairs (two
+// products per instruction, each exact in fp32, accumulated in fp32), then
+// their sum.  All of a one-token kernel's loads land over the launch's last
+// microseconds, so this arithmetic after the last load is exposed: 8
+// conversions and 8 v_dot2c per lane and chunk, where widening both
+// operands to fp32 and multiplying took 24 to 40 VALU operations.
+template <bool kBf16>
+__device__ __forceinline__ float lane_dot16(const uint32_t (&xp)[8], i32x4 w, float scale = 1.0f) {
+    float d0 = 0.0f, d1 = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t q = (uint32_t)w[i];
+        if constexpr (kBf16) {
+            d0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, xp[2 * i]),
+                                                 __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q, scale, false), d0, false);
+            d1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, xp[2 * i + 1]),
+                                                 __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q, scale, true), d1, false);
+        } else {
+            d0 = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, xp[2 * i]),
+                                        __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(q, scale, false), d0, false);
+            d1 = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, xp[2 * i + 1]),
+                                        __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(q, scale, true), d1, false);
+        }
+    }
+    return d0 + d1;
 }
 
 // v plus the value of the lane given by DPP control `ctl` (a lane move
@@ -91,20 +150,13 @@ __device__ __forceinline__ float add_dpp(float v) {
     return v + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), ctl, 0xF, 0xF, false));
 }
 
-// Sum of x[i] * w[i] over one lane's 16 values, then over the 8 lanes of its
-// 128-K block (lanes 8 j .. 8 j + 7): every lane of the group returns the
-// block's dot product, in one fixed order.  The lane sums pair lanes i ^ 1,
-// then i ^ 2 (quad permutes), then the other quad of the eight (half-row
-// mirror: after the first two steps every lane of a quad holds the same
-// value, so lane 7 - i stands for lane i ^ 4).
-__device__ __forceinline__ float block_dot16(const float* x, const float* w) {
-    float d0 = 0.0f, d1 = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; i += 2) {
-        d0 = __builtin_fmaf(x[i], w[i], d0);
-        d1 = __builtin_fmaf(x[i + 1], w[i + 1], d1);
-    }
-    float d = d0 + d1;
+// Sum of a lane's partial over the 8 lanes of its 128-K block (lanes 8 j ..
+// 8 j + 7): every lane of the group returns the block's sum, in one fixed
+// order.  The lane sums pair lanes i ^ 1, then i ^ 2 (quad permutes), then
+// the other quad of the eight (half-row mirror: after the first two steps
+// every lane of a quad holds the same value, so lane 7 - i stands for lane
+// i ^ 4).
+__device__ __forceinline__ float block_sum8(float d) {
     d = add_dpp<0xB1>(d);    // quad_perm [1, 0, 3, 2]: lane i ^ 1
     d = add_dpp<0x4E>(d);    // quad_perm [2, 3, 0, 1]: lane i ^ 2
     d = add_dpp<0x141>(d);   // row_half_mirror: the other quad

@@ -186,7 +186,7 @@ bfp8_status bfp8_gemm_w8a8_blk128_noalloc(const uint8_t* xq, const float* xs,
  *   workspace: at least bfp8_workspace_bytes(BFP8_OP_QUANT_GEMM_W8A8_BLK128,
  *       M, N, K) bytes, zero-filled before its first use, left ready for the
  *       next call; calls that overlap in time must not share one.  For M = 1
- *       with K <= 4096 (the one-token kernel; no workspace) and for M <= 8
+ *       with K <= 8192 (the one-token kernel; no workspace) and for M <= 8
  *       where bfp8_gemm_w8a8_blk128 uses the weight-streaming kernel, the
  *       kernel quantises the activations itself; otherwise the codes and
  *       scales are staged in the workspace by the 1x128 quantiser.
@@ -198,17 +198,17 @@ bfp8_status bfp8_quant_gemm_w8a8_blk128(const void* x, int x_dtype,
                                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * W8A16 blockwise GEMM: 16-bit activations, E4M3 weights expanded to 16 bits
- * in registers by integer bit operations, the exponent-bias difference
- * (2^8 for fp16, 2^120 for bf16) folded into the block scale ([3090] §4.1;
- * [ARC] "What this adds": the conversion is exact and the scale is applied
- * once per 128 K values).
+ * W8A16 blockwise GEMM: 16-bit activations, E4M3 weights widened to the
+ * activations' type in registers by the FP8 conversion instructions
+ * ([3090] §2, §4.1: the widening is exact; [ARC] "What this adds": the
+ * scale is applied once per 128 K values).
  *   Y[m, n] = sum_kb ws[n / 128, kb] * sum over k in kb of x[m, k] * E4M3(wq[n, k])
  *   x   [M, K] bf16 or fp16, wq [N, K] E4M3, ws [ceil(N/128), K/128] fp32.
  *   y   [M, N] in y_dtype (BF16 / F16 / F32); workspace as for W8A8 (sized
  *       by bfp8_workspace_bytes(BFP8_OP_GEMM_W8A16_BLK128, M, N, K)).
- * M = 1 with K <= 4096 runs a dot-product kernel on the vector ALUs (the
- * weights widened to fp32); M <= 16 otherwise streams the weights (decode);
+ * M = 1 with K <= 12288 runs a dot-product kernel on the vector ALUs (two
+ * 16-bit products per instruction); M <= 16 otherwise streams the weights
+ * (decode);
  * larger M reads all tokens per weight tile or runs a tiled MFMA kernel that
  * widens each weight fragment once per wave and reuses it for up to 64
  * tokens ([3090] §4.4: at prefill the weight-only cost is a few percent).
@@ -221,9 +221,11 @@ bfp8_status bfp8_gemm_w8a16_blk128(const void* x, int x_dtype,
 
 /*
  * W8A16 GEMM with 32x32 weight tiles and power-of-two (UE8M0) scales
- * ([SM70] "How it works", "Exactness"): each weight is expanded to fp16 by
- * integer bit operations and multiplied exactly by its tile's 2^e (exact in
- * fp16 for e in [-14, 7]), then contracted with fp32 accumulation.
+ * ([SM70] "How it works", "Exactness"): each weight is widened to fp16 and
+ * multiplied by its tile's 2^e in one conversion instruction (exact in fp16
+ * for e in [-14, 7]), then contracted with fp32 accumulation.  One token
+ * with K <= 8192 runs a dot-product kernel on the vector ALUs, M <= 16
+ * otherwise streams the weights, larger M streams them once per 16 tokens.
  *   Y[m, n] = sum_k x[m, k] * (E4M3(wq[n, k]) * 2^(e8m0[n/32, k/32] - 127))
  *   x     [M, K] fp16 (x_dtype BFP8_F16).
  *   wq    [N, K] E4M3.
@@ -270,9 +272,9 @@ size_t bfp8_workspace_bytes(int op, int64_t M, int64_t N, int64_t K);
  *   n_multiple    N must be a multiple of this.
  *   align_bytes   required alignment of every device pointer.
  *   m_stream_max  largest M always served by the weight-streaming decode
- *                 kernels (one token with K <= 4096 runs a dot-product
- *                 kernel on the vector ALUs instead, for every blk128 GEMM
- *                 and the fused call; W8A8 streams when K needs no split across
+ *                 kernels (one token runs a dot-product kernel on the
+ *                 vector ALUs instead: with K <= 8192 for W8A8, the fused
+ *                 call and blk32, K <= 12288 for W8A16; W8A8 streams when K needs no split across
  *                 workgroups, or N < 1024; W8A8 also streams up to
  *                 4 * m_stream_max, one workgroup per 16-token tile, when
  *                 those workgroups fit one round on the CUs without a split
@@ -284,7 +286,8 @@ size_t bfp8_workspace_bytes(int op, int64_t M, int64_t N, int64_t K);
  *                 weight tile for m_stream_max < M <= 16 * m_stream_max
  *                 when K <= 4096 and either M <= 2 * m_stream_max or
  *                 M * N <= 2^19, and uses its tiled MFMA kernel
- *                 otherwise; blk32 always streams.
+ *                 otherwise; blk32 streams whenever it does not run its
+ *                 one-token kernel.
  * Any output pointer may be NULL.
  */
 bfp8_status bfp8_get_limits(int op, int64_t* k_multiple, int64_t* n_multiple,

@@ -45,8 +45,13 @@ W8A8_THRESHOLD = [(1, 384, 640, "w8a8_gemv")] + \
     [(M, 384, 640, "w8a8_stream") for M in (2, 3, 5, 8, 15, 16, 17, 24, 31, 32, 33, 48, 63, 64)] + \
     [(M, 384, 640, "w8a8_wide:16x32w8") for M in (65, 129, 200)]
 
+# One token, K <= 8192: 4 or 8 chunks of 1 KB per lane, K ending inside a
+# chunk, one or two weight rows per wave (two from N = 8192).
 W8A8_ONE_TOKEN = [(1, N, K, "w8a8_gemv") for N, K in
-                  ((16, 128), (16, 1152), (64, 4096), (1024, 4096), (2064, 1024), (4096, 3968), (12288, 2048))]
+                  ((16, 128), (16, 1152), (64, 4096), (1024, 4096), (2064, 1024), (4096, 3968), (12288, 2048),
+                   (512, 4224), (4096, 7168), (2064, 5120), (8192, 8192))]
+# Just above the one-token range.
+W8A8_ABOVE_ONE_TOKEN = [(1, 512, 8320, "w8a8_stream/split"), (1, 4096, 12416, "w8a8_stream")]
 
 # N not a multiple of 128: tiles straddle weight-scale rows.
 W8A8_STRADDLE = [(M, N, 256, "w8a8_stream") for N in (16, 48, 144, 272) for M in (4, 40)]
@@ -90,7 +95,8 @@ W8A8_DETERMINISTIC = (64, 512, 1024, "w8a8_stream")
 # Fused quantise + W8A8 (bit-identical to quantise-then-GEMM).
 QUANT_W8A8 = [
     (1, 4096, 4096, "w8a8_gemv_quant"), (1, 16, 128, "w8a8_gemv_quant"), (1, 1024, 1152, "w8a8_gemv_quant"),
-    (1, 2064, 3968, "w8a8_gemv_quant"), (1, 512, 4224, "w8a8_stream_quant"), (2, 1024, 4096, "w8a8_stream_quant"),
+    (1, 2064, 3968, "w8a8_gemv_quant"), (1, 512, 4224, "w8a8_gemv_quant"), (1, 4096, 7168, "w8a8_gemv_quant"),
+    (1, 512, 8320, "w8a8_stream_quant/split"), (2, 1024, 4096, "w8a8_stream_quant"),
     (3, 512, 640, "w8a8_stream_quant"), (4, 384, 12288, "w8a8_stream_quant/split"),
     (5, 1024, 4096, "w8a8_stream_quant"), (8, 512, 1024, "w8a8_stream_quant"), (9, 512, 640, "quant+w8a8_stream"),
     (16, 1024, 4096, "quant+w8a8_stream"), (17, 384, 640, "quant+w8a8_stream"), (64, 1024, 4096, "quant+w8a8_stream"),
@@ -101,9 +107,10 @@ QUANT_W8A8 = [
 W8A16_BY_M = [(1, 512, 1024, "w8a16_gemv")] + \
     [(M, 512, 1024, "w8a16_stream") for M in (2, 3, 4, 5, 8, 12, 16)] + \
     [(M, 512, 1024, "w8a16_wide:16x32w8") for M in (17, 33, 64, 65, 130)]
+# One token, K <= 12288: 4, 8 or 12 chunks, one or two rows per wave.
 W8A16_ONE_TOKEN = [(1, N, K, "w8a16_gemv") for N, K in
                    ((16, 128), (16, 1152), (64, 4096), (1024, 4096), (2064, 1024), (4096, 4096), (4096, 3968),
-                    (12288, 2048))]
+                    (12288, 2048), (2064, 5120), (8192, 8192), (4096, 12288))]
 W8A16_ALL_TOKENS = [
     (17, 1024, 4096, "w8a16_wide:16x32w8"), (32, 4096, 4096, "w8a16_wide:16x32w8"),
     (50, 1024, 4096, "w8a16_wide:16x32w8"), (64, 4096, 4096, "w8a16_wide:32x32w8"),
@@ -111,7 +118,7 @@ W8A16_ALL_TOKENS = [
     (128, 4096, 4096, "w8a16_wide:32x64w8"), (100, 4112, 1024, "w8a16_wide:32x64w8"),
     (256, 1024, 4096, "w8a16_wide:32x32w8"), (200, 1040, 1024, "w8a16_wide:16x64w8"),
 ]
-W8A16_LONG_K = [(M, 4096, 12288, "w8a16_stream") for M in (1, 3, 16)]
+W8A16_LONG_K = [(1, 4096, 12416, "w8a16_stream")] + [(M, 4096, 12288, "w8a16_stream") for M in (3, 16)]
 W8A16_SPLIT_K_STREAM = [(4, 512, 12288, "w8a16_stream/split")]
 W8A16_ONE_HOT = [(1, 256, 256, "w8a16_gemv"), (4, 256, 256, "w8a16_stream"), (40, 256, 256, "w8a16_wide:16x32w8")]
 W8A16_TILE_SPLIT = [(40, 1024, 8192, "w8a16_tile:128x64w8/split"), (100, 1040, 8192, "w8a16_tile:128x128w8/split"),
@@ -123,11 +130,13 @@ W8A16_PREFILL_OPROJ = (4096, 4096, 4096, "w8a16_tile:256x128w8")
 W8A16_DECODE_OPROJ = (1, 4096, 4096, "w8a16_gemv")
 
 # ---------------------------------------------------------------- blk32 ----
-BLK32_WORKLOAD = [(M, 4096, 7168, "blk32_stream_lds") for M in (1, 2, 3, 4, 8, 12, 16)]
-# One token with K <= 4096: the dot-product kernel on the vector ALUs (one and
-# two rows per wave, K of one block and K ending inside a 1 KB chunk).
+BLK32_WORKLOAD = [(1, 4096, 7168, "blk32_gemv")] + [(M, 4096, 7168, "blk32_stream_lds") for M in (2, 3, 4, 8, 12, 16)]
+# One token with K <= 8192: the dot-product kernel on the vector ALUs (one and
+# two rows per wave, K of one block and K ending inside a 1 KB chunk), and
+# just above that range.
 BLK32_ONE_TOKEN = [(1, 4096, 4096, "blk32_gemv"), (1, 32, 128, "blk32_gemv"), (1, 8192, 1152, "blk32_gemv"),
-                   (1, 1024, 3968, "blk32_gemv")]
+                   (1, 1024, 3968, "blk32_gemv"), (1, 1024, 8192, "blk32_gemv"), (1, 8192, 7168, "blk32_gemv"),
+                   (1, 4096, 12416, "blk32_stream_lds")]
 BLK32_ONE_HOT_ONE_TOKEN = (1, 704, 256, "blk32_gemv")
 # Above the streaming range ([SM70] "Results" times M = 32 ... 4096).
 BLK32_ABOVE_16 = [(M, 4096, 7168, "blk32_stream") for M in (17, 32, 64, 128, 512)]
@@ -151,7 +160,7 @@ def all_cases():
     """(op, M, N, K, variant) for every case above."""
     out = []
     tables = {
-        W8A8: [W8A8_THRESHOLD, W8A8_ONE_TOKEN, W8A8_STRADDLE, W8A8_SPLIT_K_STREAM, W8A8_NO_WORKSPACE, W8A8_TILE,
+        W8A8: [W8A8_THRESHOLD, W8A8_ONE_TOKEN, W8A8_ABOVE_ONE_TOKEN, W8A8_STRADDLE, W8A8_SPLIT_K_STREAM, W8A8_NO_WORKSPACE, W8A8_TILE,
                [W8A8_LARGE_RAGGED, W8A8_DECODE_OPROJ, W8A8_PREFILL_OPROJ, W8A8_DETERMINISTIC], W8A8_ONE_HOT],
         QW8A8: [QUANT_W8A8],
         W8A16: [W8A16_BY_M, W8A16_ONE_TOKEN, W8A16_ALL_TOKENS, W8A16_LONG_K, W8A16_SPLIT_K_STREAM, W8A16_ONE_HOT,

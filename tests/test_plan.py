@@ -66,14 +66,17 @@ def test_plan_agrees_with_workspace_bytes_and_grid():
 
 def test_routing_rules_read_off_the_plan():
     """Rules the header states, checked over the sweep."""
+    # One token: W8A8 (codes and fused) and block-32 up to K = 8192, W8A16 up to 12288.
+    one_token_k = {cases.W8A8: 8192, cases.QW8A8: 8192, cases.W8A16: 12288, cases.BLK32: 8192}
     for op, M, N, K in _sweep():
         name = bfp8.bfp8_get_plan(op, M, N, K)["kernel_name"]
+        one = M == 1 and K <= one_token_k[op]
         if op in (cases.W8A8, cases.QW8A8, cases.W8A16):
-            assert ("gemv" in name) == (M == 1 and K <= 4096), (op, M, N, K, name)
-        if op == cases.W8A16 and M <= 16 and not (M == 1 and K <= 4096):
+            assert ("gemv" in name) == one, (op, M, N, K, name)
+        if op == cases.W8A16 and M <= 16 and not one:
             assert name == "w8a16_stream"
         if op == cases.BLK32:
-            want = "blk32_gemv" if M == 1 and K <= 4096 else "blk32_stream_lds" if M <= 16 else "blk32_stream"
+            want = "blk32_gemv" if one else "blk32_stream_lds" if M <= 16 else "blk32_stream"
             assert name == want, (M, N, K, name)
         if op == cases.QW8A8 and name.endswith("_quant"):
             assert M == 1 or M <= 8
