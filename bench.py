@@ -424,10 +424,14 @@ def extra_blk32(torch, bfp8, inputs, args, M=1):
 
     _, _, kern, _ = run_steps(torch, [("g", gemm)], args.steps, args.warmup)
     us = kern["g"]["avg_us"]
+    # The streaming-read floor over the same rotated weight copies (29 MB a
+    # launch, so not the decode line's 16 MiB floor).
+    floor = read_floor(torch, [a[0] for a in copies], N * K, args.steps, args.warmup)
     del copies
     return {"avg_us": us, "alg_bytes": nb, "GBps": nb / (us * 1e3), "hbm_frac": nb / (us * 1e3) / HBM_PEAK_GBS,
             "M": M, "N": N, "K": K, "weight_copies": ncopy,
-            "kernel": bfp8.bfp8_get_plan(bfp8.OP_GEMM_W8A16_BLK32_UE8M0, M, N, K)["kernel_name"]}
+            "kernel": bfp8.bfp8_get_plan(bfp8.OP_GEMM_W8A16_BLK32_UE8M0, M, N, K)["kernel_name"],
+            "read_floor_us": floor["avg_us"], "vs_read_floor": us / floor["avg_us"]}
 
 
 # --------------------------------------------------------------- workloads ----

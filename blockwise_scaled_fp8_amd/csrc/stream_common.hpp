@@ -163,9 +163,42 @@ __device__ __forceinline__ float block_sum8(float d) {
     return d;
 }
 
-// Maximum over aligned groups of kLanes lanes (2 .. 64): lane moves inside
-// the ALU up to 16 lanes (the half-row mirror and row rotation stand for
-// i ^ 4 and i ^ 8 once the smaller groups agree), LDS permutes beyond.
+// The values of lanes i and i ^ kD (kD = 16 or 32), lower lane first, in
+// every lane i: v_permlane16_swap / v_permlane32_swap with both operands v
+// exchange rows of 16 lanes (halves of the wave) inside the ALU, where
+// __shfl_xor goes through an LDS permute (checked on the GPU over every
+// lane).  Combining the pair with a commutative operation gives the same
+// bits as combining v with __shfl_xor(v, kD).  The compiler's optimiser
+// folds a sum of the two results into twice the first one (seen in its IR
+// for lo + hi; the hardware returns different rows), so the second result
+// goes through an empty register constraint it cannot see into before use.
+template <int kD>
+__device__ __forceinline__ void lane_pair(float v, float& lo, float& hi) {
+    static_assert(kD == 16 || kD == 32, "row or half-wave exchange");
+    const uint32_t u = __builtin_bit_cast(uint32_t, v);
+    const auto p = kD == 16 ? __builtin_amdgcn_permlane16_swap(u, u, false, false)
+                            : __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    uint32_t h = p[1];
+    asm volatile("" : "+v"(h));
+    lo = __builtin_bit_cast(float, (uint32_t)p[0]);
+    hi = __builtin_bit_cast(float, h);
+}
+template <int kD>
+__device__ __forceinline__ float add_pair(float v) {
+    float lo, hi;
+    lane_pair<kD>(v, lo, hi);
+    return lo + hi;
+}
+template <int kD>
+__device__ __forceinline__ float max_pair(float v) {
+    float lo, hi;
+    lane_pair<kD>(v, lo, hi);
+    return fmaxf(lo, hi);
+}
+
+// Maximum over aligned groups of kLanes lanes (2 .. 64), all by lane moves
+// inside the ALU (the half-row mirror and row rotation stand for i ^ 4 and
+// i ^ 8 once the smaller groups agree, lane_pair for i ^ 16 and i ^ 32).
 template <int kLanes>
 __device__ __forceinline__ float group_max(float v) {
     auto max_dpp = [](float a, auto ctl) {
@@ -176,16 +209,16 @@ __device__ __forceinline__ float group_max(float v) {
     if constexpr (kLanes > 2) v = max_dpp(v, std::integral_constant<int, 0x4E>{});
     if constexpr (kLanes > 4) v = max_dpp(v, std::integral_constant<int, 0x141>{});
     if constexpr (kLanes > 8) v = max_dpp(v, std::integral_constant<int, 0x128>{});
-    if constexpr (kLanes > 16) v = fmaxf(v, __shfl_xor(v, 16, kWave));
-    if constexpr (kLanes > 32) v = fmaxf(v, __shfl_xor(v, 32, kWave));
+    if constexpr (kLanes > 16) v = max_pair<16>(v);
+    if constexpr (kLanes > 32) v = max_pair<32>(v);
     return v;
 }
 
 // Sum of the eight block groups' promoted sums of a lane (lanes 8 apart).
 __device__ __forceinline__ float group_sum8(float v) {
     v = add_dpp<0x128>(v);   // row_ror 8: lane i ^ 8 within its row of 16
-    v += __shfl_xor(v, 16, kWave);
-    v += __shfl_xor(v, 32, kWave);
+    v = add_pair<16>(v);     // lane i ^ 16
+    v = add_pair<32>(v);     // lane i ^ 32
     return v;
 }
 
