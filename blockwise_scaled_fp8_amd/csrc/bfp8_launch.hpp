@@ -172,12 +172,12 @@ constexpr int64_t kOneTokenRouteK = 8192;      // W8A8 (codes and fused), block-
 constexpr int64_t kOneTokenRouteK16 = 12288;   // W8A16 blk128
 inline bool one_token(int64_t M, int64_t K) { return M == 1 && K <= kOneTokenRouteK; }
 inline bool one_token_w8a16(int64_t M, int64_t K) { return M == 1 && K <= kOneTokenRouteK16; }
-// Weight rows per wave of the one-token kernels: two only for the largest
-// projections (measured, us, one row vs two: W8A8 4096 x 4096 5.28 vs 5.53,
-// 12288 x 4096 11.2 vs 10.9; W8A16 2048 x 4096 3.81 vs 3.87, 4096 x 4096
-// 5.34 vs 5.35, 12288 x 4096 11.3 vs 11.1), and only up to K = 8192: two
-// rows of 12 or 16 chunks hold more loads in flight than registers.
-inline int gemv_rows_per_wave(int64_t N, int64_t K) { return N >= 8192 && K <= 8192 ? 2 : 1; }
+// One weight row per wave in the one-token kernels.  With four-wave
+// workgroups that read the token from L2, two rows per wave paid on the
+// largest projections (12288 x 4096: W8A8 10.6 vs 10.2 us); with eight-wave
+// workgroups that share the token through LDS, one row is faster there too
+// (W8A8 9.8 vs 10.6 us, W8A16 9.7 vs 10.55) and equal at 4096 x 7168.
+constexpr int kGemvRowsPerWave = 1;
 constexpr int kGemvLaunchWaves = 8;    // waves per workgroup of the one-token kernels
 constexpr int kStreamLaunchWaves = 16;  // waves per workgroup of the streaming kernels
 constexpr int kWideLaunchWaves = 8;     // waves per workgroup of the all-token kernels

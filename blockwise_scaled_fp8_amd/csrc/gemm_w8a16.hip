@@ -650,7 +650,7 @@ __global__ __launch_bounds__(kGemvThreads) void w8a16_blk32_gemv_kernel(
 hipError_t launch_w8a16_gemv(const void* x, bool x_bf16, const uint8_t* wq, const float* ws, void* y, int y_dtype,
                              int64_t N, int64_t K, hipStream_t stream) {
     if (N % 16 != 0 || K > kGemvMaxK) return hipErrorInvalidValue;
-    const int kr = gemv_rows_per_wave(N, K);
+    constexpr int kr = kGemvRowsPerWave;
     const dim3 grid((unsigned)((N + kGemvWaves * kr - 1) / (kGemvWaves * kr)));
     const uint16_t* xh = static_cast<const uint16_t*>(x);
 #define BFP8_LAUNCH_GEMV(B, R, C)                                                                              \
@@ -663,14 +663,8 @@ hipError_t launch_w8a16_gemv(const void* x, bool x_bf16, const uint8_t* wq, cons
         case 12: BFP8_LAUNCH_GEMV(B, R, 12); break; \
         default: BFP8_LAUNCH_GEMV(B, R, 16); break; \
     }
-    // Two rows per wave only with K <= 8192 (gemv_rows_per_wave): 4 or 8 chunks.
-    if (x_bf16) {
-        if (kr == 2) { if (gemv_chunks(K) == 4) BFP8_LAUNCH_GEMV(true, 2, 4); else BFP8_LAUNCH_GEMV(true, 2, 8); }
-        else { BFP8_LAUNCH_GEMV_C(true, 1) }
-    } else {
-        if (kr == 2) { if (gemv_chunks(K) == 4) BFP8_LAUNCH_GEMV(false, 2, 4); else BFP8_LAUNCH_GEMV(false, 2, 8); }
-        else { BFP8_LAUNCH_GEMV_C(false, 1) }
-    }
+    if (x_bf16) { BFP8_LAUNCH_GEMV_C(true, kr) }
+    else { BFP8_LAUNCH_GEMV_C(false, kr) }
 #undef BFP8_LAUNCH_GEMV_C
 #undef BFP8_LAUNCH_GEMV
     return hipGetLastError();
@@ -679,7 +673,7 @@ hipError_t launch_w8a16_gemv(const void* x, bool x_bf16, const uint8_t* wq, cons
 hipError_t launch_w8a16_blk32_gemv(const void* x, const uint8_t* wq, const uint8_t* e8m0, void* y, int y_dtype,
                                    int64_t N, int64_t K, hipStream_t stream) {
     if (N % 32 != 0 || K > kGemvMaxK) return hipErrorInvalidValue;
-    const int kr = gemv_rows_per_wave(N, K);
+    constexpr int kr = kGemvRowsPerWave;
     const dim3 grid((unsigned)((N + kGemvWaves * kr - 1) / (kGemvWaves * kr)));
     const uint16_t* xh = static_cast<const uint16_t*>(x);
 #define BFP8_LAUNCH_GEMV32(R, C)                                                                                    \
@@ -692,9 +686,7 @@ hipError_t launch_w8a16_blk32_gemv(const void* x, const uint8_t* wq, const uint8
         case 12: BFP8_LAUNCH_GEMV32(R, 12); break; \
         default: BFP8_LAUNCH_GEMV32(R, 16); break; \
     }
-    // Two rows per wave only with K <= 8192 (gemv_rows_per_wave): 4 or 8 chunks.
-    if (kr == 2) { if (gemv_chunks(K) == 4) BFP8_LAUNCH_GEMV32(2, 4); else BFP8_LAUNCH_GEMV32(2, 8); }
-    else { BFP8_LAUNCH_GEMV32_C(1) }
+    BFP8_LAUNCH_GEMV32_C(kr)
 #undef BFP8_LAUNCH_GEMV32_C
 #undef BFP8_LAUNCH_GEMV32
     return hipGetLastError();

@@ -732,7 +732,7 @@ hipError_t launch_w8a8_gemv(const uint8_t* xq, const float* xs, const uint8_t* w
                             int y_dtype, int64_t N, int64_t K, hipStream_t stream) {
     if (N % 16 != 0 || K > kGemvMaxK) return hipErrorInvalidValue;
     static_assert(kGemvWaves == kGemvLaunchWaves, "plan and launch agree");
-    const int kr = gemv_rows_per_wave(N, K);
+    constexpr int kr = kGemvRowsPerWave;
     const dim3 grid((unsigned)((N + kGemvWaves * kr - 1) / (kGemvWaves * kr)));
 #define BFP8_LAUNCH_GEMV8(R, C)                                                                                    \
     hipLaunchKernelGGL((w8a8_gemv_kernel<R, C>), grid, dim3(kGemvThreads), 0, stream, xq, xs, wq, ws, y, \
@@ -744,9 +744,7 @@ hipError_t launch_w8a8_gemv(const uint8_t* xq, const float* xs, const uint8_t* w
         case 12: BFP8_LAUNCH_GEMV8(R, 12); break; \
         default: BFP8_LAUNCH_GEMV8(R, 16); break; \
     }
-    // Two rows per wave only with K <= 8192 (gemv_rows_per_wave): 4 or 8 chunks.
-    if (kr == 2) { if (gemv_chunks(K) == 4) BFP8_LAUNCH_GEMV8(2, 4); else BFP8_LAUNCH_GEMV8(2, 8); }
-    else { BFP8_LAUNCH_GEMV8_C(1) }
+    BFP8_LAUNCH_GEMV8_C(kr)
 #undef BFP8_LAUNCH_GEMV8_C
 #undef BFP8_LAUNCH_GEMV8
     return hipGetLastError();

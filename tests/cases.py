@@ -46,7 +46,7 @@ W8A8_THRESHOLD = [(1, 384, 640, "w8a8_gemv")] + \
     [(M, 384, 640, "w8a8_wide:16x32w8") for M in (65, 129, 200)]
 
 # One token, K <= 8192: 4 or 8 chunks of 1 KB per lane, K ending inside a
-# chunk, one or two weight rows per wave (two from N = 8192).
+# chunk, one weight row per wave, N of one workgroup up to 12288.
 W8A8_ONE_TOKEN = [(1, N, K, "w8a8_gemv") for N, K in
                   ((16, 128), (16, 1152), (64, 4096), (1024, 4096), (2064, 1024), (4096, 3968), (12288, 2048),
                    (512, 4224), (4096, 7168), (2064, 5120), (8192, 8192))]
@@ -107,7 +107,7 @@ QUANT_W8A8 = [
 W8A16_BY_M = [(1, 512, 1024, "w8a16_gemv")] + \
     [(M, 512, 1024, "w8a16_stream") for M in (2, 3, 4, 5, 8, 12, 16)] + \
     [(M, 512, 1024, "w8a16_wide:16x32w8") for M in (17, 33, 64, 65, 130)]
-# One token, K <= 12288: 4, 8 or 12 chunks, one or two rows per wave.
+# One token, K <= 12288: 4, 8 or 12 chunks, one row per wave.
 W8A16_ONE_TOKEN = [(1, N, K, "w8a16_gemv") for N, K in
                    ((16, 128), (16, 1152), (64, 4096), (1024, 4096), (2064, 1024), (4096, 4096), (4096, 3968),
                     (12288, 2048), (2064, 5120), (8192, 8192), (4096, 12288))]
@@ -132,7 +132,7 @@ W8A16_DECODE_OPROJ = (1, 4096, 4096, "w8a16_gemv")
 # ---------------------------------------------------------------- blk32 ----
 BLK32_WORKLOAD = [(1, 4096, 7168, "blk32_gemv")] + [(M, 4096, 7168, "blk32_stream_lds") for M in (2, 3, 4, 8, 12, 16)]
 # One token with K <= 8192: the dot-product kernel on the vector ALUs (one and
-# two rows per wave, K of one block and K ending inside a 1 KB chunk), and
+# 4 or 8 chunks, K of one block and K ending inside a 1 KB chunk), and
 # just above that range.
 BLK32_ONE_TOKEN = [(1, 4096, 4096, "blk32_gemv"), (1, 32, 128, "blk32_gemv"), (1, 8192, 1152, "blk32_gemv"),
                    (1, 1024, 3968, "blk32_gemv"), (1, 1024, 8192, "blk32_gemv"), (1, 8192, 7168, "blk32_gemv"),

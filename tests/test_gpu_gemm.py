@@ -56,8 +56,8 @@ def test_w8a8_across_the_stream_tile_threshold(gpu_lib, M, N, K, kernel):
 
 @pytest.mark.parametrize("M,N,K,kernel", cases.W8A8_ONE_TOKEN)
 def test_w8a8_one_token(gpu_lib, M, N, K, kernel):
-    """M = 1 with K <= 8192: the vector-ALU dot-product kernel (one or two
-    weight rows per wave, four or eight 1 KB chunks per lane), with K of one
+    """M = 1 with K <= 8192: the vector-ALU dot-product kernel (one weight
+    row per wave, four or eight 1 KB chunks per lane), with K of one
     block and K ending inside a chunk; no workspace."""
     assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 1, N, K) == 0
     _w8a8_check(1, N, K, 450 + N + K // 128, what="one token", kernel=kernel)
@@ -248,8 +248,8 @@ def test_w8a16_blk128(gpu_lib, M, N, K, kernel, xdtype):
 @pytest.mark.parametrize("xdtype", [torch.bfloat16, torch.float16])
 @pytest.mark.parametrize("M,N,K,kernel", cases.W8A16_ONE_TOKEN)
 def test_w8a16_gemv_one_token(gpu_lib, M, N, K, kernel, xdtype):
-    """M = 1 with K <= 12288: the vector-ALU dot-product kernel, one or two
-    weight rows per wave, 4, 8 or 12 chunks of 1 KB per lane; a K of one
+    """M = 1 with K <= 12288: the vector-ALU dot-product kernel, one weight
+    row per wave, 4, 8 or 12 chunks of 1 KB per lane; a K of one
     block, K ending inside a chunk (1152, 3968, 5120), N of one workgroup;
     all three output types."""
     say("w8a16 gemv", xdtype, f"N={N} K={K}")
@@ -456,8 +456,8 @@ def test_blk32_block32_workload_shape(gpu_lib, M, N, K, kernel):
 
 @pytest.mark.parametrize("M,N,K,kernel", cases.BLK32_ONE_TOKEN)
 def test_blk32_one_token(gpu_lib, M, N, K, kernel):
-    """One token with K <= 8192: the vector-ALU kernel (two rows per wave at
-    N = 8192), e uniform on [-14, 7], and the streaming kernel just above;
+    """One token with K <= 8192: the vector-ALU kernel (one row per wave, 4
+    or 8 chunks), e uniform on [-14, 7], and the streaming kernel just above;
     fp32 output against the oracle, fp16 output as RNE of the fp32
     result."""
     say("blk32 one token", N, K)
