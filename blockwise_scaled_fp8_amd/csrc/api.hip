@@ -449,7 +449,7 @@ bfp8_status bfp8_get_plan(int op, int64_t M, int64_t N, int64_t K, bfp8_plan* pl
         case BFP8_KERNEL_W8A8_GEMV:
         case BFP8_KERNEL_W8A16_GEMV:
         case BFP8_KERNEL_BLK32_GEMV: {
-            p.tile_n = kGemvLaunchWaves * kGemvRowsPerWave;
+            p.tile_n = kGemvLaunchWaves;   // one weight row per wave
             p.tile_m = 1;
             p.waves = kGemvLaunchWaves;
             p.workgroups = (N + p.tile_n - 1) / p.tile_n;

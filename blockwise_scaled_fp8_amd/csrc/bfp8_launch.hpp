@@ -172,12 +172,11 @@ constexpr int64_t kOneTokenRouteK = 8192;      // W8A8 (codes and fused), block-
 constexpr int64_t kOneTokenRouteK16 = 12288;   // W8A16 blk128
 inline bool one_token(int64_t M, int64_t K) { return M == 1 && K <= kOneTokenRouteK; }
 inline bool one_token_w8a16(int64_t M, int64_t K) { return M == 1 && K <= kOneTokenRouteK16; }
-// One weight row per wave in the one-token kernels.  With four-wave
+// The one-token kernels give each wave one weight row.  With four-wave
 // workgroups that read the token from L2, two rows per wave paid on the
 // largest projections (12288 x 4096: W8A8 10.6 vs 10.2 us); with eight-wave
 // workgroups that share the token through LDS, one row is faster there too
 // (W8A8 9.8 vs 10.6 us, W8A16 9.7 vs 10.55) and equal at 4096 x 7168.
-constexpr int kGemvRowsPerWave = 1;
 constexpr int kGemvLaunchWaves = 8;    // waves per workgroup of the one-token kernels
 constexpr int kStreamLaunchWaves = 16;  // waves per workgroup of the streaming kernels
 constexpr int kWideLaunchWaves = 8;     // waves per workgroup of the all-token kernels

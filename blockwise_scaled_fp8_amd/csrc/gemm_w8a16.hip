@@ -522,26 +522,26 @@ __device__ __forceinline__ const uint32_t (&pairs(const i32x4 (&x)[2]))[8] {
     return *reinterpret_cast<const uint32_t(*)[8]>(&x[0]);
 }
 
-template <bool kXBf16, int kR, int kC>
+template <bool kXBf16, int kC>
 __global__ __launch_bounds__(kGemvThreads) void w8a16_gemv_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq, const float* __restrict__ ws,
     void* __restrict__ y, int y_dtype, int64_t N, int64_t K) {
     constexpr int kU = kC / 4;   // 8 KB rounds of the 16-bit token (2 KB per chunk)
     __shared__ __attribute__((aligned(16))) uint8_t x_lds[2048 * kC];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
-    const int64_t n0 = ((int64_t)blockIdx.x * kGemvWaves + wave) * kR;   // wave-uniform: scalar descriptors
+    const int64_t n = (int64_t)blockIdx.x * kGemvWaves + wave;   // wave-uniform: scalar descriptors
     // The launch covers N exactly (N % 16 == 0); a wave past N would still
     // take part in the token copy and the barrier, with empty descriptors.
-    const int64_t rows = n0 >= N ? 0 : N - n0 < kR ? N - n0 : kR;
-    const int64_t nb = rows > 0 ? n0 : 0;
+    const bool live = n < N;
+    const int64_t nb = live ? n : 0;
     const int KB = (int)(K / 128);
-    const int w_bytes = (int)(rows * K);
-    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void*)(wq + nb * K), 0, w_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rw =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(wq + nb * K), 0, live ? (int)K : 0, 0x00020000);
     const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)x, 0, (int)(2 * K), 0x00020000);
     const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(ws + (nb / 128) * KB), 0, rows > 0 ? KB * 4 : 0, 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc((void*)(ws + (nb / 128) * KB), 0, live ? KB * 4 : 0, 0x00020000);
 
-    i32x4 xr[kU], wv[kC][kR];
+    i32x4 xr[kU], wv[kC];
     float wsv[kC];
     gemv_x_issue<kU>(rx, xr);
 #pragma unroll
@@ -550,11 +550,7 @@ __global__ __launch_bounds__(kGemvThreads) void w8a16_gemv_kernel(
 #pragma unroll
     for (int c = 0; c < kC; ++c) {
         const int k = 1024 * c + 16 * lane;
-#pragma unroll
-        for (int r = 0; r < kR; ++r) {
-            const int off = k < K ? (int)(r * K) + k : w_bytes;
-            wv[c][r] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, 0));
-        }
+        wv[c] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, k < K ? k : (int)K, 0, 0));
     }
     // Keep every load ahead of the token copy and the arithmetic: the
     // scheduler would otherwise sink the later chunks' loads below the
@@ -563,53 +559,45 @@ __global__ __launch_bounds__(kGemvThreads) void w8a16_gemv_kernel(
     gemv_x_store<kU>(x_lds, xr);
     __syncthreads();
 
-    float acc[kR];
-#pragma unroll
-    for (int r = 0; r < kR; ++r) acc[r] = 0.0f;
+    float acc = 0.0f;
 #pragma unroll
     for (int c = 0; c < kC; ++c) {
         // Lane l's 16 activations of chunk c: bytes 2048 c + 32 l .. + 31.
         // Chunks past K hold zeros only (weights and token), so they add
         // nothing and need no branch.
         const i32x4 xv[2] = {gemv_x_read(x_lds, 128 * c + 2 * lane), gemv_x_read(x_lds, 128 * c + 2 * lane + 1)};
-#pragma unroll
-        for (int r = 0; r < kR; ++r)
-            acc[r] = __builtin_fmaf(block_sum8(lane_dot16<kXBf16>(pairs(xv), wv[c][r])), wsv[c], acc[r]);
+        acc = __builtin_fmaf(block_sum8(lane_dot16<kXBf16>(pairs(xv), wv[c])), wsv[c], acc);
     }
-#pragma unroll
-    for (int r = 0; r < kR; ++r) {
-        const float v = group_sum8(acc[r]);
-        if (lane == 0 && r < rows) store_out(y, y_dtype, n0 + r, v);
-    }
+    const float v = group_sum8(acc);
+    if (lane == 0 && live) store_out(y, y_dtype, n, v);
 }
 
 // Block-32 UE8M0 weights, one token ([SM70] "How it works": a GEMV for the
 // fewest tokens): the one-token layout above with fp16 activations.  A
 // lane's 16 weights of a chunk lie in one 32-wide K tile (16 divides 32), so
-// they share one scale 2^e: the lane's 16 products of exact fp32 values
-// (E4M3 widened, fp16 widened) are summed in fp32 and multiplied once by
-// 2^e, which is exact; the lane totals are summed over the wave in one fixed
-// order.  The scale byte E (e = E - 127) of lane l in chunk c is
+// they share one scale 2^e, which the conversion applies: each weight
+// becomes the fp16 number value * 2^e exactly, the lane's 16 products (each
+// exact in fp32) are summed by v_dot2c, and the lane totals over the wave in
+// one fixed order.  The scale byte E (e = E - 127) of lane l in chunk c is
 // e8m0[n / 32, 32 c + l / 2].
-template <int kR, int kC>
+template <int kC>
 __global__ __launch_bounds__(kGemvThreads) void w8a16_blk32_gemv_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq, const uint8_t* __restrict__ e8m0,
     void* __restrict__ y, int y_dtype, int64_t N, int64_t K) {
     constexpr int kU = kC / 4;
     __shared__ __attribute__((aligned(16))) uint8_t x_lds[2048 * kC];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
-    const int64_t n0 = ((int64_t)blockIdx.x * kGemvWaves + wave) * kR;   // wave-uniform: scalar descriptors
-    const int64_t rows = n0 >= N ? 0 : N - n0 < kR ? N - n0 : kR;     // as in w8a16_gemv_kernel
-    const int64_t nb = rows > 0 ? n0 : 0;
+    const int64_t n = (int64_t)blockIdx.x * kGemvWaves + wave;   // wave-uniform: scalar descriptors
+    const bool live = n < N;                                      // as in w8a16_gemv_kernel
+    const int64_t nb = live ? n : 0;
     const int K32 = (int)(K / 32);
-    const int w_bytes = (int)(rows * K);
-    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void*)(wq + nb * K), 0, w_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rw =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(wq + nb * K), 0, live ? (int)K : 0, 0x00020000);
     const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)x, 0, (int)(2 * K), 0x00020000);
-    // The kR rows lie in one 32-row scale tile (kR divides 32 and n0 is a multiple of kR).
     const __amdgpu_buffer_rsrc_t re =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(e8m0 + (nb / 32) * K32), 0, rows > 0 ? K32 : 0, 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc((void*)(e8m0 + (nb / 32) * K32), 0, live ? K32 : 0, 0x00020000);
 
-    i32x4 xr[kU], wv[kC][kR];
+    i32x4 xr[kU], wv[kC];
     uint32_t eb[kC];
     gemv_x_issue<kU>(rx, xr);
 #pragma unroll
@@ -617,54 +605,41 @@ __global__ __launch_bounds__(kGemvThreads) void w8a16_blk32_gemv_kernel(
 #pragma unroll
     for (int c = 0; c < kC; ++c) {
         const int k = 1024 * c + 16 * lane;
-#pragma unroll
-        for (int r = 0; r < kR; ++r) {
-            const int off = k < K ? (int)(r * K) + k : w_bytes;
-            wv[c][r] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, 0));
-        }
+        wv[c] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, k < K ? k : (int)K, 0, 0));
     }
     __builtin_amdgcn_sched_barrier(0);   // every load ahead of the token copy and the arithmetic
     gemv_x_store<kU>(x_lds, xr);
     __syncthreads();
 
-    float acc[kR];
-#pragma unroll
-    for (int r = 0; r < kR; ++r) acc[r] = 0.0f;
+    float acc = 0.0f;
 #pragma unroll
     for (int c = 0; c < kC; ++c) {
         const i32x4 xv[2] = {gemv_x_read(x_lds, 128 * c + 2 * lane), gemv_x_read(x_lds, 128 * c + 2 * lane + 1)};
         // 2^(E - 127) (E in [113, 134]) goes into the widening: each weight
         // becomes the fp16 number value * 2^e exactly.  Lanes past K read
         // E = 0 and zero weights, which widen to zeros.
-        const float scale = ue8m0_scale(eb[c]);
-#pragma unroll
-        for (int r = 0; r < kR; ++r) acc[r] += lane_dot16<false>(pairs(xv), wv[c][r], scale);
+        acc += lane_dot16<false>(pairs(xv), wv[c], ue8m0_scale(eb[c]));
     }
-#pragma unroll
-    for (int r = 0; r < kR; ++r) {
-        const float v = wave_sum(acc[r]);
-        if (lane == 0 && r < rows) store_out(y, y_dtype, n0 + r, v);
-    }
+    const float v = wave_sum(acc);
+    if (lane == 0 && live) store_out(y, y_dtype, n, v);
 }
 
 hipError_t launch_w8a16_gemv(const void* x, bool x_bf16, const uint8_t* wq, const float* ws, void* y, int y_dtype,
                              int64_t N, int64_t K, hipStream_t stream) {
     if (N % 16 != 0 || K > kGemvMaxK) return hipErrorInvalidValue;
-    constexpr int kr = kGemvRowsPerWave;
-    const dim3 grid((unsigned)((N + kGemvWaves * kr - 1) / (kGemvWaves * kr)));
+    const dim3 grid((unsigned)((N + kGemvWaves - 1) / kGemvWaves));
     const uint16_t* xh = static_cast<const uint16_t*>(x);
-#define BFP8_LAUNCH_GEMV(B, R, C)                                                                              \
-    hipLaunchKernelGGL((w8a16_gemv_kernel<B, R, C>), grid, dim3(kGemvThreads), 0, stream, xh, wq, ws, y, \
-                       y_dtype, N, K)
-#define BFP8_LAUNCH_GEMV_C(B, R)                    \
-    switch (gemv_chunks(K)) {                        \
-        case 4: BFP8_LAUNCH_GEMV(B, R, 4); break;   \
-        case 8: BFP8_LAUNCH_GEMV(B, R, 8); break;   \
-        case 12: BFP8_LAUNCH_GEMV(B, R, 12); break; \
-        default: BFP8_LAUNCH_GEMV(B, R, 16); break; \
+#define BFP8_LAUNCH_GEMV(B, C)                                                                                    \
+    hipLaunchKernelGGL((w8a16_gemv_kernel<B, C>), grid, dim3(kGemvThreads), 0, stream, xh, wq, ws, y, y_dtype, N, K)
+#define BFP8_LAUNCH_GEMV_C(B)                    \
+    switch (gemv_chunks(K)) {                     \
+        case 4: BFP8_LAUNCH_GEMV(B, 4); break;   \
+        case 8: BFP8_LAUNCH_GEMV(B, 8); break;   \
+        case 12: BFP8_LAUNCH_GEMV(B, 12); break; \
+        default: BFP8_LAUNCH_GEMV(B, 16); break; \
     }
-    if (x_bf16) { BFP8_LAUNCH_GEMV_C(true, kr) }
-    else { BFP8_LAUNCH_GEMV_C(false, kr) }
+    if (x_bf16) { BFP8_LAUNCH_GEMV_C(true) }
+    else { BFP8_LAUNCH_GEMV_C(false) }
 #undef BFP8_LAUNCH_GEMV_C
 #undef BFP8_LAUNCH_GEMV
     return hipGetLastError();
@@ -673,21 +648,17 @@ hipError_t launch_w8a16_gemv(const void* x, bool x_bf16, const uint8_t* wq, cons
 hipError_t launch_w8a16_blk32_gemv(const void* x, const uint8_t* wq, const uint8_t* e8m0, void* y, int y_dtype,
                                    int64_t N, int64_t K, hipStream_t stream) {
     if (N % 32 != 0 || K > kGemvMaxK) return hipErrorInvalidValue;
-    constexpr int kr = kGemvRowsPerWave;
-    const dim3 grid((unsigned)((N + kGemvWaves * kr - 1) / (kGemvWaves * kr)));
+    const dim3 grid((unsigned)((N + kGemvWaves - 1) / kGemvWaves));
     const uint16_t* xh = static_cast<const uint16_t*>(x);
-#define BFP8_LAUNCH_GEMV32(R, C)                                                                                    \
-    hipLaunchKernelGGL((w8a16_blk32_gemv_kernel<R, C>), grid, dim3(kGemvThreads), 0, stream, xh, wq, e8m0, y, \
-                       y_dtype, N, K)
-#define BFP8_LAUNCH_GEMV32_C(R)                    \
-    switch (gemv_chunks(K)) {                       \
-        case 4: BFP8_LAUNCH_GEMV32(R, 4); break;   \
-        case 8: BFP8_LAUNCH_GEMV32(R, 8); break;   \
-        case 12: BFP8_LAUNCH_GEMV32(R, 12); break; \
-        default: BFP8_LAUNCH_GEMV32(R, 16); break; \
+#define BFP8_LAUNCH_GEMV32(C)                                                                                    \
+    hipLaunchKernelGGL((w8a16_blk32_gemv_kernel<C>), grid, dim3(kGemvThreads), 0, stream, xh, wq, e8m0, y, y_dtype, \
+                       N, K)
+    switch (gemv_chunks(K)) {
+        case 4: BFP8_LAUNCH_GEMV32(4); break;
+        case 8: BFP8_LAUNCH_GEMV32(8); break;
+        case 12: BFP8_LAUNCH_GEMV32(12); break;
+        default: BFP8_LAUNCH_GEMV32(16); break;
     }
-    BFP8_LAUNCH_GEMV32_C(kr)
-#undef BFP8_LAUNCH_GEMV32_C
 #undef BFP8_LAUNCH_GEMV32
     return hipGetLastError();
 }

@@ -556,77 +556,69 @@ hipError_t launch_w8a8_wide(const uint8_t* xq, const float* xs, const uint8_t* w
 // ------------------------------------------------ W8A8 GEMV, M = 1 ----
 // One token with K <= 16384 (batch-1 decode): the dot products run on the
 // vector ALUs, laid out as in the W8A16 one-token kernel (stream_common.hpp:
-// lane l covers K offsets 1024 c + 16 l of every 1 KB chunk c of its weight
-// rows, kC chunks).  Each lane widens its 16 activation codes (once per
-// chunk, for all of its rows) and 16 weight codes to bf16 (exact), sums the
-// 16 products with v_dot2c (lane_dot16: a product of two E4M3 values is
+// one weight row per wave, lane l covering K offsets 1024 c + 16 l of every
+// 1 KB chunk c, kC chunks; the token's codes shared through LDS).  Each lane
+// widens its 16 activation codes and 16 weight codes to bf16 (exact), sums
+// the 16 products with v_dot2c (lane_dot16: a product of two E4M3 values is
 // exact in fp32), block_sum8 gives the 128-K block's dot product to the 8
 // lanes of the block, and the block is promoted once with
 // xs[kb] * ws[n / 128, kb] ([ADA] "The fix"; [ARC] "What this adds").  All
-// loads are issued before the first product; there is no LDS and no
-// barrier.  gemv_rows is that arithmetic; the kernel that quantises its own
-// activations calls it too, so the fused call and quantise-then-GEMM give
-// the same bits.
-template <int kR, int kC>
-__device__ __forceinline__ void gemv_rows(const uint32_t (&xp)[kC][8], const float (&sx)[kC],
-                                          const i32x4 (&wv)[kC][kR], const float (&wsv)[kC], float (&acc)[kR]) {
+// loads are issued before the first product.  gemv_row is that arithmetic;
+// the kernel that quantises its own activations calls it too, so the fused
+// call and quantise-then-GEMM give the same bits.
+template <int kC>
+__device__ __forceinline__ float gemv_row(const uint32_t (&xp)[kC][8], const float (&sx)[kC], const i32x4 (&wv)[kC],
+                                          const float (&wsv)[kC]) {
+    float acc = 0.0f;
 #pragma unroll
-    for (int r = 0; r < kR; ++r) acc[r] = 0.0f;
-#pragma unroll
-    for (int c = 0; c < kC; ++c) {
-        const float sc = sx[c] * wsv[c];
-#pragma unroll
-        for (int r = 0; r < kR; ++r) acc[r] = __builtin_fmaf(block_sum8(lane_dot16<true>(xp[c], wv[c][r])), sc, acc[r]);
-    }
-#pragma unroll
-    for (int r = 0; r < kR; ++r) acc[r] = group_sum8(acc[r]);
+    for (int c = 0; c < kC; ++c)
+        acc = __builtin_fmaf(block_sum8(lane_dot16<true>(xp[c], wv[c])), sx[c] * wsv[c], acc);
+    return group_sum8(acc);
 }
 
-// Issue the loads of the kR weight rows from row n0 and of their weight
-// scales, chunk by chunk; lanes past K read zeros.
-template <int kR, int kC>
-__device__ __forceinline__ void gemv_load_weights(const uint8_t* wq, const float* ws, int64_t n0, int64_t rows,
-                                                  int64_t K, int lane, i32x4 (&wv)[kC][kR], float (&wsv)[kC]) {
+// Issue the loads of weight row n (when `live`) and of its weight scales,
+// chunk by chunk; lanes past K, and every lane of a row that is not live,
+// read zeros.
+template <int kC>
+__device__ __forceinline__ void gemv_load_weights(const uint8_t* wq, const float* ws, int64_t n, bool live, int64_t K,
+                                                  int lane, i32x4 (&wv)[kC], float (&wsv)[kC]) {
     const int KB = (int)(K / 128);
-    const int w_bytes = (int)(rows * K);
-    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void*)(wq + n0 * K), 0, w_bytes, 0x00020000);
+    const int64_t nb = live ? n : 0;
+    const __amdgpu_buffer_rsrc_t rw =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(wq + nb * K), 0, live ? (int)K : 0, 0x00020000);
     const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(ws + (n0 / 128) * KB), 0, KB * 4, 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc((void*)(ws + (nb / 128) * KB), 0, live ? KB * 4 : 0, 0x00020000);
 #pragma unroll
     for (int c = 0; c < kC; ++c)
         wsv[c] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * ((1024 * c + 16 * lane) / 128), 0, 0));
 #pragma unroll
     for (int c = 0; c < kC; ++c) {
         const int k = 1024 * c + 16 * lane;
-#pragma unroll
-        for (int r = 0; r < kR; ++r) {
-            const int off = k < K ? (int)(r * K) + k : w_bytes;
-            wv[c][r] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, 0));
-        }
+        wv[c] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, k < K ? k : (int)K, 0, 0));
     }
 }
 
-template <int kR, int kC>
+template <int kC>
 __global__ __launch_bounds__(kGemvThreads) void w8a8_gemv_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ xs, const uint8_t* __restrict__ wq,
     const float* __restrict__ ws, void* __restrict__ y, int y_dtype, int64_t N, int64_t K) {
     constexpr int kU = (kC + 7) / 8;   // 8 KB rounds of the token's codes (1 KB per chunk)
     __shared__ __attribute__((aligned(16))) uint8_t x_lds[8192 * kU];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
-    const int64_t n0 = ((int64_t)blockIdx.x * kGemvWaves + wave) * kR;   // wave-uniform: scalar descriptors
+    const int64_t n = (int64_t)blockIdx.x * kGemvWaves + wave;   // wave-uniform: scalar descriptors
     // The launch covers N exactly (N % 16 == 0); a wave past N would still
     // take part in the token copy and the barrier, reading no weights.
-    const int64_t rows = n0 >= N ? 0 : N - n0 < kR ? N - n0 : kR;
+    const bool live = n < N;
     const int KB = (int)(K / 128);
     const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)xq, 0, (int)K, 0x00020000);
     const __amdgpu_buffer_rsrc_t rxs = __builtin_amdgcn_make_buffer_rsrc((void*)xs, 0, KB * 4, 0x00020000);
-    i32x4 xr[kU], wv[kC][kR];
+    i32x4 xr[kU], wv[kC];
     float sx[kC], wsv[kC];
     gemv_x_issue<kU>(rx, xr);
 #pragma unroll
     for (int c = 0; c < kC; ++c)
         sx[c] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rxs, 4 * ((1024 * c + 16 * lane) / 128), 0, 0));
-    gemv_load_weights<kR, kC>(wq, ws, rows > 0 ? n0 : 0, rows, K, lane, wv, wsv);
+    gemv_load_weights<kC>(wq, ws, n, live, K, lane, wv, wsv);
     // Keep every load ahead of the token copy and the arithmetic: the
     // scheduler would otherwise sink the later chunks' loads below the
     // first chunk's products.
@@ -636,21 +628,19 @@ __global__ __launch_bounds__(kGemvThreads) void w8a8_gemv_kernel(
     uint32_t xp[kC][8];
 #pragma unroll
     for (int c = 0; c < kC; ++c) e4m3x16_to_bf16x2(gemv_x_read(x_lds, 64 * c + lane), xp[c]);
-    float acc[kR];
-    gemv_rows<kR, kC>(xp, sx, wv, wsv, acc);
-#pragma unroll
-    for (int r = 0; r < kR; ++r)
-        if (lane == 0 && r < rows) store_out(y, y_dtype, n0 + r, acc[r]);
+    const float v = gemv_row<kC>(xp, sx, wv, wsv);
+    if (lane == 0 && live) store_out(y, y_dtype, n, v);
 }
 
 // The same product from 16-bit activations, quantised once per workgroup:
 // kW waves, one weight row each.  The token is quantised in rounds of 4096
-// values: in round t, wave w quantises activations 4096 t + 1024 w ..
-// + 1023, V = 16 consecutive values per lane, so a 1x128 group spans 8
-// lanes; their maximum (lane moves), scale amax / 448 and codes
+// values: in round t, wave w quantises activations 4096 t + (4096 / kW) w
+// .. + 4096 / kW - 1, V = 4096 / (64 kW) consecutive values per lane (8 with
+// eight waves), so a 1x128 group spans 128 / V lanes; their maximum (lane
+// moves), scale amax / 448 and codes
 // (quantize_v, the quantiser's own arithmetic) equal bfp8_quantize_act_1x128's
 // bit for bit.  Codes and scales go to LDS; after one barrier every wave
-// reads back its lanes' 16 codes per chunk and runs gemv_rows.  The weight
+// reads back its lanes' 16 codes per chunk and runs gemv_row.  The weight
 // loads are issued first, so the quantisation runs while they stream.
 template <bool kXBf16, int kW, int kC>
 __global__ __launch_bounds__(kW * kWave) void w8a8_gemv_quant_kernel(
@@ -686,9 +676,9 @@ __global__ __launch_bounds__(kW * kWave) void w8a8_gemv_quant_kernel(
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    i32x4 wv[kC][1];
+    i32x4 wv[kC];
     float wsv[kC];
-    gemv_load_weights<1, kC>(wq, ws, n0, 1, K, lane, wv, wsv);
+    gemv_load_weights<kC>(wq, ws, n0, true, K, lane, wv, wsv);
     __builtin_amdgcn_sched_barrier(0);   // keep the weight loads ahead of the quantisation
 
 #pragma unroll
@@ -723,29 +713,23 @@ __global__ __launch_bounds__(kW * kWave) void w8a8_gemv_quant_kernel(
         // stale value enters the promotion.
         sx[c] = k < K ? scale_lds[k / 128] : 0.0f;
     }
-    float acc[1];
-    gemv_rows<1, kC>(xp, sx, wv, wsv, acc);
-    if (lane == 0) store_out(y, y_dtype, n0, acc[0]);
+    const float v = gemv_row<kC>(xp, sx, wv, wsv);
+    if (lane == 0) store_out(y, y_dtype, n0, v);
 }
 
 hipError_t launch_w8a8_gemv(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws, void* y,
                             int y_dtype, int64_t N, int64_t K, hipStream_t stream) {
     if (N % 16 != 0 || K > kGemvMaxK) return hipErrorInvalidValue;
     static_assert(kGemvWaves == kGemvLaunchWaves, "plan and launch agree");
-    constexpr int kr = kGemvRowsPerWave;
-    const dim3 grid((unsigned)((N + kGemvWaves * kr - 1) / (kGemvWaves * kr)));
-#define BFP8_LAUNCH_GEMV8(R, C)                                                                                    \
-    hipLaunchKernelGGL((w8a8_gemv_kernel<R, C>), grid, dim3(kGemvThreads), 0, stream, xq, xs, wq, ws, y, \
-                       y_dtype, N, K)
-#define BFP8_LAUNCH_GEMV8_C(R)                    \
-    switch (gemv_chunks(K)) {                      \
-        case 4: BFP8_LAUNCH_GEMV8(R, 4); break;   \
-        case 8: BFP8_LAUNCH_GEMV8(R, 8); break;   \
-        case 12: BFP8_LAUNCH_GEMV8(R, 12); break; \
-        default: BFP8_LAUNCH_GEMV8(R, 16); break; \
+    const dim3 grid((unsigned)((N + kGemvWaves - 1) / kGemvWaves));
+#define BFP8_LAUNCH_GEMV8(C)                                                                                    \
+    hipLaunchKernelGGL((w8a8_gemv_kernel<C>), grid, dim3(kGemvThreads), 0, stream, xq, xs, wq, ws, y, y_dtype, N, K)
+    switch (gemv_chunks(K)) {
+        case 4: BFP8_LAUNCH_GEMV8(4); break;
+        case 8: BFP8_LAUNCH_GEMV8(8); break;
+        case 12: BFP8_LAUNCH_GEMV8(12); break;
+        default: BFP8_LAUNCH_GEMV8(16); break;
     }
-    BFP8_LAUNCH_GEMV8_C(kr)
-#undef BFP8_LAUNCH_GEMV8_C
 #undef BFP8_LAUNCH_GEMV8
     return hipGetLastError();
 }
