@@ -19,8 +19,8 @@
 // sees exactly the weights of a load-time fp16 dequantisation and
 // accumulates in fp32 across all K.
 //
-// M = 1 with K <= 4096 runs a plain dot-product kernel on the vector ALUs
-// (w8a16_gemv_kernel below).  The other kernels here stream the weights like
+// M = 1 with K <= 12288 (block-32: 8192) runs a plain dot-product kernel on
+// the vector ALUs (w8a16_gemv_kernel, w8a16_blk32_gemv_kernel below).  The other kernels here stream the weights like
 // the W8A8 decode kernel: one
 // workgroup per 16 weight rows (and per split of K), 16 tokens on the MFMA
 // column axis, sixteen waves taking interleaved 128-K blocks.  W8A16 blk128
@@ -497,25 +497,24 @@ hipError_t launch_w8a16_wide(const void* x, bool x_bf16, const uint8_t* wq, cons
 }
 
 // ------------------------------------------------ W8A16 GEMV, M = 1 ----
-// One token (batch-1 decode) with K <= 4096 needs no matrix core: the work
-// is one dot product per weight row.  A wave owns kR weight rows.  Lane l
-// takes, in each 1 KB chunk c of a row, the 16 weight bytes at K offset
+// One token (batch-1 decode) needs no matrix core: the work is one dot
+// product per weight row.  A wave owns one weight row.  Lane l takes, in
+// each 1 KB chunk c of the row, the 16 weight bytes at K offset
 // 1024 c + 16 l (one load instruction covers 8 whole 128-byte lines) and the
 // 16 matching activations, widens the E4M3 weights to the activations'
 // 16-bit type (exact) and sums the 16 products with v_dot2c (lane_dot16).
-// Lanes 8 j ..
-// 8 j + 7 hold 128-K block 8 c + j: three lane exchanges give every one of
-// them the block's dot product, which is promoted once with the block's
-// weight scale (the per-block promotion of [ARC] "What this adds", here
-// without a matrix instruction).  The eight lane groups' promoted
-// sums are added at the end (three more exchanges) and lane 0 stores the
-// row.  Every load is issued before the first product; there is no LDS
-// staging and no barrier, so the cross-wave reduction of the streaming
-// kernel, about half a microsecond of a 5.7 us launch at N = K = 4096, is
-// gone (measured 5.33-5.42 vs 5.69 us there, 3.00 vs 3.96 us at N = 1024
-// and 11.1 vs 11.5 us at N = 12288).  The lane sums use DPP lane moves
-// (block_sum8, group_sum8).  Lanes past K read zeros (their offsets are
-// moved past the descriptor's range).
+// Lanes 8 j .. 8 j + 7 hold 128-K block 8 c + j: three lane exchanges give
+// every one of them the block's dot product, which is promoted once with
+// the block's weight scale (the per-block promotion of [ARC] "What this
+// adds", here without a matrix instruction).  The eight lane groups'
+// promoted sums are added at the end (three more exchanges, inside the ALU)
+// and lane 0 stores the row.  Every load is issued before the first product
+// and the token is shared through LDS (stream_common.hpp); there is no
+// cross-wave reduction, which costs the streaming kernel about half a
+// microsecond of a 5.7 us launch at N = K = 4096 (the first, four-wave form
+// of this kernel measured 5.33-5.42 vs 5.69 us there, 3.00 vs 3.96 us at
+// N = 1024 and 11.1 vs 11.5 us at N = 12288).  Lanes past K read zeros
+// (their offsets are moved past the descriptor's range).
 
 // A lane's 16 activations of a chunk (two 16-byte loads) as 8 pairs.
 __device__ __forceinline__ const uint32_t (&pairs(const i32x4 (&x)[2]))[8] {

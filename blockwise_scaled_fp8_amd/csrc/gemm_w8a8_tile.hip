@@ -25,11 +25,11 @@
 // (lanes 16g..16g+15) takes chunks g and g + 4 of the row, the same for both
 // operands, so the contraction is over the same 128 K values.
 //
-// Tile shapes ([ADA] "One tile doesn't fit all M"): 256x256, 256x128 or
-// 128x128 by estimated time (plan_tile) among those that occupy most CUs;
-// below that, for long K 128x128 with four waves and K split 2 or 4 ways,
-// else 64x128 (or 128x64 for M <= 64) with K split over several
-// workgroups so that about one workgroup per CU exists.  Split partial tiles go to the
+// Tile shapes ([ADA] "One tile doesn't fit all M"): 256x256, 256x128,
+// 128x128, 64x128 and 128x64, the last three with K optionally split over
+// several workgroups; plan_tile picks the shape and split with the least
+// estimated time (a cost model fitted to measured per-block and hand-off
+// times).  Split partial tiles go to the
 // workspace in fp32 and the last workgroup of a tile sums them in split
 // order (no float atomics, identical from run to run), with the same
 // fence-free hand-off as the streaming kernels.
