@@ -142,6 +142,7 @@ __global__ __launch_bounds__(kStreamThreads) void w8a16_blk128_stream_lds_kernel
     __shared__ __attribute__((aligned(1024))) uint8_t wslab[kStreamWaves][kW8A16LdsChunk][kSlabBytes];
     float* red = slab_scratch(&wslab[0][0][0]);   // used after the last block only
     const int64_t nt = blockIdx.x, split = blockIdx.y;
+    const bool nt_loads = weights_nt(N, K);   // M <= 16: one token tile, no other workgroup reads these weights
     const int64_t KB = K / 128;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
     const int r = lane & 15, g = lane >> 4;
@@ -185,7 +186,7 @@ __global__ __launch_bounds__(kStreamThreads) void w8a16_blk128_stream_lds_kernel
 #pragma unroll
         for (int c = 0; c < kW8A16LdsChunk; ++c) {
             const int64_t kb = kb0 + c * kStreamWaves;
-            if (kb < kb_end) slab_issue(wslab[wave][c], rsrc_w, lane_off_w, K, kb);
+            if (kb < kb_end) slab_issue(wslab[wave][c], rsrc_w, lane_off_w, K, kb, nt_loads);
         }
         const bool two = kb0 + kStreamWaves < kb_end;     // wave-uniform
 #pragma unroll
@@ -238,6 +239,7 @@ __global__ __launch_bounds__(kStreamThreads) void w8a16_blk32_stream_lds_kernel(
     __shared__ __attribute__((aligned(1024))) uint8_t wslab[kStreamWaves][kW8A16LdsChunk][kSlabBytes];
     float* red = slab_scratch(&wslab[0][0][0]);   // used after the last block only
     const int64_t nt = blockIdx.x, split = blockIdx.y;
+    const bool nt_loads = weights_nt(N, K);   // M <= 16: one token tile, no other workgroup reads these weights
     const int64_t KB = K / 128, K32 = K / 32;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
     const int r = lane & 15, g = lane >> 4;
@@ -282,7 +284,7 @@ __global__ __launch_bounds__(kStreamThreads) void w8a16_blk32_stream_lds_kernel(
 #pragma unroll
         for (int c = 0; c < kW8A16LdsChunk; ++c) {
             const int64_t kb = kb0 + c * kStreamWaves;
-            if (kb < kb_end) slab_issue(wslab[wave][c], rsrc_w, lane_off_w, K, kb);
+            if (kb < kb_end) slab_issue(wslab[wave][c], rsrc_w, lane_off_w, K, kb, nt_loads);
         }
         const bool two = kb0 + kStreamWaves < kb_end;     // wave-uniform
 #pragma unroll
@@ -521,7 +523,7 @@ __device__ __forceinline__ const uint32_t (&pairs(const i32x4 (&x)[2]))[8] {
     return *reinterpret_cast<const uint32_t(*)[8]>(&x[0]);
 }
 
-template <bool kXBf16, int kC>
+template <bool kXBf16, int kC, int kPol>
 __global__ __launch_bounds__(kGemvThreads) void w8a16_gemv_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq, const float* __restrict__ ws,
     void* __restrict__ y, int y_dtype, int64_t N, int64_t K) {
@@ -549,7 +551,7 @@ __global__ __launch_bounds__(kGemvThreads) void w8a16_gemv_kernel(
 #pragma unroll
     for (int c = 0; c < kC; ++c) {
         const int k = 1024 * c + 16 * lane;
-        wv[c] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, k < K ? k : (int)K, 0, 0));
+        wv[c] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, k < K ? k : (int)K, 0, kPol));
     }
     // Keep every load ahead of the token copy and the arithmetic: the
     // scheduler would otherwise sink the later chunks' loads below the
@@ -579,7 +581,7 @@ __global__ __launch_bounds__(kGemvThreads) void w8a16_gemv_kernel(
 // exact in fp32) are summed by v_dot2c, and the lane totals over the wave in
 // one fixed order.  The scale byte E (e = E - 127) of lane l in chunk c is
 // e8m0[n / 32, 32 c + l / 2].
-template <int kC>
+template <int kC, int kPol>
 __global__ __launch_bounds__(kGemvThreads) void w8a16_blk32_gemv_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq, const uint8_t* __restrict__ e8m0,
     void* __restrict__ y, int y_dtype, int64_t N, int64_t K) {
@@ -604,7 +606,7 @@ __global__ __launch_bounds__(kGemvThreads) void w8a16_blk32_gemv_kernel(
 #pragma unroll
     for (int c = 0; c < kC; ++c) {
         const int k = 1024 * c + 16 * lane;
-        wv[c] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, k < K ? k : (int)K, 0, 0));
+        wv[c] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, k < K ? k : (int)K, 0, kPol));
     }
     __builtin_amdgcn_sched_barrier(0);   // every load ahead of the token copy and the arithmetic
     gemv_x_store<kU>(x_lds, xr);
@@ -628,17 +630,23 @@ hipError_t launch_w8a16_gemv(const void* x, bool x_bf16, const uint8_t* wq, cons
     if (N % 16 != 0 || K > kGemvMaxK) return hipErrorInvalidValue;
     const dim3 grid((unsigned)((N + kGemvWaves - 1) / kGemvWaves));
     const uint16_t* xh = static_cast<const uint16_t*>(x);
-#define BFP8_LAUNCH_GEMV(B, C)                                                                                    \
-    hipLaunchKernelGGL((w8a16_gemv_kernel<B, C>), grid, dim3(kGemvThreads), 0, stream, xh, wq, ws, y, y_dtype, N, K)
-#define BFP8_LAUNCH_GEMV_C(B)                    \
-    switch (gemv_chunks(K)) {                     \
-        case 4: BFP8_LAUNCH_GEMV(B, 4); break;   \
-        case 8: BFP8_LAUNCH_GEMV(B, 8); break;   \
-        case 12: BFP8_LAUNCH_GEMV(B, 12); break; \
-        default: BFP8_LAUNCH_GEMV(B, 16); break; \
+#define BFP8_LAUNCH_GEMV(B, C, P)                                                                                  \
+    hipLaunchKernelGGL((w8a16_gemv_kernel<B, C, P>), grid, dim3(kGemvThreads), 0, stream, xh, wq, ws, y, y_dtype, N, K)
+#define BFP8_LAUNCH_GEMV_C(B, P)                    \
+    switch (gemv_chunks(K)) {                        \
+        case 4: BFP8_LAUNCH_GEMV(B, 4, P); break;   \
+        case 8: BFP8_LAUNCH_GEMV(B, 8, P); break;   \
+        case 12: BFP8_LAUNCH_GEMV(B, 12, P); break; \
+        default: BFP8_LAUNCH_GEMV(B, 16, P); break; \
     }
-    if (x_bf16) { BFP8_LAUNCH_GEMV_C(true) }
-    else { BFP8_LAUNCH_GEMV_C(false) }
+    const bool nt = weights_nt(N, K);
+    if (x_bf16) {
+        if (nt) { BFP8_LAUNCH_GEMV_C(true, kLoadNt) }
+        else { BFP8_LAUNCH_GEMV_C(true, 0) }
+    } else {
+        if (nt) { BFP8_LAUNCH_GEMV_C(false, kLoadNt) }
+        else { BFP8_LAUNCH_GEMV_C(false, 0) }
+    }
 #undef BFP8_LAUNCH_GEMV_C
 #undef BFP8_LAUNCH_GEMV
     return hipGetLastError();
@@ -649,15 +657,19 @@ hipError_t launch_w8a16_blk32_gemv(const void* x, const uint8_t* wq, const uint8
     if (N % 32 != 0 || K > kGemvMaxK) return hipErrorInvalidValue;
     const dim3 grid((unsigned)((N + kGemvWaves - 1) / kGemvWaves));
     const uint16_t* xh = static_cast<const uint16_t*>(x);
-#define BFP8_LAUNCH_GEMV32(C)                                                                                    \
-    hipLaunchKernelGGL((w8a16_blk32_gemv_kernel<C>), grid, dim3(kGemvThreads), 0, stream, xh, wq, e8m0, y, y_dtype, \
-                       N, K)
-    switch (gemv_chunks(K)) {
-        case 4: BFP8_LAUNCH_GEMV32(4); break;
-        case 8: BFP8_LAUNCH_GEMV32(8); break;
-        case 12: BFP8_LAUNCH_GEMV32(12); break;
-        default: BFP8_LAUNCH_GEMV32(16); break;
+#define BFP8_LAUNCH_GEMV32(C, P)                                                                                  \
+    hipLaunchKernelGGL((w8a16_blk32_gemv_kernel<C, P>), grid, dim3(kGemvThreads), 0, stream, xh, wq, e8m0, y,        \
+                       y_dtype, N, K)
+#define BFP8_LAUNCH_GEMV32_C(P)                    \
+    switch (gemv_chunks(K)) {                       \
+        case 4: BFP8_LAUNCH_GEMV32(4, P); break;   \
+        case 8: BFP8_LAUNCH_GEMV32(8, P); break;   \
+        case 12: BFP8_LAUNCH_GEMV32(12, P); break; \
+        default: BFP8_LAUNCH_GEMV32(16, P); break; \
     }
+    if (weights_nt(N, K)) { BFP8_LAUNCH_GEMV32_C(kLoadNt) }
+    else { BFP8_LAUNCH_GEMV32_C(0) }
+#undef BFP8_LAUNCH_GEMV32_C
 #undef BFP8_LAUNCH_GEMV32
     return hipGetLastError();
 }

@@ -110,9 +110,12 @@ __global__ __launch_bounds__(kStreamThreads) void w8a8_stream_lds_kernel(
     __shared__ __attribute__((aligned(1024))) uint8_t xrows[kStreamWaves][kCodesLdsChunk][kRowsBytes];
     __shared__ __attribute__((aligned(1024))) uint8_t wslab[kStreamWaves][kCodesLdsChunk][kSlabBytes];
     float* red = slab_scratch(&wslab[0][0][0]);   // used after the last block only
-    // Token tile mt = blockIdx.z: tokens m0 .. m0 + Mt - 1.
+    // Token tile mt = blockIdx.z: tokens m0 .. m0 + Mt - 1.  With one token
+    // tile no other workgroup reads these weights: non-temporal loads when
+    // they are large enough (weights_nt).
     const int64_t nt = blockIdx.x, split = blockIdx.y, mt = blockIdx.z;
     const int64_t m0 = 16 * mt, Mt = M - m0 < 16 ? M - m0 : 16;
+    const bool nt_loads = gridDim.z == 1 && weights_nt(N, K);
     const int64_t KB = K / 128;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
     const int r = lane & 15, g = lane >> 4;
@@ -148,7 +151,7 @@ __global__ __launch_bounds__(kStreamThreads) void w8a8_stream_lds_kernel(
 #pragma unroll
         for (int c = 0; c < kCodesLdsChunk; ++c) {
             const int64_t kb = kb0 + c * kStreamWaves;
-            if (kb < kb_end) slab_issue(wslab[wave][c], rsrc_w, lane_off_w, K, kb);
+            if (kb < kb_end) slab_issue(wslab[wave][c], rsrc_w, lane_off_w, K, kb, nt_loads);
         }
         const bool two = kb0 + kStreamWaves < kb_end;     // wave-uniform
 #pragma unroll
@@ -272,6 +275,7 @@ __global__ __launch_bounds__(kStreamThreads) void w8a8_stream_quant_kernel(
     __shared__ __attribute__((aligned(1024))) uint8_t wslab[kStreamWaves][kFusedChunk][kSlabBytes];
     float* red = slab_scratch(&wslab[0][0][0]);   // used after the last block only
     const int64_t nt = blockIdx.x, split = blockIdx.y;
+    const bool nt_loads = weights_nt(N, K);   // M <= 8: one token tile, no other workgroup reads these weights
     const int64_t KB = K / 128;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
     const int r = lane & 15, g = lane >> 4;
@@ -309,7 +313,7 @@ __global__ __launch_bounds__(kStreamThreads) void w8a8_stream_quant_kernel(
 #pragma unroll
         for (int c = 0; c < kFusedChunk; ++c) {
             const int64_t kb = kb0 + c * kStreamWaves;
-            if (kb < kb_end) slab_issue(wslab[wave][c], rsrc_w, lane_off_w, K, kb);
+            if (kb < kb_end) slab_issue(wslab[wave][c], rsrc_w, lane_off_w, K, kb, nt_loads);
         }
         // Token rows in: the two slab loads per block issued after them may
         // still be in flight.
@@ -577,9 +581,9 @@ __device__ __forceinline__ float gemv_row(const uint32_t (&xp)[kC][8], const flo
 }
 
 // Issue the loads of weight row n (when `live`) and of its weight scales,
-// chunk by chunk; lanes past K, and every lane of a row that is not live,
-// read zeros.
-template <int kC>
+// chunk by chunk, the weights with cache policy kPol; lanes past K, and
+// every lane of a row that is not live, read zeros.
+template <int kC, int kPol>
 __device__ __forceinline__ void gemv_load_weights(const uint8_t* wq, const float* ws, int64_t n, bool live, int64_t K,
                                                   int lane, i32x4 (&wv)[kC], float (&wsv)[kC]) {
     const int KB = (int)(K / 128);
@@ -594,11 +598,11 @@ __device__ __forceinline__ void gemv_load_weights(const uint8_t* wq, const float
 #pragma unroll
     for (int c = 0; c < kC; ++c) {
         const int k = 1024 * c + 16 * lane;
-        wv[c] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, k < K ? k : (int)K, 0, 0));
+        wv[c] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, k < K ? k : (int)K, 0, kPol));
     }
 }
 
-template <int kC>
+template <int kC, int kPol>
 __global__ __launch_bounds__(kGemvThreads) void w8a8_gemv_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ xs, const uint8_t* __restrict__ wq,
     const float* __restrict__ ws, void* __restrict__ y, int y_dtype, int64_t N, int64_t K) {
@@ -618,7 +622,7 @@ __global__ __launch_bounds__(kGemvThreads) void w8a8_gemv_kernel(
 #pragma unroll
     for (int c = 0; c < kC; ++c)
         sx[c] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rxs, 4 * ((1024 * c + 16 * lane) / 128), 0, 0));
-    gemv_load_weights<kC>(wq, ws, n, live, K, lane, wv, wsv);
+    gemv_load_weights<kC, kPol>(wq, ws, n, live, K, lane, wv, wsv);
     // Keep every load ahead of the token copy and the arithmetic: the
     // scheduler would otherwise sink the later chunks' loads below the
     // first chunk's products.
@@ -642,7 +646,7 @@ __global__ __launch_bounds__(kGemvThreads) void w8a8_gemv_kernel(
 // bit for bit.  Codes and scales go to LDS; after one barrier every wave
 // reads back its lanes' 16 codes per chunk and runs gemv_row.  The weight
 // loads are issued first, so the quantisation runs while they stream.
-template <bool kXBf16, int kW, int kC>
+template <bool kXBf16, int kW, int kC, int kPol>
 __global__ __launch_bounds__(kW * kWave) void w8a8_gemv_quant_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq, const float* __restrict__ ws,
     void* __restrict__ y, int y_dtype, int64_t N, int64_t K) {
@@ -678,7 +682,7 @@ __global__ __launch_bounds__(kW * kWave) void w8a8_gemv_quant_kernel(
     __builtin_amdgcn_sched_barrier(0);
     i32x4 wv[kC];
     float wsv[kC];
-    gemv_load_weights<kC>(wq, ws, n0, true, K, lane, wv, wsv);
+    gemv_load_weights<kC, kPol>(wq, ws, n0, true, K, lane, wv, wsv);
     __builtin_amdgcn_sched_barrier(0);   // keep the weight loads ahead of the quantisation
 
 #pragma unroll
@@ -722,14 +726,18 @@ hipError_t launch_w8a8_gemv(const uint8_t* xq, const float* xs, const uint8_t* w
     if (N % 16 != 0 || K > kGemvMaxK) return hipErrorInvalidValue;
     static_assert(kGemvWaves == kGemvLaunchWaves, "plan and launch agree");
     const dim3 grid((unsigned)((N + kGemvWaves - 1) / kGemvWaves));
-#define BFP8_LAUNCH_GEMV8(C)                                                                                    \
-    hipLaunchKernelGGL((w8a8_gemv_kernel<C>), grid, dim3(kGemvThreads), 0, stream, xq, xs, wq, ws, y, y_dtype, N, K)
-    switch (gemv_chunks(K)) {
-        case 4: BFP8_LAUNCH_GEMV8(4); break;
-        case 8: BFP8_LAUNCH_GEMV8(8); break;
-        case 12: BFP8_LAUNCH_GEMV8(12); break;
-        default: BFP8_LAUNCH_GEMV8(16); break;
+#define BFP8_LAUNCH_GEMV8(C, P)                                                                                   \
+    hipLaunchKernelGGL((w8a8_gemv_kernel<C, P>), grid, dim3(kGemvThreads), 0, stream, xq, xs, wq, ws, y, y_dtype, N, K)
+#define BFP8_LAUNCH_GEMV8_C(P)                    \
+    switch (gemv_chunks(K)) {                      \
+        case 4: BFP8_LAUNCH_GEMV8(4, P); break;   \
+        case 8: BFP8_LAUNCH_GEMV8(8, P); break;   \
+        case 12: BFP8_LAUNCH_GEMV8(12, P); break; \
+        default: BFP8_LAUNCH_GEMV8(16, P); break; \
     }
+    if (weights_nt(N, K)) { BFP8_LAUNCH_GEMV8_C(kLoadNt) }
+    else { BFP8_LAUNCH_GEMV8_C(0) }
+#undef BFP8_LAUNCH_GEMV8_C
 #undef BFP8_LAUNCH_GEMV8
     return hipGetLastError();
 }
@@ -745,18 +753,24 @@ hipError_t launch_w8a8_gemv_quant(const void* x, bool x_bf16, const uint8_t* wq,
     // 5.25-5.29 for four waves (16 values per lane) and 5.43 for sixteen.
     constexpr int kQW = kGemvWaves;
     const dim3 grid((unsigned)(N / kQW));
-#define BFP8_LAUNCH_GEMVQ(B, C)                                                                                    \
-    hipLaunchKernelGGL((w8a8_gemv_quant_kernel<B, kQW, C>), grid, dim3(kQW * kWave), 0, stream, xh, wq, ws, y, y_dtype, \
-                       N, K)
-#define BFP8_LAUNCH_GEMVQ_C(B)                    \
-    switch (gemv_chunks(K)) {                      \
-        case 4: BFP8_LAUNCH_GEMVQ(B, 4); break;   \
-        case 8: BFP8_LAUNCH_GEMVQ(B, 8); break;   \
-        case 12: BFP8_LAUNCH_GEMVQ(B, 12); break; \
-        default: BFP8_LAUNCH_GEMVQ(B, 16); break; \
+#define BFP8_LAUNCH_GEMVQ(B, C, P)                                                                                 \
+    hipLaunchKernelGGL((w8a8_gemv_quant_kernel<B, kQW, C, P>), grid, dim3(kQW * kWave), 0, stream, xh, wq, ws, y,      \
+                       y_dtype, N, K)
+#define BFP8_LAUNCH_GEMVQ_C(B, P)                    \
+    switch (gemv_chunks(K)) {                         \
+        case 4: BFP8_LAUNCH_GEMVQ(B, 4, P); break;   \
+        case 8: BFP8_LAUNCH_GEMVQ(B, 8, P); break;   \
+        case 12: BFP8_LAUNCH_GEMVQ(B, 12, P); break; \
+        default: BFP8_LAUNCH_GEMVQ(B, 16, P); break; \
     }
-    if (x_bf16) { BFP8_LAUNCH_GEMVQ_C(true) }
-    else { BFP8_LAUNCH_GEMVQ_C(false) }
+    const bool nt = weights_nt(N, K);
+    if (x_bf16) {
+        if (nt) { BFP8_LAUNCH_GEMVQ_C(true, kLoadNt) }
+        else { BFP8_LAUNCH_GEMVQ_C(true, 0) }
+    } else {
+        if (nt) { BFP8_LAUNCH_GEMVQ_C(false, kLoadNt) }
+        else { BFP8_LAUNCH_GEMVQ_C(false, 0) }
+    }
 #undef BFP8_LAUNCH_GEMVQ_C
 #undef BFP8_LAUNCH_GEMVQ
     return hipGetLastError();

@@ -9,8 +9,10 @@
 // Each thread issues kLoads independent 16-byte loads before it combines
 // any of them (all of a wave's loads are in flight together); consecutive
 // lanes read consecutive 16 bytes, so each load instruction of a wave covers
-// eight whole 128-byte lines.  Bytes past `bytes` are not read (buffer
-// descriptor range check).
+// eight whole 128-byte lines.  The loads are non-temporal (nt), the policy
+// that reads rotated copies fastest (4.42 vs 4.57 us for 16 MiB; sc0 or sc1
+// alone: no change) and the one the decode kernels use for their weights.
+// Bytes past `bytes` are not read (buffer descriptor range check).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -29,7 +31,7 @@ __global__ __launch_bounds__(kThreads) void read_probe_kernel(const uint8_t* __r
     i32x4 v[kLoads];
 #pragma unroll
     for (int i = 0; i < kLoads; ++i)
-        v[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)(base + i * kThreads * 16), 0, 0);
+        v[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)(base + i * kThreads * 16), 0, 2 /* nt */);
     int acc = 0;
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) acc ^= v[i][0] ^ v[i][1] ^ v[i][2] ^ v[i][3];

@@ -85,6 +85,16 @@ inline int gemv_chunks(int64_t K) { return K <= 4096 ? 4 : K <= 8192 ? 8 : K <= 
 // 2 l and then 2 l + 1 (a 16-bit chunk: 32 bytes per lane) hits 16
 // distinct bank groups per 16 lanes in each read.
 constexpr int kGemvThreads = kGemvWaves * kWave;
+// Cache policy of weight loads that no other workgroup of the call repeats
+// (the one-token kernels; the streaming kernels with one token tile):
+// non-temporal (nt) from 8 MiB of weights up.  A plain read of rotated
+// copies measured (us, default / nt): 2 MiB 2.43-2.56 / 2.57-2.64, 4 MiB
+// 2.51-2.52 / 2.71-2.78, 8 MiB 3.45 / 3.30-3.34, 16 MiB 4.61-4.62 /
+// 4.48-4.49, 32 MiB 6.83-6.85 / 6.70-6.72; sc0 or sc1 alone changed
+// nothing.  The token, which every workgroup reads, keeps the default.
+constexpr int kLoadNt = 2;                           // the nt bit of a buffer load's cache policy
+constexpr int64_t kNtMinWeightBytes = (int64_t)8 << 20;
+__host__ __device__ inline bool weights_nt(int64_t N, int64_t K) { return N * K >= kNtMinWeightBytes; }
 __device__ __forceinline__ int gemv_x_unit(int u) { return u ^ ((u >> 4) & 1); }
 template <int kU>
 __device__ __forceinline__ void gemv_x_issue(__amdgpu_buffer_rsrc_t rx, i32x4 (&v)[kU]) {
@@ -246,12 +256,21 @@ __device__ __forceinline__ int slab_lane_offset(int lane, int64_t K) {
     return (int)((lane >> 3) * K) + (((lane & 7) ^ ((lane >> 3) & 7)) << 4);
 }
 
-// Issue the two loads of block kb of the 16 rows that `rsrc` covers.
-__device__ __forceinline__ void slab_issue(uint8_t* slab, i32x4 rsrc, int lane_off, int64_t K, int64_t kb) {
+// Issue the two loads of block kb of the 16 rows that `rsrc` covers;
+// non-temporal when `nt` (wave-uniform: no other workgroup of the call
+// reads the same weights, and they are large enough, weights_nt).
+__device__ __forceinline__ void slab_issue(uint8_t* slab, i32x4 rsrc, int lane_off, int64_t K, int64_t kb,
+                                           bool nt) {
     const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_address(slab));
     const int k_off = __builtin_amdgcn_readfirstlane((int)(kb * 128));
-    dma16(lds, rsrc, lane_off, 0, k_off);
-    dma16(lds + 1024, rsrc, lane_off, __builtin_amdgcn_readfirstlane((int)(8 * K)), k_off);
+    const int row8 = __builtin_amdgcn_readfirstlane((int)(8 * K));
+    if (nt) {
+        dma16_nt(lds, rsrc, lane_off, 0, k_off);
+        dma16_nt(lds + 1024, rsrc, lane_off, row8, k_off);
+    } else {
+        dma16(lds, rsrc, lane_off, 0, k_off);
+        dma16(lds + 1024, rsrc, lane_off, row8, k_off);
+    }
 }
 
 __device__ __forceinline__ void slab_read(const uint8_t* slab, int r, int g, u32x4& lo, u32x4& hi) {
