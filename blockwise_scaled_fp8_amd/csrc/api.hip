@@ -112,6 +112,7 @@ int route(int op, int64_t M, int64_t N, int64_t K) {
             return BFP8_KERNEL_W8A16_STREAM;
         case BFP8_OP_GEMM_W8A16_BLK32_UE8M0:
             if (one_token(M, K)) return BFP8_KERNEL_BLK32_GEMV;
+            if (w8a16_one_tile(M, N, K)) return BFP8_KERNEL_BLK32_WIDE;
             return M <= kStreamMaxM ? BFP8_KERNEL_BLK32_STREAM_LDS : BFP8_KERNEL_BLK32_STREAM;
         case BFP8_OP_QUANT_ACT_1X128:
             return BFP8_KERNEL_QUANT_ACT;
@@ -353,9 +354,15 @@ bfp8_status bfp8_gemm_w8a16_blk32_ue8m0(const void* x, int x_dtype, const uint8_
     if (st != BFP8_OK) return st;
     if (x_dtype != BFP8_F16) return BFP8_E_DTYPE;
     if ((M + 15) / 16 > 65535) return BFP8_E_SHAPE;
-    if (route(BFP8_OP_GEMM_W8A16_BLK32_UE8M0, M, N, K) == BFP8_KERNEL_BLK32_GEMV)
-        return launched(launch_w8a16_blk32_gemv(x, wq, e8m0, y, y_dtype, N, K, as_stream(stream)));
-    return launched(launch_w8a16_blk32_stream(x, wq, e8m0, y, y_dtype, M, N, K, workspace, as_stream(stream)));
+    switch (route(BFP8_OP_GEMM_W8A16_BLK32_UE8M0, M, N, K)) {
+        case BFP8_KERNEL_BLK32_GEMV:   // one token: dot products on the vector ALUs
+            return launched(launch_w8a16_blk32_gemv(x, wq, e8m0, y, y_dtype, N, K, as_stream(stream)));
+        case BFP8_KERNEL_BLK32_WIDE:   // 8 < M <= 16: one token tile, token rows through LDS
+            return launched(launch_w8a16_blk32_wide(x, wq, e8m0, y, y_dtype, M, N, K, as_stream(stream)));
+        default:
+            return launched(launch_w8a16_blk32_stream(x, wq, e8m0, y, y_dtype, M, N, K, workspace,
+                                                      as_stream(stream)));
+    }
 }
 
 bfp8_status bfp8_prepare_blk32_ue8m0(const uint8_t* wq_host, const float* scale_host, int64_t N, int64_t K,
@@ -476,8 +483,9 @@ bfp8_status bfp8_get_plan(int op, int64_t M, int64_t N, int64_t K, bfp8_plan* pl
             break;
         }
         case BFP8_KERNEL_W8A8_WIDE:
-        case BFP8_KERNEL_W8A16_WIDE: {
-            const WideShape w = wide_shape(M, N);
+        case BFP8_KERNEL_W8A16_WIDE:
+        case BFP8_KERNEL_BLK32_WIDE: {
+            const WideShape w = p.kernel == BFP8_KERNEL_W8A8_WIDE ? wide_shape(M, N) : w16_wide_shape(M, N);
             p.tile_n = 16 * w.kr;
             p.tile_m = 16 * w.kt;
             p.waves = kWideLaunchWaves;
@@ -519,6 +527,7 @@ const char* bfp8_kernel_name(int kernel) {
         case BFP8_KERNEL_BLK32_STREAM_LDS: return "blk32_stream_lds";
         case BFP8_KERNEL_BLK32_STREAM: return "blk32_stream";
         case BFP8_KERNEL_BLK32_GEMV: return "blk32_gemv";
+        case BFP8_KERNEL_BLK32_WIDE: return "blk32_wide";
         default: return "unknown kernel";
     }
 }

@@ -81,6 +81,30 @@ inline WideShape wide_shape(int64_t M, int64_t N) {
     return best;
 }
 
+// Shape of a W8A16 all-token launch (blk128 and block-32): wide_shape above
+// 16 tokens; for M <= 16 one 16-token tile (kt = 1) and kr by the same rule
+// (fewest workgroups that still give one per CU, two row tiles on a tie,
+// else the most workgroups): measured at M = 16, kR = 1 against 2 (us):
+// 4096 x 4096 6.91 / 7.73, 1024 x 4096 4.59 / 5.33, 4096 x 12288 14.57 /
+// 18.22, but 12288 x 4096 17.63 / 15.39 (768 workgroups against 384).
+inline WideShape w16_wide_shape(int64_t M, int64_t N) {
+    if (M > 16) return wide_shape(M, N);
+    WideShape best{1, 1, 0, 1};
+    int64_t best_wg = -1;
+    bool best_full = false;
+    for (int kr = 2; kr >= 1; --kr) {
+        const int64_t wg = (N + 16 * kr - 1) / (16 * kr);
+        const bool full = wg >= 256;
+        const bool better = best_wg < 0 || (full && (!best_full || wg < best_wg)) || (!full && !best_full && wg > best_wg);
+        if (better) {
+            best = WideShape{kr, 1, (unsigned)wg, 1};
+            best_wg = wg;
+            best_full = full;
+        }
+    }
+    return best;
+}
+
 // W8A8 dispatch (codes in), from the projection sweep:
 //  * the streaming kernel for M <= 16 when it needs no split of K, or when
 //    N < 1024, and for M <= 64 when its workgroups fit one round unsplit;
@@ -141,14 +165,29 @@ hipError_t launch_w8a8_stream_quant(const void* x, bool x_bf16, const uint8_t* w
                                     void* workspace, hipStream_t stream);
 hipError_t launch_w8a16_tile(const void* x, bool x_bf16, const uint8_t* wq, const float* ws, void* y,
                              int y_dtype, int64_t M, int64_t N, int64_t K, void* workspace, hipStream_t stream);
-// W8A16 blk128 dispatch: the streaming kernel for M <= 16; the all-token
-// kernel (launch_w8a16_wide) for 16 < M <= 256 when K <= 4096 and either
-// M <= 32 or M * N <= 2^19; the tiled kernel otherwise.  Measured, us, all
-// with K = 4096: N = 4096 M = 32 / 64 / 128 9.6 / 11.9 / 17.8 against
-// 13.7 / 14.2 / 20.4 tiled; N = 1024 M = 64 / 128 / 256 7.0 / 7.5 / 9.8
-// against 11.5 / 17.0 / 18.1; N = 12288 M = 32 22.3 vs 26.3, while from
-// M = 64 there (27.5 vs 33.5) and from K = 12288 the tiled kernel wins.
+// W8A16 (blk128 and block-32) with 8 < M <= 16, when the streaming plan
+// would not split K: the all-token kernel with one 16-token tile.  Its
+// token rows arrive by direct-to-LDS loads of whole lines into per-wave
+// rings, where the streaming kernel's sixteen live token rows per block
+// stay register loads in the MFMA layout (half lines); measured at M = 16
+// (us, streaming against all-token): blk128 4096 x 4096 7.33 / 6.91,
+// 4096 x 7168 11.2 / 9.41, 4096 x 12288 17.7 / 14.57, 1024 x 4096 6.35 /
+// 4.59, 12288 x 4096 16.34 / 15.39.  At M <= 8 the streaming kernel, whose
+// token rows already come through LDS there, stays ahead (M = 8: 5.95 vs
+// 6.3 us at 4096 x 4096).
+inline bool w8a16_one_tile(int64_t M, int64_t N, int64_t K) {
+    return M > kStreamMaxM / 2 && M <= kStreamMaxM && K <= kTileMaxK && plan_stream(M, N, K).splits == 1;
+}
+// W8A16 blk128 dispatch: the streaming kernel for M <= 16 except where
+// w8a16_one_tile holds; the all-token kernel (launch_w8a16_wide) there and
+// for 16 < M <= 256 when K <= 4096 and either M <= 32 or M * N <= 2^19; the
+// tiled kernel otherwise.  Measured, us, all with K = 4096: N = 4096 M = 32
+// / 64 / 128 9.6 / 11.9 / 17.8 against 13.7 / 14.2 / 20.4 tiled; N = 1024
+// M = 64 / 128 / 256 7.0 / 7.5 / 9.8 against 11.5 / 17.0 / 18.1; N = 12288
+// M = 32 22.3 vs 26.3, while from M = 64 there (27.5 vs 33.5) and from
+// K = 12288 the tiled kernel wins.
 inline bool w8a16_wide(int64_t M, int64_t N, int64_t K) {
+    if (w8a16_one_tile(M, N, K)) return true;
     return M > kStreamMaxM && M <= 16 * kStreamMaxM && K <= 4096 &&
            (M <= 2 * kStreamMaxM || M * N <= ((int64_t)1 << 19));
 }
@@ -201,5 +240,9 @@ hipError_t launch_w8a16_blk32_gemv(const void* x, const uint8_t* wq, const uint8
 hipError_t launch_w8a16_blk32_stream(const void* x, const uint8_t* wq, const uint8_t* e8m0,
                                      void* y, int y_dtype, int64_t M, int64_t N, int64_t K,
                                      void* workspace, hipStream_t stream);
+// Block-32 all-token kernel (shape w16_wide_shape; N a multiple of 32, K of
+// 128, K <= kTileMaxK); needs no workspace.
+hipError_t launch_w8a16_blk32_wide(const void* x, const uint8_t* wq, const uint8_t* e8m0, void* y, int y_dtype,
+                                   int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
 }  // namespace bfp8

@@ -314,21 +314,30 @@ __global__ __launch_bounds__(kStreamThreads) void w8a16_blk32_stream_lds_kernel(
 }
 
 // ------------------------------------------------- W8A16 all-token kernel ----
-// The W8A16 blk128 product with every token per workgroup (see w8a16_wide
-// for where it is used): a workgroup owns 16 kR weight rows (kR = 1 or 2)
-// and 16 kT tokens (kT = 2 or 4 token tiles; grid.y walks further groups of
-// 16 kT tokens) over all of K, so nothing is split across workgroups.  Eight
+// The W8A16 product with every token of a group per workgroup (see
+// w8a16_wide and w8a16_one_tile for where it is used), for blk128 weights
+// and for block-32 UE8M0 weights (kBlk32): a workgroup owns 16 kR weight
+// rows (kR = 1 or 2) and 16 kT tokens (kT = 1, 2 or 4 token tiles; grid.y
+// walks further groups of 16 kT tokens) over all of K, so nothing is split
+// across workgroups.  Eight
 // waves: wave w takes token tile tg = w % kT and the 128-K blocks kw,
 // kw + KW, ... (kw = w / kT, KW = 8 / kT).  Each wave owns a ring of LDS
 // slots (three for kR = 1, two for kR = 2); a slot holds one block: the
 // 16 kR weight rows (2 KB each 16, E4M3), the wave's 16 token rows (16-bit,
-// 256 bytes each) and the weight scale, all by direct-to-LDS 16-byte loads
-// of whole lines.  Token row R of a tile keeps its 16-byte chunk c at
-// position c ^ sw(R), sw(R) = ((R & 3) << 2) | (R >> 2), so the 16 rows of
-// one MFMA read hit 16 distinct bank groups.  The weights are widened in
-// registers (widen8) and feed four 16x16x32 MFMAs per block and row tile,
-// promoted with the block scale as in the streaming kernel.  The waves'
-// partial sums meet in LDS once, at the end, and are added in K-lane order.
+// 256 bytes each) and the block's weight scale word, all by direct-to-LDS
+// loads of whole lines (16 bytes a lane; the scale word one dword).  Token
+// row R of a tile keeps its 16-byte chunk c at position c ^ sw(R),
+// sw(R) = ((R & 3) << 2) | (R >> 2), so the 16 rows of one MFMA read hit
+// 16 distinct bank groups.  The weights are widened in registers (widen8)
+// and feed four 16x16x32 MFMAs per block and row tile.  blk128: the block
+// partial is promoted with the fp32 block scale, as in the streaming
+// kernel.  Block-32: the scale word holds the four UE8M0 bytes of the
+// block's 32x32 tiles in the row tile's 32-row band ([SM70] "How it works":
+// one power-of-two scale per 32x32 tile), and each lane applies the two
+// that cover its two 16-K chunks inside the widening, exactly, so the MFMAs
+// accumulate across all of K with no promotion step, as in the block-32
+// streaming kernel.  The waves' partial sums meet in LDS once, at the end,
+// and are added in K-lane order.
 constexpr int kW16WideWaves = 8;
 static_assert(kW16WideWaves == kWideLaunchWaves, "plan and launch agree");
 constexpr int kW16WideThreads = kW16WideWaves * kWave;
@@ -351,14 +360,15 @@ __device__ __forceinline__ void w16_wait_n() {
 
 __device__ __forceinline__ int w16_sw(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
 
-template <bool kXBf16, int kT, int kR>
+template <bool kBlk32, bool kXBf16, int kT, int kR>
 __global__ __launch_bounds__(kW16WideThreads, 1) void w8a16_wide_kernel(
-    const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq, const float* __restrict__ ws,
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq, const void* __restrict__ scales,
     void* __restrict__ y, int y_dtype, int64_t M, int64_t N, int64_t K) {
     constexpr int KW = kW16WideWaves / kT;
     using SL = W16Slot<kR>;
     constexpr int kW16WideSlots = SL::kSlots, kW16Slot = SL::kBytes, kW16OffX = SL::kOffX, kW16OffWs = SL::kOffWs;
-    static_assert(kT == 2 || kT == 4, "token tiles");
+    static_assert(kT == 1 || kT == 2 || kT == 4, "token tiles");
+    static_assert(!kBlk32 || !kXBf16, "block-32 takes fp16 activations");
     __shared__ __attribute__((aligned(1024))) uint8_t ring[kW16WideWaves * kW16WideSlots * kW16Slot];
     const int64_t nt = blockIdx.x, mg = blockIdx.y;
     const int KB = (int)(K / 128);
@@ -372,7 +382,13 @@ __global__ __launch_bounds__(kW16WideThreads, 1) void w8a16_wide_kernel(
     const i32x4 rsrc_w = buffer_rsrc(wq + n0 * K, (uint32_t)(rows_w * K));
     const int64_t rows_x = M - m0 > 0 ? (M - m0 < 16 ? M - m0 : 16) : 0;
     const i32x4 rsrc_x = buffer_rsrc(x + m0 * K, (uint32_t)(rows_x * K * 2));
-    const i32x4 rsrc_ws = buffer_rsrc(ws + (n0 / 128) * KB, (uint32_t)(KB * 4));
+    // The block's scale word: the fp32 ws[n0 / 128, kb], or the UE8M0 bytes
+    // of 32x32 tiles (n0 / 32, 4 kb .. 4 kb + 3) (K / 32 bytes a band, a
+    // multiple of 4 since K % 128 == 0; the kR = 2 rows n0 = 32 nt .. +31
+    // share one band).
+    const i32x4 rsrc_ws =
+        kBlk32 ? buffer_rsrc(static_cast<const uint8_t*>(scales) + (n0 / 32) * (K / 32), (uint32_t)(KB * 4))
+               : buffer_rsrc(static_cast<const float*>(scales) + (n0 / 128) * KB, (uint32_t)(KB * 4));
     const int lane_off_w = slab_lane_offset(lane, K);
     // Token-row loads: instruction q covers rows 4q .. 4q + 3; lane l fills
     // position l % 16 of row 4q + l / 16 with logical chunk (l % 16) ^ sw(row).
@@ -425,22 +441,34 @@ __global__ __launch_bounds__(kW16WideThreads, 1) void w8a16_wide_kernel(
             const int c = i < 2 ? 2 * g + i : 8 + 2 * g + (i - 2);
             xv[i] = *reinterpret_cast<const u32x4*>(sl + kW16OffX + r * 256 + ((c ^ sw) << 4));
         }
-        const float wsv = *reinterpret_cast<const float*>(sl + kW16OffWs);
+        const uint32_t sword = *reinterpret_cast<const uint32_t*>(sl + kW16OffWs);
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         if (j + kW16WideSlots < nj) issue(slot, kw + KW * (j + kW16WideSlots));
-        const float sc = wsv;
 #pragma unroll
         for (int rt = 0; rt < kR; ++rt) {
             const uint32_t q8[8] = {wa0[rt][0], wa0[rt][1], wa0[rt][2], wa0[rt][3],
                                     wa1[rt][0], wa1[rt][1], wa1[rt][2], wa1[rt][3]};
-            f32x4 blk = zero;
+            if constexpr (kBlk32) {
+                // Chunk g (K 16 g .. 16 g + 15) lies in tile 4 kb + g / 2,
+                // chunk g + 4 in tile 4 kb + 2 + g / 2.
+                const float e0 = ue8m0_scale((sword >> (8 * (g >> 1))) & 0xFF);
+                const float e1 = ue8m0_scale((sword >> (8 * (2 + (g >> 1)))) & 0xFF);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const u32x4 a = widen8<kXBf16>(q8[2 * i], q8[2 * i + 1]);
-                blk = kXBf16 ? mfma_bf16_16x16x32(a, xv[i], blk) : mfma_f16_16x16x32(a, xv[i], blk);
+                for (int i = 0; i < 4; ++i) {
+                    const u32x4 a = widen8<false>(q8[2 * i], q8[2 * i + 1], i < 2 ? e0 : e1);
+                    acc[rt] = mfma_f16_16x16x32(a, xv[i], acc[rt]);
+                }
+            } else {
+                f32x4 blk = zero;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const u32x4 a = widen8<kXBf16>(q8[2 * i], q8[2 * i + 1]);
+                    blk = kXBf16 ? mfma_bf16_16x16x32(a, xv[i], blk) : mfma_f16_16x16x32(a, xv[i], blk);
+                }
+                const float sc = __builtin_bit_cast(float, sword);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[rt][e] = __builtin_fmaf(blk[e], sc, acc[rt][e]);
             }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[rt][e] = __builtin_fmaf(blk[e], sc, acc[rt][e]);
         }
         slot = slot + 1 == kW16WideSlots ? 0 : slot + 1;
     }
@@ -473,30 +501,48 @@ __global__ __launch_bounds__(kW16WideThreads, 1) void w8a16_wide_kernel(
     }
 }
 
+#define BFP8_LAUNCH_W16(S, B, T, R)                                                                                \
+    hipLaunchKernelGGL((w8a16_wide_kernel<S, B, T, R>), grid, dim3(kW16WideThreads), 0, stream, xh, wq, scales, y, \
+                       y_dtype, M, N, K)
+#define BFP8_LAUNCH_W16_KR(S, B, T)          \
+    if (w.kr == 1) BFP8_LAUNCH_W16(S, B, T, 1); \
+    else BFP8_LAUNCH_W16(S, B, T, 2);
+
 hipError_t launch_w8a16_wide(const void* x, bool x_bf16, const uint8_t* wq, const float* ws, void* y, int y_dtype,
                              int64_t M, int64_t N, int64_t K, hipStream_t stream) {
     if (M < 1 || N % 16 != 0 || K > kTileMaxK) return hipErrorInvalidValue;
-    const WideShape w = wide_shape(M, N);
+    const WideShape w = w16_wide_shape(M, N);
     if (w.groups_m > 65535) return hipErrorInvalidValue;
     const dim3 grid(w.groups_n, w.groups_m);
     const uint16_t* xh = static_cast<const uint16_t*>(x);
-#define BFP8_LAUNCH_W16(B, T, R)                                                                                  \
-    hipLaunchKernelGGL((w8a16_wide_kernel<B, T, R>), grid, dim3(kW16WideThreads), 0, stream, xh, wq, ws, y, y_dtype, \
-                       M, N, K)
-#define BFP8_LAUNCH_W16_KR(B, T)          \
-    if (w.kr == 1) BFP8_LAUNCH_W16(B, T, 1); \
-    else BFP8_LAUNCH_W16(B, T, 2);
+    const void* scales = ws;
     if (x_bf16) {
-        if (w.kt == 2) { BFP8_LAUNCH_W16_KR(true, 2) }
-        else { BFP8_LAUNCH_W16_KR(true, 4) }
+        if (w.kt == 1) { BFP8_LAUNCH_W16_KR(false, true, 1) }
+        else if (w.kt == 2) { BFP8_LAUNCH_W16_KR(false, true, 2) }
+        else { BFP8_LAUNCH_W16_KR(false, true, 4) }
     } else {
-        if (w.kt == 2) { BFP8_LAUNCH_W16_KR(false, 2) }
-        else { BFP8_LAUNCH_W16_KR(false, 4) }
+        if (w.kt == 1) { BFP8_LAUNCH_W16_KR(false, false, 1) }
+        else if (w.kt == 2) { BFP8_LAUNCH_W16_KR(false, false, 2) }
+        else { BFP8_LAUNCH_W16_KR(false, false, 4) }
     }
-#undef BFP8_LAUNCH_W16_KR
-#undef BFP8_LAUNCH_W16
     return hipGetLastError();
 }
+
+hipError_t launch_w8a16_blk32_wide(const void* x, const uint8_t* wq, const uint8_t* e8m0, void* y, int y_dtype,
+                                   int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+    if (M < 1 || N % 32 != 0 || K % 128 != 0 || K > kTileMaxK) return hipErrorInvalidValue;
+    const WideShape w = w16_wide_shape(M, N);
+    if (w.groups_m > 65535) return hipErrorInvalidValue;
+    const dim3 grid(w.groups_n, w.groups_m);
+    const uint16_t* xh = static_cast<const uint16_t*>(x);
+    const void* scales = e8m0;
+    if (w.kt == 1) { BFP8_LAUNCH_W16_KR(true, false, 1) }
+    else if (w.kt == 2) { BFP8_LAUNCH_W16_KR(true, false, 2) }
+    else { BFP8_LAUNCH_W16_KR(true, false, 4) }
+    return hipGetLastError();
+}
+#undef BFP8_LAUNCH_W16_KR
+#undef BFP8_LAUNCH_W16
 
 // ------------------------------------------------ W8A16 GEMV, M = 1 ----
 // One token (batch-1 decode) needs no matrix core: the work is one dot

@@ -271,23 +271,27 @@ size_t bfp8_workspace_bytes(int op, int64_t M, int64_t N, int64_t K);
  *   k_multiple    K must be a multiple of this.
  *   n_multiple    N must be a multiple of this.
  *   align_bytes   required alignment of every device pointer.
- *   m_stream_max  largest M always served by the weight-streaming decode
- *                 kernels (one token runs a dot-product kernel on the
- *                 vector ALUs instead: with K <= 8192 for W8A8, the fused
- *                 call and blk32, K <= 12288 for W8A16; W8A8 streams when K needs no split across
- *                 workgroups, or N < 1024; W8A8 also streams up to
- *                 4 * m_stream_max, one workgroup per 16-token tile, when
- *                 those workgroups fit one round on the CUs without a split
- *                 of K).  W8A8 uses a kernel that reads all tokens per
- *                 16- or 32-row weight tile for the other M <= 2 * m_stream_max,
- *                 and when K <= 4096 and M * N <= 2^19 (measured faster
- *                 there), the tiled MFMA kernels otherwise.  W8A16
- *                 blk128 streams M <= m_stream_max, reads all tokens per
- *                 weight tile for m_stream_max < M <= 16 * m_stream_max
- *                 when K <= 4096 and either M <= 2 * m_stream_max or
- *                 M * N <= 2^19, and uses its tiled MFMA kernel
- *                 otherwise; blk32 streams whenever it does not run its
- *                 one-token kernel.
+ *   m_stream_max  largest M served by the small-M (decode) kernels, one
+ *                 16-token MFMA tile.  One token runs a dot-product kernel
+ *                 on the vector ALUs: with K <= 8192 for W8A8, the fused
+ *                 call and blk32, K <= 12288 for W8A16.  Otherwise W8A8
+ *                 streams the weights when K needs no split across
+ *                 workgroups, or N < 1024, and also up to 4 * m_stream_max,
+ *                 one workgroup per 16-token tile, when those workgroups
+ *                 fit one round on the CUs without a split of K; it uses a
+ *                 kernel that reads all tokens per 16- or 32-row weight
+ *                 tile for the other M <= 2 * m_stream_max, and when
+ *                 K <= 4096 and M * N <= 2^19 (measured faster there), the
+ *                 tiled MFMA kernels otherwise.  W8A16 blk128 and blk32
+ *                 stream M <= m_stream_max / 2; for m_stream_max / 2 < M <=
+ *                 m_stream_max they run the all-token kernel with one
+ *                 16-token tile unless the streaming plan would split K
+ *                 (then they stream).  Above m_stream_max, W8A16 blk128
+ *                 reads all tokens per weight tile for M <= 16 *
+ *                 m_stream_max when K <= 4096 and either M <= 2 *
+ *                 m_stream_max or M * N <= 2^19, and uses its tiled MFMA
+ *                 kernel otherwise; blk32 streams one 16-token tile per
+ *                 workgroup.
  * Any output pointer may be NULL.
  */
 bfp8_status bfp8_get_limits(int op, int64_t* k_multiple, int64_t* n_multiple,
@@ -316,7 +320,8 @@ enum {
     BFP8_KERNEL_BLK32_STREAM_LDS = 13,  /* block-32, M <= 16: weights through LDS slabs */
     BFP8_KERNEL_BLK32_STREAM = 14,      /* block-32, M > 16: one 16-token tile per workgroup */
     BFP8_KERNEL_BLK32_GEMV = 15,        /* block-32, one token: dot products on the vector ALUs */
-    BFP8_KERNEL_COUNT = 16
+    BFP8_KERNEL_BLK32_WIDE = 16,        /* block-32, 8 < M <= 16: one 16-token tile per weight tile */
+    BFP8_KERNEL_COUNT = 17
 };
 
 /* A call's launch plan (filled by bfp8_get_plan). */

@@ -105,8 +105,17 @@ QUANT_W8A8 = [
 
 # ---------------------------------------------------------------- W8A16 ----
 W8A16_BY_M = [(1, 512, 1024, "w8a16_gemv")] + \
-    [(M, 512, 1024, "w8a16_stream") for M in (2, 3, 4, 5, 8, 12, 16)] + \
+    [(M, 512, 1024, "w8a16_stream") for M in (2, 3, 4, 5, 8)] + \
+    [(M, 512, 1024, "w8a16_wide:16x16w8") for M in (9, 12, 16)] + \
     [(M, 512, 1024, "w8a16_wide:16x32w8") for M in (17, 33, 64, 65, 130)]
+# 8 < M <= 16 without a split of K: the all-token kernel with one 16-token
+# tile, one or two weight-row tiles (a half-filled pair at N = 16), ragged
+# M, K of one block and long K.
+W8A16_ONE_TILE = [
+    (16, 4096, 4096, "w8a16_wide:16x16w8"), (9, 1024, 4096, "w8a16_wide:16x16w8"),
+    (13, 12288, 512, "w8a16_wide:32x16w8"), (16, 16, 4096, "w8a16_wide:32x16w8"), (11, 64, 128, "w8a16_wide:16x16w8"),
+    (16, 4096, 7168, "w8a16_wide:16x16w8"),
+]
 # One token, K <= 12288: 4, 8 or 12 chunks, one row per wave.
 W8A16_ONE_TOKEN = [(1, N, K, "w8a16_gemv") for N, K in
                    ((16, 128), (16, 1152), (64, 4096), (1024, 4096), (2064, 1024), (4096, 4096), (4096, 3968),
@@ -118,9 +127,13 @@ W8A16_ALL_TOKENS = [
     (128, 4096, 4096, "w8a16_wide:32x64w8"), (100, 4112, 1024, "w8a16_wide:32x64w8"),
     (256, 1024, 4096, "w8a16_wide:32x32w8"), (200, 1040, 1024, "w8a16_wide:16x64w8"),
 ]
-W8A16_LONG_K = [(1, 4096, 12416, "w8a16_stream")] + [(M, 4096, 12288, "w8a16_stream") for M in (3, 16)]
-W8A16_SPLIT_K_STREAM = [(4, 512, 12288, "w8a16_stream/split")]
-W8A16_ONE_HOT = [(1, 256, 256, "w8a16_gemv"), (4, 256, 256, "w8a16_stream"), (40, 256, 256, "w8a16_wide:16x32w8")]
+W8A16_LONG_K = [(1, 4096, 12416, "w8a16_stream"), (3, 4096, 12288, "w8a16_stream"),
+                (16, 4096, 12288, "w8a16_wide:16x16w8")]
+# K split over workgroups, also with sixteen live token rows (8 < M <= 16,
+# the streaming kernel's register-operand tokens).
+W8A16_SPLIT_K_STREAM = [(4, 512, 12288, "w8a16_stream/split"), (12, 512, 12288, "w8a16_stream/split")]
+W8A16_ONE_HOT = [(1, 256, 256, "w8a16_gemv"), (4, 256, 256, "w8a16_stream"), (16, 256, 256, "w8a16_wide:16x16w8"),
+                 (40, 256, 256, "w8a16_wide:16x32w8")]
 W8A16_TILE_SPLIT = [(40, 1024, 8192, "w8a16_tile:128x64w8/split"), (100, 1040, 8192, "w8a16_tile:128x128w8/split"),
                     (300, 2048, 2176, "w8a16_tile:128x128w8/split"), (40, 16384, 512, "w8a16_tile:128x64w8")]
 W8A16_TILE_ONE_HOT = (300, 256, 256, "w8a16_tile:128x128w8")
@@ -130,7 +143,14 @@ W8A16_PREFILL_OPROJ = (4096, 4096, 4096, "w8a16_tile:256x128w8")
 W8A16_DECODE_OPROJ = (1, 4096, 4096, "w8a16_gemv")
 
 # ---------------------------------------------------------------- blk32 ----
-BLK32_WORKLOAD = [(1, 4096, 7168, "blk32_gemv")] + [(M, 4096, 7168, "blk32_stream_lds") for M in (2, 3, 4, 8, 12, 16)]
+BLK32_WORKLOAD = [(1, 4096, 7168, "blk32_gemv")] + [(M, 4096, 7168, "blk32_stream_lds") for M in (2, 3, 4, 8)] + \
+    [(M, 4096, 7168, "blk32_wide:16x16w8") for M in (9, 12, 16)]
+# 8 < M <= 16 without a split of K: the all-token kernel with one 16-token
+# tile, the UE8M0 scales applied in the widening; one and two weight-row
+# tiles (two: 16 weight rows of each of two 16-row halves of a 32-row scale
+# band), ragged M, tiny N.
+BLK32_ONE_TILE = [(13, 8192, 1152, "blk32_wide:32x16w8"), (16, 12288, 1024, "blk32_wide:32x16w8"),
+                  (10, 64, 4096, "blk32_wide:16x16w8"), (16, 32, 256, "blk32_wide:16x16w8")]
 # One token with K <= 8192: the dot-product kernel on the vector ALUs (one and
 # 4 or 8 chunks, K of one block and K ending inside a 1 KB chunk), and
 # just above that range.
@@ -141,9 +161,11 @@ BLK32_ONE_HOT_ONE_TOKEN = (1, 704, 256, "blk32_gemv")
 # Above the streaming range ([SM70] "Results" times M = 32 ... 4096).
 BLK32_ABOVE_16 = [(M, 4096, 7168, "blk32_stream") for M in (17, 32, 64, 128, 512)]
 BLK32_WINDOW = (8, 512, 1024, "blk32_stream_lds")
-BLK32_ONE_HOT = (16, 704, 256, "blk32_stream_lds")
+BLK32_ONE_HOT = (16, 704, 256, "blk32_wide:16x16w8")
+BLK32_ONE_HOT_STREAM = (8, 704, 256, "blk32_stream_lds")
 BLK32_ONE_HOT_ABOVE_16 = (17, 704, 256, "blk32_stream")
 BLK32_SPLIT_K = (4, 1024, 12288, "blk32_stream_lds/split")
+BLK32_SPLIT_K_16 = (16, 1024, 12288, "blk32_stream_lds/split")
 BLK32_SPLIT_K_ABOVE_16 = (20, 512, 12288, "blk32_stream/split")
 
 
@@ -163,12 +185,13 @@ def all_cases():
         W8A8: [W8A8_THRESHOLD, W8A8_ONE_TOKEN, W8A8_ABOVE_ONE_TOKEN, W8A8_STRADDLE, W8A8_SPLIT_K_STREAM, W8A8_NO_WORKSPACE, W8A8_TILE,
                [W8A8_LARGE_RAGGED, W8A8_DECODE_OPROJ, W8A8_PREFILL_OPROJ, W8A8_DETERMINISTIC], W8A8_ONE_HOT],
         QW8A8: [QUANT_W8A8],
-        W8A16: [W8A16_BY_M, W8A16_ONE_TOKEN, W8A16_ALL_TOKENS, W8A16_LONG_K, W8A16_SPLIT_K_STREAM, W8A16_ONE_HOT,
+        W8A16: [W8A16_BY_M, W8A16_ONE_TOKEN, W8A16_ONE_TILE, W8A16_ALL_TOKENS, W8A16_LONG_K, W8A16_SPLIT_K_STREAM,
+                W8A16_ONE_HOT,
                 W8A16_TILE_SPLIT, [W8A16_TILE_ONE_HOT, W8A16_TILE_LARGE_RAGGED, W8A16_TILE_LARGE_ONE_HOT,
                                    W8A16_PREFILL_OPROJ, W8A16_DECODE_OPROJ]],
-        BLK32: [BLK32_WORKLOAD, BLK32_ONE_TOKEN, BLK32_ABOVE_16,
-                [BLK32_WINDOW, BLK32_ONE_HOT, BLK32_ONE_HOT_ABOVE_16, BLK32_ONE_HOT_ONE_TOKEN, BLK32_SPLIT_K,
-                 BLK32_SPLIT_K_ABOVE_16]],
+        BLK32: [BLK32_WORKLOAD, BLK32_ONE_TOKEN, BLK32_ONE_TILE, BLK32_ABOVE_16,
+                [BLK32_WINDOW, BLK32_ONE_HOT, BLK32_ONE_HOT_STREAM, BLK32_ONE_HOT_ABOVE_16, BLK32_ONE_HOT_ONE_TOKEN,
+                 BLK32_SPLIT_K, BLK32_SPLIT_K_16, BLK32_SPLIT_K_ABOVE_16]],
     }
     for op, tabs in tables.items():
         for tab in tabs:

@@ -267,6 +267,28 @@ def test_w8a16_gemv_one_token(gpu_lib, M, N, K, kernel, xdtype):
 
 
 @pytest.mark.parametrize("xdtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("M,N,K,kernel", cases.W8A16_ONE_TILE)
+def test_w8a16_one_token_tile(gpu_lib, M, N, K, kernel, xdtype):
+    """8 < M <= 16 without a split of K: the all-token kernel with a single
+    16-token tile (token rows of a ragged M past the end load as zeros), one
+    or two weight-row tiles per workgroup (a half-filled pair at N = 16),
+    K of one block and long K; no workspace."""
+    assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A16_BLK128, M, N, K) == 0
+    say("w8a16 one tile", xdtype, f"M={M} N={N} K={K}")
+    expect(W8A16, M, N, K, kernel)
+    x = inputs.activations(M, K, workload=670 + M, stream=K, outliers=True, dtype=xdtype)
+    wq, ws = oracle.quantize_weight_128x128(f32(inputs.weights_bf16(N, K, workload=670 + N, stream=K)))
+    y0 = oracle.gemm_w8a16_blk128(f32(x), wq, ws)
+    xd, wqd, wsd = x.cuda(), dev(wq), dev(ws)
+    y32 = run_w8a16(xd, wqd, wsd, torch.float32)
+    assert_fp32_bar(y32, y0, f"w8a16 one tile M={M} N={N} K={K}")
+    y16 = run_w8a16(xd, wqd, wsd, xdtype)
+    assert_16bit_bar(y16, y32, y0, "bf16" if xdtype == torch.bfloat16 else "f16", f"w8a16 one tile M={M}")
+    y2 = run_w8a16(xd, wqd, wsd, torch.float32)
+    assert torch.equal(y32.view(torch.int32), y2.view(torch.int32))
+
+
+@pytest.mark.parametrize("xdtype", [torch.bfloat16, torch.float16])
 @pytest.mark.parametrize("M,N,K,kernel", cases.W8A16_ALL_TOKENS)
 def test_w8a16_all_tokens(gpu_lib, M, N, K, kernel, xdtype):
     """16 < M <= 256 with K <= 4096: every token of a group per 16- or 32-row
@@ -311,7 +333,7 @@ def test_w8a16_blk128_long_k(gpu_lib, M, N, K, kernel):
 def test_w8a16_blk128_one_hot_all_codes_exact(gpu_lib, xdtype, M, N, K, kernel):
     """x one-hot 1.0: Y[:, n] = E4M3(wq[n, k]) * ws exactly, subnormal codes
     included (vector-ALU kernel at M = 1, streaming kernel at M = 4,
-    all-token kernel at M = 40)."""
+    all-token kernel with one token tile at M = 16 and with two at M = 40)."""
     expect(W8A16, M, N, K, kernel)
     wq = np.zeros((N, K), np.uint8)
     wq[:254, :] = FINITE_CODES[:, None]
@@ -440,7 +462,8 @@ def _blk32_inputs(M, N, K, wid, lo=-14, hi=7):
 @pytest.mark.parametrize("M,N,K,kernel", cases.BLK32_WORKLOAD)
 def test_blk32_block32_workload_shape(gpu_lib, M, N, K, kernel):
     """N=4096, K=7168 block-32 weights, e uniform on [-14, 7] (M = 1 on the
-    one-token kernel, M = 2 .. 16 streaming)."""
+    one-token kernel, M = 2 .. 8 streaming, M = 9 .. 16 on the all-token
+    kernel with one token tile)."""
     say("blk32", M)
     expect(BLK32, M, N, K, kernel)
     x, wq, e8 = _blk32_inputs(M, N, K, 3)
@@ -482,15 +505,15 @@ def test_blk32_window_ends(gpu_lib, lo, hi):
     assert_fp32_bar(y32, y0, f"blk32 e={lo}")
 
 
-@pytest.mark.parametrize("case", [cases.BLK32_ONE_HOT, cases.BLK32_ONE_HOT_ABOVE_16, cases.BLK32_ONE_HOT_ONE_TOKEN],
-                         ids=lambda c: c[3])
+@pytest.mark.parametrize("case", [cases.BLK32_ONE_HOT, cases.BLK32_ONE_HOT_STREAM, cases.BLK32_ONE_HOT_ABOVE_16,
+                                  cases.BLK32_ONE_HOT_ONE_TOKEN], ids=lambda c: c[3])
 @pytest.mark.parametrize("out", [torch.float32, torch.float16])
 def test_blk32_one_hot_all_codes_all_exponents_exact(gpu_lib, out, case):
     """Every finite code times every window exponent is produced exactly
-    (fp16 subnormals at e = -14 included), by the streaming kernel of M <= 16,
-    by the one for M > 16 (M = 17: a full token tile and a second one with a
-    single live row) and by the one-token kernel (M = 1: one column k per
-    call)."""
+    (fp16 subnormals at e = -14 included), by the all-token kernel with one
+    token tile (M = 16), the streaming kernel of M <= 8, the one for M > 16
+    (M = 17: a full token tile and a second one with a single live row) and
+    the one-token kernel (M = 1: one column k per call)."""
     exps = np.arange(-14, 8)
     M, N, K, kernel = case
     assert N == 32 * exps.size
@@ -510,7 +533,8 @@ def test_blk32_one_hot_all_codes_all_exponents_exact(gpu_lib, out, case):
             np.testing.assert_array_equal(y[row].reshape(exps.size, 32), np.repeat(want[:, None], 32, axis=1))
 
 
-@pytest.mark.parametrize("case", [cases.BLK32_SPLIT_K, cases.BLK32_SPLIT_K_ABOVE_16], ids=lambda c: c[3])
+@pytest.mark.parametrize("case", [cases.BLK32_SPLIT_K, cases.BLK32_SPLIT_K_16, cases.BLK32_SPLIT_K_ABOVE_16],
+                         ids=lambda c: f"M{c[0]}-{c[3]}")
 def test_blk32_split_k_and_determinism(gpu_lib, case):
     M, N, K, kernel = case
     expect(BLK32, M, N, K, kernel)
@@ -523,6 +547,27 @@ def test_blk32_split_k_and_determinism(gpu_lib, case):
     b = run_blk32(x.cuda(), dev(wq), dev(e8), torch.float32, wsb)
     assert_fp32_bar(a, y0, "blk32 split-K")
     assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+@pytest.mark.parametrize("M,N,K,kernel", cases.BLK32_ONE_TILE)
+def test_blk32_one_token_tile(gpu_lib, M, N, K, kernel):
+    """8 < M <= 16 without a split of K: the all-token kernel with one
+    16-token tile, the UE8M0 scale word of each block applied in the
+    widening; one and two weight-row tiles (two 16-row halves of one
+    32-row scale band), ragged M, tiny N; fp32 output against the oracle,
+    fp16 as RNE of the fp32 result, a rerun bit-identical."""
+    say("blk32 one tile", M, N, K)
+    expect(BLK32, M, N, K, kernel)
+    assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A16_BLK32_UE8M0, M, N, K) == 0
+    x, wq, e8 = _blk32_inputs(M, N, K, 70 + M)
+    y0 = oracle.gemm_w8a16_blk32_ue8m0(f32(x), wq, e8)
+    xd, wqd, e8d = x.cuda(), dev(wq), dev(e8)
+    y32 = run_blk32(xd, wqd, e8d, torch.float32)
+    assert_fp32_bar(y32, y0, f"blk32 one tile M={M} N={N} K={K}")
+    yh = run_blk32(xd, wqd, e8d, torch.float16)
+    assert_16bit_bar(yh, y32, y0, "f16", f"blk32 one tile M={M}")
+    y2 = run_blk32(xd, wqd, e8d, torch.float32)
+    assert torch.equal(y32.view(torch.int32), y2.view(torch.int32))
 
 
 @pytest.mark.parametrize("M,N,K,kernel", cases.BLK32_ABOVE_16)

@@ -48,7 +48,7 @@ def test_every_reachable_kernel_variant_has_a_parity_case():
     assert any("/split" in c[4] for c in staged) and any("/split" not in c[4] for c in staged)
     # and the sweep reaches every kernel id the router knows of
     ids = {bfp8.bfp8_get_plan(op, M, N, K)["kernel"] for op, M, N, K in _sweep()}
-    assert ids == set(range(3, 16)), sorted(ids)
+    assert ids == set(range(3, 17)), sorted(ids)
 
 
 def test_plan_agrees_with_workspace_bytes_and_grid():
@@ -73,10 +73,20 @@ def test_routing_rules_read_off_the_plan():
         one = M == 1 and K <= one_token_k[op]
         if op in (cases.W8A8, cases.QW8A8, cases.W8A16):
             assert ("gemv" in name) == one, (op, M, N, K, name)
-        if op == cases.W8A16 and M <= 16 and not one:
-            assert name == "w8a16_stream"
-        if op == cases.BLK32:
-            want = "blk32_gemv" if one else "blk32_stream_lds" if M <= 16 else "blk32_stream"
+        if op in (cases.W8A16, cases.BLK32) and M <= 16 and not one:
+            # 8 < M <= 16: one token tile on the all-token kernel unless the
+            # streaming plan splits K; M <= 8 streams.
+            p = bfp8.bfp8_get_plan(op, M, N, K)
+            stream = "w8a16_stream" if op == cases.W8A16 else "blk32_stream_lds"
+            wide = "w8a16_wide" if op == cases.W8A16 else "blk32_wide"
+            if M <= 8:
+                assert name == stream, (op, M, N, K, name)
+            elif name == wide:
+                assert p["tile_m"] == 16 and p["workspace_bytes"] == 0, (op, M, N, K, p)
+            else:
+                assert name == stream and p["splits"] > 1, (op, M, N, K, p)
+        if op == cases.BLK32 and (one or M > 16):
+            want = "blk32_gemv" if one else "blk32_stream"
             assert name == want, (M, N, K, name)
         if op == cases.QW8A8 and name.endswith("_quant"):
             assert M == 1 or M <= 8
@@ -105,6 +115,6 @@ def test_quantiser_plans():
 
 
 def test_kernel_names():
-    names = [bfp8.bfp8_kernel_name(k) for k in range(16)]
-    assert len(set(names)) == 16 and "unknown kernel" not in names
+    names = [bfp8.bfp8_kernel_name(k) for k in range(17)]
+    assert len(set(names)) == 17 and "unknown kernel" not in names
     assert bfp8.bfp8_kernel_name(99) == "unknown kernel"
