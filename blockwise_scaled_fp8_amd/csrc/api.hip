@@ -112,7 +112,7 @@ int route(int op, int64_t M, int64_t N, int64_t K) {
             return BFP8_KERNEL_W8A16_STREAM;
         case BFP8_OP_GEMM_W8A16_BLK32_UE8M0:
             if (one_token(M, K)) return BFP8_KERNEL_BLK32_GEMV;
-            if (w8a16_one_tile(M, N, K)) return BFP8_KERNEL_BLK32_WIDE;
+            if (blk32_wide(M, N, K)) return BFP8_KERNEL_BLK32_WIDE;
             return M <= kStreamMaxM ? BFP8_KERNEL_BLK32_STREAM_LDS : BFP8_KERNEL_BLK32_STREAM;
         case BFP8_OP_QUANT_ACT_1X128:
             return BFP8_KERNEL_QUANT_ACT;
@@ -357,7 +357,7 @@ bfp8_status bfp8_gemm_w8a16_blk32_ue8m0(const void* x, int x_dtype, const uint8_
     switch (route(BFP8_OP_GEMM_W8A16_BLK32_UE8M0, M, N, K)) {
         case BFP8_KERNEL_BLK32_GEMV:   // one token: dot products on the vector ALUs
             return launched(launch_w8a16_blk32_gemv(x, wq, e8m0, y, y_dtype, N, K, as_stream(stream)));
-        case BFP8_KERNEL_BLK32_WIDE:   // 8 < M <= 16: one token tile, token rows through LDS
+        case BFP8_KERNEL_BLK32_WIDE:   // M > 8: all tokens of a group per weight tile, rows through LDS
             return launched(launch_w8a16_blk32_wide(x, wq, e8m0, y, y_dtype, M, N, K, as_stream(stream)));
         default:
             return launched(launch_w8a16_blk32_stream(x, wq, e8m0, y, y_dtype, M, N, K, workspace,

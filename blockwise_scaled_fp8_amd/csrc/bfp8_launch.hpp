@@ -178,6 +178,18 @@ hipError_t launch_w8a16_tile(const void* x, bool x_bf16, const uint8_t* wq, cons
 inline bool w8a16_one_tile(int64_t M, int64_t N, int64_t K) {
     return M > kStreamMaxM / 2 && M <= kStreamMaxM && K <= kTileMaxK && plan_stream(M, N, K).splits == 1;
 }
+// Block-32 dispatch: the one-token kernel for M = 1 (K <= kOneTokenRouteK);
+// the all-token kernel (launch_w8a16_blk32_wide) for every M > 8 whose
+// streaming plan would not split K, one 16-token tile up to M = 16 and
+// token groups of 32 or 64 above (wide_shape); the streaming kernels
+// otherwise (M <= 8, and where K is split).  Above M = 16 the streaming
+// kernel runs one 16-token tile per workgroup and so reads the weights
+// once per tile; measured at 4096 x 7168 (us, streaming against
+// all-token): M = 17 19.8 / 11.4, 32 23.8 / 13.4, 64 44.0 / 16.5,
+// 128 86.0 / 26.5, 256 170.2 / 43.3.
+inline bool blk32_wide(int64_t M, int64_t N, int64_t K) {
+    return M > kStreamMaxM / 2 && K <= kTileMaxK && plan_stream(M, N, K).splits == 1;
+}
 // W8A16 blk128 dispatch: the streaming kernel for M <= 16 except where
 // w8a16_one_tile holds; the all-token kernel (launch_w8a16_wide) there and
 // for 16 < M <= 256 when K <= 4096 and either M <= 32 or M * N <= 2^19; the

@@ -159,11 +159,15 @@ BLK32_ONE_TOKEN = [(1, 4096, 4096, "blk32_gemv"), (1, 32, 128, "blk32_gemv"), (1
                    (1, 4096, 12416, "blk32_stream_lds")]
 BLK32_ONE_HOT_ONE_TOKEN = (1, 704, 256, "blk32_gemv")
 # Above the streaming range ([SM70] "Results" times M = 32 ... 4096).
-BLK32_ABOVE_16 = [(M, 4096, 7168, "blk32_stream") for M in (17, 32, 64, 128, 512)]
+BLK32_ABOVE_16 = [(17, 4096, 7168, "blk32_wide:16x32w8"), (32, 4096, 7168, "blk32_wide:16x32w8"),
+                  (64, 4096, 7168, "blk32_wide:32x32w8"), (128, 4096, 7168, "blk32_wide:32x64w8"),
+                  (512, 4096, 7168, "blk32_wide:32x64w8"), (100, 1024, 4096, "blk32_wide:16x32w8"),
+                  (200, 1024, 1024, "blk32_wide:16x64w8")]
 BLK32_WINDOW = (8, 512, 1024, "blk32_stream_lds")
 BLK32_ONE_HOT = (16, 704, 256, "blk32_wide:16x16w8")
 BLK32_ONE_HOT_STREAM = (8, 704, 256, "blk32_stream_lds")
-BLK32_ONE_HOT_ABOVE_16 = (17, 704, 256, "blk32_stream")
+BLK32_ONE_HOT_ABOVE_16 = (17, 704, 256, "blk32_wide:16x32w8")
+BLK32_ONE_HOT_ABOVE_16_SPLIT = (17, 704, 8320, "blk32_stream/split")
 BLK32_SPLIT_K = (4, 1024, 12288, "blk32_stream_lds/split")
 BLK32_SPLIT_K_16 = (16, 1024, 12288, "blk32_stream_lds/split")
 BLK32_SPLIT_K_ABOVE_16 = (20, 512, 12288, "blk32_stream/split")
@@ -190,7 +194,8 @@ def all_cases():
                 W8A16_TILE_SPLIT, [W8A16_TILE_ONE_HOT, W8A16_TILE_LARGE_RAGGED, W8A16_TILE_LARGE_ONE_HOT,
                                    W8A16_PREFILL_OPROJ, W8A16_DECODE_OPROJ]],
         BLK32: [BLK32_WORKLOAD, BLK32_ONE_TOKEN, BLK32_ONE_TILE, BLK32_ABOVE_16,
-                [BLK32_WINDOW, BLK32_ONE_HOT, BLK32_ONE_HOT_STREAM, BLK32_ONE_HOT_ABOVE_16, BLK32_ONE_HOT_ONE_TOKEN,
+                [BLK32_WINDOW, BLK32_ONE_HOT, BLK32_ONE_HOT_STREAM, BLK32_ONE_HOT_ABOVE_16,
+                 BLK32_ONE_HOT_ABOVE_16_SPLIT, BLK32_ONE_HOT_ONE_TOKEN,
                  BLK32_SPLIT_K, BLK32_SPLIT_K_16, BLK32_SPLIT_K_ABOVE_16]],
     }
     for op, tabs in tables.items():

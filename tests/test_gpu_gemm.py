@@ -506,14 +506,16 @@ def test_blk32_window_ends(gpu_lib, lo, hi):
 
 
 @pytest.mark.parametrize("case", [cases.BLK32_ONE_HOT, cases.BLK32_ONE_HOT_STREAM, cases.BLK32_ONE_HOT_ABOVE_16,
-                                  cases.BLK32_ONE_HOT_ONE_TOKEN], ids=lambda c: c[3])
+                                  cases.BLK32_ONE_HOT_ABOVE_16_SPLIT, cases.BLK32_ONE_HOT_ONE_TOKEN],
+                         ids=lambda c: c[3])
 @pytest.mark.parametrize("out", [torch.float32, torch.float16])
 def test_blk32_one_hot_all_codes_all_exponents_exact(gpu_lib, out, case):
     """Every finite code times every window exponent is produced exactly
     (fp16 subnormals at e = -14 included), by the all-token kernel with one
-    token tile (M = 16), the streaming kernel of M <= 8, the one for M > 16
-    (M = 17: a full token tile and a second one with a single live row) and
-    the one-token kernel (M = 1: one column k per call)."""
+    token tile (M = 16) and with a group of two (M = 17: a full tile and one
+    with a single live row), the streaming kernel of M <= 8, the one for
+    M > 16 with K split (M = 17, K = 8320) and the one-token kernel (M = 1:
+    one column k per call)."""
     exps = np.arange(-14, 8)
     M, N, K, kernel = case
     assert N == 32 * exps.size
@@ -572,10 +574,12 @@ def test_blk32_one_token_tile(gpu_lib, M, N, K, kernel):
 
 @pytest.mark.parametrize("M,N,K,kernel", cases.BLK32_ABOVE_16)
 def test_blk32_above_the_streaming_range(gpu_lib, M, N, K, kernel):
-    """M > 16 on the block-32 workload shape (N = 4096, K = 7168): one
-    16-token tile per workgroup, ragged last tile at M = 17; fp32 output
-    against the oracle (all rows up to M = 64, sampled rows above, the last
-    tile's rows always included) and fp16 output as RNE of the fp32 result."""
+    """M > 16 on the block-32 workload shape (N = 4096, K = 7168) and on
+    1024 x 4096: all tokens of a group of 32 or 64 per 16- or 32-row weight
+    tile, several token groups (grid.y) at M = 100, 128 and 512, a ragged
+    last tile at M = 17 and 100; fp32 output against the oracle (all rows up
+    to M = 64, sampled rows above, the last tile's rows always included) and
+    fp16 output as RNE of the fp32 result."""
     say("blk32 M > 16", M)
     expect(BLK32, M, N, K, kernel)
     x, wq, e8 = _blk32_inputs(M, N, K, 40 + M)

@@ -86,8 +86,13 @@ def test_routing_rules_read_off_the_plan():
             else:
                 assert name == stream and p["splits"] > 1, (op, M, N, K, p)
         if op == cases.BLK32 and (one or M > 16):
-            want = "blk32_gemv" if one else "blk32_stream"
-            assert name == want, (M, N, K, name)
+            p = bfp8.bfp8_get_plan(op, M, N, K)
+            if one:
+                assert name == "blk32_gemv", (M, N, K, name)
+            elif name == "blk32_stream":
+                assert p["splits"] > 1, (M, N, K, p)   # only where the streaming plan splits K
+            else:
+                assert name == "blk32_wide" and p["workspace_bytes"] == 0, (M, N, K, p)
         if op == cases.QW8A8 and name.endswith("_quant"):
             assert M == 1 or M <= 8
 
