@@ -112,6 +112,7 @@ int route(int op, int64_t M, int64_t N, int64_t K) {
             return BFP8_KERNEL_W8A16_STREAM;
         case BFP8_OP_GEMM_W8A16_BLK32_UE8M0:
             if (one_token(M, K)) return BFP8_KERNEL_BLK32_GEMV;
+            if (blk32_tile(M, N, K)) return BFP8_KERNEL_BLK32_TILE;
             if (blk32_wide(M, N, K)) return BFP8_KERNEL_BLK32_WIDE;
             return M <= kStreamMaxM ? BFP8_KERNEL_BLK32_STREAM_LDS : BFP8_KERNEL_BLK32_STREAM;
         case BFP8_OP_QUANT_ACT_1X128:
@@ -138,6 +139,7 @@ size_t kernel_workspace(int kernel, int64_t M, int64_t N, int64_t K) {
         case BFP8_KERNEL_W8A8_TILE:
             return K <= kTileMaxK ? tile_workspace_bytes(M, N, K) : 0;
         case BFP8_KERNEL_W8A16_TILE:
+        case BFP8_KERNEL_BLK32_TILE:
             return K <= kTileMaxK ? tile16_workspace_bytes(M, N, K) : 0;
         default:
             return 0;
@@ -359,6 +361,8 @@ bfp8_status bfp8_gemm_w8a16_blk32_ue8m0(const void* x, int x_dtype, const uint8_
             return launched(launch_w8a16_blk32_gemv(x, wq, e8m0, y, y_dtype, N, K, as_stream(stream)));
         case BFP8_KERNEL_BLK32_WIDE:   // M > 8: all tokens of a group per weight tile, rows through LDS
             return launched(launch_w8a16_blk32_wide(x, wq, e8m0, y, y_dtype, M, N, K, as_stream(stream)));
+        case BFP8_KERNEL_BLK32_TILE:   // tiled MFMA kernel, scales applied in the widening
+            return launched(launch_w8a16_blk32_tile(x, wq, e8m0, y, y_dtype, M, N, K, workspace, as_stream(stream)));
         default:
             return launched(launch_w8a16_blk32_stream(x, wq, e8m0, y, y_dtype, M, N, K, workspace,
                                                       as_stream(stream)));
@@ -493,7 +497,8 @@ bfp8_status bfp8_get_plan(int op, int64_t M, int64_t N, int64_t K, bfp8_plan* pl
             break;
         }
         case BFP8_KERNEL_W8A8_TILE:
-        case BFP8_KERNEL_W8A16_TILE: {
+        case BFP8_KERNEL_W8A16_TILE:
+        case BFP8_KERNEL_BLK32_TILE: {
             const TileInfo t = p.kernel == BFP8_KERNEL_W8A8_TILE ? tile_info(M, N, K) : tile16_info(M, N, K);
             p.tile_n = t.tile_n;
             p.tile_m = t.tile_m;
@@ -528,6 +533,7 @@ const char* bfp8_kernel_name(int kernel) {
         case BFP8_KERNEL_BLK32_STREAM: return "blk32_stream";
         case BFP8_KERNEL_BLK32_GEMV: return "blk32_gemv";
         case BFP8_KERNEL_BLK32_WIDE: return "blk32_wide";
+        case BFP8_KERNEL_BLK32_TILE: return "blk32_tile";
         default: return "unknown kernel";
     }
 }

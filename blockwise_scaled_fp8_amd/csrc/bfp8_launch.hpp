@@ -165,6 +165,10 @@ hipError_t launch_w8a8_stream_quant(const void* x, bool x_bf16, const uint8_t* w
                                     void* workspace, hipStream_t stream);
 hipError_t launch_w8a16_tile(const void* x, bool x_bf16, const uint8_t* wq, const float* ws, void* y,
                              int y_dtype, int64_t M, int64_t N, int64_t K, void* workspace, hipStream_t stream);
+// The W8A16 tiled kernel for block-32 weights (fp16 activations; N a
+// multiple of 32, the plan and workspace of launch_w8a16_tile).
+hipError_t launch_w8a16_blk32_tile(const void* x, const uint8_t* wq, const uint8_t* e8m0, void* y, int y_dtype,
+                                   int64_t M, int64_t N, int64_t K, void* workspace, hipStream_t stream);
 // W8A16 (blk128 and block-32) with 8 < M <= 16, when the streaming plan
 // would not split K: the all-token kernel with one 16-token tile.  Its
 // token rows arrive by direct-to-LDS loads of whole lines into per-wave
@@ -178,18 +182,6 @@ hipError_t launch_w8a16_tile(const void* x, bool x_bf16, const uint8_t* wq, cons
 inline bool w8a16_one_tile(int64_t M, int64_t N, int64_t K) {
     return M > kStreamMaxM / 2 && M <= kStreamMaxM && K <= kTileMaxK && plan_stream(M, N, K).splits == 1;
 }
-// Block-32 dispatch: the one-token kernel for M = 1 (K <= kOneTokenRouteK);
-// the all-token kernel (launch_w8a16_blk32_wide) for every M > 8 whose
-// streaming plan would not split K, one 16-token tile up to M = 16 and
-// token groups of 32 or 64 above (wide_shape); the streaming kernels
-// otherwise (M <= 8, and where K is split).  Above M = 16 the streaming
-// kernel runs one 16-token tile per workgroup and so reads the weights
-// once per tile; measured at 4096 x 7168 (us, streaming against
-// all-token): M = 17 19.8 / 11.4, 32 23.8 / 13.4, 64 44.0 / 16.5,
-// 128 86.0 / 26.5, 256 170.2 / 43.3.
-inline bool blk32_wide(int64_t M, int64_t N, int64_t K) {
-    return M > kStreamMaxM / 2 && K <= kTileMaxK && plan_stream(M, N, K).splits == 1;
-}
 // W8A16 blk128 dispatch: the streaming kernel for M <= 16 except where
 // w8a16_one_tile holds; the all-token kernel (launch_w8a16_wide) there and
 // for 16 < M <= 256 when K <= 4096 and either M <= 32 or M * N <= 2^19; the
@@ -202,6 +194,31 @@ inline bool w8a16_wide(int64_t M, int64_t N, int64_t K) {
     if (w8a16_one_tile(M, N, K)) return true;
     return M > kStreamMaxM && M <= 16 * kStreamMaxM && K <= 4096 &&
            (M <= 2 * kStreamMaxM || M * N <= ((int64_t)1 << 19));
+}
+// Block-32 dispatch: the one-token kernel for M = 1 (K <= kOneTokenRouteK);
+// the tiled kernel where blk32_tile holds; the all-token kernel
+// (launch_w8a16_blk32_wide) for the other M > 8 whose streaming plan would
+// not split K, one 16-token tile up to M = 16 and token groups of 32 or 64
+// above (wide_shape); the streaming kernels otherwise (M <= 8, and where K
+// is split).  Above M = 16 the streaming
+// kernel runs one 16-token tile per workgroup and so reads the weights
+// once per tile; measured at 4096 x 7168 (us, streaming against
+// all-token): M = 17 19.8 / 11.4, 32 23.8 / 13.4, 64 44.0 / 16.5,
+// 128 86.0 / 26.5, 256 170.2 / 43.3.
+inline bool blk32_wide(int64_t M, int64_t N, int64_t K) {
+    return M > kStreamMaxM / 2 && K <= kTileMaxK && plan_stream(M, N, K).splits == 1;
+}
+// Block-32 on the tiled MFMA kernel (launch_w8a16_blk32_tile, the W8A16
+// tiles with the UE8M0 scales applied in the widening and no promotion
+// step) for M > 32 unless M <= 256, K <= 4096 and M * N <= 2^19; the
+// all-token kernel keeps the rest.  Measured (us, all-token / tiled):
+// 4096 x 7168 M = 17 11.4 / 13.4, 32 13.4 / 13.7, 64 16.5 / 14.4,
+// 128 26.7 / 21.4, 256 43.4 / 26.0, 512 76.9 / 38.1, 1024 145 / 63.2,
+// 4096 548 / 204; 1024 x 4096 M = 64 6.3 / 9.9, 256 7.6 / 16.5,
+// 1024 22.8 / 20.0; 12288 x 4096 M = 64 31.4 / 23.1, 256 72.7 / 48.1.
+inline bool blk32_tile(int64_t M, int64_t N, int64_t K) {
+    if (M <= 2 * kStreamMaxM || K > kTileMaxK) return false;
+    return !(M <= 16 * kStreamMaxM && K <= 4096 && M * N <= ((int64_t)1 << 19));
 }
 // One token (W8A8 codes, W8A8 with activations quantised in the kernel,
 // W8A16 blk128, block-32): dot-product kernels on the vector ALUs, no

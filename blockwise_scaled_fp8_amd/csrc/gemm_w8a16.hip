@@ -40,11 +40,6 @@
 
 namespace bfp8 {
 
-// The UE8M0 byte E of a 32x32 weight tile as the fp32 scale 2^(E - 127)
-// (the byte is an fp32 exponent field; prepared weights have E in
-// [113, 134]).
-__device__ __forceinline__ float ue8m0_scale(uint32_t E) { return __builtin_bit_cast(float, E << 23); }
-
 constexpr int kW8A16Chunk = 4;   // 128-K blocks per wave with loads in flight together
 
 // blk32 with M > 16: one 16-token tile per workgroup (grid z), register

@@ -50,14 +50,20 @@ constexpr int kCUs = 256;
 
 // Token operand of a tile configuration: E4M3 codes with 1x128 scales
 // (W8A8), or 16-bit activations with E4M3 weights widened in registers
-// (W8A16, bf16 or fp16).
-enum TileX { kTileCodes = 0, kTileBf16 = 1, kTileF16 = 2 };
+// (W8A16, bf16 or fp16, 128x128 fp32 weight scales; or fp16 with block-32
+// UE8M0 weight scales, kTileF16Blk32).
+enum TileX { kTileCodes = 0, kTileBf16 = 1, kTileF16 = 2, kTileF16Blk32 = 3 };
 
 template <int BN_, int BM_, int WAVES_N, int WAVES_M, bool SPLIT, int X_ = kTileCodes, int FILL_ROWS_ = 0>
 struct TileCfg {
     static constexpr int BN = BN_, BM = BM_;
     static constexpr int X = X_;
     static constexpr bool kX16 = X_ != kTileCodes;  // 16-bit token rows, no token scales
+    static constexpr bool kXBf16 = X_ == kTileBf16;
+    // Block-32 weights: the stage's per-wave scale word holds the four UE8M0
+    // bytes of the block's 32x32 tiles in the wave's 32-row band, applied
+    // in the widening, and the MFMAs accumulate across K with no promotion.
+    static constexpr bool kBlk32 = X_ == kTileF16Blk32;
     static constexpr bool kSplit = SPLIT;           // plans for this shape may split K
     static constexpr int kWavesN = WAVES_N, kWavesM = WAVES_M;
     static constexpr int kWaves = kWavesN * kWavesM;
@@ -97,6 +103,7 @@ struct TileCfg {
     static_assert(BN % (kRowsPerLoad * kWaves) == 0 && BM % (kBRowsPerLoad * kWaves) == 0, "load split");
     static_assert(kX16 || (kXsLanes >= 1 && kXsLanes <= kWave), "token-scale loads");
     static_assert(128 % kWaveN == 0 || kWaveN % 128 == 0, "one weight-scale row per wave");
+    static_assert(!kBlk32 || kWaveN == 32, "one 32-row scale band per wave");
     static_assert(kTi >= 1 && kTj >= 1 && kStages >= 2 && (kStages - 2) * kVmemPerStage < 64, "wave tile");
 };
 
@@ -284,7 +291,7 @@ __device__ __forceinline__ void store8(void* y, int y_dtype, int64_t idx, f32x4 
 template <class C>
 __global__ __launch_bounds__(C::kThreads, 1) void w8a8_tile_kernel(
     const void* __restrict__ xin, const float* __restrict__ xs,
-    const uint8_t* __restrict__ wq, const float* __restrict__ ws,
+    const uint8_t* __restrict__ wq, const void* __restrict__ wscale,
     void* __restrict__ y, int y_dtype, int64_t M, int64_t N, int64_t K,
     int64_t tiles_n, int64_t tiles_m, int64_t splits, int64_t kb_per_split,
     float* __restrict__ partials, uint32_t* __restrict__ counters) {
@@ -324,10 +331,29 @@ __global__ __launch_bounds__(C::kThreads, 1) void w8a8_tile_kernel(
     const int q_stride_b = (int)(C::kBRowsPerLoad * C::kWaves * K * kXBytes);
     const int xs_off = (int)((C::kXsLanes * wave + lane) * KB * 4);
 
-    // Weight scales: one row of ws per wave (its weight rows share it).
-    int64_t nb = (n0 + C::kWaveN * wn) / 128;
-    nb = nb < NB ? nb : NB - 1;
-    const i32x4 rsrc_ws = buffer_rsrc(ws + nb * KB, (uint32_t)(KB * 4));
+    // Weight scales: one row of ws per wave (its weight rows share it), or
+    // for block-32 the wave's 32-row band of UE8M0 bytes (K / 32 a band, a
+    // dword of four per 128-K block).  A wave whose rows lie past N takes
+    // the last row or band, so its scale loads stay inside the array.
+    const i32x4 rsrc_ws = [&] {
+        if constexpr (C::kBlk32) {
+            int64_t band = (n0 + C::kWaveN * wn) / 32;
+            band = band < N / 32 ? band : N / 32 - 1;
+            return buffer_rsrc(static_cast<const uint8_t*>(wscale) + band * (K / 32), (uint32_t)(KB * 4));
+        } else {
+            int64_t nb = (n0 + C::kWaveN * wn) / 128;
+            nb = nb < NB ? nb : NB - 1;
+            return buffer_rsrc(static_cast<const float*>(wscale) + nb * KB, (uint32_t)(KB * 4));
+        }
+    }();
+    // Block-32: this lane's two UE8M0 scales of a block (chunk g, K 16 g ..
+    // 16 g + 15, lies in tile 4 kb + g / 2; chunk g + 4 in tile
+    // 4 kb + 2 + g / 2) from the stage's scale word.
+    auto band_scales = [&](const uint8_t* stage, float& e0, float& e1) {
+        const uint32_t sw = reinterpret_cast<const uint32_t*>(stage + C::kOffWs)[wave];
+        e0 = ue8m0_scale((sw >> (8 * (g >> 1))) & 0xFF);
+        e1 = ue8m0_scale((sw >> (8 * (2 + (g >> 1)))) & 0xFF);
+    };
 
     f32x4 acc[C::kTi][C::kTj];
 #pragma unroll
@@ -353,13 +379,15 @@ __global__ __launch_bounds__(C::kThreads, 1) void w8a8_tile_kernel(
         // token tile column j is read (one ahead) and multiplied by every row;
         // the promotion of column j - 1 follows the MFMAs of column j.
         const float wsc = reinterpret_cast<const float*>(stage + C::kOffWs)[wave];
+        float e0 = 1.0f, e1 = 1.0f;
+        if constexpr (C::kBlk32) band_scales(stage, e0, e1);
         u32x4 aop[C::kTi][4];
 #pragma unroll
         for (int i = 0; i < C::kTi; ++i) {
             const i32x8 af = read_frag<true>(stage, a_base + a_row(i, r), g);
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj)
-                aop[i][jj] = widen8<C::X == kTileBf16>((uint32_t)af[2 * jj], (uint32_t)af[2 * jj + 1]);
+                aop[i][jj] = widen8<C::kXBf16>((uint32_t)af[2 * jj], (uint32_t)af[2 * jj + 1], jj < 2 ? e0 : e1);
         }
         auto read_b = [&](int j, u32x4 (&b)[4]) {
             const int row = C::kWaveM * wm + 16 * j + r;
@@ -377,17 +405,22 @@ __global__ __launch_bounds__(C::kThreads, 1) void w8a8_tile_kernel(
             if (j + 1 < C::kTj) read_b(j + 1, bnext);
 #pragma unroll
             for (int i = 0; i < C::kTi; ++i) {
-                f32x4 blk = zero;
+                if constexpr (C::kBlk32) {
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj)
-                    blk = C::X == kTileBf16 ? mfma_bf16_16x16x32(aop[i][jj], bcur[jj], blk)
-                                            : mfma_f16_16x16x32(aop[i][jj], bcur[jj], blk);
-                tmp[c][i] = blk;
+                    for (int jj = 0; jj < 4; ++jj) acc[i][j] = mfma_f16_16x16x32(aop[i][jj], bcur[jj], acc[i][j]);
+                } else {
+                    f32x4 blk = zero;
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj)
+                        blk = C::kXBf16 ? mfma_bf16_16x16x32(aop[i][jj], bcur[jj], blk)
+                                        : mfma_f16_16x16x32(aop[i][jj], bcur[jj], blk);
+                    tmp[c][i] = blk;
+                }
             }
             if constexpr (decltype(refill)::value)
                 issue_stage<C>(fill, rsrc_a, rsrc_b, rsrc_xs, rsrc_ws, lane_off_a, lane_off_b, q_stride, q_stride_b,
                                xs_off, fill_kb, wave, lane, C::fill_lo_j(j), C::fill_lo_j(j + 1), false);
-            if (j > 0) {
+            if (!C::kBlk32 && j > 0) {
 #pragma unroll
                 for (int i = 0; i < C::kTi; ++i)
 #pragma unroll
@@ -399,11 +432,13 @@ __global__ __launch_bounds__(C::kThreads, 1) void w8a8_tile_kernel(
                 for (int jj = 0; jj < 4; ++jj) bcur[jj] = bnext[jj];
             }
         }
+        if constexpr (!C::kBlk32) {
 #pragma unroll
-        for (int i = 0; i < C::kTi; ++i)
+            for (int i = 0; i < C::kTi; ++i)
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                acc[i][C::kTj - 1][e] = __builtin_fmaf(tmp[(C::kTj - 1) & 1][i][e], wsc, acc[i][C::kTj - 1][e]);
+                for (int e = 0; e < 4; ++e)
+                    acc[i][C::kTj - 1][e] = __builtin_fmaf(tmp[(C::kTj - 1) & 1][i][e], wsc, acc[i][C::kTj - 1][e]);
+        }
       } else if constexpr (C::kX16) {
         // W8A16: per 16x16 tile and block, four 16x16x32 MFMAs on weights
         // widened in registers to their exact 16-bit values (widen8).  MFMA jj
@@ -420,29 +455,36 @@ __global__ __launch_bounds__(C::kThreads, 1) void w8a8_tile_kernel(
                 bfr[j][jj] = *reinterpret_cast<const u32x4*>(
                     stage + C::kStageA + swz_b16(row, 2 * g + 8 * (jj >> 1) + (jj & 1)));
         }
+        float e0 = 1.0f, e1 = 1.0f;
+        if constexpr (C::kBlk32) band_scales(stage, e0, e1);
         f32x4 tmp[2][C::kTj];
         i32x8 af = read_frag<true>(stage, a_base + a_row(0, r), g);
 #pragma unroll
         for (int i = 0; i < C::kTi; ++i) {
             const int c = i & 1;
-            const u32x4 aop[4] = {widen8<C::X == kTileBf16>((uint32_t)af[0], (uint32_t)af[1]),
-                                  widen8<C::X == kTileBf16>((uint32_t)af[2], (uint32_t)af[3]),
-                                  widen8<C::X == kTileBf16>((uint32_t)af[4], (uint32_t)af[5]),
-                                  widen8<C::X == kTileBf16>((uint32_t)af[6], (uint32_t)af[7])};
+            const u32x4 aop[4] = {widen8<C::kXBf16>((uint32_t)af[0], (uint32_t)af[1], e0),
+                                  widen8<C::kXBf16>((uint32_t)af[2], (uint32_t)af[3], e0),
+                                  widen8<C::kXBf16>((uint32_t)af[4], (uint32_t)af[5], e1),
+                                  widen8<C::kXBf16>((uint32_t)af[6], (uint32_t)af[7], e1)};
             if (i + 1 < C::kTi) af = read_frag<true>(stage, a_base + a_row(i + 1, r), g);
 #pragma unroll
             for (int j = 0; j < C::kTj; ++j) {
-                f32x4 blk = zero;
+                if constexpr (C::kBlk32) {
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj)
-                    blk = C::X == kTileBf16 ? mfma_bf16_16x16x32(aop[jj], bfr[j][jj], blk)
-                                            : mfma_f16_16x16x32(aop[jj], bfr[j][jj], blk);
-                tmp[c][j] = blk;
+                    for (int jj = 0; jj < 4; ++jj) acc[i][j] = mfma_f16_16x16x32(aop[jj], bfr[j][jj], acc[i][j]);
+                } else {
+                    f32x4 blk = zero;
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj)
+                        blk = C::kXBf16 ? mfma_bf16_16x16x32(aop[jj], bfr[j][jj], blk)
+                                        : mfma_f16_16x16x32(aop[jj], bfr[j][jj], blk);
+                    tmp[c][j] = blk;
+                }
             }
             if constexpr (decltype(refill)::value)
                 issue_stage<C>(fill, rsrc_a, rsrc_b, rsrc_xs, rsrc_ws, lane_off_a, lane_off_b, q_stride, q_stride_b,
                                xs_off, fill_kb, wave, lane, C::fill_lo(i), C::fill_lo(i + 1), false);
-            if (i > 0) {
+            if (!C::kBlk32 && i > 0) {
 #pragma unroll
                 for (int j = 0; j < C::kTj; ++j)
 #pragma unroll
@@ -450,11 +492,13 @@ __global__ __launch_bounds__(C::kThreads, 1) void w8a8_tile_kernel(
                         acc[i - 1][j][e] = __builtin_fmaf(tmp[c ^ 1][j][e], wsc, acc[i - 1][j][e]);
             }
         }
+        if constexpr (!C::kBlk32) {
 #pragma unroll
-        for (int j = 0; j < C::kTj; ++j)
+            for (int j = 0; j < C::kTj; ++j)
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                acc[C::kTi - 1][j][e] = __builtin_fmaf(tmp[(C::kTi - 1) & 1][j][e], wsc, acc[C::kTi - 1][j][e]);
+                for (int e = 0; e < 4; ++e)
+                    acc[C::kTi - 1][j][e] = __builtin_fmaf(tmp[(C::kTi - 1) & 1][j][e], wsc, acc[C::kTi - 1][j][e]);
+        }
       } else {
         const float wsc = reinterpret_cast<const float*>(stage + C::kOffWs)[wave];
         const float* xs_lds = reinterpret_cast<const float*>(stage + C::kOffXs);
@@ -715,7 +759,7 @@ size_t counter_bytes(const TilePlan& p) {
 }
 
 template <class C>
-void launch(const TilePlan& p, const void* xq, const float* xs, const uint8_t* wq, const float* ws, void* y,
+void launch(const TilePlan& p, const void* xq, const float* xs, const uint8_t* wq, const void* ws, void* y,
             int y_dtype, int64_t M, int64_t N, int64_t K, float* partials, uint32_t* counters,
             hipStream_t stream) {
     const dim3 grid((unsigned)(p.tiles_n * p.tiles_m * p.splits));
@@ -788,6 +832,21 @@ hipError_t launch_w8a16_tile(const void* x, bool x_bf16, const uint8_t* wq, cons
         if (x_bf16) launch<Cfg16_128<kTileBf16>>(p, x, nullptr, wq, ws, y, y_dtype, M, N, K, partials, counters, stream);
         else launch<Cfg16_128<kTileF16>>(p, x, nullptr, wq, ws, y, y_dtype, M, N, K, partials, counters, stream);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_w8a16_blk32_tile(const void* x, const uint8_t* wq, const uint8_t* e8m0, void* y, int y_dtype,
+                                   int64_t M, int64_t N, int64_t K, void* workspace, hipStream_t stream) {
+    const TilePlan p = plan_tile16(M, N, K);
+    uint32_t* counters;
+    float* partials;
+    if (!split_parts(p, workspace, counters, partials)) return hipErrorInvalidValue;
+    if (p.shape == TileShape::k16_256)
+        launch<Cfg16_256<kTileF16Blk32>>(p, x, nullptr, wq, e8m0, y, y_dtype, M, N, K, partials, counters, stream);
+    else if (p.shape == TileShape::k16_64)
+        launch<Cfg16_64<kTileF16Blk32>>(p, x, nullptr, wq, e8m0, y, y_dtype, M, N, K, partials, counters, stream);
+    else
+        launch<Cfg16_128<kTileF16Blk32>>(p, x, nullptr, wq, e8m0, y, y_dtype, M, N, K, partials, counters, stream);
     return hipGetLastError();
 }
 

@@ -290,9 +290,12 @@ size_t bfp8_workspace_bytes(int op, int64_t M, int64_t N, int64_t K);
  *                 reads all tokens per weight tile for M <= 16 *
  *                 m_stream_max when K <= 4096 and either M <= 2 *
  *                 m_stream_max or M * N <= 2^19, and uses its tiled MFMA
- *                 kernel otherwise; blk32 reads all tokens of a group of
- *                 32 or 64 per weight tile, and streams one 16-token tile
- *                 per workgroup only where that plan splits K.
+ *                 kernel otherwise; blk32 runs the same tiled kernel
+ *                 (scales applied in the widening) for M > 2 *
+ *                 m_stream_max unless M <= 16 * m_stream_max, K <= 4096
+ *                 and M * N <= 2^19, reads all tokens of a group of 32 or
+ *                 64 per weight tile otherwise, and streams one 16-token
+ *                 tile per workgroup only where that plan splits K.
  * Any output pointer may be NULL.
  */
 bfp8_status bfp8_get_limits(int op, int64_t* k_multiple, int64_t* n_multiple,
@@ -322,7 +325,8 @@ enum {
     BFP8_KERNEL_BLK32_STREAM = 14,      /* block-32, M > 16 with K split: one 16-token tile per workgroup */
     BFP8_KERNEL_BLK32_GEMV = 15,        /* block-32, one token: dot products on the vector ALUs */
     BFP8_KERNEL_BLK32_WIDE = 16,        /* block-32, M > 8: all tokens of a group per weight tile */
-    BFP8_KERNEL_COUNT = 17
+    BFP8_KERNEL_BLK32_TILE = 17,        /* block-32, larger M: tiled MFMA kernel */
+    BFP8_KERNEL_COUNT = 18
 };
 
 /* A call's launch plan (filled by bfp8_get_plan). */

@@ -160,9 +160,17 @@ BLK32_ONE_TOKEN = [(1, 4096, 4096, "blk32_gemv"), (1, 32, 128, "blk32_gemv"), (1
 BLK32_ONE_HOT_ONE_TOKEN = (1, 704, 256, "blk32_gemv")
 # Above the streaming range ([SM70] "Results" times M = 32 ... 4096).
 BLK32_ABOVE_16 = [(17, 4096, 7168, "blk32_wide:16x32w8"), (32, 4096, 7168, "blk32_wide:16x32w8"),
-                  (64, 4096, 7168, "blk32_wide:32x32w8"), (128, 4096, 7168, "blk32_wide:32x64w8"),
-                  (512, 4096, 7168, "blk32_wide:32x64w8"), (100, 1024, 4096, "blk32_wide:16x32w8"),
+                  (32, 8192, 1024, "blk32_wide:32x32w8"), (64, 4096, 2048, "blk32_wide:32x32w8"),
+                  (128, 4096, 4096, "blk32_wide:32x64w8"), (100, 1024, 4096, "blk32_wide:16x32w8"),
                   (200, 1024, 1024, "blk32_wide:16x64w8")]
+# Larger M: the W8A16 tiled kernel with the UE8M0 scales applied in the
+# widening; every tile shape, split and unsplit, ragged M and N (N = 1056
+# and 4128: waves of the last weight tile past N read the last scale band).
+BLK32_TILE = [(64, 4096, 7168, "blk32_tile:128x64w8/split"), (48, 16384, 512, "blk32_tile:128x64w8"),
+              (128, 4096, 7168, "blk32_tile:128x128w8/split"), (300, 1056, 2048, "blk32_tile:128x128w8/split"),
+              (600, 256, 256, "blk32_tile:128x128w8"), (2048, 4096, 256, "blk32_tile:256x128w8"),
+              (2000, 4128, 512, "blk32_tile:256x128w8")]
+BLK32_TILE_ONE_HOT = (300, 704, 256, "blk32_tile:128x128w8")
 BLK32_WINDOW = (8, 512, 1024, "blk32_stream_lds")
 BLK32_ONE_HOT = (16, 704, 256, "blk32_wide:16x16w8")
 BLK32_ONE_HOT_STREAM = (8, 704, 256, "blk32_stream_lds")
@@ -193,7 +201,7 @@ def all_cases():
                 W8A16_ONE_HOT,
                 W8A16_TILE_SPLIT, [W8A16_TILE_ONE_HOT, W8A16_TILE_LARGE_RAGGED, W8A16_TILE_LARGE_ONE_HOT,
                                    W8A16_PREFILL_OPROJ, W8A16_DECODE_OPROJ]],
-        BLK32: [BLK32_WORKLOAD, BLK32_ONE_TOKEN, BLK32_ONE_TILE, BLK32_ABOVE_16,
+        BLK32: [BLK32_WORKLOAD, BLK32_ONE_TOKEN, BLK32_ONE_TILE, BLK32_ABOVE_16, BLK32_TILE, [BLK32_TILE_ONE_HOT],
                 [BLK32_WINDOW, BLK32_ONE_HOT, BLK32_ONE_HOT_STREAM, BLK32_ONE_HOT_ABOVE_16,
                  BLK32_ONE_HOT_ABOVE_16_SPLIT, BLK32_ONE_HOT_ONE_TOKEN,
                  BLK32_SPLIT_K, BLK32_SPLIT_K_16, BLK32_SPLIT_K_ABOVE_16]],

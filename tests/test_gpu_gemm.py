@@ -506,16 +506,18 @@ def test_blk32_window_ends(gpu_lib, lo, hi):
 
 
 @pytest.mark.parametrize("case", [cases.BLK32_ONE_HOT, cases.BLK32_ONE_HOT_STREAM, cases.BLK32_ONE_HOT_ABOVE_16,
-                                  cases.BLK32_ONE_HOT_ABOVE_16_SPLIT, cases.BLK32_ONE_HOT_ONE_TOKEN],
-                         ids=lambda c: c[3])
+                                  cases.BLK32_ONE_HOT_ABOVE_16_SPLIT, cases.BLK32_TILE_ONE_HOT,
+                                  cases.BLK32_ONE_HOT_ONE_TOKEN], ids=lambda c: c[3])
 @pytest.mark.parametrize("out", [torch.float32, torch.float16])
 def test_blk32_one_hot_all_codes_all_exponents_exact(gpu_lib, out, case):
     """Every finite code times every window exponent is produced exactly
     (fp16 subnormals at e = -14 included), by the all-token kernel with one
     token tile (M = 16) and with a group of two (M = 17: a full tile and one
     with a single live row), the streaming kernel of M <= 8, the one for
-    M > 16 with K split (M = 17, K = 8320) and the one-token kernel (M = 1:
-    one column k per call)."""
+    M > 16 with K split (M = 17, K = 8320), the tiled kernel (M = 300: the
+    last 128-row weight tile ends at N = 704, its waves past N reading the
+    last scale band) and the one-token kernel (M = 1: one column k per
+    call)."""
     exps = np.arange(-14, 8)
     M, N, K, kernel = case
     assert N == 32 * exps.size
@@ -572,14 +574,42 @@ def test_blk32_one_token_tile(gpu_lib, M, N, K, kernel):
     assert torch.equal(y32.view(torch.int32), y2.view(torch.int32))
 
 
+@pytest.mark.parametrize("M,N,K,kernel", cases.BLK32_TILE)
+def test_blk32_tiled(gpu_lib, M, N, K, kernel):
+    """Block-32 on the W8A16 tiled kernel: 128x64, 128x128 and 256x128
+    tiles, K split and not, ragged M and N; fp32 output against the oracle
+    on all rows up to M = 64 and sampled rows above (the last token tile's
+    rows always included), fp16 output as RNE of the fp32 result, and a
+    rerun on the same workspace bit-identical."""
+    say("blk32 tiled", M, N, K, kernel)
+    expect(BLK32, M, N, K, kernel)
+    x, wq, e8 = _blk32_inputs(M, N, K, 80 + M)
+    xd, wqd, e8d = x.cuda(), dev(wq), dev(e8)
+    wsb = workspace(BLK32, M, N, K)
+    assert (wsb is not None) == kernel.endswith("/split")
+    y32 = run_blk32(xd, wqd, e8d, torch.float32, wsb)
+    yh = run_blk32(xd, wqd, e8d, torch.float16, wsb)
+    y2 = run_blk32(xd, wqd, e8d, torch.float32, wsb)
+    assert torch.equal(y32.view(torch.int32), y2.view(torch.int32))
+    if M <= 64:
+        rows = np.arange(M)
+    else:
+        rows = np.unique(np.concatenate([np.random.default_rng(M).choice(M, 40, replace=False),
+                                         np.arange(M - 16, M)]))
+    y0 = oracle.gemm_w8a16_blk32_ue8m0(f32(x[rows]), wq, e8)
+    assert_fp32_bar(y32[rows], y0, f"blk32 tiled M={M} N={N} K={K}")
+    assert_16bit_bar(yh[rows], y32[rows], y0, "f16", f"blk32 tiled M={M}")
+
+
 @pytest.mark.parametrize("M,N,K,kernel", cases.BLK32_ABOVE_16)
 def test_blk32_above_the_streaming_range(gpu_lib, M, N, K, kernel):
-    """M > 16 on the block-32 workload shape (N = 4096, K = 7168) and on
-    1024 x 4096: all tokens of a group of 32 or 64 per 16- or 32-row weight
-    tile, several token groups (grid.y) at M = 100, 128 and 512, a ragged
-    last tile at M = 17 and 100; fp32 output against the oracle (all rows up
-    to M = 64, sampled rows above, the last tile's rows always included) and
-    fp16 output as RNE of the fp32 result."""
+    """16 < M where block-32 reads all tokens of a group of 32 or 64 per 16-
+    or 32-row weight tile: the workload shape (N = 4096, K = 7168) at
+    M = 17 and 32, one and two row tiles, several token groups (grid.y) at
+    M = 64, 100, 128 and 200, a ragged last group at M = 17, 100 and 200;
+    fp32 output against the oracle (all rows up to M = 64, sampled rows
+    above, the last tile's rows always included) and fp16 output as RNE of
+    the fp32 result."""
     say("blk32 M > 16", M)
     expect(BLK32, M, N, K, kernel)
     x, wq, e8 = _blk32_inputs(M, N, K, 40 + M)

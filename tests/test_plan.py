@@ -48,7 +48,7 @@ def test_every_reachable_kernel_variant_has_a_parity_case():
     assert any("/split" in c[4] for c in staged) and any("/split" not in c[4] for c in staged)
     # and the sweep reaches every kernel id the router knows of
     ids = {bfp8.bfp8_get_plan(op, M, N, K)["kernel"] for op, M, N, K in _sweep()}
-    assert ids == set(range(3, 17)), sorted(ids)
+    assert ids == set(range(3, 18)), sorted(ids)
 
 
 def test_plan_agrees_with_workspace_bytes_and_grid():
@@ -87,8 +87,11 @@ def test_routing_rules_read_off_the_plan():
                 assert name == stream and p["splits"] > 1, (op, M, N, K, p)
         if op == cases.BLK32 and (one or M > 16):
             p = bfp8.bfp8_get_plan(op, M, N, K)
+            tiled = M > 32 and not (M <= 256 and K <= 4096 and M * N <= 1 << 19)
             if one:
                 assert name == "blk32_gemv", (M, N, K, name)
+            elif tiled:
+                assert name == "blk32_tile", (M, N, K, name)
             elif name == "blk32_stream":
                 assert p["splits"] > 1, (M, N, K, p)   # only where the streaming plan splits K
             else:
@@ -120,6 +123,6 @@ def test_quantiser_plans():
 
 
 def test_kernel_names():
-    names = [bfp8.bfp8_kernel_name(k) for k in range(17)]
-    assert len(set(names)) == 17 and "unknown kernel" not in names
+    names = [bfp8.bfp8_kernel_name(k) for k in range(18)]
+    assert len(set(names)) == 18 and "unknown kernel" not in names
     assert bfp8.bfp8_kernel_name(99) == "unknown kernel"
