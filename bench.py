@@ -545,6 +545,7 @@ def bench_decode(torch, bfp8, inputs, args):
         kern["prefill_gemm_w8a8_blk128"] = extra_prefill(torch, bfp8, inputs, args)
         torch.cuda.empty_cache()
         kern["blk32_m1"] = extra_blk32(torch, bfp8, inputs, args, M=1)
+        kern["blk32_m16"] = extra_blk32(torch, bfp8, inputs, args, M=16)
 
     if not args.no_cpu_baseline:
         import oracle
