@@ -182,25 +182,38 @@ hipError_t launch_w8a16_blk32_tile(const void* x, const uint8_t* wq, const uint8
 inline bool w8a16_one_tile(int64_t M, int64_t N, int64_t K) {
     return M > kStreamMaxM / 2 && M <= kStreamMaxM && K <= kTileMaxK && plan_stream(M, N, K).splits == 1;
 }
+// The W8A16 all-token launch of an M x N product fits one round of
+// workgroups on the 256 CUs.
+inline bool w16_one_round(int64_t M, int64_t N) {
+    const WideShape w = w16_wide_shape(M, N);
+    return (int64_t)w.groups_n * w.groups_m <= 256;
+}
 // W8A16 blk128 dispatch: the streaming kernel for M <= 16 except where
-// w8a16_one_tile holds; the all-token kernel (launch_w8a16_wide) there and
-// for 16 < M <= 256 when K <= 4096 and either M <= 32 or M * N <= 2^19; the
-// tiled kernel otherwise.  Measured, us, all with K = 4096: N = 4096 M = 32
-// / 64 / 128 9.6 / 11.9 / 17.8 against 13.7 / 14.2 / 20.4 tiled; N = 1024
-// M = 64 / 128 / 256 7.0 / 7.5 / 9.8 against 11.5 / 17.0 / 18.1; N = 12288
-// M = 32 22.3 vs 26.3, while from M = 64 there (27.5 vs 33.5) and from
-// K = 12288 the tiled kernel wins.
+// w8a16_one_tile holds; the all-token kernel (launch_w8a16_wide) there, for
+// 16 < M <= 256 when K <= 4096 and either M <= 32 or M * N <= 2^19, and for
+// 16 < M <= 64 when 4096 < K <= 8192 and its launch fits one round; the
+// tiled kernel otherwise.  Measured, us (all-token against tiled): K = 4096
+// N = 4096 M = 32 / 64 / 128 9.6 / 11.9 / 17.8 against 13.7 / 14.2 / 20.4;
+// N = 1024 M = 64 / 128 / 256 7.0 / 7.5 / 9.8 against 11.5 / 17.0 / 18.1;
+// N = 12288 M = 32 22.3 vs 26.3, but from M = 64 there the tiled kernel wins
+// (27.5 vs 33.5); 4096 x 7168 M = 17 / 32 / 48 / 64 11.5 / 13.5 / 14.8 /
+// 16.6 against 13.9 / 14.4 / 15.6 / 16.8, 1024 x 8192 M = 17 / 64 10.0 /
+// 11.3 against 13.0 / 13.7; but 12288 x 8192 (two rounds) M = 17 / 32 34.1
+// / 38.5 against 31.9 / 33.0 and 4096 x 12288 M = 17 / 32 18.2 / 22.2
+// against 17.3 / 17.6.
 inline bool w8a16_wide(int64_t M, int64_t N, int64_t K) {
     if (w8a16_one_tile(M, N, K)) return true;
-    return M > kStreamMaxM && M <= 16 * kStreamMaxM && K <= 4096 &&
-           (M <= 2 * kStreamMaxM || M * N <= ((int64_t)1 << 19));
+    if (M <= kStreamMaxM || M > 16 * kStreamMaxM) return false;
+    if (K <= 4096) return M <= 2 * kStreamMaxM || M * N <= ((int64_t)1 << 19);
+    return K <= 8192 && M <= 4 * kStreamMaxM && w16_one_round(M, N);
 }
 // Block-32 dispatch: the one-token kernel for M = 1 (K <= kOneTokenRouteK);
 // the tiled kernel where blk32_tile holds; the all-token kernel
 // (launch_w8a16_blk32_wide) for the other M > 8 whose streaming plan would
 // not split K, one 16-token tile up to M = 16 and token groups of 32 or 64
 // above (wide_shape); the streaming kernels otherwise (M <= 8, and where K
-// is split).  Above M = 16 the streaming
+// is split: w8a16_blk32_stream_lds_kernel up to M = 16, one 16-token tile
+// per workgroup above).  Above M = 16 the streaming
 // kernel runs one 16-token tile per workgroup and so reads the weights
 // once per tile; measured at 4096 x 7168 (us, streaming against
 // all-token): M = 17 19.8 / 11.4, 32 23.8 / 13.4, 64 44.0 / 16.5,
@@ -210,15 +223,22 @@ inline bool blk32_wide(int64_t M, int64_t N, int64_t K) {
 }
 // Block-32 on the tiled MFMA kernel (launch_w8a16_blk32_tile, the W8A16
 // tiles with the UE8M0 scales applied in the widening and no promotion
-// step) for M > 32 unless M <= 256, K <= 4096 and M * N <= 2^19; the
-// all-token kernel keeps the rest.  Measured (us, all-token / tiled):
-// 4096 x 7168 M = 17 11.4 / 13.4, 32 13.4 / 13.7, 64 16.5 / 14.4,
-// 128 26.7 / 21.4, 256 43.4 / 26.0, 512 76.9 / 38.1, 1024 145 / 63.2,
-// 4096 548 / 204; 1024 x 4096 M = 64 6.3 / 9.9, 256 7.6 / 16.5,
-// 1024 22.8 / 20.0; 12288 x 4096 M = 64 31.4 / 23.1, 256 72.7 / 48.1.
+// step) for M > 16 whose streaming plan does not split K, unless the
+// all-token kernel is ahead: K <= 4096 with M <= 32 or M <= 256 and
+// M * N <= 2^19, or K <= 8192 with M <= 32 and a one-round launch.
+// Measured (us, all-token / tiled): 4096 x 7168 M = 17 11.4 / 13.4,
+// 32 13.4 / 13.7, 64 16.5 / 14.4, 128 26.7 / 21.4, 256 43.4 / 26.0,
+// 512 76.9 / 38.1, 1024 145 / 63.2, 4096 548 / 204; 1024 x 4096 M = 64
+// 6.3 / 9.9, 256 7.6 / 16.5, 1024 22.8 / 20.0; 12288 x 4096 M = 32 20.7 /
+// 23.1, 64 31.4 / 23.1, 256 72.7 / 48.1; 4096 x 12288 M = 17 18.2 / 17.1;
+// 2048 x 12288 M = 24 18.9 / 17.2.  Where the streaming plan splits K
+// (few weight-row tiles, long K) the streaming kernel beats the tiled one:
+// M = 20, 512 x 12288 8.2 vs 13.2; M = 17, 704 x 8320 9.2 vs 13.1; M = 32,
+// 1024 x 16384 15.7 vs 20.4.
 inline bool blk32_tile(int64_t M, int64_t N, int64_t K) {
-    if (M <= 2 * kStreamMaxM || K > kTileMaxK) return false;
-    return !(M <= 16 * kStreamMaxM && K <= 4096 && M * N <= ((int64_t)1 << 19));
+    if (M <= kStreamMaxM || K > kTileMaxK || plan_stream(M, N, K).splits > 1) return false;
+    if (K <= 4096) return !(M <= 2 * kStreamMaxM || (M <= 16 * kStreamMaxM && M * N <= ((int64_t)1 << 19)));
+    return !(K <= 8192 && M <= 2 * kStreamMaxM && w16_one_round(M, N));
 }
 // One token (W8A8 codes, W8A8 with activations quantised in the kernel,
 // W8A16 blk128, block-32): dot-product kernels on the vector ALUs, no

@@ -289,13 +289,14 @@ size_t bfp8_workspace_bytes(int op, int64_t M, int64_t N, int64_t K);
  *                 (then they stream).  Above m_stream_max, W8A16 blk128
  *                 reads all tokens per weight tile for M <= 16 *
  *                 m_stream_max when K <= 4096 and either M <= 2 *
- *                 m_stream_max or M * N <= 2^19, and uses its tiled MFMA
- *                 kernel otherwise; blk32 runs the same tiled kernel
- *                 (scales applied in the widening) for M > 2 *
- *                 m_stream_max unless M <= 16 * m_stream_max, K <= 4096
- *                 and M * N <= 2^19, reads all tokens of a group of 32 or
- *                 64 per weight tile otherwise, and streams one 16-token
- *                 tile per workgroup only where that plan splits K.
+ *                 m_stream_max or M * N <= 2^19, and for M <= 4 *
+ *                 m_stream_max when K <= 8192 and that launch fits one
+ *                 round of workgroups on the CUs, and uses its tiled MFMA
+ *                 kernel otherwise; blk32 does the same with the all-token
+ *                 range at K > 4096 limited to M <= 2 * m_stream_max (its
+ *                 tiled form, scales applied in the widening, has no
+ *                 promotion step), and streams one 16-token tile per
+ *                 workgroup where that plan splits K.
  * Any output pointer may be NULL.
  */
 bfp8_status bfp8_get_limits(int op, int64_t* k_multiple, int64_t* n_multiple,

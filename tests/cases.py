@@ -126,6 +126,7 @@ W8A16_ALL_TOKENS = [
     (24, 12288, 512, "w8a16_wide:32x32w8"), (20, 16, 4096, "w8a16_wide:32x32w8"), (20, 64, 128, "w8a16_wide:16x32w8"),
     (128, 4096, 4096, "w8a16_wide:32x64w8"), (100, 4112, 1024, "w8a16_wide:32x64w8"),
     (256, 1024, 4096, "w8a16_wide:32x32w8"), (200, 1040, 1024, "w8a16_wide:16x64w8"),
+    (40, 1024, 8192, "w8a16_wide:16x32w8"), (48, 4096, 7168, "w8a16_wide:32x32w8"),
 ]
 W8A16_LONG_K = [(1, 4096, 12416, "w8a16_stream"), (3, 4096, 12288, "w8a16_stream"),
                 (16, 4096, 12288, "w8a16_wide:16x16w8")]
@@ -134,7 +135,7 @@ W8A16_LONG_K = [(1, 4096, 12416, "w8a16_stream"), (3, 4096, 12288, "w8a16_stream
 W8A16_SPLIT_K_STREAM = [(4, 512, 12288, "w8a16_stream/split"), (12, 512, 12288, "w8a16_stream/split")]
 W8A16_ONE_HOT = [(1, 256, 256, "w8a16_gemv"), (4, 256, 256, "w8a16_stream"), (16, 256, 256, "w8a16_wide:16x16w8"),
                  (40, 256, 256, "w8a16_wide:16x32w8")]
-W8A16_TILE_SPLIT = [(40, 1024, 8192, "w8a16_tile:128x64w8/split"), (100, 1040, 8192, "w8a16_tile:128x128w8/split"),
+W8A16_TILE_SPLIT = [(40, 1024, 12288, "w8a16_tile:128x64w8/split"), (100, 1040, 8192, "w8a16_tile:128x128w8/split"),
                     (300, 2048, 2176, "w8a16_tile:128x128w8/split"), (40, 16384, 512, "w8a16_tile:128x64w8")]
 W8A16_TILE_ONE_HOT = (300, 256, 256, "w8a16_tile:128x128w8")
 W8A16_TILE_LARGE_RAGGED = (2000, 4112, 1024, "w8a16_tile:256x128w8")

@@ -87,15 +87,17 @@ def test_routing_rules_read_off_the_plan():
                 assert name == stream and p["splits"] > 1, (op, M, N, K, p)
         if op == cases.BLK32 and (one or M > 16):
             p = bfp8.bfp8_get_plan(op, M, N, K)
-            tiled = M > 32 and not (M <= 256 and K <= 4096 and M * N <= 1 << 19)
+            short_k = K <= 4096 and (M <= 32 or (M <= 256 and M * N <= 1 << 19))
             if one:
                 assert name == "blk32_gemv", (M, N, K, name)
-            elif tiled:
-                assert name == "blk32_tile", (M, N, K, name)
             elif name == "blk32_stream":
                 assert p["splits"] > 1, (M, N, K, p)   # only where the streaming plan splits K
+            elif name == "blk32_wide":
+                # the all-token kernel: K <= 4096 as for W8A16, or K <= 8192, M <= 32 in one round
+                assert p["workspace_bytes"] == 0, (M, N, K, p)
+                assert short_k or (K <= 8192 and M <= 32 and p["workgroups"] <= 256), (M, N, K, p)
             else:
-                assert name == "blk32_wide" and p["workspace_bytes"] == 0, (M, N, K, p)
+                assert name == "blk32_tile" and not short_k, (M, N, K, p)
         if op == cases.QW8A8 and name.endswith("_quant"):
             assert M == 1 or M <= 8
 
