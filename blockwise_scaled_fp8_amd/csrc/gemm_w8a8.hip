@@ -374,32 +374,38 @@ __global__ __launch_bounds__(kStreamThreads) void w8a8_stream_quant_kernel(
 // All-token kernel (see w8a8_wide for where it is used): a workgroup owns
 // 16 kR weight rows (kR = 1 or 2 MFMA row tiles) and 16 kT tokens (kT = 2
 // or 4 token tiles; grid.y covers the tokens beyond) over all of K, so the
-// weights are read once and no split-K hand-off is needed.  Eight waves:
-// wave w takes token tiles 2 tg, 2 tg + 1 (tg = w % G, G = kT / 2) and the
-// 128-K blocks kw, kw + KW, ... (kw = w / G, KW = 8 / G).  Each wave owns a
-// ring of LDS slots (three for kR = 1, two for kR = 2); a slot holds one
-// block: the workgroup's 16 kR weight rows, the wave's 32 token rows, their
-// token scales and the weight scale, brought in by direct-to-LDS loads of
-// whole 128-byte lines (a load instruction covers eight full lines; register
-// loads of MFMA fragments touch sixteen half lines each, which a read probe
-// measured at half the throughput from L2).  A wave multiplies block j while
-// the younger blocks of its ring are in flight and refills the slot as soon
-// as it has read block j's operands; the slots are private, so there is no
-// barrier until the end, where the KW partial tiles of every output tile are
-// summed in LDS in K order.
-constexpr int kWideWaves = 8;
-static_assert(kWideWaves == kWideLaunchWaves, "plan and launch agree");
-constexpr int kWideThreads = kWideWaves * kWave;
-template <int kR>
+// weights are read once and no split-K hand-off is needed.  Every wave
+// takes all kT token tiles and the 128-K blocks w, w + W, ... (W waves:
+// eight for kT = 2, four for kT = 4, whose slots are twice as large), so
+// each block's weight rows are loaded once per workgroup.  Each wave owns
+// a ring of LDS slots (two or three); a slot holds one block: the
+// workgroup's 16 kR weight rows, the 16 kT token rows, their token scales
+// and the weight scale, brought in by direct-to-LDS loads of whole 128-byte
+// lines (a load instruction covers eight full lines; register loads of MFMA
+// fragments touch sixteen half lines each, which a read probe measured at
+// half the throughput from L2).  A wave multiplies block j while the younger
+// blocks of its ring are in flight and refills the slot as soon as it has
+// read block j's operands; the slots are private, so there is no barrier
+// until the end, where the W partial tiles of every output tile are summed
+// in LDS in K order.  With four token tiles, eight waves of two tiles each
+// (two token groups) measured slower: each group's wave loaded its own copy
+// of the weight rows (4096 x 4096 M = 128 12.36 vs 11.33 us, M = 96 10.53 vs
+// 10.21; 1024 x 4096 M = 512 8.34 vs 8.13); with two token tiles eight
+// waves stay ahead of four (M = 24 / 32: 6.84 / 7.37 vs 7.08 / 7.52 us).
+template <int kT>
+constexpr int wide_waves() { return w8a8_wide_waves(kT); }
+template <int kR, int kT>
 struct WideSlot {
-    static constexpr int kOffX = kR * kSlabBytes;                 // 32 token rows
-    static constexpr int kOffXs = kOffX + 32 * 128;               // 64 token scales (lanes >= 32 load padding)
+    static constexpr int kWaves = wide_waves<kT>();
+    static constexpr int kOffX = kR * kSlabBytes;                 // 16 kT token rows
+    static constexpr int kOffXs = kOffX + kT * kSlabBytes;        // 64 token scales (lanes past 16 kT load padding)
     static constexpr int kOffWs = kOffXs + 64 * 4;                // weight scale
     static constexpr int kBytes = (kOffWs + 4 + 255) / 256 * 256;
-    static constexpr int kSlotsFit = 160 * 1024 / (kWideWaves * kBytes);
+    static constexpr int kSlotsFit = 160 * 1024 / (kWaves * kBytes);
     static constexpr int kSlots = kSlotsFit > 3 ? 3 : kSlotsFit;
-    static constexpr int kVmem = 2 * kR + 4 + 1 + 1;             // load instructions per block
+    static constexpr int kVmem = 2 * kR + 2 * kT + 1 + 1;        // load instructions per block
     static_assert(kSlots >= 2, "LDS ring");
+    static_assert(16 * kT <= kWave, "one token scale per lane");
 };
 
 template <int V, int Y>
@@ -409,30 +415,28 @@ __device__ __forceinline__ void wide_wait_n() {
 }
 
 template <int kR, int kT>
-__global__ __launch_bounds__(kWideThreads, 1) void w8a8_wide_kernel(
+__global__ __launch_bounds__(wide_waves<kT>() * kWave, 1) void w8a8_wide_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ xs,
     const uint8_t* __restrict__ wq, const float* __restrict__ ws,
     void* __restrict__ y, int y_dtype, int64_t M, int64_t N, int64_t K) {
-    constexpr int G = kT / 2, KW = kWideWaves / G;
-    using SL = WideSlot<kR>;
+    using SL = WideSlot<kR, kT>;
+    constexpr int W = SL::kWaves;
     constexpr int kWideSlots = SL::kSlots, kWideSlot = SL::kBytes;
-    constexpr int kWideOffX = SL::kOffX, kWideOffXs = SL::kOffXs, kWideOffWs = SL::kOffWs;
-    static_assert(kT == 2 || kT == 4 || kT == 8, "token tiles");
-    __shared__ __attribute__((aligned(1024))) uint8_t ring[kWideWaves * kWideSlots * kWideSlot];
+    static_assert(kT == 2 || kT == 4, "token tiles");
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[W * kWideSlots * kWideSlot];
     const int64_t nt = blockIdx.x;            // 16 kR weight rows
     const int64_t mg = blockIdx.y;            // 16 kT tokens
     const int KB = (int)(K / 128);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
-    const int tg = wave % G, kw = wave / G;
     const int r = lane & 15, g = lane >> 4;
-    const int64_t m0 = 16 * kT * mg + 32 * tg;        // first token of this wave's tiles
+    const int64_t m0 = 16 * kT * mg;          // first token of the group
     const int64_t n0 = 16 * kR * nt;
     const int64_t rows_w = N - n0 < 16 * kR ? N - n0 : 16 * kR;
 
     const i32x4 rsrc_w = buffer_rsrc(wq + n0 * K, (uint32_t)(rows_w * K));
-    // The wave's 32 token rows and their scales from row m0 on; rows at or
-    // past M (and the padding scales of lanes 32..63) load as zeros.
-    const int64_t rows_x = M - m0 > 0 ? (M - m0 < 32 ? M - m0 : 32) : 0;
+    // The group's token rows and their scales from row m0 on; rows at or
+    // past M (and the padding scales of lanes past 16 kT) load as zeros.
+    const int64_t rows_x = M - m0 > 0 ? (M - m0 < 16 * kT ? M - m0 : 16 * kT) : 0;
     const i32x4 rsrc_x = buffer_rsrc(xq + m0 * K, (uint32_t)(rows_x * K));
     const i32x4 rsrc_xs = buffer_rsrc(xs + m0 * KB, (uint32_t)(rows_x * KB * 4));
     const i32x4 rsrc_ws = buffer_rsrc(ws + (n0 / 128) * KB, (uint32_t)(KB * 4));
@@ -447,20 +451,23 @@ __global__ __launch_bounds__(kWideThreads, 1) void w8a8_wide_kernel(
         for (int q = 0; q < 2 * kR; ++q)
             dma16(base + 1024 * q, rsrc_w, lane_off, __builtin_amdgcn_readfirstlane((int)(8 * q * K)), k_off);
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            dma16(base + kWideOffX + 1024 * q, rsrc_x, lane_off, __builtin_amdgcn_readfirstlane((int)(8 * q * K)), k_off);
-        dma4(base + kWideOffXs, rsrc_xs, xs_off, __builtin_amdgcn_readfirstlane(kb * 4));
-        if (lane == 0) dma4(base + kWideOffWs, rsrc_ws, 0, __builtin_amdgcn_readfirstlane(kb * 4));
+        for (int q = 0; q < 2 * kT; ++q)
+            dma16(base + SL::kOffX + 1024 * q, rsrc_x, lane_off, __builtin_amdgcn_readfirstlane((int)(8 * q * K)),
+                  k_off);
+        dma4(base + SL::kOffXs, rsrc_xs, xs_off, __builtin_amdgcn_readfirstlane(kb * 4));
+        if (lane == 0) dma4(base + SL::kOffWs, rsrc_ws, 0, __builtin_amdgcn_readfirstlane(kb * 4));
     };
 
-    const int nj = kw < KB ? (KB - 1 - kw) / KW + 1 : 0;   // blocks of this wave
+    const int nj = wave < KB ? (KB - 1 - wave) / W + 1 : 0;   // blocks of this wave
 #pragma unroll
     for (int s = 0; s < kWideSlots; ++s)
-        if (s < nj) issue(s, kw + KW * s);
+        if (s < nj) issue(s, wave + W * s);
 
-    f32x4 acc[kR][2];
+    f32x4 acc[kR][kT];
 #pragma unroll
-    for (int i = 0; i < kR; ++i) acc[i][0] = acc[i][1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int i = 0; i < kR; ++i)
+#pragma unroll
+        for (int t = 0; t < kT; ++t) acc[i][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
     int slot = 0;
     for (int j = 0; j < nj; ++j) {
@@ -472,24 +479,24 @@ __global__ __launch_bounds__(kWideThreads, 1) void w8a8_wide_kernel(
         else wide_wait_n<SL::kVmem, 0>();
         asm volatile("" ::: "memory");
         const uint8_t* sl = my_ring + slot * kWideSlot;
-        u32x4 a0[kR], a1[kR], b0[2], b1[2];
+        u32x4 a0[kR], a1[kR], b0[kT], b1[kT];
 #pragma unroll
         for (int i = 0; i < kR; ++i) slab_read(sl + i * kSlabBytes, r, g, a0[i], a1[i]);
-        float xsv[2];
+        float xsv[kT];
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            slab_read(sl + kWideOffX + t * 2048, r, g, b0[t], b1[t]);
-            xsv[t] = reinterpret_cast<const float*>(sl + kWideOffXs)[16 * t + r];
+        for (int t = 0; t < kT; ++t) {
+            slab_read(sl + SL::kOffX + t * kSlabBytes, r, g, b0[t], b1[t]);
+            xsv[t] = reinterpret_cast<const float*>(sl + SL::kOffXs)[16 * t + r];
         }
-        const float wsv = *reinterpret_cast<const float*>(sl + kWideOffWs);
+        const float wsv = *reinterpret_cast<const float*>(sl + SL::kOffWs);
         // Every operand of block j is in registers before the slot is refilled.
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        if (j + kWideSlots < nj) issue(slot, kw + KW * (j + kWideSlots));
+        if (j + kWideSlots < nj) issue(slot, wave + W * (j + kWideSlots));
 #pragma unroll
         for (int i = 0; i < kR; ++i) {
             const i32x8 a = __builtin_bit_cast(i32x8, __builtin_shufflevector(a0[i], a1[i], 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
+            for (int t = 0; t < kT; ++t) {
                 const i32x8 b = __builtin_bit_cast(i32x8, __builtin_shufflevector(b0[t], b1[t], 0, 1, 2, 3, 4, 5, 6, 7));
                 const f32x4 blk = mfma_e4m3_16x16x128(a, b, zero);
                 const float sc = xsv[t] * wsv;
@@ -500,28 +507,27 @@ __global__ __launch_bounds__(kWideThreads, 1) void w8a8_wide_kernel(
         slot = slot + 1 == kWideSlots ? 0 : slot + 1;
     }
 
-    // Sum the KW partial tiles of every token tile in K order.  Every
-    // wave's loads are done (its last wait was vmcnt(0)); the barrier
-    // orders the reuse of the ring.
+    // Sum the W partial tiles of every output tile in K order.  Every wave's
+    // loads are done (its last wait was vmcnt(0)); the barrier orders the
+    // reuse of the ring.
     __syncthreads();
     float* red = reinterpret_cast<float*>(ring);
-    // Slot of (row tile i, token tile tt = 2 tg + t, K lane kw):
-    // (((kw * kR + i) * kT + tt) * 64 + lane) * 4 floats.
+    // Slot of (row tile i, token tile t, K lane w): (((w kR + i) kT + t) * 64 + lane) * 4 floats.
 #pragma unroll
     for (int i = 0; i < kR; ++i)
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
-            *reinterpret_cast<f32x4*>(red + (((kw * kR + i) * kT + 2 * tg + t) * kWave + lane) * 4) = acc[i][t];
+        for (int t = 0; t < kT; ++t)
+            *reinterpret_cast<f32x4*>(red + (((wave * kR + i) * kT + t) * kWave + lane) * 4) = acc[i][t];
     __syncthreads();
-    // Thread x: lane L = x % 64 of output tiles u = x / 64, x / 64 + 8, ...
-    // (u = i * kT + tt).
+    // Thread x: lane L = x % 64 of output tiles u = x / 64, x / 64 + W, ...
+    // (u = i * kT + t).
     const int L = threadIdx.x % kWave, rr = L & 15, gg = L >> 4;
-    for (int u = threadIdx.x / kWave; u < kR * kT; u += kWideWaves) {
+    for (int u = threadIdx.x / kWave; u < kR * kT; u += W) {
         f32x4 v = *reinterpret_cast<const f32x4*>(red + (u * kWave + L) * 4);
 #pragma unroll
-        for (int w = 1; w < KW; ++w) v += *reinterpret_cast<const f32x4*>(red + ((w * kR * kT + u) * kWave + L) * 4);
+        for (int w = 1; w < W; ++w) v += *reinterpret_cast<const f32x4*>(red + ((w * kR * kT + u) * kWave + L) * 4);
         const int i = u / kT, tt = u % kT;
-        const int64_t m = 16 * kT * mg + 16 * tt + rr;
+        const int64_t m = m0 + 16 * tt + rr;
         const int64_t n = n0 + 16 * i + 4 * gg;
         if (m < M && n < N) {
             const int64_t idx = m * N + n;
@@ -530,7 +536,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void w8a8_wide_kernel(
             } else {
                 uint32_t h[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) h[i] = y_dtype == 0 ? float_to_bf16_bits(v[i]) : float_to_f16_bits(v[i]);
+                for (int e = 0; e < 4; ++e) h[e] = y_dtype == 0 ? float_to_bf16_bits(v[e]) : float_to_f16_bits(v[e]);
                 *reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + idx) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
             }
         }
@@ -543,9 +549,9 @@ hipError_t launch_w8a8_wide(const uint8_t* xq, const float* xs, const uint8_t* w
     const WideShape w = wide_shape(M, N);
     if (w.groups_m > 65535) return hipErrorInvalidValue;
     const dim3 grid(w.groups_n, w.groups_m);
-#define BFP8_LAUNCH_WIDE(R, T)                                                                                 \
-    hipLaunchKernelGGL((w8a8_wide_kernel<R, T>), grid, dim3(kWideThreads), 0, stream, xq, xs, wq, ws, y, y_dtype, \
-                       M, N, K)
+#define BFP8_LAUNCH_WIDE(R, T)                                                                                \
+    hipLaunchKernelGGL((w8a8_wide_kernel<R, T>), grid, dim3(wide_waves<T>() * kWave), 0, stream, xq, xs, wq, ws, y, \
+                       y_dtype, M, N, K)
     if (w.kr == 1) {
         if (w.kt == 2) BFP8_LAUNCH_WIDE(1, 2);
         else BFP8_LAUNCH_WIDE(1, 4);

@@ -66,10 +66,10 @@ W8A8_NO_WORKSPACE = [
     (32, 4096, 4096, "w8a8_wide:16x32w8"), (33, 4096, 4096, "w8a8_wide:32x32w8"), (50, 1024, 4096, "w8a8_stream"),
     (64, 4096, 4096, "w8a8_wide:32x32w8"), (32, 12288, 256, "w8a8_wide:32x32w8"), (20, 16, 8192, "w8a8_stream"),
     (20, 8208, 256, "w8a8_wide:32x32w8"), (65, 8192, 512, "w8a8_tile:64x128w8"),
-    (100, 4096, 1024, "w8a8_wide:32x64w8"), (128, 1040, 2048, "w8a8_wide:16x32w8"), (20, 64, 128, "w8a8_stream"),
+    (100, 4096, 1024, "w8a8_wide:32x64w4"), (128, 1040, 2048, "w8a8_wide:16x32w8"), (20, 64, 128, "w8a8_stream"),
     (128, 8192, 128, "w8a8_tile:64x128w8"), (64, 1024, 4096, "w8a8_stream"), (40, 2048, 1024, "w8a8_wide:16x32w8"),
-    (61, 512, 8192, "w8a8_stream"), (300, 1024, 2048, "w8a8_wide:32x32w8"), (512, 1024, 512, "w8a8_wide:32x64w8"),
-    (256, 1040, 1024, "w8a8_wide:16x64w8"),
+    (61, 512, 8192, "w8a8_stream"), (300, 1024, 2048, "w8a8_wide:32x32w8"), (512, 1024, 512, "w8a8_wide:32x64w4"),
+    (256, 1040, 1024, "w8a8_wide:16x64w4"),
 ]
 
 # Every tiled configuration, ragged M and N tiles, split K.
@@ -100,7 +100,7 @@ QUANT_W8A8 = [
     (3, 512, 640, "w8a8_stream_quant"), (4, 384, 12288, "w8a8_stream_quant/split"),
     (5, 1024, 4096, "w8a8_stream_quant"), (8, 512, 1024, "w8a8_stream_quant"), (9, 512, 640, "quant+w8a8_stream"),
     (16, 1024, 4096, "quant+w8a8_stream"), (17, 384, 640, "quant+w8a8_stream"), (64, 1024, 4096, "quant+w8a8_stream"),
-    (300, 1040, 1024, "quant+w8a8_wide:16x64w8"), (200, 4096, 2176, "quant+w8a8_tile:64x128w8/split"),
+    (300, 1040, 1024, "quant+w8a8_wide:16x64w4"), (200, 4096, 2176, "quant+w8a8_tile:64x128w8/split"),
 ]
 
 # ---------------------------------------------------------------- W8A16 ----
