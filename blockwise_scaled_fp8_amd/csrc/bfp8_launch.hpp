@@ -267,9 +267,13 @@ inline bool one_token_w8a16(int64_t M, int64_t K) { return M == 1 && K <= kOneTo
 // (W8A8 9.8 vs 10.6 us, W8A16 9.7 vs 10.55) and equal at 4096 x 7168.
 constexpr int kGemvLaunchWaves = 8;    // waves per workgroup of the one-token kernels
 constexpr int kStreamLaunchWaves = 16;  // waves per workgroup of the streaming kernels
-constexpr int kWideLaunchWaves = 8;     // waves per workgroup of the W8A16 all-token kernel
 // Waves per workgroup of the W8A8 all-token kernel for kt token tiles.
 constexpr int w8a8_wide_waves(int kt) { return kt == 4 ? 4 : 8; }
+// W8A16 all-token kernel (kr weight-row tiles, kt token tiles): token tiles
+// per wave, all of them wherever four waves' LDS rings hold them (every
+// case but kt = 4 with kr = 2), else one; and the waves per workgroup.
+constexpr int w16_wide_tiles_per_wave(int kr, int kt) { return kt == 1 || (kt == 4 && kr == 2) ? 1 : kt; }
+constexpr int w16_wide_waves(int kr, int kt) { return w16_wide_tiles_per_wave(kr, kt) > 1 ? 4 : 8; }
 constexpr int kQuantLaunchWaves = 4;    // waves per workgroup of the quantisers
 // Workgroups of the 1x128 activation quantiser's grid.
 int64_t quant_act_workgroups(int64_t M, int64_t K);

@@ -314,17 +314,22 @@ __global__ __launch_bounds__(kStreamThreads) void w8a16_blk32_stream_lds_kernel(
 // and for block-32 UE8M0 weights (kBlk32): a workgroup owns 16 kR weight
 // rows (kR = 1 or 2) and 16 kT tokens (kT = 1, 2 or 4 token tiles; grid.y
 // walks further groups of 16 kT tokens) over all of K, so nothing is split
-// across workgroups.  Eight
-// waves: wave w takes token tile tg = w % kT and the 128-K blocks kw,
-// kw + KW, ... (kw = w / kT, KW = 8 / kT).  Each wave owns a ring of LDS
-// slots (three for kR = 1, two for kR = 2); a slot holds one block: the
-// 16 kR weight rows (2 KB each 16, E4M3), the wave's 16 token rows (16-bit,
-// 256 bytes each) and the block's weight scale word, all by direct-to-LDS
-// loads of whole lines (16 bytes a lane; the scale word one dword).  Token
-// row R of a tile keeps its 16-byte chunk c at position c ^ sw(R),
-// sw(R) = ((R & 3) << 2) | (R >> 2), so the 16 rows of one MFMA read hit
-// 16 distinct bank groups.  The weights are widened in registers (widen8)
-// and feed four 16x16x32 MFMAs per block and row tile.  blk128: the block
+// across workgroups.  A wave takes kTw of the kT token tiles (tiles
+// kTw tg .. kTw tg + kTw - 1) and the 128-K blocks kw, kw + KW, ...; with
+// G = kT / kTw token groups, wave w has tg = w % G and kw = w / G, and
+// KW = W / G.  Where the LDS allows, every wave takes every token tile
+// (kTw = kT, four waves: w16_wide_tiles_per_wave), so each block's weight
+// rows are loaded and widened once per workgroup; otherwise (one token
+// tile, or four tiles of two weight-row tiles) eight waves take one tile
+// each.  Each wave owns a ring of LDS slots (two or three); a slot holds
+// one block: the 16 kR weight rows (2 KB each 16, E4M3), the wave's
+// 16 kTw token rows (16-bit, 256 bytes each) and the block's weight scale
+// word, all by direct-to-LDS loads of whole lines (16 bytes a lane; the
+// scale word one dword).  Token row R of a tile keeps its 16-byte chunk c
+// at position c ^ sw(R), sw(R) = ((R & 3) << 2) | (R >> 2), so the 16 rows
+// of one MFMA read hit 16 distinct bank groups.  The weights are widened
+// in registers (widen8) and feed four 16x16x32 MFMAs per block, row tile
+// and token tile.  blk128: the block
 // partial is promoted with the fp32 block scale, as in the streaming
 // kernel.  Block-32: the scale word holds the four UE8M0 bytes of the
 // block's 32x32 tiles in the row tile's 32-row band ([SM70] "How it works":
@@ -333,17 +338,14 @@ __global__ __launch_bounds__(kStreamThreads) void w8a16_blk32_stream_lds_kernel(
 // accumulate across all of K with no promotion step, as in the block-32
 // streaming kernel.  The waves' partial sums meet in LDS once, at the end,
 // and are added in K-lane order.
-constexpr int kW16WideWaves = 8;
-static_assert(kW16WideWaves == kWideLaunchWaves, "plan and launch agree");
-constexpr int kW16WideThreads = kW16WideWaves * kWave;
-template <int kR>
+template <int kR, int kTw, int kW>
 struct W16Slot {
-    static constexpr int kOffX = kR * kSlabBytes;                  // 16 token rows x 256 bytes
-    static constexpr int kOffWs = kOffX + 16 * 256;
+    static constexpr int kOffX = kR * kSlabBytes;                  // 16 kTw token rows x 256 bytes
+    static constexpr int kOffWs = kOffX + kTw * 16 * 256;
     static constexpr int kBytes = (kOffWs + 4 + 255) / 256 * 256;
-    static constexpr int kSlotsFit = 160 * 1024 / (kW16WideWaves * kBytes);
+    static constexpr int kSlotsFit = 160 * 1024 / (kW * kBytes);
     static constexpr int kSlots = kSlotsFit > 3 ? 3 : kSlotsFit;
-    static constexpr int kVmem = 2 * kR + 4 + 1;                   // load instructions per block
+    static constexpr int kVmem = 2 * kR + 4 * kTw + 1;             // load instructions per block
     static_assert(kSlots >= 2, "LDS ring");
 };
 
@@ -356,26 +358,28 @@ __device__ __forceinline__ void w16_wait_n() {
 __device__ __forceinline__ int w16_sw(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
 
 template <bool kBlk32, bool kXBf16, int kT, int kR>
-__global__ __launch_bounds__(kW16WideThreads, 1) void w8a16_wide_kernel(
+__global__ __launch_bounds__(w16_wide_waves(kR, kT) * kWave, 1) void w8a16_wide_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq, const void* __restrict__ scales,
     void* __restrict__ y, int y_dtype, int64_t M, int64_t N, int64_t K) {
-    constexpr int KW = kW16WideWaves / kT;
-    using SL = W16Slot<kR>;
+    constexpr int kTw = w16_wide_tiles_per_wave(kR, kT), kW = w16_wide_waves(kR, kT);
+    constexpr int G = kT / kTw, KW = kW / G;
+    using SL = W16Slot<kR, kTw, kW>;
     constexpr int kW16WideSlots = SL::kSlots, kW16Slot = SL::kBytes, kW16OffX = SL::kOffX, kW16OffWs = SL::kOffWs;
     static_assert(kT == 1 || kT == 2 || kT == 4, "token tiles");
+    static_assert(kT % kTw == 0 && kW % G == 0, "wave layout");
     static_assert(!kBlk32 || !kXBf16, "block-32 takes fp16 activations");
-    __shared__ __attribute__((aligned(1024))) uint8_t ring[kW16WideWaves * kW16WideSlots * kW16Slot];
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[kW * kW16WideSlots * kW16Slot];
     const int64_t nt = blockIdx.x, mg = blockIdx.y;
     const int KB = (int)(K / 128);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
-    const int tg = wave % kT, kw = wave / kT;
+    const int tg = wave % G, kw = wave / G;
     const int r = lane & 15, g = lane >> 4;
-    const int64_t m0 = 16 * kT * mg + 16 * tg;         // first token of this wave's tile
+    const int64_t m0 = 16 * kT * mg + 16 * kTw * tg;   // first token of this wave's tiles
 
     const int64_t n0 = 16 * kR * nt;
     const int64_t rows_w = N - n0 < 16 * kR ? N - n0 : 16 * kR;
     const i32x4 rsrc_w = buffer_rsrc(wq + n0 * K, (uint32_t)(rows_w * K));
-    const int64_t rows_x = M - m0 > 0 ? (M - m0 < 16 ? M - m0 : 16) : 0;
+    const int64_t rows_x = M - m0 > 0 ? (M - m0 < 16 * kTw ? M - m0 : 16 * kTw) : 0;
     const i32x4 rsrc_x = buffer_rsrc(x + m0 * K, (uint32_t)(rows_x * K * 2));
     // The block's scale word: the fp32 ws[n0 / 128, kb], or the UE8M0 bytes
     // of 32x32 tiles (n0 / 32, 4 kb .. 4 kb + 3) (K / 32 bytes a band, a
@@ -385,11 +389,12 @@ __global__ __launch_bounds__(kW16WideThreads, 1) void w8a16_wide_kernel(
         kBlk32 ? buffer_rsrc(static_cast<const uint8_t*>(scales) + (n0 / 32) * (K / 32), (uint32_t)(KB * 4))
                : buffer_rsrc(static_cast<const float*>(scales) + (n0 / 128) * KB, (uint32_t)(KB * 4));
     const int lane_off_w = slab_lane_offset(lane, K);
-    // Token-row loads: instruction q covers rows 4q .. 4q + 3; lane l fills
-    // position l % 16 of row 4q + l / 16 with logical chunk (l % 16) ^ sw(row).
-    int x_off[4];
+    // Token-row loads: instruction q covers rows 4q .. 4q + 3 (tile q / 4);
+    // lane l fills position l % 16 of row 4q + l / 16 with logical chunk
+    // (l % 16) ^ sw(row).
+    int x_off[4 * kTw];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < 4 * kTw; ++q) {
         const int row = 4 * q + (lane >> 4);
         x_off[q] = (int)(row * K * 2) + (((lane & 15) ^ w16_sw(row)) << 4);
     }
@@ -403,7 +408,7 @@ __global__ __launch_bounds__(kW16WideThreads, 1) void w8a16_wide_kernel(
         for (int q = 0; q < 2 * kR; ++q)
             dma16(base + 1024 * q, rsrc_w, lane_off_w, __builtin_amdgcn_readfirstlane((int)(8 * q * K)), k_off);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) dma16(base + kW16OffX + 1024 * q, rsrc_x, x_off[q], 0, k_off_x);
+        for (int q = 0; q < 4 * kTw; ++q) dma16(base + kW16OffX + 1024 * q, rsrc_x, x_off[q], 0, k_off_x);
         if (lane == 0) dma4(base + kW16OffWs, rsrc_ws, 0, __builtin_amdgcn_readfirstlane(kb * 4));
     };
 
@@ -412,9 +417,11 @@ __global__ __launch_bounds__(kW16WideThreads, 1) void w8a16_wide_kernel(
     for (int s = 0; s < kW16WideSlots; ++s)
         if (s < nj) issue(s, kw + KW * s);
 
-    f32x4 acc[kR];
+    f32x4 acc[kR][kTw];
 #pragma unroll
-    for (int i = 0; i < kR; ++i) acc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int i = 0; i < kR; ++i)
+#pragma unroll
+        for (int t = 0; t < kTw; ++t) acc[i][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
     const int sw = w16_sw(r);
     int slot = 0;
@@ -430,12 +437,14 @@ __global__ __launch_bounds__(kW16WideThreads, 1) void w8a16_wide_kernel(
         for (int i = 0; i < kR; ++i) slab_read(sl + i * kSlabBytes, r, g, wa0[i], wa1[i]);
         // MFMA i takes K offsets 16 g + 8 i (i < 2) and 64 + 16 g + 8 (i - 2):
         // 16-bit chunks 2 g + i and 8 + 2 g + (i - 2) of the token row.
-        u32x4 xv[4];
+        u32x4 xv[kTw][4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int c = i < 2 ? 2 * g + i : 8 + 2 * g + (i - 2);
-            xv[i] = *reinterpret_cast<const u32x4*>(sl + kW16OffX + r * 256 + ((c ^ sw) << 4));
-        }
+        for (int t = 0; t < kTw; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int c = i < 2 ? 2 * g + i : 8 + 2 * g + (i - 2);
+                xv[t][i] = *reinterpret_cast<const u32x4*>(sl + kW16OffX + t * 4096 + r * 256 + ((c ^ sw) << 4));
+            }
         const uint32_t sword = *reinterpret_cast<const uint32_t*>(sl + kW16OffWs);
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         if (j + kW16WideSlots < nj) issue(slot, kw + KW * (j + kW16WideSlots));
@@ -448,21 +457,27 @@ __global__ __launch_bounds__(kW16WideThreads, 1) void w8a16_wide_kernel(
                 // chunk g + 4 in tile 4 kb + 2 + g / 2.
                 const float e0 = ue8m0_scale((sword >> (8 * (g >> 1))) & 0xFF);
                 const float e1 = ue8m0_scale((sword >> (8 * (2 + (g >> 1)))) & 0xFF);
+                u32x4 a[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const u32x4 a = widen8<false>(q8[2 * i], q8[2 * i + 1], i < 2 ? e0 : e1);
-                    acc[rt] = mfma_f16_16x16x32(a, xv[i], acc[rt]);
-                }
+                for (int i = 0; i < 4; ++i) a[i] = widen8<false>(q8[2 * i], q8[2 * i + 1], i < 2 ? e0 : e1);
+#pragma unroll
+                for (int t = 0; t < kTw; ++t)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[rt][t] = mfma_f16_16x16x32(a[i], xv[t][i], acc[rt][t]);
             } else {
-                f32x4 blk = zero;
+                u32x4 a[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const u32x4 a = widen8<kXBf16>(q8[2 * i], q8[2 * i + 1]);
-                    blk = kXBf16 ? mfma_bf16_16x16x32(a, xv[i], blk) : mfma_f16_16x16x32(a, xv[i], blk);
-                }
+                for (int i = 0; i < 4; ++i) a[i] = widen8<kXBf16>(q8[2 * i], q8[2 * i + 1]);
                 const float sc = __builtin_bit_cast(float, sword);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) acc[rt][e] = __builtin_fmaf(blk[e], sc, acc[rt][e]);
+                for (int t = 0; t < kTw; ++t) {
+                    f32x4 blk = zero;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        blk = kXBf16 ? mfma_bf16_16x16x32(a[i], xv[t][i], blk) : mfma_f16_16x16x32(a[i], xv[t][i], blk);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[rt][t][e] = __builtin_fmaf(blk[e], sc, acc[rt][t][e]);
+                }
             }
         }
         slot = slot + 1 == kW16WideSlots ? 0 : slot + 1;
@@ -472,10 +487,12 @@ __global__ __launch_bounds__(kW16WideThreads, 1) void w8a16_wide_kernel(
     float* red = reinterpret_cast<float*>(ring);
 #pragma unroll
     for (int i = 0; i < kR; ++i)
-        *reinterpret_cast<f32x4*>(red + (((kw * kR + i) * kT + tg) * kWave + lane) * 4) = acc[i];
+#pragma unroll
+        for (int t = 0; t < kTw; ++t)
+            *reinterpret_cast<f32x4*>(red + (((kw * kR + i) * kT + kTw * tg + t) * kWave + lane) * 4) = acc[i][t];
     __syncthreads();
     const int L = threadIdx.x % kWave, rr = L & 15, gg = L >> 4;
-    for (int u = threadIdx.x / kWave; u < kR * kT; u += kW16WideWaves) {
+    for (int u = threadIdx.x / kWave; u < kR * kT; u += kW) {
         f32x4 v = *reinterpret_cast<const f32x4*>(red + (u * kWave + L) * 4);
 #pragma unroll
         for (int w = 1; w < KW; ++w) v += *reinterpret_cast<const f32x4*>(red + ((w * kR * kT + u) * kWave + L) * 4);
@@ -496,9 +513,9 @@ __global__ __launch_bounds__(kW16WideThreads, 1) void w8a16_wide_kernel(
     }
 }
 
-#define BFP8_LAUNCH_W16(S, B, T, R)                                                                                \
-    hipLaunchKernelGGL((w8a16_wide_kernel<S, B, T, R>), grid, dim3(kW16WideThreads), 0, stream, xh, wq, scales, y, \
-                       y_dtype, M, N, K)
+#define BFP8_LAUNCH_W16(S, B, T, R)                                                                       \
+    hipLaunchKernelGGL((w8a16_wide_kernel<S, B, T, R>), grid, dim3(w16_wide_waves(R, T) * kWave), 0, stream, xh, \
+                       wq, scales, y, y_dtype, M, N, K)
 #define BFP8_LAUNCH_W16_KR(S, B, T)          \
     if (w.kr == 1) BFP8_LAUNCH_W16(S, B, T, 1); \
     else BFP8_LAUNCH_W16(S, B, T, 2);

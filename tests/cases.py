@@ -107,7 +107,7 @@ QUANT_W8A8 = [
 W8A16_BY_M = [(1, 512, 1024, "w8a16_gemv")] + \
     [(M, 512, 1024, "w8a16_stream") for M in (2, 3, 4, 5, 8)] + \
     [(M, 512, 1024, "w8a16_wide:16x16w8") for M in (9, 12, 16)] + \
-    [(M, 512, 1024, "w8a16_wide:16x32w8") for M in (17, 33, 64, 65, 130)]
+    [(M, 512, 1024, "w8a16_wide:16x32w4") for M in (17, 33, 64, 65, 130)]
 # 8 < M <= 16 without a split of K: the all-token kernel with one 16-token
 # tile, one or two weight-row tiles (a half-filled pair at N = 16), ragged
 # M, K of one block and long K.
@@ -121,12 +121,12 @@ W8A16_ONE_TOKEN = [(1, N, K, "w8a16_gemv") for N, K in
                    ((16, 128), (16, 1152), (64, 4096), (1024, 4096), (2064, 1024), (4096, 4096), (4096, 3968),
                     (12288, 2048), (2064, 5120), (8192, 8192), (4096, 12288))]
 W8A16_ALL_TOKENS = [
-    (17, 1024, 4096, "w8a16_wide:16x32w8"), (32, 4096, 4096, "w8a16_wide:16x32w8"),
-    (50, 1024, 4096, "w8a16_wide:16x32w8"), (64, 4096, 4096, "w8a16_wide:32x32w8"),
-    (24, 12288, 512, "w8a16_wide:32x32w8"), (20, 16, 4096, "w8a16_wide:32x32w8"), (20, 64, 128, "w8a16_wide:16x32w8"),
+    (17, 1024, 4096, "w8a16_wide:16x32w4"), (32, 4096, 4096, "w8a16_wide:16x32w4"),
+    (50, 1024, 4096, "w8a16_wide:16x32w4"), (64, 4096, 4096, "w8a16_wide:32x32w4"),
+    (24, 12288, 512, "w8a16_wide:32x32w4"), (20, 16, 4096, "w8a16_wide:32x32w4"), (20, 64, 128, "w8a16_wide:16x32w4"),
     (128, 4096, 4096, "w8a16_wide:32x64w8"), (100, 4112, 1024, "w8a16_wide:32x64w8"),
-    (256, 1024, 4096, "w8a16_wide:32x32w8"), (200, 1040, 1024, "w8a16_wide:16x64w8"),
-    (40, 1024, 8192, "w8a16_wide:16x32w8"), (48, 4096, 7168, "w8a16_wide:32x32w8"),
+    (256, 1024, 4096, "w8a16_wide:32x32w4"), (200, 1040, 1024, "w8a16_wide:16x64w4"),
+    (40, 1024, 8192, "w8a16_wide:16x32w4"), (48, 4096, 7168, "w8a16_wide:32x32w4"),
 ]
 W8A16_LONG_K = [(1, 4096, 12416, "w8a16_stream"), (3, 4096, 12288, "w8a16_stream"),
                 (16, 4096, 12288, "w8a16_wide:16x16w8")]
@@ -134,7 +134,7 @@ W8A16_LONG_K = [(1, 4096, 12416, "w8a16_stream"), (3, 4096, 12288, "w8a16_stream
 # the streaming kernel's register-operand tokens).
 W8A16_SPLIT_K_STREAM = [(4, 512, 12288, "w8a16_stream/split"), (12, 512, 12288, "w8a16_stream/split")]
 W8A16_ONE_HOT = [(1, 256, 256, "w8a16_gemv"), (4, 256, 256, "w8a16_stream"), (16, 256, 256, "w8a16_wide:16x16w8"),
-                 (40, 256, 256, "w8a16_wide:16x32w8")]
+                 (40, 256, 256, "w8a16_wide:16x32w4")]
 W8A16_TILE_SPLIT = [(40, 1024, 12288, "w8a16_tile:128x64w8/split"), (100, 1040, 8192, "w8a16_tile:128x128w8/split"),
                     (300, 2048, 2176, "w8a16_tile:128x128w8/split"), (40, 16384, 512, "w8a16_tile:128x64w8")]
 W8A16_TILE_ONE_HOT = (300, 256, 256, "w8a16_tile:128x128w8")
@@ -160,10 +160,10 @@ BLK32_ONE_TOKEN = [(1, 4096, 4096, "blk32_gemv"), (1, 32, 128, "blk32_gemv"), (1
                    (1, 4096, 12416, "blk32_stream_lds")]
 BLK32_ONE_HOT_ONE_TOKEN = (1, 704, 256, "blk32_gemv")
 # Above the streaming range ([SM70] "Results" times M = 32 ... 4096).
-BLK32_ABOVE_16 = [(17, 4096, 7168, "blk32_wide:16x32w8"), (32, 4096, 7168, "blk32_wide:16x32w8"),
-                  (32, 8192, 1024, "blk32_wide:32x32w8"), (64, 4096, 2048, "blk32_wide:32x32w8"),
-                  (128, 4096, 4096, "blk32_wide:32x64w8"), (100, 1024, 4096, "blk32_wide:16x32w8"),
-                  (200, 1024, 1024, "blk32_wide:16x64w8")]
+BLK32_ABOVE_16 = [(17, 4096, 7168, "blk32_wide:16x32w4"), (32, 4096, 7168, "blk32_wide:16x32w4"),
+                  (32, 8192, 1024, "blk32_wide:32x32w4"), (64, 4096, 2048, "blk32_wide:32x32w4"),
+                  (128, 4096, 4096, "blk32_wide:32x64w8"), (100, 1024, 4096, "blk32_wide:16x32w4"),
+                  (200, 1024, 1024, "blk32_wide:16x64w4")]
 # Larger M: the W8A16 tiled kernel with the UE8M0 scales applied in the
 # widening; every tile shape, split and unsplit, ragged M and N (N = 1056
 # and 4128: waves of the last weight tile past N read the last scale band).
@@ -175,7 +175,7 @@ BLK32_TILE_ONE_HOT = (300, 704, 256, "blk32_tile:128x128w8")
 BLK32_WINDOW = (8, 512, 1024, "blk32_stream_lds")
 BLK32_ONE_HOT = (16, 704, 256, "blk32_wide:16x16w8")
 BLK32_ONE_HOT_STREAM = (8, 704, 256, "blk32_stream_lds")
-BLK32_ONE_HOT_ABOVE_16 = (17, 704, 256, "blk32_wide:16x32w8")
+BLK32_ONE_HOT_ABOVE_16 = (17, 704, 256, "blk32_wide:16x32w4")
 BLK32_ONE_HOT_ABOVE_16_SPLIT = (17, 704, 8320, "blk32_stream/split")
 BLK32_SPLIT_K = (4, 1024, 12288, "blk32_stream_lds/split")
 BLK32_SPLIT_K_16 = (16, 1024, 12288, "blk32_stream_lds/split")
