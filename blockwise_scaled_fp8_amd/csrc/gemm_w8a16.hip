@@ -310,34 +310,36 @@ __global__ __launch_bounds__(kStreamThreads) void w8a16_blk32_stream_lds_kernel(
 
 // ------------------------------------------------- W8A16 all-token kernel ----
 // The W8A16 product with every token of a group per workgroup (see
-// w8a16_wide and w8a16_one_tile for where it is used), for blk128 weights
-// and for block-32 UE8M0 weights (kBlk32): a workgroup owns 16 kR weight
-// rows (kR = 1 or 2) and 16 kT tokens (kT = 1, 2 or 4 token tiles; grid.y
-// walks further groups of 16 kT tokens) over all of K, so nothing is split
-// across workgroups.  A wave takes kTw of the kT token tiles (tiles
-// kTw tg .. kTw tg + kTw - 1) and the 128-K blocks kw, kw + KW, ...; with
-// G = kT / kTw token groups, wave w has tg = w % G and kw = w / G, and
-// KW = W / G.  Where the LDS allows, every wave takes every token tile
-// (kTw = kT, four waves: w16_wide_tiles_per_wave), so each block's weight
-// rows are loaded and widened once per workgroup; otherwise (one token
-// tile, or four tiles of two weight-row tiles) eight waves take one tile
-// each.  Each wave owns a ring of LDS slots (two or three); a slot holds
-// one block: the 16 kR weight rows (2 KB each 16, E4M3), the wave's
-// 16 kTw token rows (16-bit, 256 bytes each) and the block's weight scale
-// word, all by direct-to-LDS loads of whole lines (16 bytes a lane; the
-// scale word one dword).  Token row R of a tile keeps its 16-byte chunk c
-// at position c ^ sw(R), sw(R) = ((R & 3) << 2) | (R >> 2), so the 16 rows
-// of one MFMA read hit 16 distinct bank groups.  The weights are widened
-// in registers (widen8) and feed four 16x16x32 MFMAs per block, row tile
-// and token tile.  blk128: the block
-// partial is promoted with the fp32 block scale, as in the streaming
-// kernel.  Block-32: the scale word holds the four UE8M0 bytes of the
-// block's 32x32 tiles in the row tile's 32-row band ([SM70] "How it works":
-// one power-of-two scale per 32x32 tile), and each lane applies the two
-// that cover its two 16-K chunks inside the widening, exactly, so the MFMAs
-// accumulate across all of K with no promotion step, as in the block-32
-// streaming kernel.  The waves' partial sums meet in LDS once, at the end,
-// and are added in K-lane order.
+// w8a16_wide, w8a16_one_tile and blk32_wide for where it is used), for
+// blk128 weights and for block-32 UE8M0 weights (kBlk32): a workgroup owns
+// 16 kR weight rows (kR = 1 or 2) and 16 kT tokens (kT = 1, 2 or 4 token
+// tiles; grid.y walks further groups of 16 kT tokens) over all of K, so
+// nothing is split across workgroups.
+//
+// A wave takes kTw of the kT token tiles (tiles kTw tg .. kTw tg + kTw - 1)
+// and the 128-K blocks kw, kw + KW, ...: with G = kT / kTw token groups
+// and kW waves, wave w has tg = w % G, kw = w / G, and KW = kW / G.  Where
+// the LDS allows, every wave takes every token tile (kTw = kT, four waves;
+// w16_wide_tiles_per_wave), so each block's weight rows are loaded and
+// widened once per workgroup; one token tile, and four tiles of two
+// weight-row tiles, run eight waves of one tile each.
+//
+// Each wave owns a ring of LDS slots (two or three); a slot holds one
+// block: the kR 16-row weight slabs (E4M3, 2 KB each), the wave's 16 kTw
+// token rows (16-bit, 256 bytes each) and the block's weight scale word,
+// all by direct-to-LDS loads of whole lines (16 bytes a lane; the scale
+// word one dword).  Token row R of a tile keeps its 16-byte chunk c at
+// position c ^ sw(R), sw(R) = ((R & 3) << 2) | (R >> 2), so the 16 rows of
+// one MFMA read hit 16 distinct bank groups.  The weights are widened in
+// registers (widen8) and feed four 16x16x32 MFMAs per block, row tile and
+// token tile.  blk128: the block partial is promoted with the fp32 block
+// scale, as in the streaming kernel.  Block-32: the scale word holds the
+// four UE8M0 bytes of the block's 32x32 tiles in the row tile's 32-row band
+// ([SM70] "How it works": one power-of-two scale per 32x32 tile), and each
+// lane applies the two that cover its two 16-K chunks inside the widening,
+// exactly, so the MFMAs accumulate across all of K with no promotion step,
+// as in the block-32 streaming kernel.  The waves' partial sums meet in
+// LDS once, at the end, and are added in K-lane order.
 template <int kR, int kTw, int kW>
 struct W16Slot {
     static constexpr int kOffX = kR * kSlabBytes;                  // 16 kTw token rows x 256 bytes

@@ -1,4 +1,7 @@
-// W8A8 blockwise GEMM, tiled kernels for M > 16 on gfx950.
+// W8A8 blockwise GEMM, tiled kernels for M > 16 on gfx950; the same kernel
+// serves the weight-only products at larger M (TileX: 16-bit token rows,
+// E4M3 weights widened in registers, with 128x128 fp32 weight scales or
+// block-32 UE8M0 scales applied in the widening).
 //
 // A workgroup computes a BN (weight rows n) x BM (tokens m) tile of Y over a
 // range of 128-wide K blocks, one scale block per LDS stage ([ARC] "What
