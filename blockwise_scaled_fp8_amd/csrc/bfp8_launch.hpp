@@ -42,23 +42,22 @@ struct StreamPlan {
 };
 StreamPlan plan_stream(int64_t M, int64_t N, int64_t K);
 
-// Shape of a launch of the all-token kernels (W8A8 and W8A16): kr 16-row
-// weight tiles and kt 16-token tiles per workgroup, groups_n x groups_m
-// workgroups.  Among (kr, kt) in {1, 2} x {2, 4} (kt = 4 only when M needs
-// at least four token tiles) it takes the one with the fewest workgroups
-// that still gives at least 256, one per CU, and two weight tiles on a tie
-// (each token byte then feeds twice the weights); with no such candidate,
-// the one with the most workgroups.  Measured over every (kr, kt), K = 4096,
-// 32 rotated weight copies, this picks the fastest at each point tried
-// (us, W8A8 / W8A16): 4096 x 4096 M = 32 (1, 2) 6.7 / 9.6, M = 48 (2, 2)
-// 7.8 against 9.4 for (1, 4), M = 64 (2, 2) 8.7 / 11.9 against 10.7 / 14.0,
-// M = 128 (2, 4) 12.5 / 17.8; 1024 x 4096 M = 128 (1, 2) 5.4 / 7.5 against
-// 7.5 / 10.4 for (1, 4), M = 256 (2, 2) 6.4 / 9.8, M = 512 (2, 4) 9.4;
-// 12288 x 4096 M = 32 (2, 2) - / 22.3.
+// Shape of a launch of the all-token kernels: kr 16-row weight tiles and
+// kt 16-token tiles per workgroup, groups_n x groups_m workgroups.
 struct WideShape {
     int kr, kt;
     unsigned groups_n, groups_m;
 };
+// W8A16 rule (w16_wide_shape above 16 tokens): among (kr, kt) in {1, 2} x
+// {2, 4} (kt = 4 only when M needs at least four token tiles) the one with
+// the fewest workgroups that still gives at least 256, one per CU, and two
+// weight tiles on a tie (each token byte then feeds twice the weights);
+// with no such candidate, the one with the most workgroups.  Measured over
+// every (kr, kt), K = 4096, 32 rotated weight copies, this picks the
+// fastest at each point tried (us): 4096 x 4096 M = 32 (1, 2) 9.6, M = 64
+// (2, 2) 11.9 against 14.0 for (1, 4), M = 128 (2, 4) 17.8; 1024 x 4096
+// M = 128 (1, 2) 7.5 against 10.4 for (1, 4), M = 256 (2, 2) 9.8;
+// 12288 x 4096 M = 32 (2, 2) 22.3.
 inline WideShape wide_shape(int64_t M, int64_t N) {
     const int64_t m_tiles = (M + 15) / 16;
     WideShape best{1, 2, 0, 0};
@@ -79,6 +78,54 @@ inline WideShape wide_shape(int64_t M, int64_t N) {
         }
     }
     return best;
+}
+
+// W8A8 rule: (kr, kt) in {1, 2, 4} x {2, 4} (kt = 4 only when M needs at
+// least four token tiles).  When some candidate fits one round on the CUs
+// (at most 256 workgroups), the one with the most workgroups, the larger kr
+// on a tie; otherwise the one with the fewest, the larger kr on a tie.  Two
+// rounds of this kernel cost more than one round of larger tiles, and at
+// equal counts more weight rows per workgroup cut the token bytes per
+// output.  Measured (us, 32 rotated weight copies, K = 4096; the pick
+// first): 4096 x 4096 M = 64 (2, 2) 8.4 against 10.7 for (4, 2), M = 96
+// (2, 4) 10.1 against 10.7 for (4, 2), M = 128 (4, 2) 10.7 against 11.2 for
+// (2, 4) and 14.2 for (4, 4), M = 160 / 192 / 256 (4, 4) 13.0 / 13.9 / 14.0
+// (192 / 192 / 256 workgroups) against 17.8 for (2, 4) at M = 192;
+// 1024 x 4096 M = 256 (2, 2) 5.9 against 6.8 for (1, 4), M = 512 (4, 2) 8.35
+// against 8.46 for (2, 4), M = 768 / 1024 (4, 4) 10.2 / 11.6; 2048 x 4096
+// M = 128 (2, 2) 6.7 against 8.0 for (1, 4), M = 512 (4, 4) 12.7;
+// 12288 x 4096 M = 32 (4, 2) 13.8 against 16.4 for (2, 2), M = 64 (4, 4)
+// 17.1 against 21.9 for (2, 2); 16384 x 4096 M = 32 (4, 2) 16.7 against 18.1.
+inline WideShape w8a8_wide_shape(int64_t M, int64_t N) {
+    const int64_t m_tiles = (M + 15) / 16;
+    WideShape best{1, 2, 0, 0};
+    int64_t best_wg = -1;
+    bool best_one_round = false;
+    for (int kt = 2; kt <= 4; kt += 2) {
+        if (kt > 2 && kt > m_tiles) continue;
+        for (int kr = 4; kr >= 1; kr /= 2) {
+            const int64_t gn = (N + 16 * kr - 1) / (16 * kr), gm = (M + 16 * kt - 1) / (16 * kt);
+            const int64_t wg = gn * gm;
+            const bool one_round = wg <= 256;
+            // Candidates come larger kr first within a kt, so a strict
+            // comparison keeps the larger kr on a tie within that kt; across
+            // kt a tie goes to the larger kr explicitly.
+            const bool tie_kr = wg == best_wg && kr > best.kr;
+            const bool better = best_wg < 0 || (one_round && !best_one_round) ||
+                                (one_round && best_one_round && (wg > best_wg || tie_kr)) ||
+                                (!one_round && !best_one_round && (wg < best_wg || tie_kr));
+            if (better) {
+                best = WideShape{kr, kt, (unsigned)gn, (unsigned)(gm > 65535 ? 65536 : gm)};
+                best_wg = wg;
+                best_one_round = one_round;
+            }
+        }
+    }
+    return best;
+}
+inline bool w8a8_wide_one_round(int64_t M, int64_t N) {
+    const WideShape w = w8a8_wide_shape(M, N);
+    return (int64_t)w.groups_n * w.groups_m <= 256;
 }
 
 // Shape of a W8A16 all-token launch (blk128 and block-32): wide_shape above
@@ -107,23 +154,48 @@ inline WideShape w16_wide_shape(int64_t M, int64_t N) {
 
 // W8A8 dispatch (codes in), from the projection sweep:
 //  * the streaming kernel for M <= 16 when it needs no split of K, or when
-//    N < 1024, and for M <= 64 when its workgroups fit one round unsplit;
+//    N < 1024, except for 4 < M <= 16 with K <= 4096 where its launch takes
+//    more than one round (over 256 weight-row tiles) and the all-token
+//    kernel's fits one; and for M <= 64 when its workgroups fit one round
+//    unsplit;
 //  * the all-token kernel (launch_w8a8_wide: every token of a 32- or
 //    64-token group per workgroup, no split) for the other M <= 32, and
-//    when K <= 4096 and M * N <= 2^19 (M <= 128 at N = 4096, M <= 512 at
-//    N = 1024); measured (us, 32 rotated weight copies): 1024 x 4096 at
+//    when K <= 4096 and its launch fits one round (w8a8_wide_shape; up to
+//    M * N = 2^20: M <= 256 at N = 4096, M <= 1024 at N = 1024); measured
+//    (us, 32 rotated weight copies): 1024 x 4096 at
 //    M = 1 / 16: 4.3 / 4.4 against 5.3 / 5.5 streamed with K split 4 ways;
 //    at M = 32: 4096 x 4096 6.7, 1024 x 4096 4.9, 12288 x 4096 16.5,
 //    4096 x 12288 17.1 against 11.6, 9.8, 22.5 and 17.8 tiled; 4096 x 4096
 //    at M = 48 / 64 / 96 / 128: 7.8 / 8.7 / 10.8 / 12.5 against 12.1 /
 //    12.7 / 13.5 / 14.3 tiled; 1024 x 4096 at M = 128 / 256 / 512: 5.4 /
-//    6.4 / 9.4 against 11.2 / 11.9 / 12.9; but 4096 x 4096 at M = 256 21.2
-//    vs 18.0 and 2048 x 4096 at M = 512 19.4 vs 16.9, 12288 x 4096 at
-//    M = 64 / 128 even (24.1 / 33.9 vs 24.3 / 33.8), and with K = 12288 and
-//    M >= 64 the tiled kernels win (M = 64: 19.2 vs 29.0 us);
+//    6.4 / 9.4 against 11.2 / 11.9 / 12.9; with four weight-row tiles per
+//    workgroup 4096 x 4096 at M = 160 / 192 / 256 13.0 / 13.9 / 14.0 against
+//    16.2 / 16.4 / 17.7 tiled, 2048 x 4096 at M = 384 / 512 12.2 / 12.7
+//    against 16.5 / 17.1, 1024 x 4096 at M = 768 / 1024 10.2 / 11.6 against
+//    15.4 / 16.6, 12288 x 4096 at M = 64 17.1 against 17.4; but two rounds
+//    lose (4096 x 4096 M = 320 / 384: 21.4 / 21.9 against 18.5 / 20.4 tiled,
+//    12288 x 4096 M = 48 / 128 18.8 / 25.5 against 16.2 / 22.5), and with
+//    K > 4096 and M > 32 the tiled kernels win or tie (4096 x 12288 M = 64
+//    / 128: 19.9 / 26.1 against 18.3 / 24.7; 2048 x 8192 M = 256 22.3
+//    against 18.2);
 //  * the tiled kernels otherwise.
 inline bool w8a8_streams(int64_t M, int64_t N, int64_t K) {
-    if (M <= kStreamMaxM) return N < 1024 || K > kTileMaxK || plan_stream(M, N, K).splits == 1;
+    if (M <= kStreamMaxM) {
+        if (N < 1024 || K > kTileMaxK) return true;
+        const StreamPlan p = plan_stream(M, N, K);
+        if (p.splits > 1) return false;
+        // One round of the all-token kernel against several of the streaming
+        // kernel's 16-row workgroups (us, streaming against all-token, K =
+        // 4096): 12288 x 4096 M = 5 / 8 / 16 14.2 / 14.3 / 15.3 against
+        // 12.1 / 11.8 / 12.1, 8192 x 4096 M = 5 / 8 / 16 9.8 / 10.2 / 10.8
+        // against 9.2 / 9.2 / 9.2, 6144 x 4096 M = 16 10.2 against 8.1,
+        // 16384 x 4096 M = 16 19.6 against 15.9.  Not at M <= 4 (12288 x
+        // 4096 M = 2 / 4: 11.3 / 11.4 against 12.1 / 11.7), nor where the
+        // streaming launch fits one round (4096 x 4096 M = 8 / 16: 5.7 / 6.1
+        // against 6.2 / 6.4), nor at K = 8192 (8192 x 8192 M = 8 / 16: 15.1 /
+        // 17.0 against 18.1 / 18.3).
+        return !(M > 4 && K <= 4096 && p.n_tiles * p.m_tiles > 256 && w8a8_wide_one_round(M, N));
+    }
     // More than one token tile (one workgroup per weight-row tile and token
     // tile, the weights read once per token tile): on small projections,
     // where every such workgroup fits in one round on the CUs without a
@@ -135,7 +207,7 @@ inline bool w8a8_streams(int64_t M, int64_t N, int64_t K) {
 }
 inline bool w8a8_wide(int64_t M, int64_t N, int64_t K) {
     if (K > kTileMaxK || w8a8_streams(M, N, K)) return false;
-    return M <= 2 * kStreamMaxM || (K <= 4096 && M * N <= ((int64_t)1 << 19));
+    return M <= 2 * kStreamMaxM || (K <= 4096 && w8a8_wide_one_round(M, N));
 }
 // Workspace bytes of a streaming plan: tile counters, then fp32 partial tiles.
 size_t stream_workspace_bytes(const StreamPlan& p);
@@ -267,8 +339,10 @@ inline bool one_token_w8a16(int64_t M, int64_t K) { return M == 1 && K <= kOneTo
 // (W8A8 9.8 vs 10.6 us, W8A16 9.7 vs 10.55) and equal at 4096 x 7168.
 constexpr int kGemvLaunchWaves = 8;    // waves per workgroup of the one-token kernels
 constexpr int kStreamLaunchWaves = 16;  // waves per workgroup of the streaming kernels
-// Waves per workgroup of the W8A8 all-token kernel for kt token tiles.
-constexpr int w8a8_wide_waves(int kt) { return kt == 4 ? 4 : 8; }
+// Waves per workgroup of the W8A8 all-token kernel for kr weight-row tiles
+// and kt token tiles: four where a slot is large (kr = 4 or kt = 4), so
+// that two or three slots per wave fit in LDS, else eight.
+constexpr int w8a8_wide_waves(int kr, int kt) { return kr == 4 || kt == 4 ? 4 : 8; }
 // W8A16 all-token kernel (kr weight-row tiles, kt token tiles): token tiles
 // per wave, all of them wherever four waves' LDS rings hold them (every
 // case but kt = 4 with kr = 2), else one; and the waves per workgroup.

@@ -372,12 +372,12 @@ __global__ __launch_bounds__(kStreamThreads) void w8a8_stream_quant_kernel(
 
 // ------------------------------------------------------------ wide stream ----
 // All-token kernel (see w8a8_wide for where it is used): a workgroup owns
-// 16 kR weight rows (kR = 1 or 2 MFMA row tiles) and 16 kT tokens (kT = 2
-// or 4 token tiles; grid.y covers the tokens beyond) over all of K, so the
-// weights are read once and no split-K hand-off is needed.  Every wave
-// takes all kT token tiles and the 128-K blocks w, w + W, ... (W waves:
-// eight for kT = 2, four for kT = 4, whose slots are twice as large), so
-// each block's weight rows are loaded once per workgroup.  Each wave owns
+// 16 kR weight rows (kR = 1, 2 or 4 MFMA row tiles) and 16 kT tokens
+// (kT = 2 or 4 token tiles; grid.y covers the tokens beyond) over all of K,
+// so no split-K hand-off is needed.  Every wave takes all kR x kT output
+// tiles and the 128-K blocks w, w + W, ... (W waves: eight for kR <= 2 with
+// kT = 2, four where the slots are larger, kR = 4 or kT = 4), so each
+// block's weight rows are loaded once per workgroup.  Each wave owns
 // a ring of LDS slots (two or three); a slot holds one block: the
 // workgroup's 16 kR weight rows, the 16 kT token rows, their token scales
 // and the weight scale, brought in by direct-to-LDS loads of whole 128-byte
@@ -392,11 +392,14 @@ __global__ __launch_bounds__(kStreamThreads) void w8a8_stream_quant_kernel(
 // of the weight rows (4096 x 4096 M = 128 12.36 vs 11.33 us, M = 96 10.53 vs
 // 10.21; 1024 x 4096 M = 512 8.34 vs 8.13); with two token tiles eight
 // waves stay ahead of four (M = 24 / 32: 6.84 / 7.37 vs 7.08 / 7.52 us).
-template <int kT>
-constexpr int wide_waves() { return w8a8_wide_waves(kT); }
+// Four weight-row tiles (a 64 x 64 output tile per wave with kT = 4) serve
+// where they keep the launch to one round, e.g. 4096 x 4096 at M = 256 in
+// 14.0 us against 17.7 for the best tiled plan (w8a8_wide_shape).
+template <int kR, int kT>
+constexpr int wide_waves() { return w8a8_wide_waves(kR, kT); }
 template <int kR, int kT>
 struct WideSlot {
-    static constexpr int kWaves = wide_waves<kT>();
+    static constexpr int kWaves = wide_waves<kR, kT>();
     static constexpr int kOffX = kR * kSlabBytes;                 // 16 kT token rows
     static constexpr int kOffXs = kOffX + kT * kSlabBytes;        // 64 token scales (lanes past 16 kT load padding)
     static constexpr int kOffWs = kOffXs + 64 * 4;                // weight scale
@@ -415,7 +418,7 @@ __device__ __forceinline__ void wide_wait_n() {
 }
 
 template <int kR, int kT>
-__global__ __launch_bounds__(wide_waves<kT>() * kWave, 1) void w8a8_wide_kernel(
+__global__ __launch_bounds__((wide_waves<kR, kT>()) * kWave, 1) void w8a8_wide_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ xs,
     const uint8_t* __restrict__ wq, const float* __restrict__ ws,
     void* __restrict__ y, int y_dtype, int64_t M, int64_t N, int64_t K) {
@@ -423,7 +426,9 @@ __global__ __launch_bounds__(wide_waves<kT>() * kWave, 1) void w8a8_wide_kernel(
     constexpr int W = SL::kWaves;
     constexpr int kWideSlots = SL::kSlots, kWideSlot = SL::kBytes;
     static_assert(kT == 2 || kT == 4, "token tiles");
+    static_assert(kR == 1 || kR == 2 || kR == 4, "weight-row tiles within one 128-row scale block");
     __shared__ __attribute__((aligned(1024))) uint8_t ring[W * kWideSlots * kWideSlot];
+    static_assert(W * kR * kT * kWave * 16 <= W * kWideSlots * kWideSlot, "partial tiles fit the ring");
     const int64_t nt = blockIdx.x;            // 16 kR weight rows
     const int64_t mg = blockIdx.y;            // 16 kT tokens
     const int KB = (int)(K / 128);
@@ -546,13 +551,16 @@ __global__ __launch_bounds__(wide_waves<kT>() * kWave, 1) void w8a8_wide_kernel(
 hipError_t launch_w8a8_wide(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
                             void* y, int y_dtype, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
     if (M < 1 || N % 16 != 0 || K > kTileMaxK) return hipErrorInvalidValue;
-    const WideShape w = wide_shape(M, N);
+    const WideShape w = w8a8_wide_shape(M, N);
     if (w.groups_m > 65535) return hipErrorInvalidValue;
     const dim3 grid(w.groups_n, w.groups_m);
-#define BFP8_LAUNCH_WIDE(R, T)                                                                                \
-    hipLaunchKernelGGL((w8a8_wide_kernel<R, T>), grid, dim3(wide_waves<T>() * kWave), 0, stream, xq, xs, wq, ws, y, \
-                       y_dtype, M, N, K)
-    if (w.kr == 1) {
+#define BFP8_LAUNCH_WIDE(R, T)                                                                                   \
+    hipLaunchKernelGGL((w8a8_wide_kernel<R, T>), grid, dim3(wide_waves<R, T>() * kWave), 0, stream, xq, xs, wq, ws, \
+                       y, y_dtype, M, N, K)
+    if (w.kr == 4) {
+        if (w.kt == 2) BFP8_LAUNCH_WIDE(4, 2);
+        else BFP8_LAUNCH_WIDE(4, 4);
+    } else if (w.kr == 1) {
         if (w.kt == 2) BFP8_LAUNCH_WIDE(1, 2);
         else BFP8_LAUNCH_WIDE(1, 4);
     } else {

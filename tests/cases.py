@@ -64,12 +64,20 @@ W8A8_NO_WORKSPACE = [
     (1, 1024, 12288, "w8a8_wide:16x32w8"), (5, 2048, 12288, "w8a8_wide:16x32w8"),
     (16, 1024, 12288, "w8a8_wide:16x32w8"), (17, 1024, 4096, "w8a8_stream"), (24, 1024, 4096, "w8a8_stream"),
     (32, 4096, 4096, "w8a8_wide:16x32w8"), (33, 4096, 4096, "w8a8_wide:32x32w8"), (50, 1024, 4096, "w8a8_stream"),
-    (64, 4096, 4096, "w8a8_wide:32x32w8"), (32, 12288, 256, "w8a8_wide:32x32w8"), (20, 16, 8192, "w8a8_stream"),
-    (20, 8208, 256, "w8a8_wide:32x32w8"), (65, 8192, 512, "w8a8_tile:64x128w8"),
-    (100, 4096, 1024, "w8a8_wide:32x64w4"), (128, 1040, 2048, "w8a8_wide:16x32w8"), (20, 64, 128, "w8a8_stream"),
-    (128, 8192, 128, "w8a8_tile:64x128w8"), (64, 1024, 4096, "w8a8_stream"), (40, 2048, 1024, "w8a8_wide:16x32w8"),
-    (61, 512, 8192, "w8a8_stream"), (300, 1024, 2048, "w8a8_wide:32x32w8"), (512, 1024, 512, "w8a8_wide:32x64w4"),
-    (256, 1040, 1024, "w8a8_wide:16x64w4"),
+    (64, 4096, 4096, "w8a8_wide:32x32w8"), (32, 12288, 256, "w8a8_wide:64x32w4"), (20, 16, 8192, "w8a8_stream"),
+    (20, 8208, 256, "w8a8_wide:64x32w4"),                 # last 64-row weight tile holds 16 rows
+    (65, 8192, 512, "w8a8_wide:64x64w4"),
+    (100, 4096, 1024, "w8a8_wide:64x32w4"), (128, 1040, 2048, "w8a8_wide:32x32w8"), (20, 64, 128, "w8a8_stream"),
+    (128, 8192, 128, "w8a8_wide:64x64w4"),                # one K block: three of the four waves idle
+    (64, 1024, 4096, "w8a8_stream"), (40, 2048, 1024, "w8a8_wide:16x32w8"),
+    (61, 512, 8192, "w8a8_stream"), (300, 1024, 2048, "w8a8_wide:64x32w4"), (512, 1024, 512, "w8a8_wide:64x32w4"),
+    (256, 1040, 1024, "w8a8_wide:64x32w4"), (90, 4096, 1024, "w8a8_wide:32x64w4"),
+    (144, 1040, 1024, "w8a8_wide:16x64w4"),               # ragged M and N
+    (260, 2064, 1024, "w8a8_wide:64x64w4"),               # ragged M and N (16 rows in the last weight tile)
+    (256, 4096, 4096, "w8a8_wide:64x64w4"),
+    # 4 < M <= 16 where streaming would take several rounds of 16-row tiles
+    (8, 12288, 1024, "w8a8_wide:64x32w4"), (16, 6160, 2048, "w8a8_wide:32x32w8"),   # ragged N
+    (5, 8192, 512, "w8a8_wide:32x32w8"), (12, 16400, 256, "w8a8_stream"),          # no one-round shape
 ]
 
 # Every tiled configuration, ragged M and N tiles, split K.
@@ -77,9 +85,9 @@ W8A8_TILE = [
     (40, 8192, 8192, "w8a8_tile:128x64w8/split"),
     (65, 1024, 8192, "w8a8_tile:64x128w8/split"),
     (100, 1024, 8192, "w8a8_tile:64x128w8/split"),
-    (200, 4096, 2176, "w8a8_tile:64x128w8/split"),        # last split shorter
+    (200, 2048, 4224, "w8a8_tile:64x128w8/split"),        # last split shorter (33 blocks in 4)
     (66, 2064, 8192, "w8a8_tile:64x128w8/split"),         # ragged N and M
-    (300, 2064, 1024, "w8a8_tile:64x128w8"),              # ragged N, K not split
+    (500, 2064, 1024, "w8a8_tile:64x128w8"),              # ragged N and M, K not split
     (1000, 4096, 1024, "w8a8_tile:128x128w8"),
     (400, 2048, 8192, "w8a8_tile:128x128w8/split"),       # ragged M
     (512, 4096, 8192, "w8a8_tile:128x128w8/split"),
@@ -100,7 +108,8 @@ QUANT_W8A8 = [
     (3, 512, 640, "w8a8_stream_quant"), (4, 384, 12288, "w8a8_stream_quant/split"),
     (5, 1024, 4096, "w8a8_stream_quant"), (8, 512, 1024, "w8a8_stream_quant"), (9, 512, 640, "quant+w8a8_stream"),
     (16, 1024, 4096, "quant+w8a8_stream"), (17, 384, 640, "quant+w8a8_stream"), (64, 1024, 4096, "quant+w8a8_stream"),
-    (300, 1040, 1024, "quant+w8a8_wide:16x64w4"), (200, 4096, 2176, "quant+w8a8_tile:64x128w8/split"),
+    (300, 1040, 1024, "quant+w8a8_wide:64x32w4"), (200, 2048, 4224, "quant+w8a8_tile:64x128w8/split"),
+    (6, 8192, 1024, "quant+w8a8_wide:32x32w8"), (16, 12288, 512, "quant+w8a8_wide:64x32w4"),
 ]
 
 # ---------------------------------------------------------------- W8A16 ----

@@ -103,14 +103,18 @@ def test_workspace_sizes(lib):
     assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 1, 1024, 12288) == 0  # all-token kernel
     assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 4096, 1024, 4096) == 0   # 128x128 tiles
     assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 4096, 4096, 4096) == 0   # 256x256 tiles
-    # 16 < M <= 32, and M * N <= 2^19 with K <= 4096: one workgroup per 16 or
-    # 32 weight rows holds every token of its group over all of K, no workspace
+    # 16 < M <= 32, and K <= 4096 where the launch fits one round: one
+    # workgroup per 16, 32 or 64 weight rows holds every token of its group
+    # over all of K, no workspace
     assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 32, 1024, 4096) == 0
     assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 32, 12288, 4096) == 0
     assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 64, 4096, 4096) == 0
-    # ... while 12288 x 4096 at M = 64 is tiled (128x64 tiles, K split 2 ways:
-    # 192 workgroups in one round), and so is 4096 x 12288 (K split 8 ways)
-    assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 64, 12288, 4096) == 512 + 96 * 2 * 128 * 64 * 4
+    assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 64, 12288, 4096) == 0
+    assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 256, 4096, 4096) == 0
+    # ... while 12288 x 4096 at M = 128 is tiled (128x128 tiles, K split 2
+    # ways: 192 workgroups in one round), and so is 4096 x 12288 at M = 64
+    # (K split 8 ways)
+    assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 128, 12288, 4096) == 512 + 96 * 2 * 128 * 128 * 4
     assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 64, 4096, 12288) == 256 + 32 * 8 * 128 * 64 * 4
     # mid M: 64x128 tiles, K split 4 ways -> counters + 4 fp32 partial tiles per output tile
     assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 100, 4096, 8192) == 256 + 64 * 4 * 64 * 128 * 4

@@ -93,13 +93,15 @@ def test_w8a8_split_k_narrow_projection(gpu_lib, M, N, K, kernel):
 
 @pytest.mark.parametrize("M,N,K,kernel", cases.W8A8_NO_WORKSPACE)
 def test_w8a8_wide_all_tokens(gpu_lib, M, N, K, kernel):
-    """The paths that need no workspace for M <= 128: the kernel that holds
-    every token per 16- or 32-row weight tile (M <= 16 where streaming would
-    split K, 16 < M <= 32, M <= 128 with K <= 4096) and the streaming kernel
-    over 16-token tiles on small projections (grid.z, e.g. N = 1024 or 16 at
-    M <= 64); ragged M inside the last token tile and in a second token
-    group, a single 16-row weight tile, a 32-row tile with only 16 live rows
-    (N = 8208), and K spread unevenly over the waves."""
+    """The paths that need no workspace for M <= 512: the kernel that holds
+    every token of a group per 16-, 32- or 64-row weight tile (M <= 16 where
+    streaming would split K or take several rounds, 16 < M <= 32, and K <=
+    4096 where its launch fits one round) and the streaming kernel over
+    16-token tiles on small projections (grid.z, e.g. N = 1024 or 16 at
+    M <= 64); ragged M inside the last token tile and in a further token
+    group, a single 16-row weight tile, 64-row tiles with only 16 live rows
+    (N = 8208, 2064), one K block for four waves, and K spread unevenly over
+    the waves."""
     assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, M, N, K) == 0
     _w8a8_check(M, N, K, 900 + M, what="wide", kernel=kernel)
 

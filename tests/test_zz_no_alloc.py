@@ -39,8 +39,8 @@ def _both(xq, xs, wq, ws, out_dtype):
 
 
 @pytest.mark.parametrize("first,second", [
-    ((400, 2048, 8192), (100, 1024, 8192)),     # 128x128 four waves split 4, then 64x128 split 16
-    ((200, 4096, 2176), (16, 512, 12288)),      # 64x128 split 2, then the streaming kernel split over K
+    ((400, 2048, 8192), (100, 1024, 8192)),     # 128x128 split 4, then 64x128 split 8
+    ((200, 2048, 4224), (16, 512, 12288)),      # 64x128 split 4, then the streaming kernel split over K
     ((128, 4096, 4096), (1, 1024, 4096)),       # no workspace: all-token kernel, then one token
 ])
 def test_noalloc_matches_workspace_call(gpu_lib, first, second):
