@@ -489,7 +489,9 @@ bfp8_status bfp8_get_plan(int op, int64_t M, int64_t N, int64_t K, bfp8_plan* pl
         case BFP8_KERNEL_W8A8_WIDE:
         case BFP8_KERNEL_W8A16_WIDE:
         case BFP8_KERNEL_BLK32_WIDE: {
-            const WideShape w = p.kernel == BFP8_KERNEL_W8A8_WIDE ? w8a8_wide_shape(M, N) : w16_wide_shape(M, N);
+            const WideShape w = p.kernel == BFP8_KERNEL_W8A8_WIDE   ? w8a8_wide_shape(M, N)
+                                : p.kernel == BFP8_KERNEL_BLK32_WIDE ? blk32_wide_shape(M, N)
+                                                                     : w16_wide_shape(M, N);
             p.tile_n = 16 * w.kr;
             p.tile_m = 16 * w.kt;
             p.waves = p.kernel == BFP8_KERNEL_W8A8_WIDE ? w8a8_wide_waves(w.kr, w.kt) : w16_wide_waves(w.kr, w.kt);

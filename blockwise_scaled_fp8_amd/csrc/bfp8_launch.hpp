@@ -48,22 +48,104 @@ struct WideShape {
     int kr, kt;
     unsigned groups_n, groups_m;
 };
-// W8A16 rule (w16_wide_shape above 16 tokens): among (kr, kt) in {1, 2} x
-// {2, 4} (kt = 4 only when M needs at least four token tiles) the one with
-// the fewest workgroups that still gives at least 256, one per CU, and two
-// weight tiles on a tie (each token byte then feeds twice the weights);
-// with no such candidate, the one with the most workgroups.  Measured over
-// every (kr, kt), K = 4096, 32 rotated weight copies, this picks the
-// fastest at each point tried (us): 4096 x 4096 M = 32 (1, 2) 9.6, M = 64
-// (2, 2) 11.9 against 14.0 for (1, 4), M = 128 (2, 4) 17.8; 1024 x 4096
-// M = 128 (1, 2) 7.5 against 10.4 for (1, 4), M = 256 (2, 2) 9.8;
-// 12288 x 4096 M = 32 (2, 2) 22.3.
-inline WideShape wide_shape(int64_t M, int64_t N) {
-    const int64_t m_tiles = (M + 15) / 16;
+
+// One-round choice of the W8A8 and W8A16 blk128 all-token shapes: when some
+// candidate's launch fits one round on the CUs (at most 256 workgroups), the
+// one with the most workgroups, the larger kr on a tie; otherwise the one
+// with the fewest, the larger kr on a tie.  Two rounds of these kernels cost
+// more than one round of larger tiles, and at equal counts more weight rows
+// per workgroup cut the token bytes per output.
+struct WidePick {
     WideShape best{1, 2, 0, 0};
     int64_t best_wg = -1;
-    bool best_full = false;
+    bool best_one_round = false;
+    void consider(int kr, int kt, int64_t M, int64_t N) {
+        if (kr > 1 && N <= 8 * kr) return;   // half the rows or more would be padding
+        const int64_t gn = (N + 16 * kr - 1) / (16 * kr), gm = (M + 16 * kt - 1) / (16 * kt);
+        const int64_t wg = gn * gm;
+        const bool one_round = wg <= 256;
+        const bool tie_kr = wg == best_wg && kr > best.kr;
+        const bool better = best_wg < 0 || (one_round && !best_one_round) ||
+                            (one_round && best_one_round && (wg > best_wg || tie_kr)) ||
+                            (!one_round && !best_one_round && (wg < best_wg || tie_kr));
+        if (better) {
+            best = WideShape{kr, kt, (unsigned)gn, (unsigned)(gm > 65535 ? 65536 : gm)};
+            best_wg = wg;
+            best_one_round = one_round;
+        }
+    }
+};
+
+// W8A8: (kr, kt) in {1, 2, 4} x {2, 4} (kt = 4 only when M needs at least
+// four token tiles), chosen by WidePick.  Measured (us, 32 rotated weight
+// copies, K = 4096; the pick first): 4096 x 4096 M = 64 (2, 2) 8.4 against
+// 10.7 for (4, 2), M = 96 (2, 4) 10.1 against 10.7 for (4, 2), M = 128
+// (4, 2) 10.7 against 11.2 for (2, 4) and 14.2 for (4, 4), M = 160 / 192 /
+// 256 (4, 4) 13.0 / 13.9 / 14.0 (192 / 192 / 256 workgroups) against 17.8
+// for (2, 4) at M = 192; 1024 x 4096 M = 256 (2, 2) 5.9 against 6.8 for
+// (1, 4), M = 512 (4, 2) 8.35 against 8.46 for (2, 4), M = 768 / 1024
+// (4, 4) 10.2 / 11.6; 2048 x 4096 M = 128 (2, 2) 6.7 against 8.0 for (1, 4),
+// M = 512 (4, 4) 12.7; 12288 x 4096 M = 32 (4, 2) 13.8 against 16.4 for
+// (2, 2), M = 64 (4, 4) 17.1 against 21.9 for (2, 2); 16384 x 4096 M = 32
+// (4, 2) 16.7 against 18.1.
+inline WideShape w8a8_wide_shape(int64_t M, int64_t N) {
+    const int64_t m_tiles = (M + 15) / 16;
+    WidePick pick;
     for (int kt = 2; kt <= 4; kt += 2) {
+        if (kt > 2 && kt > m_tiles) continue;
+        for (int kr = 4; kr >= 1; kr /= 2) pick.consider(kr, kt, M, N);
+    }
+    return pick.best;
+}
+inline bool w8a8_wide_one_round(int64_t M, int64_t N) {
+    const WideShape w = w8a8_wide_shape(M, N);
+    return (int64_t)w.groups_n * w.groups_m <= 256;
+}
+
+// W8A16 blk128: one 16-token tile (kt = 1) for M <= 16, else kt = 2 or 4
+// (4 only when M needs at least four token tiles); kr = 1, 2 or 4, without
+// (4, 4) (its slots do not fit LDS twice per wave) and (2, 4) (its token
+// tiles go to different waves, each loading the same weight rows); chosen
+// by WidePick.  Measured (us, K = 4096, 32 rotated weight copies; the pick
+// first): 4096 x 4096 M = 16 (1, 1) 6.8 against 10.2 for (4, 1), M = 96
+// (4, 2) 12.1 (192 workgroups) against 15.2 for (2, 4) (256), M = 128
+// (4, 2) 12.1 against 16.4 for (2, 4); 12288 x 4096 M = 12 / 16 (4, 1)
+// 12.7 / 13.1 against 15.0 / 15.4 for (2, 1), M = 24 / 32 (4, 2) 14.5 /
+// 15.2 against 18.2 / 19.2 for (2, 2); 8192 x 4096 M = 16 (2, 1) 9.5
+// against 11.4 for (4, 1), M = 32 (2, 2) 11.6 against 13.7 for (4, 2);
+// 16384 x 4096 M = 16 (4, 1) 16.1 against 17.2 for (2, 1); 1024 x 4096
+// M = 256 (2, 2) 7.7 against 9.4 for (4, 2), M = 512 (4, 2) 10.3 (the tiled
+// kernel 19.1); 4096 x 7168 M = 32 (1, 2) 12.2 against 19.8 for (4, 2).
+inline WideShape w16_wide_shape(int64_t M, int64_t N) {
+    WidePick pick;
+    if (M <= 16) {
+        for (int kr = 4; kr >= 1; kr /= 2) pick.consider(kr, 1, M, N);
+        return pick.best;
+    }
+    const int64_t m_tiles = (M + 15) / 16;
+    for (int kt = 2; kt <= 4; kt += 2) {
+        if (kt > 2 && kt > m_tiles) continue;
+        for (int kr = 4; kr >= 1; kr /= 2)
+            if (kt == 2 || kr == 1) pick.consider(kr, kt, M, N);
+    }
+    return pick.best;
+}
+
+// Block-32 all-token shape (kr <= 2: a workgroup's rows share one 32-row
+// band of UE8M0 scales): for M <= 16 one 16-token tile and kr = 1 or 2,
+// the fewest workgroups that still give one per CU, two row tiles on a tie,
+// else the most workgroups (measured at M = 16 on the blk128 kernel, kR = 1
+// against 2, us: 4096 x 4096 6.91 / 7.73, 1024 x 4096 4.59 / 5.33,
+// 4096 x 12288 14.57 / 18.22, but 12288 x 4096 17.63 / 15.39); above 16
+// tokens (kr, kt) in {1, 2} x {2, 4} by the same rule (kt = 4 only when M
+// needs at least four token tiles; 4096 x 7168 M = 32 (1, 2) 12.2, M = 64
+// (2, 2) 16.5).
+inline WideShape blk32_wide_shape(int64_t M, int64_t N) {
+    const int64_t m_tiles = (M + 15) / 16;
+    WideShape best{1, M <= 16 ? 1 : 2, 0, 0};
+    int64_t best_wg = -1;
+    bool best_full = false;
+    for (int kt = M <= 16 ? 1 : 2; kt <= (M <= 16 ? 1 : 4); kt *= 2) {
         if (kt > 2 && kt > m_tiles) continue;
         for (int kr = 2; kr >= 1; --kr) {
             const int64_t gn = (N + 16 * kr - 1) / (16 * kr), gm = (M + 16 * kt - 1) / (16 * kt);
@@ -80,78 +162,6 @@ inline WideShape wide_shape(int64_t M, int64_t N) {
     return best;
 }
 
-// W8A8 rule: (kr, kt) in {1, 2, 4} x {2, 4} (kt = 4 only when M needs at
-// least four token tiles).  When some candidate fits one round on the CUs
-// (at most 256 workgroups), the one with the most workgroups, the larger kr
-// on a tie; otherwise the one with the fewest, the larger kr on a tie.  Two
-// rounds of this kernel cost more than one round of larger tiles, and at
-// equal counts more weight rows per workgroup cut the token bytes per
-// output.  Measured (us, 32 rotated weight copies, K = 4096; the pick
-// first): 4096 x 4096 M = 64 (2, 2) 8.4 against 10.7 for (4, 2), M = 96
-// (2, 4) 10.1 against 10.7 for (4, 2), M = 128 (4, 2) 10.7 against 11.2 for
-// (2, 4) and 14.2 for (4, 4), M = 160 / 192 / 256 (4, 4) 13.0 / 13.9 / 14.0
-// (192 / 192 / 256 workgroups) against 17.8 for (2, 4) at M = 192;
-// 1024 x 4096 M = 256 (2, 2) 5.9 against 6.8 for (1, 4), M = 512 (4, 2) 8.35
-// against 8.46 for (2, 4), M = 768 / 1024 (4, 4) 10.2 / 11.6; 2048 x 4096
-// M = 128 (2, 2) 6.7 against 8.0 for (1, 4), M = 512 (4, 4) 12.7;
-// 12288 x 4096 M = 32 (4, 2) 13.8 against 16.4 for (2, 2), M = 64 (4, 4)
-// 17.1 against 21.9 for (2, 2); 16384 x 4096 M = 32 (4, 2) 16.7 against 18.1.
-inline WideShape w8a8_wide_shape(int64_t M, int64_t N) {
-    const int64_t m_tiles = (M + 15) / 16;
-    WideShape best{1, 2, 0, 0};
-    int64_t best_wg = -1;
-    bool best_one_round = false;
-    for (int kt = 2; kt <= 4; kt += 2) {
-        if (kt > 2 && kt > m_tiles) continue;
-        for (int kr = 4; kr >= 1; kr /= 2) {
-            const int64_t gn = (N + 16 * kr - 1) / (16 * kr), gm = (M + 16 * kt - 1) / (16 * kt);
-            const int64_t wg = gn * gm;
-            const bool one_round = wg <= 256;
-            // Candidates come larger kr first within a kt, so a strict
-            // comparison keeps the larger kr on a tie within that kt; across
-            // kt a tie goes to the larger kr explicitly.
-            const bool tie_kr = wg == best_wg && kr > best.kr;
-            const bool better = best_wg < 0 || (one_round && !best_one_round) ||
-                                (one_round && best_one_round && (wg > best_wg || tie_kr)) ||
-                                (!one_round && !best_one_round && (wg < best_wg || tie_kr));
-            if (better) {
-                best = WideShape{kr, kt, (unsigned)gn, (unsigned)(gm > 65535 ? 65536 : gm)};
-                best_wg = wg;
-                best_one_round = one_round;
-            }
-        }
-    }
-    return best;
-}
-inline bool w8a8_wide_one_round(int64_t M, int64_t N) {
-    const WideShape w = w8a8_wide_shape(M, N);
-    return (int64_t)w.groups_n * w.groups_m <= 256;
-}
-
-// Shape of a W8A16 all-token launch (blk128 and block-32): wide_shape above
-// 16 tokens; for M <= 16 one 16-token tile (kt = 1) and kr by the same rule
-// (fewest workgroups that still give one per CU, two row tiles on a tie,
-// else the most workgroups): measured at M = 16, kR = 1 against 2 (us):
-// 4096 x 4096 6.91 / 7.73, 1024 x 4096 4.59 / 5.33, 4096 x 12288 14.57 /
-// 18.22, but 12288 x 4096 17.63 / 15.39 (768 workgroups against 384).
-inline WideShape w16_wide_shape(int64_t M, int64_t N) {
-    if (M > 16) return wide_shape(M, N);
-    WideShape best{1, 1, 0, 1};
-    int64_t best_wg = -1;
-    bool best_full = false;
-    for (int kr = 2; kr >= 1; --kr) {
-        const int64_t wg = (N + 16 * kr - 1) / (16 * kr);
-        const bool full = wg >= 256;
-        const bool better = best_wg < 0 || (full && (!best_full || wg < best_wg)) || (!full && !best_full && wg > best_wg);
-        if (better) {
-            best = WideShape{kr, 1, (unsigned)wg, 1};
-            best_wg = wg;
-            best_full = full;
-        }
-    }
-    return best;
-}
-
 // W8A8 dispatch (codes in), from the projection sweep:
 //  * the streaming kernel for M <= 16 when it needs no split of K, or when
 //    N < 1024, except for 4 < M <= 16 with K <= 4096 where its launch takes
@@ -160,8 +170,9 @@ inline WideShape w16_wide_shape(int64_t M, int64_t N) {
 //    unsplit;
 //  * the all-token kernel (launch_w8a8_wide: every token of a 32- or
 //    64-token group per workgroup, no split) for the other M <= 32, and
-//    when K <= 4096 and its launch fits one round (w8a8_wide_shape; up to
-//    M * N = 2^20: M <= 256 at N = 4096, M <= 1024 at N = 1024); measured
+//    when K <= 4096 and either M * N <= 2^19 or N >= 512 and its launch
+//    fits one round (w8a8_wide_shape; up to M * N = 2^20: M <= 256 at
+//    N = 4096, M <= 1024 at N = 1024); measured
 //    (us, 32 rotated weight copies): 1024 x 4096 at
 //    M = 1 / 16: 4.3 / 4.4 against 5.3 / 5.5 streamed with K split 4 ways;
 //    at M = 32: 4096 x 4096 6.7, 1024 x 4096 4.9, 12288 x 4096 16.5,
@@ -207,7 +218,12 @@ inline bool w8a8_streams(int64_t M, int64_t N, int64_t K) {
 }
 inline bool w8a8_wide(int64_t M, int64_t N, int64_t K) {
     if (K > kTileMaxK || w8a8_streams(M, N, K)) return false;
-    return M <= 2 * kStreamMaxM || (K <= 4096 && w8a8_wide_one_round(M, N));
+    // Past M * N = 2^19 only for N >= 512: with four or fewer 64-row tiles
+    // the workgroups that share a token group sit on different XCDs and each
+    // fetches it (4096 tokens x 256 rows: 21.1 us against 16.8 tiled;
+    // 2048 x 512 14.8 against 16.8).
+    return M <= 2 * kStreamMaxM ||
+           (K <= 4096 && (M * N <= ((int64_t)1 << 19) || (N >= 512 && w8a8_wide_one_round(M, N))));
 }
 // Workspace bytes of a streaming plan: tile counters, then fp32 partial tiles.
 size_t stream_workspace_bytes(const StreamPlan& p);
@@ -254,17 +270,22 @@ hipError_t launch_w8a16_blk32_tile(const void* x, const uint8_t* wq, const uint8
 inline bool w8a16_one_tile(int64_t M, int64_t N, int64_t K) {
     return M > kStreamMaxM / 2 && M <= kStreamMaxM && K <= kTileMaxK && plan_stream(M, N, K).splits == 1;
 }
-// The W8A16 all-token launch of an M x N product fits one round of
-// workgroups on the 256 CUs.
+// The W8A16 blk128 / block-32 all-token launch of an M x N product fits one
+// round of workgroups on the 256 CUs.
 inline bool w16_one_round(int64_t M, int64_t N) {
     const WideShape w = w16_wide_shape(M, N);
     return (int64_t)w.groups_n * w.groups_m <= 256;
 }
+inline bool blk32_one_round(int64_t M, int64_t N) {
+    const WideShape w = blk32_wide_shape(M, N);
+    return (int64_t)w.groups_n * w.groups_m <= 256;
+}
 // W8A16 blk128 dispatch: the streaming kernel for M <= 16 except where
 // w8a16_one_tile holds; the all-token kernel (launch_w8a16_wide) there, for
-// 16 < M <= 256 when K <= 4096 and either M <= 32 or M * N <= 2^19, and for
-// 16 < M <= 64 when 4096 < K <= 8192 and its launch fits one round; the
-// tiled kernel otherwise.  Measured, us (all-token against tiled): K = 4096
+// M > 16 when K <= 4096 and either M <= 32 or its launch fits one round
+// (w16_wide_shape), and for 16 < M <= 64 when 4096 < K <= 8192 and its
+// launch fits one round; the tiled kernel otherwise.  Measured, us
+// (all-token against tiled; before four-row tiles): K = 4096
 // N = 4096 M = 32 / 64 / 128 9.6 / 11.9 / 17.8 against 13.7 / 14.2 / 20.4;
 // N = 1024 M = 64 / 128 / 256 7.0 / 7.5 / 9.8 against 11.5 / 17.0 / 18.1;
 // N = 12288 M = 32 22.3 vs 26.3, but from M = 64 there the tiled kernel wins
@@ -272,18 +293,20 @@ inline bool w16_one_round(int64_t M, int64_t N) {
 // 16.6 against 13.9 / 14.4 / 15.6 / 16.8, 1024 x 8192 M = 17 / 64 10.0 /
 // 11.3 against 13.0 / 13.7; but 12288 x 8192 (two rounds) M = 17 / 32 34.1
 // / 38.5 against 31.9 / 33.0 and 4096 x 12288 M = 17 / 32 18.2 / 22.2
-// against 17.3 / 17.6.
+// against 17.3 / 17.6.  With four-row tiles one round reaches further:
+// 1024 x 4096 M = 512 10.3 against 19.1 tiled, 12288 x 4096 M = 64 (two
+// rounds, left tiled) 22.9 against 25.9.
 inline bool w8a16_wide(int64_t M, int64_t N, int64_t K) {
     if (w8a16_one_tile(M, N, K)) return true;
-    if (M <= kStreamMaxM || M > 16 * kStreamMaxM) return false;
-    if (K <= 4096) return M <= 2 * kStreamMaxM || M * N <= ((int64_t)1 << 19);
+    if (M <= kStreamMaxM) return false;
+    if (K <= 4096) return M <= 2 * kStreamMaxM || w16_one_round(M, N);
     return K <= 8192 && M <= 4 * kStreamMaxM && w16_one_round(M, N);
 }
 // Block-32 dispatch: the one-token kernel for M = 1 (K <= kOneTokenRouteK);
 // the tiled kernel where blk32_tile holds; the all-token kernel
 // (launch_w8a16_blk32_wide) for the other M > 8 whose streaming plan would
 // not split K, one 16-token tile up to M = 16 and token groups of 32 or 64
-// above (wide_shape); the streaming kernels otherwise (M <= 8, and where K
+// above (blk32_wide_shape); the streaming kernels otherwise (M <= 8, and where K
 // is split: w8a16_blk32_stream_lds_kernel up to M = 16, one 16-token tile
 // per workgroup above).  Above M = 16 the streaming
 // kernel runs one 16-token tile per workgroup and so reads the weights
@@ -310,7 +333,7 @@ inline bool blk32_wide(int64_t M, int64_t N, int64_t K) {
 inline bool blk32_tile(int64_t M, int64_t N, int64_t K) {
     if (M <= kStreamMaxM || K > kTileMaxK || plan_stream(M, N, K).splits > 1) return false;
     if (K <= 4096) return !(M <= 2 * kStreamMaxM || (M <= 16 * kStreamMaxM && M * N <= ((int64_t)1 << 19)));
-    return !(K <= 8192 && M <= 2 * kStreamMaxM && w16_one_round(M, N));
+    return !(K <= 8192 && M <= 2 * kStreamMaxM && blk32_one_round(M, N));
 }
 // One token (W8A8 codes, W8A8 with activations quantised in the kernel,
 // W8A16 blk128, block-32): dot-product kernels on the vector ALUs, no
@@ -345,9 +368,10 @@ constexpr int kStreamLaunchWaves = 16;  // waves per workgroup of the streaming 
 constexpr int w8a8_wide_waves(int kr, int kt) { return kr == 4 || kt == 4 ? 4 : 8; }
 // W8A16 all-token kernel (kr weight-row tiles, kt token tiles): token tiles
 // per wave, all of them wherever four waves' LDS rings hold them (every
-// case but kt = 4 with kr = 2), else one; and the waves per workgroup.
-constexpr int w16_wide_tiles_per_wave(int kr, int kt) { return kt == 1 || (kt == 4 && kr == 2) ? 1 : kt; }
-constexpr int w16_wide_waves(int kr, int kt) { return w16_wide_tiles_per_wave(kr, kt) > 1 ? 4 : 8; }
+// case but kt = 4 with kr = 2; kr = 4 only with kt <= 2), else one; and the
+// waves per workgroup (four for kr = 4, whose weight slabs fill the slots).
+constexpr int w16_wide_tiles_per_wave(int kr, int kt) { return kr == 4 ? kt : kt == 1 || (kt == 4 && kr == 2) ? 1 : kt; }
+constexpr int w16_wide_waves(int kr, int kt) { return kr == 4 || w16_wide_tiles_per_wave(kr, kt) > 1 ? 4 : 8; }
 constexpr int kQuantLaunchWaves = 4;    // waves per workgroup of the quantisers
 // Workgroups of the 1x128 activation quantiser's grid.
 int64_t quant_act_workgroups(int64_t M, int64_t K);

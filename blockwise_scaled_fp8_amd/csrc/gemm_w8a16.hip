@@ -312,17 +312,18 @@ __global__ __launch_bounds__(kStreamThreads) void w8a16_blk32_stream_lds_kernel(
 // The W8A16 product with every token of a group per workgroup (see
 // w8a16_wide, w8a16_one_tile and blk32_wide for where it is used), for
 // blk128 weights and for block-32 UE8M0 weights (kBlk32): a workgroup owns
-// 16 kR weight rows (kR = 1 or 2) and 16 kT tokens (kT = 1, 2 or 4 token
-// tiles; grid.y walks further groups of 16 kT tokens) over all of K, so
-// nothing is split across workgroups.
+// 16 kR weight rows (kR = 1 or 2, and 4 for blk128 with kT <= 2) and 16 kT
+// tokens (kT = 1, 2 or 4 token tiles; grid.y walks further groups of 16 kT
+// tokens) over all of K, so nothing is split across workgroups.
 //
 // A wave takes kTw of the kT token tiles (tiles kTw tg .. kTw tg + kTw - 1)
 // and the 128-K blocks kw, kw + KW, ...: with G = kT / kTw token groups
 // and kW waves, wave w has tg = w % G, kw = w / G, and KW = kW / G.  Where
 // the LDS allows, every wave takes every token tile (kTw = kT, four waves;
 // w16_wide_tiles_per_wave), so each block's weight rows are loaded and
-// widened once per workgroup; one token tile, and four tiles of two
-// weight-row tiles, run eight waves of one tile each.
+// widened once per workgroup; one token tile and four tiles of two
+// weight-row tiles run eight waves of one tile each, except that four
+// weight-row tiles (8 KB of slabs a slot) always run four waves.
 //
 // Each wave owns a ring of LDS slots (two or three); a slot holds one
 // block: the kR 16-row weight slabs (E4M3, 2 KB each), the wave's 16 kTw
@@ -370,6 +371,7 @@ __global__ __launch_bounds__(w16_wide_waves(kR, kT) * kWave, 1) void w8a16_wide_
     static_assert(kT == 1 || kT == 2 || kT == 4, "token tiles");
     static_assert(kT % kTw == 0 && kW % G == 0, "wave layout");
     static_assert(!kBlk32 || !kXBf16, "block-32 takes fp16 activations");
+    static_assert(kR == 1 || kR == 2 || (kR == 4 && !kBlk32 && kT <= 2), "row tiles: one UE8M0 band, LDS slots");
     __shared__ __attribute__((aligned(1024))) uint8_t ring[kW * kW16WideSlots * kW16Slot];
     const int64_t nt = blockIdx.x, mg = blockIdx.y;
     const int KB = (int)(K / 128);
@@ -518,15 +520,17 @@ __global__ __launch_bounds__(w16_wide_waves(kR, kT) * kWave, 1) void w8a16_wide_
 #define BFP8_LAUNCH_W16(S, B, T, R)                                                                       \
     hipLaunchKernelGGL((w8a16_wide_kernel<S, B, T, R>), grid, dim3(w16_wide_waves(R, T) * kWave), 0, stream, xh, \
                        wq, scales, y, y_dtype, M, N, K)
-#define BFP8_LAUNCH_W16_KR(S, B, T)          \
-    if (w.kr == 1) BFP8_LAUNCH_W16(S, B, T, 1); \
-    else BFP8_LAUNCH_W16(S, B, T, 2);
+// kr = 4 (blk128, kt <= 2 only) is instantiated only where it can run.
+#define BFP8_LAUNCH_W16_KR(S, B, T)                                                     \
+    if (w.kr == 1) BFP8_LAUNCH_W16(S, B, T, 1);                                         \
+    else if (w.kr == 2 || (S) || (T) == 4) BFP8_LAUNCH_W16(S, B, T, 2);                 \
+    else BFP8_LAUNCH_W16(S, B, T, ((S) || (T) == 4 ? 2 : 4));
 
 hipError_t launch_w8a16_wide(const void* x, bool x_bf16, const uint8_t* wq, const float* ws, void* y, int y_dtype,
                              int64_t M, int64_t N, int64_t K, hipStream_t stream) {
     if (M < 1 || N % 16 != 0 || K > kTileMaxK) return hipErrorInvalidValue;
     const WideShape w = w16_wide_shape(M, N);
-    if (w.groups_m > 65535) return hipErrorInvalidValue;
+    if (w.groups_m > 65535 || (w.kr == 4 && w.kt > 2)) return hipErrorInvalidValue;
     const dim3 grid(w.groups_n, w.groups_m);
     const uint16_t* xh = static_cast<const uint16_t*>(x);
     const void* scales = ws;
@@ -545,8 +549,8 @@ hipError_t launch_w8a16_wide(const void* x, bool x_bf16, const uint8_t* wq, cons
 hipError_t launch_w8a16_blk32_wide(const void* x, const uint8_t* wq, const uint8_t* e8m0, void* y, int y_dtype,
                                    int64_t M, int64_t N, int64_t K, hipStream_t stream) {
     if (M < 1 || N % 32 != 0 || K % 128 != 0 || K > kTileMaxK) return hipErrorInvalidValue;
-    const WideShape w = w16_wide_shape(M, N);
-    if (w.groups_m > 65535) return hipErrorInvalidValue;
+    const WideShape w = blk32_wide_shape(M, N);
+    if (w.groups_m > 65535 || w.kr > 2) return hipErrorInvalidValue;
     const dim3 grid(w.groups_n, w.groups_m);
     const uint16_t* xh = static_cast<const uint16_t*>(x);
     const void* scales = e8m0;

@@ -122,7 +122,9 @@ W8A16_BY_M = [(1, 512, 1024, "w8a16_gemv")] + \
 # M, K of one block and long K.
 W8A16_ONE_TILE = [
     (16, 4096, 4096, "w8a16_wide:16x16w8"), (9, 1024, 4096, "w8a16_wide:16x16w8"),
-    (13, 12288, 512, "w8a16_wide:32x16w8"), (16, 16, 4096, "w8a16_wide:32x16w8"), (11, 64, 128, "w8a16_wide:16x16w8"),
+    (13, 12288, 512, "w8a16_wide:64x16w4"), (16, 16, 4096, "w8a16_wide:16x16w8"), (11, 64, 128, "w8a16_wide:16x16w8"),
+    (16, 8176, 512, "w8a16_wide:32x16w8"),                # last 32-row weight tile holds 16 rows
+    (12, 8208, 256, "w8a16_wide:64x16w4"),                # last 64-row weight tile holds 16 rows
     (16, 4096, 7168, "w8a16_wide:16x16w8"),
 ]
 # One token, K <= 12288: 4, 8 or 12 chunks, one row per wave.
@@ -132,9 +134,11 @@ W8A16_ONE_TOKEN = [(1, N, K, "w8a16_gemv") for N, K in
 W8A16_ALL_TOKENS = [
     (17, 1024, 4096, "w8a16_wide:16x32w4"), (32, 4096, 4096, "w8a16_wide:16x32w4"),
     (50, 1024, 4096, "w8a16_wide:16x32w4"), (64, 4096, 4096, "w8a16_wide:32x32w4"),
-    (24, 12288, 512, "w8a16_wide:32x32w4"), (20, 16, 4096, "w8a16_wide:32x32w4"), (20, 64, 128, "w8a16_wide:16x32w4"),
-    (128, 4096, 4096, "w8a16_wide:32x64w8"), (100, 4112, 1024, "w8a16_wide:32x64w8"),
-    (256, 1024, 4096, "w8a16_wide:32x32w4"), (200, 1040, 1024, "w8a16_wide:16x64w4"),
+    (24, 12288, 512, "w8a16_wide:64x32w4"), (20, 16, 4096, "w8a16_wide:16x32w4"), (20, 64, 128, "w8a16_wide:16x32w4"),
+    (128, 4096, 4096, "w8a16_wide:64x32w4"), (90, 4112, 1024, "w8a16_wide:64x32w4"),   # ragged M and N
+    (256, 1024, 4096, "w8a16_wide:32x32w4"), (144, 1040, 1024, "w8a16_wide:16x64w4"),
+    (32, 8176, 512, "w8a16_wide:32x32w4"),                # last 32-row weight tile holds 16 rows
+    (512, 1024, 4096, "w8a16_wide:64x32w4"), (200, 1040, 1024, "w8a16_wide:32x32w4"),
     (40, 1024, 8192, "w8a16_wide:16x32w4"), (48, 4096, 7168, "w8a16_wide:32x32w4"),
 ]
 W8A16_LONG_K = [(1, 4096, 12416, "w8a16_stream"), (3, 4096, 12288, "w8a16_stream"),
@@ -146,7 +150,7 @@ W8A16_ONE_HOT = [(1, 256, 256, "w8a16_gemv"), (4, 256, 256, "w8a16_stream"), (16
                  (40, 256, 256, "w8a16_wide:16x32w4")]
 W8A16_TILE_SPLIT = [(40, 1024, 12288, "w8a16_tile:128x64w8/split"), (100, 1040, 8192, "w8a16_tile:128x128w8/split"),
                     (300, 2048, 2176, "w8a16_tile:128x128w8/split"), (40, 16384, 512, "w8a16_tile:128x64w8")]
-W8A16_TILE_ONE_HOT = (300, 256, 256, "w8a16_tile:128x128w8")
+W8A16_TILE_ONE_HOT = (8200, 256, 256, "w8a16_tile:128x128w8")
 W8A16_TILE_LARGE_RAGGED = (2000, 4112, 1024, "w8a16_tile:256x128w8")
 W8A16_TILE_LARGE_ONE_HOT = (2048, 4096, 256, "w8a16_tile:256x128w8")
 W8A16_PREFILL_OPROJ = (4096, 4096, 4096, "w8a16_tile:256x128w8")

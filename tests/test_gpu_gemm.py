@@ -372,7 +372,8 @@ def test_w8a16_tile_split_k(gpu_lib, M, N, K, kernel, xdtype):
 
 @pytest.mark.parametrize("xdtype", [torch.bfloat16, torch.float16])
 def test_w8a16_tile_one_hot_all_codes_exact(gpu_lib, xdtype):
-    """Tiled path (M = 300): x one-hot 1.0 gives E4M3(wq[n, k]) * ws exactly."""
+    """Tiled path (M = 8200: no one-round all-token shape at N = 256): x
+    one-hot 1.0 gives E4M3(wq[n, k]) * ws exactly."""
     M, N, K, kernel = cases.W8A16_TILE_ONE_HOT
     expect(W8A16, M, N, K, kernel)
     wq = np.zeros((N, K), np.uint8)
