@@ -76,8 +76,12 @@ struct WidePick {
     }
 };
 
-// W8A8: (kr, kt) in {1, 2, 4} x {2, 4} (kt = 4 only when M needs at least
-// four token tiles), chosen by WidePick.  Measured (us, 32 rotated weight
+// W8A8: (kr, kt) with kr in {1, 2, 4}, kt = 1 for M <= 16 (one token tile:
+// two would double the token loads and MFMAs for nothing; 1024 x 12288 M = 8
+// 9.0 against 10.5 us, 2048 x 12288 M = 5 9.2 against 10.9, 12288 x 4096
+// M = 16 11.5 against 12.0, 8192 x 4096 M = 16 8.7 against 9.1) and
+// kt in {2, 4} above (kt = 4 only when M needs at least four token tiles),
+// chosen by WidePick.  Measured (us, 32 rotated weight
 // copies, K = 4096; the pick first): 4096 x 4096 M = 64 (2, 2) 8.4 against
 // 10.7 for (4, 2), M = 96 (2, 4) 10.1 against 10.7 for (4, 2), M = 128
 // (4, 2) 10.7 against 11.2 for (2, 4) and 14.2 for (4, 4), M = 160 / 192 /
@@ -91,6 +95,10 @@ struct WidePick {
 inline WideShape w8a8_wide_shape(int64_t M, int64_t N) {
     const int64_t m_tiles = (M + 15) / 16;
     WidePick pick;
+    if (M <= 16) {
+        for (int kr = 4; kr >= 1; kr /= 2) pick.consider(kr, 1, M, N);
+        return pick.best;
+    }
     for (int kt = 2; kt <= 4; kt += 2) {
         if (kt > 2 && kt > m_tiles) continue;
         for (int kr = 4; kr >= 1; kr /= 2) pick.consider(kr, kt, M, N);

@@ -373,10 +373,11 @@ __global__ __launch_bounds__(kStreamThreads) void w8a8_stream_quant_kernel(
 // ------------------------------------------------------------ wide stream ----
 // All-token kernel (see w8a8_wide for where it is used): a workgroup owns
 // 16 kR weight rows (kR = 1, 2 or 4 MFMA row tiles) and 16 kT tokens
-// (kT = 2 or 4 token tiles; grid.y covers the tokens beyond) over all of K,
+// (kT = 1 for M <= 16, else 2 or 4 token tiles; grid.y covers the tokens
+// beyond) over all of K,
 // so no split-K hand-off is needed.  Every wave takes all kR x kT output
 // tiles and the 128-K blocks w, w + W, ... (W waves: eight for kR <= 2 with
-// kT = 2, four where the slots are larger, kR = 4 or kT = 4), so each
+// kT <= 2, four where the slots are larger, kR = 4 or kT = 4), so each
 // block's weight rows are loaded once per workgroup.  Each wave owns
 // a ring of LDS slots (two or three); a slot holds one block: the
 // workgroup's 16 kR weight rows, the 16 kT token rows, their token scales
@@ -425,7 +426,7 @@ __global__ __launch_bounds__((wide_waves<kR, kT>()) * kWave, 1) void w8a8_wide_k
     using SL = WideSlot<kR, kT>;
     constexpr int W = SL::kWaves;
     constexpr int kWideSlots = SL::kSlots, kWideSlot = SL::kBytes;
-    static_assert(kT == 2 || kT == 4, "token tiles");
+    static_assert(kT == 1 || kT == 2 || kT == 4, "token tiles");
     static_assert(kR == 1 || kR == 2 || kR == 4, "weight-row tiles within one 128-row scale block");
     __shared__ __attribute__((aligned(1024))) uint8_t ring[W * kWideSlots * kWideSlot];
     static_assert(W * kR * kT * kWave * 16 <= W * kWideSlots * kWideSlot, "partial tiles fit the ring");
@@ -557,7 +558,11 @@ hipError_t launch_w8a8_wide(const uint8_t* xq, const float* xs, const uint8_t* w
 #define BFP8_LAUNCH_WIDE(R, T)                                                                                   \
     hipLaunchKernelGGL((w8a8_wide_kernel<R, T>), grid, dim3(wide_waves<R, T>() * kWave), 0, stream, xq, xs, wq, ws, \
                        y, y_dtype, M, N, K)
-    if (w.kr == 4) {
+    if (w.kt == 1) {
+        if (w.kr == 4) BFP8_LAUNCH_WIDE(4, 1);
+        else if (w.kr == 2) BFP8_LAUNCH_WIDE(2, 1);
+        else BFP8_LAUNCH_WIDE(1, 1);
+    } else if (w.kr == 4) {
         if (w.kt == 2) BFP8_LAUNCH_WIDE(4, 2);
         else BFP8_LAUNCH_WIDE(4, 4);
     } else if (w.kr == 1) {

@@ -61,8 +61,8 @@ W8A8_SPLIT_K_STREAM = [(M, 512, 12288, "w8a8_stream/split") for M in (1, 4, 16)]
 # Paths that need no workspace for M <= 512 (all-token kernel, or the
 # streaming kernel over 16-token tiles on small projections).
 W8A8_NO_WORKSPACE = [
-    (1, 1024, 12288, "w8a8_wide:16x32w8"), (5, 2048, 12288, "w8a8_wide:16x32w8"),
-    (16, 1024, 12288, "w8a8_wide:16x32w8"), (17, 1024, 4096, "w8a8_stream"), (24, 1024, 4096, "w8a8_stream"),
+    (1, 1024, 12288, "w8a8_wide:16x16w8"), (5, 2048, 12288, "w8a8_wide:16x16w8"),
+    (16, 1024, 12288, "w8a8_wide:16x16w8"), (17, 1024, 4096, "w8a8_stream"), (24, 1024, 4096, "w8a8_stream"),
     (32, 4096, 4096, "w8a8_wide:16x32w8"), (33, 4096, 4096, "w8a8_wide:32x32w8"), (50, 1024, 4096, "w8a8_stream"),
     (64, 4096, 4096, "w8a8_wide:32x32w8"), (32, 12288, 256, "w8a8_wide:64x32w4"), (20, 16, 8192, "w8a8_stream"),
     (20, 8208, 256, "w8a8_wide:64x32w4"),                 # last 64-row weight tile holds 16 rows
@@ -76,8 +76,8 @@ W8A8_NO_WORKSPACE = [
     (260, 2064, 1024, "w8a8_wide:64x64w4"),               # ragged M and N (16 rows in the last weight tile)
     (256, 4096, 4096, "w8a8_wide:64x64w4"),
     # 4 < M <= 16 where streaming would take several rounds of 16-row tiles
-    (8, 12288, 1024, "w8a8_wide:64x32w4"), (16, 6160, 2048, "w8a8_wide:32x32w8"),   # ragged N
-    (5, 8192, 512, "w8a8_wide:32x32w8"), (12, 16400, 256, "w8a8_stream"),          # no one-round shape
+    (8, 12288, 1024, "w8a8_wide:64x16w4"), (16, 6160, 2048, "w8a8_wide:32x16w8"),   # ragged N
+    (5, 8192, 512, "w8a8_wide:32x16w8"), (12, 16400, 256, "w8a8_stream"),          # no one-round shape
 ]
 
 # Every tiled configuration, ragged M and N tiles, split K.
@@ -109,7 +109,7 @@ QUANT_W8A8 = [
     (5, 1024, 4096, "w8a8_stream_quant"), (8, 512, 1024, "w8a8_stream_quant"), (9, 512, 640, "quant+w8a8_stream"),
     (16, 1024, 4096, "quant+w8a8_stream"), (17, 384, 640, "quant+w8a8_stream"), (64, 1024, 4096, "quant+w8a8_stream"),
     (300, 1040, 1024, "quant+w8a8_wide:64x32w4"), (200, 2048, 4224, "quant+w8a8_tile:64x128w8/split"),
-    (6, 8192, 1024, "quant+w8a8_wide:32x32w8"), (16, 12288, 512, "quant+w8a8_wide:64x32w4"),
+    (6, 8192, 1024, "quant+w8a8_wide:32x16w8"), (16, 12288, 512, "quant+w8a8_wide:64x16w4"),
 ]
 
 # ---------------------------------------------------------------- W8A16 ----

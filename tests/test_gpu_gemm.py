@@ -94,8 +94,9 @@ def test_w8a8_split_k_narrow_projection(gpu_lib, M, N, K, kernel):
 @pytest.mark.parametrize("M,N,K,kernel", cases.W8A8_NO_WORKSPACE)
 def test_w8a8_wide_all_tokens(gpu_lib, M, N, K, kernel):
     """The paths that need no workspace for M <= 512: the kernel that holds
-    every token of a group per 16-, 32- or 64-row weight tile (M <= 16 where
-    streaming would split K or take several rounds, 16 < M <= 32, and K <=
+    every token of a group per 16-, 32- or 64-row weight tile (one 16-token
+    tile for M <= 16 where streaming would split K or take several rounds;
+    groups of 32 or 64 tokens for 16 < M <= 32, and K <=
     4096 where its launch fits one round) and the streaming kernel over
     16-token tiles on small projections (grid.z, e.g. N = 1024 or 16 at
     M <= 64); ragged M inside the last token tile and in a further token
