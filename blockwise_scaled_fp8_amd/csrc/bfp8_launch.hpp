@@ -170,12 +170,16 @@ inline WideShape blk32_wide_shape(int64_t M, int64_t N) {
     return best;
 }
 
+// Largest M for which the W8A8 streaming kernel quantises its 16-bit
+// activations itself; above it the fused call runs the quantiser first.
+constexpr int64_t kFusedQuantMaxM = 8;
 // W8A8 dispatch (codes in), from the projection sweep:
 //  * the streaming kernel for M <= 16 when it needs no split of K, or when
 //    N < 1024, except for 4 < M <= 16 with K <= 4096 where its launch takes
 //    more than one round (over 256 weight-row tiles) and the all-token
-//    kernel's fits one; and for M <= 64 when its workgroups fit one round
-//    unsplit;
+//    kernel's fits one, and for 8 < M <= 16 where it leaves CUs idle
+//    (fewer than 256 weight-row tiles); and for M <= 64 when its workgroups
+//    fit one round unsplit;
 //  * the all-token kernel (launch_w8a8_wide: every token of a 32- or
 //    64-token group per workgroup, no split) for the other M <= 32, and
 //    when K <= 4096 and either M * N <= 2^19 or N >= 512 and its launch
@@ -213,7 +217,20 @@ inline bool w8a8_streams(int64_t M, int64_t N, int64_t K) {
         // streaming launch fits one round (4096 x 4096 M = 8 / 16: 5.7 / 6.1
         // against 6.2 / 6.4), nor at K = 8192 (8192 x 8192 M = 8 / 16: 15.1 /
         // 17.0 against 18.1 / 18.3).
-        return !(M > 4 && K <= 4096 && p.n_tiles * p.m_tiles > 256 && w8a8_wide_one_round(M, N));
+        const int64_t wg = p.n_tiles * p.m_tiles;
+        if (M > 4 && K <= 4096 && wg > 256 && w8a8_wide_one_round(M, N)) return false;
+        // Fewer streaming workgroups than CUs (N < 4096): the all-token
+        // kernel with one token tile, as many workgroups but eight waves each
+        // keeping three blocks in flight, is ahead at every M and K measured
+        // (us, streaming against all-token): 1024 x 4096 M = 2 / 4 / 16 3.99 /
+        // 4.07 / 4.64 against 3.69 / 3.72 / 3.98, 2048 x 4096 M = 2 / 16
+        // 4.68 / 5.56 against 4.29 / 4.82, 3072 x 4096 M = 8 / 16 5.32 / 5.89
+        // against 5.33 / 5.61, 1024 x 8192 M = 8 6.86 against 5.69, 2048 x
+        // 7168 M = 16 8.35 against 7.48, 2048 x 2048 M = 16 3.82 against 3.23.
+        // Taken only above kFusedQuantMaxM tokens: up to there the fused
+        // quantise + W8A8 call quantises inside the streaming kernel, and it
+        // must run the codes call's kernel to give the same bits.
+        return !(M > kFusedQuantMaxM && wg < 256);
     }
     // More than one token tile (one workgroup per weight-row tile and token
     // tile, the weights read once per token tile): on small projections,
@@ -252,9 +269,6 @@ hipError_t launch_w8a8_wide(const uint8_t* xq, const float* xs, const uint8_t* w
 hipError_t launch_w8a8_stream(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
                               void* y, int y_dtype, int64_t M, int64_t N, int64_t K,
                               void* workspace, hipStream_t stream);
-// Largest M for which the W8A8 streaming kernel quantises its 16-bit
-// activations itself; above it the fused call runs the quantiser first.
-constexpr int64_t kFusedQuantMaxM = 8;
 // Streaming W8A8 that quantises its 16-bit activations itself (M <= kFusedQuantMaxM).
 hipError_t launch_w8a8_stream_quant(const void* x, bool x_bf16, const uint8_t* wq, const float* ws,
                                     void* y, int y_dtype, int64_t M, int64_t N, int64_t K,
@@ -289,7 +303,8 @@ inline bool blk32_one_round(int64_t M, int64_t N) {
     return (int64_t)w.groups_n * w.groups_m <= 256;
 }
 // W8A16 blk128 dispatch: the streaming kernel for M <= 16 except where
-// w8a16_one_tile holds; the all-token kernel (launch_w8a16_wide) there, for
+// w8a16_one_tile holds or, at 4 <= M <= 8, the streaming launch would take
+// several rounds; the all-token kernel (launch_w8a16_wide) there, for
 // M > 16 when K <= 4096 and either M <= 32 or its launch fits one round
 // (w16_wide_shape), and for 16 < M <= 64 when 4096 < K <= 8192 and its
 // launch fits one round; the tiled kernel otherwise.  Measured, us
@@ -306,7 +321,17 @@ inline bool blk32_one_round(int64_t M, int64_t N) {
 // rounds, left tiled) 22.9 against 25.9.
 inline bool w8a16_wide(int64_t M, int64_t N, int64_t K) {
     if (w8a16_one_tile(M, N, K)) return true;
-    if (M <= kStreamMaxM) return false;
+    if (M <= kStreamMaxM) {
+        // 4 <= M <= 8 where the streaming launch takes several rounds and a
+        // one-round all-token shape exists (us, streaming against all-token
+        // with one token tile): 12288 x 4096 M = 4 / 8 13.4 / 14.2 against
+        // 12.1 / 12.0.  Not where the streaming launch fits one round or
+        // fewer (4096 x 4096 M = 4 5.57 against 6.21; 1024 x 4096 M = 2 / 4 /
+        // 8 3.68 / 3.80 / 4.10 against 4.27 / 4.29 / 4.41).
+        if (M < 4 || K > 4096) return false;
+        const StreamPlan p = plan_stream(M, N, K);
+        return p.splits == 1 && p.n_tiles * p.m_tiles > 256 && w16_one_round(M, N);
+    }
     if (K <= 4096) return M <= 2 * kStreamMaxM || w16_one_round(M, N);
     return K <= 8192 && M <= 4 * kStreamMaxM && w16_one_round(M, N);
 }

@@ -78,6 +78,8 @@ W8A8_NO_WORKSPACE = [
     # 4 < M <= 16 where streaming would take several rounds of 16-row tiles
     (8, 12288, 1024, "w8a8_wide:64x16w4"), (16, 6160, 2048, "w8a8_wide:32x16w8"),   # ragged N
     (5, 8192, 512, "w8a8_wide:32x16w8"), (12, 16400, 256, "w8a8_stream"),          # no one-round shape
+    # 8 < M <= 16 where streaming would leave CUs idle (fewer than 256 weight-row tiles)
+    (12, 2064, 1024, "w8a8_wide:16x16w8"), (9, 1024, 6144, "w8a8_wide:16x16w8"), (8, 2048, 4096, "w8a8_stream"),
 ]
 
 # Every tiled configuration, ragged M and N tiles, split K.
@@ -107,7 +109,7 @@ QUANT_W8A8 = [
     (1, 512, 8320, "w8a8_stream_quant/split"), (2, 1024, 4096, "w8a8_stream_quant"),
     (3, 512, 640, "w8a8_stream_quant"), (4, 384, 12288, "w8a8_stream_quant/split"),
     (5, 1024, 4096, "w8a8_stream_quant"), (8, 512, 1024, "w8a8_stream_quant"), (9, 512, 640, "quant+w8a8_stream"),
-    (16, 1024, 4096, "quant+w8a8_stream"), (17, 384, 640, "quant+w8a8_stream"), (64, 1024, 4096, "quant+w8a8_stream"),
+    (16, 1024, 4096, "quant+w8a8_wide:16x16w8"), (17, 384, 640, "quant+w8a8_stream"), (64, 1024, 4096, "quant+w8a8_stream"),
     (300, 1040, 1024, "quant+w8a8_wide:64x32w4"), (200, 2048, 4224, "quant+w8a8_tile:64x128w8/split"),
     (6, 8192, 1024, "quant+w8a8_wide:32x16w8"), (16, 12288, 512, "quant+w8a8_wide:64x16w4"),
 ]
@@ -125,6 +127,8 @@ W8A16_ONE_TILE = [
     (13, 12288, 512, "w8a16_wide:64x16w4"), (16, 16, 4096, "w8a16_wide:16x16w8"), (11, 64, 128, "w8a16_wide:16x16w8"),
     (16, 8176, 512, "w8a16_wide:32x16w8"),                # last 32-row weight tile holds 16 rows
     (12, 8208, 256, "w8a16_wide:64x16w4"),                # last 64-row weight tile holds 16 rows
+    # 4 <= M <= 8 where streaming would take several rounds
+    (4, 12288, 512, "w8a16_wide:64x16w4"), (8, 8208, 1024, "w8a16_wide:64x16w4"), (3, 12288, 512, "w8a16_stream"),
     (16, 4096, 7168, "w8a16_wide:16x16w8"),
 ]
 # One token, K <= 12288: 4, 8 or 12 chunks, one row per wave.

@@ -272,10 +272,11 @@ def test_w8a16_gemv_one_token(gpu_lib, M, N, K, kernel, xdtype):
 @pytest.mark.parametrize("xdtype", [torch.bfloat16, torch.float16])
 @pytest.mark.parametrize("M,N,K,kernel", cases.W8A16_ONE_TILE)
 def test_w8a16_one_token_tile(gpu_lib, M, N, K, kernel, xdtype):
-    """8 < M <= 16 without a split of K: the all-token kernel with a single
-    16-token tile (token rows of a ragged M past the end load as zeros), one
-    or two weight-row tiles per workgroup (a half-filled pair at N = 16),
-    K of one block and long K; no workspace."""
+    """8 < M <= 16 without a split of K, and 4 <= M <= 8 where streaming
+    would take several rounds: the all-token kernel with a single 16-token
+    tile (token rows of a ragged M past the end load as zeros), one, two or
+    four weight-row tiles per workgroup (a last tile with 16 live rows), K of
+    one block and long K; no workspace."""
     assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A16_BLK128, M, N, K) == 0
     say("w8a16 one tile", xdtype, f"M={M} N={N} K={K}")
     expect(W8A16, M, N, K, kernel)

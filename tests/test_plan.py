@@ -75,11 +75,16 @@ def test_routing_rules_read_off_the_plan():
             assert ("gemv" in name) == one, (op, M, N, K, name)
         if op in (cases.W8A16, cases.BLK32) and M <= 16 and not one:
             # 8 < M <= 16: one token tile on the all-token kernel unless the
-            # streaming plan splits K; M <= 8 streams.
+            # streaming plan splits K; M <= 8 streams, except W8A16 at
+            # 4 <= M <= 8 with K <= 4096 where streaming would take several
+            # rounds (over 256 16-row tiles) and the all-token launch fits one.
             p = bfp8.bfp8_get_plan(op, M, N, K)
             stream = "w8a16_stream" if op == cases.W8A16 else "blk32_stream_lds"
             wide = "w8a16_wide" if op == cases.W8A16 else "blk32_wide"
-            if M <= 8:
+            if M <= 8 and name == wide:
+                assert op == cases.W8A16 and M >= 4 and K <= 4096 and N > 16 * 256, (op, M, N, K, p)
+                assert p["tile_m"] == 16 and p["workgroups"] <= 256 and p["workspace_bytes"] == 0, (op, M, N, K, p)
+            elif M <= 8:
                 assert name == stream, (op, M, N, K, name)
             elif name == wide:
                 assert p["tile_m"] == 16 and p["workspace_bytes"] == 0, (op, M, N, K, p)
