@@ -138,6 +138,8 @@ size_t kernel_workspace(int kernel, int64_t M, int64_t N, int64_t K) {
             return stream_workspace_bytes(plan_stream(M, N, K));
         case BFP8_KERNEL_W8A8_TILE:
             return K <= kTileMaxK ? tile_workspace_bytes(M, N, K) : 0;
+        case BFP8_KERNEL_W8A8_WIDE:
+            return w8a8_wide_workspace_bytes(w8a8_wide_shape(M, N, K));
         case BFP8_KERNEL_W8A16_TILE:
         case BFP8_KERNEL_BLK32_TILE:
             return K <= kTileMaxK ? tile16_workspace_bytes(M, N, K) : 0;
@@ -157,7 +159,7 @@ hipError_t launch_w8a8(const uint8_t* xq, const float* xs, const uint8_t* wq, co
         case BFP8_KERNEL_W8A8_GEMV: return launch_w8a8_gemv(xq, xs, wq, ws, y, y_dtype, N, K, stream);
         case BFP8_KERNEL_W8A8_STREAM:
             return launch_w8a8_stream(xq, xs, wq, ws, y, y_dtype, M, N, K, workspace, stream);
-        case BFP8_KERNEL_W8A8_WIDE: return launch_w8a8_wide(xq, xs, wq, ws, y, y_dtype, M, N, K, stream);
+        case BFP8_KERNEL_W8A8_WIDE: return launch_w8a8_wide(xq, xs, wq, ws, y, y_dtype, M, N, K, workspace, stream);
         default: return launch_w8a8_tile(xq, xs, wq, ws, y, y_dtype, M, N, K, workspace, stream);
     }
 }
@@ -264,6 +266,8 @@ size_t w8a8_counter_bytes(int64_t M, int64_t N, int64_t K) {
         }
         case BFP8_KERNEL_W8A8_TILE:
             return tile_counter_bytes(M, N, K);
+        case BFP8_KERNEL_W8A8_WIDE:
+            return w8a8_wide_counter_bytes(w8a8_wide_shape(M, N, K));
         default:
             return 0;
     }
@@ -489,13 +493,14 @@ bfp8_status bfp8_get_plan(int op, int64_t M, int64_t N, int64_t K, bfp8_plan* pl
         case BFP8_KERNEL_W8A8_WIDE:
         case BFP8_KERNEL_W8A16_WIDE:
         case BFP8_KERNEL_BLK32_WIDE: {
-            const WideShape w = p.kernel == BFP8_KERNEL_W8A8_WIDE   ? w8a8_wide_shape(M, N)
+            const WideShape w = p.kernel == BFP8_KERNEL_W8A8_WIDE   ? w8a8_wide_shape(M, N, K)
                                 : p.kernel == BFP8_KERNEL_BLK32_WIDE ? blk32_wide_shape(M, N)
                                                                      : w16_wide_shape(M, N);
             p.tile_n = 16 * w.kr;
             p.tile_m = 16 * w.kt;
             p.waves = p.kernel == BFP8_KERNEL_W8A8_WIDE ? w8a8_wide_waves(w.kr, w.kt) : w16_wide_waves(w.kr, w.kt);
-            p.workgroups = (int64_t)w.groups_n * w.groups_m;
+            p.splits = w.splits;
+            p.workgroups = (int64_t)w.groups_n * w.groups_m * w.splits;
             break;
         }
         case BFP8_KERNEL_W8A8_TILE:

@@ -47,6 +47,7 @@ StreamPlan plan_stream(int64_t M, int64_t N, int64_t K);
 struct WideShape {
     int kr, kt;
     unsigned groups_n, groups_m;
+    int splits = 1;   // K parts over grid.z (W8A8 at long K), partial tiles handed off
 };
 
 // One-round choice of the W8A8 and W8A16 blk128 all-token shapes: when some
@@ -92,22 +93,71 @@ struct WidePick {
 // M = 512 (4, 4) 12.7; 12288 x 4096 M = 32 (4, 2) 13.8 against 16.4 for
 // (2, 2), M = 64 (4, 4) 17.1 against 21.9 for (2, 2); 16384 x 4096 M = 32
 // (4, 2) 16.7 against 18.1.
-inline WideShape w8a8_wide_shape(int64_t M, int64_t N) {
+//
+// At K >= 12288, where the unsplit pick leaves three quarters of the CUs
+// idle (at most 64 workgroups), the K blocks may also be split over two or
+// four workgroups (grid.z; at least 24 blocks each), the last one of a tile
+// summing the parts in split order: among the one-round configurations with
+// more workgroups than the unsplit pick, the one with the most, then the
+// largest tile (kr kt), then the larger kr.  Measured (us): 1024 x 12288
+// M = 8 / 16 (1, 1) split 4 7.5 / 7.7 against 9.0 / 10.8 unsplit (64
+// workgroups); with 128 unsplit workgroups no gain (2048 x 12288 M = 5
+// (2, 1) split 4 9.36 against 9.2).  Where the unsplit pick already fills the CUs a
+// split buys only a larger tile, and the hand-off of partial tiles cost
+// what the larger tile saved (4096 x 12288, split against unsplit or
+// tiled: M = 16 (4, 1) split 4 13.5 against 13.2 streamed, M = 32 (4, 2)
+// split 4 16.3 against 16.8 for (1, 2), M = 64 (4, 4) split 4 21.2
+// against 18.2 tiled, M = 128 (4, 4) split 2 25.0 against 25.0 tiled).
+inline WideShape w8a8_wide_shape(int64_t M, int64_t N, int64_t K) {
     const int64_t m_tiles = (M + 15) / 16;
     WidePick pick;
-    if (M <= 16) {
-        for (int kr = 4; kr >= 1; kr /= 2) pick.consider(kr, 1, M, N);
-        return pick.best;
-    }
-    for (int kt = 2; kt <= 4; kt += 2) {
+    const int kt_lo = M <= 16 ? 1 : 2, kt_hi = M <= 16 ? 1 : 4;
+    for (int kt = kt_lo; kt <= kt_hi; kt *= 2) {
         if (kt > 2 && kt > m_tiles) continue;
         for (int kr = 4; kr >= 1; kr /= 2) pick.consider(kr, kt, M, N);
     }
-    return pick.best;
+    WideShape best = pick.best;
+    const int64_t unsplit_wg = (int64_t)best.groups_n * best.groups_m;
+    int64_t best_wg = unsplit_wg;
+    const int64_t KB = K / 128;
+    if (KB < 96 || unsplit_wg > 64) return best;
+    for (int kt = kt_lo; kt <= kt_hi; kt *= 2) {
+        if (kt > 2 && kt > m_tiles) continue;
+        for (int kr = 4; kr >= 1; kr /= 2) {
+            if (kr > 1 && N <= 8 * kr) continue;
+            for (int sp = 2; sp <= 4; sp *= 2) {
+                if (KB / sp < 24) continue;
+                const int64_t gn = (N + 16 * kr - 1) / (16 * kr), gm = (M + 16 * kt - 1) / (16 * kt);
+                const int64_t wg = gn * gm * sp;
+                if (wg > 256 || wg <= unsplit_wg || gm > 65535) continue;
+                const int area = kr * kt, best_area = best.kr * best.kt;
+                const bool better = wg > best_wg || (best.splits > 1 && wg == best_wg && area > best_area) ||
+                                    (best.splits > 1 && wg == best_wg && area == best_area && kr > best.kr);
+                if (better) {
+                    best = WideShape{kr, kt, (unsigned)gn, (unsigned)gm, sp};
+                    best_wg = wg;
+                }
+            }
+        }
+    }
+    return best;
 }
-inline bool w8a8_wide_one_round(int64_t M, int64_t N) {
-    const WideShape w = w8a8_wide_shape(M, N);
-    return (int64_t)w.groups_n * w.groups_m <= 256;
+inline bool w8a8_wide_one_round(int64_t M, int64_t N, int64_t K) {
+    const WideShape w = w8a8_wide_shape(M, N, K);
+    return (int64_t)w.groups_n * w.groups_m * w.splits <= 256;
+}
+// Workspace of a W8A8 all-token launch: the split tiles' arrival counters
+// (256-byte aligned), then each tile's fp32 partial tiles, split by split
+// (kr kt output tiles of 64 lanes x 4 floats each); nothing when K is not
+// split.
+inline size_t w8a8_wide_counter_bytes(const WideShape& w) {
+    if (w.splits == 1) return 0;
+    return ((size_t)w.groups_n * w.groups_m * 4 + 255) / 256 * 256;
+}
+inline size_t w8a8_wide_workspace_bytes(const WideShape& w) {
+    if (w.splits == 1) return 0;
+    return w8a8_wide_counter_bytes(w) +
+           (size_t)w.groups_n * w.groups_m * w.splits * (size_t)(w.kr * w.kt) * 256 * sizeof(float);
 }
 
 // W8A16 blk128: one 16-token tile (kt = 1) for M <= 16, else kt = 2 or 4
@@ -218,7 +268,7 @@ inline bool w8a8_streams(int64_t M, int64_t N, int64_t K) {
         // against 6.2 / 6.4), nor at K = 8192 (8192 x 8192 M = 8 / 16: 15.1 /
         // 17.0 against 18.1 / 18.3).
         const int64_t wg = p.n_tiles * p.m_tiles;
-        if (M > 4 && K <= 4096 && wg > 256 && w8a8_wide_one_round(M, N)) return false;
+        if (M > 4 && K <= 4096 && wg > 256 && w8a8_wide_one_round(M, N, K)) return false;
         // Fewer streaming workgroups than CUs (N < 4096): the all-token
         // kernel with one token tile, as many workgroups but eight waves each
         // keeping three blocks in flight, is ahead at every M and K measured
@@ -248,7 +298,7 @@ inline bool w8a8_wide(int64_t M, int64_t N, int64_t K) {
     // fetches it (4096 tokens x 256 rows: 21.1 us against 16.8 tiled;
     // 2048 x 512 14.8 against 16.8).
     return M <= 2 * kStreamMaxM ||
-           (K <= 4096 && (M * N <= ((int64_t)1 << 19) || (N >= 512 && w8a8_wide_one_round(M, N))));
+           (K <= 4096 && (M * N <= ((int64_t)1 << 19) || (N >= 512 && w8a8_wide_one_round(M, N, K))));
 }
 // Workspace bytes of a streaming plan: tile counters, then fp32 partial tiles.
 size_t stream_workspace_bytes(const StreamPlan& p);
@@ -265,7 +315,8 @@ hipError_t launch_w8a8_tile(const uint8_t* xq, const float* xs, const uint8_t* w
                             hipStream_t stream);
 // M >= 1, N a multiple of 16, K <= kTileMaxK; needs no workspace.
 hipError_t launch_w8a8_wide(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
-                            void* y, int y_dtype, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+                            void* y, int y_dtype, int64_t M, int64_t N, int64_t K, void* workspace,
+                            hipStream_t stream);
 hipError_t launch_w8a8_stream(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
                               void* y, int y_dtype, int64_t M, int64_t N, int64_t K,
                               void* workspace, hipStream_t stream);

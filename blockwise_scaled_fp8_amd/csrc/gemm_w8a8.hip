@@ -395,7 +395,10 @@ __global__ __launch_bounds__(kStreamThreads) void w8a8_stream_quant_kernel(
 // waves stay ahead of four (M = 24 / 32: 6.84 / 7.37 vs 7.08 / 7.52 us).
 // Four weight-row tiles (a 64 x 64 output tile per wave with kT = 4) serve
 // where they keep the launch to one round, e.g. 4096 x 4096 at M = 256 in
-// 14.0 us against 17.7 for the best tiled plan (w8a8_wide_shape).
+// 14.0 us against 17.7 for the best tiled plan (w8a8_wide_shape).  At long K
+// on small projections the K blocks may be split over gridDim.z workgroups:
+// each writes its partial tiles to the workspace and the last of a tile to
+// arrive sums them in split order (the streaming kernels' hand-off).
 template <int kR, int kT>
 constexpr int wide_waves() { return w8a8_wide_waves(kR, kT); }
 template <int kR, int kT>
@@ -422,14 +425,15 @@ template <int kR, int kT>
 __global__ __launch_bounds__((wide_waves<kR, kT>()) * kWave, 1) void w8a8_wide_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ xs,
     const uint8_t* __restrict__ wq, const float* __restrict__ ws,
-    void* __restrict__ y, int y_dtype, int64_t M, int64_t N, int64_t K) {
+    void* __restrict__ y, int y_dtype, int64_t M, int64_t N, int64_t K, float* __restrict__ partials,
+    uint32_t* __restrict__ counters) {
     using SL = WideSlot<kR, kT>;
     constexpr int W = SL::kWaves;
     constexpr int kWideSlots = SL::kSlots, kWideSlot = SL::kBytes;
     static_assert(kT == 1 || kT == 2 || kT == 4, "token tiles");
     static_assert(kR == 1 || kR == 2 || kR == 4, "weight-row tiles within one 128-row scale block");
     __shared__ __attribute__((aligned(1024))) uint8_t ring[W * kWideSlots * kWideSlot];
-    static_assert(W * kR * kT * kWave * 16 <= W * kWideSlots * kWideSlot, "partial tiles fit the ring");
+    static_assert(W * kR * kT * kWave * 16 + 16 <= W * kWideSlots * kWideSlot, "partial tiles and arrival word fit");
     const int64_t nt = blockIdx.x;            // 16 kR weight rows
     const int64_t mg = blockIdx.y;            // 16 kT tokens
     const int KB = (int)(K / 128);
@@ -464,10 +468,14 @@ __global__ __launch_bounds__((wide_waves<kR, kT>()) * kWave, 1) void w8a8_wide_k
         if (lane == 0) dma4(base + SL::kOffWs, rsrc_ws, 0, __builtin_amdgcn_readfirstlane(kb * 4));
     };
 
-    const int nj = wave < KB ? (KB - 1 - wave) / W + 1 : 0;   // blocks of this wave
+    // This workgroup's K blocks: part blockIdx.z of gridDim.z.
+    const int splits = (int)gridDim.z, split = (int)blockIdx.z;
+    const int kb_lo = (int)((int64_t)KB * split / splits), kb_hi = (int)((int64_t)KB * (split + 1) / splits);
+    const int KBs = kb_hi - kb_lo;
+    const int nj = wave < KBs ? (KBs - 1 - wave) / W + 1 : 0;   // blocks of this wave
 #pragma unroll
     for (int s = 0; s < kWideSlots; ++s)
-        if (s < nj) issue(s, wave + W * s);
+        if (s < nj) issue(s, kb_lo + wave + W * s);
 
     f32x4 acc[kR][kT];
 #pragma unroll
@@ -497,7 +505,7 @@ __global__ __launch_bounds__((wide_waves<kR, kT>()) * kWave, 1) void w8a8_wide_k
         const float wsv = *reinterpret_cast<const float*>(sl + SL::kOffWs);
         // Every operand of block j is in registers before the slot is refilled.
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        if (j + kWideSlots < nj) issue(slot, wave + W * (j + kWideSlots));
+        if (j + kWideSlots < nj) issue(slot, kb_lo + wave + W * (j + kWideSlots));
 #pragma unroll
         for (int i = 0; i < kR; ++i) {
             const i32x8 a = __builtin_bit_cast(i32x8, __builtin_shufflevector(a0[i], a1[i], 0, 1, 2, 3, 4, 5, 6, 7));
@@ -528,10 +536,7 @@ __global__ __launch_bounds__((wide_waves<kR, kT>()) * kWave, 1) void w8a8_wide_k
     // Thread x: lane L = x % 64 of output tiles u = x / 64, x / 64 + W, ...
     // (u = i * kT + t).
     const int L = threadIdx.x % kWave, rr = L & 15, gg = L >> 4;
-    for (int u = threadIdx.x / kWave; u < kR * kT; u += W) {
-        f32x4 v = *reinterpret_cast<const f32x4*>(red + (u * kWave + L) * 4);
-#pragma unroll
-        for (int w = 1; w < W; ++w) v += *reinterpret_cast<const f32x4*>(red + ((w * kR * kT + u) * kWave + L) * 4);
+    auto store_tile = [&](int u, f32x4 v) {
         const int i = u / kT, tt = u % kT;
         const int64_t m = m0 + 16 * tt + rr;
         const int64_t n = n0 + 16 * i + 4 * gg;
@@ -546,18 +551,71 @@ __global__ __launch_bounds__((wide_waves<kR, kT>()) * kWave, 1) void w8a8_wide_k
                 *reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + idx) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
             }
         }
+    };
+    // With K split, partial tile (tile, part, u) at float offset
+    // ((tile * splits + part) * kR kT + u) * 256 + 4 L of the workspace.
+    // The parts are written and read with 16-byte device-coherent (sc1)
+    // buffer accesses, which go through to memory every XCD sees, as in the
+    // tiled kernel's split hand-off.
+    constexpr int kSc1 = 16;
+    const int64_t tile = mg * (int64_t)gridDim.x + nt;
+    float* tile_parts = partials == nullptr ? nullptr : partials + tile * splits * (kR * kT) * 256;
+    const __amdgpu_buffer_rsrc_t prs =
+        __builtin_amdgcn_make_buffer_rsrc(tile_parts, 0, splits > 1 ? splits * (kR * kT) * 256 * 4 : 0, 0x00020000);
+    for (int u = threadIdx.x / kWave; u < kR * kT; u += W) {
+        f32x4 v = *reinterpret_cast<const f32x4*>(red + (u * kWave + L) * 4);
+#pragma unroll
+        for (int w = 1; w < W; ++w) v += *reinterpret_cast<const f32x4*>(red + ((w * kR * kT + u) * kWave + L) * 4);
+        if (splits == 1)
+            store_tile(u, v);
+        else
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), prs,
+                                                   ((split * (kR * kT) + u) * 256 + 4 * L) * 4, 0, kSc1);
     }
+    if (splits == 1) return;
+    // Hand-off as in the streaming kernels (stream_finish): every partial
+    // store has completed before the barrier that precedes the counter
+    // increment; the last part of the tile to arrive sums the parts in split
+    // order, stores Y and re-arms the counter.
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    uint32_t* arrived = reinterpret_cast<uint32_t*>(red + W * kR * kT * kWave * 4);
+    if (threadIdx.x == 0)
+        *arrived = __hip_atomic_fetch_add(&counters[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (*arrived != (uint32_t)(splits - 1)) return;
+    for (int u = threadIdx.x / kWave; u < kR * kT; u += W) {
+        i32x4 p[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (q < splits)
+                p[q] = __builtin_amdgcn_raw_buffer_load_b128(prs, ((q * (kR * kT) + u) * 256 + 4 * L) * 4, 0, kSc1);
+        f32x4 v = __builtin_bit_cast(f32x4, p[0]);
+#pragma unroll
+        for (int q = 1; q < 4; ++q)
+            if (q < splits) v += __builtin_bit_cast(f32x4, p[q]);
+        store_tile(u, v);
+    }
+    if (threadIdx.x == 0) __hip_atomic_store(&counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 hipError_t launch_w8a8_wide(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
-                            void* y, int y_dtype, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+                            void* y, int y_dtype, int64_t M, int64_t N, int64_t K, void* workspace,
+                            hipStream_t stream) {
     if (M < 1 || N % 16 != 0 || K > kTileMaxK) return hipErrorInvalidValue;
-    const WideShape w = w8a8_wide_shape(M, N);
-    if (w.groups_m > 65535) return hipErrorInvalidValue;
-    const dim3 grid(w.groups_n, w.groups_m);
+    const WideShape w = w8a8_wide_shape(M, N, K);
+    if (w.groups_m > 65535 || w.splits < 1 || w.splits > 4) return hipErrorInvalidValue;
+    uint32_t* counters = nullptr;
+    float* partials = nullptr;
+    if (w.splits > 1) {
+        if (!workspace) return hipErrorInvalidValue;
+        counters = static_cast<uint32_t*>(workspace);
+        partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + w8a8_wide_counter_bytes(w));
+    }
+    const dim3 grid(w.groups_n, w.groups_m, (unsigned)w.splits);
 #define BFP8_LAUNCH_WIDE(R, T)                                                                                   \
     hipLaunchKernelGGL((w8a8_wide_kernel<R, T>), grid, dim3(wide_waves<R, T>() * kWave), 0, stream, xq, xs, wq, ws, \
-                       y, y_dtype, M, N, K)
+                       y, y_dtype, M, N, K, partials, counters)
     if (w.kt == 1) {
         if (w.kr == 4) BFP8_LAUNCH_WIDE(4, 1);
         else if (w.kr == 2) BFP8_LAUNCH_WIDE(2, 1);

@@ -61,8 +61,7 @@ W8A8_SPLIT_K_STREAM = [(M, 512, 12288, "w8a8_stream/split") for M in (1, 4, 16)]
 # Paths that need no workspace for M <= 512 (all-token kernel, or the
 # streaming kernel over 16-token tiles on small projections).
 W8A8_NO_WORKSPACE = [
-    (1, 1024, 12288, "w8a8_wide:16x16w8"), (5, 2048, 12288, "w8a8_wide:16x16w8"),
-    (16, 1024, 12288, "w8a8_wide:16x16w8"), (17, 1024, 4096, "w8a8_stream"), (24, 1024, 4096, "w8a8_stream"),
+    (17, 1024, 4096, "w8a8_stream"), (24, 1024, 4096, "w8a8_stream"), (32, 12288, 12288, "w8a8_wide:64x32w4"),
     (32, 4096, 4096, "w8a8_wide:16x32w8"), (33, 4096, 4096, "w8a8_wide:32x32w8"), (50, 1024, 4096, "w8a8_stream"),
     (64, 4096, 4096, "w8a8_wide:32x32w8"), (32, 12288, 256, "w8a8_wide:64x32w4"), (20, 16, 8192, "w8a8_stream"),
     (20, 8208, 256, "w8a8_wide:64x32w4"),                 # last 64-row weight tile holds 16 rows
@@ -80,6 +79,17 @@ W8A8_NO_WORKSPACE = [
     (5, 8192, 512, "w8a8_wide:32x16w8"), (12, 16400, 256, "w8a8_stream"),          # no one-round shape
     # 8 < M <= 16 where streaming would leave CUs idle (fewer than 256 weight-row tiles)
     (12, 2064, 1024, "w8a8_wide:16x16w8"), (9, 1024, 6144, "w8a8_wide:16x16w8"), (8, 2048, 4096, "w8a8_stream"),
+]
+
+# Long K on the all-token kernel with K split over two or four workgroups
+# where the unsplit launch would leave most CUs idle (N <= 1024): ragged M,
+# an uneven split (K = 12416: 97 blocks in four parts), K = 16384, one
+# token, a single 16-row weight tile.
+W8A8_WIDE_SPLIT = [
+    (1, 1024, 12288, "w8a8_wide:16x16w8/split"), (5, 1024, 12288, "w8a8_wide:16x16w8/split"),
+    (16, 1024, 12288, "w8a8_wide:16x16w8/split"), (11, 1024, 16384, "w8a8_wide:16x16w8/split"),
+    (20, 1008, 12416, "w8a8_wide:16x32w8/split"), (32, 1024, 16384, "w8a8_wide:16x32w8/split"),
+    (31, 1008, 12288, "w8a8_wide:16x32w8/split"), (17, 16, 12288, "w8a8_wide:16x32w8/split"),
 ]
 
 # Every tiled configuration, ragged M and N tiles, split K.
@@ -212,7 +222,8 @@ def all_cases():
     """(op, M, N, K, variant) for every case above."""
     out = []
     tables = {
-        W8A8: [W8A8_THRESHOLD, W8A8_ONE_TOKEN, W8A8_ABOVE_ONE_TOKEN, W8A8_STRADDLE, W8A8_SPLIT_K_STREAM, W8A8_NO_WORKSPACE, W8A8_TILE,
+        W8A8: [W8A8_THRESHOLD, W8A8_ONE_TOKEN, W8A8_ABOVE_ONE_TOKEN, W8A8_STRADDLE, W8A8_SPLIT_K_STREAM, W8A8_NO_WORKSPACE,
+               W8A8_WIDE_SPLIT, W8A8_TILE,
                [W8A8_LARGE_RAGGED, W8A8_DECODE_OPROJ, W8A8_PREFILL_OPROJ, W8A8_DETERMINISTIC], W8A8_ONE_HOT],
         QW8A8: [QUANT_W8A8],
         W8A16: [W8A16_BY_M, W8A16_ONE_TOKEN, W8A16_ONE_TILE, W8A16_ALL_TOKENS, W8A16_LONG_K, W8A16_SPLIT_K_STREAM,

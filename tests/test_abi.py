@@ -100,7 +100,8 @@ def test_workspace_sizes(lib):
     assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 1, 4096, 4096) == 0
     assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 1, 512, 12288) > 0
     assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 1, 1024, 4096) == 0   # K not split up to 8192
-    assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 1, 1024, 12288) == 0  # all-token kernel
+    # all-token kernel with K split 4 ways: counters (64 tiles, 256-byte aligned) + 4 fp32 partial 16x16 tiles each
+    assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 1, 1024, 12288) == 256 + 64 * 4 * 256 * 4
     assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 4096, 1024, 4096) == 0   # 128x128 tiles
     assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 4096, 4096, 4096) == 0   # 256x256 tiles
     # 16 < M <= 32, and K <= 4096 where the launch fits one round: one
@@ -112,10 +113,11 @@ def test_workspace_sizes(lib):
     assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 64, 12288, 4096) == 0
     assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 256, 4096, 4096) == 0
     # ... while 12288 x 4096 at M = 128 is tiled (128x128 tiles, K split 2
-    # ways: 192 workgroups in one round), and so is 4096 x 12288 at M = 64
-    # (K split 8 ways)
+    # ways: 192 workgroups in one round), and so are 4096 x 12288 at M = 64
+    # (128x64 tiles, K split 8 ways) and M = 256 (128x128, K split 4 ways)
     assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 128, 12288, 4096) == 512 + 96 * 2 * 128 * 128 * 4
     assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 64, 4096, 12288) == 256 + 32 * 8 * 128 * 64 * 4
+    assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 256, 4096, 12288) == 256 + 32 * 2 * 4 * 128 * 128 * 4
     # mid M: 64x128 tiles, K split 4 ways -> counters + 4 fp32 partial tiles per output tile
     assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 100, 4096, 8192) == 256 + 64 * 4 * 64 * 128 * 4
     assert bfp8.bfp8_workspace_bytes(bfp8.OP_GEMM_W8A8_BLK128, 100, 4096, 4096) == 0    # all-token kernel

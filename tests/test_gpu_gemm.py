@@ -107,6 +107,27 @@ def test_w8a8_wide_all_tokens(gpu_lib, M, N, K, kernel):
     _w8a8_check(M, N, K, 900 + M, what="wide", kernel=kernel)
 
 
+@pytest.mark.parametrize("M,N,K,kernel", cases.W8A8_WIDE_SPLIT)
+def test_w8a8_wide_split_k(gpu_lib, M, N, K, kernel):
+    """Long K on the all-token kernel with K split over two or four
+    workgroups: the last part of each tile to arrive sums the parts in split
+    order and re-arms its counter, so two calls on one workspace give the
+    same bits; ragged M, an uneven split, K = 16384, one token."""
+    say("w8a8 wide split", kernel, f"M={M} N={N} K={K}")
+    expect(W8A8, M, N, K, kernel)
+    xq, xs, wq, ws = _w8a8_inputs(M, N, K, 1300 + M)
+    y0 = oracle.gemm_w8a8_blk128(xq, xs, wq, ws)
+    d = [dev(a) for a in (xq, xs, wq, ws)]
+    wsb = workspace(bfp8.OP_GEMM_W8A8_BLK128, M, N, K)
+    assert wsb is not None
+    y1 = run_w8a8(*d, torch.float32, wsb)
+    assert_fp32_bar(y1, y0, f"wide split {kernel} M={M} N={N} K={K}")
+    y16 = run_w8a8(*d, torch.bfloat16, wsb)
+    assert_16bit_bar(y16, y1, y0, "bf16", f"wide split {kernel}")
+    y2 = run_w8a8(*d, torch.float32, wsb)
+    assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
+
+
 @pytest.mark.parametrize("M,N,K,shape", cases.W8A8_TILE)
 def test_w8a8_tile_shapes_and_split_k(gpu_lib, M, N, K, shape):
     """Every tiled configuration, with ragged M and N tiles and split K; the
