@@ -276,27 +276,37 @@ size_t bfp8_workspace_bytes(int op, int64_t M, int64_t N, int64_t K);
  *                 on the vector ALUs: with K <= 8192 for W8A8, the fused
  *                 call and blk32, K <= 12288 for W8A16.  Otherwise W8A8
  *                 streams the weights when K needs no split across
- *                 workgroups, or N < 1024, and also up to 4 * m_stream_max,
- *                 one workgroup per 16-token tile, when those workgroups
- *                 fit one round on the CUs without a split of K; it uses a
- *                 kernel that reads all tokens per 16- or 32-row weight
- *                 tile for the other M <= 2 * m_stream_max, and when
- *                 K <= 4096 and M * N <= 2^19 (measured faster there), the
- *                 tiled MFMA kernels otherwise.  W8A16 blk128 and blk32
- *                 stream M <= m_stream_max / 2; for m_stream_max / 2 < M <=
- *                 m_stream_max they run the all-token kernel with one
- *                 16-token tile unless the streaming plan would split K
- *                 (then they stream).  Above m_stream_max, W8A16 blk128
- *                 reads all tokens per weight tile for M <= 16 *
- *                 m_stream_max when K <= 4096 and either M <= 2 *
- *                 m_stream_max or M * N <= 2^19, and for M <= 4 *
- *                 m_stream_max when K <= 8192 and that launch fits one
- *                 round of workgroups on the CUs, and uses its tiled MFMA
- *                 kernel otherwise; blk32 does the same with the all-token
- *                 range at K > 4096 limited to M <= 2 * m_stream_max (its
- *                 tiled form, scales applied in the widening, has no
- *                 promotion step), and streams one 16-token tile per
- *                 workgroup where that plan splits K.
+ *                 workgroups, or N < 1024, except that above 4 tokens
+ *                 (with K <= 4096) where streaming would take several
+ *                 rounds of workgroups, and above m_stream_max / 2 tokens
+ *                 where it would leave CUs idle, a kernel that reads all
+ *                 tokens of a 16-token tile per 16-, 32- or 64-row weight
+ *                 tile runs instead; up to 4 * m_stream_max it also streams
+ *                 one workgroup per 16-token tile when those workgroups
+ *                 fit one round on the CUs without a split of K.  The
+ *                 all-token kernel serves the other M <= 2 * m_stream_max
+ *                 (splitting K over two or four workgroups at K >= 12288
+ *                 where one workgroup per weight tile would leave most CUs
+ *                 idle), and K <= 4096 where M * N <= 2^19 or, for
+ *                 N >= 512, its launch fits one round of workgroups on the
+ *                 CUs; the tiled MFMA kernels otherwise.  W8A16 blk128 and
+ *                 blk32 stream M <= m_stream_max / 2 (W8A16 blk128 at
+ *                 M >= 4 with K <= 4096 runs the all-token kernel where
+ *                 streaming would take several rounds); for m_stream_max /
+ *                 2 < M <= m_stream_max they run the all-token kernel with
+ *                 one 16-token tile unless the streaming plan would split
+ *                 K (then they stream).  Above m_stream_max, W8A16 blk128
+ *                 reads all tokens per weight tile when K <= 4096 and
+ *                 either M <= 2 * m_stream_max or that launch fits one
+ *                 round of workgroups, and for M <= 4 * m_stream_max when
+ *                 K <= 8192 and the launch fits one round, and uses its
+ *                 tiled MFMA kernel otherwise; blk32 reads all tokens for
+ *                 M <= 16 * m_stream_max when K <= 4096 and either M <= 2 *
+ *                 m_stream_max or M * N <= 2^19, and for M <= 2 *
+ *                 m_stream_max when K <= 8192 in one round (its tiled form,
+ *                 scales applied in the widening, has no promotion step),
+ *                 and streams one 16-token tile per workgroup where that
+ *                 plan splits K.
  * Any output pointer may be NULL.
  */
 bfp8_status bfp8_get_limits(int op, int64_t* k_multiple, int64_t* n_multiple,
