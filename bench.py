@@ -404,6 +404,29 @@ def extra_prefill(torch, bfp8, inputs, args):
     return out
 
 
+def extra_w8a16_tile(torch, bfp8, inputs, args):
+    """The W8A16 blk128 GEMM at M = N = K = 4096 (bf16 activations, the
+    tiled kernel) after the same clock ramp as the prefill GEMM."""
+    M = N = K = 4096
+    x = inputs.activations(M, K, workload=2, stream=0, outliers=True).cuda()
+    wq, ws = bfp8.quantize_weight(inputs.workload(2)["w"].cuda())
+    copies = [(wq.clone(), ws.clone()) for _ in range(4)]
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    wsb = bfp8.make_workspace(bfp8.OP_GEMM_W8A16_BLK128, M, N, K)
+
+    def gemm(i):
+        a = copies[i % len(copies)]
+        bfp8.bfp8_gemm_w8a16_blk128(x, a[0], a[1], y, wsb)
+
+    us, n_warm, warm_ms = timed_after_ramp(torch, gemm, 100, args.prefill_warm_ms)
+    flops = 2.0 * M * N * K
+    del copies, y, wsb
+    return {"avg_us": us, "TFLOPs": flops / (us * 1e6), "mfma_frac": flops / (us * 1e6) / BF16_PEAK_TFLOPS,
+            "M": M, "N": N, "K": K, "x_dtype": "bf16",
+            "kernel": bfp8.bfp8_get_plan(bfp8.OP_GEMM_W8A16_BLK128, M, N, K)["kernel_name"],
+            "ramp": f"{n_warm} launches (~{warm_ms:.0f} ms of GPU time) back to back before 100 timed launches"}
+
+
 def extra_blk32(torch, bfp8, inputs, args, M=1):
     N, K = 4096, 7168
     x = inputs.activations(M, K, workload=3, dtype=torch.float16).cuda()
@@ -543,6 +566,7 @@ def bench_decode(torch, bfp8, inputs, args):
                 kern[n]["vs_read_floor"] = kern[n]["avg_us"] / floor["avg_us"]
         kern["read_floor"] = floor
         kern["prefill_gemm_w8a8_blk128"] = extra_prefill(torch, bfp8, inputs, args)
+        kern["w8a16_tile_m4096"] = extra_w8a16_tile(torch, bfp8, inputs, args)
         torch.cuda.empty_cache()
         kern["blk32_m1"] = extra_blk32(torch, bfp8, inputs, args, M=1)
         kern["blk32_m16"] = extra_blk32(torch, bfp8, inputs, args, M=16)
