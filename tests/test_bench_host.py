@@ -1,6 +1,6 @@
 """Host-side logic of bench.py, on the CPU: the weight rotation never lets a
 timed launch find its weights in the 256 MiB last-level cache, for the
-driver's invocation and the defaults, and the reuse check catches a rotation
+short runs (--steps 20 --warmup 5) and the defaults, and the reuse check catches a rotation
 that does."""
 
 import pytest

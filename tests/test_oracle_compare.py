@@ -7,7 +7,7 @@ Y0, max |Y - Y0| <= 1e-2 * rms(Y0) with rms over all M*N outputs of Y0, and
 carry half an ulp of the output format at |Y0| (round-to-nearest of a result
 that already meets the fp32 bar).  The pins below fix every piece of that:
 hand-computed values of the error measures, arrays built to sit just inside
-and just outside each bound (the verdict must flip), the half-ulp against the
+and just outside each bound (pass must turn to fail), the half-ulp against the
 spacing of the formats taken from their bit patterns, and rms taken over Y0,
 not over Y."""
 
