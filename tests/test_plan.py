@@ -107,6 +107,42 @@ def test_routing_rules_read_off_the_plan():
             assert M == 1 or M <= 8
 
 
+def test_all_token_shapes_follow_their_rules():
+    """The all-token shape rules the launch header states, over the sweep:
+    one token tile up to 16 tokens; W8A8 past M * N = 2^19 (K <= 4096, M >
+    32) only in one round with N >= 512; a K split only at K >= 12288 for
+    M <= 32, where one workgroup per weight tile would leave at least three
+    quarters of the CUs idle, and always in one round; W8A16 blk128 without
+    the (4, 4) and (2, 4) forms; block-32 at most two weight-row tiles."""
+    for op, M, N, K in _sweep():
+        p = bfp8.bfp8_get_plan(op, M, N, K)
+        name = p["kernel_name"]
+        if not name.endswith("_wide"):
+            continue
+        kr, kt = p["tile_n"] // 16, p["tile_m"] // 16
+        where = (op, M, N, K, p)
+        assert kr in (1, 2, 4) and kt in (1, 2, 4), where
+        assert (kt == 1) == (M <= 16), where
+        # (the fused call's workspace also holds the staged codes)
+        assert op == cases.QW8A8 or p["workspace_bytes"] == 0 or p["splits"] > 1, where
+        if name == "w8a8_wide":
+            if M > 32 and M * N > 1 << 19:
+                assert K <= 4096 and N >= 512 and p["workgroups"] <= 256, where
+            if p["splits"] > 1:
+                assert K >= 12288 and M <= 32 and p["splits"] in (2, 4), where
+                assert p["workgroups"] <= 256 and p["workgroups"] // p["splits"] <= 64, where
+                assert (K // 128) // p["splits"] >= 24 and p["workspace_bytes"] > 0, where
+                if op == cases.W8A8:
+                    assert p["workspace_bytes"] == 256 * ((p["workgroups"] // p["splits"] * 4 + 255) // 256) + \
+                        p["workgroups"] * kr * kt * 256 * 4, where
+            assert p["waves"] == (4 if kr == 4 or kt == 4 else 8), where
+        elif name == "w8a16_wide":
+            assert p["splits"] == 1 and (kr, kt) not in ((4, 4), (2, 4)), where
+            assert p["waves"] == (4 if kr == 4 or (kt > 1 and not (kt == 4 and kr == 2)) else 8), where
+        else:
+            assert name == "blk32_wide" and kr <= 2 and p["splits"] == 1, where
+
+
 def test_plan_refusals():
     p = bfp8.bfp8_get_plan(cases.W8A8, 1, 4096, 4096)
     assert p["kernel_name"] == "w8a8_gemv"
