@@ -74,6 +74,7 @@ W8A8_NO_WORKSPACE = [
     (144, 1040, 1024, "w8a8_wide:16x64w4"),               # ragged M and N
     (260, 2064, 1024, "w8a8_wide:64x64w4"),               # ragged M and N (16 rows in the last weight tile)
     (256, 4096, 4096, "w8a8_wide:64x64w4"),
+    (1000, 1024, 512, "w8a8_wide:64x64w4"),               # 16 token groups, ragged last group
     # 4 < M <= 16 where streaming would take several rounds of 16-row tiles
     (8, 12288, 1024, "w8a8_wide:64x16w4"), (16, 6160, 2048, "w8a8_wide:32x16w8"),   # ragged N
     (5, 8192, 512, "w8a8_wide:32x16w8"), (12, 16400, 256, "w8a8_stream"),          # no one-round shape
