@@ -562,10 +562,16 @@ __global__ __launch_bounds__((wide_waves<kR, kT>()) * kWave, 1) void w8a8_wide_k
     float* tile_parts = partials == nullptr ? nullptr : partials + tile * splits * (kR * kT) * 256;
     const __amdgpu_buffer_rsrc_t prs =
         __builtin_amdgcn_make_buffer_rsrc(tile_parts, 0, splits > 1 ? splits * (kR * kT) * 256 * 4 : 0, 0x00020000);
-    for (int u = threadIdx.x / kWave; u < kR * kT; u += W) {
+    constexpr int kU = (kR * kT + W - 1) / W;   // output tiles per thread
+    f32x4 own[kU];
+#pragma unroll
+    for (int iu = 0; iu < kU; ++iu) {
+        const int u = (int)threadIdx.x / kWave + W * iu;
+        if (u >= kR * kT) continue;
         f32x4 v = *reinterpret_cast<const f32x4*>(red + (u * kWave + L) * 4);
 #pragma unroll
         for (int w = 1; w < W; ++w) v += *reinterpret_cast<const f32x4*>(red + ((w * kR * kT + u) * kWave + L) * 4);
+        own[iu] = v;
         if (splits == 1)
             store_tile(u, v);
         else
@@ -584,16 +590,21 @@ __global__ __launch_bounds__((wide_waves<kR, kT>()) * kWave, 1) void w8a8_wide_k
         *arrived = __hip_atomic_fetch_add(&counters[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     if (*arrived != (uint32_t)(splits - 1)) return;
-    for (int u = threadIdx.x / kWave; u < kR * kT; u += W) {
+    // This workgroup's own part is still in registers (the same bits it
+    // wrote): only the other parts are read back.
+#pragma unroll
+    for (int iu = 0; iu < kU; ++iu) {
+        const int u = (int)threadIdx.x / kWave + W * iu;
+        if (u >= kR * kT) continue;
         i32x4 p[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-            if (q < splits)
+            if (q < splits && q != split)
                 p[q] = __builtin_amdgcn_raw_buffer_load_b128(prs, ((q * (kR * kT) + u) * 256 + 4 * L) * 4, 0, kSc1);
-        f32x4 v = __builtin_bit_cast(f32x4, p[0]);
+        f32x4 v = split == 0 ? own[iu] : __builtin_bit_cast(f32x4, p[0]);
 #pragma unroll
         for (int q = 1; q < 4; ++q)
-            if (q < splits) v += __builtin_bit_cast(f32x4, p[q]);
+            if (q < splits) v += q == split ? own[iu] : __builtin_bit_cast(f32x4, p[q]);
         store_tile(u, v);
     }
     if (threadIdx.x == 0) __hip_atomic_store(&counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -626,10 +626,16 @@ __global__ __launch_bounds__(C::kThreads, 1) void w8a8_tile_kernel(
         __syncthreads();
         if (arrived != (uint32_t)(splits - 1)) return;
 
+        // This workgroup's own part is still in registers (the same bits it
+        // wrote): only the other splits are read back.
+        f32x4 own[C::kTi][C::kTj];
 #pragma unroll
         for (int i = 0; i < C::kTi; ++i)
 #pragma unroll
-            for (int j = 0; j < C::kTj; ++j) acc[i][j] = zero;
+            for (int j = 0; j < C::kTj; ++j) {
+                own[i][j] = acc[i][j];
+                acc[i][j] = zero;
+            }
         // kGroup slots at a time (at most 8 x kChunk loads in flight: the
         // partials of a whole large tile would not fit in registers), each
         // summed over the splits in split order.
@@ -641,7 +647,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void w8a8_tile_kernel(
                 i32x4 v[kChunk][kGroup];
 #pragma unroll
                 for (int u = 0; u < kChunk; ++u) {
-                    if (s0 + u >= splits) continue;
+                    if (s0 + u >= splits || s0 + u == split) continue;
 #pragma unroll
                     for (int q = 0; q < kGroup; ++q)
                         v[u][q] = __builtin_amdgcn_raw_buffer_load_b128(prs, slot_off(s0 + u, g0 + q), 0, kSc1);
@@ -650,8 +656,10 @@ __global__ __launch_bounds__(C::kThreads, 1) void w8a8_tile_kernel(
                 for (int u = 0; u < kChunk; ++u) {
                     if (s0 + u >= splits) continue;
 #pragma unroll
-                    for (int q = 0; q < kGroup; ++q)
-                        acc[(g0 + q) / C::kTj][(g0 + q) % C::kTj] += __builtin_bit_cast(f32x4, v[u][q]);
+                    for (int q = 0; q < kGroup; ++q) {
+                        const int i = (g0 + q) / C::kTj, j = (g0 + q) % C::kTj;
+                        acc[i][j] += s0 + u == split ? own[i][j] : __builtin_bit_cast(f32x4, v[u][q]);
+                    }
                 }
             }
         }
@@ -693,9 +701,11 @@ TilePlan make_plan(TileShape s, int64_t bn, int64_t bm, int64_t M, int64_t N, in
 // 64x128 and 128x64 0.77 (a four-wave 128x128 variant with 64 x 64 wave
 // tiles measured the same as the eight-wave one, within 5%).  t_split
 // is the hand-off of the partial tiles (written through to memory, summed
-// by the last workgroup of a tile): 3.4 us + 0.021 us per KB the last
-// workgroup reads (splits x the tile in fp32), fitted to measured split
-// plans (64 KB: 4.7-5.1 us, 128 KB: 6.1-6.6 us, 512 KB: 14 us).  Split
+// by the last workgroup of a tile): 3.4 us + 0.021 us per KB of the
+// splits' partial tiles (splits x the tile in fp32), fitted to measured
+// split plans (64 KB: 4.7-5.1 us, 128 KB: 6.1-6.6 us, 512 KB: 14 us) when
+// the last workgroup still read its own part back; it now keeps that part
+// in registers (4096 x 4096 M = 512, split 2: 22.0 -> 21.2 us).  Split
 // plans are kept to one round of workgroups and 16 MiB of partial tiles.
 // Measured against the rules this replaces (us, N x K, M): 4096 x 4096
 // M = 512 24.6 -> 21.3 (128x128 split 2), M = 256 17.4 -> 16.3 (128x64

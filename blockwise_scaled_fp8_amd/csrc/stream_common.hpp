@@ -369,7 +369,8 @@ __device__ __forceinline__ void stream_finish(f32x4 acc, float* red, void* y, in
 
     if (t < 256) {
         // Sum in split order; the loads of eight splits are issued together
-        // before any is added (one memory round trip per eight splits).
+        // before any is added (one memory round trip per eight splits).  This
+        // workgroup's own part is v, the same bits it wrote.
         constexpr int kChunk = 8;
         float s = 0.0f;
         for (int64_t k0 = 0; k0 < splits; k0 += kChunk) {
@@ -377,7 +378,9 @@ __device__ __forceinline__ void stream_finish(f32x4 acc, float* red, void* y, in
 #pragma unroll
             for (int u = 0; u < kChunk; ++u)
                 if (k0 + u < splits)
-                    p[u] = __hip_atomic_load(&my_tiles[(k0 + u) * 256 + t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    p[u] = k0 + u == split ? v
+                                           : __hip_atomic_load(&my_tiles[(k0 + u) * 256 + t], __ATOMIC_RELAXED,
+                                                               __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
             for (int u = 0; u < kChunk; ++u)
                 if (k0 + u < splits) s += p[u];
