@@ -67,6 +67,29 @@ def build(verbose=False):
     return LIB
 
 
+# Host code under AddressSanitizer and UndefinedBehaviorSanitizer, device
+# code as for libbfp8.so: each -fsanitize= applies to the host compile only.
+SANITIZE_HOST_FLAGS = [f for opt in ("-fsanitize=address", "-fsanitize=undefined",
+                                      "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer")
+                       for f in ("-Xarch_host", opt)]
+
+
+def build_host_sanitized(out):
+    """libbfp8.so's sources built into `out` with the host code instrumented
+    by AddressSanitizer and UndefinedBehaviorSanitizer, for CPU tests of the
+    host-side argument checks, planners and the block-32 packer.  The
+    sanitizer runtime is not linked in: a process that loads the library
+    preloads it (LD_PRELOAD)."""
+    _link_to(SOURCES, out, SANITIZE_HOST_FLAGS)
+    return out
+
+
+def _link_to(sources, out, extra):
+    tmp = out + ".tmp"
+    _run([HIPCC] + COMMON_FLAGS + extra + ["-shared", "-o", tmp] + [os.path.join(CSRC, s) for s in sources])
+    os.replace(tmp, out)
+
+
 def kernel_resources(sources=None):
     """Per-kernel resource usage from a device-only compile of the sources.
 
