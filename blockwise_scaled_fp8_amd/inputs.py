@@ -19,6 +19,12 @@ Workloads (the shapes and value distributions of the pages' problems):
                        scale 2^e per 32x32 tile, e uniform on {-14, ..., 7}
   4  projection sweep: W8A8 like workload 0 for (N, K) in {4096x4096, 1024x4096,
                        12288x4096, 4096x12288}
+  5  longest K (2^23, the calls' limit), a few rows: E4M3 codes drawn
+                       uniformly from the 254 finite codes for both operands,
+                       fp32 block scales 2^u with u uniform on [-10, -4),
+                       16-bit activations ~ N(0, 1) (drawn as codes and scales
+                       directly: the 16-bit matrices and their quantisation
+                       would take tens of GB on the host)
 """
 
 import numpy as np
@@ -68,6 +74,20 @@ def block32_scales(N, K, workload, stream=2, lo=-14, hi=7):
     """fp32 [N/32, K/32] scales 2^e with e uniform on {lo, ..., hi}."""
     e = rng(workload, stream).integers(lo, hi + 1, size=(N // 32, K // 32))
     return torch.from_numpy(np.ldexp(np.float32(1.0), e).astype(np.float32))
+
+
+def e4m3_codes(rows, K, workload, stream):
+    """uint8 [rows, K] codes drawn uniformly from the 254 finite E4M3 codes
+    (every byte but 0x7F and 0xFF)."""
+    v = rng(workload, stream).integers(0, 254, size=(rows, K), dtype=np.uint8)
+    v += v >= 0x7F
+    return torch.from_numpy(v)
+
+
+def block_scales(rows, cols, workload, stream, lo=-10.0, hi=-4.0):
+    """fp32 [rows, cols] positive scales 2^u, u uniform on [lo, hi)."""
+    u = rng(workload, stream).uniform(lo, hi, size=(rows, cols))
+    return torch.from_numpy(np.exp2(u).astype(np.float32))
 
 
 def workload(wid, M=None):

@@ -210,6 +210,17 @@ BLK32_SPLIT_K_16 = (16, 1024, 12288, "blk32_stream_lds/split")
 BLK32_SPLIT_K_ABOVE_16 = (20, 512, 12288, "blk32_stream/split")
 
 
+# The longest K the calls accept (2^23): every kernel family's 32-bit buffer
+# offsets at their largest (weight and token rows 2^23 bytes, or 2^24 for
+# 16-bit tokens, apart), with K split across workgroups.
+K_MAX = 1 << 23
+W8A8_MAX_K = [(3, 32, K_MAX, "w8a8_stream/split"), (20, 64, K_MAX, "w8a8_wide:16x32w8/split"),
+              (40, 128, K_MAX, "w8a8_tile:64x128w8/split")]
+QUANT_W8A8_MAX_K = [(2, 32, K_MAX, "w8a8_stream_quant/split")]
+W8A16_MAX_K = [(3, 32, K_MAX, "w8a16_stream/split"), (40, 128, K_MAX, "w8a16_tile:128x64w8/split")]
+BLK32_MAX_K = [(1, 32, K_MAX, "blk32_stream_lds/split"), (40, 64, K_MAX, "blk32_stream/split")]
+
+
 def coverage_key(op, v):
     """The fused call that stages the codes through the quantiser runs the
     same W8A8 kernel as the codes call: its variants count as that call's
@@ -225,16 +236,17 @@ def all_cases():
     tables = {
         W8A8: [W8A8_THRESHOLD, W8A8_ONE_TOKEN, W8A8_ABOVE_ONE_TOKEN, W8A8_STRADDLE, W8A8_SPLIT_K_STREAM, W8A8_NO_WORKSPACE,
                W8A8_WIDE_SPLIT, W8A8_TILE,
-               [W8A8_LARGE_RAGGED, W8A8_DECODE_OPROJ, W8A8_PREFILL_OPROJ, W8A8_DETERMINISTIC], W8A8_ONE_HOT],
-        QW8A8: [QUANT_W8A8],
+               [W8A8_LARGE_RAGGED, W8A8_DECODE_OPROJ, W8A8_PREFILL_OPROJ, W8A8_DETERMINISTIC], W8A8_ONE_HOT,
+               W8A8_MAX_K],
+        QW8A8: [QUANT_W8A8, QUANT_W8A8_MAX_K],
         W8A16: [W8A16_BY_M, W8A16_ONE_TOKEN, W8A16_ONE_TILE, W8A16_ALL_TOKENS, W8A16_LONG_K, W8A16_SPLIT_K_STREAM,
                 W8A16_ONE_HOT,
                 W8A16_TILE_SPLIT, [W8A16_TILE_ONE_HOT, W8A16_TILE_LARGE_RAGGED, W8A16_TILE_LARGE_ONE_HOT,
-                                   W8A16_PREFILL_OPROJ, W8A16_DECODE_OPROJ]],
+                                   W8A16_PREFILL_OPROJ, W8A16_DECODE_OPROJ], W8A16_MAX_K],
         BLK32: [BLK32_WORKLOAD, BLK32_ONE_TOKEN, BLK32_ONE_TILE, BLK32_ABOVE_16, BLK32_TILE, [BLK32_TILE_ONE_HOT],
                 [BLK32_WINDOW, BLK32_ONE_HOT, BLK32_ONE_HOT_STREAM, BLK32_ONE_HOT_ABOVE_16,
                  BLK32_ONE_HOT_ABOVE_16_SPLIT, BLK32_ONE_HOT_ONE_TOKEN,
-                 BLK32_SPLIT_K, BLK32_SPLIT_K_16, BLK32_SPLIT_K_ABOVE_16]],
+                 BLK32_SPLIT_K, BLK32_SPLIT_K_16, BLK32_SPLIT_K_ABOVE_16], BLK32_MAX_K],
     }
     for op, tabs in tables.items():
         for tab in tabs:
