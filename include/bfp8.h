@@ -287,7 +287,9 @@ size_t bfp8_workspace_bytes(int op, int64_t M, int64_t N, int64_t K);
  *                 all-token kernel serves the other M <= 2 * m_stream_max
  *                 (splitting K over two or four workgroups at K >= 12288
  *                 where one workgroup per weight tile would leave most CUs
- *                 idle), and K <= 4096 where M * N <= 2^19 or, for
+ *                 idle, and over two for 32-row tiles in place of 16-row
+ *                 ones above m_stream_max tokens, which halves the token
+ *                 rows each workgroup reads), and K <= 4096 where M * N <= 2^19 or, for
  *                 N >= 512, its launch fits one round of workgroups on the
  *                 CUs; the tiled MFMA kernels otherwise.  W8A16 blk128 and
  *                 blk32 stream M <= m_stream_max / 2 (W8A16 blk128 at

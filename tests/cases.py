@@ -91,6 +91,10 @@ W8A8_WIDE_SPLIT = [
     (16, 1024, 12288, "w8a8_wide:16x16w8/split"), (11, 1024, 16384, "w8a8_wide:16x16w8/split"),
     (20, 1008, 12416, "w8a8_wide:16x32w8/split"), (32, 1024, 16384, "w8a8_wide:16x32w8/split"),
     (31, 1008, 12288, "w8a8_wide:16x32w8/split"), (17, 16, 12288, "w8a8_wide:16x32w8/split"),
+    # 32-row tiles split two ways where 16-row tiles would fill more than 64 workgroups:
+    # the down_proj shape, a ragged last tile (N = 1040, 33 tiles), an uneven split (97 blocks) with ragged M
+    (32, 4096, 12288, "w8a8_wide:32x32w8/split"), (17, 1040, 12288, "w8a8_wide:32x32w8/split"),
+    (25, 4080, 12416, "w8a8_wide:32x32w8/split"),
 ]
 
 # Every tiled configuration, ragged M and N tiles, split K.

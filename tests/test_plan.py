@@ -112,7 +112,9 @@ def test_all_token_shapes_follow_their_rules():
     one token tile up to 16 tokens; W8A8 past M * N = 2^19 (K <= 4096, M >
     32) only in one round with N >= 512; a K split only at K >= 12288 for
     M <= 32, where one workgroup per weight tile would leave at least three
-    quarters of the CUs idle, and always in one round; W8A16 blk128 without
+    quarters of the CUs idle, or, for 16 < M <= 32, as 32-row tiles split two
+    ways in place of more than 64 16-row tiles, and always in one round;
+    W8A16 blk128 without
     the (4, 4) and (2, 4) forms; block-32 at most two weight-row tiles."""
     for op, M, N, K in _sweep():
         p = bfp8.bfp8_get_plan(op, M, N, K)
@@ -130,7 +132,11 @@ def test_all_token_shapes_follow_their_rules():
                 assert K <= 4096 and N >= 512 and p["workgroups"] <= 256, where
             if p["splits"] > 1:
                 assert K >= 12288 and M <= 32 and p["splits"] in (2, 4), where
-                assert p["workgroups"] <= 256 and p["workgroups"] // p["splits"] <= 64, where
+                assert p["workgroups"] <= 256, where
+                if p["workgroups"] // p["splits"] > 64:
+                    # 32-row tiles split two ways in place of 16-row tiles on more than 64 workgroups
+                    assert (kr, kt, p["splits"]) == (2, 2, 2) and M > 16, where
+                    assert (N + 15) // 16 > 64 and p["workgroups"] >= (N + 15) // 16, where
                 assert (K // 128) // p["splits"] >= 24 and p["workspace_bytes"] > 0, where
                 if op == cases.W8A8:
                     assert p["workspace_bytes"] == 256 * ((p["workgroups"] // p["splits"] * 4 + 255) // 256) + \
