@@ -43,6 +43,7 @@ def _both(xq, xs, wq, ws, out_dtype):
     ((200, 2048, 4224), (16, 512, 12288)),      # 64x128 split 4, then the streaming kernel split over K
     ((128, 4096, 4096), (1, 1024, 4096)),       # no workspace: all-token kernel, then one token
     ((24, 1024, 12288), (5, 1024, 12288)),      # all-token kernel with K split 4 ways, twice (counters re-armed)
+    ((32, 4096, 12288), (20, 2064, 12288)),     # 32-row all-token tiles split two ways, then fewer of them
 ])
 def test_noalloc_matches_workspace_call(gpu_lib, first, second):
     assert np.prod(second) < np.prod(first)
